@@ -1,0 +1,16 @@
+"""CPU oracle for per-token adapter routing (MoLoRA).  TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the benchmark's CPU-baseline leg
+may import this package.  The GPU library never calls it and shares no code
+with it.  See ``oracle/molora_oracle.py`` for the functions and their sources.
+"""
+from .molora_oracle import (  # noqa: F401
+    bf16_to_f64,
+    route_vocab,
+    router_logits,
+    route_topk,
+    dispatch,
+    apply,
+    apply_masked_passes,
+    pairs_of,
+)
