@@ -1,0 +1,228 @@
+/*
+ * molora.h — C ABI of the MI355X (gfx950) per-token adapter-routing library.
+ *
+ * The method (MoLoRA pages, "MoLoRA: Composable Specialization via Per-Token
+ * Adapter Routing"; the technical figures and tables are on the
+ * thelatestinai.com page): every token is routed to one adapter by its
+ * vocabulary range, or to k adapters by a learned top-k gate (Table 1,
+ * "Routing decision"); the routed (token, adapter) pairs are counted per
+ * adapter, turned into offsets ("pointer arrays") and grouped by adapter
+ * (Table 1 rows "Histogram computation", "Pointer arrays"; Figure 2 right);
+ * grouped LoRA shrink x·A_e (d_in -> r) and expand h·B_e (r -> d_out) run
+ * over adapters held at fixed GPU addresses (Figure 4, hot set; Table 10 for
+ * the shapes A (K, d, r) and B (K, r, d)); the gate-weighted deltas, scaled by
+ * the LoRA factor alpha/r, are added into the base output y (Figure 2 left:
+ * weighted sum).
+ *
+ * Conventions for every entry point:
+ *  - Pointers named as device pointers must point to memory of the current
+ *    HIP device, 16-byte aligned.  "host" pointers are read during the call.
+ *  - The caller owns every buffer.  The library owns only the host-side
+ *    molora_hotset descriptor.
+ *  - `stream` is a hipStream_t (NULL = the legacy default stream).  Except
+ *    for molora_hotset_init / molora_hotset_destroy, every call only
+ *    enqueues work on `stream`: it never synchronises the host and never
+ *    reads device memory from the host, so the calls can be captured into a
+ *    HIP graph.
+ *  - Return value: MOLORA_OK, or an error code.  Argument errors are detected
+ *    on the host before anything is enqueued; molora_last_error() then holds
+ *    a message (thread-local).  MOLORA_EHIP reports a HIP runtime error.
+ *  - N = 0 (no tokens) is a successful no-op.
+ *  - Data-dependent conditions are not errors: a token id outside every
+ *    vocabulary range, or an adapter index outside [0, K), marks the pair
+ *    "unrouted"; such pairs are left out of counts/offsets/perm and add no
+ *    delta.
+ *  - bf16 means the 16-bit bfloat16 format (upper half of an IEEE fp32).
+ */
+#ifndef MOLORA_H
+#define MOLORA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  MOLORA_OK = 0,
+  MOLORA_EINVAL = 1,  /* null/misaligned pointer, bad shape or count */
+  MOLORA_ENOTSUP = 2, /* shape outside the supported set (see each call) */
+  MOLORA_ENOSPC = 3,  /* slab or workspace smaller than required */
+  MOLORA_EHIP = 4     /* HIP runtime or launch error */
+};
+
+enum { MOLORA_LAYOUT_DIRECT = 0, MOLORA_LAYOUT_INDIRECT = 1 };
+enum { MOLORA_PATH_AUTO = 0, MOLORA_PATH_GROUPED = 1, MOLORA_PATH_SKINNY = 2 };
+enum { MOLORA_BF16 = 0, MOLORA_F32 = 1 };
+
+/* Limits of this build. */
+#define MOLORA_MAX_ADAPTERS 64 /* K (hot-set capacity per target) */
+#define MOLORA_MAX_RANK 64     /* r */
+#define MOLORA_MAX_TOPK 8      /* k */
+#define MOLORA_ROUTER_HIDDEN 64 /* H of the router MLP d -> H -> K */
+
+/* Message for the last non-OK return on this thread ("" if none). */
+const char *molora_last_error(void);
+
+/* ------------------------------------------------------------------------
+ * Hot set (thelatestinai.com, Figure 4: adapters pre-allocated on the GPU at
+ * fixed addresses so that the step can be captured in a graph; Table 2:
+ * direct versus indirect memory layout).
+ *
+ * One hot set holds K adapters of rank r for each of n_targets projections
+ * (e.g. the 7 LoRA targets of one transformer layer).  Target t has input
+ * width d_in and output width d_out; its user-facing weights are
+ *   A: bf16 [K][d_in][r]   row-major (Table 10: A has shape (K, d, r))
+ *   B: bf16 [K][r][d_out]  row-major (Table 10: B has shape (K, r, d))
+ * molora_hotset_init copies them into the caller's slab in the library's
+ * internal layout (transposed, rank padded to a multiple of 16) and records
+ * their addresses in the descriptor.  The slab must stay allocated and must
+ * not move until molora_hotset_destroy: graphs captured over molora_apply
+ * embed its addresses.
+ *   layout = MOLORA_LAYOUT_DIRECT:   adapter e of target t lives at
+ *            base_t + e * stride_t; kernels compute the address.
+ *   layout = MOLORA_LAYOUT_INDIRECT: adapters are placed at permuted slots of
+ *            the slab and kernels load their addresses from a per-target
+ *            pointer table held in the slab (same arithmetic, one extra
+ *            dependent load).
+ * Supported: 1 <= K <= 64, 1 <= r <= 64, d_in and d_out multiples of 128,
+ * 1 <= n_targets <= 16.
+ * ------------------------------------------------------------------------ */
+typedef struct molora_hotset molora_hotset;
+
+typedef struct {
+  int d_in;      /* input width of the projection */
+  int d_out;     /* output width of the projection */
+  const void *A; /* device, bf16 [K][d_in][r]; read only during init */
+  const void *B; /* device, bf16 [K][r][d_out]; read only during init */
+} molora_target;
+
+/* Bytes of slab that molora_hotset_init needs (host arithmetic only). */
+int molora_hotset_bytes(int K, int r, int n_targets, const molora_target *targets,
+                        int layout, size_t *bytes);
+
+/* Build a hot set.  `scale` is the LoRA factor alpha/r applied to every delta.
+ * Synchronous: enqueues the relayout on `stream` and waits for it.  Must not
+ * be called while `stream` is being captured.  On success *out owns a new
+ * descriptor. */
+int molora_hotset_init(molora_hotset **out, int K, int r, float scale, int n_targets,
+                       const molora_target *targets, int layout, void *slab,
+                       size_t slab_bytes, void *stream);
+
+/* Free the descriptor (not the slab).  NULL is accepted. */
+int molora_hotset_destroy(molora_hotset *hs);
+
+/* ------------------------------------------------------------------------
+ * Vocabulary routing R_vocab(v) (thelatestinai.com, Table 1).
+ *   ids    device int32 [N]: token ids
+ *   bounds host int32 [K+1], non-decreasing: adapter e owns the half-open
+ *          id range [bounds[e], bounds[e+1])
+ *   idx    device int32 [N] out: adapter of each token, -1 if the id lies
+ *          outside [bounds[0], bounds[K])
+ *   w      device fp32 [N] out: gate weight, 1 for routed tokens, 0 else
+ * 1 <= K <= 64.
+ * ------------------------------------------------------------------------ */
+int molora_route_vocab(const int32_t *ids, int N, const int32_t *bounds, int K,
+                       int32_t *idx, float *w, void *stream);
+
+/* ------------------------------------------------------------------------
+ * Learned top-k routing TopK(g_theta(x)) (thelatestinai.com, Table 1 with the
+ * routing cost O(64d + 64K), read as the MLP d -> 64 -> K; Figure 2: top-k
+ * adapters combined by a weighted sum).
+ *   Router mode (W1 != NULL):
+ *     x      device bf16 [N][d]
+ *     W1     device bf16 [64][d]   (nn.Linear layout: [out][in])
+ *     b1     device fp32 [64] or NULL
+ *     W2     device bf16 [K][64]
+ *     b2     device fp32 [K] or NULL
+ *     logits device fp32 [N][K] out: ReLU(x W1^T + b1) W2^T + b2, fp32
+ *            accumulation of the bf16 products
+ *   Logits mode (W1 == NULL; x, b1, W2, b2 ignored):
+ *     logits device fp32 [N][K] in: precomputed gate logits
+ *   Selection, both modes:
+ *     idx    device int32 [N][k] out: the k largest logits; equal logits are
+ *            taken in ascending adapter index; a token's k slots are stored
+ *            in ascending adapter index
+ *     w      device fp32 [N][k] out: softmax over the k selected logits
+ *     flags  device uint8 [N] out or NULL: 1 when k < K and the k-th largest
+ *            logit exceeds the (k+1)-th by less than 1e-4 (a near tie)
+ * Supported: 1 <= K <= 64, 1 <= k <= min(K, 8); router mode needs
+ * d a multiple of 128.
+ * ------------------------------------------------------------------------ */
+int molora_route_topk(const void *x, int N, int d, const void *W1, const float *b1,
+                      const void *W2, const float *b2, float *logits, int K, int k,
+                      int32_t *idx, float *w, uint8_t *flags, void *stream);
+
+/* ------------------------------------------------------------------------
+ * Dispatch: histogram, offsets and grouping permutation (thelatestinai.com,
+ * Table 1 rows "Histogram computation" and "Pointer arrays"; Figure 2 right:
+ * tokens grouped by their selected adapter).
+ *   idx     device int32 [N*k]: adapter of pair p = t*k + s
+ *   w       device fp32  [N*k]: gate weight of pair p
+ *   counts  device int32 [K] out: routed pairs per adapter
+ *   offsets device int32 [K+1] out: exclusive prefix sum of counts;
+ *           offsets[K] = number of routed pairs (N*k when all are routed)
+ *   perm    device int32 [N*k] out: perm[q] = pair id at grouped position q
+ *           (entries q >= offsets[K] are left untouched); inside adapter e's
+ *           segment [offsets[e], offsets[e+1]) the pair ids ascend, so the
+ *           result is unique and deterministic
+ *   perm_w  device fp32 [N*k] out: perm_w[q] = w[perm[q]]
+ *   inv     device int32 [N*k] out or NULL: inv[p] = q with perm[q] = p, or
+ *           -1 for an unrouted pair
+ *   ws      device workspace of at least molora_dispatch_workspace() bytes
+ *           (may be NULL when that size is 0)
+ * Supported: 1 <= K <= 64, 1 <= k <= 8, N*k < 2^31.
+ * ------------------------------------------------------------------------ */
+int molora_dispatch_workspace(int N, int k, int K, size_t *bytes);
+int molora_dispatch(const int32_t *idx, const float *w, int N, int k, int K,
+                    int32_t *counts, int32_t *offsets, int32_t *perm, float *perm_w,
+                    int32_t *inv, void *ws, size_t ws_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
+ * Apply: grouped LoRA shrink/expand with the gate-weighted, alpha/r-scaled
+ * scatter-add (thelatestinai.com, Figure 2: per-token weighted sum computed by
+ * a grouped GEMM over tokens grouped by adapter; Table 10 shapes).
+ * For every routed pair q of the dispatch (token t = perm[q] / k, adapter e
+ * = the segment holding q):
+ *     y[t] = y0[t] + sum_q perm_w[q] * scale * (x[t] A_e) B_e
+ * Tokens with no routed pair get y[t] = y0[t].
+ *   hs, target  hot set and the projection index inside it
+ *   x       device bf16 [N][d_in]
+ *   y0      device [N][d_out] base output, dtype y0_dtype (MOLORA_BF16 or
+ *           MOLORA_F32); may be the same buffer as y (in place)
+ *   y       device [N][d_out] out, dtype y_dtype
+ *   offsets, perm, perm_w, inv: the outputs of molora_dispatch for this
+ *           routing (inv is required when k > 1, ignored when k == 1)
+ *   path    MOLORA_PATH_AUTO (chosen on the host from N*k), _GROUPED (MFMA
+ *           tiles) or _SKINNY (per-pair dot products, for small batches)
+ *   ws      device workspace of at least molora_apply_workspace() bytes
+ * Accumulation is fp32; the shrink result h stays fp32 and enters the
+ * expand as a bf16 hi/lo pair, so bf16 rounding happens only at the store
+ * of y when y_dtype is MOLORA_BF16 (round to nearest even).
+ * ------------------------------------------------------------------------ */
+int molora_apply_workspace(const molora_hotset *hs, int target, int N, int k, int path,
+                           size_t *bytes);
+int molora_apply(const molora_hotset *hs, int target, const void *x, const void *y0,
+                 int y0_dtype, void *y, int y_dtype, int N, int k, const int32_t *offsets,
+                 const int32_t *perm, const float *perm_w, const int32_t *inv, int path,
+                 void *ws, size_t ws_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
+ * Per-sequence comparator metadata (thelatestinai.com, Table 3: per-sequence
+ * routing needs K passes for a K-modality batch; the abstract: work K*N
+ * versus N).  From a k = 1 routing idx [N], builds K one-hot dispatches: pass e
+ * routes every token to adapter e with weight 1 if idx[t] == e, else 0, so
+ * K molora_apply calls (in place, y0 == y after the first) reproduce the
+ * per-token result with K*N adapter applications.
+ *   offsets device int32 [K][K+1] out;  perm device int32 [N] out (identity);
+ *   perm_w  device fp32 [K][N] out.
+ * ------------------------------------------------------------------------ */
+int molora_seqpass_meta(const int32_t *idx, int N, int K, int32_t *offsets, int32_t *perm,
+                        float *perm_w, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOLORA_H */

@@ -1,0 +1,271 @@
+"""GPU parity: hot set + grouped apply (all paths and layouts) against the CPU oracle."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import apply, apply_masked_passes, dispatch, route_topk, route_vocab, router_logits
+from tests.gpu_util import (check_bf16_output, check_float_output, dev, dev_bf16, f64, host, need_gpu)
+
+pytestmark = pytest.mark.gpu
+
+
+def make_hotset(m, targets, scale, layout=0):
+    return m.molora_hotset_init([(dev_bf16(t.A), dev_bf16(t.B)) for t in targets], scale, layout=layout)
+
+
+def oracle_from_gpu_routing(tgt, scale, idx, w, K, k):
+    """Oracle dispatch + apply on the routing the GPU produced (fp64)."""
+    counts, offsets, perm, perm_w, inv = dispatch(idx, w.astype(np.float64), K)
+    return apply(f64(tgt.y0), f64(tgt.x), f64(tgt.A), f64(tgt.B), scale, perm, perm_w, offsets, k)
+
+
+def run_pipeline_vocab(m, case, hs, y_dtype, path=0, y=None, in_place=False):
+    t = case.targets[0]
+    idx, w = m.molora_route_vocab(dev(case.ids), case.bounds.tolist())
+    counts, offsets, perm, perm_w, inv = m.molora_dispatch(idx, w, case.K, 1)
+    x = dev_bf16(t.x)
+    y0 = dev_bf16(t.y0)
+    if y_dtype == torch.float32:
+        y0 = y0.float()
+    out = m.molora_apply(hs, x, y0, offsets, perm, perm_w, inv, k=1, y=y0 if in_place else y, y_dtype=y_dtype,
+                         path=path)
+    return out, idx, w
+
+
+@pytest.mark.parametrize("layout", [0, 1])
+@pytest.mark.parametrize("y_dtype", [torch.float32, torch.bfloat16])
+def test_tiny_vocab_pipeline(layout, y_dtype):
+    m = need_gpu()
+    c = synth.tiny_vocab()
+    hs = make_hotset(m, c.targets, c.scale, layout)
+    y, idx, w = run_pipeline_vocab(m, c, hs, y_dtype)
+    ref = oracle_from_gpu_routing(c.targets[0], c.scale, host(idx), host(w), c.K, 1)
+    if y_dtype == torch.float32:
+        check_float_output(host(y), ref, f64(c.targets[0].y0))
+    else:
+        check_bf16_output(host(y), ref)
+
+
+@pytest.mark.parametrize("path", [1, 2])
+def test_modality4_full_size(path):
+    m = need_gpu()
+    c = synth.modality4()
+    hs = make_hotset(m, c.targets, c.scale)
+    y, idx, w = run_pipeline_vocab(m, c, hs, torch.float32, path=path)
+    ri, rw = route_vocab(c.ids, c.bounds)
+    np.testing.assert_array_equal(host(idx), ri)
+    t = c.targets[0]
+    ref = oracle_from_gpu_routing(t, c.scale, ri, rw, c.K, 1)
+    check_float_output(host(y), ref, f64(t.y0))
+    yb, _, _ = run_pipeline_vocab(m, c, hs, torch.bfloat16, path=path)
+    check_bf16_output(host(yb), ref)
+
+
+def test_modality4_per_sequence_comparator():
+    """K masked dense passes (per-sequence routing) give the per-token result with K*N work."""
+    m = need_gpu()
+    c = synth.modality4()
+    t = c.targets[0]
+    hs = make_hotset(m, c.targets, c.scale)
+    idx, w = m.molora_route_vocab(dev(c.ids), c.bounds.tolist())
+    offs, perm, pw = m.molora_seqpass_meta(idx, c.K)
+    ho = host(offs)
+    for e in range(c.K):
+        assert ho[e, e] == 0 and ho[e, e + 1] == c.N  # pass e applies adapter e to all N tokens
+    x = dev_bf16(t.x)
+    y = dev_bf16(t.y0).float()
+    inv = perm  # identity
+    for e in range(c.K):
+        m.molora_apply(hs, x, y, offs[e].contiguous(), perm, pw[e].contiguous(), inv, k=1, y=y, path=1)
+    ri, rw = route_vocab(c.ids, c.bounds)
+    ref = apply_masked_passes(f64(t.y0), f64(t.x), f64(t.A), f64(t.B), c.scale, ri, rw)
+    check_float_output(host(y), ref, f64(t.y0))
+
+
+def test_small_integers_bit_exact():
+    m = need_gpu()
+    N, d_in, d_out, K, r = 50, 256, 384, 3, 8
+    xb, Ab, Bb, yb = synth.small_int_case(N, d_in, d_out, K, r, lo=-2, hi=3)
+    tg = synth.Target("p", d_in, d_out, Ab, Bb, xb, yb)
+    idx = np.random.default_rng(1).integers(0, K, N).astype(np.int32)
+    w = np.ones(N, np.float32)
+    for layout in (0, 1):
+        hs = m.molora_hotset_init([(dev_bf16(Ab), dev_bf16(Bb))], 2.0, layout=layout)
+        counts, offsets, perm, perm_w, inv = m.molora_dispatch(dev(idx), dev(w), K, 1)
+        for path in (1, 2):
+            y = m.molora_apply(hs, dev_bf16(xb), dev_bf16(yb).float(), offsets, perm, perm_w, inv, k=1,
+                               y_dtype=torch.float32, path=path)
+            ref = oracle_from_gpu_routing(tg, 2.0, idx, w, K, 1)
+            assert np.abs(ref).max() < 2 ** 24
+            np.testing.assert_array_equal(host(y), ref)
+
+
+SHAPES = [
+    # N, d_in, d_out, K, r, k
+    (1, 128, 128, 1, 8, 1),
+    (3, 512, 256, 4, 16, 1),
+    (37, 256, 512, 5, 32, 1),
+    (300, 384, 640, 7, 64, 1),
+    (1000, 1024, 1024, 64, 16, 1),
+    (17, 256, 256, 4, 16, 2),
+    (301, 512, 384, 6, 24, 3),
+    (1000, 256, 1024, 16, 64, 4),
+    (2500, 640, 512, 8, 16, 8),
+]
+
+
+@pytest.mark.parametrize("N,d_in,d_out,K,r,k", SHAPES)
+@pytest.mark.parametrize("path", [1, 2])
+def test_apply_shapes_paths(N, d_in, d_out, K, r, k, path):
+    m = need_gpu()
+    g = np.random.default_rng(N * 31 + d_in + K * 7 + r + k)
+    xb = synth.to_bf16_bits(g.standard_normal((N, d_in)).astype(np.float32))
+    Ab = synth.to_bf16_bits((g.standard_normal((K, d_in, r)) / np.sqrt(d_in)).astype(np.float32))
+    Bb = synth.to_bf16_bits((g.standard_normal((K, r, d_out)) / np.sqrt(r)).astype(np.float32))
+    yb = synth.to_bf16_bits(g.standard_normal((N, d_out)).astype(np.float32))
+    tg = synth.Target("p", d_in, d_out, Ab, Bb, xb, yb)
+    lg = g.standard_normal((N, K)).astype(np.float32)
+    oi, ow, _ = route_topk(lg.astype(np.float64), k)
+    idx = oi.astype(np.int32)
+    w = ow.astype(np.float32)
+    if N > 5:
+        idx[N // 3, 0] = -1  # an unrouted pair
+    hs = m.molora_hotset_init([(dev_bf16(Ab), dev_bf16(Bb))], 2.0)
+    counts, offsets, perm, perm_w, inv = m.molora_dispatch(dev(idx), dev(w), K, k)
+    ref = oracle_from_gpu_routing(tg, 2.0, idx, w, K, k)
+    y = m.molora_apply(hs, dev_bf16(xb), dev_bf16(yb), offsets, perm, perm_w, inv, k=k, y_dtype=torch.float32,
+                       path=path)
+    check_float_output(host(y), ref, f64(yb))
+    yb16 = m.molora_apply(hs, dev_bf16(xb), dev_bf16(yb), offsets, perm, perm_w, inv, k=k, y_dtype=torch.bfloat16,
+                          path=path)
+    check_bf16_output(host(yb16), ref)
+
+
+def test_in_place_and_unrouted_rows():
+    m = need_gpu()
+    c = synth.tiny_vocab()
+    ids = c.ids.copy()
+    ids[::5] = 40000  # outside every range: unrouted
+    c.ids = ids
+    t = c.targets[0]
+    hs = make_hotset(m, c.targets, c.scale)
+    y_out, idx, w = run_pipeline_vocab(m, c, hs, torch.float32)
+    ri, rw = route_vocab(ids, c.bounds)
+    ref = oracle_from_gpu_routing(t, c.scale, ri, rw, c.K, 1)
+    check_float_output(host(y_out), ref, f64(t.y0))
+    np.testing.assert_array_equal(host(y_out)[::5], f64(t.y0)[::5])  # untouched rows copied exactly
+    y_in, _, _ = run_pipeline_vocab(m, c, hs, torch.float32, in_place=True)
+    np.testing.assert_array_equal(host(y_in), host(y_out))
+
+
+@pytest.mark.parametrize("B", [1, 16, 64, 160, 512, 2048])
+def test_decode_sweep(B):
+    m = need_gpu()
+    c = synth.decode_batch(B)
+    t = c.targets[0]
+    hs_d = make_hotset(m, c.targets, c.scale, 0)
+    hs_i = make_hotset(m, c.targets, c.scale, 1)
+    w = np.ones(B, np.float32)
+    counts, offsets, perm, perm_w, inv = m.molora_dispatch(dev(c.idx), dev(w), c.K, 1)
+    ref = oracle_from_gpu_routing(t, c.scale, c.idx, w, c.K, 1)
+    outs = []
+    for hs in (hs_d, hs_i):
+        for path in (1, 2):
+            y = m.molora_apply(hs, dev_bf16(t.x), dev_bf16(t.y0), offsets, perm, perm_w, inv, k=1,
+                               y_dtype=torch.float32, path=path)
+            check_float_output(host(y), ref, f64(t.y0))
+            outs.append(host(y))
+    np.testing.assert_array_equal(outs[0], outs[2])  # direct == indirect, bit for bit
+    np.testing.assert_array_equal(outs[1], outs[3])
+
+
+def test_qwen_layer_all_targets():
+    m = need_gpu()
+    c = synth.qwen_layer()
+    r = c.router
+    x0 = c.targets[0].x
+    logits, idx, w, flags = m.molora_route_topk(
+        c.k, c.K, x=dev_bf16(x0), W1=dev_bf16(np.ascontiguousarray(r["W1"].T)), b1=dev(r["b1"]),
+        W2=dev_bf16(np.ascontiguousarray(r["W2"].T)), b2=dev(r["b2"]))
+    counts, offsets, perm, perm_w, inv = m.molora_dispatch(idx, w, c.K, c.k)
+    gi, gw = host(idx), host(w)
+    hs = make_hotset(m, c.targets, c.scale)
+    for ti, t in enumerate(c.targets):
+        y = m.molora_apply(hs, dev_bf16(t.x), dev_bf16(t.y0), offsets, perm, perm_w, inv, k=c.k, target=ti,
+                           y_dtype=torch.float32)
+        ref = oracle_from_gpu_routing(t, c.scale, gi, gw, c.K, c.k)
+        check_float_output(host(y), ref, f64(t.y0))
+
+
+@pytest.mark.parametrize("k", [1, 2, 3, 4])
+def test_stress_full_size(k):
+    m = need_gpu()
+    c = synth.stress(k)
+    t = c.targets[0]
+    _, idx, w, _ = m.molora_route_topk(k, c.K, logits=dev(c.logits))
+    counts, offsets, perm, perm_w, inv = m.molora_dispatch(idx, w, c.K, k)
+    hs = make_hotset(m, c.targets, c.scale)
+    y = m.molora_apply(hs, dev_bf16(t.x), dev_bf16(t.y0), offsets, perm, perm_w, inv, k=k, y_dtype=torch.float32)
+    gi, gw = host(idx), host(w)
+    oi, _, _ = route_topk(c.logits.astype(np.float64), k)
+    np.testing.assert_array_equal(gi, oi)
+    # full-size oracle on a sample of tokens (all of their pairs), to keep the CPU time bounded
+    rows = np.random.default_rng(k).choice(c.N, 2048, replace=False)
+    sub = synth.Target("s", t.d_in, t.d_out, t.A, t.B, t.x[rows], t.y0[rows])
+    ref = oracle_from_gpu_routing(sub, c.scale, gi[rows], gw[rows], c.K, k)
+    check_float_output(host(y)[rows], ref, f64(t.y0[rows]))
+
+
+def test_graph_replay_matches_eager():
+    """The vocab step captured in a HIP graph, replayed with eager work in between."""
+    m = need_gpu()
+    c = synth.modality4()
+    t = c.targets[0]
+    hs = make_hotset(m, c.targets, c.scale)
+    ids = dev(c.ids)
+    x, y0 = dev_bf16(t.x), dev_bf16(t.y0)
+    idx = torch.empty(c.N, dtype=torch.int32, device="cuda")
+    w = torch.empty(c.N, dtype=torch.float32, device="cuda")
+    meta = (torch.empty(c.K, dtype=torch.int32, device="cuda"), torch.empty(c.K + 1, dtype=torch.int32, device="cuda"),
+            torch.empty(c.N, dtype=torch.int32, device="cuda"), torch.empty(c.N, dtype=torch.float32, device="cuda"),
+            torch.empty(c.N, dtype=torch.int32, device="cuda"))
+    y = torch.empty(c.N, t.d_out, dtype=torch.bfloat16, device="cuda")
+
+    def step():
+        m.molora_route_vocab(ids, c.bounds.tolist(), idx=idx, w=w)
+        m.molora_dispatch(idx, w, c.K, 1, out=meta)
+        m.molora_apply(hs, x, y0, meta[1], meta[2], meta[3], meta[4], k=1, y=y)
+
+    step()
+    torch.cuda.synchronize()
+    eager = host(y).copy()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(4):
+        y.zero_()
+        meta[2].fill_(-7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(host(y), eager)
+
+
+def test_zero_tokens_is_noop():
+    m = need_gpu()
+    c = synth.tiny_vocab()
+    hs = make_hotset(m, c.targets, c.scale)
+    empty = torch.empty(0, dtype=torch.int32, device="cuda")
+    idx, w = m.molora_route_vocab(empty, c.bounds.tolist())
+    assert idx.numel() == 0
+    x = torch.empty(0, 512, dtype=torch.bfloat16, device="cuda")
+    y = m.molora_apply(hs, x, x.clone(), torch.zeros(5, dtype=torch.int32, device="cuda"), empty, empty.float(),
+                       empty, k=1)
+    assert y.shape == (0, 512)

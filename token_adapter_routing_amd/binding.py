@@ -1,0 +1,290 @@
+"""ctypes binding of libmolora.so with the C entry points' names.
+
+Argument marshalling only: every function checks tensor placement, dtype and contiguity,
+allocates missing outputs with torch (device memory is torch's; the work is the library's),
+passes raw pointers and the current HIP stream, and turns a non-OK status into
+``MoloraError``.  Nothing here computes any part of the routing path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence, Tuple
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmolora.so")
+
+MOLORA_OK, MOLORA_EINVAL, MOLORA_ENOTSUP, MOLORA_ENOSPC, MOLORA_EHIP = range(5)
+LAYOUT_DIRECT, LAYOUT_INDIRECT = 0, 1
+PATH_AUTO, PATH_GROUPED, PATH_SKINNY = 0, 1, 2
+BF16, F32 = 0, 1
+
+_c_p = ctypes.c_void_p
+_c_i = ctypes.c_int
+_c_f = ctypes.c_float
+_c_sz = ctypes.c_size_t
+
+
+class MoloraError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"molora error {code}: {msg}")
+        self.code = code
+
+
+class MoloraTarget(ctypes.Structure):
+    _fields_ = [("d_in", _c_i), ("d_out", _c_i), ("A", _c_p), ("B", _c_p)]
+
+
+_SIGS = {
+    "molora_last_error": (ctypes.c_char_p, []),
+    "molora_hotset_bytes": (_c_i, [_c_i, _c_i, _c_i, ctypes.POINTER(MoloraTarget), _c_i, ctypes.POINTER(_c_sz)]),
+    "molora_hotset_init": (_c_i, [ctypes.POINTER(_c_p), _c_i, _c_i, _c_f, _c_i, ctypes.POINTER(MoloraTarget), _c_i,
+                                  _c_p, _c_sz, _c_p]),
+    "molora_hotset_destroy": (_c_i, [_c_p]),
+    "molora_route_vocab": (_c_i, [_c_p, _c_i, _c_p, _c_i, _c_p, _c_p, _c_p]),
+    "molora_route_topk": (_c_i, [_c_p, _c_i, _c_i, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i, _c_i, _c_p, _c_p, _c_p, _c_p]),
+    "molora_dispatch_workspace": (_c_i, [_c_i, _c_i, _c_i, ctypes.POINTER(_c_sz)]),
+    "molora_dispatch": (_c_i, [_c_p, _c_p, _c_i, _c_i, _c_i, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_sz, _c_p]),
+    "molora_apply_workspace": (_c_i, [_c_p, _c_i, _c_i, _c_i, _c_i, ctypes.POINTER(_c_sz)]),
+    "molora_apply": (_c_i, [_c_p, _c_i, _c_p, _c_p, _c_i, _c_p, _c_i, _c_i, _c_i, _c_p, _c_p, _c_p, _c_p, _c_i,
+                            _c_p, _c_sz, _c_p]),
+    "molora_seqpass_meta": (_c_i, [_c_p, _c_i, _c_i, _c_p, _c_p, _c_p, _c_p]),
+}
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load the HIP library.  Raises if it has not been built: there is no fallback."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with __graft_entry__.build() "
+                          f"(python -m token_adapter_routing_amd.build)")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in _SIGS.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def exported_symbols() -> Sequence[str]:
+    return tuple(_SIGS)
+
+
+def _check(rc: int):
+    if rc != MOLORA_OK:
+        raise MoloraError(rc, load_library().molora_last_error().decode())
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _ptr(t: Optional[torch.Tensor], dtype=None, name: str = "tensor") -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise ValueError(f"unsupported dtype {t.dtype}")
+
+
+# ----------------------------------------------------------------------------------- hot set
+
+class HotSet:
+    """Owns a molora_hotset descriptor and the torch slab it points into."""
+
+    def __init__(self, handle: int, slab: torch.Tensor, K: int, r: int, scale: float, dims, layout: int):
+        self.handle = handle
+        self.slab = slab
+        self.K, self.r, self.scale, self.dims, self.layout = K, r, scale, list(dims), layout
+
+    def close(self):
+        if self.handle:
+            _check(load_library().molora_hotset_destroy(self.handle))
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def _targets(targets) -> Tuple[ctypes.Array, list]:
+    arr = (MoloraTarget * len(targets))()
+    dims = []
+    for i, t in enumerate(targets):
+        A, B = t
+        K, d_in, r = A.shape
+        K2, r2, d_out = B.shape
+        if K2 != K or r2 != r:
+            raise ValueError("A must be [K][d_in][r] and B [K][r][d_out]")
+        arr[i] = MoloraTarget(int(d_in), int(d_out), _ptr(A, torch.bfloat16, "A"), _ptr(B, torch.bfloat16, "B"))
+        dims.append((int(d_in), int(d_out)))
+    return arr, dims
+
+
+def molora_hotset_bytes(K: int, r: int, dims, layout: int = LAYOUT_DIRECT) -> int:
+    arr = (MoloraTarget * len(dims))()
+    for i, (d_in, d_out) in enumerate(dims):
+        arr[i] = MoloraTarget(int(d_in), int(d_out), None, None)
+    out = _c_sz()
+    _check(load_library().molora_hotset_bytes(K, r, len(dims), arr, layout, ctypes.byref(out)))
+    return out.value
+
+
+def molora_hotset_init(targets, scale: float, layout: int = LAYOUT_DIRECT, slab: Optional[torch.Tensor] = None,
+                       stream=None) -> HotSet:
+    """targets: list of (A [K][d_in][r] bf16, B [K][r][d_out] bf16) device tensors."""
+    lib = load_library()
+    arr, dims = _targets(targets)
+    K, _, r = targets[0][0].shape
+    nbytes = molora_hotset_bytes(int(K), int(r), dims, layout)
+    if slab is None:
+        slab = torch.empty(nbytes, dtype=torch.uint8, device=targets[0][0].device)
+    h = _c_p()
+    _check(lib.molora_hotset_init(ctypes.byref(h), int(K), int(r), float(scale), len(dims), arr, layout,
+                                  _ptr(slab, torch.uint8, "slab"), slab.numel(), _stream(stream)))
+    return HotSet(h.value, slab, int(K), int(r), float(scale), dims, layout)
+
+
+def molora_hotset_destroy(hs: HotSet):
+    hs.close()
+
+
+# ----------------------------------------------------------------------------------- routing
+
+def molora_route_vocab(ids: torch.Tensor, bounds: Sequence[int], idx: Optional[torch.Tensor] = None,
+                       w: Optional[torch.Tensor] = None, stream=None):
+    N = ids.numel()
+    K = len(bounds) - 1
+    if idx is None:
+        idx = torch.empty(N, dtype=torch.int32, device=ids.device)
+    if w is None:
+        w = torch.empty(N, dtype=torch.float32, device=ids.device)
+    b = (ctypes.c_int32 * len(bounds))(*[int(v) for v in bounds])
+    _check(load_library().molora_route_vocab(_ptr(ids, torch.int32, "ids"), N, ctypes.cast(b, _c_p), K,
+                                             _ptr(idx, torch.int32, "idx"), _ptr(w, torch.float32, "w"),
+                                             _stream(stream)))
+    return idx, w
+
+
+def molora_route_topk(k: int, K: int, x: Optional[torch.Tensor] = None, W1: Optional[torch.Tensor] = None,
+                      b1: Optional[torch.Tensor] = None, W2: Optional[torch.Tensor] = None,
+                      b2: Optional[torch.Tensor] = None, logits: Optional[torch.Tensor] = None,
+                      idx: Optional[torch.Tensor] = None, w: Optional[torch.Tensor] = None,
+                      flags: Optional[torch.Tensor] = None, want_flags: bool = True, stream=None):
+    """Router mode when W1 is given (W1 [64][d], W2 [K][64], nn.Linear layout), else logits mode."""
+    router = W1 is not None
+    if router:
+        N, d = x.shape
+        dev = x.device
+    else:
+        N = logits.shape[0]
+        d = 0
+        dev = logits.device
+    if logits is None:
+        logits = torch.empty(N, K, dtype=torch.float32, device=dev)
+    if idx is None:
+        idx = torch.empty(N, k, dtype=torch.int32, device=dev)
+    if w is None:
+        w = torch.empty(N, k, dtype=torch.float32, device=dev)
+    if flags is None and want_flags:
+        flags = torch.empty(N, dtype=torch.uint8, device=dev)
+    _check(load_library().molora_route_topk(
+        _ptr(x, torch.bfloat16, "x") if router else None, N, d,
+        _ptr(W1, torch.bfloat16, "W1") if router else None, _ptr(b1, torch.float32, "b1") if router else None,
+        _ptr(W2, torch.bfloat16, "W2") if router else None, _ptr(b2, torch.float32, "b2") if router else None,
+        _ptr(logits, torch.float32, "logits"), K, k, _ptr(idx, torch.int32, "idx"), _ptr(w, torch.float32, "w"),
+        _ptr(flags, torch.uint8, "flags"), _stream(stream)))
+    return logits, idx, w, flags
+
+
+# ----------------------------------------------------------------------------------- dispatch
+
+def molora_dispatch_workspace(N: int, k: int, K: int) -> int:
+    out = _c_sz()
+    _check(load_library().molora_dispatch_workspace(N, k, K, ctypes.byref(out)))
+    return out.value
+
+
+def molora_dispatch(idx: torch.Tensor, w: torch.Tensor, K: int, k: int = 1, out=None, ws=None, stream=None):
+    """Returns (counts, offsets, perm, perm_w, inv); ``out`` may supply those five tensors."""
+    P = idx.numel()
+    N = P // k
+    dev = idx.device
+    if out is None:
+        out = (torch.empty(K, dtype=torch.int32, device=dev), torch.empty(K + 1, dtype=torch.int32, device=dev),
+               torch.empty(max(P, 1), dtype=torch.int32, device=dev), torch.empty(max(P, 1), dtype=torch.float32, device=dev),
+               torch.empty(max(P, 1), dtype=torch.int32, device=dev))
+    counts, offsets, perm, perm_w, inv = out
+    nws = molora_dispatch_workspace(N, k, K)
+    if nws and ws is None:
+        ws = torch.empty(nws, dtype=torch.uint8, device=dev)
+    _check(load_library().molora_dispatch(
+        _ptr(idx, torch.int32, "idx"), _ptr(w, torch.float32, "w"), N, k, K, _ptr(counts, torch.int32, "counts"),
+        _ptr(offsets, torch.int32, "offsets"), _ptr(perm, torch.int32, "perm"), _ptr(perm_w, torch.float32, "perm_w"),
+        _ptr(inv, torch.int32, "inv"), _ptr(ws, None, "ws") if ws is not None else None,
+        ws.numel() if ws is not None else 0, _stream(stream)))
+    return counts, offsets, perm, perm_w, inv
+
+
+# ----------------------------------------------------------------------------------- apply
+
+def molora_apply_workspace(hs: HotSet, target: int, N: int, k: int, path: int = PATH_AUTO) -> int:
+    out = _c_sz()
+    _check(load_library().molora_apply_workspace(hs.handle, target, N, k, path, ctypes.byref(out)))
+    return out.value
+
+
+def molora_apply(hs: HotSet, x: torch.Tensor, y0: torch.Tensor, offsets: torch.Tensor, perm: torch.Tensor,
+                 perm_w: torch.Tensor, inv: torch.Tensor, k: int = 1, target: int = 0, y: Optional[torch.Tensor] = None,
+                 y_dtype=None, path: int = PATH_AUTO, ws: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    N = x.shape[0]
+    d_out = hs.dims[target][1]
+    if y is None:
+        y = torch.empty(N, d_out, dtype=y_dtype or y0.dtype, device=x.device)
+    need = molora_apply_workspace(hs, target, N, k, path)
+    if need and (ws is None or ws.numel() < need):
+        ws = torch.empty(need, dtype=torch.uint8, device=x.device)
+    _check(load_library().molora_apply(
+        hs.handle, target, _ptr(x, torch.bfloat16, "x"), _ptr(y0, None, "y0"), _dtype_code(y0), _ptr(y, None, "y"),
+        _dtype_code(y), N, k, _ptr(offsets, torch.int32, "offsets"), _ptr(perm, torch.int32, "perm"),
+        _ptr(perm_w, torch.float32, "perm_w"), _ptr(inv, torch.int32, "inv"), path,
+        _ptr(ws, None, "ws") if ws is not None else None, ws.numel() if ws is not None else 0, _stream(stream)))
+    return y
+
+
+def molora_seqpass_meta(idx: torch.Tensor, K: int, stream=None):
+    """Returns (offsets [K][K+1], perm [N], perm_w [K][N]) for K one-hot passes."""
+    N = idx.numel()
+    dev = idx.device
+    offsets = torch.empty(K, K + 1, dtype=torch.int32, device=dev)
+    perm = torch.empty(max(N, 1), dtype=torch.int32, device=dev)
+    perm_w = torch.empty(K, max(N, 1), dtype=torch.float32, device=dev)
+    _check(load_library().molora_seqpass_meta(_ptr(idx, torch.int32, "idx"), N, K, _ptr(offsets, torch.int32, "offsets"),
+                                              _ptr(perm, torch.int32, "perm"), _ptr(perm_w, torch.float32, "perm_w"),
+                                              _stream(stream)))
+    return offsets, perm, perm_w

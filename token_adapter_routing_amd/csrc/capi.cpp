@@ -1,0 +1,339 @@
+// C-ABI entry points: argument validation on the host, hot-set slab layout, launches.
+// Every check that can be made without reading device memory is made here, before anything
+// is enqueued; kernels then assume valid shapes.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "../../include/molora.h"
+#include "molora_launch.h"
+
+struct molora_hotset {
+  int K = 0, r = 0, r_pad = 0, layout = 0, n_targets = 0;
+  float scale = 1.f;
+  std::vector<molora::TargetDev> tg;
+  void* slab = nullptr;
+  size_t slab_bytes = 0;
+};
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int ok() {
+  g_err.clear();
+  return MOLORA_OK;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(MOLORA_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+int rank_pad(int r) { return (r + 15) / 16 * 16; }
+
+// Slot of adapter e in the indirect layout: a fixed permutation of [0, K) so that adapter
+// addresses are not an affine function of e.
+int indirect_slot(int e, int K) {
+  const int mult = (K % 37 == 0) ? 41 : 37;
+  return (int)(((long long)e * mult + 11) % K);
+}
+
+struct SlabPlan {
+  struct T {
+    size_t offA, offB, offPA, offPB, sizeA, sizeB;
+  };
+  std::vector<T> t;
+  size_t total = 0;
+};
+
+int check_targets(int K, int r, int n_targets, const molora_target* targets, bool need_ptrs) {
+  if (K < 1 || K > MOLORA_MAX_ADAPTERS) return fail(MOLORA_ENOTSUP, "K=%d outside [1, %d]", K, MOLORA_MAX_ADAPTERS);
+  if (r < 1 || r > MOLORA_MAX_RANK) return fail(MOLORA_ENOTSUP, "r=%d outside [1, %d]", r, MOLORA_MAX_RANK);
+  if (n_targets < 1 || n_targets > 16) return fail(MOLORA_EINVAL, "n_targets=%d outside [1, 16]", n_targets);
+  if (targets == nullptr) return fail(MOLORA_EINVAL, "targets is NULL");
+  for (int t = 0; t < n_targets; ++t) {
+    const molora_target& g = targets[t];
+    if (g.d_in <= 0 || g.d_out <= 0 || g.d_in % 128 != 0 || g.d_out % 128 != 0)
+      return fail(MOLORA_ENOTSUP, "target %d: d_in=%d d_out=%d must be positive multiples of 128", t, g.d_in,
+                  g.d_out);
+    if (need_ptrs) {
+      if (g.A == nullptr || g.B == nullptr) return fail(MOLORA_EINVAL, "target %d: A or B is NULL", t);
+      if (!aligned(g.A, 2) || !aligned(g.B, 2)) return fail(MOLORA_EINVAL, "target %d: A or B misaligned", t);
+    }
+  }
+  return MOLORA_OK;
+}
+
+SlabPlan plan_slab(int K, int r, int n_targets, const molora_target* targets, int layout) {
+  SlabPlan p;
+  const int rp = rank_pad(r);
+  size_t cur = 0;
+  for (int t = 0; t < n_targets; ++t) {
+    SlabPlan::T s{};
+    s.sizeA = align_up((size_t)rp * targets[t].d_in * 2, 256);
+    s.sizeB = align_up((size_t)targets[t].d_out * rp * 2, 256);
+    s.offA = cur;
+    cur += (size_t)K * s.sizeA;
+    s.offB = cur;
+    cur += (size_t)K * s.sizeB;
+    if (layout == MOLORA_LAYOUT_INDIRECT) {
+      s.offPA = cur;
+      cur = align_up(cur + (size_t)K * sizeof(void*), 256);
+      s.offPB = cur;
+      cur = align_up(cur + (size_t)K * sizeof(void*), 256);
+    }
+    p.t.push_back(s);
+  }
+  p.total = cur;
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* molora_last_error(void) { return g_err.c_str(); }
+
+int molora_hotset_bytes(int K, int r, int n_targets, const molora_target* targets, int layout, size_t* bytes) {
+  if (bytes == nullptr) return fail(MOLORA_EINVAL, "bytes is NULL");
+  if (layout != MOLORA_LAYOUT_DIRECT && layout != MOLORA_LAYOUT_INDIRECT)
+    return fail(MOLORA_EINVAL, "unknown layout %d", layout);
+  const int rc = check_targets(K, r, n_targets, targets, false);
+  if (rc != MOLORA_OK) return rc;
+  *bytes = plan_slab(K, r, n_targets, targets, layout).total;
+  return ok();
+}
+
+int molora_hotset_init(molora_hotset** out, int K, int r, float scale, int n_targets, const molora_target* targets,
+                       int layout, void* slab, size_t slab_bytes, void* stream) {
+  if (out == nullptr) return fail(MOLORA_EINVAL, "out is NULL");
+  *out = nullptr;
+  if (layout != MOLORA_LAYOUT_DIRECT && layout != MOLORA_LAYOUT_INDIRECT)
+    return fail(MOLORA_EINVAL, "unknown layout %d", layout);
+  int rc = check_targets(K, r, n_targets, targets, true);
+  if (rc != MOLORA_OK) return rc;
+  if (slab == nullptr || !aligned(slab, 256)) return fail(MOLORA_EINVAL, "slab is NULL or not 256-byte aligned");
+  const SlabPlan plan = plan_slab(K, r, n_targets, targets, layout);
+  if (slab_bytes < plan.total)
+    return fail(MOLORA_ENOSPC, "slab holds %zu bytes, %zu needed", slab_bytes, plan.total);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  molora_hotset* hs = new (std::nothrow) molora_hotset;
+  if (hs == nullptr) return fail(MOLORA_EINVAL, "out of host memory");
+  hs->K = K;
+  hs->r = r;
+  hs->r_pad = rank_pad(r);
+  hs->layout = layout;
+  hs->n_targets = n_targets;
+  hs->scale = scale;
+  hs->slab = slab;
+  hs->slab_bytes = slab_bytes;
+  char* base = reinterpret_cast<char*>(slab);
+  std::vector<std::vector<const void*>> tablesA(n_targets), tablesB(n_targets);
+  for (int t = 0; t < n_targets; ++t) {
+    const molora_target& g = targets[t];
+    const SlabPlan::T& p = plan.t[t];
+    molora::TargetDev d{};
+    d.d_in = g.d_in;
+    d.d_out = g.d_out;
+    d.r_pad = hs->r_pad;
+    for (int e = 0; e < K; ++e) {
+      const int slot = (layout == MOLORA_LAYOUT_DIRECT) ? e : indirect_slot(e, K);
+      uint16_t* At = reinterpret_cast<uint16_t*>(base + p.offA + (size_t)slot * p.sizeA);
+      uint16_t* Bt = reinterpret_cast<uint16_t*>(base + p.offB + (size_t)slot * p.sizeB);
+      const uint16_t* A = reinterpret_cast<const uint16_t*>(g.A) + (size_t)e * g.d_in * r;
+      const uint16_t* B = reinterpret_cast<const uint16_t*>(g.B) + (size_t)e * r * g.d_out;
+      hipError_t err = molora::launch_relayout(A, B, g.d_in, g.d_out, r, hs->r_pad, At, Bt, s);
+      if (err != hipSuccess) {
+        delete hs;
+        return hip_fail(err, "hot-set relayout");
+      }
+      tablesA[t].push_back(At);
+      tablesB[t].push_back(Bt);
+    }
+    if (layout == MOLORA_LAYOUT_DIRECT) {
+      d.At = reinterpret_cast<const uint16_t*>(base + p.offA);
+      d.Bt = reinterpret_cast<const uint16_t*>(base + p.offB);
+      d.strideA = (long long)(p.sizeA / 2);
+      d.strideB = (long long)(p.sizeB / 2);
+    } else {
+      d.ptrA = reinterpret_cast<const uint16_t* const*>(base + p.offPA);
+      d.ptrB = reinterpret_cast<const uint16_t* const*>(base + p.offPB);
+      hipError_t err = hipMemcpyAsync(base + p.offPA, tablesA[t].data(), (size_t)K * sizeof(void*),
+                                      hipMemcpyHostToDevice, s);
+      if (err == hipSuccess)
+        err = hipMemcpyAsync(base + p.offPB, tablesB[t].data(), (size_t)K * sizeof(void*), hipMemcpyHostToDevice, s);
+      if (err != hipSuccess) {
+        delete hs;
+        return hip_fail(err, "pointer tables");
+      }
+    }
+    hs->tg.push_back(d);
+  }
+  const hipError_t err = hipStreamSynchronize(s);  // host tables above must outlive the copies
+  if (err != hipSuccess) {
+    delete hs;
+    return hip_fail(err, "hot-set init");
+  }
+  *out = hs;
+  return ok();
+}
+
+int molora_hotset_destroy(molora_hotset* hs) {
+  delete hs;
+  return ok();
+}
+
+int molora_route_vocab(const int32_t* ids, int N, const int32_t* bounds, int K, int32_t* idx, float* w,
+                       void* stream) {
+  if (N < 0) return fail(MOLORA_EINVAL, "N=%d < 0", N);
+  if (K < 1 || K > MOLORA_MAX_ADAPTERS) return fail(MOLORA_ENOTSUP, "K=%d outside [1, %d]", K, MOLORA_MAX_ADAPTERS);
+  if (bounds == nullptr) return fail(MOLORA_EINVAL, "bounds is NULL");
+  molora::VocabBounds vb{};
+  for (int e = 0; e <= K; ++e) {
+    vb.b[e] = bounds[e];
+    if (e > 0 && bounds[e] < bounds[e - 1]) return fail(MOLORA_EINVAL, "bounds must be non-decreasing");
+  }
+  if (N == 0) return ok();
+  if (ids == nullptr || idx == nullptr || w == nullptr) return fail(MOLORA_EINVAL, "ids, idx or w is NULL");
+  if (!aligned(ids, 4) || !aligned(idx, 4) || !aligned(w, 4)) return fail(MOLORA_EINVAL, "misaligned pointer");
+  const hipError_t e = molora::launch_route_vocab(ids, N, vb, K, idx, w, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ok() : hip_fail(e, "route_vocab launch");
+}
+
+int molora_route_topk(const void* x, int N, int d, const void* W1, const float* b1, const void* W2, const float* b2,
+                      float* logits, int K, int k, int32_t* idx, float* w, uint8_t* flags, void* stream) {
+  if (N < 0) return fail(MOLORA_EINVAL, "N=%d < 0", N);
+  if (K < 1 || K > MOLORA_MAX_ADAPTERS) return fail(MOLORA_ENOTSUP, "K=%d outside [1, %d]", K, MOLORA_MAX_ADAPTERS);
+  if (k < 1 || k > K || k > MOLORA_MAX_TOPK) return fail(MOLORA_ENOTSUP, "k=%d outside [1, min(K, %d)]", k, MOLORA_MAX_TOPK);
+  if (W1 != nullptr) {
+    if (d <= 0 || d % 128 != 0) return fail(MOLORA_ENOTSUP, "router mode needs d a positive multiple of 128 (d=%d)", d);
+    if (W2 == nullptr) return fail(MOLORA_EINVAL, "router mode needs W2");
+    if (N > 0 && x == nullptr) return fail(MOLORA_EINVAL, "router mode needs x");
+    if (!aligned(W1, 16) || !aligned(W2, 16) || (x != nullptr && !aligned(x, 16)))
+      return fail(MOLORA_EINVAL, "x, W1 and W2 must be 16-byte aligned");
+    if ((b1 != nullptr && !aligned(b1, 4)) || (b2 != nullptr && !aligned(b2, 4)))
+      return fail(MOLORA_EINVAL, "misaligned bias");
+  }
+  if (N == 0) return ok();
+  if (logits == nullptr || idx == nullptr || w == nullptr) return fail(MOLORA_EINVAL, "logits, idx or w is NULL");
+  if (!aligned(logits, 4) || !aligned(idx, 4) || !aligned(w, 4)) return fail(MOLORA_EINVAL, "misaligned pointer");
+  const hipError_t e = molora::launch_route_topk(
+      reinterpret_cast<const uint16_t*>(x), N, d, reinterpret_cast<const uint16_t*>(W1), b1,
+      reinterpret_cast<const uint16_t*>(W2), b2, logits, K, k, idx, w, flags, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ok() : hip_fail(e, "route_topk launch");
+}
+
+int molora_dispatch_workspace(int N, int k, int K, size_t* bytes) {
+  if (bytes == nullptr) return fail(MOLORA_EINVAL, "bytes is NULL");
+  if (N < 0 || k < 1 || k > MOLORA_MAX_TOPK) return fail(MOLORA_EINVAL, "bad N=%d or k=%d", N, k);
+  if (K < 1 || K > MOLORA_MAX_ADAPTERS) return fail(MOLORA_ENOTSUP, "K=%d outside [1, %d]", K, MOLORA_MAX_ADAPTERS);
+  *bytes = 0;
+  return ok();
+}
+
+int molora_dispatch(const int32_t* idx, const float* w, int N, int k, int K, int32_t* counts, int32_t* offsets,
+                    int32_t* perm, float* perm_w, int32_t* inv, void* ws, size_t ws_bytes, void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  if (N < 0) return fail(MOLORA_EINVAL, "N=%d < 0", N);
+  if (k < 1 || k > MOLORA_MAX_TOPK) return fail(MOLORA_ENOTSUP, "k=%d outside [1, %d]", k, MOLORA_MAX_TOPK);
+  if (K < 1 || K > MOLORA_MAX_ADAPTERS) return fail(MOLORA_ENOTSUP, "K=%d outside [1, %d]", K, MOLORA_MAX_ADAPTERS);
+  if ((long long)N * k >= (1ll << 31)) return fail(MOLORA_ENOTSUP, "N*k too large");
+  if (N == 0) return ok();
+  if (idx == nullptr || w == nullptr || counts == nullptr || offsets == nullptr || perm == nullptr || perm_w == nullptr)
+    return fail(MOLORA_EINVAL, "a required pointer is NULL");
+  if (!aligned(idx, 4) || !aligned(w, 4) || !aligned(counts, 4) || !aligned(offsets, 4) || !aligned(perm, 4) ||
+      !aligned(perm_w, 4) || (inv != nullptr && !aligned(inv, 4)))
+    return fail(MOLORA_EINVAL, "misaligned pointer");
+  const hipError_t e = molora::launch_dispatch(idx, w, N * k, K, counts, offsets, perm, perm_w, inv,
+                                               reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ok() : hip_fail(e, "dispatch launch");
+}
+
+int molora_apply_workspace(const molora_hotset* hs, int target, int N, int k, int path, size_t* bytes) {
+  if (bytes == nullptr) return fail(MOLORA_EINVAL, "bytes is NULL");
+  if (hs == nullptr) return fail(MOLORA_EINVAL, "hot set is NULL");
+  if (target < 0 || target >= hs->n_targets) return fail(MOLORA_EINVAL, "target %d outside [0, %d)", target, hs->n_targets);
+  if (N < 0 || k < 1 || k > MOLORA_MAX_TOPK || k > hs->K) return fail(MOLORA_EINVAL, "bad N=%d or k=%d", N, k);
+  if (path < MOLORA_PATH_AUTO || path > MOLORA_PATH_SKINNY) return fail(MOLORA_EINVAL, "unknown path %d", path);
+  *bytes = molora::apply_ws_bytes(N, k, hs->r_pad, hs->tg[target].d_in, path);
+  return ok();
+}
+
+int molora_apply(const molora_hotset* hs, int target, const void* x, const void* y0, int y0_dtype, void* y, int y_dtype,
+                 int N, int k, const int32_t* offsets, const int32_t* perm, const float* perm_w, const int32_t* inv,
+                 int path, void* ws, size_t ws_bytes, void* stream) {
+  if (hs == nullptr) return fail(MOLORA_EINVAL, "hot set is NULL");
+  if (target < 0 || target >= hs->n_targets) return fail(MOLORA_EINVAL, "target %d outside [0, %d)", target, hs->n_targets);
+  if (N < 0) return fail(MOLORA_EINVAL, "N=%d < 0", N);
+  if (k < 1 || k > MOLORA_MAX_TOPK || k > hs->K) return fail(MOLORA_ENOTSUP, "k=%d outside [1, min(K, %d)]", k, MOLORA_MAX_TOPK);
+  if ((long long)N * k >= (1ll << 31)) return fail(MOLORA_ENOTSUP, "N*k too large");
+  if ((y0_dtype != MOLORA_BF16 && y0_dtype != MOLORA_F32) || (y_dtype != MOLORA_BF16 && y_dtype != MOLORA_F32))
+    return fail(MOLORA_EINVAL, "unknown dtype");
+  if (path < MOLORA_PATH_AUTO || path > MOLORA_PATH_SKINNY) return fail(MOLORA_EINVAL, "unknown path %d", path);
+  if (y0 == y && y0_dtype != y_dtype) return fail(MOLORA_EINVAL, "in-place apply needs y0_dtype == y_dtype");
+  if (N == 0) return ok();
+  if (x == nullptr || y0 == nullptr || y == nullptr) return fail(MOLORA_EINVAL, "x, y0 or y is NULL");
+  if (!aligned(x, 16) || !aligned(y0, 16) || !aligned(y, 16)) return fail(MOLORA_EINVAL, "x, y0 and y must be 16-byte aligned");
+  if (offsets == nullptr || perm == nullptr || perm_w == nullptr || inv == nullptr)
+    return fail(MOLORA_EINVAL, "offsets, perm, perm_w and inv are required");
+  if (!aligned(offsets, 4) || !aligned(perm, 4) || !aligned(perm_w, 4) || !aligned(inv, 4))
+    return fail(MOLORA_EINVAL, "misaligned pointer");
+  const molora::TargetDev& tg = hs->tg[target];
+  const size_t need = molora::apply_ws_bytes(N, k, hs->r_pad, tg.d_in, path);
+  if (need > 0 && (ws == nullptr || ws_bytes < need || !aligned(ws, 16)))
+    return fail(MOLORA_ENOSPC, "workspace of %zu bytes (16-byte aligned) needed, %zu given", need, ws_bytes);
+  molora::ApplyLaunch a{};
+  a.tgt = tg;
+  a.indirect = hs->layout == MOLORA_LAYOUT_INDIRECT;
+  a.x = reinterpret_cast<const uint16_t*>(x);
+  a.y0 = y0;
+  a.y = y;
+  a.y0_f32 = y0_dtype == MOLORA_F32;
+  a.y_f32 = y_dtype == MOLORA_F32;
+  a.N = N;
+  a.k = k;
+  a.K = hs->K;
+  a.scale = hs->scale;
+  a.offsets = offsets;
+  a.perm = perm;
+  a.perm_w = perm_w;
+  a.inv = inv;
+  a.path = molora::apply_resolve_path(N, k, path);
+  a.ws = reinterpret_cast<float*>(ws);
+  a.col_groups = 0;
+  const hipError_t e = molora::launch_apply(a, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ok() : hip_fail(e, "apply launch");
+}
+
+int molora_seqpass_meta(const int32_t* idx, int N, int K, int32_t* offsets, int32_t* perm, float* perm_w, void* stream) {
+  if (N < 0) return fail(MOLORA_EINVAL, "N=%d < 0", N);
+  if (K < 1 || K > MOLORA_MAX_ADAPTERS) return fail(MOLORA_ENOTSUP, "K=%d outside [1, %d]", K, MOLORA_MAX_ADAPTERS);
+  if (N == 0) return ok();
+  if (idx == nullptr || offsets == nullptr || perm == nullptr || perm_w == nullptr)
+    return fail(MOLORA_EINVAL, "a required pointer is NULL");
+  const hipError_t e =
+      molora::launch_seqpass_meta(idx, N, K, offsets, perm, perm_w, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ok() : hip_fail(e, "seqpass_meta launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,56 @@
+// Host-side launchers of the gfx950 kernels (internal to the library).  Every launcher
+// assumes its arguments were validated by the C-ABI layer and only enqueues work.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "molora_dev.h"
+
+namespace molora {
+
+struct VocabBounds {
+  int b[65];
+};
+
+hipError_t launch_route_vocab(const int32_t* ids, int N, const VocabBounds& bounds, int K,
+                              int32_t* idx, float* w, hipStream_t s);
+
+hipError_t launch_route_topk(const uint16_t* x, int N, int d, const uint16_t* W1, const float* b1,
+                             const uint16_t* W2, const float* b2, float* logits, int K, int k,
+                             int32_t* idx, float* w, uint8_t* flags, hipStream_t s);
+
+hipError_t launch_dispatch(const int32_t* idx, const float* w, int P, int K, int32_t* counts,
+                           int32_t* offsets, int32_t* perm, float* perm_w, int32_t* inv,
+                           hipStream_t s);
+
+hipError_t launch_relayout(const uint16_t* A, const uint16_t* B, int d_in, int d_out, int r,
+                           int r_pad, uint16_t* At, uint16_t* Bt, hipStream_t s);
+
+struct ApplyLaunch {
+  TargetDev tgt;
+  bool indirect;
+  const uint16_t* x;
+  const void* y0;
+  void* y;
+  int y0_f32, y_f32;
+  int N, k, K;
+  float scale;
+  const int32_t* offsets;
+  const int32_t* perm;
+  const float* perm_w;
+  const int32_t* inv;
+  int path;          // resolved path (GROUPED or SKINNY)
+  float* ws;         // fp32 workspace (partials of the shrink)
+  int col_groups;    // 0 = choose
+};
+
+// Workspace bytes a resolved apply needs.
+size_t apply_ws_bytes(int N, int k, int r_pad, int d_in, int path);
+int apply_resolve_path(int N, int k, int path);
+hipError_t launch_apply(const ApplyLaunch& a, hipStream_t s);
+
+hipError_t launch_seqpass_meta(const int32_t* idx, int N, int K, int32_t* offsets, int32_t* perm,
+                               float* perm_w, hipStream_t s);
+
+}  // namespace molora

@@ -1,0 +1,154 @@
+// Routing decisions on gfx950 (MoLoRA pages, thelatestinai.com, Table 1 "Routing decision":
+// the vocabulary range function R_vocab(v), cost O(1), or TopK over a learned gate
+// g_theta(x), cost O(64d + 64K); Figure 2: the k selected adapters are combined by a
+// weighted sum, here the softmax over the selected logits).
+//
+//   route_vocab_k   one thread per token: binary search of the id in the K+1 range bounds.
+//   route_topk_k    a workgroup owns 16 tokens.  Router mode: the first layer x W1^T (d -> 64)
+//                   is an MFMA product with the same gather/shrink core as the LoRA shrink,
+//                   the 4 waves splitting d and meeting in LDS; bias and ReLU follow in LDS;
+//                   the second layer (64 -> K) runs on the VALU with one lane per adapter.
+//                   Selection: one wave per token holds the K logits in its lanes; k rounds of
+//                   (wave max, ballot of lanes equal to it, lowest lane wins) pick the top-k
+//                   with ties to the lower adapter index; one more round gives the (k+1)-th
+//                   value for the near-tie flag, whose margin is taken in fp64.
+#include <cmath>
+
+#include "molora_launch.h"
+#include "molora_mfma.h"
+
+namespace molora {
+
+__global__ __launch_bounds__(256) void route_vocab_k(const int32_t* __restrict__ ids, int N, VocabBounds b,
+                                                     int K, int32_t* __restrict__ idx, float* __restrict__ w) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= N) return;
+  const int v = ids[i];
+  int e = -1;
+  if (v >= b.b[0] && v < b.b[K]) {
+    int lo = 0, hi = K;  // b[lo] <= v < b[hi]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (b.b[mid] <= v) lo = mid;
+      else hi = mid;
+    }
+    e = lo;
+  }
+  idx[i] = e;
+  w[i] = (e >= 0) ? 1.0f : 0.0f;
+}
+
+hipError_t launch_route_vocab(const int32_t* ids, int N, const VocabBounds& bounds, int K, int32_t* idx,
+                              float* w, hipStream_t s) {
+  hipLaunchKernelGGL(route_vocab_k, dim3((N + 255) / 256), dim3(256), 0, s, ids, N, bounds, K, idx, w);
+  return hipGetLastError();
+}
+
+// Top-k of one token whose logit for adapter `lane` is `l` (lanes >= K hold nothing).
+__device__ __forceinline__ void topk_one_token(float l, int K, int k, int lane, int32_t* __restrict__ idx_row,
+                                               float* __restrict__ w_row, uint8_t* flag) {
+  const bool mine = lane < K;
+  uint64_t taken = 0;
+  float vmax = 0.f, kth = 0.f;
+  for (int s = 0; s < k; ++s) {
+    const bool avail = mine && !((taken >> lane) & 1ull);
+    const float m = wave_max(avail ? l : -INFINITY);
+    uint64_t bm = __ballot(avail && l == m);
+    if (bm == 0) bm = __ballot(avail);  // only reachable with non-finite logits
+    taken |= 1ull << __builtin_ctzll(bm);
+    if (s == 0) vmax = m;
+    kth = m;
+  }
+  bool near_tie = false;
+  if (k < K) {
+    const bool avail = mine && !((taken >> lane) & 1ull);
+    const float m2 = wave_max(avail ? l : -INFINITY);
+    near_tie = ((double)kth - (double)m2) < 1e-4;
+  }
+  const bool sel = (taken >> lane) & 1ull;
+  const float ex = sel ? expf(l - vmax) : 0.f;
+  const float sum = wave_sum(ex);
+  if (sel) {
+    const int slot = __popcll(taken & lanemask_lt(lane));
+    idx_row[slot] = lane;
+    w_row[slot] = ex / sum;
+  }
+  if (flag != nullptr && lane == 0) *flag = near_tie ? 1 : 0;
+}
+
+struct TopkArgs {
+  const uint16_t* x;
+  int N, d;
+  const uint16_t* W1;  // [64][d]
+  const float* b1;
+  const uint16_t* W2;  // [K][64]
+  const float* b2;
+  float* logits;
+  int K, k;
+  int32_t* idx;
+  float* w;
+  uint8_t* flags;
+};
+
+template <bool ROUTER>
+__global__ __launch_bounds__(256) void route_topk_k(TopkArgs a) {
+  constexpr int RB = 4;  // 64 hidden units = 4 blocks of 16
+  constexpr int RS = RedLds<RB>::RS;
+  __shared__ float red[ROUTER ? RedLds<RB>::kFloats : 1];
+  __shared__ float hid[ROUTER ? 16 * 64 : 1];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t0 = blockIdx.x * 16;
+  if constexpr (ROUTER) {
+    const int n = lane & 15;
+    const int tok = min(t0 + n, a.N - 1);
+    f32x4_t acc[RB];
+#pragma unroll
+    for (int u = 0; u < RB; ++u) acc[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    const int S = a.d / kStepK;
+    shrink_steps<RB>(acc, a.x + (size_t)tok * a.d, a.W1, a.d, (S * wave) / 4, (S * (wave + 1)) / 4, lane);
+    shrink_to_lds<RB>(acc, red, wave, lane);
+    __syncthreads();
+    for (int i = threadIdx.x; i < 16 * 64; i += 256) {
+      const int row = i >> 6, j = i & 63;
+      float v = 0.f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) v += red[(w * 16 + row) * RS + j];
+      if (a.b1 != nullptr) v += a.b1[j];
+      hid[i] = v > 0.f ? v : 0.f;
+    }
+    __syncthreads();
+  }
+  for (int r = 0; r < 4; ++r) {
+    const int row = wave * 4 + r;
+    const int tok = t0 + row;
+    if (tok >= a.N) break;  // uniform per wave
+    float l = -INFINITY;
+    if constexpr (ROUTER) {
+      if (lane < a.K) {
+        const uint16_t* w2 = a.W2 + (size_t)lane * 64;
+        float s = 0.f;
+#pragma unroll 8
+        for (int j = 0; j < 64; ++j) s = fmaf(hid[row * 64 + j], bf16_to_f32(w2[j]), s);
+        if (a.b2 != nullptr) s += a.b2[lane];
+        l = s;
+        a.logits[(size_t)tok * a.K + lane] = l;
+      }
+    } else {
+      if (lane < a.K) l = a.logits[(size_t)tok * a.K + lane];
+    }
+    topk_one_token(l, a.K, a.k, lane, a.idx + (size_t)tok * a.k, a.w + (size_t)tok * a.k,
+                   a.flags ? a.flags + tok : nullptr);
+  }
+}
+
+hipError_t launch_route_topk(const uint16_t* x, int N, int d, const uint16_t* W1, const float* b1,
+                             const uint16_t* W2, const float* b2, float* logits, int K, int k, int32_t* idx,
+                             float* w, uint8_t* flags, hipStream_t s) {
+  TopkArgs a{x, N, d, W1, b1, W2, b2, logits, K, k, idx, w, flags};
+  const dim3 grid((N + 15) / 16);
+  if (W1 != nullptr) hipLaunchKernelGGL(route_topk_k<true>, grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL(route_topk_k<false>, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace molora
