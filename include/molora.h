@@ -53,7 +53,7 @@ enum {
 };
 
 enum { MOLORA_LAYOUT_DIRECT = 0, MOLORA_LAYOUT_INDIRECT = 1 };
-enum { MOLORA_PATH_AUTO = 0, MOLORA_PATH_GROUPED = 1, MOLORA_PATH_SKINNY = 2 };
+enum { MOLORA_PATH_AUTO = 0, MOLORA_PATH_GROUPED = 1, MOLORA_PATH_SKINNY = 2, MOLORA_PATH_TILE = 3 };
 enum { MOLORA_BF16 = 0, MOLORA_F32 = 1 };
 
 /* Limits of this build. */
@@ -194,8 +194,11 @@ int molora_dispatch(const int32_t *idx, const float *w, int N, int k, int K,
  *   y       device [N][d_out] out, dtype y_dtype
  *   offsets, perm, perm_w, inv: the outputs of molora_dispatch for this
  *           routing (inv is required when k > 1, ignored when k == 1)
- *   path    MOLORA_PATH_AUTO (chosen on the host from N*k), _GROUPED (MFMA
- *           tiles) or _SKINNY (per-pair dot products, for small batches)
+ *   path    MOLORA_PATH_AUTO (chosen on the host from N*k, K and r),
+ *           _GROUPED (MFMA tiles of 16 grouped rows of one adapter),
+ *           _SKINNY (the grouped shrink split over d_in, for small batches), or
+ *           _TILE (16 consecutive tokens per tile, grouped by adapter inside the
+ *           tile; needs K <= 16)
  *   ws      device workspace of at least molora_apply_workspace() bytes
  * Accumulation is fp32; the shrink result h stays fp32 and enters the
  * expand as a bf16 hi/lo pair, so bf16 rounding happens only at the store

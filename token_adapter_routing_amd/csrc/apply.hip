@@ -7,22 +7,24 @@
 // Figure 5 / Figure 9 (a matrix-core kernel for large batches, a skinny kernel for small ones).
 //
 // Kernels:
-//   apply_fused_k1     one routed adapter per token: a workgroup owns 16 grouped rows of one
-//                      adapter and a slice of the output columns; it gathers the 16 x rows,
-//                      shrinks with MFMA (the 4 waves split d_in and meet in LDS), then
-//                      streams y0 -> y for its columns with MFMA expands.  Each token is
-//                      written by exactly one tile, so no combine is needed.
-//   shrink_grouped     the same shrink, written as fp32 partials (optionally split over d_in)
-//                      into a workspace, already multiplied by gate weight and alpha/r.
-//   expand_grouped_k1  one adapter per token, expand from those partials (small batches).
-//   expand_tokens      k > 1: a workgroup owns 16 consecutive tokens; for every adapter any of
-//                      them uses (ascending), an MFMA expand with the other tokens' rows zeroed,
-//                      summed in registers; y0 is read and y written once per token, in a fixed
-//                      order, so the result is deterministic.
+//   apply_tile         token-major tiles with grouping inside the tile (any k, K <= 16): a
+//                      workgroup owns 16 consecutive tokens and a slice of output columns;
+//                      its x / y0 / y rows depend only on the token index, so those streams
+//                      start as soon as the (small) routing loads are done; for every adapter
+//                      used in the tile (ascending) one MFMA shrink over the 16 rows and one
+//                      masked MFMA expand, summed in registers; y is written once.
+//   apply_fused_k1     globally grouped tiles, one adapter per token: a workgroup owns 16
+//                      grouped rows of one adapter (gathered through perm) and a slice of the
+//                      output columns; shrink and expand fused; each token written once.
+//   shrink_grouped     the grouped shrink into an fp32 workspace (weighted by gate and
+//                      alpha/r), optionally split over d_in (the skinny path), for
+//   expand_grouped_k1  (one adapter per token) and
+//   expand_tokens      (k > 1: token-major, every adapter of the tile, fixed order).
 //   copy_unrouted      y = y0 for tokens that no adapter was applied to (out-of-place calls).
 //
-// The shrink result h is kept in fp32 and enters the expand MFMA as a bf16 hi/lo pair
-// (h = hi + lo to about 2^-17 relative), stacked along the reduction dimension.
+// The shrink result h stays fp32 and enters the expand MFMA as a bf16 hi/lo pair
+// (h = hi + lo to about 2^-17 relative).  Workgroups that share x rows are numbered so that
+// they run back to back on the same XCD (block b runs on XCD b % 8) and share its L2.
 #include <algorithm>
 #include <cstdlib>
 
@@ -31,138 +33,27 @@
 
 namespace molora {
 
-// hi/lo split of 8 fp32 values into the expand's B operand: groups G = 0, 1 carry the bf16
-// rounding hi of ranks 16u + 8(G&1) + i, groups 2, 3 the remainder lo = bf16(v - hi).
-__device__ __forceinline__ bf16x8_t split_hilo(const float (&v)[8], bool lo_part) {
-  bf16x8_t out;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const __bf16 hi = (__bf16)v[i];
-    out[i] = lo_part ? (__bf16)(v[i] - (float)hi) : hi;
-  }
-  return out;
-}
+constexpr int kWaves8 = 8;    // waves per workgroup of the fused kernels
+constexpr int kPrefetch = 2;  // expand blocks per wave whose y0 is requested up front
+constexpr int kTileMaxU = kApplyTileMaxAdapters;
 
-// Sum the four waves' partials of the lane's row n (fixed order), scale, split.
-template <int RB>
-__device__ __forceinline__ void h_operand_from_lds(bf16x8_t (&hb)[RB], const float* red, float wgt,
-                                                   int lane) {
-  constexpr int RS = RedLds<RB>::RS;
-  const int n = lane & 15, G = lane >> 4;
+// Rows of tokens 4G..4G+3 of a tile, given the token held by each lane n < 16.
+template <typename P>
+__device__ __forceinline__ void tile_rows(P base, size_t row_bytes, int tok_of_lane, int G, P (&rows)[4]) {
 #pragma unroll
-  for (int u = 0; u < RB; ++u) {
-    const int col = u * 16 + (G & 1) * 8;
-    float v[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = 0.f;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const float* p = red + (w * 16 + n) * RS + col;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] += p[i];
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] *= wgt;
-    hb[u] = split_hilo(v, G >= 2);
-  }
-}
-
-// --------------------------------------------------------------------------------------
-// expand core
-// Output column permutation: within a block of 128 columns at colbase, MFMA j (0..7) row m
-// is column colbase + 32(j/2) + 8(m/4) + 4(j%2) + m%4.  The D fragment of lane (n, G) then
-// covers, for c = 0..3, the 8 contiguous columns colbase + 32c + 8G .. +7 of token n, so the
-// four lanes G = 0..3 of a token read/write 64 contiguous bytes (bf16) per c.
-template <bool F32>
-struct RowChunk;
-template <>
-struct RowChunk<false> {
-  u32x4_t v[4];
-};
-template <>
-struct RowChunk<true> {
-  u32x4_t v[8];
-};
-
-template <bool F32>
-__device__ __forceinline__ void load_row_chunk(RowChunk<F32>& r, const void* row, int colbase, int G) {
-  if constexpr (F32) {
-    const float* p = reinterpret_cast<const float*>(row) + colbase + G * 8;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      r.v[2 * c] = ld16_nt(p + c * 32);
-      r.v[2 * c + 1] = ld16_nt(p + c * 32 + 4);
-    }
-  } else {
-    const uint16_t* p = reinterpret_cast<const uint16_t*>(row) + colbase + G * 8;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) r.v[c] = ld16_nt(p + c * 32);
-  }
-}
-
-template <int RB>
-__device__ __forceinline__ void expand_mfma(f32x4_t (&acc)[8], const bf16x8_t (&hb)[RB],
-                                            const uint16_t* __restrict__ Bt, int r_pad, int colbase,
-                                            int lane) {
-  const int n = lane & 15, G = lane >> 4;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int col = colbase + (j >> 1) * 32 + (n >> 2) * 8 + (j & 1) * 4 + (n & 3);
-    const uint16_t* bp = Bt + (size_t)col * r_pad + (G & 1) * 8;
-#pragma unroll
-    for (int u = 0; u < RB; ++u) acc[j] = mfma16x16x32(as_bf16x8(ld16(bp + u * 16)), hb[u], acc[j]);
-  }
-}
-
-template <bool Y0F32, bool YF32>
-__device__ __forceinline__ void epilogue_store(const f32x4_t (&acc)[8], const RowChunk<Y0F32>& y0c,
-                                               void* yrow, int colbase, int G) {
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    float o[8];
-#pragma unroll
-    for (int t = 0; t < 8; ++t) o[t] = acc[2 * c + (t >> 2)][t & 3];
-    if constexpr (Y0F32) {
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        o[t] += __uint_as_float(y0c.v[2 * c][t]);
-        o[t + 4] += __uint_as_float(y0c.v[2 * c + 1][t]);
-      }
-    } else {
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const uint32_t wv = y0c.v[c][t];
-        o[2 * t] += bf16_to_f32(wv & 0xffffu);
-        o[2 * t + 1] += bf16_to_f32(wv >> 16);
-      }
-    }
-    if constexpr (YF32) {
-      float* p = reinterpret_cast<float*>(yrow) + colbase + c * 32 + G * 8;
-      u32x4_t a, b;
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        a[t] = __float_as_uint(o[t]);
-        b[t] = __float_as_uint(o[t + 4]);
-      }
-      st16_nt(p, a);
-      st16_nt(p + 4, b);
-    } else {
-      uint16_t* p = reinterpret_cast<uint16_t*>(yrow) + colbase + c * 32 + G * 8;
-      u32x4_t a;
-#pragma unroll
-      for (int t = 0; t < 4; ++t) a[t] = pack_bf16x2(o[2 * t], o[2 * t + 1]);
-      st16_nt(p, a);
-    }
+  for (int i = 0; i < 4; ++i) {
+    const int t = __shfl(tok_of_lane, 4 * G + i, kWave);
+    rows[i] = base + (size_t)t * row_bytes;
   }
 }
 
 // --------------------------------------------------------------------------------------
 // y = y0 for rows no tile writes (k = 1, out of place).  Token t is unrouted iff inv[t] < 0.
-template <bool Y0F32, bool YF32>
-__device__ void copy_unrouted(const void* y0, void* y, const int32_t* __restrict__ inv, int N,
-                              int d_out, int cb, int ncb) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (int base = (cb * 4 + wave) * kWave; base < N; base += ncb * 4 * kWave) {
+template <bool Y0F32, bool YF32, int NW>
+__device__ void copy_unrouted(const void* y0, void* y, const int32_t* __restrict__ inv, int N, int d_out, int cb,
+                              int ncb) {
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  for (int base = (cb * NW + wave) * kWave; base < N; base += ncb * NW * kWave) {
     const int t = base + lane;
     uint64_t m = __ballot(t < N && inv[t] < 0);
     while (m) {
@@ -194,6 +85,176 @@ __device__ void copy_unrouted(const void* y0, void* y, const int32_t* __restrict
 }
 
 // --------------------------------------------------------------------------------------
+// Tile-local grouping (token-major), any k, K <= 16.
+struct TileArgs {
+  TargetDev tgt;
+  const uint16_t* x;
+  const void* y0;
+  void* y;
+  const int32_t* offsets;
+  const float* perm_w;
+  const int32_t* inv;
+  int N, K, k;
+  float scale;
+  int col_groups;
+  int tiles;          // token tiles (ceil(N / 16))
+  int tiles_per_xcd;  // grid = 8 * tiles_per_xcd * col_groups
+};
+
+template <int RB>
+struct TileGroup {
+  static constexpr int UP = RB == 1 ? 4 : (RB == 2 ? 2 : 1);  // adapters per shrink group
+};
+
+template <int RB, int KMAX, bool INDIRECT, bool Y0F32, bool YF32>
+__global__ __launch_bounds__(kWaves8 * 64) void apply_tile(TileArgs a) {
+  constexpr int NW = kWaves8;
+  constexpr int PF = kPrefetch;
+  constexpr size_t y0b = Y0F32 ? 4 : 2, yb = YF32 ? 4 : 2;
+  constexpr int UP = TileGroup<RB>::UP;
+  __shared__ float red[UP * RedLds<RB, NW>::kFloats];  // the waves' partials of one adapter group
+  __shared__ u32x4_t hbl[kTileMaxU * 16 * RB * 4];    // per used adapter: [token][u][G] operand pieces
+  __shared__ int offs[65];
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const int g = slot % a.col_groups;
+  const int tt = (slot / a.col_groups) * 8 + xcd;
+  if (tt >= a.tiles) return;
+  const int n = lane & 15, G = lane >> 4;
+  const int t0 = tt * 16;
+  const int tok = t0 + n;
+  const bool valid = tok < a.N;
+  const int tokc = valid ? tok : a.N - 1;
+  const int d_in = a.tgt.d_in, d_out = a.tgt.d_out;
+  const int cols = d_out / a.col_groups;
+  const int c0 = g * cols;
+  const int nblk = cols / kColBlock;
+
+  // 1. routing of the tile's tokens (small loads, done before the large streams start)
+  if (threadIdx.x <= a.K) offs[threadIdx.x] = a.offsets[threadIdx.x];
+  __syncthreads();
+  int es[KMAX];
+  float ws[KMAX];
+  uint64_t mine = 0;
+#pragma unroll
+  for (int s = 0; s < KMAX; ++s) {
+    es[s] = -1;
+    ws[s] = 0.f;
+    if (s < a.k && valid) {
+      const int q = a.inv[(long long)tok * a.k + s];
+      if (q >= 0) {
+        es[s] = segment_of(offs, a.K, q);
+        ws[s] = a.perm_w[q] * a.scale;
+        mine |= 1ull << es[s];
+      }
+    }
+  }
+  uint64_t used = mine;
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const uint32_t lo = __shfl_xor((uint32_t)used, d, kWave);
+    const uint32_t hi = __shfl_xor((uint32_t)(used >> 32), d, kWave);
+    used |= ((uint64_t)hi << 32) | lo;
+  }
+  const int nU = __popcll(used);
+
+  // 2. y0 rows of the first output blocks
+  const char* y0rows[4];
+  char* yrows[4];
+  unsigned vmask = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int t = t0 + 4 * G + i;
+    const int tc = t < a.N ? t : a.N - 1;
+    vmask |= (t < a.N ? 1u : 0u) << i;
+    y0rows[i] = reinterpret_cast<const char*>(a.y0) + (size_t)tc * d_out * y0b;
+    yrows[i] = reinterpret_cast<char*>(a.y) + (size_t)tc * d_out * yb;
+  }
+  RowChunk<Y0F32> y0c[PF];
+#pragma unroll
+  for (int i = 0; i < PF; ++i) {
+    const int blk = wave + i * NW;
+    if (blk < nblk) load_row_chunk<Y0F32>(y0c[i], y0rows, c0 + blk * kColBlock, n);
+  }
+
+  // 3. shrink in groups of UP used adapters (ascending): x is loaded once per group and
+  //    contracted with each adapter's A; the waves' partials meet in LDS and wave j reduces
+  //    group slot j into that adapter's expand operand in hbl
+  const int S = d_in / kStepK;
+  const int s0 = (S * wave) / NW, s1 = (S * (wave + 1)) / NW;
+  uint64_t rem = used;
+  for (int base = 0; base < nU; base += UP) {
+    const int nP = min(UP, nU - base);
+    int eu[UP];
+    const uint16_t* At[UP];
+#pragma unroll
+    for (int j = 0; j < UP; ++j) {
+      eu[j] = -1;
+      At[j] = a.tgt.At;  // never read for j >= nP
+      if (j < nP) {
+        eu[j] = __builtin_ctzll(rem);
+        rem &= rem - 1;
+        At[j] = adapter_A<INDIRECT>(a.tgt, eu[j]);
+      }
+    }
+    f32x4_t acc[UP][RB];
+#pragma unroll
+    for (int j = 0; j < UP; ++j)
+#pragma unroll
+      for (int u = 0; u < RB; ++u) acc[j][u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    shrink_multi<RB, UP>(acc, a.x + (size_t)tokc * d_in, At, nP, d_in, s0, s1, lane);
+#pragma unroll
+    for (int j = 0; j < UP; ++j)
+      if (j < nP) shrink_to_lds<RB, NW>(acc[j], red + j * RedLds<RB, NW>::kFloats, wave, lane);
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < UP; ++j) {
+      if (j < nP && j == wave) {
+        float wt = 0.f;
+#pragma unroll
+        for (int s = 0; s < KMAX; ++s)
+          if (es[s] == eu[j]) wt += ws[s];
+        bf16x8_t hb[RB];
+        h_operand_from_lds<RB, NW>(hb, red + j * RedLds<RB, NW>::kFloats, wt, lane);
+#pragma unroll
+        for (int u = 0; u < RB; ++u)
+          hbl[(((base + j) * 16 + n) * RB + u) * 4 + G] = __builtin_bit_cast(u32x4_t, hb[u]);
+      }
+    }
+    __syncthreads();  // hbl of the group complete; red free for the next group
+  }
+
+  // 4. expand: every used adapter accumulated in registers, then y = y0 + acc
+  for (int r0 = 0; wave + r0 * NW < nblk; r0 += PF) {
+#pragma unroll
+    for (int i = 0; i < PF; ++i) {
+      const int blk = wave + (r0 + i) * NW;
+      if (blk < nblk) {
+        f32x4_t o[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) o[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        uint64_t r2 = used;
+        for (int sl = 0; sl < nU; ++sl) {
+          const int e = __builtin_ctzll(r2);
+          r2 &= r2 - 1;
+          bf16x8_t hb[RB];
+#pragma unroll
+          for (int u = 0; u < RB; ++u) hb[u] = __builtin_bit_cast(bf16x8_t, hbl[((sl * 16 + n) * RB + u) * 4 + G]);
+          expand_mfma<RB>(o, hb, adapter_B<INDIRECT>(a.tgt, e), a.tgt.r_pad, c0 + blk * kColBlock, lane);
+        }
+        epilogue_store<Y0F32, YF32>(o, y0c[i], yrows, c0 + blk * kColBlock, n, vmask);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < PF; ++i) {
+      const int blk = wave + (r0 + PF + i) * NW;
+      if (blk < nblk) load_row_chunk<Y0F32>(y0c[i], y0rows, c0 + blk * kColBlock, n);
+    }
+  }
+}
+
+// --------------------------------------------------------------------------------------
+// Globally grouped tiles, one adapter per token.
 struct FusedArgs {
   TargetDev tgt;
   const uint16_t* x;
@@ -210,17 +271,17 @@ struct FusedArgs {
   int copy_blocks;    // trailing blocks that copy unrouted rows (0 when in place)
 };
 
-// Block b -> (XCD b%8, slot b/8).  Slots of one XCD enumerate (tile, column group) with the
-// column group fastest, so the col_groups workgroups of a tile run back to back on the same
-// XCD and share its L2 for the gathered x rows.
 template <int RB, bool INDIRECT, bool Y0F32, bool YF32>
-__global__ __launch_bounds__(256) void apply_fused_k1(FusedArgs a) {
-  __shared__ float red[RedLds<RB>::kFloats];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+__global__ __launch_bounds__(kWaves8 * 64) void apply_fused_k1(FusedArgs a) {
+  constexpr int NW = kWaves8;
+  constexpr int PF = kPrefetch;
+  constexpr size_t y0b = Y0F32 ? 4 : 2, yb = YF32 ? 4 : 2;
+  __shared__ float red[RedLds<RB, NW>::kFloats];
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int b = blockIdx.x;
   const int main_blocks = 8 * a.tiles_per_xcd * a.col_groups;
   if (b >= main_blocks) {
-    copy_unrouted<Y0F32, YF32>(a.y0, a.y, a.inv, a.N, a.tgt.d_out, b - main_blocks, a.copy_blocks);
+    copy_unrouted<Y0F32, YF32, NW>(a.y0, a.y, a.inv, a.N, a.tgt.d_out, b - main_blocks, a.copy_blocks);
     return;
   }
   const int xcd = b & 7, slot = b >> 3;
@@ -239,34 +300,48 @@ __global__ __launch_bounds__(256) void apply_fused_k1(FusedArgs a) {
   const int cols = d_out / a.col_groups;
   const int c0 = g * cols;
   const int nblk = cols / kColBlock;
-  const char* y0row = reinterpret_cast<const char*>(a.y0) + (size_t)tok * d_out * (Y0F32 ? 4 : 2);
-  char* yrow = reinterpret_cast<char*>(a.y) + (size_t)tok * d_out * (YF32 ? 4 : 2);
+  const char* y0rows[4];
+  char* yrows[4];
+  tile_rows<const char*>(reinterpret_cast<const char*>(a.y0), (size_t)d_out * y0b, tok, G, y0rows);
+  tile_rows<char*>(reinterpret_cast<char*>(a.y), (size_t)d_out * yb, tok, G, yrows);
+  unsigned vmask = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) vmask |= ((4 * G + i) < nrows ? 1u : 0u) << i;
 
-  // y0 of the first block is independent of the shrink: start fetching it now.
-  RowChunk<Y0F32> cur;
-  int blk = wave;
-  if (blk < nblk) load_row_chunk<Y0F32>(cur, y0row, c0 + blk * kColBlock, G);
-
+  RowChunk<Y0F32> y0c[PF];
+#pragma unroll
+  for (int i = 0; i < PF; ++i) {
+    const int blk = wave + i * NW;
+    if (blk < nblk) load_row_chunk<Y0F32>(y0c[i], y0rows, c0 + blk * kColBlock, n);
+  }
   f32x4_t acc[RB];
 #pragma unroll
   for (int u = 0; u < RB; ++u) acc[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   const int S = d_in / kStepK;
-  shrink_steps<RB>(acc, a.x + (size_t)tok * d_in, At, d_in, (S * wave) / 4, (S * (wave + 1)) / 4, lane);
-  shrink_to_lds<RB>(acc, red, wave, lane);
+  shrink_steps_batched<RB, true>(acc, a.x + (size_t)tok * d_in, At, d_in, (S * wave) / NW, (S * (wave + 1)) / NW,
+                                 lane);
+  shrink_to_lds<RB, NW>(acc, red, wave, lane);
   __syncthreads();
   bf16x8_t hb[RB];
-  h_operand_from_lds<RB>(hb, red, wgt, lane);
+  h_operand_from_lds<RB, NW>(hb, red, wgt, lane);
 
-  for (; blk < nblk; blk += 4) {
-    RowChunk<Y0F32> nxt;
-    const int nb = blk + 4;
-    if (nb < nblk) load_row_chunk<Y0F32>(nxt, y0row, c0 + nb * kColBlock, G);
-    f32x4_t o[8];
+  for (int r0 = 0; wave + r0 * NW < nblk; r0 += PF) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) o[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    expand_mfma<RB>(o, hb, Bt, a.tgt.r_pad, c0 + blk * kColBlock, lane);
-    if (valid) epilogue_store<Y0F32, YF32>(o, cur, yrow, c0 + blk * kColBlock, G);
-    cur = nxt;
+    for (int i = 0; i < PF; ++i) {
+      const int blk = wave + (r0 + i) * NW;
+      if (blk < nblk) {
+        f32x4_t o[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) o[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        expand_mfma<RB>(o, hb, Bt, a.tgt.r_pad, c0 + blk * kColBlock, lane);
+        epilogue_store<Y0F32, YF32>(o, y0c[i], yrows, c0 + blk * kColBlock, n, vmask);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < PF; ++i) {
+      const int blk = wave + (r0 + PF + i) * NW;
+      if (blk < nblk) load_row_chunk<Y0F32>(y0c[i], y0rows, c0 + blk * kColBlock, n);
+    }
   }
 }
 
@@ -279,8 +354,8 @@ struct ShrinkArgs {
   const float* perm_w;
   int K, k;
   float scale;
-  float* hpart;     // [nsplit][P][r_pad] fp32, row q = grouped position
-  long long P;      // rows per split slice
+  float* hpart;  // [nsplit][P][r_pad] fp32, row q = grouped position
+  long long P;   // rows per split slice
   int nsplit;
 };
 
@@ -289,7 +364,7 @@ template <int RB, bool INDIRECT>
 __global__ __launch_bounds__(256) void shrink_grouped(ShrinkArgs a) {
   __shared__ float red[RedLds<RB>::kFloats];
   constexpr int RS = RedLds<RB>::RS;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int T = blockIdx.x, sp = blockIdx.y;
   int e, row0, nrows;
   if (!find_tile(a.offsets, a.K, T, lane, e, row0, nrows)) return;
@@ -305,8 +380,8 @@ __global__ __launch_bounds__(256) void shrink_grouped(ShrinkArgs a) {
   f32x4_t acc[RB];
 #pragma unroll
   for (int u = 0; u < RB; ++u) acc[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  shrink_steps<RB>(acc, a.x + (size_t)tok * d_in, At, d_in, sa + (len * wave) / 4,
-                   sa + (len * (wave + 1)) / 4, lane);
+  shrink_steps_batched<RB, true>(acc, a.x + (size_t)tok * d_in, At, d_in, sa + (len * wave) / 4,
+                                 sa + (len * (wave + 1)) / 4, lane);
   shrink_to_lds<RB>(acc, red, wave, lane);
   __syncthreads();
   // lane (n, G) writes ranks [G * RB * 4, (G + 1) * RB * 4) of row n
@@ -331,8 +406,8 @@ __global__ __launch_bounds__(256) void shrink_grouped(ShrinkArgs a) {
 
 // Sum the nsplit partials of grouped row q for the lane's rank pieces and split hi/lo.
 template <int RB>
-__device__ __forceinline__ void h_operand_from_ws(bf16x8_t (&hb)[RB], const float* __restrict__ hpart,
-                                                  long long P, int nsplit, int q, bool valid, int lane) {
+__device__ __forceinline__ void h_operand_from_ws(bf16x8_t (&hb)[RB], const float* __restrict__ hpart, long long P,
+                                                  int nsplit, int q, bool valid, int lane) {
   const int G = lane >> 4;
 #pragma unroll
   for (int u = 0; u < RB; ++u) {
@@ -342,11 +417,11 @@ __device__ __forceinline__ void h_operand_from_ws(bf16x8_t (&hb)[RB], const floa
     if (valid) {
       for (int sp = 0; sp < nsplit; ++sp) {
         const float* p = hpart + ((long long)sp * P + q) * (RB * 16) + u * 16 + (G & 1) * 8;
-        const u32x4_t a = ld16(p), b = ld16(p + 4);
+        const u32x4_t x0 = ld16(p), x1 = ld16(p + 4);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          v[i] += __uint_as_float(a[i]);
-          v[i + 4] += __uint_as_float(b[i]);
+          v[i] += __uint_as_float(x0[i]);
+          v[i + 4] += __uint_as_float(x1[i]);
         }
       }
     }
@@ -373,10 +448,11 @@ struct ExpandArgs {
 // k = 1, small batches: grid = tile slots * col_groups (+ copy blocks).
 template <int RB, bool INDIRECT, bool Y0F32, bool YF32>
 __global__ __launch_bounds__(256) void expand_grouped_k1(ExpandArgs a) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  constexpr size_t y0b = Y0F32 ? 4 : 2, yb = YF32 ? 4 : 2;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int b = blockIdx.x;
   if (b >= a.main_blocks) {
-    copy_unrouted<Y0F32, YF32>(a.y0, a.y, a.inv, a.N, a.tgt.d_out, b - a.main_blocks, a.copy_blocks);
+    copy_unrouted<Y0F32, YF32, 4>(a.y0, a.y, a.inv, a.N, a.tgt.d_out, b - a.main_blocks, a.copy_blocks);
     return;
   }
   const int g = b % a.col_groups, T = b / a.col_groups;
@@ -391,26 +467,32 @@ __global__ __launch_bounds__(256) void expand_grouped_k1(ExpandArgs a) {
   const int cols = d_out / a.col_groups;
   const int c0 = g * cols;
   const int nblk = cols / kColBlock;
-  const char* y0row = reinterpret_cast<const char*>(a.y0) + (size_t)tok * d_out * (Y0F32 ? 4 : 2);
-  char* yrow = reinterpret_cast<char*>(a.y) + (size_t)tok * d_out * (YF32 ? 4 : 2);
+  const char* y0rows[4];
+  char* yrows[4];
+  tile_rows<const char*>(reinterpret_cast<const char*>(a.y0), (size_t)d_out * y0b, tok, G, y0rows);
+  tile_rows<char*>(reinterpret_cast<char*>(a.y), (size_t)d_out * yb, tok, G, yrows);
+  unsigned vmask = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) vmask |= ((4 * G + i) < nrows ? 1u : 0u) << i;
   bf16x8_t hb[RB];
   h_operand_from_ws<RB>(hb, a.hpart, a.P, a.nsplit, q, valid, lane);
   for (int blk = wave; blk < nblk; blk += 4) {
     RowChunk<Y0F32> cur;
-    load_row_chunk<Y0F32>(cur, y0row, c0 + blk * kColBlock, G);
+    load_row_chunk<Y0F32>(cur, y0rows, c0 + blk * kColBlock, n);
     f32x4_t o[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) o[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     expand_mfma<RB>(o, hb, Bt, a.tgt.r_pad, c0 + blk * kColBlock, lane);
-    if (valid) epilogue_store<Y0F32, YF32>(o, cur, yrow, c0 + blk * kColBlock, G);
+    epilogue_store<Y0F32, YF32>(o, cur, yrows, c0 + blk * kColBlock, n, vmask);
   }
 }
 
 // k > 1: grid = ceil(N/16) token tiles * col_groups.  KMAX bounds k (register arrays).
 template <int RB, int KMAX, bool INDIRECT, bool Y0F32, bool YF32>
 __global__ __launch_bounds__(256) void expand_tokens(ExpandArgs a) {
+  constexpr size_t y0b = Y0F32 ? 4 : 2, yb = YF32 ? 4 : 2;
   __shared__ int offs[65];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (threadIdx.x <= a.K) offs[threadIdx.x] = a.offsets[threadIdx.x];
   __syncthreads();
   const int g = blockIdx.x % a.col_groups, tt = blockIdx.x / a.col_groups;
@@ -418,8 +500,7 @@ __global__ __launch_bounds__(256) void expand_tokens(ExpandArgs a) {
   const int t0 = tt * 16;
   const int tok = t0 + n;
   const bool valid = tok < a.N;
-  const int tokc = valid ? tok : t0;
-  // the token's slots: grouped position and adapter, and its h operand per slot
+  const int tokc = valid ? tok : a.N - 1;
   int es[KMAX];
   bf16x8_t hs[KMAX][RB];
   uint64_t mine = 0;
@@ -434,7 +515,6 @@ __global__ __launch_bounds__(256) void expand_tokens(ExpandArgs a) {
     }
     h_operand_from_ws<RB>(hs[s], a.hpart, a.P, a.nsplit, q < 0 ? 0 : q, q >= 0, lane);
   }
-  // adapters used by any token of the tile (every wave of the block computes the same set)
   uint64_t used = mine;
 #pragma unroll
   for (int d = 1; d < kWave; d <<= 1) {
@@ -446,11 +526,20 @@ __global__ __launch_bounds__(256) void expand_tokens(ExpandArgs a) {
   const int cols = d_out / a.col_groups;
   const int c0 = g * cols;
   const int nblk = cols / kColBlock;
-  const char* y0row = reinterpret_cast<const char*>(a.y0) + (size_t)tokc * d_out * (Y0F32 ? 4 : 2);
-  char* yrow = reinterpret_cast<char*>(a.y) + (size_t)tokc * d_out * (YF32 ? 4 : 2);
+  const char* y0rows[4];
+  char* yrows[4];
+  unsigned vmask = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int t = t0 + 4 * G + i;
+    const int tc = t < a.N ? t : a.N - 1;
+    vmask |= (t < a.N ? 1u : 0u) << i;
+    y0rows[i] = reinterpret_cast<const char*>(a.y0) + (size_t)tc * d_out * y0b;
+    yrows[i] = reinterpret_cast<char*>(a.y) + (size_t)tc * d_out * yb;
+  }
   for (int blk = wave; blk < nblk; blk += 4) {
     RowChunk<Y0F32> cur;
-    load_row_chunk<Y0F32>(cur, y0row, c0 + blk * kColBlock, G);
+    load_row_chunk<Y0F32>(cur, y0rows, c0 + blk * kColBlock, n);
     f32x4_t o[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) o[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -469,16 +558,17 @@ __global__ __launch_bounds__(256) void expand_tokens(ExpandArgs a) {
         }
       expand_mfma<RB>(o, hb, adapter_B<INDIRECT>(a.tgt, e), a.tgt.r_pad, c0 + blk * kColBlock, lane);
     }
-    if (valid) epilogue_store<Y0F32, YF32>(o, cur, yrow, c0 + blk * kColBlock, G);
+    epilogue_store<Y0F32, YF32>(o, cur, yrows, c0 + blk * kColBlock, n, vmask);
   }
 }
 
 // --------------------------------------------------------------------------------------
 // host side
 
-int apply_resolve_path(int N, int k, int path) {
+int apply_resolve_path(int N, int k, int path, int K, int r_pad) {
   if (path != 0) return path;
   const long long P = (long long)N * k;
+  if (K <= kTileMaxU && r_pad <= 32 && P >= 192) return 3;  // few, small adapters: tile-local grouping
   if (k == 1) return P >= 192 ? 1 : 2;
   return P >= 1024 ? 1 : 2;
 }
@@ -491,9 +581,9 @@ static int skinny_splits(int d_in) {
   return ns;
 }
 
-size_t apply_ws_bytes(int N, int k, int r_pad, int d_in, int path) {
-  const int p = apply_resolve_path(N, k, path);
-  if (k == 1 && p == 1) return 0;
+size_t apply_ws_bytes(int N, int k, int K, int r_pad, int d_in, int path) {
+  const int p = apply_resolve_path(N, k, path, K, r_pad);
+  if (p == 3 || (k == 1 && p == 1)) return 0;
   const int ns = (p == 2) ? skinny_splits(d_in) : 1;
   return (size_t)ns * (size_t)N * (size_t)k * (size_t)r_pad * sizeof(float);
 }
@@ -503,18 +593,23 @@ static int env_int(const char* name, int dflt) {
   return (s && *s) ? atoi(s) : dflt;
 }
 
-// Column groups: enough workgroups to cover the chip (about two per CU) while every wave
-// keeps at least one 128-column block.
-static int choose_col_groups(long long tiles, int d_out, int target_blocks) {
+// Column groups: enough workgroups to cover the chip while every wave keeps output blocks.
+static int choose_col_groups(long long tiles, int d_out, int target_blocks, int min_blocks_per_group) {
   const int nblk = d_out / kColBlock;
   int c = 1;
-  while (tiles * c < target_blocks && nblk % (2 * c) == 0 && nblk / (2 * c) >= 4) c *= 2;
+  while (tiles * c < target_blocks && nblk % (2 * c) == 0 && nblk / (2 * c) >= min_blocks_per_group) c *= 2;
   return c;
+}
+
+static int col_groups_for(int requested, long long tiles, int d_out, int target, int minb) {
+  int cg = requested > 0 ? requested : env_int("MOLORA_APPLY_COLGROUPS", 0);
+  if (cg <= 0 || (d_out / kColBlock) % cg != 0) cg = choose_col_groups(tiles, d_out, target, minb);
+  return cg;
 }
 
 template <int RB, bool IND, bool Y0F, bool YF>
 static hipError_t launch_fused_t(const FusedArgs& fa, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((apply_fused_k1<RB, IND, Y0F, YF>), dim3(grid), dim3(256), 0, s, fa);
+  hipLaunchKernelGGL((apply_fused_k1<RB, IND, Y0F, YF>), dim3(grid), dim3(kWaves8 * 64), 0, s, fa);
   return hipGetLastError();
 }
 template <int RB, bool IND>
@@ -528,19 +623,24 @@ static hipError_t launch_expand_k1_t(const ExpandArgs& ea, int grid, hipStream_t
   return hipGetLastError();
 }
 template <int RB, int KM, bool IND, bool Y0F, bool YF>
+static hipError_t launch_tile_t(const TileArgs& ta, int grid, hipStream_t s) {
+  hipLaunchKernelGGL((apply_tile<RB, KM, IND, Y0F, YF>), dim3(grid), dim3(kWaves8 * 64), 0, s, ta);
+  return hipGetLastError();
+}
+template <int RB, int KM, bool IND, bool Y0F, bool YF>
 static hipError_t launch_expand_tok_t(const ExpandArgs& ea, int grid, hipStream_t s) {
   hipLaunchKernelGGL((expand_tokens<RB, KM, IND, Y0F, YF>), dim3(grid), dim3(256), 0, s, ea);
   return hipGetLastError();
 }
 
-// Dispatch a runtime (RB, indirect, y0 f32, y f32) to the template instance.
-#define MOLORA_DISPATCH_RB(RBV, ...)                                     \
-  switch (RBV) {                                                         \
-    case 1: { constexpr int RB = 1; __VA_ARGS__; } break;                \
-    case 2: { constexpr int RB = 2; __VA_ARGS__; } break;                \
-    case 3: { constexpr int RB = 3; __VA_ARGS__; } break;                \
-    case 4: { constexpr int RB = 4; __VA_ARGS__; } break;                \
-    default: return hipErrorInvalidValue;                                \
+// Runtime (RB, indirect, y0 f32, y f32) -> template instance.
+#define MOLORA_DISPATCH_RB(RBV, ...)                      \
+  switch (RBV) {                                          \
+    case 1: { constexpr int RB = 1; __VA_ARGS__; } break; \
+    case 2: { constexpr int RB = 2; __VA_ARGS__; } break; \
+    case 3: { constexpr int RB = 3; __VA_ARGS__; } break; \
+    case 4: { constexpr int RB = 4; __VA_ARGS__; } break; \
+    default: return hipErrorInvalidValue;                 \
   }
 #define MOLORA_DISPATCH_BOOL(V, NAME, ...) \
   if (V) { constexpr bool NAME = true; __VA_ARGS__; } else { constexpr bool NAME = false; __VA_ARGS__; }
@@ -550,20 +650,36 @@ hipError_t launch_apply(const ApplyLaunch& a, hipStream_t s) {
   const int RBv = a.tgt.r_pad / 16;
   const long long tiles = P / kTileRows + a.K + 1;  // upper bound on tiles of any grouping
   const bool in_place = (a.y0 == a.y);
-  const int copy_blocks = in_place ? 0 : (int)std::min<long long>((a.N + 255) / 256, 64);
   hipError_t err = hipSuccess;
+
+  if (a.path == 3) {
+    TileArgs ta;
+    ta.tgt = a.tgt; ta.x = a.x; ta.y0 = a.y0; ta.y = a.y; ta.offsets = a.offsets; ta.perm_w = a.perm_w;
+    ta.inv = a.inv; ta.N = a.N; ta.K = a.K; ta.k = a.k; ta.scale = a.scale;
+    ta.tiles = (a.N + 15) / 16;
+    ta.col_groups = col_groups_for(a.col_groups, ta.tiles, a.tgt.d_out, 256, kWaves8);
+    ta.tiles_per_xcd = (ta.tiles + 7) / 8;
+    const int grid = 8 * ta.tiles_per_xcd * ta.col_groups;
+#define MOLORA_TILE(KM)                                                                                \
+  MOLORA_DISPATCH_RB(RBv, MOLORA_DISPATCH_BOOL(a.indirect, IND, MOLORA_DISPATCH_BOOL(a.y0_f32, Y0F,  \
+      MOLORA_DISPATCH_BOOL(a.y_f32, YF, err = (launch_tile_t<RB, KM, IND, Y0F, YF>(ta, grid, s))))))
+    if (a.k == 1) { MOLORA_TILE(1) }
+    else if (a.k <= 2) { MOLORA_TILE(2) }
+    else if (a.k <= 4) { MOLORA_TILE(4) }
+    else { MOLORA_TILE(8) }
+#undef MOLORA_TILE
+    return err;
+  }
 
   if (a.k == 1 && a.path == 1) {
     FusedArgs fa;
     fa.tgt = a.tgt; fa.x = a.x; fa.y0 = a.y0; fa.y = a.y;
     fa.offsets = a.offsets; fa.perm = a.perm; fa.perm_w = a.perm_w; fa.inv = a.inv;
     fa.N = a.N; fa.K = a.K; fa.scale = a.scale;
-    int cg = a.col_groups > 0 ? a.col_groups : env_int("MOLORA_APPLY_COLGROUPS", 0);
-    if (cg <= 0 || (a.tgt.d_out / kColBlock) % cg != 0) cg = choose_col_groups(tiles, a.tgt.d_out, 512);
-    fa.col_groups = cg;
+    fa.col_groups = col_groups_for(a.col_groups, tiles, a.tgt.d_out, 256, kWaves8);
     fa.tiles_per_xcd = (int)((tiles + 7) / 8);
-    fa.copy_blocks = copy_blocks;
-    const int grid = 8 * fa.tiles_per_xcd * cg + copy_blocks;
+    fa.copy_blocks = in_place ? 0 : (int)std::min<long long>((a.N + 511) / 512, 64);
+    const int grid = 8 * fa.tiles_per_xcd * fa.col_groups + fa.copy_blocks;
     MOLORA_DISPATCH_RB(RBv, MOLORA_DISPATCH_BOOL(a.indirect, IND, MOLORA_DISPATCH_BOOL(a.y0_f32, Y0F,
         MOLORA_DISPATCH_BOOL(a.y_f32, YF, err = (launch_fused_t<RB, IND, Y0F, YF>(fa, grid, s))))));
     return err;
@@ -574,31 +690,28 @@ hipError_t launch_apply(const ApplyLaunch& a, hipStream_t s) {
   ShrinkArgs sa;
   sa.tgt = a.tgt; sa.x = a.x; sa.offsets = a.offsets; sa.perm = a.perm; sa.perm_w = a.perm_w;
   sa.K = a.K; sa.k = a.k; sa.scale = a.scale; sa.hpart = a.ws; sa.P = P; sa.nsplit = nsplit;
-  MOLORA_DISPATCH_RB(RBv, MOLORA_DISPATCH_BOOL(a.indirect, IND,
-      err = (launch_shrink_t<RB, IND>(sa, (int)tiles, s))));
+  MOLORA_DISPATCH_RB(RBv, MOLORA_DISPATCH_BOOL(a.indirect, IND, err = (launch_shrink_t<RB, IND>(sa, (int)tiles, s))));
   if (err != hipSuccess) return err;
 
   ExpandArgs ea;
   ea.tgt = a.tgt; ea.y0 = a.y0; ea.y = a.y; ea.offsets = a.offsets; ea.perm = a.perm; ea.inv = a.inv;
   ea.hpart = a.ws; ea.P = P; ea.nsplit = nsplit; ea.N = a.N; ea.K = a.K; ea.k = a.k;
-  ea.copy_blocks = copy_blocks;
   if (a.k == 1) {
-    const int cg = choose_col_groups(tiles, a.tgt.d_out, 512);
-    ea.col_groups = cg;
-    ea.main_blocks = (int)tiles * cg;
-    const int grid = ea.main_blocks + copy_blocks;
+    ea.col_groups = choose_col_groups(tiles, a.tgt.d_out, 512, 4);
+    ea.main_blocks = (int)tiles * ea.col_groups;
+    ea.copy_blocks = in_place ? 0 : (int)std::min<long long>((a.N + 255) / 256, 64);
+    const int grid = ea.main_blocks + ea.copy_blocks;
     MOLORA_DISPATCH_RB(RBv, MOLORA_DISPATCH_BOOL(a.indirect, IND, MOLORA_DISPATCH_BOOL(a.y0_f32, Y0F,
         MOLORA_DISPATCH_BOOL(a.y_f32, YF, err = (launch_expand_k1_t<RB, IND, Y0F, YF>(ea, grid, s))))));
     return err;
   }
   const long long ttiles = (a.N + 15) / 16;
-  const int cg = choose_col_groups(ttiles, a.tgt.d_out, 512);
-  ea.col_groups = cg;
-  ea.main_blocks = (int)(ttiles * cg);
+  ea.col_groups = choose_col_groups(ttiles, a.tgt.d_out, 512, 4);
+  ea.main_blocks = (int)(ttiles * ea.col_groups);
   ea.copy_blocks = 0;  // every token is visited
   const int grid = ea.main_blocks;
-#define MOLORA_TOK(KM)                                                                                  \
-  MOLORA_DISPATCH_RB(RBv, MOLORA_DISPATCH_BOOL(a.indirect, IND, MOLORA_DISPATCH_BOOL(a.y0_f32, Y0F,      \
+#define MOLORA_TOK(KM)                                                                                \
+  MOLORA_DISPATCH_RB(RBv, MOLORA_DISPATCH_BOOL(a.indirect, IND, MOLORA_DISPATCH_BOOL(a.y0_f32, Y0F,  \
       MOLORA_DISPATCH_BOOL(a.y_f32, YF, err = (launch_expand_tok_t<RB, KM, IND, Y0F, YF>(ea, grid, s))))))
   if (a.k <= 2) { MOLORA_TOK(2) }
   else if (a.k <= 4) { MOLORA_TOK(4) }
@@ -608,21 +721,31 @@ hipError_t launch_apply(const ApplyLaunch& a, hipStream_t s) {
 }
 
 // --------------------------------------------------------------------------------------
-// hot-set relayout: A [d_in][r] -> A^T [r_pad][d_in]; B [r][d_out] -> B^T [d_out][r_pad];
-// rank padding rows/columns are zero.
-__global__ void relayout_A(const uint16_t* __restrict__ A, uint16_t* __restrict__ At, int d_in, int r,
-                           int r_pad) {
-  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= (long long)r_pad * d_in) return;
-  const int j = (int)(i / d_in), c = (int)(i % d_in);
-  At[i] = (j < r) ? A[(long long)c * r + j] : (uint16_t)0;
+// Hot-set relayout of one adapter.
+//   A [d_in][r] -> swizzled slab blocks (see a_swz_index); ranks r..r_pad-1 are zero.
+//   B [r][d_out] -> B^T [d_out][r_pad] with the columns of each 128-column block permuted
+//   (slab row w holds column b_perm_col(w)); ranks r..r_pad-1 are zero.
+__global__ void relayout_A(const uint16_t* __restrict__ A, uint16_t* __restrict__ As, int d_in, int r, int r_pad) {
+  const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (long long)r_pad * d_in) return;
+  const int RB = r_pad / 16;
+  long long v = idx;
+  const int i = (int)(v % 8); v /= 8;
+  const int G = (int)(v % 4); v /= 4;
+  const int n = (int)(v % 16); v /= 16;
+  const int u = (int)(v % RB); v /= RB;
+  const int c = (int)(v % 4); v /= 4;
+  const int s = (int)v;
+  const int j = u * 16 + n;
+  const int col = s * kStepK + c * 32 + G * 8 + i;
+  As[idx] = (j < r) ? A[(long long)col * r + j] : (uint16_t)0;
 }
-__global__ void relayout_B(const uint16_t* __restrict__ B, uint16_t* __restrict__ Bt, int d_out, int r,
-                           int r_pad) {
+__global__ void relayout_B(const uint16_t* __restrict__ B, uint16_t* __restrict__ Bt, int d_out, int r, int r_pad) {
   const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= (long long)d_out * r_pad) return;
-  const int c = (int)(i / r_pad), j = (int)(i % r_pad);
-  Bt[i] = (j < r) ? B[(long long)j * d_out + c] : (uint16_t)0;
+  const int row = (int)(i / r_pad), j = (int)(i % r_pad);
+  const int col = b_perm_col(row);
+  Bt[i] = (j < r) ? B[(long long)j * d_out + col] : (uint16_t)0;
 }
 
 hipError_t launch_relayout(const uint16_t* A, const uint16_t* B, int d_in, int d_out, int r, int r_pad,
@@ -651,12 +774,12 @@ __global__ void seqpass_meta(const int32_t* __restrict__ idx, int N, int K, int3
   }
 }
 
-hipError_t launch_seqpass_meta(const int32_t* idx, int N, int K, int32_t* offsets, int32_t* perm,
-                               float* perm_w, hipStream_t s) {
+hipError_t launch_seqpass_meta(const int32_t* idx, int N, int K, int32_t* offsets, int32_t* perm, float* perm_w,
+                               hipStream_t s) {
   long long n = (long long)K * N;
   if (n < (long long)K * (K + 1)) n = (long long)K * (K + 1);
-  hipLaunchKernelGGL(seqpass_meta, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, idx, N, K, offsets,
-                     perm, perm_w);
+  hipLaunchKernelGGL(seqpass_meta, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, idx, N, K, offsets, perm,
+                     perm_w);
   return hipGetLastError();
 }
 

@@ -274,8 +274,8 @@ int molora_apply_workspace(const molora_hotset* hs, int target, int N, int k, in
   if (hs == nullptr) return fail(MOLORA_EINVAL, "hot set is NULL");
   if (target < 0 || target >= hs->n_targets) return fail(MOLORA_EINVAL, "target %d outside [0, %d)", target, hs->n_targets);
   if (N < 0 || k < 1 || k > MOLORA_MAX_TOPK || k > hs->K) return fail(MOLORA_EINVAL, "bad N=%d or k=%d", N, k);
-  if (path < MOLORA_PATH_AUTO || path > MOLORA_PATH_SKINNY) return fail(MOLORA_EINVAL, "unknown path %d", path);
-  *bytes = molora::apply_ws_bytes(N, k, hs->r_pad, hs->tg[target].d_in, path);
+  if (path < MOLORA_PATH_AUTO || path > MOLORA_PATH_TILE) return fail(MOLORA_EINVAL, "unknown path %d", path);
+  *bytes = molora::apply_ws_bytes(N, k, hs->K, hs->r_pad, hs->tg[target].d_in, path);
   return ok();
 }
 
@@ -289,7 +289,9 @@ int molora_apply(const molora_hotset* hs, int target, const void* x, const void*
   if ((long long)N * k >= (1ll << 31)) return fail(MOLORA_ENOTSUP, "N*k too large");
   if ((y0_dtype != MOLORA_BF16 && y0_dtype != MOLORA_F32) || (y_dtype != MOLORA_BF16 && y_dtype != MOLORA_F32))
     return fail(MOLORA_EINVAL, "unknown dtype");
-  if (path < MOLORA_PATH_AUTO || path > MOLORA_PATH_SKINNY) return fail(MOLORA_EINVAL, "unknown path %d", path);
+  if (path < MOLORA_PATH_AUTO || path > MOLORA_PATH_TILE) return fail(MOLORA_EINVAL, "unknown path %d", path);
+  if (path == MOLORA_PATH_TILE && hs->K > molora::kApplyTileMaxAdapters)
+    return fail(MOLORA_ENOTSUP, "the tile path supports K <= %d", molora::kApplyTileMaxAdapters);
   if (y0 == y && y0_dtype != y_dtype) return fail(MOLORA_EINVAL, "in-place apply needs y0_dtype == y_dtype");
   if (N == 0) return ok();
   if (x == nullptr || y0 == nullptr || y == nullptr) return fail(MOLORA_EINVAL, "x, y0 or y is NULL");
@@ -299,7 +301,7 @@ int molora_apply(const molora_hotset* hs, int target, const void* x, const void*
   if (!aligned(offsets, 4) || !aligned(perm, 4) || !aligned(perm_w, 4) || !aligned(inv, 4))
     return fail(MOLORA_EINVAL, "misaligned pointer");
   const molora::TargetDev& tg = hs->tg[target];
-  const size_t need = molora::apply_ws_bytes(N, k, hs->r_pad, tg.d_in, path);
+  const size_t need = molora::apply_ws_bytes(N, k, hs->K, hs->r_pad, tg.d_in, path);
   if (need > 0 && (ws == nullptr || ws_bytes < need || !aligned(ws, 16)))
     return fail(MOLORA_ENOSPC, "workspace of %zu bytes (16-byte aligned) needed, %zu given", need, ws_bytes);
   molora::ApplyLaunch a{};
@@ -318,7 +320,7 @@ int molora_apply(const molora_hotset* hs, int target, const void* x, const void*
   a.perm = perm;
   a.perm_w = perm_w;
   a.inv = inv;
-  a.path = molora::apply_resolve_path(N, k, path);
+  a.path = molora::apply_resolve_path(N, k, path, hs->K, hs->r_pad);
   a.ws = reinterpret_cast<float*>(ws);
   a.col_groups = 0;
   const hipError_t e = molora::launch_apply(a, reinterpret_cast<hipStream_t>(stream));

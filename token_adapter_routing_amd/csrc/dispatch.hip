@@ -42,7 +42,7 @@ __global__ __launch_bounds__(kDispThreads) void dispatch_single(const int32_t* _
   __shared__ int offs[65];
   __shared__ int base[64];
   __shared__ int wcnt[kDispMaxE * kDispWaves * 64];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const uint64_t lt = lanemask_lt(lane);
   if (tid < 64) {
     cnt[tid] = 0;

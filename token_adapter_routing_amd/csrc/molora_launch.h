@@ -40,14 +40,15 @@ struct ApplyLaunch {
   const int32_t* perm;
   const float* perm_w;
   const int32_t* inv;
-  int path;          // resolved path (GROUPED or SKINNY)
+  int path;          // resolved path (1 GROUPED, 2 SKINNY, 3 TILE)
   float* ws;         // fp32 workspace (partials of the shrink)
   int col_groups;    // 0 = choose
 };
 
 // Workspace bytes a resolved apply needs.
-size_t apply_ws_bytes(int N, int k, int r_pad, int d_in, int path);
-int apply_resolve_path(int N, int k, int path);
+size_t apply_ws_bytes(int N, int k, int K, int r_pad, int d_in, int path);
+int apply_resolve_path(int N, int k, int path, int K, int r_pad);
+constexpr int kApplyTileMaxAdapters = 16;  // tile-local path: distinct adapters per tile
 hipError_t launch_apply(const ApplyLaunch& a, hipStream_t s);
 
 hipError_t launch_seqpass_meta(const int32_t* idx, int N, int K, int32_t* offsets, int32_t* perm,

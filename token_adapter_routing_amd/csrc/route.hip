@@ -96,7 +96,7 @@ __global__ __launch_bounds__(256) void route_topk_k(TopkArgs a) {
   constexpr int RS = RedLds<RB>::RS;
   __shared__ float red[ROUTER ? RedLds<RB>::kFloats : 1];
   __shared__ float hid[ROUTER ? 16 * 64 : 1];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int t0 = blockIdx.x * 16;
   if constexpr (ROUTER) {
     const int n = lane & 15;
@@ -105,7 +105,7 @@ __global__ __launch_bounds__(256) void route_topk_k(TopkArgs a) {
 #pragma unroll
     for (int u = 0; u < RB; ++u) acc[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     const int S = a.d / kStepK;
-    shrink_steps<RB>(acc, a.x + (size_t)tok * a.d, a.W1, a.d, (S * wave) / 4, (S * (wave + 1)) / 4, lane);
+    shrink_steps_batched<RB, false>(acc, a.x + (size_t)tok * a.d, a.W1, a.d, (S * wave) / 4, (S * (wave + 1)) / 4, lane);
     shrink_to_lds<RB>(acc, red, wave, lane);
     __syncthreads();
     for (int i = threadIdx.x; i < 16 * 64; i += 256) {
