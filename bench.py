@@ -4,18 +4,21 @@ Workload (default): the 4-modality kernel benchmark shape -- N=2048 tokens, d=40
 adapters (text/image/audio/video) of rank 16, vocabulary routing, k=1, bf16 data with fp32
 accumulation; modality runs with geometric lengths (mean 64) and mix 0.4/0.3/0.15/0.15.
 
-One step = one pass of the whole hot path over one batch: vocabulary routing -> dispatch
-(histogram, offsets, stable permutation) -> grouped LoRA apply (shrink, expand, gate-weighted
-alpha/r add into y), on adapters held in a hot-set slab.  Inputs are resident in HBM; S
-buffer sets (about 410 MB in all, above the 256 MB Infinity Cache) rotate so that every step
-streams its x / y0 / y from HBM.  The timed steps are replayed from one HIP graph that holds
-one step per buffer set.
+One step = one pass of the whole hot path over one batch: vocabulary routing, dispatch
+(histogram, offsets, stable permutation) and the LoRA apply (shrink, expand, gate-weighted
+alpha/r add into y) on adapters held in a hot-set slab.  The headline step is the one-launch
+form (`molora_step_vocab`); the three-launch form (route, dispatch, apply) and the
+per-sequence comparator (K masked dense passes) are timed beside it.  Inputs are resident in
+HBM; S buffer sets (about 410 MB in all, above the 256 MB Infinity Cache) rotate so that
+every step streams x / y0 / y from HBM.  Timed steps are replayed from one HIP graph that
+holds one step per buffer set.
 
 Prints one JSON line.  `--gpus N` with N > 1 is refused: this build measures one GPU.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import statistics
@@ -29,14 +32,19 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 KERNEL_SOURCES = ("token_adapter_routing_amd/csrc/apply.hip", "token_adapter_routing_amd/csrc/molora_mfma.h",
-                  "token_adapter_routing_amd/csrc/molora_dev.h")
+                  "token_adapter_routing_amd/csrc/molora_dev.h", "token_adapter_routing_amd/csrc/dispatch_dev.h")
+COUNTER_SUMMARY = "step_vocab_modality4.md"
+
+
+def kernel_source_hash() -> str:
+    src = "".join(open(os.path.join(ROOT, f)).read() for f in KERNEL_SOURCES)
+    return hashlib.sha256(src.encode()).hexdigest()[:16]
 
 
 def counter_traffic(summary: str):
     """HBM bytes per launch of the dominant kernel from a committed rocprofv3 counter summary
     (FETCH_SIZE / WRITE_SIZE scaled by a copy calibration), or None when the kernel sources
     changed after the counters were taken."""
-    import hashlib
     path = os.path.join(ROOT, "profiles", summary)
     if not os.path.exists(path):
         return None
@@ -45,8 +53,7 @@ def counter_traffic(summary: str):
         if ":" in line and not line.startswith(("|", "#", "`")):
             k, v = line.split(":", 1)
             fields[k.strip()] = v.strip()
-    src = "".join(open(os.path.join(ROOT, f)).read() for f in KERNEL_SOURCES)
-    if hashlib.sha256(src.encode()).hexdigest()[:16] != fields.get("kernel_source_sha256_16"):
+    if kernel_source_hash() != fields.get("kernel_source_sha256_16"):
         return None
     try:
         return int(fields["traffic_bytes_per_launch"])
@@ -62,8 +69,8 @@ def parse():
     p.add_argument("--sets", type=int, default=8, help="rotating input/output buffer sets")
     p.add_argument("--latency-reps", type=int, default=1000)
     p.add_argument("--kernel-reps", type=int, default=200)
-    p.add_argument("--path", default="auto", choices=["auto", "grouped", "tile", "skinny"])
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-extras", action="store_true", help="skip the three-launch and per-sequence lines")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run plain device copies of known size (for HBM counter scaling)")
@@ -105,7 +112,6 @@ def main():
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
 
     hs = m.molora_hotset_init([(bf(t.A), bf(t.B))], case.scale)
-    PATH = {"auto": m.PATH_AUTO, "grouped": m.PATH_GROUPED, "tile": m.PATH_TILE, "skinny": m.PATH_SKINNY}[args.path]
     bounds = case.bounds.tolist()
     S = args.sets
     sets = []
@@ -116,90 +122,87 @@ def main():
         sets.append(dict(
             ids=ids_h.to(dev), x=x_h.clone(), y0=y0_h.clone(),
             y=torch.empty(N, d_out, dtype=torch.bfloat16, device=dev),
-            idx=torch.empty(N, dtype=torch.int32, device=dev), w=torch.empty(N, dtype=torch.float32, device=dev),
+            route=(torch.empty(N, dtype=torch.int32, device=dev), torch.empty(N, dtype=torch.float32, device=dev)),
             meta=(torch.empty(K, dtype=torch.int32, device=dev), torch.empty(K + 1, dtype=torch.int32, device=dev),
                   torch.empty(N, dtype=torch.int32, device=dev), torch.empty(N, dtype=torch.float32, device=dev),
                   torch.empty(N, dtype=torch.int32, device=dev))))
     del x_h, y0_h
 
-    def step(s):
+    def step(s):  # one launch: route + dispatch + apply
         b = sets[s]
-        m.molora_route_vocab(b["ids"], bounds, idx=b["idx"], w=b["w"])
-        m.molora_dispatch(b["idx"], b["w"], K, 1, out=b["meta"])
-        mt = b["meta"]
-        m.molora_apply(hs, b["x"], b["y0"], mt[1], mt[2], mt[3], mt[4], k=1, y=b["y"], path=PATH)
+        m.molora_step_vocab(hs, b["ids"], bounds, b["x"], b["y0"], y=b["y"], route=b["route"], meta=b["meta"])
 
-    def apply_only(s):
+    def step3(s):  # three launches
         b = sets[s]
+        idx, w = b["route"]
         mt = b["meta"]
-        m.molora_apply(hs, b["x"], b["y0"], mt[1], mt[2], mt[3], mt[4], k=1, y=b["y"], path=PATH)
+        m.molora_route_vocab(b["ids"], bounds, idx=idx, w=w)
+        m.molora_dispatch(idx, w, K, 1, out=mt)
+        m.molora_apply(hs, b["x"], b["y0"], mt[1], mt[2], mt[3], mt[4], k=1, y=b["y"], path=m.PATH_AUTO)
 
-    # warm the library and the buffers
     for s in range(S):
         step(s)
+        step3(s)
     torch.cuda.synchronize()
 
     stream = torch.cuda.Stream()
-    # one graph holding one step per buffer set (S steps per replay)
     torch.cuda.current_stream().wait_stream(stream)
-    g_all = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g_all, stream=stream):
-        for s in range(S):
-            step(s)
-    # one graph per set (single-step replays, for latency percentiles)
-    g_one = []
-    for s in range(S):
+
+    def graph_of(fn, sets_range):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=stream):
-            step(s)
-        g_one.append(g)
-    torch.cuda.synchronize()
+            for s in sets_range:
+                fn(s)
+        return g
 
     reps = max(1, args.steps // S)
     steps = reps * S
     wreps = max(1, args.warmup // S)
-    with torch.cuda.stream(stream):
-        for _ in range(wreps):
-            g_all.replay()
-    torch.cuda.synchronize()
 
-    # ---------------- timed region: `steps` steps, bracketed by synchronisation
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    with torch.cuda.stream(stream):
-        e0.record(stream)
-        for _ in range(reps):
-            g_all.replay()
-        e1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    gpu_ms = e0.elapsed_time(e1)
-    ms_per_step = gpu_ms / steps
+    def time_graph(g):
+        with torch.cuda.stream(stream):
+            for _ in range(wreps):
+                g.replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        with torch.cuda.stream(stream):
+            e0.record(stream)
+            for _ in range(reps):
+                g.replay()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps, time.perf_counter() - t0
+
+    # ---------------- timed region (headline): `steps` one-launch steps
+    g_all = graph_of(step, range(S))
+    ms_per_step, wall = time_graph(g_all)
     value = N / (ms_per_step * 1e-3)
 
-    # ---------------- dominant kernel: the apply, launched back to back on `stream`
+    # ---------------- dominant kernel: the one-launch step, back to back on `stream`
     kreps = max(S, args.kernel_reps // S * S)
     ka = torch.cuda.Event(enable_timing=True)
     kb = torch.cuda.Event(enable_timing=True)
     with torch.cuda.stream(stream):
         for s in range(S):
-            apply_only(s)
+            step(s)
         ka.record(stream)
         for i in range(kreps):
-            apply_only(i % S)
+            step(i % S)
         kb.record(stream)
     torch.cuda.synchronize()
-    apply_us = ka.elapsed_time(kb) * 1e3 / kreps
-    pairs = N * k
-    apply_bytes = (N * d_in * 2 + 2 * N * d_out * 2  # x read, y0 read, y written (bf16)
-                   + K * (d_in * r + r * d_out) * 2  # adapters of the hot set used (all K)
-                   + pairs * 8)                      # perm + perm_w
-    apply_gbs = apply_bytes / (apply_us * 1e-6) / 1e9
+    kernel_us = ka.elapsed_time(kb) * 1e3 / kreps
+    adapters = K * (d_in * r + r * d_out) * 2
+    step_bytes = (N * d_in * 2 + 2 * N * d_out * 2  # x read, y0 read, y written (bf16)
+                  + adapters                         # hot-set adapters used (all K)
+                  + N * 4                            # token ids
+                  + N * (4 + 4 + 4 + 4 + 4) + (2 * K + 1) * 4)  # idx, w, perm, perm_w, inv, counts, offsets
+    kernel_gbs = step_bytes / (kernel_us * 1e-6) / 1e9
 
     # ---------------- step latency percentiles over single-step graph replays
-    lat = []
+    g_one = [graph_of(step, [s]) for s in range(S)]
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(args.latency_reps)]
     with torch.cuda.stream(stream):
@@ -213,35 +216,6 @@ def main():
     p99 = lat[min(len(lat) - 1, int(0.99 * len(lat)))]
     cv = statistics.pstdev(lat) / statistics.mean(lat)
 
-    # ---------------- per-sequence comparator: K masked dense passes over all N tokens
-    seq = []
-    for s in range(S):
-        b = sets[s]
-        offs, perm, pw = m.molora_seqpass_meta(b["idx"], K)
-        seq.append((offs, perm, pw))
-    torch.cuda.synchronize()
-
-    def seq_step(s):
-        b = sets[s]
-        offs, perm, pw = seq[s]
-        m.molora_apply(hs, b["x"], b["y0"], offs[0], perm, pw[0], perm, k=1, y=b["y"], path=m.PATH_GROUPED)
-        for e in range(1, K):
-            m.molora_apply(hs, b["x"], b["y"], offs[e], perm, pw[e], perm, k=1, y=b["y"], path=m.PATH_GROUPED)
-
-    g_seq = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g_seq, stream=stream):
-        for s in range(S):
-            seq_step(s)
-    with torch.cuda.stream(stream):
-        g_seq.replay()
-        e0.record(stream)
-        for _ in range(reps):
-            g_seq.replay()
-        e1.record(stream)
-    torch.cuda.synchronize()
-    seq_ms = e0.elapsed_time(e1) / steps
-
-    step_bytes = apply_bytes + N * 4  # + token ids
     out = {
         "metric": "routed tokens/s at N=2048 d=4096 K=4; % of HBM roofline; P99 step latency",
         "value": value,
@@ -256,19 +230,40 @@ def main():
         "dtype": "bf16",
         "data": "synthetic (seeded; modality runs, bf16 N(0,1) activations, LoRA A~N(0,1/d), B~N(0,1/r))",
         "config": {"workload": "4-modality vocab routing N=2048 d=4096 K=4 r=16 k=1", "N": N, "d": d_in, "K": K,
-                   "r": r, "k": k, "alpha_over_r": case.scale, "buffer_sets": S, "launch": "hipGraph, one step per set",
-                   "path": f"route_vocab -> dispatch -> apply({args.path})"},
+                   "r": r, "k": k, "alpha_over_r": case.scale, "buffer_sets": S,
+                   "launch": "hipGraph, one step per buffer set",
+                   "step": "molora_step_vocab (route + dispatch + tile-local apply in one launch)"},
         "step_roofline_frac": step_bytes / (ms_per_step * 1e-3) / (HBM_PEAK_GBS * 1e9),
         "step_latency_us": {"p50": p50, "p99": p99, "cv": cv, "replays": len(lat), "graph": "single step"},
         "wall_s_timed_region": wall,
-        "per_sequence_comparator": {"ms_per_step": seq_ms, "passes": K, "speedup_per_token": seq_ms / ms_per_step},
-        "roofline": {"bound": "hbm", "achieved": apply_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": apply_gbs / HBM_PEAK_GBS,
-                     "traffic": counter_traffic("apply_tile_modality4.md") if args.path in ("auto", "tile") else None,
-                     "kernel": {"auto": "apply_tile", "tile": "apply_tile", "grouped": "apply_fused_k1",
-                                "skinny": "shrink_grouped+expand_grouped_k1"}[args.path],
-                     "kernel_us": apply_us, "algorithmic_bytes": apply_bytes},
+        "roofline": {"bound": "hbm", "achieved": kernel_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": kernel_gbs / HBM_PEAK_GBS, "traffic": counter_traffic(COUNTER_SUMMARY),
+                     "kernel": "step_vocab", "kernel_us": kernel_us, "algorithmic_bytes": step_bytes},
     }
+
+    if not args.no_extras:
+        # three launches per step (route_vocab, dispatch, apply)
+        ms3, _ = time_graph(graph_of(step3, range(S)))
+        # per-sequence comparator: K masked dense passes over all N tokens (metadata from the routing)
+        seq = []
+        for s in range(S):
+            b = sets[s]
+            offs, perm, pw = m.molora_seqpass_meta(b["route"][0], K)
+            seq.append((offs, perm, pw))
+        torch.cuda.synchronize()
+
+        def seq_step(s):
+            b = sets[s]
+            offs, perm, pw = seq[s]
+            m.molora_apply(hs, b["x"], b["y0"], offs[0], perm, pw[0], perm, k=1, y=b["y"], path=m.PATH_GROUPED)
+            for e in range(1, K):
+                m.molora_apply(hs, b["x"], b["y"], offs[e], perm, pw[e], perm, k=1, y=b["y"], path=m.PATH_GROUPED)
+
+        seq_ms, _ = time_graph(graph_of(seq_step, range(S)))
+        out["three_launch_step"] = {"ms_per_step": ms3, "routed_tokens_per_s": N / (ms3 * 1e-3)}
+        out["per_sequence_comparator"] = {"ms_per_step": seq_ms, "passes": K,
+                                          "speedup_per_token": seq_ms / ms_per_step}
+
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
     print(json.dumps(out))

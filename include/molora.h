@@ -212,6 +212,27 @@ int molora_apply(const molora_hotset *hs, int target, const void *x, const void 
                  void *ws, size_t ws_bytes, void *stream);
 
 /* ------------------------------------------------------------------------
+ * The whole vocabulary-routed step in one launch (thelatestinai.com, Table 1:
+ * routing decision, histogram, pointer arrays and grouped dispatch; Figure 2:
+ * per-token weighted sum; Table 4 "Per-token + Graph": the step as few
+ * launches as possible).  Equivalent to molora_route_vocab, molora_dispatch
+ * and molora_apply(MOLORA_PATH_TILE) with k = 1, producing bit-identical
+ * idx, w, counts, offsets, perm, perm_w, inv and y.  Workgroup 0 also runs the
+ * dispatch; every tile routes its own tokens from their ids, so no workgroup
+ * waits for another.
+ *   hs, target    hot set with K = hs->K adapters (K <= 16) and the projection
+ *   ids, bounds   as molora_route_vocab (bounds: host int32 [K+1])
+ *   x, y0, y      as molora_apply (y0 may equal y)
+ *   idx, w        device [N] out, as molora_route_vocab
+ *   counts..inv   device out, as molora_dispatch with k = 1 (inv required)
+ * ------------------------------------------------------------------------ */
+int molora_step_vocab(const molora_hotset *hs, int target, const int32_t *ids, int N,
+                      const int32_t *bounds, const void *x, const void *y0, int y0_dtype,
+                      void *y, int y_dtype, int32_t *idx, float *w, int32_t *counts,
+                      int32_t *offsets, int32_t *perm, float *perm_w, int32_t *inv,
+                      void *stream);
+
+/* ------------------------------------------------------------------------
  * Per-sequence comparator metadata (thelatestinai.com, Table 3: per-sequence
  * routing needs K passes for a K-modality batch; the abstract: work K*N
  * versus N).  From a k = 1 routing idx [N], builds K one-hot dispatches: pass e

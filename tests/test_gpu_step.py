@@ -1,0 +1,105 @@
+"""GPU parity: the one-launch vocabulary step against the three separate calls and the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import apply, dispatch, route_vocab
+from tests.gpu_util import check_bf16_output, check_float_output, dev, dev_bf16, f64, host, need_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+def three_calls(m, hs, ids, bounds, K, x, y0, y_dtype):
+    idx, w = m.molora_route_vocab(ids, bounds)
+    meta = m.molora_dispatch(idx, w, K, 1)
+    counts, offsets, perm, perm_w, inv = meta
+    y = m.molora_apply(hs, x, y0, offsets, perm, perm_w, inv, k=1, y_dtype=y_dtype, path=m.PATH_TILE)
+    return y, (idx, w), meta
+
+
+def cases():
+    tiny = synth.tiny_vocab()
+    mod = synth.modality4()
+    odd = synth.vocab_case(N=1000, d=640, K=7, r=24, case_id=11, runs=True, probs=(0.3, 0.2, 0.1, 0.1, 0.1, 0.1, 0.1))
+    odd.ids = odd.ids.copy()
+    odd.ids[::37] = -5        # unrouted
+    odd.ids[5::41] = 10 ** 6  # unrouted
+    return [("tiny", tiny), ("modality4", mod), ("ragged_unrouted", odd)]
+
+
+@pytest.mark.parametrize("layout", [0, 1])
+@pytest.mark.parametrize("y_dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("name,case", cases())
+def test_step_equals_three_calls_and_oracle(name, case, y_dtype, layout):
+    m = need_gpu()
+    t = case.targets[0]
+    hs = m.molora_hotset_init([(dev_bf16(t.A), dev_bf16(t.B))], case.scale, layout=layout)
+    ids = dev(case.ids)
+    bounds = case.bounds.tolist()
+    x, y0 = dev_bf16(t.x), dev_bf16(t.y0)
+    y1, r1, m1 = m.molora_step_vocab(hs, ids, bounds, x, y0, y_dtype=y_dtype)
+    y3, r3, m3 = three_calls(m, hs, ids, bounds, case.K, x, y0, y_dtype)
+    N = case.N
+    np.testing.assert_array_equal(host(r1[0])[:N], host(r3[0]))
+    np.testing.assert_array_equal(host(r1[1])[:N], host(r3[1]))
+    n_routed = int(host(m3[1])[-1])
+    for a, b, full in zip(m1, m3, (True, True, False, False, True)):
+        ha, hb = host(a), host(b)
+        if full:
+            np.testing.assert_array_equal(ha, hb)
+        else:
+            np.testing.assert_array_equal(ha[:n_routed], hb[:n_routed])
+    np.testing.assert_array_equal(host(y1), host(y3))
+    # against the oracle
+    ri, rw = route_vocab(case.ids, case.bounds)
+    np.testing.assert_array_equal(host(r1[0])[:N], ri)
+    oc, oo, op, opw, oinv = dispatch(ri, rw, case.K)
+    np.testing.assert_array_equal(host(m1[0]), oc)
+    np.testing.assert_array_equal(host(m1[1]), oo)
+    np.testing.assert_array_equal(host(m1[2])[:oo[-1]], op)
+    np.testing.assert_array_equal(host(m1[4])[:N], oinv)
+    ref = apply(f64(t.y0), f64(t.x), f64(t.A), f64(t.B), case.scale, op, opw, oo, 1)
+    if y_dtype == torch.float32:
+        check_float_output(host(y1), ref, f64(t.y0))
+    else:
+        check_bf16_output(host(y1), ref)
+
+
+def test_step_in_place_and_graph_replay():
+    m = need_gpu()
+    c = synth.modality4()
+    t = c.targets[0]
+    hs = m.molora_hotset_init([(dev_bf16(t.A), dev_bf16(t.B))], c.scale)
+    ids = dev(c.ids)
+    bounds = c.bounds.tolist()
+    x = dev_bf16(t.x)
+    y_ref, _, _ = m.molora_step_vocab(hs, ids, bounds, x, dev_bf16(t.y0))
+    y = dev_bf16(t.y0)
+    m.molora_step_vocab(hs, ids, bounds, x, y, y=y)  # in place
+    np.testing.assert_array_equal(host(y), host(y_ref))
+    # graph capture of the one-launch step, replayed with eager work in between
+    y0 = dev_bf16(t.y0)
+    out = torch.empty_like(y0)
+    route = (torch.empty(c.N, dtype=torch.int32, device="cuda"), torch.empty(c.N, dtype=torch.float32, device="cuda"))
+    meta = (torch.empty(c.K, dtype=torch.int32, device="cuda"), torch.empty(c.K + 1, dtype=torch.int32, device="cuda"),
+            torch.empty(c.N, dtype=torch.int32, device="cuda"), torch.empty(c.N, dtype=torch.float32, device="cuda"),
+            torch.empty(c.N, dtype=torch.int32, device="cuda"))
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        m.molora_step_vocab(hs, ids, bounds, x, y0, y=out, route=route, meta=meta)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        m.molora_step_vocab(hs, ids, bounds, x, y0, y=out, route=route, meta=meta)
+    for _ in range(3):
+        out.zero_()
+        meta[2].fill_(-1)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(host(out), host(y_ref))
+        ri, rw = route_vocab(c.ids, c.bounds)
+        np.testing.assert_array_equal(host(meta[2]), dispatch(ri, rw, c.K)[2])

@@ -51,6 +51,8 @@ _SIGS = {
     "molora_apply": (_c_i, [_c_p, _c_i, _c_p, _c_p, _c_i, _c_p, _c_i, _c_i, _c_i, _c_p, _c_p, _c_p, _c_p, _c_i,
                             _c_p, _c_sz, _c_p]),
     "molora_seqpass_meta": (_c_i, [_c_p, _c_i, _c_i, _c_p, _c_p, _c_p, _c_p]),
+    "molora_step_vocab": (_c_i, [_c_p, _c_i, _c_p, _c_i, _c_p, _c_p, _c_p, _c_i, _c_p, _c_i, _c_p, _c_p, _c_p, _c_p,
+                                 _c_p, _c_p, _c_p, _c_p]),
 }
 
 _lib = None
@@ -275,6 +277,35 @@ def molora_apply(hs: HotSet, x: torch.Tensor, y0: torch.Tensor, offsets: torch.T
         _ptr(perm_w, torch.float32, "perm_w"), _ptr(inv, torch.int32, "inv"), path,
         _ptr(ws, None, "ws") if ws is not None else None, ws.numel() if ws is not None else 0, _stream(stream)))
     return y
+
+
+def molora_step_vocab(hs: HotSet, ids: torch.Tensor, bounds: Sequence[int], x: torch.Tensor, y0: torch.Tensor,
+                      target: int = 0, y: Optional[torch.Tensor] = None, y_dtype=None, route=None, meta=None,
+                      stream=None):
+    """One launch of route_vocab + dispatch + apply (k = 1).  Returns (y, (idx, w),
+    (counts, offsets, perm, perm_w, inv)); `route` and `meta` may supply those buffers."""
+    N = ids.numel()
+    K = len(bounds) - 1
+    dev = ids.device
+    d_out = hs.dims[target][1]
+    if y is None:
+        y = torch.empty(N, d_out, dtype=y_dtype or y0.dtype, device=dev)
+    if route is None:
+        route = (torch.empty(max(N, 1), dtype=torch.int32, device=dev), torch.empty(max(N, 1), dtype=torch.float32, device=dev))
+    if meta is None:
+        meta = (torch.empty(K, dtype=torch.int32, device=dev), torch.empty(K + 1, dtype=torch.int32, device=dev),
+                torch.empty(max(N, 1), dtype=torch.int32, device=dev), torch.empty(max(N, 1), dtype=torch.float32, device=dev),
+                torch.empty(max(N, 1), dtype=torch.int32, device=dev))
+    b = (ctypes.c_int32 * len(bounds))(*[int(v) for v in bounds])
+    idx, w = route
+    counts, offsets, perm, perm_w, inv = meta
+    _check(load_library().molora_step_vocab(
+        hs.handle, target, _ptr(ids, torch.int32, "ids"), N, ctypes.cast(b, _c_p), _ptr(x, torch.bfloat16, "x"),
+        _ptr(y0, None, "y0"), _dtype_code(y0), _ptr(y, None, "y"), _dtype_code(y), _ptr(idx, torch.int32, "idx"),
+        _ptr(w, torch.float32, "w"), _ptr(counts, torch.int32, "counts"), _ptr(offsets, torch.int32, "offsets"),
+        _ptr(perm, torch.int32, "perm"), _ptr(perm_w, torch.float32, "perm_w"), _ptr(inv, torch.int32, "inv"),
+        _stream(stream)))
+    return y, route, meta
 
 
 def molora_seqpass_meta(idx: torch.Tensor, K: int, stream=None):

@@ -28,6 +28,7 @@
 #include <algorithm>
 #include <cstdlib>
 
+#include "dispatch_dev.h"
 #include "molora_launch.h"
 #include "molora_mfma.h"
 
@@ -106,49 +107,35 @@ struct TileGroup {
   static constexpr int UP = RB == 1 ? 4 : (RB == 2 ? 2 : 1);  // adapters per shrink group
 };
 
+template <int RB>
+struct TileLds {
+  float red[TileGroup<RB>::UP * RedLds<RB, kWaves8>::kFloats];  // the waves' partials of one adapter group
+  u32x4_t hbl[kTileMaxU * 16 * RB * 4];                         // per used adapter: [token][u][G] operand
+};
+
+// Body of one tile workgroup, given the token slots of this lane's token (adapter es[s] and
+// gate weight times alpha/r ws[s]; es = -1 for none).  Every thread of the workgroup calls it.
 template <int RB, int KMAX, bool INDIRECT, bool Y0F32, bool YF32>
-__global__ __launch_bounds__(kWaves8 * 64) void apply_tile(TileArgs a) {
+__device__ __forceinline__ void tile_body(const TileArgs& a, TileLds<RB>& L, int tt, int g, const int (&es)[KMAX],
+                                          const float (&ws)[KMAX]) {
   constexpr int NW = kWaves8;
   constexpr int PF = kPrefetch;
-  constexpr size_t y0b = Y0F32 ? 4 : 2, yb = YF32 ? 4 : 2;
   constexpr int UP = TileGroup<RB>::UP;
-  __shared__ float red[UP * RedLds<RB, NW>::kFloats];  // the waves' partials of one adapter group
-  __shared__ u32x4_t hbl[kTileMaxU * 16 * RB * 4];    // per used adapter: [token][u][G] operand pieces
-  __shared__ int offs[65];
+  constexpr size_t y0b = Y0F32 ? 4 : 2, yb = YF32 ? 4 : 2;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-  const int g = slot % a.col_groups;
-  const int tt = (slot / a.col_groups) * 8 + xcd;
-  if (tt >= a.tiles) return;
   const int n = lane & 15, G = lane >> 4;
   const int t0 = tt * 16;
   const int tok = t0 + n;
-  const bool valid = tok < a.N;
-  const int tokc = valid ? tok : a.N - 1;
+  const int tokc = tok < a.N ? tok : a.N - 1;
   const int d_in = a.tgt.d_in, d_out = a.tgt.d_out;
   const int cols = d_out / a.col_groups;
   const int c0 = g * cols;
   const int nblk = cols / kColBlock;
 
-  // 1. routing of the tile's tokens (small loads, done before the large streams start)
-  if (threadIdx.x <= a.K) offs[threadIdx.x] = a.offsets[threadIdx.x];
-  __syncthreads();
-  int es[KMAX];
-  float ws[KMAX];
   uint64_t mine = 0;
 #pragma unroll
-  for (int s = 0; s < KMAX; ++s) {
-    es[s] = -1;
-    ws[s] = 0.f;
-    if (s < a.k && valid) {
-      const int q = a.inv[(long long)tok * a.k + s];
-      if (q >= 0) {
-        es[s] = segment_of(offs, a.K, q);
-        ws[s] = a.perm_w[q] * a.scale;
-        mine |= 1ull << es[s];
-      }
-    }
-  }
+  for (int s = 0; s < KMAX; ++s)
+    if (es[s] >= 0) mine |= 1ull << es[s];
   uint64_t used = mine;
 #pragma unroll
   for (int d = 1; d < kWave; d <<= 1) {
@@ -158,7 +145,7 @@ __global__ __launch_bounds__(kWaves8 * 64) void apply_tile(TileArgs a) {
   }
   const int nU = __popcll(used);
 
-  // 2. y0 rows of the first output blocks
+  // y0 rows of the first output blocks
   const char* y0rows[4];
   char* yrows[4];
   unsigned vmask = 0;
@@ -177,9 +164,9 @@ __global__ __launch_bounds__(kWaves8 * 64) void apply_tile(TileArgs a) {
     if (blk < nblk) load_row_chunk<Y0F32>(y0c[i], y0rows, c0 + blk * kColBlock, n);
   }
 
-  // 3. shrink in groups of UP used adapters (ascending): x is loaded once per group and
-  //    contracted with each adapter's A; the waves' partials meet in LDS and wave j reduces
-  //    group slot j into that adapter's expand operand in hbl
+  // shrink in groups of UP used adapters (ascending): x is loaded once per group and contracted
+  // with each adapter's A; the waves' partials meet in LDS and wave j reduces group slot j into
+  // that adapter's expand operand in hbl
   const int S = d_in / kStepK;
   const int s0 = (S * wave) / NW, s1 = (S * (wave + 1)) / NW;
   uint64_t rem = used;
@@ -205,7 +192,7 @@ __global__ __launch_bounds__(kWaves8 * 64) void apply_tile(TileArgs a) {
     shrink_multi<RB, UP>(acc, a.x + (size_t)tokc * d_in, At, nP, d_in, s0, s1, lane);
 #pragma unroll
     for (int j = 0; j < UP; ++j)
-      if (j < nP) shrink_to_lds<RB, NW>(acc[j], red + j * RedLds<RB, NW>::kFloats, wave, lane);
+      if (j < nP) shrink_to_lds<RB, NW>(acc[j], L.red + j * RedLds<RB, NW>::kFloats, wave, lane);
     __syncthreads();
 #pragma unroll
     for (int j = 0; j < UP; ++j) {
@@ -215,16 +202,16 @@ __global__ __launch_bounds__(kWaves8 * 64) void apply_tile(TileArgs a) {
         for (int s = 0; s < KMAX; ++s)
           if (es[s] == eu[j]) wt += ws[s];
         bf16x8_t hb[RB];
-        h_operand_from_lds<RB, NW>(hb, red + j * RedLds<RB, NW>::kFloats, wt, lane);
+        h_operand_from_lds<RB, NW>(hb, L.red + j * RedLds<RB, NW>::kFloats, wt, lane);
 #pragma unroll
         for (int u = 0; u < RB; ++u)
-          hbl[(((base + j) * 16 + n) * RB + u) * 4 + G] = __builtin_bit_cast(u32x4_t, hb[u]);
+          L.hbl[(((base + j) * 16 + n) * RB + u) * 4 + G] = __builtin_bit_cast(u32x4_t, hb[u]);
       }
     }
     __syncthreads();  // hbl of the group complete; red free for the next group
   }
 
-  // 4. expand: every used adapter accumulated in registers, then y = y0 + acc
+  // expand: every used adapter accumulated in registers, then y = y0 + acc
   for (int r0 = 0; wave + r0 * NW < nblk; r0 += PF) {
 #pragma unroll
     for (int i = 0; i < PF; ++i) {
@@ -239,7 +226,7 @@ __global__ __launch_bounds__(kWaves8 * 64) void apply_tile(TileArgs a) {
           r2 &= r2 - 1;
           bf16x8_t hb[RB];
 #pragma unroll
-          for (int u = 0; u < RB; ++u) hb[u] = __builtin_bit_cast(bf16x8_t, hbl[((sl * 16 + n) * RB + u) * 4 + G]);
+          for (int u = 0; u < RB; ++u) hb[u] = __builtin_bit_cast(bf16x8_t, L.hbl[((sl * 16 + n) * RB + u) * 4 + G]);
           expand_mfma<RB>(o, hb, adapter_B<INDIRECT>(a.tgt, e), a.tgt.r_pad, c0 + blk * kColBlock, lane);
         }
         epilogue_store<Y0F32, YF32>(o, y0c[i], yrows, c0 + blk * kColBlock, n, vmask);
@@ -251,6 +238,107 @@ __global__ __launch_bounds__(kWaves8 * 64) void apply_tile(TileArgs a) {
       if (blk < nblk) load_row_chunk<Y0F32>(y0c[i], y0rows, c0 + blk * kColBlock, n);
     }
   }
+}
+
+// Block b runs on XCD b % 8; slots of one XCD enumerate (tile, column group), column group
+// fastest, so the column groups of a tile run back to back on one XCD and share its L2.
+__device__ __forceinline__ void tile_of_block(int b, int col_groups, int& tt, int& g) {
+  const int xcd = b & 7, slot = b >> 3;
+  g = slot % col_groups;
+  tt = (slot / col_groups) * 8 + xcd;
+}
+
+template <int RB, int KMAX, bool INDIRECT, bool Y0F32, bool YF32>
+__global__ __launch_bounds__(kWaves8 * 64) void apply_tile(TileArgs a) {
+  __shared__ TileLds<RB> L;
+  __shared__ int offs[65];
+  int tt, g;
+  tile_of_block(blockIdx.x, a.col_groups, tt, g);
+  if (tt >= a.tiles) return;
+  const int lane = threadIdx.x & 63, n = lane & 15;
+  const int tok = tt * 16 + n;
+  const bool valid = tok < a.N;
+  // routing of the tile's tokens (small loads, done before the large streams start)
+  if (threadIdx.x <= a.K) offs[threadIdx.x] = a.offsets[threadIdx.x];
+  __syncthreads();
+  int es[KMAX];
+  float ws[KMAX];
+#pragma unroll
+  for (int s = 0; s < KMAX; ++s) {
+    es[s] = -1;
+    ws[s] = 0.f;
+    if (s < a.k && valid) {
+      const int q = a.inv[(long long)tok * a.k + s];
+      if (q >= 0) {
+        es[s] = segment_of(offs, a.K, q);
+        ws[s] = a.perm_w[q] * a.scale;
+      }
+    }
+  }
+  tile_body<RB, KMAX, INDIRECT, Y0F32, YF32>(a, L, tt, g, es, ws);
+}
+
+// --------------------------------------------------------------------------------------
+// One launch of the vocabulary-routed step (k = 1): workgroup 0 routes every token, writes
+// idx / w and runs the stable counting sort (dispatch_block) before its own tile; every tile
+// workgroup routes its 16 tokens from their ids with the same range lookup, so the apply never
+// waits for the dispatch and no workgroup waits for another.
+constexpr int kStepDispatchThreads = kWaves8 * 64;
+
+struct StepArgs {
+  TileArgs t;
+  VocabBounds bounds;
+  const int32_t* ids;
+  int32_t* idx;
+  float* w;
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* perm;
+  float* perm_w;
+  int32_t* inv;
+};
+
+struct VocabSource {
+  const int32_t* ids;
+  const int* bl;
+  int K;
+  __device__ __forceinline__ void operator()(int p, int& e, float& wv) const {
+    e = vocab_owner(ids[p], bl, K);
+    wv = (e >= 0) ? 1.0f : 0.0f;
+  }
+};
+
+template <int RB, bool INDIRECT, bool Y0F32, bool YF32>
+__global__ __launch_bounds__(kWaves8 * 64) void step_vocab(StepArgs a) {
+  __shared__ TileLds<RB> L;
+  __shared__ DispatchLds<kStepDispatchThreads> DL;
+  __shared__ int bl[65];
+  const int K = a.t.K, N = a.t.N;
+  bounds_to_lds(a.bounds, bl, K);
+  __syncthreads();
+  if (blockIdx.x == 0) {
+    const VocabSource src{a.ids, bl, K};
+    for (int t = threadIdx.x; t < N; t += kStepDispatchThreads) {
+      int e;
+      float wv;
+      src(t, e, wv);
+      a.idx[t] = e;
+      a.w[t] = wv;
+    }
+    dispatch_block<kStepDispatchThreads>(DL, src, N, K, a.counts, a.offsets, a.perm, a.perm_w, a.inv);
+  }
+  int tt, g;
+  tile_of_block(blockIdx.x, a.t.col_groups, tt, g);
+  if (tt >= a.t.tiles) return;
+  const int n = threadIdx.x & 15;
+  const int tok = tt * 16 + n;
+  int es[1] = {-1};
+  float ws[1] = {0.f};
+  if (tok < N) {
+    es[0] = vocab_owner(a.ids[tok], bl, K);
+    ws[0] = (es[0] >= 0) ? 1.0f * a.t.scale : 0.f;
+  }
+  tile_body<RB, 1, INDIRECT, Y0F32, YF32>(a.t, L, tt, g, es, ws);
 }
 
 // --------------------------------------------------------------------------------------
@@ -607,6 +695,16 @@ static int col_groups_for(int requested, long long tiles, int d_out, int target,
   return cg;
 }
 
+static TileArgs tile_args(const ApplyLaunch& a) {
+  TileArgs ta;
+  ta.tgt = a.tgt; ta.x = a.x; ta.y0 = a.y0; ta.y = a.y; ta.offsets = a.offsets; ta.perm_w = a.perm_w;
+  ta.inv = a.inv; ta.N = a.N; ta.K = a.K; ta.k = a.k; ta.scale = a.scale;
+  ta.tiles = (a.N + 15) / 16;
+  ta.col_groups = col_groups_for(a.col_groups, ta.tiles, a.tgt.d_out, 256, kWaves8);
+  ta.tiles_per_xcd = (ta.tiles + 7) / 8;
+  return ta;
+}
+
 template <int RB, bool IND, bool Y0F, bool YF>
 static hipError_t launch_fused_t(const FusedArgs& fa, int grid, hipStream_t s) {
   hipLaunchKernelGGL((apply_fused_k1<RB, IND, Y0F, YF>), dim3(grid), dim3(kWaves8 * 64), 0, s, fa);
@@ -625,6 +723,11 @@ static hipError_t launch_expand_k1_t(const ExpandArgs& ea, int grid, hipStream_t
 template <int RB, int KM, bool IND, bool Y0F, bool YF>
 static hipError_t launch_tile_t(const TileArgs& ta, int grid, hipStream_t s) {
   hipLaunchKernelGGL((apply_tile<RB, KM, IND, Y0F, YF>), dim3(grid), dim3(kWaves8 * 64), 0, s, ta);
+  return hipGetLastError();
+}
+template <int RB, bool IND, bool Y0F, bool YF>
+static hipError_t launch_step_t(const StepArgs& sa, int grid, hipStream_t s) {
+  hipLaunchKernelGGL((step_vocab<RB, IND, Y0F, YF>), dim3(grid), dim3(kWaves8 * 64), 0, s, sa);
   return hipGetLastError();
 }
 template <int RB, int KM, bool IND, bool Y0F, bool YF>
@@ -653,12 +756,7 @@ hipError_t launch_apply(const ApplyLaunch& a, hipStream_t s) {
   hipError_t err = hipSuccess;
 
   if (a.path == 3) {
-    TileArgs ta;
-    ta.tgt = a.tgt; ta.x = a.x; ta.y0 = a.y0; ta.y = a.y; ta.offsets = a.offsets; ta.perm_w = a.perm_w;
-    ta.inv = a.inv; ta.N = a.N; ta.K = a.K; ta.k = a.k; ta.scale = a.scale;
-    ta.tiles = (a.N + 15) / 16;
-    ta.col_groups = col_groups_for(a.col_groups, ta.tiles, a.tgt.d_out, 256, kWaves8);
-    ta.tiles_per_xcd = (ta.tiles + 7) / 8;
+    const TileArgs ta = tile_args(a);
     const int grid = 8 * ta.tiles_per_xcd * ta.col_groups;
 #define MOLORA_TILE(KM)                                                                                \
   MOLORA_DISPATCH_RB(RBv, MOLORA_DISPATCH_BOOL(a.indirect, IND, MOLORA_DISPATCH_BOOL(a.y0_f32, Y0F,  \
@@ -717,6 +815,20 @@ hipError_t launch_apply(const ApplyLaunch& a, hipStream_t s) {
   else if (a.k <= 4) { MOLORA_TOK(4) }
   else { MOLORA_TOK(8) }
 #undef MOLORA_TOK
+  return err;
+}
+
+hipError_t launch_step_vocab(const StepVocabLaunch& a, hipStream_t s) {
+  StepArgs sa;
+  sa.t = tile_args(a.apply);
+  sa.bounds = a.bounds;
+  sa.ids = a.ids; sa.idx = a.idx; sa.w = a.w; sa.counts = a.counts; sa.offsets = a.offsets; sa.perm = a.perm;
+  sa.perm_w = a.perm_w; sa.inv = a.inv;
+  const int grid = 8 * sa.t.tiles_per_xcd * sa.t.col_groups;
+  const int RBv = a.apply.tgt.r_pad / 16;
+  hipError_t err = hipSuccess;
+  MOLORA_DISPATCH_RB(RBv, MOLORA_DISPATCH_BOOL(a.apply.indirect, IND, MOLORA_DISPATCH_BOOL(a.apply.y0_f32, Y0F,
+      MOLORA_DISPATCH_BOOL(a.apply.y_f32, YF, err = (launch_step_t<RB, IND, Y0F, YF>(sa, grid, s))))));
   return err;
 }
 

@@ -327,6 +327,61 @@ int molora_apply(const molora_hotset* hs, int target, const void* x, const void*
   return e == hipSuccess ? ok() : hip_fail(e, "apply launch");
 }
 
+int molora_step_vocab(const molora_hotset* hs, int target, const int32_t* ids, int N, const int32_t* bounds,
+                      const void* x, const void* y0, int y0_dtype, void* y, int y_dtype, int32_t* idx, float* w,
+                      int32_t* counts, int32_t* offsets, int32_t* perm, float* perm_w, int32_t* inv, void* stream) {
+  if (hs == nullptr) return fail(MOLORA_EINVAL, "hot set is NULL");
+  if (target < 0 || target >= hs->n_targets) return fail(MOLORA_EINVAL, "target %d outside [0, %d)", target, hs->n_targets);
+  if (N < 0) return fail(MOLORA_EINVAL, "N=%d < 0", N);
+  if (hs->K > molora::kApplyTileMaxAdapters)
+    return fail(MOLORA_ENOTSUP, "the one-launch step supports K <= %d", molora::kApplyTileMaxAdapters);
+  if (bounds == nullptr) return fail(MOLORA_EINVAL, "bounds is NULL");
+  molora::StepVocabLaunch st{};
+  for (int e = 0; e <= hs->K; ++e) {
+    st.bounds.b[e] = bounds[e];
+    if (e > 0 && bounds[e] < bounds[e - 1]) return fail(MOLORA_EINVAL, "bounds must be non-decreasing");
+  }
+  if ((y0_dtype != MOLORA_BF16 && y0_dtype != MOLORA_F32) || (y_dtype != MOLORA_BF16 && y_dtype != MOLORA_F32))
+    return fail(MOLORA_EINVAL, "unknown dtype");
+  if (y0 == y && y0_dtype != y_dtype) return fail(MOLORA_EINVAL, "in-place step needs y0_dtype == y_dtype");
+  if (N == 0) return ok();
+  if (ids == nullptr || x == nullptr || y0 == nullptr || y == nullptr || idx == nullptr || w == nullptr ||
+      counts == nullptr || offsets == nullptr || perm == nullptr || perm_w == nullptr || inv == nullptr)
+    return fail(MOLORA_EINVAL, "a required pointer is NULL");
+  if (!aligned(x, 16) || !aligned(y0, 16) || !aligned(y, 16)) return fail(MOLORA_EINVAL, "x, y0 and y must be 16-byte aligned");
+  if (!aligned(ids, 4) || !aligned(idx, 4) || !aligned(w, 4) || !aligned(counts, 4) || !aligned(offsets, 4) ||
+      !aligned(perm, 4) || !aligned(perm_w, 4) || !aligned(inv, 4))
+    return fail(MOLORA_EINVAL, "misaligned pointer");
+  molora::ApplyLaunch& a = st.apply;
+  a.tgt = hs->tg[target];
+  a.indirect = hs->layout == MOLORA_LAYOUT_INDIRECT;
+  a.x = reinterpret_cast<const uint16_t*>(x);
+  a.y0 = y0;
+  a.y = y;
+  a.y0_f32 = y0_dtype == MOLORA_F32;
+  a.y_f32 = y_dtype == MOLORA_F32;
+  a.N = N;
+  a.k = 1;
+  a.K = hs->K;
+  a.scale = hs->scale;
+  a.offsets = offsets;
+  a.perm = perm;
+  a.perm_w = perm_w;
+  a.inv = inv;
+  a.path = 3;
+  a.col_groups = 0;
+  st.ids = ids;
+  st.idx = idx;
+  st.w = w;
+  st.counts = counts;
+  st.offsets = offsets;
+  st.perm = perm;
+  st.perm_w = perm_w;
+  st.inv = inv;
+  const hipError_t e = molora::launch_step_vocab(st, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ok() : hip_fail(e, "step launch");
+}
+
 int molora_seqpass_meta(const int32_t* idx, int N, int K, int32_t* offsets, int32_t* perm, float* perm_w, void* stream) {
   if (N < 0) return fail(MOLORA_EINVAL, "N=%d < 0", N);
   if (K < 1 || K > MOLORA_MAX_ADAPTERS) return fail(MOLORA_ENOTSUP, "K=%d outside [1, %d]", K, MOLORA_MAX_ADAPTERS);

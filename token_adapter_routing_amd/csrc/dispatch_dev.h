@@ -1,0 +1,180 @@
+// Single-workgroup stable counting sort of routed pairs by adapter (MoLoRA pages,
+// thelatestinai.com, Table 1 rows "Histogram computation" and "Pointer arrays"; Figure 2
+// right: tokens grouped by their selected adapter).
+//
+// NT threads (NW = NT/64 waves).  Pairs are produced by a source functor src(p) -> (e, w).
+//   pass 1  wave64 "match" masks (ballots over the bits of the adapter index) give each group
+//           of equal adapters in a wave its size; the group's lowest lane adds it to an LDS
+//           counter.  Wave 0 scans the K counters into offsets.
+//   pass 2  pairs are taken in chunks of E*NT (E <= 8), pair p = chunk + j*NT + tid.  A lane's
+//           rank among equal adapters of its wave is popcount(match & lanes below); group
+//           sizes go to LDS as [j][wave][adapter]; NT/64 threads per adapter scan them in
+//           (j, wave) order -- ascending pair id -- on top of the adapter's offset and the
+//           pairs of earlier chunks, which makes the permutation stable and deterministic.
+#pragma once
+
+#include "molora_dev.h"
+
+namespace molora {
+
+constexpr int kDispMaxE = 8;
+
+// Lanes of the wave that hold the same adapter index as this lane (valid lanes only).
+__device__ __forceinline__ uint64_t match_mask(int e, bool v, int nbits) {
+  uint64_t m = __ballot(v);
+  for (int b = 0; b < nbits; ++b) {
+    const bool bit = v && ((e >> b) & 1);
+    const uint64_t bb = __ballot(bit);
+    m &= bit ? bb : ~bb;
+  }
+  return m;
+}
+
+template <int NT>
+struct DispatchLds {
+  static constexpr int NW = NT / kWave;
+  int cnt[64];
+  int offs[64];
+  int base[64];
+  int wcnt[kDispMaxE * NW * 64];
+};
+
+// src(p) returns adapter e (outside [0, K) = unrouted) and gate weight w of pair p < P.
+template <int NT, typename Src>
+__device__ void dispatch_block(DispatchLds<NT>& L, Src src, int P, int K, int32_t* __restrict__ counts,
+                               int32_t* __restrict__ offsets, int32_t* __restrict__ perm, float* __restrict__ perm_w,
+                               int32_t* __restrict__ inv) {
+  constexpr int NW = NT / kWave;
+  constexpr int TPA = NT / 64;  // threads per adapter in the scan
+  static_assert(NT % 64 == 0 && TPA >= 1 && TPA <= 16, "dispatch block size");
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const uint64_t lt = lanemask_lt(lane);
+  int nbits = 0;
+  while ((1 << nbits) < K) ++nbits;
+  int E = (P + NT - 1) / NT;
+  if (E < 1) E = 1;
+  if (E > kDispMaxE) E = kDispMaxE;
+  if (tid < 64) {
+    L.cnt[tid] = 0;
+    L.base[tid] = 0;
+  }
+  __syncthreads();
+
+  // pass 1: histogram.  Each chunk's source reads are issued together; when all pairs fit in
+  // one chunk the values stay in registers for pass 2.
+  const int chunk = E * NT;
+  const bool one_chunk = P <= chunk;
+  int ev[kDispMaxE];
+  float wv[kDispMaxE];
+  for (int c0 = 0; c0 < P; c0 += chunk) {
+#pragma unroll
+    for (int j = 0; j < kDispMaxE; ++j) {
+      ev[j] = -1;
+      wv[j] = 0.f;
+      const int p = c0 + j * NT + tid;
+      if (j < E && p < P) src(p, ev[j], wv[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < kDispMaxE; ++j) {
+      if (j < E) {
+        const bool v = (ev[j] >= 0) && (ev[j] < K);
+        const uint64_t m = match_mask(ev[j], v, nbits);
+        if (v && (m & lt) == 0) atomicAdd(&L.cnt[ev[j]], __popcll(m));
+      }
+    }
+  }
+  __syncthreads();
+  if (wave == 0) {
+    const int c = (lane < K) ? L.cnt[lane] : 0;
+    const int incl = wave_incl_scan(c, lane);
+    if (lane < K) {
+      counts[lane] = c;
+      offsets[lane + 1] = incl;
+      L.offs[lane] = incl - c;
+    }
+    if (lane == 0) offsets[0] = 0;
+  }
+  __syncthreads();
+
+  // pass 2: stable scatter
+  for (int c0 = 0; c0 < P; c0 += chunk) {
+    for (int i = tid; i < E * NW * 64; i += NT) L.wcnt[i] = 0;
+    if (!one_chunk) {
+#pragma unroll
+      for (int j = 0; j < kDispMaxE; ++j) {
+        ev[j] = -1;
+        wv[j] = 0.f;
+        const int p = c0 + j * NT + tid;
+        if (j < E && p < P) src(p, ev[j], wv[j]);
+      }
+    }
+    __syncthreads();
+    int rk[kDispMaxE];
+#pragma unroll
+    for (int j = 0; j < kDispMaxE; ++j) {
+      rk[j] = 0;
+      if (j < E) {
+        const bool v = (ev[j] >= 0) && (ev[j] < K);
+        const uint64_t m = match_mask(ev[j], v, nbits);
+        if (v) {
+          rk[j] = __popcll(m & lt);
+          if (rk[j] == 0) L.wcnt[(j * NW + wave) * 64 + ev[j]] = __popcll(m);
+        } else {
+          ev[j] = -1;
+        }
+      }
+    }
+    __syncthreads();
+    {
+      // adapter ae's E*NW group sizes in (j, wave) order, split over TPA threads of one wave;
+      // thread pi takes the entries [pi * E * NW / TPA, (pi + 1) * E * NW / TPA)
+      const int ae = tid / TPA, pi = tid % TPA;
+      constexpr int PER = kDispMaxE * NW / TPA;  // upper bound of entries per thread
+      const int per = E * NW / TPA;
+      int loc[PER];
+      int sum = 0;
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        loc[i] = 0;
+        if (i < per) {
+          loc[i] = L.wcnt[(pi * per + i) * 64 + ae];
+          sum += loc[i];
+        }
+      }
+      int incl = sum;
+#pragma unroll
+      for (int d = 1; d < TPA; d <<= 1) {
+        const int o = __shfl_up(incl, d, TPA);
+        if (pi >= d) incl += o;
+      }
+      const int b0 = (ae < K) ? L.offs[ae] + L.base[ae] : 0;
+      int run = b0 + incl - sum;
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        if (i < per) {
+          L.wcnt[(pi * per + i) * 64 + ae] = run;
+          run += loc[i];
+        }
+      }
+      if (pi == TPA - 1 && ae < K) L.base[ae] = L.base[ae] + incl;  // same wave read base[ae] above
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kDispMaxE; ++j) {
+      if (j < E) {
+        const int p = c0 + j * NT + tid;
+        if (ev[j] >= 0) {
+          const int pos = L.wcnt[(j * NW + wave) * 64 + ev[j]] + rk[j];
+          perm[pos] = p;
+          perm_w[pos] = wv[j];
+          if (inv != nullptr) inv[p] = pos;
+        } else if (p < P && inv != nullptr) {
+          inv[p] = -1;
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
+}  // namespace molora

@@ -119,6 +119,19 @@ __device__ __forceinline__ bool find_tile(const int* __restrict__ offsets, int K
   return true;
 }
 
+// Vocabulary range lookup (largest e with b[e] <= v, if b[0] <= v < b[K]; else -1), on bounds
+// held in LDS or registers.
+__device__ __forceinline__ int vocab_owner(int v, const int* b, int K) {
+  if (v < b[0] || v >= b[K]) return -1;
+  int lo = 0, hi = K;  // b[lo] <= v < b[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (b[mid] <= v) lo = mid;
+    else hi = mid;
+  }
+  return lo;
+}
+
 // Adapter owning grouped position q (offsets in LDS, K+1 entries): largest e with offsets[e] <= q.
 __device__ __forceinline__ int segment_of(const int* offs, int K, int q) {
   int lo = 0, hi = K;  // invariant: offs[lo] <= q < offs[hi]

@@ -13,6 +13,13 @@ struct VocabBounds {
   int b[65];
 };
 
+// Copy the K+1 bounds from kernel arguments into LDS (static indices only).
+__device__ __forceinline__ void bounds_to_lds(const VocabBounds& vb, int* lds, int K) {
+#pragma unroll
+  for (int i = 0; i < 65; ++i)
+    if ((int)threadIdx.x == i && i <= K) lds[i] = vb.b[i];
+}
+
 hipError_t launch_route_vocab(const int32_t* ids, int N, const VocabBounds& bounds, int K,
                               int32_t* idx, float* w, hipStream_t s);
 
@@ -50,6 +57,20 @@ size_t apply_ws_bytes(int N, int k, int K, int r_pad, int d_in, int path);
 int apply_resolve_path(int N, int k, int path, int K, int r_pad);
 constexpr int kApplyTileMaxAdapters = 16;  // tile-local path: distinct adapters per tile
 hipError_t launch_apply(const ApplyLaunch& a, hipStream_t s);
+
+struct StepVocabLaunch {
+  ApplyLaunch apply;  // x, y0, y, N, K, scale, target; k = 1
+  VocabBounds bounds;
+  const int32_t* ids;
+  int32_t* idx;
+  float* w;
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* perm;
+  float* perm_w;
+  int32_t* inv;
+};
+hipError_t launch_step_vocab(const StepVocabLaunch& a, hipStream_t s);
 
 hipError_t launch_seqpass_meta(const int32_t* idx, int N, int K, int32_t* offsets, int32_t* perm,
                                float* perm_w, hipStream_t s);

@@ -3,7 +3,7 @@
 // g_theta(x), cost O(64d + 64K); Figure 2: the k selected adapters are combined by a
 // weighted sum, here the softmax over the selected logits).
 //
-//   route_vocab_k   one thread per token: binary search of the id in the K+1 range bounds.
+//   route_vocab_k   one thread per token: binary search of the id in the K+1 range bounds (LDS).
 //   route_topk_k    a workgroup owns 16 tokens.  Router mode: the first layer x W1^T (d -> 64)
 //                   is an MFMA product with the same gather/shrink core as the LoRA shrink,
 //                   the 4 waves splitting d and meeting in LDS; bias and ReLU follow in LDS;
@@ -21,19 +21,12 @@ namespace molora {
 
 __global__ __launch_bounds__(256) void route_vocab_k(const int32_t* __restrict__ ids, int N, VocabBounds b,
                                                      int K, int32_t* __restrict__ idx, float* __restrict__ w) {
+  __shared__ int bl[65];
+  bounds_to_lds(b, bl, K);
+  __syncthreads();
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= N) return;
-  const int v = ids[i];
-  int e = -1;
-  if (v >= b.b[0] && v < b.b[K]) {
-    int lo = 0, hi = K;  // b[lo] <= v < b[hi]
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (b.b[mid] <= v) lo = mid;
-      else hi = mid;
-    }
-    e = lo;
-  }
+  const int e = vocab_owner(ids[i], bl, K);
   idx[i] = e;
   w[i] = (e >= 0) ? 1.0f : 0.0f;
 }
