@@ -5,7 +5,8 @@ import torch
 
 import synth
 from oracle import apply, apply_masked_passes, dispatch, route_topk, route_vocab, router_logits
-from tests.gpu_util import (check_bf16_output, check_float_output, dev, dev_bf16, f64, host, need_gpu)
+from tests.gpu_util import (DESIGN_MAXABS, check_bf16_output, check_float_output, dev, dev_bf16, f64, host,
+                            need_gpu)
 
 pytestmark = pytest.mark.gpu
 
@@ -84,14 +85,16 @@ def test_modality4_per_sequence_comparator():
 
 
 @pytest.mark.parametrize("case", ["tiny", "modality4"])
-def test_k1_paths_bit_identical(case):
-    """For one adapter per token the grouped and tile paths do the same arithmetic
-    per token (same reduction split and order), so their outputs agree bit for bit."""
+def test_k1_paths_deterministic_and_close(case):
+    """The grouped and the tile paths split the reductions differently, so they agree to the
+    rounding of the bf16 output, not bit for bit; each is deterministic (same bits on a repeat)."""
     m = need_gpu()
     c = synth.tiny_vocab() if case == "tiny" else synth.modality4()
     hs = make_hotset(m, c.targets, c.scale)
-    outs = [host(run_pipeline_vocab(m, c, hs, torch.bfloat16, path=p)[0]) for p in (1, 3)]
-    np.testing.assert_array_equal(outs[0], outs[1])
+    outs = {p: [host(run_pipeline_vocab(m, c, hs, torch.float32, path=p)[0]) for _ in range(2)] for p in (1, 3)}
+    for p in (1, 3):
+        np.testing.assert_array_equal(outs[p][0], outs[p][1])
+    assert np.abs(outs[1][0] - outs[3][0]).max() <= DESIGN_MAXABS
 
 
 def test_small_integers_bit_exact():

@@ -26,17 +26,19 @@
 // (h = hi + lo to about 2^-17 relative).  Workgroups that share x rows are numbered so that
 // they run back to back on the same XCD (block b runs on XCD b % 8) and share its L2.
 #include <algorithm>
+#include <climits>
 #include <cstdlib>
 
 #include "dispatch_dev.h"
 #include "molora_launch.h"
 #include "molora_mfma.h"
+#include "tile8_dev.h"
 
 namespace molora {
 
 constexpr int kWaves8 = 8;    // waves per workgroup of the fused kernels
 constexpr int kPrefetch = 2;  // expand blocks per wave whose y0 is requested up front
-constexpr int kTileMaxU = kApplyTileMaxAdapters;
+static_assert(kT8MaxU == kApplyTileMaxAdapters, "tile path adapter bound");
 
 // Rows of tokens 4G..4G+3 of a tile, given the token held by each lane n < 16.
 template <typename P>
@@ -86,208 +88,69 @@ __device__ void copy_unrouted(const void* y0, void* y, const int32_t* __restrict
 }
 
 // --------------------------------------------------------------------------------------
-// Tile-local grouping (token-major), any k, K <= 16.
-struct TileArgs {
-  TargetDev tgt;
-  const uint16_t* x;
-  const void* y0;
-  void* y;
+// Token-major 8-token tiles (any k, K <= 16): the routing of a tile's pairs comes from the
+// dispatch outputs (inv gives the grouped position q of pair p, offsets its adapter, perm_w
+// its gate weight).  The inverse-permutation loads are issued before the x / y0 streams; the
+// gate-weight loads after them (they are first needed after the shrink).
+struct T8ApplyArgs {
+  T8Args t;
   const int32_t* offsets;
   const float* perm_w;
   const int32_t* inv;
-  int N, K, k;
-  float scale;
-  int col_groups;
-  int tiles;          // token tiles (ceil(N / 16))
-  int tiles_per_xcd;  // grid = 8 * tiles_per_xcd * col_groups
 };
 
-template <int RB>
-struct TileGroup {
-  static constexpr int UP = RB == 1 ? 4 : (RB == 2 ? 2 : 1);  // adapters per shrink group
-};
-
-template <int RB>
-struct TileLds {
-  float red[TileGroup<RB>::UP * RedLds<RB, kWaves8>::kFloats];  // the waves' partials of one adapter group
-  u32x4_t hbl[kTileMaxU * 16 * RB * 4];                         // per used adapter: [token][u][G] operand
-};
-
-// Body of one tile workgroup, given the token slots of this lane's token (adapter es[s] and
-// gate weight times alpha/r ws[s]; es = -1 for none).  Every thread of the workgroup calls it.
-template <int RB, int KMAX, bool INDIRECT, bool Y0F32, bool YF32>
-__device__ __forceinline__ void tile_body(const TileArgs& a, TileLds<RB>& L, int tt, int g, const int (&es)[KMAX],
-                                          const float (&ws)[KMAX]) {
-  constexpr int NW = kWaves8;
-  constexpr int PF = kPrefetch;
-  constexpr int UP = TileGroup<RB>::UP;
-  constexpr size_t y0b = Y0F32 ? 4 : 2, yb = YF32 ? 4 : 2;
-  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int n = lane & 15, G = lane >> 4;
-  const int t0 = tt * 16;
-  const int tok = t0 + n;
-  const int tokc = tok < a.N ? tok : a.N - 1;
-  const int d_in = a.tgt.d_in, d_out = a.tgt.d_out;
-  const int cols = d_out / a.col_groups;
-  const int c0 = g * cols;
-  const int nblk = cols / kColBlock;
-
-  uint64_t mine = 0;
-#pragma unroll
-  for (int s = 0; s < KMAX; ++s)
-    if (es[s] >= 0) mine |= 1ull << es[s];
-  uint64_t used = mine;
-#pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    const uint32_t lo = __shfl_xor((uint32_t)used, d, kWave);
-    const uint32_t hi = __shfl_xor((uint32_t)(used >> 32), d, kWave);
-    used |= ((uint64_t)hi << 32) | lo;
-  }
-  const int nU = __popcll(used);
-
-  // y0 rows of the first output blocks
-  const char* y0rows[4];
-  char* yrows[4];
-  unsigned vmask = 0;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int t = t0 + 4 * G + i;
-    const int tc = t < a.N ? t : a.N - 1;
-    vmask |= (t < a.N ? 1u : 0u) << i;
-    y0rows[i] = reinterpret_cast<const char*>(a.y0) + (size_t)tc * d_out * y0b;
-    yrows[i] = reinterpret_cast<char*>(a.y) + (size_t)tc * d_out * yb;
-  }
-  RowChunk<Y0F32> y0c[PF];
-#pragma unroll
-  for (int i = 0; i < PF; ++i) {
-    const int blk = wave + i * NW;
-    if (blk < nblk) load_row_chunk<Y0F32>(y0c[i], y0rows, c0 + blk * kColBlock, n);
-  }
-
-  // shrink in groups of UP used adapters (ascending): x is loaded once per group and contracted
-  // with each adapter's A; the waves' partials meet in LDS and wave j reduces group slot j into
-  // that adapter's expand operand in hbl
-  const int S = d_in / kStepK;
-  const int s0 = (S * wave) / NW, s1 = (S * (wave + 1)) / NW;
-  uint64_t rem = used;
-  for (int base = 0; base < nU; base += UP) {
-    const int nP = min(UP, nU - base);
-    int eu[UP];
-    const uint16_t* At[UP];
-#pragma unroll
-    for (int j = 0; j < UP; ++j) {
-      eu[j] = -1;
-      At[j] = a.tgt.At;  // never read for j >= nP
-      if (j < nP) {
-        eu[j] = __builtin_ctzll(rem);
-        rem &= rem - 1;
-        At[j] = adapter_A<INDIRECT>(a.tgt, eu[j]);
-      }
-    }
-    f32x4_t acc[UP][RB];
-#pragma unroll
-    for (int j = 0; j < UP; ++j)
-#pragma unroll
-      for (int u = 0; u < RB; ++u) acc[j][u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    shrink_multi<RB, UP>(acc, a.x + (size_t)tokc * d_in, At, nP, d_in, s0, s1, lane);
-#pragma unroll
-    for (int j = 0; j < UP; ++j)
-      if (j < nP) shrink_to_lds<RB, NW>(acc[j], L.red + j * RedLds<RB, NW>::kFloats, wave, lane);
-    __syncthreads();
-#pragma unroll
-    for (int j = 0; j < UP; ++j) {
-      if (j < nP && j == wave) {
-        float wt = 0.f;
-#pragma unroll
-        for (int s = 0; s < KMAX; ++s)
-          if (es[s] == eu[j]) wt += ws[s];
-        bf16x8_t hb[RB];
-        h_operand_from_lds<RB, NW>(hb, L.red + j * RedLds<RB, NW>::kFloats, wt, lane);
-#pragma unroll
-        for (int u = 0; u < RB; ++u)
-          L.hbl[(((base + j) * 16 + n) * RB + u) * 4 + G] = __builtin_bit_cast(u32x4_t, hb[u]);
-      }
-    }
-    __syncthreads();  // hbl of the group complete; red free for the next group
-  }
-
-  // expand: every used adapter accumulated in registers, then y = y0 + acc
-  for (int r0 = 0; wave + r0 * NW < nblk; r0 += PF) {
-#pragma unroll
-    for (int i = 0; i < PF; ++i) {
-      const int blk = wave + (r0 + i) * NW;
-      if (blk < nblk) {
-        f32x4_t o[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) o[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        uint64_t r2 = used;
-        for (int sl = 0; sl < nU; ++sl) {
-          const int e = __builtin_ctzll(r2);
-          r2 &= r2 - 1;
-          bf16x8_t hb[RB];
-#pragma unroll
-          for (int u = 0; u < RB; ++u) hb[u] = __builtin_bit_cast(bf16x8_t, L.hbl[((sl * 16 + n) * RB + u) * 4 + G]);
-          expand_mfma<RB>(o, hb, adapter_B<INDIRECT>(a.tgt, e), a.tgt.r_pad, c0 + blk * kColBlock, lane);
-        }
-        epilogue_store<Y0F32, YF32>(o, y0c[i], yrows, c0 + blk * kColBlock, n, vmask);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < PF; ++i) {
-      const int blk = wave + (r0 + PF + i) * NW;
-      if (blk < nblk) load_row_chunk<Y0F32>(y0c[i], y0rows, c0 + blk * kColBlock, n);
-    }
-  }
-}
-
-// Block b runs on XCD b % 8; slots of one XCD enumerate (tile, column group), column group
-// fastest, so the column groups of a tile run back to back on one XCD and share its L2.
-__device__ __forceinline__ void tile_of_block(int b, int col_groups, int& tt, int& g) {
-  const int xcd = b & 7, slot = b >> 3;
-  g = slot % col_groups;
-  tt = (slot / col_groups) * 8 + xcd;
-}
-
-template <int RB, int KMAX, bool INDIRECT, bool Y0F32, bool YF32>
-__global__ __launch_bounds__(kWaves8 * 64) void apply_tile(TileArgs a) {
-  __shared__ TileLds<RB> L;
-  __shared__ int offs[65];
+template <int RB, bool INDIRECT, bool Y0F32, bool YF32>
+__global__ __launch_bounds__(kT8Threads) void apply_t8(T8ApplyArgs a) {
+  __shared__ T8Lds<RB> L;
   int tt, g;
-  tile_of_block(blockIdx.x, a.col_groups, tt, g);
-  if (tt >= a.tiles) return;
-  const int lane = threadIdx.x & 63, n = lane & 15;
-  const int tok = tt * 16 + n;
-  const bool valid = tok < a.N;
-  // routing of the tile's tokens (small loads, done before the large streams start)
-  if (threadIdx.x <= a.K) offs[threadIdx.x] = a.offsets[threadIdx.x];
-  __syncthreads();
-  int es[KMAX];
-  float ws[KMAX];
-#pragma unroll
-  for (int s = 0; s < KMAX; ++s) {
-    es[s] = -1;
-    ws[s] = 0.f;
-    if (s < a.k && valid) {
-      const int q = a.inv[(long long)tok * a.k + s];
-      if (q >= 0) {
-        es[s] = segment_of(offs, a.K, q);
-        ws[s] = a.perm_w[q] * a.scale;
-      }
-    }
-  }
-  tile_body<RB, KMAX, INDIRECT, Y0F32, YF32>(a, L, tt, g, es, ws);
+  t8_tile_of_block(blockIdx.x, a.t, tt, g);
+  if (tt >= a.t.tiles) return;
+  const int lane = threadIdx.x & 63;
+  const int k = a.t.k, K = a.t.K;
+  // lane l < 8k: pair (token t0 + l / k, slot l % k), tokens past N - 1 cloned from N - 1;
+  // the small loads go first, unconditionally, so that the later waits on them are exact
+  const int tc = min(tt * kT8Tokens + lane / k, a.t.N - 1);
+  const bool mine = lane < kT8Tokens * k;
+  const int qv = a.inv[(long long)tc * k + lane % k];
+  const int ov = a.offsets[min(lane, K)];  // lane i holds offsets[i]
+  T8Stream<RB, Y0F32> st;
+  t8_prefetch<RB, Y0F32, YF32>(a.t, tt, g, st);
+  // adapter of grouped position q: the number of segment starts offsets[1 .. K-1] at or below q
+  const int q = mine ? qv : -1;
+  int seg = 0;
+  for (int i = 1; i < K; ++i) seg += (__shfl(ov, i, kWave) <= q) ? 1 : 0;
+  const int pe = q >= 0 ? seg : -1;
+  const float pw = q >= 0 ? a.perm_w[q] * a.t.scale : 0.f;
+  t8_main<RB, INDIRECT, Y0F32, YF32>(a.t, L, st, pe, pw, [] {});
 }
 
 // --------------------------------------------------------------------------------------
-// One launch of the vocabulary-routed step (k = 1): workgroup 0 routes every token, writes
-// idx / w and runs the stable counting sort (dispatch_block) before its own tile; every tile
-// workgroup routes its 16 tokens from their ids with the same range lookup, so the apply never
-// waits for the dispatch and no workgroup waits for another.
-constexpr int kStepDispatchThreads = kWaves8 * 64;
+// One launch of the vocabulary-routed step (k = 1).  Every workgroup routes its 8 tokens from
+// their ids and applies the adapters, as apply_t8 does.  It also derives its share of the
+// dispatch outputs without waiting for any other workgroup: it counts the adapters of all N
+// tokens and of the tokens before its tile (the same range lookup on every id), which gives
+// the offsets and each of its tokens' positions in the stable grouped order.  This runs after
+// the apply body, while its stores drain.  Workgroups of column group 0 write their tokens'
+// idx / w / inv / perm / perm_w; the first tile writes counts and offsets.
+constexpr int kStepIdsPerThread = 4;  // ids held from the start: N <= 512 * 4 in one pass
+constexpr int kStepMaxN = 4096;       // larger batches take the three-launch step
+
+// Vocabulary ranges as kernel arguments: [lo, hi) is routed; the owner of v is the number of
+// interior bounds b[1..K-1] at or below v (mid[i - 1] = b[i]; unused entries hold INT_MAX).
+struct StepBounds {
+  int lo, hi;
+  int mid[kT8MaxU - 1];
+};
+__device__ __forceinline__ int step_owner(int v, const StepBounds& b) {
+  int e = 0;
+#pragma unroll
+  for (int i = 0; i < kT8MaxU - 1; ++i) e += (v >= b.mid[i]) ? 1 : 0;
+  return (v >= b.lo && v < b.hi) ? e : -1;
+}
 
 struct StepArgs {
-  TileArgs t;
-  VocabBounds bounds;
+  T8Args t;
+  StepBounds bounds;
   const int32_t* ids;
   int32_t* idx;
   float* w;
@@ -298,47 +161,101 @@ struct StepArgs {
   int32_t* inv;
 };
 
-struct VocabSource {
-  const int32_t* ids;
-  const int* bl;
-  int K;
-  __device__ __forceinline__ void operator()(int p, int& e, float& wv) const {
-    e = vocab_owner(ids[p], bl, K);
-    wv = (e >= 0) ? 1.0f : 0.0f;
-  }
+struct StepLds {
+  int gcnt[64];   // adapter counts over all tokens
+  int pcnt[64];   // adapter counts over the tokens before the tile
+  int offs[65];
 };
 
+// Count ids [c0 .. c0 + 512 * kStepIdsPerThread) (held in v) into gcnt and, for tokens below
+// t0, pcnt.  Wave-level match masks make one LDS atomic per group of equal adapters.
+__device__ __forceinline__ void step_count(StepLds& S, const StepBounds& bd, const int (&v)[kStepIdsPerThread],
+                                           int c0, int N, int nbits, int t0) {
+  const int lane = threadIdx.x & 63;
+  const uint64_t lt = lanemask_lt(lane);
+#pragma unroll
+  for (int j = 0; j < kStepIdsPerThread; ++j) {
+    const int t = c0 + j * kT8Threads + threadIdx.x;
+    const int e = t < N ? step_owner(v[j], bd) : -1;
+    const bool valid = e >= 0;
+    const uint64_t m = match_mask(e, valid, nbits);
+    if (valid && (m & lt) == 0) atomicAdd(&S.gcnt[e], __popcll(m));
+    const uint64_t mp = m & __ballot(t < t0);
+    if (valid && t < t0 && (mp & lt) == 0) atomicAdd(&S.pcnt[e], __popcll(mp));
+  }
+}
+
 template <int RB, bool INDIRECT, bool Y0F32, bool YF32>
-__global__ __launch_bounds__(kWaves8 * 64) void step_vocab(StepArgs a) {
-  __shared__ TileLds<RB> L;
-  __shared__ DispatchLds<kStepDispatchThreads> DL;
-  __shared__ int bl[65];
-  const int K = a.t.K, N = a.t.N;
-  bounds_to_lds(a.bounds, bl, K);
-  __syncthreads();
-  if (blockIdx.x == 0) {
-    const VocabSource src{a.ids, bl, K};
-    for (int t = threadIdx.x; t < N; t += kStepDispatchThreads) {
-      int e;
-      float wv;
-      src(t, e, wv);
-      a.idx[t] = e;
-      a.w[t] = wv;
-    }
-    dispatch_block<kStepDispatchThreads>(DL, src, N, K, a.counts, a.offsets, a.perm, a.perm_w, a.inv);
-  }
+__global__ __launch_bounds__(kT8Threads) void step_vocab(StepArgs a) {
+  __shared__ T8Lds<RB> L;
+  __shared__ StepLds S;
   int tt, g;
-  tile_of_block(blockIdx.x, a.t.col_groups, tt, g);
+  t8_tile_of_block(blockIdx.x, a.t, tt, g);
   if (tt >= a.t.tiles) return;
-  const int n = threadIdx.x & 15;
-  const int tok = tt * 16 + n;
-  int es[1] = {-1};
-  float ws[1] = {0.f};
-  if (tok < N) {
-    es[0] = vocab_owner(a.ids[tok], bl, K);
-    ws[0] = (es[0] >= 0) ? 1.0f * a.t.scale : 0.f;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int N = a.t.N, K = a.t.K;
+  const int t0 = tt * kT8Tokens;
+  // small loads first, unconditionally (indices clamped): the tile's ids (positions past N - 1
+  // clone token N - 1), then this thread's share of the first 2048 ids
+  if (threadIdx.x < 64) {
+    S.gcnt[threadIdx.x] = 0;
+    S.pcnt[threadIdx.x] = 0;
   }
-  tile_body<RB, 1, INDIRECT, Y0F32, YF32>(a.t, L, tt, g, es, ws);
+  __syncthreads();  // counters cleared (before any load is in flight, so this costs nothing)
+  const int tok = t0 + lane;
+  const int myid = a.ids[min(tok, N - 1)];
+  int dv[kStepIdsPerThread];
+#pragma unroll
+  for (int j = 0; j < kStepIdsPerThread; ++j) dv[j] = a.ids[min(j * kT8Threads + (int)threadIdx.x, N - 1)];
+  T8Stream<RB, Y0F32> st;
+  t8_prefetch<RB, Y0F32, YF32>(a.t, tt, g, st);
+  const int pe = lane < kT8Tokens ? step_owner(myid, a.bounds) : -1;
+  const float pw = pe >= 0 ? 1.0f * a.t.scale : 0.f;
+  int nbits = 0;
+  while ((1 << nbits) < K) ++nbits;
+  // the dispatch counts run while the first adapter loads are in flight
+  t8_main<RB, INDIRECT, Y0F32, YF32>(a.t, L, st, pe, pw, [&] {
+    step_count(S, a.bounds, dv, 0, N, nbits, t0);
+    for (int c0 = kStepIdsPerThread * kT8Threads; c0 < N; c0 += kStepIdsPerThread * kT8Threads) {
+#pragma unroll
+      for (int j = 0; j < kStepIdsPerThread; ++j) dv[j] = a.ids[min(c0 + j * kT8Threads + (int)threadIdx.x, N - 1)];
+      step_count(S, a.bounds, dv, c0, N, nbits, t0);
+    }
+  });
+
+  // dispatch share: offsets, then this tile's tokens' grouped positions
+  __syncthreads();
+  if (wave == 0) {
+    const int c = lane < K ? S.gcnt[lane] : 0;
+    const int incl = wave_incl_scan(c, lane);
+    if (lane < K) S.offs[lane] = incl - c;
+    if (tt == 0 && g == 0) {
+      if (lane < K) {
+        a.counts[lane] = c;
+        a.offsets[lane + 1] = incl;
+      }
+      if (lane == 0) a.offsets[0] = 0;
+    }
+  }
+  __syncthreads();
+  if (wave == 0 && g == 0) {
+    // the tile's tokens in lanes 0..7: rank among the tile's earlier tokens of the same adapter
+    const bool real = tok < N;
+    const bool valid = real && pe >= 0;
+    const uint64_t m = match_mask(pe, valid, nbits);
+    if (lane < kT8Tokens && real) {
+      a.idx[tok] = pe;
+      a.w[tok] = valid ? 1.0f : 0.0f;
+      if (valid) {
+        const int pos = S.offs[pe] + S.pcnt[pe] + __popcll(m & lanemask_lt(lane));
+        a.inv[tok] = pos;
+        a.perm[pos] = tok;
+        a.perm_w[pos] = 1.0f;
+      } else {
+        a.inv[tok] = -1;
+      }
+    }
+  }
 }
 
 // --------------------------------------------------------------------------------------
@@ -656,7 +573,7 @@ __global__ __launch_bounds__(256) void expand_tokens(ExpandArgs a) {
 int apply_resolve_path(int N, int k, int path, int K, int r_pad) {
   if (path != 0) return path;
   const long long P = (long long)N * k;
-  if (K <= kTileMaxU && r_pad <= 32 && P >= 192) return 3;  // few, small adapters: tile-local grouping
+  if (K <= kT8MaxU && r_pad <= 32 && P >= 192) return 3;  // few, small adapters: tile-local grouping
   if (k == 1) return P >= 192 ? 1 : 2;
   return P >= 1024 ? 1 : 2;
 }
@@ -695,14 +612,25 @@ static int col_groups_for(int requested, long long tiles, int d_out, int target,
   return cg;
 }
 
-static TileArgs tile_args(const ApplyLaunch& a) {
-  TileArgs ta;
-  ta.tgt = a.tgt; ta.x = a.x; ta.y0 = a.y0; ta.y = a.y; ta.offsets = a.offsets; ta.perm_w = a.perm_w;
-  ta.inv = a.inv; ta.N = a.N; ta.K = a.K; ta.k = a.k; ta.scale = a.scale;
-  ta.tiles = (a.N + 15) / 16;
-  ta.col_groups = col_groups_for(a.col_groups, ta.tiles, a.tgt.d_out, 256, kWaves8);
-  ta.tiles_per_xcd = (ta.tiles + 7) / 8;
-  return ta;
+// Column groups of the 8-token tiles: more workgroups while there are fewer tiles than compute
+// units, as long as every wave of a group keeps a 256-column unit.
+static int t8_col_groups(int requested, long long tiles, int d_out) {
+  const int nblk = d_out / kColBlock;
+  int cg = requested > 0 ? requested : env_int("MOLORA_APPLY_COLGROUPS", 0);
+  if (cg > 0 && nblk % cg == 0) return cg;
+  cg = 1;
+  while (tiles * cg < 256 && nblk % (2 * cg) == 0 && nblk / (2 * cg) >= 2 * kT8Waves) cg *= 2;
+  return cg;
+}
+
+static T8Args t8_args(const ApplyLaunch& a) {
+  T8Args t;
+  t.tgt = a.tgt; t.x = a.x; t.y0 = a.y0; t.y = a.y;
+  t.N = a.N; t.K = a.K; t.k = a.k; t.scale = a.scale;
+  t.tiles = (a.N + kT8Tokens - 1) / kT8Tokens;
+  t.col_groups = t8_col_groups(a.col_groups, t.tiles, a.tgt.d_out);
+  t.tiles_per_xcd = (t.tiles + 7) / 8;
+  return t;
 }
 
 template <int RB, bool IND, bool Y0F, bool YF>
@@ -720,14 +648,14 @@ static hipError_t launch_expand_k1_t(const ExpandArgs& ea, int grid, hipStream_t
   hipLaunchKernelGGL((expand_grouped_k1<RB, IND, Y0F, YF>), dim3(grid), dim3(256), 0, s, ea);
   return hipGetLastError();
 }
-template <int RB, int KM, bool IND, bool Y0F, bool YF>
-static hipError_t launch_tile_t(const TileArgs& ta, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((apply_tile<RB, KM, IND, Y0F, YF>), dim3(grid), dim3(kWaves8 * 64), 0, s, ta);
+template <int RB, bool IND, bool Y0F, bool YF>
+static hipError_t launch_t8_t(const T8ApplyArgs& ta, int grid, hipStream_t s) {
+  hipLaunchKernelGGL((apply_t8<RB, IND, Y0F, YF>), dim3(grid), dim3(kT8Threads), 0, s, ta);
   return hipGetLastError();
 }
 template <int RB, bool IND, bool Y0F, bool YF>
 static hipError_t launch_step_t(const StepArgs& sa, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((step_vocab<RB, IND, Y0F, YF>), dim3(grid), dim3(kWaves8 * 64), 0, s, sa);
+  hipLaunchKernelGGL((step_vocab<RB, IND, Y0F, YF>), dim3(grid), dim3(kT8Threads), 0, s, sa);
   return hipGetLastError();
 }
 template <int RB, int KM, bool IND, bool Y0F, bool YF>
@@ -756,16 +684,12 @@ hipError_t launch_apply(const ApplyLaunch& a, hipStream_t s) {
   hipError_t err = hipSuccess;
 
   if (a.path == 3) {
-    const TileArgs ta = tile_args(a);
-    const int grid = 8 * ta.tiles_per_xcd * ta.col_groups;
-#define MOLORA_TILE(KM)                                                                                \
-  MOLORA_DISPATCH_RB(RBv, MOLORA_DISPATCH_BOOL(a.indirect, IND, MOLORA_DISPATCH_BOOL(a.y0_f32, Y0F,  \
-      MOLORA_DISPATCH_BOOL(a.y_f32, YF, err = (launch_tile_t<RB, KM, IND, Y0F, YF>(ta, grid, s))))))
-    if (a.k == 1) { MOLORA_TILE(1) }
-    else if (a.k <= 2) { MOLORA_TILE(2) }
-    else if (a.k <= 4) { MOLORA_TILE(4) }
-    else { MOLORA_TILE(8) }
-#undef MOLORA_TILE
+    T8ApplyArgs ta;
+    ta.t = t8_args(a);
+    ta.offsets = a.offsets; ta.perm_w = a.perm_w; ta.inv = a.inv;
+    const int grid = 8 * ta.t.tiles_per_xcd * ta.t.col_groups;
+    MOLORA_DISPATCH_RB(RBv, MOLORA_DISPATCH_BOOL(a.indirect, IND, MOLORA_DISPATCH_BOOL(a.y0_f32, Y0F,
+        MOLORA_DISPATCH_BOOL(a.y_f32, YF, err = (launch_t8_t<RB, IND, Y0F, YF>(ta, grid, s))))));
     return err;
   }
 
@@ -818,10 +742,15 @@ hipError_t launch_apply(const ApplyLaunch& a, hipStream_t s) {
   return err;
 }
 
+bool step_vocab_fused(int N) { return N <= kStepMaxN; }
+
 hipError_t launch_step_vocab(const StepVocabLaunch& a, hipStream_t s) {
   StepArgs sa;
-  sa.t = tile_args(a.apply);
-  sa.bounds = a.bounds;
+  sa.t = t8_args(a.apply);
+  const int K = a.apply.K;
+  sa.bounds.lo = a.bounds.b[0];
+  sa.bounds.hi = a.bounds.b[K];
+  for (int i = 0; i < kT8MaxU - 1; ++i) sa.bounds.mid[i] = (i + 1 < K) ? a.bounds.b[i + 1] : INT_MAX;
   sa.ids = a.ids; sa.idx = a.idx; sa.w = a.w; sa.counts = a.counts; sa.offsets = a.offsets; sa.perm = a.perm;
   sa.perm_w = a.perm_w; sa.inv = a.inv;
   const int grid = 8 * sa.t.tiles_per_xcd * sa.t.col_groups;

@@ -378,7 +378,14 @@ int molora_step_vocab(const molora_hotset* hs, int target, const int32_t* ids, i
   st.perm = perm;
   st.perm_w = perm_w;
   st.inv = inv;
-  const hipError_t e = molora::launch_step_vocab(st, reinterpret_cast<hipStream_t>(stream));
+  const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (molora::step_vocab_fused(N)) {
+    const hipError_t e = molora::launch_step_vocab(st, s);
+    return e == hipSuccess ? ok() : hip_fail(e, "step launch");
+  }
+  hipError_t e = molora::launch_route_vocab(ids, N, st.bounds, hs->K, idx, w, s);
+  if (e == hipSuccess) e = molora::launch_dispatch(idx, w, N, hs->K, counts, offsets, perm, perm_w, inv, s);
+  if (e == hipSuccess) e = molora::launch_apply(a, s);
   return e == hipSuccess ? ok() : hip_fail(e, "step launch");
 }
 

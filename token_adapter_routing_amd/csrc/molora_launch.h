@@ -70,6 +70,9 @@ struct StepVocabLaunch {
   float* perm_w;
   int32_t* inv;
 };
+// True when the one-launch step handles N tokens (its per-workgroup dispatch share reads all N
+// ids); larger batches run route, dispatch and the tile apply as three launches.
+bool step_vocab_fused(int N);
 hipError_t launch_step_vocab(const StepVocabLaunch& a, hipStream_t s);
 
 hipError_t launch_seqpass_meta(const int32_t* idx, int N, int K, int32_t* offsets, int32_t* perm,
