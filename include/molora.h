@@ -53,7 +53,8 @@ enum {
 };
 
 enum { MOLORA_LAYOUT_DIRECT = 0, MOLORA_LAYOUT_INDIRECT = 1 };
-enum { MOLORA_PATH_AUTO = 0, MOLORA_PATH_GROUPED = 1, MOLORA_PATH_SKINNY = 2, MOLORA_PATH_TILE = 3 };
+enum { MOLORA_PATH_AUTO = 0, MOLORA_PATH_GROUPED = 1, MOLORA_PATH_SKINNY = 2, MOLORA_PATH_TILE = 3,
+       MOLORA_PATH_BLOCK = 4 };
 enum { MOLORA_BF16 = 0, MOLORA_F32 = 1 };
 
 /* Limits of this build. */
@@ -197,9 +198,15 @@ int molora_dispatch(const int32_t *idx, const float *w, int N, int k, int K,
  *   path    MOLORA_PATH_AUTO (chosen on the host from N*k, K and r),
  *           _GROUPED (MFMA tiles of 16 grouped rows of one adapter),
  *           _SKINNY (the grouped shrink split over d_in, for small batches), or
- *           _TILE (16 consecutive tokens per tile, grouped by adapter inside the
- *           tile; needs K <= 16)
- *   ws      device workspace of at least molora_apply_workspace() bytes
+ *           _TILE (8 consecutive tokens per workgroup, every adapter the tile
+ *           uses applied in turn; needs K <= 16), or
+ *           _BLOCK (64 consecutive tokens per block, two launches: the shrink
+ *           split over workgroups by 512-wide slices of d_in, writing partial
+ *           sums to the workspace, then the expand split by 512-wide slices of
+ *           d_out; needs K <= 16 and r <= 32)
+ *   ws      device workspace of at least molora_apply_workspace() bytes (no
+ *           initial contents needed); calls that share a workspace must not
+ *           run concurrently
  * Accumulation is fp32; the shrink result h stays fp32 and enters the
  * expand as a bf16 hi/lo pair, so bf16 rounding happens only at the store
  * of y when y_dtype is MOLORA_BF16 (round to nearest even).
@@ -216,21 +223,26 @@ int molora_apply(const molora_hotset *hs, int target, const void *x, const void 
  * routing decision, histogram, pointer arrays and grouped dispatch; Figure 2:
  * per-token weighted sum; Table 4 "Per-token + Graph": the step as few
  * launches as possible).  Equivalent to molora_route_vocab, molora_dispatch
- * and molora_apply(MOLORA_PATH_TILE) with k = 1, producing bit-identical
- * idx, w, counts, offsets, perm, perm_w, inv and y.  Workgroup 0 also runs the
- * dispatch; every tile routes its own tokens from their ids, so no workgroup
- * waits for another.
+ * and molora_apply with k = 1, producing bit-identical idx, w, counts,
+ * offsets, perm, perm_w, inv and y: with a workspace of
+ * molora_step_workspace() bytes the apply is MOLORA_PATH_BLOCK (a shrink
+ * launch and an expand launch), without one (ws NULL) MOLORA_PATH_TILE (one
+ * launch).  Every workgroup routes its own tokens from their ids and derives
+ * its share of the dispatch outputs by counting all N ids.  Batches above
+ * 4096 tokens run route, dispatch and apply as separate launches.
  *   hs, target    hot set with K = hs->K adapters (K <= 16) and the projection
  *   ids, bounds   as molora_route_vocab (bounds: host int32 [K+1])
  *   x, y0, y      as molora_apply (y0 may equal y)
  *   idx, w        device [N] out, as molora_route_vocab
  *   counts..inv   device out, as molora_dispatch with k = 1 (inv required)
+ *   ws            NULL, or device workspace of molora_step_workspace() bytes
  * ------------------------------------------------------------------------ */
+int molora_step_workspace(const molora_hotset *hs, int target, int N, size_t *bytes);
 int molora_step_vocab(const molora_hotset *hs, int target, const int32_t *ids, int N,
                       const int32_t *bounds, const void *x, const void *y0, int y0_dtype,
                       void *y, int y_dtype, int32_t *idx, float *w, int32_t *counts,
                       int32_t *offsets, int32_t *perm, float *perm_w, int32_t *inv,
-                      void *stream);
+                      void *ws, size_t ws_bytes, void *stream);
 
 /* ------------------------------------------------------------------------
  * Per-sequence comparator metadata (thelatestinai.com, Table 3: per-sequence

@@ -48,7 +48,7 @@ def test_tiny_vocab_pipeline(layout, y_dtype):
         check_bf16_output(host(y), ref)
 
 
-@pytest.mark.parametrize("path", [1, 2, 3])
+@pytest.mark.parametrize("path", [1, 2, 3, 4])
 def test_modality4_full_size(path):
     m = need_gpu()
     c = synth.modality4()
@@ -107,7 +107,7 @@ def test_small_integers_bit_exact():
     for layout in (0, 1):
         hs = m.molora_hotset_init([(dev_bf16(Ab), dev_bf16(Bb))], 2.0, layout=layout)
         counts, offsets, perm, perm_w, inv = m.molora_dispatch(dev(idx), dev(w), K, 1)
-        for path in (1, 2, 3):
+        for path in (1, 2, 3, 4):
             y = m.molora_apply(hs, dev_bf16(xb), dev_bf16(yb).float(), offsets, perm, perm_w, inv, k=1,
                                y_dtype=torch.float32, path=path)
             ref = oracle_from_gpu_routing(tg, 2.0, idx, w, K, 1)
@@ -130,11 +130,13 @@ SHAPES = [
 
 
 @pytest.mark.parametrize("N,d_in,d_out,K,r,k", SHAPES)
-@pytest.mark.parametrize("path", [1, 2, 3])
+@pytest.mark.parametrize("path", [1, 2, 3, 4])
 def test_apply_shapes_paths(N, d_in, d_out, K, r, k, path):
     m = need_gpu()
-    if path == 3 and K > 16:
-        pytest.skip("the tile path takes K <= 16")
+    if path in (3, 4) and K > 16:
+        pytest.skip("the tile and block paths take K <= 16")
+    if path == 4 and r > 32:
+        pytest.skip("the block path takes r <= 32")
     g = np.random.default_rng(N * 31 + d_in + K * 7 + r + k)
     xb = synth.to_bf16_bits(g.standard_normal((N, d_in)).astype(np.float32))
     Ab = synth.to_bf16_bits((g.standard_normal((K, d_in, r)) / np.sqrt(d_in)).astype(np.float32))
@@ -233,7 +235,8 @@ def test_stress_full_size(k):
     check_float_output(host(y)[rows], ref, f64(t.y0[rows]))
 
 
-def test_graph_replay_matches_eager():
+@pytest.mark.parametrize("path", [0, 4])
+def test_graph_replay_matches_eager(path):
     """The vocab step captured in a HIP graph, replayed with eager work in between."""
     m = need_gpu()
     c = synth.modality4()
@@ -247,11 +250,13 @@ def test_graph_replay_matches_eager():
             torch.empty(c.N, dtype=torch.int32, device="cuda"), torch.empty(c.N, dtype=torch.float32, device="cuda"),
             torch.empty(c.N, dtype=torch.int32, device="cuda"))
     y = torch.empty(c.N, t.d_out, dtype=torch.bfloat16, device="cuda")
+    need = m.molora_apply_workspace(hs, 0, c.N, 1, path)
+    ws = torch.zeros(max(need, 1), dtype=torch.uint8, device="cuda")
 
     def step():
         m.molora_route_vocab(ids, c.bounds.tolist(), idx=idx, w=w)
         m.molora_dispatch(idx, w, c.K, 1, out=meta)
-        m.molora_apply(hs, x, y0, meta[1], meta[2], meta[3], meta[4], k=1, y=y)
+        m.molora_apply(hs, x, y0, meta[1], meta[2], meta[3], meta[4], k=1, y=y, path=path, ws=ws)
 
     step()
     torch.cuda.synchronize()

@@ -10,12 +10,20 @@ from tests.gpu_util import check_bf16_output, check_float_output, dev, dev_bf16,
 pytestmark = pytest.mark.gpu
 
 
-def three_calls(m, hs, ids, bounds, K, x, y0, y_dtype):
+def three_calls(m, hs, ids, bounds, K, x, y0, y_dtype, path):
     idx, w = m.molora_route_vocab(ids, bounds)
     meta = m.molora_dispatch(idx, w, K, 1)
     counts, offsets, perm, perm_w, inv = meta
-    y = m.molora_apply(hs, x, y0, offsets, perm, perm_w, inv, k=1, y_dtype=y_dtype, path=m.PATH_TILE)
+    y = m.molora_apply(hs, x, y0, offsets, perm, perm_w, inv, k=1, y_dtype=y_dtype, path=path)
     return y, (idx, w), meta
+
+
+def step_ws(m, hs, N, block):
+    """A step workspace (block apply), or None (tile apply); filled with NaN bytes, so that a
+    partial sum read before it is written would show."""
+    if not block:
+        return None
+    return torch.full((m.molora_step_workspace(hs, 0, N),), 0xFF, dtype=torch.uint8, device="cuda")
 
 
 def cases():
@@ -28,18 +36,19 @@ def cases():
     return [("tiny", tiny), ("modality4", mod), ("ragged_unrouted", odd)]
 
 
+@pytest.mark.parametrize("block", [False, True])
 @pytest.mark.parametrize("layout", [0, 1])
 @pytest.mark.parametrize("y_dtype", [torch.bfloat16, torch.float32])
 @pytest.mark.parametrize("name,case", cases())
-def test_step_equals_three_calls_and_oracle(name, case, y_dtype, layout):
+def test_step_equals_three_calls_and_oracle(name, case, y_dtype, layout, block):
     m = need_gpu()
     t = case.targets[0]
     hs = m.molora_hotset_init([(dev_bf16(t.A), dev_bf16(t.B))], case.scale, layout=layout)
     ids = dev(case.ids)
     bounds = case.bounds.tolist()
     x, y0 = dev_bf16(t.x), dev_bf16(t.y0)
-    y1, r1, m1 = m.molora_step_vocab(hs, ids, bounds, x, y0, y_dtype=y_dtype)
-    y3, r3, m3 = three_calls(m, hs, ids, bounds, case.K, x, y0, y_dtype)
+    y1, r1, m1 = m.molora_step_vocab(hs, ids, bounds, x, y0, y_dtype=y_dtype, ws=step_ws(m, hs, case.N, block))
+    y3, r3, m3 = three_calls(m, hs, ids, bounds, case.K, x, y0, y_dtype, m.PATH_BLOCK if block else m.PATH_TILE)
     N = case.N
     np.testing.assert_array_equal(host(r1[0])[:N], host(r3[0]))
     np.testing.assert_array_equal(host(r1[1])[:N], host(r3[1]))
@@ -103,3 +112,55 @@ def test_step_in_place_and_graph_replay():
         np.testing.assert_array_equal(host(out), host(y_ref))
         ri, rw = route_vocab(c.ids, c.bounds)
         np.testing.assert_array_equal(host(meta[2]), dispatch(ri, rw, c.K)[2])
+
+
+def test_block_step_reuses_workspace_across_inputs_and_graph_replays():
+    """One step workspace across different batches and across graph replays: every result
+    matches the oracle (no partial sums left over from an earlier call)."""
+    m = need_gpu()
+    cases_ = [synth.modality4(),
+              synth.vocab_case(N=2048, d=4096, K=4, r=16, case_id=23, runs=True, probs=(0.25, 0.25, 0.25, 0.25))]
+    t0 = cases_[0].targets[0]
+    hs = m.molora_hotset_init([(dev_bf16(t0.A), dev_bf16(t0.B))], cases_[0].scale)
+    ws = step_ws(m, hs, 2048, True)
+    for case in cases_:
+        t = case.targets[0]
+        ids = dev(case.ids)
+        y, r, meta = m.molora_step_vocab(hs, ids, case.bounds.tolist(), dev_bf16(t.x), dev_bf16(t.y0),
+                                         y_dtype=torch.float32, ws=ws)
+        torch.cuda.synchronize()
+        ri, rw = route_vocab(case.ids, case.bounds)
+        oc, oo, op, opw, oinv = dispatch(ri, rw, case.K)
+        ref = apply(f64(t.y0), f64(t.x), f64(t0.A), f64(t0.B), case.scale, op, opw, oo, 1)
+        check_float_output(host(y), ref, f64(t.y0))
+    # graph replays, eager work between them
+    case = cases_[0]
+    t = case.targets[0]
+    ids, x, y0 = dev(case.ids), dev_bf16(t.x), dev_bf16(t.y0)
+    y = torch.empty(case.N, t.d_out, dtype=torch.bfloat16, device="cuda")
+    route = (torch.empty(case.N, dtype=torch.int32, device="cuda"), torch.empty(case.N, dtype=torch.float32, device="cuda"))
+    meta = (torch.empty(case.K, dtype=torch.int32, device="cuda"), torch.empty(case.K + 1, dtype=torch.int32, device="cuda"),
+            torch.empty(case.N, dtype=torch.int32, device="cuda"), torch.empty(case.N, dtype=torch.float32, device="cuda"),
+            torch.empty(case.N, dtype=torch.int32, device="cuda"))
+
+    def step():
+        m.molora_step_vocab(hs, ids, case.bounds.tolist(), x, y0, y=y, route=route, meta=meta, ws=ws)
+
+    step()
+    torch.cuda.synchronize()
+    eager = host(y).copy()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(4):
+        y.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(host(y), eager)

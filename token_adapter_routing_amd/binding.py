@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_PKG, "libmolora.so")
 
 MOLORA_OK, MOLORA_EINVAL, MOLORA_ENOTSUP, MOLORA_ENOSPC, MOLORA_EHIP = range(5)
 LAYOUT_DIRECT, LAYOUT_INDIRECT = 0, 1
-PATH_AUTO, PATH_GROUPED, PATH_SKINNY, PATH_TILE = 0, 1, 2, 3
+PATH_AUTO, PATH_GROUPED, PATH_SKINNY, PATH_TILE, PATH_BLOCK = 0, 1, 2, 3, 4
 BF16, F32 = 0, 1
 
 _c_p = ctypes.c_void_p
@@ -51,8 +51,10 @@ _SIGS = {
     "molora_apply": (_c_i, [_c_p, _c_i, _c_p, _c_p, _c_i, _c_p, _c_i, _c_i, _c_i, _c_p, _c_p, _c_p, _c_p, _c_i,
                             _c_p, _c_sz, _c_p]),
     "molora_seqpass_meta": (_c_i, [_c_p, _c_i, _c_i, _c_p, _c_p, _c_p, _c_p]),
-    "molora_step_vocab": (_c_i, [_c_p, _c_i, _c_p, _c_i, _c_p, _c_p, _c_p, _c_i, _c_p, _c_i, _c_p, _c_p, _c_p, _c_p,
-                                 _c_p, _c_p, _c_p, _c_p]),
+    "molora_step_vocab": (_c_i, [_c_p, _c_i, _c_p, _c_i, _c_p, _c_p, _c_p, _c_i, _c_p, _c_i,  # hs .. y_dtype
+                                 _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p,  # idx, w, counts, offsets, perm, perm_w, inv
+                                 _c_p, _c_sz, _c_p]),  # ws, ws_bytes, stream
+    "molora_step_workspace": (_c_i, [_c_p, _c_i, _c_i, ctypes.POINTER(_c_sz)]),
 }
 
 _lib = None
@@ -270,7 +272,8 @@ def molora_apply(hs: HotSet, x: torch.Tensor, y0: torch.Tensor, offsets: torch.T
         y = torch.empty(N, d_out, dtype=y_dtype or y0.dtype, device=x.device)
     need = molora_apply_workspace(hs, target, N, k, path)
     if need and (ws is None or ws.numel() < need):
-        ws = torch.empty(need, dtype=torch.uint8, device=x.device)
+        # zero-filled: the block path keeps control words at the start that must begin at zero
+        ws = torch.zeros(need, dtype=torch.uint8, device=x.device)
     _check(load_library().molora_apply(
         hs.handle, target, _ptr(x, torch.bfloat16, "x"), _ptr(y0, None, "y0"), _dtype_code(y0), _ptr(y, None, "y"),
         _dtype_code(y), N, k, _ptr(offsets, torch.int32, "offsets"), _ptr(perm, torch.int32, "perm"),
@@ -279,11 +282,19 @@ def molora_apply(hs: HotSet, x: torch.Tensor, y0: torch.Tensor, offsets: torch.T
     return y
 
 
+def molora_step_workspace(hs: HotSet, target: int, N: int) -> int:
+    out = _c_sz()
+    _check(load_library().molora_step_workspace(hs.handle, target, N, ctypes.byref(out)))
+    return out.value
+
+
 def molora_step_vocab(hs: HotSet, ids: torch.Tensor, bounds: Sequence[int], x: torch.Tensor, y0: torch.Tensor,
                       target: int = 0, y: Optional[torch.Tensor] = None, y_dtype=None, route=None, meta=None,
-                      stream=None):
+                      ws: Optional[torch.Tensor] = None, stream=None):
     """One launch of route_vocab + dispatch + apply (k = 1).  Returns (y, (idx, w),
-    (counts, offsets, perm, perm_w, inv)); `route` and `meta` may supply those buffers."""
+    (counts, offsets, perm, perm_w, inv)); `route` and `meta` may supply those buffers.
+    `ws` (uint8, zero-filled, at least molora_step_workspace bytes) selects the block apply;
+    without it the tile apply runs."""
     N = ids.numel()
     K = len(bounds) - 1
     dev = ids.device
@@ -304,7 +315,7 @@ def molora_step_vocab(hs: HotSet, ids: torch.Tensor, bounds: Sequence[int], x: t
         _ptr(y0, None, "y0"), _dtype_code(y0), _ptr(y, None, "y"), _dtype_code(y), _ptr(idx, torch.int32, "idx"),
         _ptr(w, torch.float32, "w"), _ptr(counts, torch.int32, "counts"), _ptr(offsets, torch.int32, "offsets"),
         _ptr(perm, torch.int32, "perm"), _ptr(perm_w, torch.float32, "perm_w"), _ptr(inv, torch.int32, "inv"),
-        _stream(stream)))
+        _ptr(ws, None, "ws") if ws is not None else None, ws.numel() if ws is not None else 0, _stream(stream)))
     return y, route, meta
 
 

@@ -33,6 +33,7 @@
 #include "molora_launch.h"
 #include "molora_mfma.h"
 #include "tile8_dev.h"
+#include "block_dev.h"
 
 namespace molora {
 
@@ -256,6 +257,129 @@ __global__ __launch_bounds__(kT8Threads) void step_vocab(StepArgs a) {
       }
     }
   }
+}
+
+// --------------------------------------------------------------------------------------
+// 64-token blocks, shrink launch then expand launch (any k, K <= 16, r <= 32): routing from
+// the dispatch outputs.  Lane i of a wave holds offsets[i]; the adapter of grouped position q
+// is the number of segment starts offsets[1 .. K-1] at or below q.
+struct BlockApplyArgs {
+  BlockArgs b;
+  const int32_t* offsets;
+  const float* perm_w;
+  const int32_t* inv;
+};
+
+struct DispatchRoute {
+  const int32_t* inv;
+  const float* perm_w;
+  int k, K;
+  float scale;
+  int ov;  // offsets[lane]
+  __device__ __forceinline__ int operator()(int t, int s, float& w) const {
+    const int q = inv[(long long)t * k + s];
+    int seg = 0;
+    for (int i = 1; i < K; ++i) seg += (__shfl(ov, i, kWave) <= q) ? 1 : 0;
+    w = q >= 0 ? perm_w[q] * scale : 0.f;
+    return q >= 0 ? seg : -1;
+  }
+};
+
+template <int RB, bool INDIRECT>
+__global__ __launch_bounds__(kBThreads, 2) void shrink_block(BlockApplyArgs a) {
+  __shared__ BlockLds<RB> L;
+  const int lane = threadIdx.x & 63;
+  const DispatchRoute rt{a.inv, a.perm_w, a.b.k, a.b.K, a.b.scale, a.offsets[min(lane, a.b.K)]};
+  block_shrink<RB, INDIRECT>(a.b, L, rt, blockIdx.x / a.b.kslices, blockIdx.x % a.b.kslices);
+}
+
+template <int RB, bool INDIRECT, bool Y0F32, bool YF32>
+__global__ __launch_bounds__(kBThreads, 2) void expand_block(BlockApplyArgs a) {
+  __shared__ BlockLds<RB> L;
+  const int lane = threadIdx.x & 63;
+  const DispatchRoute rt{a.inv, a.perm_w, a.b.k, a.b.K, a.b.scale, a.offsets[min(lane, a.b.K)]};
+  block_expand<RB, INDIRECT, Y0F32, YF32>(a.b, L, rt, blockIdx.x / a.b.cslices, blockIdx.x % a.b.cslices, [] {});
+}
+
+// The vocabulary-routed step on 64-token blocks (k = 1), as two launches: the shrink routes
+// its block from the ids; the expand does too, and its workgroups of column slice 0 write their
+// block's share of the dispatch outputs (adapter counts over all N ids and over the ids before
+// the block give the offsets and each token's grouped position).
+struct VocabRoute {
+  const int32_t* ids;
+  StepBounds bd;
+  float scale;
+  __device__ __forceinline__ int operator()(int t, int s, float& w) const {
+    (void)s;
+    const int e = step_owner(ids[t], bd);
+    w = e >= 0 ? scale : 0.f;
+    return e;
+  }
+};
+
+template <int RB, bool INDIRECT>
+__global__ __launch_bounds__(kBThreads, 2) void step_shrink_block(StepArgs a, BlockArgs b) {
+  __shared__ BlockLds<RB> L;
+  const VocabRoute rt{a.ids, a.bounds, b.scale};
+  block_shrink<RB, INDIRECT>(b, L, rt, blockIdx.x / b.kslices, blockIdx.x % b.kslices);
+}
+
+template <int RB, bool INDIRECT, bool Y0F32, bool YF32>
+__global__ __launch_bounds__(kBThreads, 2) void step_expand_block(StepArgs a, BlockArgs b) {
+  __shared__ BlockLds<RB> L;
+  __shared__ StepLds S;
+  const VocabRoute rt{a.ids, a.bounds, b.scale};
+  const int tb = blockIdx.x / b.cslices, cs = blockIdx.x % b.cslices;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int N = b.N, K = b.K, t0 = tb * kBTok;
+  block_expand<RB, INDIRECT, Y0F32, YF32>(b, L, rt, tb, cs, [&] {
+    if (cs != 0) return;
+    if (threadIdx.x < 64) {
+      S.gcnt[threadIdx.x] = 0;
+      S.pcnt[threadIdx.x] = 0;
+    }
+    __syncthreads();
+    int nbits = 0;
+    while ((1 << nbits) < K) ++nbits;
+    int dv[kStepIdsPerThread];
+    for (int c0 = 0; c0 < N; c0 += kStepIdsPerThread * kT8Threads) {
+#pragma unroll
+      for (int j = 0; j < kStepIdsPerThread; ++j) dv[j] = a.ids[min(c0 + j * kT8Threads + (int)threadIdx.x, N - 1)];
+      step_count(S, a.bounds, dv, c0, N, nbits, t0);
+    }
+    __syncthreads();
+    if (wave == 0) {
+      const int c = lane < K ? S.gcnt[lane] : 0;
+      const int incl = wave_incl_scan(c, lane);
+      if (lane < K) S.offs[lane] = incl - c;
+      if (tb == 0) {
+        if (lane < K) {
+          a.counts[lane] = c;
+          a.offsets[lane + 1] = incl;
+        }
+        if (lane == 0) a.offsets[0] = 0;
+      }
+      // the block's tokens, one per lane: rank among the block's earlier tokens of the adapter
+      const int tok = t0 + lane;
+      const bool real = tok < N;
+      float w;
+      const int pe = rt(min(tok, N - 1), 0, w);
+      const bool valid = real && pe >= 0;
+      const uint64_t m = match_mask(pe, valid, nbits);
+      if (real) {
+        a.idx[tok] = pe;
+        a.w[tok] = valid ? 1.0f : 0.0f;
+        if (valid) {
+          const int pos = S.offs[pe] + S.pcnt[pe] + __popcll(m & lanemask_lt(lane));
+          a.inv[tok] = pos;
+          a.perm[pos] = tok;
+          a.perm_w[pos] = 1.0f;
+        } else {
+          a.inv[tok] = -1;
+        }
+      }
+    }
+  });
 }
 
 // --------------------------------------------------------------------------------------
@@ -586,8 +710,19 @@ static int skinny_splits(int d_in) {
   return ns;
 }
 
+// Block path workspace: the partial sums of the shrink launch.
+static size_t block_ws(int N, int k, int K, int r_pad, int d_in) {
+  const int nblocks = (N + kBTok - 1) / kBTok;
+  const int kslices = (d_in + kBSlice - 1) / kBSlice;
+  const int slotmax = std::min(K, kBTok * k);
+  return block_part_floats(nblocks, slotmax, kslices, r_pad) * sizeof(float);
+}
+
+size_t step_ws_bytes(int N, int K, int r_pad, int d_in) { return block_ws(N, 1, K, r_pad, d_in); }
+
 size_t apply_ws_bytes(int N, int k, int K, int r_pad, int d_in, int path) {
   const int p = apply_resolve_path(N, k, path, K, r_pad);
+  if (p == 4) return block_ws(N, k, K, r_pad, d_in);
   if (p == 3 || (k == 1 && p == 1)) return 0;
   const int ns = (p == 2) ? skinny_splits(d_in) : 1;
   return (size_t)ns * (size_t)N * (size_t)k * (size_t)r_pad * sizeof(float);
@@ -623,6 +758,18 @@ static int t8_col_groups(int requested, long long tiles, int d_out) {
   return cg;
 }
 
+static BlockArgs block_args(const ApplyLaunch& a, void* ws) {
+  BlockArgs b;
+  b.tgt = a.tgt; b.x = a.x; b.y0 = a.y0; b.y = a.y;
+  b.N = a.N; b.K = a.K; b.k = a.k; b.scale = a.scale;
+  b.nblocks = (a.N + kBTok - 1) / kBTok;
+  b.kslices = (a.tgt.d_in + kBSlice - 1) / kBSlice;
+  b.cslices = (a.tgt.d_out + kBSlice - 1) / kBSlice;
+  b.slotmax = std::min(a.K, kBTok * a.k);
+  b.part = reinterpret_cast<float*>(ws);
+  return b;
+}
+
 static T8Args t8_args(const ApplyLaunch& a) {
   T8Args t;
   t.tgt = a.tgt; t.x = a.x; t.y0 = a.y0; t.y = a.y;
@@ -654,6 +801,22 @@ static hipError_t launch_t8_t(const T8ApplyArgs& ta, int grid, hipStream_t s) {
   return hipGetLastError();
 }
 template <int RB, bool IND, bool Y0F, bool YF>
+static hipError_t launch_block_t(const BlockApplyArgs& ba, hipStream_t s) {
+  hipLaunchKernelGGL((shrink_block<RB, IND>), dim3(ba.b.nblocks * ba.b.kslices), dim3(kBThreads), 0, s, ba);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((expand_block<RB, IND, Y0F, YF>), dim3(ba.b.nblocks * ba.b.cslices), dim3(kBThreads), 0, s, ba);
+  return hipGetLastError();
+}
+template <int RB, bool IND, bool Y0F, bool YF>
+static hipError_t launch_step_block_t(const StepArgs& sa, const BlockArgs& b, hipStream_t s) {
+  hipLaunchKernelGGL((step_shrink_block<RB, IND>), dim3(b.nblocks * b.kslices), dim3(kBThreads), 0, s, sa, b);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((step_expand_block<RB, IND, Y0F, YF>), dim3(b.nblocks * b.cslices), dim3(kBThreads), 0, s, sa, b);
+  return hipGetLastError();
+}
+template <int RB, bool IND, bool Y0F, bool YF>
 static hipError_t launch_step_t(const StepArgs& sa, int grid, hipStream_t s) {
   hipLaunchKernelGGL((step_vocab<RB, IND, Y0F, YF>), dim3(grid), dim3(kT8Threads), 0, s, sa);
   return hipGetLastError();
@@ -673,6 +836,13 @@ static hipError_t launch_expand_tok_t(const ExpandArgs& ea, int grid, hipStream_
     case 4: { constexpr int RB = 4; __VA_ARGS__; } break; \
     default: return hipErrorInvalidValue;                 \
   }
+// Runtime RB -> instance for the kernels limited to ranks <= 32.
+#define MOLORA_DISPATCH_RB12(RBV, ...)                    \
+  switch (RBV) {                                          \
+    case 1: { constexpr int RB = 1; __VA_ARGS__; } break; \
+    case 2: { constexpr int RB = 2; __VA_ARGS__; } break; \
+    default: return hipErrorInvalidValue;                 \
+  }
 #define MOLORA_DISPATCH_BOOL(V, NAME, ...) \
   if (V) { constexpr bool NAME = true; __VA_ARGS__; } else { constexpr bool NAME = false; __VA_ARGS__; }
 
@@ -690,6 +860,15 @@ hipError_t launch_apply(const ApplyLaunch& a, hipStream_t s) {
     const int grid = 8 * ta.t.tiles_per_xcd * ta.t.col_groups;
     MOLORA_DISPATCH_RB(RBv, MOLORA_DISPATCH_BOOL(a.indirect, IND, MOLORA_DISPATCH_BOOL(a.y0_f32, Y0F,
         MOLORA_DISPATCH_BOOL(a.y_f32, YF, err = (launch_t8_t<RB, IND, Y0F, YF>(ta, grid, s))))));
+    return err;
+  }
+
+  if (a.path == 4) {
+    BlockApplyArgs ba;
+    ba.b = block_args(a, a.ws);
+    ba.offsets = a.offsets; ba.perm_w = a.perm_w; ba.inv = a.inv;
+    MOLORA_DISPATCH_RB12(RBv, MOLORA_DISPATCH_BOOL(a.indirect, IND, MOLORA_DISPATCH_BOOL(a.y0_f32, Y0F,
+        MOLORA_DISPATCH_BOOL(a.y_f32, YF, err = (launch_block_t<RB, IND, Y0F, YF>(ba, s))))));
     return err;
   }
 
@@ -753,9 +932,15 @@ hipError_t launch_step_vocab(const StepVocabLaunch& a, hipStream_t s) {
   for (int i = 0; i < kT8MaxU - 1; ++i) sa.bounds.mid[i] = (i + 1 < K) ? a.bounds.b[i + 1] : INT_MAX;
   sa.ids = a.ids; sa.idx = a.idx; sa.w = a.w; sa.counts = a.counts; sa.offsets = a.offsets; sa.perm = a.perm;
   sa.perm_w = a.perm_w; sa.inv = a.inv;
-  const int grid = 8 * sa.t.tiles_per_xcd * sa.t.col_groups;
   const int RBv = a.apply.tgt.r_pad / 16;
   hipError_t err = hipSuccess;
+  if (a.ws != nullptr) {
+    const BlockArgs b = block_args(a.apply, a.ws);
+    MOLORA_DISPATCH_RB12(RBv, MOLORA_DISPATCH_BOOL(a.apply.indirect, IND, MOLORA_DISPATCH_BOOL(a.apply.y0_f32, Y0F,
+        MOLORA_DISPATCH_BOOL(a.apply.y_f32, YF, err = (launch_step_block_t<RB, IND, Y0F, YF>(sa, b, s))))));
+    return err;
+  }
+  const int grid = 8 * sa.t.tiles_per_xcd * sa.t.col_groups;
   MOLORA_DISPATCH_RB(RBv, MOLORA_DISPATCH_BOOL(a.apply.indirect, IND, MOLORA_DISPATCH_BOOL(a.apply.y0_f32, Y0F,
       MOLORA_DISPATCH_BOOL(a.apply.y_f32, YF, err = (launch_step_t<RB, IND, Y0F, YF>(sa, grid, s))))));
   return err;

@@ -274,7 +274,7 @@ int molora_apply_workspace(const molora_hotset* hs, int target, int N, int k, in
   if (hs == nullptr) return fail(MOLORA_EINVAL, "hot set is NULL");
   if (target < 0 || target >= hs->n_targets) return fail(MOLORA_EINVAL, "target %d outside [0, %d)", target, hs->n_targets);
   if (N < 0 || k < 1 || k > MOLORA_MAX_TOPK || k > hs->K) return fail(MOLORA_EINVAL, "bad N=%d or k=%d", N, k);
-  if (path < MOLORA_PATH_AUTO || path > MOLORA_PATH_TILE) return fail(MOLORA_EINVAL, "unknown path %d", path);
+  if (path < MOLORA_PATH_AUTO || path > MOLORA_PATH_BLOCK) return fail(MOLORA_EINVAL, "unknown path %d", path);
   *bytes = molora::apply_ws_bytes(N, k, hs->K, hs->r_pad, hs->tg[target].d_in, path);
   return ok();
 }
@@ -289,9 +289,10 @@ int molora_apply(const molora_hotset* hs, int target, const void* x, const void*
   if ((long long)N * k >= (1ll << 31)) return fail(MOLORA_ENOTSUP, "N*k too large");
   if ((y0_dtype != MOLORA_BF16 && y0_dtype != MOLORA_F32) || (y_dtype != MOLORA_BF16 && y_dtype != MOLORA_F32))
     return fail(MOLORA_EINVAL, "unknown dtype");
-  if (path < MOLORA_PATH_AUTO || path > MOLORA_PATH_TILE) return fail(MOLORA_EINVAL, "unknown path %d", path);
-  if (path == MOLORA_PATH_TILE && hs->K > molora::kApplyTileMaxAdapters)
-    return fail(MOLORA_ENOTSUP, "the tile path supports K <= %d", molora::kApplyTileMaxAdapters);
+  if (path < MOLORA_PATH_AUTO || path > MOLORA_PATH_BLOCK) return fail(MOLORA_EINVAL, "unknown path %d", path);
+  if ((path == MOLORA_PATH_TILE || path == MOLORA_PATH_BLOCK) && hs->K > molora::kApplyTileMaxAdapters)
+    return fail(MOLORA_ENOTSUP, "the tile and block paths support K <= %d", molora::kApplyTileMaxAdapters);
+  if (path == MOLORA_PATH_BLOCK && hs->r_pad > 32) return fail(MOLORA_ENOTSUP, "the block path supports r <= 32");
   if (y0 == y && y0_dtype != y_dtype) return fail(MOLORA_EINVAL, "in-place apply needs y0_dtype == y_dtype");
   if (N == 0) return ok();
   if (x == nullptr || y0 == nullptr || y == nullptr) return fail(MOLORA_EINVAL, "x, y0 or y is NULL");
@@ -327,9 +328,19 @@ int molora_apply(const molora_hotset* hs, int target, const void* x, const void*
   return e == hipSuccess ? ok() : hip_fail(e, "apply launch");
 }
 
+int molora_step_workspace(const molora_hotset* hs, int target, int N, size_t* bytes) {
+  if (bytes == nullptr) return fail(MOLORA_EINVAL, "bytes is NULL");
+  if (hs == nullptr) return fail(MOLORA_EINVAL, "hot set is NULL");
+  if (target < 0 || target >= hs->n_targets) return fail(MOLORA_EINVAL, "target %d outside [0, %d)", target, hs->n_targets);
+  if (N < 0) return fail(MOLORA_EINVAL, "N=%d < 0", N);
+  *bytes = molora::step_ws_bytes(N, hs->K, hs->r_pad, hs->tg[target].d_in);
+  return ok();
+}
+
 int molora_step_vocab(const molora_hotset* hs, int target, const int32_t* ids, int N, const int32_t* bounds,
                       const void* x, const void* y0, int y0_dtype, void* y, int y_dtype, int32_t* idx, float* w,
-                      int32_t* counts, int32_t* offsets, int32_t* perm, float* perm_w, int32_t* inv, void* stream) {
+                      int32_t* counts, int32_t* offsets, int32_t* perm, float* perm_w, int32_t* inv, void* ws,
+                      size_t ws_bytes, void* stream) {
   if (hs == nullptr) return fail(MOLORA_EINVAL, "hot set is NULL");
   if (target < 0 || target >= hs->n_targets) return fail(MOLORA_EINVAL, "target %d outside [0, %d)", target, hs->n_targets);
   if (N < 0) return fail(MOLORA_EINVAL, "N=%d < 0", N);
@@ -352,6 +363,12 @@ int molora_step_vocab(const molora_hotset* hs, int target, const int32_t* ids, i
   if (!aligned(ids, 4) || !aligned(idx, 4) || !aligned(w, 4) || !aligned(counts, 4) || !aligned(offsets, 4) ||
       !aligned(perm, 4) || !aligned(perm_w, 4) || !aligned(inv, 4))
     return fail(MOLORA_EINVAL, "misaligned pointer");
+  if (ws != nullptr && hs->r_pad > 32) return fail(MOLORA_ENOTSUP, "the block step supports r <= 32 (pass no workspace)");
+  if (ws != nullptr) {
+    const size_t need = molora::step_ws_bytes(N, hs->K, hs->r_pad, hs->tg[target].d_in);
+    if (ws_bytes < need || !aligned(ws, 256))
+      return fail(MOLORA_ENOSPC, "step workspace of %zu bytes (256-byte aligned) needed, %zu given", need, ws_bytes);
+  }
   molora::ApplyLaunch& a = st.apply;
   a.tgt = hs->tg[target];
   a.indirect = hs->layout == MOLORA_LAYOUT_INDIRECT;
@@ -368,8 +385,10 @@ int molora_step_vocab(const molora_hotset* hs, int target, const int32_t* ids, i
   a.perm = perm;
   a.perm_w = perm_w;
   a.inv = inv;
-  a.path = 3;
+  a.path = ws != nullptr ? 4 : 3;
+  a.ws = reinterpret_cast<float*>(ws);
   a.col_groups = 0;
+  st.ws = ws;
   st.ids = ids;
   st.idx = idx;
   st.w = w;

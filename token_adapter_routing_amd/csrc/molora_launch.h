@@ -47,8 +47,8 @@ struct ApplyLaunch {
   const int32_t* perm;
   const float* perm_w;
   const int32_t* inv;
-  int path;          // resolved path (1 GROUPED, 2 SKINNY, 3 TILE)
-  float* ws;         // fp32 workspace (partials of the shrink)
+  int path;          // resolved path (1 GROUPED, 2 SKINNY, 3 TILE, 4 BLOCK)
+  float* ws;         // workspace (partials of the shrink; for BLOCK control words first)
   int col_groups;    // 0 = choose
 };
 
@@ -69,7 +69,10 @@ struct StepVocabLaunch {
   int32_t* perm;
   float* perm_w;
   int32_t* inv;
+  void* ws;           // NULL: tile apply; else the block apply's workspace
 };
+// Workspace bytes of the one-launch step on 64-token blocks.
+size_t step_ws_bytes(int N, int K, int r_pad, int d_in);
 // True when the one-launch step handles N tokens (its per-workgroup dispatch share reads all N
 // ids); larger batches run route, dispatch and the tile apply as three launches.
 bool step_vocab_fused(int N);
