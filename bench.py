@@ -33,7 +33,8 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 KERNEL_SOURCES = ("token_adapter_routing_amd/csrc/apply.hip", "token_adapter_routing_amd/csrc/molora_mfma.h",
                   "token_adapter_routing_amd/csrc/molora_dev.h", "token_adapter_routing_amd/csrc/dispatch_dev.h",
-                  "token_adapter_routing_amd/csrc/tile8_dev.h")
+                  "token_adapter_routing_amd/csrc/tile8_dev.h", "token_adapter_routing_amd/csrc/block_dev.h",
+                  "token_adapter_routing_amd/csrc/gm_dev.h")
 COUNTER_SUMMARY = "step_vocab_modality4.md"
 
 
@@ -75,6 +76,9 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run plain device copies of known size (for HBM counter scaling)")
+    p.add_argument("--rows", default="C0,C2,C3,C4,C4stack",
+                   help="other configurations to measure beside the headline (comma list, or 'none')")
+    p.add_argument("--row-reps", type=int, default=100, help="graph replays per timed row entry")
     return p.parse_args()
 
 
@@ -265,9 +269,305 @@ def main():
         out["per_sequence_comparator"] = {"ms_per_step": seq_ms, "passes": K,
                                           "speedup_per_token": seq_ms / ms_per_step}
 
+    rows = [r for r in args.rows.split(",") if r and r != "none"]
+    if rows:
+        del sets, g_all, g_one
+        torch.cuda.synchronize()
+        out["rows"] = measure_rows(m, torch, dev, rows, args.row_reps)
+
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
     print(json.dumps(out))
+
+
+# ----------------------------------------------------------------------------------------------
+# the other configurations: each step replayed from a HIP graph with inputs resident in HBM
+
+
+def graph_ms(torch, fn, reps, warm=5, inner=1):
+    """Average ms of fn() replayed from one captured graph holding `inner` consecutive calls
+    (fn must only enqueue work); inner > 1 amortises the host cost of a graph launch, which
+    otherwise bounds workloads of a few microseconds."""
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        fn()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for _ in range(inner):
+            fn()
+    with torch.cuda.stream(stream):
+        for _ in range(warm):
+            g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        for _ in range(reps):
+            g.replay()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / (reps * inner), g, stream
+
+
+def measure_rows(m, torch, dev, rows, reps):
+    import synth
+
+    def bf(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    def i32(a):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
+
+    def f32(a):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
+
+    res = {}
+    if "C0" in rows:
+        # tiny vocab case: launch-bound, no roofline claim
+        c = synth.tiny_vocab()
+        t = c.targets[0]
+        hs = m.molora_hotset_init([(bf(t.A), bf(t.B))], c.scale)
+        ids, x, y0 = i32(c.ids), bf(t.x), bf(t.y0)
+        y = torch.empty(c.N, t.d_out, dtype=torch.bfloat16, device=dev)
+        route = (torch.empty(c.N, dtype=torch.int32, device=dev), torch.empty(c.N, dtype=torch.float32, device=dev))
+        meta = (torch.empty(c.K, dtype=torch.int32, device=dev), torch.empty(c.K + 1, dtype=torch.int32, device=dev),
+                torch.empty(c.N, dtype=torch.int32, device=dev), torch.empty(c.N, dtype=torch.float32, device=dev),
+                torch.empty(c.N, dtype=torch.int32, device=dev))
+        ms, _, _ = graph_ms(torch, lambda: m.molora_step_vocab(hs, ids, c.bounds.tolist(), x, y0, y=y, route=route,
+                                                               meta=meta), reps, inner=20)
+        res["C0_tiny_vocab"] = {"workload": "vocab routing N=256 d=512 K=4 r=8 k=1", "us_per_step": ms * 1e3,
+                                "routed_tokens_per_s": c.N / (ms * 1e-3),
+                                "launch": "molora_step_vocab, one launch; 20 steps per graph"}
+        del hs, ids, x, y0, y
+    if "C2" in rows:
+        res["C2_qwen_layer"] = row_qwen_layer(m, torch, dev, bf, f32, reps)
+    if "C3" in rows:
+        res["C3_decode_sweep"] = row_decode(m, torch, dev, bf, i32, reps)
+    if "C4" in rows:
+        res["C4_stress"] = row_stress(m, torch, dev, bf, f32, max(20, reps // 4))
+    if "C4stack" in rows:
+        res["C4_stack"] = row_stack(m, torch, dev)
+    torch.cuda.synchronize()
+    return res
+
+
+def row_qwen_layer(m, torch, dev, bf, f32, reps):
+    """Learned top-k MoLoRA on one Qwen3-1.7B-shaped layer: router MLP (d->64->K, ReLU), top-2,
+    dispatch, then the 7 projections' applies (y = y0 + delta, bf16)."""
+    import synth
+    c = synth.qwen_layer()
+    N, K, k = c.N, c.K, c.k
+    r = c.router
+    xs = {}
+    for t in c.targets:  # q/k/v/gate/up share x
+        key = id(t.x)
+        if key not in xs:
+            xs[key] = bf(t.x)
+    tx = [xs[id(t.x)] for t in c.targets]
+    y0 = [bf(t.y0) for t in c.targets]
+    y = [torch.empty(N, t.d_out, dtype=torch.bfloat16, device=dev) for t in c.targets]
+    hs = m.molora_hotset_init([(bf(t.A), bf(t.B)) for t in c.targets], c.scale)
+    W1 = bf(np.ascontiguousarray(r["W1"].T))
+    W2 = bf(np.ascontiguousarray(r["W2"].T))
+    b1, b2 = f32(r["b1"]), f32(r["b2"])
+    logits = torch.empty(N, K, dtype=torch.float32, device=dev)
+    idx = torch.empty(N * k, dtype=torch.int32, device=dev)
+    w = torch.empty(N * k, dtype=torch.float32, device=dev)
+    flags = torch.empty(N, dtype=torch.uint8, device=dev)
+    meta = (torch.empty(K, dtype=torch.int32, device=dev), torch.empty(K + 1, dtype=torch.int32, device=dev),
+            torch.empty(N * k, dtype=torch.int32, device=dev), torch.empty(N * k, dtype=torch.float32, device=dev),
+            torch.empty(N * k, dtype=torch.int32, device=dev))
+    compulsory = (sum(v.numel() * 2 for v in xs.values()) + sum(2 * N * t.d_out * 2 for t in c.targets)
+                  + sum(K * (t.d_in + t.d_out) * c.r * 2 for t in c.targets)
+                  + (W1.numel() + W2.numel()) * 2 + (b1.numel() + b2.numel()) * 4)
+    d = c.targets[0].d_in
+    flops = sum(N * k * c.r * (t.d_in + t.d_out) * 2 for t in c.targets) + N * (2 * d * 64 + 2 * 64 * K)
+    out = {"workload": "Qwen3-1.7B-shaped layer N=4096 d=2048 7 targets K=4 r=16 k=2, router MLP 2048->64->4",
+           "compulsory_bytes": compulsory, "flops": flops, "paths": {}}
+    for name, path in (("auto", m.PATH_AUTO), ("grouped", m.PATH_GROUPED), ("tile", m.PATH_TILE),
+                       ("block", m.PATH_BLOCK)):
+        wss = [torch.zeros(max(1, m.molora_apply_workspace(hs, ti, N, k, path, torch.bfloat16)), dtype=torch.uint8, device=dev)
+               for ti in range(len(c.targets))]
+
+        def step():
+            m.molora_route_topk(k, K, x=tx[0], W1=W1, b1=b1, W2=W2, b2=b2, logits=logits, idx=idx, w=w, flags=flags)
+            m.molora_dispatch(idx, w, K, k, out=meta)
+            for ti in range(len(c.targets)):
+                m.molora_apply(hs, tx[ti], y0[ti], meta[1], meta[2], meta[3], meta[4], k=k, target=ti, y=y[ti],
+                               path=path, ws=wss[ti])
+
+        ms, g, _ = graph_ms(torch, step, reps)
+        out["paths"][name] = {"ms_per_step": ms, "routed_tokens_per_s": N / (ms * 1e-3),
+                              "pairs_per_s": N * k / (ms * 1e-3),
+                              "roofline_frac": compulsory / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9)}
+        del g, wss
+    best = min(out["paths"].items(), key=lambda kv: kv[1]["ms_per_step"])
+    out["best_path"] = best[0]
+    out["routed_tokens_per_s"] = best[1]["routed_tokens_per_s"]
+    out["roofline_frac"] = best[1]["roofline_frac"]
+    return out
+
+
+def row_decode(m, torch, dev, bf, i32, reps):
+    """Decode sweep: B tokens, 64 hot-set adapters of rank 16, one uniformly random adapter
+    per token (idx given): dispatch + apply, skinny vs grouped; then the slab layouts."""
+    import synth
+    out = {"workload": "decode B in {1,16,64,160,512,2048}, d=4096, K=64 r=16 k=1; 20 steps per graph",
+           "sweep": {}, "layouts": {}}
+    per_adapter = 2 * 4096 * 16 * 2
+    cache = {}
+    for B in (1, 16, 64, 160, 512, 2048):
+        c = synth.decode_batch(B)
+        t = c.targets[0]
+        if "hs" not in cache:
+            cache["hs"] = {lay: m.molora_hotset_init([(bf(t.A), bf(t.B))], c.scale, layout=lay) for lay in (0, 1)}
+        x, y0 = bf(t.x), bf(t.y0)
+        y = torch.empty(B, t.d_out, dtype=torch.bfloat16, device=dev)
+        idx = i32(c.idx)
+        w = torch.ones(B, dtype=torch.float32, device=dev)
+        meta = (torch.empty(c.K, dtype=torch.int32, device=dev), torch.empty(c.K + 1, dtype=torch.int32, device=dev),
+                torch.empty(B, dtype=torch.int32, device=dev), torch.empty(B, dtype=torch.float32, device=dev),
+                torch.empty(B, dtype=torch.int32, device=dev))
+        used = len(np.unique(c.idx))
+        nbytes = B * (t.d_in + 2 * t.d_out) * 2 + used * per_adapter
+        entry = {"distinct_adapters": used, "compulsory_bytes": nbytes}
+        for name, path in (("skinny", m.PATH_SKINNY), ("grouped", m.PATH_GROUPED)):
+            hs = cache["hs"][0]
+            ws = torch.zeros(max(1, m.molora_apply_workspace(hs, 0, B, 1, path, torch.bfloat16)), dtype=torch.uint8, device=dev)
+
+            def step():
+                m.molora_dispatch(idx, w, c.K, 1, out=meta)
+                m.molora_apply(hs, x, y0, meta[1], meta[2], meta[3], meta[4], k=1, y=y, path=path, ws=ws)
+
+            ms, g, _ = graph_ms(torch, step, reps, inner=20)
+            entry[name] = {"us_per_step": ms * 1e3, "GBps": nbytes / (ms * 1e-3) / 1e9}
+            del g
+        entry["auto_path"] = "skinny" if B * 1 < 192 else "grouped"
+        out["sweep"][str(B)] = entry
+    sk = [int(b) for b, e in out["sweep"].items() if e["grouped"]["us_per_step"] < e["skinny"]["us_per_step"]]
+    out["grouped_faster_from_B"] = min(sk) if sk else None
+    # direct vs indirect slab at 4/8/16/32/64 adapters, B = 512, identical operations
+    B = 512
+    for Kh in (4, 8, 16, 32, 64):
+        c = synth.decode_batch(B, K=Kh, case_id=30 + Kh)
+        t = c.targets[0]
+        x, y0 = bf(t.x), bf(t.y0)
+        y = torch.empty(B, t.d_out, dtype=torch.bfloat16, device=dev)
+        idx = i32(c.idx)
+        w = torch.ones(B, dtype=torch.float32, device=dev)
+        meta = m.molora_dispatch(idx, w, Kh, 1)
+        ent = {}
+        for lay, name in ((0, "direct"), (1, "indirect")):
+            hs = m.molora_hotset_init([(bf(t.A), bf(t.B))], c.scale, layout=lay)
+            ms, g, _ = graph_ms(torch, lambda: m.molora_apply(hs, x, y0, meta[1], meta[2], meta[3], meta[4], k=1, y=y),
+                                reps, inner=20)
+            ent[name + "_us"] = ms * 1e3
+            del g, hs
+        ent["indirect_over_direct"] = ent["indirect_us"] / ent["direct_us"]
+        out["layouts"][str(Kh)] = ent
+    del cache
+    return out
+
+
+def row_stress(m, torch, dev, bf, f32, reps):
+    """Stress: N=16384, d=4096, K=16 adapters of rank 64, Zipf(1.1) biased random router
+    (logits given), top-k for k = 1..4: route_topk -> dispatch -> apply."""
+    import synth
+    c = synth.stress(1)
+    t = c.targets[0]
+    N, K = c.N, c.K
+    x, y0 = bf(t.x), bf(t.y0)
+    y = torch.empty(N, t.d_out, dtype=torch.bfloat16, device=dev)
+    logits = f32(c.logits)
+    hs = m.molora_hotset_init([(bf(t.A), bf(t.B))], c.scale)
+    compulsory = 3 * N * t.d_in * 2 + K * (t.d_in + t.d_out) * c.r * 2 + logits.numel() * 4
+    out = {"workload": "stress N=16384 d=4096 K=16 r=64 Zipf(1.1) logits", "compulsory_bytes": compulsory, "k": {}}
+    for k in (1, 2, 3, 4):
+        idx = torch.empty(N * k, dtype=torch.int32, device=dev)
+        w = torch.empty(N * k, dtype=torch.float32, device=dev)
+        meta = (torch.empty(K, dtype=torch.int32, device=dev), torch.empty(K + 1, dtype=torch.int32, device=dev),
+                torch.empty(N * k, dtype=torch.int32, device=dev), torch.empty(N * k, dtype=torch.float32, device=dev),
+                torch.empty(N * k, dtype=torch.int32, device=dev))
+        ws = torch.zeros(max(1, m.molora_apply_workspace(hs, 0, N, k, m.PATH_AUTO, torch.bfloat16)), dtype=torch.uint8, device=dev)
+
+        def step():
+            m.molora_route_topk(k, K, logits=logits, idx=idx, w=w, want_flags=False)
+            m.molora_dispatch(idx, w, K, k, out=meta)
+            m.molora_apply(hs, x, y0, meta[1], meta[2], meta[3], meta[4], k=k, y=y, ws=ws)
+
+        ms, g, _ = graph_ms(torch, step, reps)
+        flops = N * k * c.r * (t.d_in + t.d_out) * 2
+        out["k"][str(k)] = {"ms_per_step": ms, "routed_tokens_per_s": N / (ms * 1e-3),
+                            "pairs_per_s": N * k / (ms * 1e-3),
+                            "roofline_frac": compulsory / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9),
+                            "mfma_utilisation_bf16": flops / (ms * 1e-3) / 2.5e15}
+        del g, ws
+    return out
+
+
+def row_stack(m, torch, dev, layers=28, B=256, K=16, r=64, k=2, replays=1000):
+    """A hipGraph of 28 layers x 7 Qwen3-1.7B projections at decode batch 256 (K=16 adapters of
+    rank 64 per projection, top-2 over Zipf logits per layer, in-place y += delta); step
+    latency percentiles over single-graph replays.  Adapters are random device tensors."""
+    import synth
+    targets = synth.QWEN3_1P7B_TARGETS
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(20260316)
+    layer_objs = []
+    nbytes = 0
+    for L in range(layers):
+        tg = []
+        for (_, d_in, d_out) in targets:
+            A = (torch.randn(K, d_in, r, device=dev, generator=gen) / d_in ** 0.5).to(torch.bfloat16)
+            Bm = (torch.randn(K, r, d_out, device=dev, generator=gen) / r ** 0.5).to(torch.bfloat16)
+            tg.append((A, Bm))
+        hs = m.molora_hotset_init(tg, 2.0)
+        del tg
+        x = torch.randn(B, 2048, device=dev, generator=gen).to(torch.bfloat16)
+        o_in = torch.randn(B, 2048, device=dev, generator=gen).to(torch.bfloat16)
+        d_in6 = torch.randn(B, 6144, device=dev, generator=gen).to(torch.bfloat16)
+        ins = {"o": o_in, "down": d_in6}
+        xs = [ins.get(name, x) for (name, _, _) in targets]
+        ys = [torch.randn(B, d_out, device=dev, generator=gen).to(torch.bfloat16) for (_, _, d_out) in targets]
+        logits = torch.from_numpy(synth.zipf_logits(5, B, K, sub=L)).to(dev)
+        idx = torch.empty(B * k, dtype=torch.int32, device=dev)
+        w = torch.empty(B * k, dtype=torch.float32, device=dev)
+        meta = (torch.empty(K, dtype=torch.int32, device=dev), torch.empty(K + 1, dtype=torch.int32, device=dev),
+                torch.empty(B * k, dtype=torch.int32, device=dev), torch.empty(B * k, dtype=torch.float32, device=dev),
+                torch.empty(B * k, dtype=torch.int32, device=dev))
+        wss = [torch.zeros(max(1, m.molora_apply_workspace(hs, ti, B, k, m.PATH_AUTO, torch.bfloat16)), dtype=torch.uint8, device=dev)
+               for ti in range(len(targets))]
+        layer_objs.append((hs, xs, ys, logits, idx, w, meta, wss))
+        nbytes += (3 * B * 2048 + B * 6144) * 2 + sum(2 * B * d_out * 2 for (_, _, d_out) in targets)
+        nbytes += sum(K * (d_in + d_out) * r * 2 for (_, d_in, d_out) in targets) + logits.numel() * 4
+    torch.cuda.synchronize()
+
+    def step():
+        for (hs, xs, ys, logits, idx, w, meta, wss) in layer_objs:
+            m.molora_route_topk(k, K, logits=logits, idx=idx, w=w, want_flags=False)
+            m.molora_dispatch(idx, w, K, k, out=meta)
+            for ti in range(len(xs)):
+                m.molora_apply(hs, xs[ti], ys[ti], meta[1], meta[2], meta[3], meta[4], k=k, target=ti, y=ys[ti],
+                               ws=wss[ti])
+
+    ms, g, stream = graph_ms(torch, step, 20)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(replays)]
+    with torch.cuda.stream(stream):
+        for a, b in evs:
+            a.record(stream)
+            g.replay()
+            b.record(stream)
+    torch.cuda.synchronize()
+    lat = sorted(a.elapsed_time(b) * 1e3 for a, b in evs)
+    out = {"workload": f"{layers} layers x 7 Qwen3-1.7B projections, decode batch {B}, K={K} r={r} k={k}",
+           "p50_us": lat[len(lat) // 2], "p99_us": lat[min(len(lat) - 1, int(0.99 * len(lat)))],
+           "cv": statistics.pstdev(lat) / statistics.mean(lat), "replays": replays,
+           "mean_us": statistics.mean(lat), "compulsory_bytes": nbytes,
+           "roofline_frac_at_p50": nbytes / (lat[len(lat) // 2] * 1e-6) / (HBM_PEAK_GBS * 1e9)}
+    del g, layer_objs
+    return out
 
 
 def cpu_baseline(case, seconds):

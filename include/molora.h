@@ -196,7 +196,9 @@ int molora_dispatch(const int32_t *idx, const float *w, int N, int k, int K,
  *   offsets, perm, perm_w, inv: the outputs of molora_dispatch for this
  *           routing (inv is required when k > 1, ignored when k == 1)
  *   path    MOLORA_PATH_AUTO (chosen on the host from N*k, K and r),
- *           _GROUPED (MFMA tiles of 16 grouped rows of one adapter),
+ *           _GROUPED (MFMA tiles of grouped rows of one adapter: 16 rows for
+ *           k == 1 and r <= 32; otherwise 64 rows, and for k > 1 (k*K <= 64)
+ *           one pass per routed pair of a token, the sum carried in fp32),
  *           _SKINNY (the grouped shrink split over d_in, for small batches), or
  *           _TILE (8 consecutive tokens per workgroup, every adapter the tile
  *           uses applied in turn; needs K <= 16), or
@@ -204,15 +206,16 @@ int molora_dispatch(const int32_t *idx, const float *w, int N, int k, int K,
  *           split over workgroups by 512-wide slices of d_in, writing partial
  *           sums to the workspace, then the expand split by 512-wide slices of
  *           d_out; needs K <= 16 and r <= 32)
- *   ws      device workspace of at least molora_apply_workspace() bytes (no
- *           initial contents needed); calls that share a workspace must not
- *           run concurrently
+ *   ws      device workspace of at least molora_apply_workspace() bytes for
+ *           the same N, k, y_dtype and path (no initial contents needed; for
+ *           k > 1 on the grouped path with a bf16 y it holds an fp32 [N][d_out]
+ *           buffer); calls that share a workspace must not run concurrently
  * Accumulation is fp32; the shrink result h stays fp32 and enters the
  * expand as a bf16 hi/lo pair, so bf16 rounding happens only at the store
  * of y when y_dtype is MOLORA_BF16 (round to nearest even).
  * ------------------------------------------------------------------------ */
-int molora_apply_workspace(const molora_hotset *hs, int target, int N, int k, int path,
-                           size_t *bytes);
+int molora_apply_workspace(const molora_hotset *hs, int target, int N, int k, int y_dtype,
+                           int path, size_t *bytes);
 int molora_apply(const molora_hotset *hs, int target, const void *x, const void *y0,
                  int y0_dtype, void *y, int y_dtype, int N, int k, const int32_t *offsets,
                  const int32_t *perm, const float *perm_w, const int32_t *inv, int path,

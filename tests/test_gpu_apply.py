@@ -126,6 +126,9 @@ SHAPES = [
     (301, 512, 384, 6, 24, 3),
     (1000, 256, 1024, 16, 64, 4),
     (2500, 640, 512, 8, 16, 8),
+    (700, 512, 512, 64, 64, 1),   # 64-row grouped tiles over 64 adapters
+    (90, 256, 2048, 16, 48, 2),   # few tiles: output columns split over workgroups
+    (4100, 128, 256, 2, 16, 2),   # one reduction step, long segments
 ]
 
 
@@ -149,6 +152,9 @@ def test_apply_shapes_paths(N, d_in, d_out, K, r, k, path):
     w = ow.astype(np.float32)
     if N > 5:
         idx[N // 3, 0] = -1  # an unrouted pair
+        idx[N // 4, :] = -1  # a token with no routed pair
+        if k > 1:
+            idx[N // 2, k - 1] = -1  # last slot unrouted
     hs = m.molora_hotset_init([(dev_bf16(Ab), dev_bf16(Bb))], 2.0)
     counts, offsets, perm, perm_w, inv = m.molora_dispatch(dev(idx), dev(w), K, k)
     ref = oracle_from_gpu_routing(tg, 2.0, idx, w, K, k)
@@ -158,6 +164,38 @@ def test_apply_shapes_paths(N, d_in, d_out, K, r, k, path):
     yb16 = m.molora_apply(hs, dev_bf16(xb), dev_bf16(yb), offsets, perm, perm_w, inv, k=k, y_dtype=torch.bfloat16,
                           path=path)
     check_bf16_output(host(yb16), ref)
+
+
+@pytest.mark.parametrize("k,r", [(2, 16), (3, 64), (1, 64)])
+@pytest.mark.parametrize("y_dtype", [torch.float32, torch.bfloat16])
+def test_grouped_in_place_multi_slot(k, r, y_dtype):
+    """In-place grouped apply (y0 is y) on the 64-row tiles: per-slot passes and the fp32 carry
+    must leave unrouted tokens untouched and give the out-of-place result bit for bit."""
+    m = need_gpu()
+    N, d_in, d_out, K = 333, 384, 768, 8
+    g = np.random.default_rng(7 * k + r)
+    xb = synth.to_bf16_bits(g.standard_normal((N, d_in)).astype(np.float32))
+    Ab = synth.to_bf16_bits((g.standard_normal((K, d_in, r)) / np.sqrt(d_in)).astype(np.float32))
+    Bb = synth.to_bf16_bits((g.standard_normal((K, r, d_out)) / np.sqrt(r)).astype(np.float32))
+    yb = synth.to_bf16_bits(g.standard_normal((N, d_out)).astype(np.float32))
+    tg = synth.Target("p", d_in, d_out, Ab, Bb, xb, yb)
+    oi, ow, _ = route_topk(g.standard_normal((N, K)), k)
+    idx, w = oi.astype(np.int32), ow.astype(np.float32)
+    idx[::7, 0] = -1
+    idx[::11, :] = -1
+    hs = m.molora_hotset_init([(dev_bf16(Ab), dev_bf16(Bb))], 2.0)
+    counts, offsets, perm, perm_w, inv = m.molora_dispatch(dev(idx), dev(w), K, k)
+    ref = oracle_from_gpu_routing(tg, 2.0, idx, w, K, k)
+    y0 = dev_bf16(yb).to(y_dtype)
+    out = m.molora_apply(hs, dev_bf16(xb), y0, offsets, perm, perm_w, inv, k=k, y_dtype=y_dtype, path=1)
+    yin = y0.clone()
+    m.molora_apply(hs, dev_bf16(xb), yin, offsets, perm, perm_w, inv, k=k, y=yin, path=1)
+    np.testing.assert_array_equal(host(yin), host(out))
+    np.testing.assert_array_equal(host(yin)[::11], f64(yb)[::11])
+    if y_dtype == torch.float32:
+        check_float_output(host(out), ref, f64(yb))
+    else:
+        check_bf16_output(host(out), ref)
 
 
 def test_in_place_and_unrouted_rows():
@@ -250,7 +288,7 @@ def test_graph_replay_matches_eager(path):
             torch.empty(c.N, dtype=torch.int32, device="cuda"), torch.empty(c.N, dtype=torch.float32, device="cuda"),
             torch.empty(c.N, dtype=torch.int32, device="cuda"))
     y = torch.empty(c.N, t.d_out, dtype=torch.bfloat16, device="cuda")
-    need = m.molora_apply_workspace(hs, 0, c.N, 1, path)
+    need = m.molora_apply_workspace(hs, 0, c.N, 1, path, torch.bfloat16)
     ws = torch.zeros(max(need, 1), dtype=torch.uint8, device="cuda")
 
     def step():

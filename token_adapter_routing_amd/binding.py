@@ -47,7 +47,7 @@ _SIGS = {
     "molora_route_topk": (_c_i, [_c_p, _c_i, _c_i, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i, _c_i, _c_p, _c_p, _c_p, _c_p]),
     "molora_dispatch_workspace": (_c_i, [_c_i, _c_i, _c_i, ctypes.POINTER(_c_sz)]),
     "molora_dispatch": (_c_i, [_c_p, _c_p, _c_i, _c_i, _c_i, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_sz, _c_p]),
-    "molora_apply_workspace": (_c_i, [_c_p, _c_i, _c_i, _c_i, _c_i, ctypes.POINTER(_c_sz)]),
+    "molora_apply_workspace": (_c_i, [_c_p, _c_i, _c_i, _c_i, _c_i, _c_i, ctypes.POINTER(_c_sz)]),
     "molora_apply": (_c_i, [_c_p, _c_i, _c_p, _c_p, _c_i, _c_p, _c_i, _c_i, _c_i, _c_p, _c_p, _c_p, _c_p, _c_i,
                             _c_p, _c_sz, _c_p]),
     "molora_seqpass_meta": (_c_i, [_c_p, _c_i, _c_i, _c_p, _c_p, _c_p, _c_p]),
@@ -257,9 +257,11 @@ def molora_dispatch(idx: torch.Tensor, w: torch.Tensor, K: int, k: int = 1, out=
 
 # ----------------------------------------------------------------------------------- apply
 
-def molora_apply_workspace(hs: HotSet, target: int, N: int, k: int, path: int = PATH_AUTO) -> int:
+def molora_apply_workspace(hs: HotSet, target: int, N: int, k: int, path: int = PATH_AUTO,
+                           y_dtype=torch.float32) -> int:
     out = _c_sz()
-    _check(load_library().molora_apply_workspace(hs.handle, target, N, k, path, ctypes.byref(out)))
+    code = F32 if y_dtype == torch.float32 else BF16
+    _check(load_library().molora_apply_workspace(hs.handle, target, N, k, code, path, ctypes.byref(out)))
     return out.value
 
 
@@ -270,7 +272,7 @@ def molora_apply(hs: HotSet, x: torch.Tensor, y0: torch.Tensor, offsets: torch.T
     d_out = hs.dims[target][1]
     if y is None:
         y = torch.empty(N, d_out, dtype=y_dtype or y0.dtype, device=x.device)
-    need = molora_apply_workspace(hs, target, N, k, path)
+    need = molora_apply_workspace(hs, target, N, k, path, y.dtype)
     if need and (ws is None or ws.numel() < need):
         # zero-filled: the block path keeps control words at the start that must begin at zero
         ws = torch.zeros(need, dtype=torch.uint8, device=x.device)

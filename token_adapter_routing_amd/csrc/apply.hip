@@ -34,6 +34,7 @@
 #include "molora_mfma.h"
 #include "tile8_dev.h"
 #include "block_dev.h"
+#include "gm_dev.h"
 
 namespace molora {
 
@@ -383,6 +384,102 @@ __global__ __launch_bounds__(kBThreads, 2) void step_expand_block(StepArgs a, Bl
 }
 
 // --------------------------------------------------------------------------------------
+// Grouped 64-row tiles (gm_dev.h).  k > 1 runs as k passes, one per slot, chained through y
+// (y = y0 + slot 0's deltas, then y += slot 1's, ...): within a pass every token has at most one
+// row, so no two workgroups write one row, and the sum order is fixed.  The per-slot grouped
+// orders come from one stable counting sort of the grouped positions by (slot, adapter).
+template <int RB, bool INDIRECT, bool Y0F32, bool YF32>
+__global__ __launch_bounds__(kGMThreads) void apply_gm(GMArgs a) {
+  __shared__ GMLds<RB> L;
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const int g = slot % a.col_groups;
+  const int T = xcd * a.tiles_per_xcd + slot / a.col_groups;
+  gm_tile<RB, INDIRECT, Y0F32, YF32>(a, L, T, g);
+}
+
+// Key of grouped position q: (rank of its pair among the token's routed pairs) * K + adapter;
+// weight: its gate weight.  Ranking the routed pairs (instead of using the slot index) makes
+// pass 0 hold every token's first routed pair, so only pass 0 reads y0.
+struct SlotKeySource {
+  const int32_t* perm;
+  const float* perm_w;
+  const int32_t* inv;
+  const int* offs;  // LDS copy of the dispatch offsets
+  int k, K;
+  __device__ __forceinline__ void operator()(int q, int& e, float& wv) const {
+    const int p = perm[q];
+    const int t = p / k, s = p - t * k;
+    int rank = 0;
+    for (int j = 0; j < s; ++j) rank += inv[(long long)t * k + j] >= 0 ? 1 : 0;
+    e = rank * K + segment_of(offs, K, q);
+    wv = perm_w[q];
+  }
+};
+
+__global__ __launch_bounds__(1024) void slot_sort(const int32_t* __restrict__ offsets, const int32_t* __restrict__ perm,
+                                                  const float* __restrict__ perm_w, const int32_t* __restrict__ inv,
+                                                  int k, int K, int32_t* __restrict__ counts2,
+                                                  int32_t* __restrict__ offsets2, int32_t* __restrict__ perm2,
+                                                  float* __restrict__ perm_w2) {
+  __shared__ DispatchLds<1024> DL;
+  __shared__ int offs[65];
+  if (threadIdx.x <= K) offs[threadIdx.x] = offsets[threadIdx.x];
+  __syncthreads();
+  const int P = offs[K];
+  dispatch_block<1024>(DL, SlotKeySource{perm, perm_w, inv, offs, k, K}, P, k * K, counts2, offsets2, perm2, perm_w2,
+                       nullptr);
+}
+
+// After the passes: y = y0 for tokens with no routed pair (copy_y0, out-of-place calls) and
+// y = z (the fp32 pass buffer) for tokens whose last routed pair came before the last pass
+// (copy_z, when z is not y itself).  One wave per 64 tokens.
+template <bool Y0F32, bool YF32>
+__global__ __launch_bounds__(256) void finish_tokens(const void* y0, const float* z, void* y,
+                                                     const int32_t* __restrict__ inv, int N, int k, int d_out,
+                                                     int copy_y0, int copy_z) {
+  const int lane = threadIdx.x & 63;
+  const int base = (blockIdx.x * 4 + (threadIdx.x >> 6)) * kWave;
+  const int t = base + lane;
+  int c = 0;
+  if (t < N)
+    for (int j = 0; j < k; ++j) c += inv[(long long)t * k + j] >= 0 ? 1 : 0;
+  uint64_t m = __ballot(t < N && ((copy_y0 && c == 0) || (copy_z && c > 0 && c < k)));
+  while (m) {
+    const int l = __builtin_ctzll(m);
+    m &= m - 1;
+    const int tt = base + l;
+    const bool from_y0 = __shfl(c, l, kWave) == 0;
+    for (int col = lane * 4; col < d_out; col += kWave * 4) {
+      float v[4];
+      if (from_y0) {
+        if constexpr (Y0F32) {
+          const float* p = reinterpret_cast<const float*>(y0) + (size_t)tt * d_out + col;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v[i] = p[i];
+        } else {
+          const uint16_t* p = reinterpret_cast<const uint16_t*>(y0) + (size_t)tt * d_out + col;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v[i] = bf16_to_f32(p[i]);
+        }
+      } else {
+        const float* p = z + (size_t)tt * d_out + col;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = p[i];
+      }
+      if constexpr (YF32) {
+        float* p = reinterpret_cast<float*>(y) + (size_t)tt * d_out + col;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) p[i] = v[i];
+      } else {
+        uint32_t* p = reinterpret_cast<uint32_t*>(reinterpret_cast<uint16_t*>(y) + (size_t)tt * d_out + col);
+        p[0] = pack_bf16x2(v[0], v[1]);
+        p[1] = pack_bf16x2(v[2], v[3]);
+      }
+    }
+  }
+}
+
+// --------------------------------------------------------------------------------------
 // Globally grouped tiles, one adapter per token.
 struct FusedArgs {
   TargetDev tgt;
@@ -697,7 +794,7 @@ __global__ __launch_bounds__(256) void expand_tokens(ExpandArgs a) {
 int apply_resolve_path(int N, int k, int path, int K, int r_pad) {
   if (path != 0) return path;
   const long long P = (long long)N * k;
-  if (K <= kT8MaxU && r_pad <= 32 && P >= 192) return 3;  // few, small adapters: tile-local grouping
+  if (k == 1 && K <= kT8MaxU && r_pad <= 32 && P >= 192) return 3;  // few, small adapters: tile-local
   if (k == 1) return P >= 192 ? 1 : 2;
   return P >= 1024 ? 1 : 2;
 }
@@ -720,9 +817,23 @@ static size_t block_ws(int N, int k, int K, int r_pad, int d_in) {
 
 size_t step_ws_bytes(int N, int K, int r_pad, int d_in) { return block_ws(N, 1, K, r_pad, d_in); }
 
-size_t apply_ws_bytes(int N, int k, int K, int r_pad, int d_in, int path) {
+// Grouped path on 64-row tiles: used for k > 1 (passes over ranked slots) or ranks above 32.
+// k > 1 workspace: the slot sort (counts and offsets in a 256-byte block, then the order and
+// the weights), then, for a bf16 y, the fp32 pass buffer z [N][d_out].
+static bool use_gm(int k, int K, int r_pad) { return (k > 1 && k * K <= 64) || (k == 1 && r_pad > 32); }
+static size_t gm_sort_bytes(long long P, int k, int K) {
+  return ((size_t)(2 * k * K + 1) * sizeof(int32_t) + 255) / 256 * 256 +
+         ((size_t)P * (sizeof(int32_t) + sizeof(float)) + 255) / 256 * 256;
+}
+static size_t gm_ws_bytes(int N, int k, int K, int d_out, bool y_f32) {
+  if (k == 1) return 0;
+  return gm_sort_bytes((long long)N * k, k, K) + (y_f32 ? 0 : (size_t)N * d_out * sizeof(float));
+}
+
+size_t apply_ws_bytes(int N, int k, int K, int r_pad, int d_in, int d_out, bool y_f32, int path) {
   const int p = apply_resolve_path(N, k, path, K, r_pad);
   if (p == 4) return block_ws(N, k, K, r_pad, d_in);
+  if (p == 1 && use_gm(k, K, r_pad)) return gm_ws_bytes(N, k, K, d_out, y_f32);
   if (p == 3 || (k == 1 && p == 1)) return 0;
   const int ns = (p == 2) ? skinny_splits(d_in) : 1;
   return (size_t)ns * (size_t)N * (size_t)k * (size_t)r_pad * sizeof(float);
@@ -801,6 +912,18 @@ static hipError_t launch_t8_t(const T8ApplyArgs& ta, int grid, hipStream_t s) {
   return hipGetLastError();
 }
 template <int RB, bool IND, bool Y0F, bool YF>
+static hipError_t launch_gm_t(const GMArgs& ga, int grid, hipStream_t s) {
+  hipLaunchKernelGGL((apply_gm<RB, IND, Y0F, YF>), dim3(grid), dim3(kGMThreads), 0, s, ga);
+  return hipGetLastError();
+}
+template <bool Y0F, bool YF>
+static hipError_t launch_finish_t(const void* y0, const float* z, void* y, const int32_t* inv, int N, int k,
+                                  int d_out, bool copy_y0, bool copy_z, hipStream_t s) {
+  hipLaunchKernelGGL((finish_tokens<Y0F, YF>), dim3((N + 255) / 256), dim3(256), 0, s, y0, z, y, inv, N, k, d_out,
+                     (int)copy_y0, (int)copy_z);
+  return hipGetLastError();
+}
+template <int RB, bool IND, bool Y0F, bool YF>
 static hipError_t launch_block_t(const BlockApplyArgs& ba, hipStream_t s) {
   hipLaunchKernelGGL((shrink_block<RB, IND>), dim3(ba.b.nblocks * ba.b.kslices), dim3(kBThreads), 0, s, ba);
   hipError_t e = hipGetLastError();
@@ -869,6 +992,64 @@ hipError_t launch_apply(const ApplyLaunch& a, hipStream_t s) {
     ba.offsets = a.offsets; ba.perm_w = a.perm_w; ba.inv = a.inv;
     MOLORA_DISPATCH_RB12(RBv, MOLORA_DISPATCH_BOOL(a.indirect, IND, MOLORA_DISPATCH_BOOL(a.y0_f32, Y0F,
         MOLORA_DISPATCH_BOOL(a.y_f32, YF, err = (launch_block_t<RB, IND, Y0F, YF>(ba, s))))));
+    return err;
+  }
+
+  if (a.path == 1 && use_gm(a.k, a.K, a.tgt.r_pad)) {
+    // 64-row grouped tiles.  k > 1: pass j applies the j-th routed pair of every token, over
+    // the (rank, adapter) order of the slot sort; pass 0 reads y0, the last pass writes y and
+    // the passes in between carry the sum in fp32 (in y itself when y is fp32, else in z), so a
+    // bf16 y is rounded once.
+    const bool in_place = (a.y0 == a.y);
+    GMArgs ga;
+    ga.tgt = a.tgt; ga.x = a.x; ga.N = a.N; ga.k = a.k; ga.scale = a.scale; ga.perm = a.perm; ga.nkeys = a.K;
+    const long long rows_max = a.k == 1 ? P : a.N;  // rows of one pass
+    const long long tiles = (rows_max + kGMRows - 1) / kGMRows + a.K;
+    const int nblk = a.tgt.d_out / kColBlock;
+    int cg = 1;
+    while (tiles * cg < 256 && nblk % (2 * cg) == 0 && nblk / (2 * cg) >= 2) cg *= 2;
+    ga.col_groups = cg;
+    ga.tiles_per_xcd = (int)((tiles + 7) / 8);
+    const int grid = 8 * ga.tiles_per_xcd * cg;
+    auto pass = [&](const void* src, bool src_f32, void* dst, bool dst_f32) {
+      ga.y0 = src;
+      ga.y = dst;
+      hipError_t e = hipSuccess;
+      MOLORA_DISPATCH_RB(RBv, MOLORA_DISPATCH_BOOL(a.indirect, IND, MOLORA_DISPATCH_BOOL(src_f32, Y0F,
+          MOLORA_DISPATCH_BOOL(dst_f32, YF, e = (launch_gm_t<RB, IND, Y0F, YF>(ga, grid, s))))));
+      return e;
+    };
+    if (a.k == 1) {
+      ga.key0 = 0; ga.offsets = a.offsets; ga.order = nullptr; ga.wts = a.perm_w;
+      err = pass(a.y0, a.y0_f32, a.y, a.y_f32);
+      if (err != hipSuccess || in_place) return err;
+      MOLORA_DISPATCH_BOOL(a.y0_f32, Y0F, MOLORA_DISPATCH_BOOL(a.y_f32, YF,
+          err = (launch_finish_t<Y0F, YF>(a.y0, nullptr, a.y, a.inv, a.N, 1, a.tgt.d_out, true, false, s))));
+      return err;
+    }
+    char* wsb = reinterpret_cast<char*>(a.ws);
+    int32_t* counts2 = reinterpret_cast<int32_t*>(wsb);
+    int32_t* offsets2 = counts2 + a.k * a.K;
+    const size_t head = ((size_t)(2 * a.k * a.K + 1) * sizeof(int32_t) + 255) / 256 * 256;
+    int32_t* perm2 = reinterpret_cast<int32_t*>(wsb + head);
+    float* w2 = reinterpret_cast<float*>(wsb + head + (size_t)P * sizeof(int32_t));
+    float* z = a.y_f32 ? reinterpret_cast<float*>(a.y) : reinterpret_cast<float*>(wsb + gm_sort_bytes(P, a.k, a.K));
+    hipLaunchKernelGGL(slot_sort, dim3(1), dim3(1024), 0, s, a.offsets, a.perm, a.perm_w, a.inv, a.k, a.K, counts2,
+                       offsets2, perm2, w2);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    ga.offsets = offsets2; ga.order = perm2; ga.wts = w2;
+    for (int j = 0; j < a.k; ++j) {
+      ga.key0 = j * a.K;
+      const bool last = j == a.k - 1;
+      err = pass(j == 0 ? a.y0 : static_cast<const void*>(z), j == 0 ? (bool)a.y0_f32 : true,
+                 last ? a.y : static_cast<void*>(z), last ? (bool)a.y_f32 : true);
+      if (err != hipSuccess) return err;
+    }
+    const bool copy_z = static_cast<void*>(z) != a.y;
+    if (in_place && !copy_z) return err;
+    MOLORA_DISPATCH_BOOL(a.y0_f32, Y0F, MOLORA_DISPATCH_BOOL(a.y_f32, YF,
+        err = (launch_finish_t<Y0F, YF>(a.y0, z, a.y, a.inv, a.N, a.k, a.tgt.d_out, !in_place, copy_z, s))));
     return err;
   }
 

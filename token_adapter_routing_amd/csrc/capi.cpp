@@ -269,13 +269,15 @@ int molora_dispatch(const int32_t* idx, const float* w, int N, int k, int K, int
   return e == hipSuccess ? ok() : hip_fail(e, "dispatch launch");
 }
 
-int molora_apply_workspace(const molora_hotset* hs, int target, int N, int k, int path, size_t* bytes) {
+int molora_apply_workspace(const molora_hotset* hs, int target, int N, int k, int y_dtype, int path, size_t* bytes) {
   if (bytes == nullptr) return fail(MOLORA_EINVAL, "bytes is NULL");
   if (hs == nullptr) return fail(MOLORA_EINVAL, "hot set is NULL");
   if (target < 0 || target >= hs->n_targets) return fail(MOLORA_EINVAL, "target %d outside [0, %d)", target, hs->n_targets);
   if (N < 0 || k < 1 || k > MOLORA_MAX_TOPK || k > hs->K) return fail(MOLORA_EINVAL, "bad N=%d or k=%d", N, k);
   if (path < MOLORA_PATH_AUTO || path > MOLORA_PATH_BLOCK) return fail(MOLORA_EINVAL, "unknown path %d", path);
-  *bytes = molora::apply_ws_bytes(N, k, hs->K, hs->r_pad, hs->tg[target].d_in, path);
+  if (y_dtype != MOLORA_BF16 && y_dtype != MOLORA_F32) return fail(MOLORA_EINVAL, "unknown dtype");
+  *bytes = molora::apply_ws_bytes(N, k, hs->K, hs->r_pad, hs->tg[target].d_in, hs->tg[target].d_out,
+                                  y_dtype == MOLORA_F32, path);
   return ok();
 }
 
@@ -302,7 +304,7 @@ int molora_apply(const molora_hotset* hs, int target, const void* x, const void*
   if (!aligned(offsets, 4) || !aligned(perm, 4) || !aligned(perm_w, 4) || !aligned(inv, 4))
     return fail(MOLORA_EINVAL, "misaligned pointer");
   const molora::TargetDev& tg = hs->tg[target];
-  const size_t need = molora::apply_ws_bytes(N, k, hs->K, hs->r_pad, tg.d_in, path);
+  const size_t need = molora::apply_ws_bytes(N, k, hs->K, hs->r_pad, tg.d_in, tg.d_out, y_dtype == MOLORA_F32, path);
   if (need > 0 && (ws == nullptr || ws_bytes < need || !aligned(ws, 16)))
     return fail(MOLORA_ENOSPC, "workspace of %zu bytes (16-byte aligned) needed, %zu given", need, ws_bytes);
   molora::ApplyLaunch a{};

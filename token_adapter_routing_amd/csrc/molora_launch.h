@@ -53,7 +53,7 @@ struct ApplyLaunch {
 };
 
 // Workspace bytes a resolved apply needs.
-size_t apply_ws_bytes(int N, int k, int K, int r_pad, int d_in, int path);
+size_t apply_ws_bytes(int N, int k, int K, int r_pad, int d_in, int d_out, bool y_f32, int path);
 int apply_resolve_path(int N, int k, int path, int K, int r_pad);
 constexpr int kApplyTileMaxAdapters = 16;  // tile-local path: distinct adapters per tile
 hipError_t launch_apply(const ApplyLaunch& a, hipStream_t s);

@@ -118,9 +118,17 @@ __device__ __forceinline__ void t8_prefetch(const T8Args& a, int tt, int g, T8St
 }
 
 // y0 rows / y rows of the lane's 4 tokens (addresses formed at each use, not held).
+// Addresses are formed where they are used: the empty asm makes the row index opaque, so the
+// compiler cannot compute the 64-bit addresses early and keep (or spill) them across the body.
+__device__ __forceinline__ int t8_opaque(int v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
 template <bool Y0F32>
 __device__ __forceinline__ void t8_load_y0(RowChunk<Y0F32>& r, const T8Args& a, int trow, int col, int n) {
   constexpr size_t y0b = Y0F32 ? 4 : 2;
+  trow = t8_opaque(trow);
   const char* rows[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -131,6 +139,7 @@ template <bool Y0F32, bool YF32>
 __device__ __forceinline__ void t8_store_y(const f32x4_t (&o)[8], const RowChunk<Y0F32>& y0c, const T8Args& a, int trow,
                                            int col, int n) {
   constexpr size_t yb = YF32 ? 4 : 2;
+  trow = t8_opaque(trow);
   char* rows[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -143,7 +152,7 @@ template <int RB, int J>
 __device__ __forceinline__ void t8_load_b(u32x4_t (&bv)[J][RB], const uint16_t* __restrict__ Bt, int r_pad,
                                           int colbase, int cend, int lane, int j0) {
   const int n = lane & 15, G = lane >> 4;
-  const uint16_t* bp = Bt + (size_t)(t8_block_col(colbase, cend, G) + n) * r_pad + (G & 1) * 8;
+  const uint16_t* bp = Bt + (size_t)(t8_block_col(t8_opaque(colbase), cend, G) + n) * r_pad + (G & 1) * 8;
 #pragma unroll
   for (int j = 0; j < J; ++j)
 #pragma unroll
