@@ -444,7 +444,7 @@ def row_decode(m, torch, dev, bf, i32, reps):
             ms, g, _ = graph_ms(torch, step, reps, inner=20)
             entry[name] = {"us_per_step": ms * 1e3, "GBps": nbytes / (ms * 1e-3) / 1e9}
             del g
-        entry["auto_path"] = "skinny" if B * 1 < 192 else "grouped"
+        entry["auto_path"] = "grouped"
         out["sweep"][str(B)] = entry
     sk = [int(b) for b, e in out["sweep"].items() if e["grouped"]["us_per_step"] < e["skinny"]["us_per_step"]]
     out["grouped_faster_from_B"] = min(sk) if sk else None

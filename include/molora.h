@@ -194,8 +194,9 @@ int molora_dispatch(const int32_t *idx, const float *w, int N, int k, int K,
  *           MOLORA_F32); may be the same buffer as y (in place)
  *   y       device [N][d_out] out, dtype y_dtype
  *   offsets, perm, perm_w, inv: the outputs of molora_dispatch for this
- *           routing (inv is required when k > 1, ignored when k == 1)
- *   path    MOLORA_PATH_AUTO (chosen on the host from N*k, K and r),
+ *           routing (all four required)
+ *   path    MOLORA_PATH_AUTO (_TILE when K <= 16, r <= 32 and N*k >= 192;
+ *           else _GROUPED, except _SKINNY for r > 32 below 1024 pairs),
  *           _GROUPED (MFMA tiles of grouped rows of one adapter: 16 rows for
  *           k == 1 and r <= 32; otherwise 64 rows, and for k > 1 (k*K <= 64)
  *           one pass per routed pair of a token, the sum carried in fp32),

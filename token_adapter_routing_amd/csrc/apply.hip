@@ -391,10 +391,7 @@ __global__ __launch_bounds__(kBThreads, 2) void step_expand_block(StepArgs a, Bl
 template <int RB, bool INDIRECT, bool Y0F32, bool YF32>
 __global__ __launch_bounds__(kGMThreads) void apply_gm(GMArgs a) {
   __shared__ GMLds<RB> L;
-  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-  const int g = slot % a.col_groups;
-  const int T = xcd * a.tiles_per_xcd + slot / a.col_groups;
-  gm_tile<RB, INDIRECT, Y0F32, YF32>(a, L, T, g);
+  gm_range<RB, INDIRECT, Y0F32, YF32>(a, L);
 }
 
 // Key of grouped position q: (rank of its pair among the token's routed pairs) * K + adapter;
@@ -794,8 +791,12 @@ __global__ __launch_bounds__(256) void expand_tokens(ExpandArgs a) {
 int apply_resolve_path(int N, int k, int path, int K, int r_pad) {
   if (path != 0) return path;
   const long long P = (long long)N * k;
-  if (k == 1 && K <= kT8MaxU && r_pad <= 32 && P >= 192) return 3;  // few, small adapters: tile-local
-  if (k == 1) return P >= 192 ? 1 : 2;
+  // few, small adapters: tile-local.  Ranks <= 32: grouped (faster than the split-reduction
+  // skinny path at every decode batch measured, 1 .. 2048 tokens).  Ranks above 32: the 64-row
+  // grouped tiles from 1024 pairs on; below that their serial per-tile pipeline is slower than
+  // the skinny path's d_in split.
+  if (K <= kT8MaxU && r_pad <= 32 && P >= 192) return 3;
+  if (r_pad <= 32) return 1;
   return P >= 1024 ? 1 : 2;
 }
 
@@ -1003,14 +1004,18 @@ hipError_t launch_apply(const ApplyLaunch& a, hipStream_t s) {
     const bool in_place = (a.y0 == a.y);
     GMArgs ga;
     ga.tgt = a.tgt; ga.x = a.x; ga.N = a.N; ga.k = a.k; ga.scale = a.scale; ga.perm = a.perm; ga.nkeys = a.K;
+    // equal row ranges of at most 64 rows (at least 16 while that leaves CUs idle), a multiple
+    // of 8 for the XCD mapping; column slices while there are fewer than 256 workgroups
     const long long rows_max = a.k == 1 ? P : a.N;  // rows of one pass
-    const long long tiles = (rows_max + kGMRows - 1) / kGMRows + a.K;
+    long long nwg = (rows_max + kGMRows - 1) / kGMRows;
+    if (nwg < 256) nwg = std::min<long long>(256, (rows_max + 15) / 16);
+    nwg = (nwg + 7) / 8 * 8;
     const int nblk = a.tgt.d_out / kColBlock;
     int cg = 1;
-    while (tiles * cg < 256 && nblk % (2 * cg) == 0 && nblk / (2 * cg) >= 2) cg *= 2;
+    while (nwg * cg < 256 && nblk % (2 * cg) == 0 && nblk / (2 * cg) >= 2) cg *= 2;
     ga.col_groups = cg;
-    ga.tiles_per_xcd = (int)((tiles + 7) / 8);
-    const int grid = 8 * ga.tiles_per_xcd * cg;
+    ga.nwg = (int)nwg;
+    const int grid = (int)nwg * cg;
     auto pass = [&](const void* src, bool src_f32, void* dst, bool dst_f32) {
       ga.y0 = src;
       ga.y = dst;

@@ -42,7 +42,7 @@ template <int RB>
 struct T8Cfg {
   static constexpr int XS = 4;                                 // x steps held in registers
   static constexpr int SB = RB == 1 ? 4 : (RB == 2 ? 2 : 1);  // A steps per register batch (divides XS)
-  static constexpr int JB = RB <= 2 ? 8 : 4;                   // MFMA columns per B register batch
+  static constexpr int JB = RB == 1 ? 8 : 4;                   // MFMA columns per B register batch
 };
 
 template <int RB>
@@ -251,7 +251,6 @@ __device__ __forceinline__ void t8_main(const T8Args& a, T8Lds<RB>& L, T8Stream<
   for (int base = 0; base < nU; ++base) {
     const uint16_t* Acur = adapter_A<INDIRECT>(a.tgt, __builtin_ctz(rem));
     rem &= rem - 1;
-    if (base > 0) load_a(Acur, st.s0);
     f32x4_t acc0[RB], acc1[RB];
 #pragma unroll
     for (int u = 0; u < RB; ++u) {
@@ -291,6 +290,8 @@ __device__ __forceinline__ void t8_main(const T8Args& a, T8Lds<RB>& L, T8Stream<
         }
       }
     }
+    // the next adapter's first A pieces stream during this adapter's reduction
+    if (base + 1 < nU) load_a(adapter_A<INDIRECT>(a.tgt, __builtin_ctz(rem)), st.s0);
     if (base == 0) {
       // the second unit's pieces and y0 rows stream during the reductions
       if (nU == 1) t8_load_b<RB, JB>(b1, adapter_B<INDIRECT>(a.tgt, e0), r_pad, cb1, st.cend, lane, 0);
