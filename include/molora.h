@@ -172,7 +172,11 @@ int molora_route_topk(const void *x, int N, int d, const void *W1, const float *
  *   inv     device int32 [N*k] out or NULL: inv[p] = q with perm[q] = p, or
  *           -1 for an unrouted pair
  *   ws      device workspace of at least molora_dispatch_workspace() bytes
- *           (may be NULL when that size is 0)
+ *           (may be NULL when that size is 0; no initial contents needed).
+ *           Up to 8192 pairs one workgroup sorts them (size 0); above that
+ *           the sort runs as two launches over up to 128 workgroups and the
+ *           workspace holds their per-adapter counts (4*K bytes each).
+ *           Calls that share a workspace must not run concurrently.
  * Supported: 1 <= K <= 64, 1 <= k <= 8, N*k < 2^31.
  * ------------------------------------------------------------------------ */
 int molora_dispatch_workspace(int N, int k, int K, size_t *bytes);

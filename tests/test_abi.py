@@ -79,7 +79,8 @@ def test_host_validation_without_launch():
     # apply: NULL hot set
     assert L.molora_apply(nul, 0, nul, nul, 0, nul, 0, 4, 1, nul, nul, nul, nul, 0, nul, 0, nul) == 1
     sz = ctypes.c_size_t()
-    assert L.molora_dispatch_workspace(16384, 4, 16, ctypes.byref(sz)) == 0 and sz.value == 0
+    assert L.molora_dispatch_workspace(2048, 4, 16, ctypes.byref(sz)) == 0 and sz.value == 0  # 8192 pairs: one workgroup
+    assert L.molora_dispatch_workspace(16384, 4, 16, ctypes.byref(sz)) == 0 and sz.value == 8 * 16 * 4
     assert L.molora_apply_workspace(nul, 0, 4, 1, 0, 0, ctypes.byref(sz)) == 1
     # hotset_init: unaligned slab is rejected before any launch
     tg = (MoloraTarget * 1)(MoloraTarget(128, 128, 2, 2))

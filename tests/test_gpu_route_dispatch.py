@@ -116,7 +116,7 @@ def _check_dispatch(idx_np, w_np, K, k, out):
 
 @pytest.mark.parametrize("N,k,K", [(1, 1, 1), (256, 1, 4), (2048, 1, 4), (1000, 2, 4), (4096, 2, 4),
                                    (333, 3, 7), (2048, 1, 64), (5000, 8, 64), (16384, 4, 16), (16384, 1, 16),
-                                   (40000, 2, 2)])
+                                   (40000, 2, 2), (8192, 1, 3), (8193, 1, 3), (1048579, 1, 64)])
 def test_dispatch_random(N, k, K):
     m = need_gpu()
     g = np.random.default_rng(N + k * 7 + K)
@@ -126,10 +126,12 @@ def test_dispatch_random(N, k, K):
     _check_dispatch(idx, w, K, k, out)
 
 
-def test_dispatch_unrouted_and_out_of_range():
+@pytest.mark.parametrize("N", [3001, 30001])
+def test_dispatch_unrouted_and_out_of_range(N):
+    """Unrouted pairs (adapter outside [0, K)) in the one-workgroup sort and in the chip-wide one."""
     m = need_gpu()
     g = np.random.default_rng(17)
-    N, k, K = 3001, 2, 5
+    k, K = 2, 5
     idx = g.integers(-3, K + 3, size=(N, k)).astype(np.int32)
     w = g.random((N, k)).astype(np.float32)
     out = m.molora_dispatch(dev(idx), dev(w), K, k)

@@ -427,6 +427,30 @@ __global__ __launch_bounds__(1024) void slot_sort(const int32_t* __restrict__ of
                        nullptr);
 }
 
+// The same sort over many pairs: histogram and scatter launches over nb workgroups.
+__global__ __launch_bounds__(1024) void slot_hist(const int32_t* __restrict__ offsets, const int32_t* __restrict__ perm,
+                                                  const float* __restrict__ perm_w, const int32_t* __restrict__ inv,
+                                                  int k, int K, int C, int32_t* __restrict__ bcnt) {
+  __shared__ DispatchLds<1024> DL;
+  __shared__ int offs[65];
+  if (threadIdx.x <= K) offs[threadIdx.x] = offsets[threadIdx.x];
+  __syncthreads();
+  dispatch_hist_part<1024>(DL, SlotKeySource{perm, perm_w, inv, offs, k, K}, offs[K], k * K, C, bcnt);
+}
+__global__ __launch_bounds__(1024) void slot_scatter(const int32_t* __restrict__ offsets,
+                                                     const int32_t* __restrict__ perm, const float* __restrict__ perm_w,
+                                                     const int32_t* __restrict__ inv, int k, int K, int C, int nb,
+                                                     const int32_t* __restrict__ bcnt, int32_t* __restrict__ counts2,
+                                                     int32_t* __restrict__ offsets2, int32_t* __restrict__ perm2,
+                                                     float* __restrict__ perm_w2) {
+  __shared__ DispatchLds<1024> DL;
+  __shared__ int offs[65];
+  if (threadIdx.x <= K) offs[threadIdx.x] = offsets[threadIdx.x];
+  __syncthreads();
+  dispatch_scatter_part<1024>(DL, SlotKeySource{perm, perm_w, inv, offs, k, K}, offs[K], k * K, C, nb, bcnt, counts2,
+                              offsets2, perm2, perm_w2, nullptr);
+}
+
 // After the passes: y = y0 for tokens with no routed pair (copy_y0, out-of-place calls) and
 // y = z (the fp32 pass buffer) for tokens whose last routed pair came before the last pass
 // (copy_z, when z is not y itself).  One wave per 64 tokens.
@@ -820,11 +844,13 @@ size_t step_ws_bytes(int N, int K, int r_pad, int d_in) { return block_ws(N, 1, 
 
 // Grouped path on 64-row tiles: used for k > 1 (passes over ranked slots) or ranks above 32.
 // k > 1 workspace: the slot sort (counts and offsets in a 256-byte block, then the order and
-// the weights), then, for a bf16 y, the fp32 pass buffer z [N][d_out].
+// the weights, then the per-workgroup counts of a chip-wide sort), then, for a bf16 y, the
+// fp32 pass buffer z [N][d_out].
 static bool use_gm(int k, int K, int r_pad) { return (k > 1 && k * K <= 64) || (k == 1 && r_pad > 32); }
+static size_t gm_head_bytes(int k, int K) { return ((size_t)(2 * k * K + 1) * sizeof(int32_t) + 255) / 256 * 256; }
+static size_t gm_order_bytes(long long P) { return ((size_t)P * (sizeof(int32_t) + sizeof(float)) + 255) / 256 * 256; }
 static size_t gm_sort_bytes(long long P, int k, int K) {
-  return ((size_t)(2 * k * K + 1) * sizeof(int32_t) + 255) / 256 * 256 +
-         ((size_t)P * (sizeof(int32_t) + sizeof(float)) + 255) / 256 * 256;
+  return gm_head_bytes(k, K) + gm_order_bytes(P) + (dispatch_ws_bytes(P, k * K) + 255) / 256 * 256;
 }
 static size_t gm_ws_bytes(int N, int k, int K, int d_out, bool y_f32) {
   if (k == 1) return 0;
@@ -1035,12 +1061,23 @@ hipError_t launch_apply(const ApplyLaunch& a, hipStream_t s) {
     char* wsb = reinterpret_cast<char*>(a.ws);
     int32_t* counts2 = reinterpret_cast<int32_t*>(wsb);
     int32_t* offsets2 = counts2 + a.k * a.K;
-    const size_t head = ((size_t)(2 * a.k * a.K + 1) * sizeof(int32_t) + 255) / 256 * 256;
+    const size_t head = gm_head_bytes(a.k, a.K);
     int32_t* perm2 = reinterpret_cast<int32_t*>(wsb + head);
     float* w2 = reinterpret_cast<float*>(wsb + head + (size_t)P * sizeof(int32_t));
+    int32_t* bcnt = reinterpret_cast<int32_t*>(wsb + head + gm_order_bytes(P));
     float* z = a.y_f32 ? reinterpret_cast<float*>(a.y) : reinterpret_cast<float*>(wsb + gm_sort_bytes(P, a.k, a.K));
-    hipLaunchKernelGGL(slot_sort, dim3(1), dim3(1024), 0, s, a.offsets, a.perm, a.perm_w, a.inv, a.k, a.K, counts2,
-                       offsets2, perm2, w2);
+    const DispatchSplit ds = dispatch_split(P);
+    if (ds.nb > 1) {
+      hipLaunchKernelGGL(slot_hist, dim3(ds.nb), dim3(1024), 0, s, a.offsets, a.perm, a.perm_w, a.inv, a.k, a.K, ds.C,
+                         bcnt);
+      err = hipGetLastError();
+      if (err != hipSuccess) return err;
+      hipLaunchKernelGGL(slot_scatter, dim3(ds.nb), dim3(1024), 0, s, a.offsets, a.perm, a.perm_w, a.inv, a.k, a.K,
+                         ds.C, ds.nb, bcnt, counts2, offsets2, perm2, w2);
+    } else {
+      hipLaunchKernelGGL(slot_sort, dim3(1), dim3(1024), 0, s, a.offsets, a.perm, a.perm_w, a.inv, a.k, a.K, counts2,
+                         offsets2, perm2, w2);
+    }
     err = hipGetLastError();
     if (err != hipSuccess) return err;
     ga.offsets = offsets2; ga.order = perm2; ga.wts = w2;

@@ -246,14 +246,12 @@ int molora_dispatch_workspace(int N, int k, int K, size_t* bytes) {
   if (bytes == nullptr) return fail(MOLORA_EINVAL, "bytes is NULL");
   if (N < 0 || k < 1 || k > MOLORA_MAX_TOPK) return fail(MOLORA_EINVAL, "bad N=%d or k=%d", N, k);
   if (K < 1 || K > MOLORA_MAX_ADAPTERS) return fail(MOLORA_ENOTSUP, "K=%d outside [1, %d]", K, MOLORA_MAX_ADAPTERS);
-  *bytes = 0;
+  *bytes = molora::dispatch_ws_bytes((long long)N * k, K);
   return ok();
 }
 
 int molora_dispatch(const int32_t* idx, const float* w, int N, int k, int K, int32_t* counts, int32_t* offsets,
                     int32_t* perm, float* perm_w, int32_t* inv, void* ws, size_t ws_bytes, void* stream) {
-  (void)ws;
-  (void)ws_bytes;
   if (N < 0) return fail(MOLORA_EINVAL, "N=%d < 0", N);
   if (k < 1 || k > MOLORA_MAX_TOPK) return fail(MOLORA_ENOTSUP, "k=%d outside [1, %d]", k, MOLORA_MAX_TOPK);
   if (K < 1 || K > MOLORA_MAX_ADAPTERS) return fail(MOLORA_ENOTSUP, "K=%d outside [1, %d]", K, MOLORA_MAX_ADAPTERS);
@@ -264,7 +262,10 @@ int molora_dispatch(const int32_t* idx, const float* w, int N, int k, int K, int
   if (!aligned(idx, 4) || !aligned(w, 4) || !aligned(counts, 4) || !aligned(offsets, 4) || !aligned(perm, 4) ||
       !aligned(perm_w, 4) || (inv != nullptr && !aligned(inv, 4)))
     return fail(MOLORA_EINVAL, "misaligned pointer");
-  const hipError_t e = molora::launch_dispatch(idx, w, N * k, K, counts, offsets, perm, perm_w, inv,
+  const size_t need = molora::dispatch_ws_bytes((long long)N * k, K);
+  if (need > 0 && (ws == nullptr || ws_bytes < need || !aligned(ws, 4)))
+    return fail(MOLORA_ENOSPC, "dispatch workspace of %zu bytes needed, %zu given", need, ws_bytes);
+  const hipError_t e = molora::launch_dispatch(idx, w, N * k, K, counts, offsets, perm, perm_w, inv, ws,
                                                reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? ok() : hip_fail(e, "dispatch launch");
 }
@@ -405,7 +406,7 @@ int molora_step_vocab(const molora_hotset* hs, int target, const int32_t* ids, i
     return e == hipSuccess ? ok() : hip_fail(e, "step launch");
   }
   hipError_t e = molora::launch_route_vocab(ids, N, st.bounds, hs->K, idx, w, s);
-  if (e == hipSuccess) e = molora::launch_dispatch(idx, w, N, hs->K, counts, offsets, perm, perm_w, inv, s);
+  if (e == hipSuccess) e = molora::launch_dispatch(idx, w, N, hs->K, counts, offsets, perm, perm_w, inv, nullptr, s);
   if (e == hipSuccess) e = molora::launch_apply(a, s);
   return e == hipSuccess ? ok() : hip_fail(e, "step launch");
 }

@@ -28,8 +28,52 @@ __global__ __launch_bounds__(kDispThreads) void dispatch_single(const int32_t* _
   dispatch_block<kDispThreads>(L, ArraySource{idx, w}, P, K, counts, offsets, perm, perm_w, inv);
 }
 
+__global__ __launch_bounds__(kDispThreads) void dispatch_hist(const int32_t* __restrict__ idx,
+                                                              const float* __restrict__ w, int P, int K, int C,
+                                                              int32_t* __restrict__ bcnt) {
+  __shared__ DispatchLds<kDispThreads> L;
+  dispatch_hist_part<kDispThreads>(L, ArraySource{idx, w}, P, K, C, bcnt);
+}
+
+__global__ __launch_bounds__(kDispThreads) void dispatch_scatter(const int32_t* __restrict__ idx,
+                                                                 const float* __restrict__ w, int P, int K, int C,
+                                                                 int nb, const int32_t* __restrict__ bcnt,
+                                                                 int32_t* __restrict__ counts,
+                                                                 int32_t* __restrict__ offsets,
+                                                                 int32_t* __restrict__ perm,
+                                                                 float* __restrict__ perm_w, int32_t* __restrict__ inv) {
+  __shared__ DispatchLds<kDispThreads> L;
+  dispatch_scatter_part<kDispThreads>(L, ArraySource{idx, w}, P, K, C, nb, bcnt, counts, offsets, perm, perm_w, inv);
+}
+
+// Pairs per workgroup of the chip-wide sort: whole 8192-pair chunks, at most 128 workgroups.
+DispatchSplit dispatch_split(long long P) {
+  DispatchSplit d{1, (int)P};
+  if (P <= kDispChunk) return d;
+  long long C = (P + kDispMaxParts - 1) / kDispMaxParts;
+  C = (C + kDispChunk - 1) / kDispChunk * kDispChunk;
+  d.C = (int)C;
+  d.nb = (int)((P + C - 1) / C);
+  return d;
+}
+
+size_t dispatch_ws_bytes(long long P, int K) {
+  const DispatchSplit d = dispatch_split(P);
+  return d.nb > 1 ? (size_t)d.nb * K * sizeof(int32_t) : 0;
+}
+
 hipError_t launch_dispatch(const int32_t* idx, const float* w, int P, int K, int32_t* counts, int32_t* offsets,
-                           int32_t* perm, float* perm_w, int32_t* inv, hipStream_t s) {
+                           int32_t* perm, float* perm_w, int32_t* inv, void* ws, hipStream_t s) {
+  const DispatchSplit d = dispatch_split(P);
+  if (d.nb > 1 && ws != nullptr) {
+    int32_t* bcnt = reinterpret_cast<int32_t*>(ws);
+    hipLaunchKernelGGL(dispatch_hist, dim3(d.nb), dim3(kDispThreads), 0, s, idx, w, P, K, d.C, bcnt);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(dispatch_scatter, dim3(d.nb), dim3(kDispThreads), 0, s, idx, w, P, K, d.C, d.nb, bcnt, counts,
+                       offsets, perm, perm_w, inv);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(dispatch_single, dim3(1), dim3(kDispThreads), 0, s, idx, w, P, K, counts, offsets, perm, perm_w,
                      inv);
   return hipGetLastError();

@@ -1,6 +1,6 @@
-// Single-workgroup stable counting sort of routed pairs by adapter (MoLoRA pages,
-// thelatestinai.com, Table 1 rows "Histogram computation" and "Pointer arrays"; Figure 2
-// right: tokens grouped by their selected adapter).
+// Stable counting sort of routed pairs by adapter (MoLoRA pages, thelatestinai.com, Table 1
+// rows "Histogram computation" and "Pointer arrays"; Figure 2 right: tokens grouped by their
+// selected adapter), in one workgroup or, for many pairs, in two chip-wide launches.
 //
 // NT threads (NW = NT/64 waves).  Pairs are produced by a source functor src(p) -> (e, w).
 //   pass 1  wave64 "match" masks (ballots over the bits of the adapter index) give each group
@@ -39,18 +39,131 @@ struct DispatchLds {
   int wcnt[kDispMaxE * NW * 64];
 };
 
-// src(p) returns adapter e (outside [0, K) = unrouted) and gate weight w of pair p < P.
+constexpr int kDispChunk = 8192;  // pairs per pass of one 1024-thread workgroup (8 per thread)
+
+// Pairs c0 + j*NT + tid (j < E, below c1) from the source: adapter (outside [0, K) = unrouted)
+// and gate weight; missing pairs get -1.
+template <int NT, typename Src>
+__device__ __forceinline__ void disp_load(Src src, int c0, int c1, int E, int (&ev)[kDispMaxE], float (&wv)[kDispMaxE]) {
+#pragma unroll
+  for (int j = 0; j < kDispMaxE; ++j) {
+    ev[j] = -1;
+    wv[j] = 0.f;
+    const int p = c0 + j * NT + (int)threadIdx.x;
+    if (j < E && p < c1) src(p, ev[j], wv[j]);
+  }
+}
+
+// Histogram of loaded pairs into L.cnt: one LDS atomic per group of equal adapters of a wave.
+template <int NT>
+__device__ __forceinline__ void disp_count(DispatchLds<NT>& L, const int (&ev)[kDispMaxE], int E, int K, int nbits) {
+  const int lane = threadIdx.x & 63;
+  const uint64_t lt = lanemask_lt(lane);
+#pragma unroll
+  for (int j = 0; j < kDispMaxE; ++j) {
+    if (j < E) {
+      const bool v = (ev[j] >= 0) && (ev[j] < K);
+      const uint64_t m = match_mask(ev[j], v, nbits);
+      if (v && (m & lt) == 0) atomicAdd(&L.cnt[ev[j]], __popcll(m));
+    }
+  }
+}
+
+// Stable scatter of the loaded pairs c0 + j*NT + tid: pair p of adapter e goes to
+// L.offs[e] + L.base[e] + (its rank among the chunk's pairs of e in ascending p); L.base[e]
+// then advances by the chunk's count.  Callers set L.offs and L.base.
+template <int NT>
+__device__ void disp_scatter(DispatchLds<NT>& L, int (&ev)[kDispMaxE], const float (&wv)[kDispMaxE], int c0, int c1,
+                             int E, int K, int nbits, int32_t* __restrict__ perm, float* __restrict__ perm_w,
+                             int32_t* __restrict__ inv) {
+  constexpr int NW = NT / kWave;
+  constexpr int TPA = NT / 64;  // threads per adapter in the scan
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const uint64_t lt = lanemask_lt(lane);
+  for (int i = tid; i < E * NW * 64; i += NT) L.wcnt[i] = 0;
+  __syncthreads();
+  int rk[kDispMaxE];
+#pragma unroll
+  for (int j = 0; j < kDispMaxE; ++j) {
+    rk[j] = 0;
+    if (j < E) {
+      const bool v = (ev[j] >= 0) && (ev[j] < K);
+      const uint64_t m = match_mask(ev[j], v, nbits);
+      if (v) {
+        rk[j] = __popcll(m & lt);
+        if (rk[j] == 0) L.wcnt[(j * NW + wave) * 64 + ev[j]] = __popcll(m);
+      } else {
+        ev[j] = -1;
+      }
+    }
+  }
+  __syncthreads();
+  {
+    // adapter ae's E*NW group sizes in (j, wave) order, split over TPA threads of one wave;
+    // thread pi takes the entries [pi * E * NW / TPA, (pi + 1) * E * NW / TPA)
+    const int ae = tid / TPA, pi = tid % TPA;
+    constexpr int PER = kDispMaxE * NW / TPA;  // upper bound of entries per thread
+    const int per = E * NW / TPA;
+    int loc[PER];
+    int sum = 0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      loc[i] = 0;
+      if (i < per) {
+        loc[i] = L.wcnt[(pi * per + i) * 64 + ae];
+        sum += loc[i];
+      }
+    }
+    int incl = sum;
+#pragma unroll
+    for (int d = 1; d < TPA; d <<= 1) {
+      const int o = __shfl_up(incl, d, TPA);
+      if (pi >= d) incl += o;
+    }
+    const int b0 = (ae < K) ? L.offs[ae] + L.base[ae] : 0;
+    int run = b0 + incl - sum;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      if (i < per) {
+        L.wcnt[(pi * per + i) * 64 + ae] = run;
+        run += loc[i];
+      }
+    }
+    if (pi == TPA - 1 && ae < K) L.base[ae] = L.base[ae] + incl;  // same wave read base[ae] above
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < kDispMaxE; ++j) {
+    if (j < E) {
+      const int p = c0 + j * NT + tid;
+      if (ev[j] >= 0) {
+        const int pos = L.wcnt[(j * NW + wave) * 64 + ev[j]] + rk[j];
+        perm[pos] = p;
+        perm_w[pos] = wv[j];
+        if (inv != nullptr) inv[p] = pos;
+      } else if (p < c1 && inv != nullptr) {
+        inv[p] = -1;
+      }
+    }
+  }
+  __syncthreads();
+}
+
+__device__ __forceinline__ int disp_nbits(int K) {
+  int nbits = 0;
+  while ((1 << nbits) < K) ++nbits;
+  return nbits;
+}
+
+// One workgroup sorts all P pairs: histogram, scan, scatter.  src(p) returns adapter e
+// (outside [0, K) = unrouted) and gate weight w of pair p < P.
 template <int NT, typename Src>
 __device__ void dispatch_block(DispatchLds<NT>& L, Src src, int P, int K, int32_t* __restrict__ counts,
                                int32_t* __restrict__ offsets, int32_t* __restrict__ perm, float* __restrict__ perm_w,
                                int32_t* __restrict__ inv) {
-  constexpr int NW = NT / kWave;
-  constexpr int TPA = NT / 64;  // threads per adapter in the scan
-  static_assert(NT % 64 == 0 && TPA >= 1 && TPA <= 16, "dispatch block size");
+  static_assert(NT % 64 == 0 && NT / 64 >= 1 && NT / 64 <= 16, "dispatch block size");
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const uint64_t lt = lanemask_lt(lane);
-  int nbits = 0;
-  while ((1 << nbits) < K) ++nbits;
+  const int nbits = disp_nbits(K);
   int E = (P + NT - 1) / NT;
   if (E < 1) E = 1;
   if (E > kDispMaxE) E = kDispMaxE;
@@ -59,29 +172,14 @@ __device__ void dispatch_block(DispatchLds<NT>& L, Src src, int P, int K, int32_
     L.base[tid] = 0;
   }
   __syncthreads();
-
-  // pass 1: histogram.  Each chunk's source reads are issued together; when all pairs fit in
-  // one chunk the values stay in registers for pass 2.
+  // pass 1: histogram.  When all pairs fit in one chunk the values stay in registers for pass 2.
   const int chunk = E * NT;
   const bool one_chunk = P <= chunk;
   int ev[kDispMaxE];
   float wv[kDispMaxE];
   for (int c0 = 0; c0 < P; c0 += chunk) {
-#pragma unroll
-    for (int j = 0; j < kDispMaxE; ++j) {
-      ev[j] = -1;
-      wv[j] = 0.f;
-      const int p = c0 + j * NT + tid;
-      if (j < E && p < P) src(p, ev[j], wv[j]);
-    }
-#pragma unroll
-    for (int j = 0; j < kDispMaxE; ++j) {
-      if (j < E) {
-        const bool v = (ev[j] >= 0) && (ev[j] < K);
-        const uint64_t m = match_mask(ev[j], v, nbits);
-        if (v && (m & lt) == 0) atomicAdd(&L.cnt[ev[j]], __popcll(m));
-      }
-    }
+    disp_load<NT>(src, c0, P, E, ev, wv);
+    disp_count<NT>(L, ev, E, K, nbits);
   }
   __syncthreads();
   if (wave == 0) {
@@ -95,85 +193,73 @@ __device__ void dispatch_block(DispatchLds<NT>& L, Src src, int P, int K, int32_
     if (lane == 0) offsets[0] = 0;
   }
   __syncthreads();
-
   // pass 2: stable scatter
   for (int c0 = 0; c0 < P; c0 += chunk) {
-    for (int i = tid; i < E * NW * 64; i += NT) L.wcnt[i] = 0;
-    if (!one_chunk) {
-#pragma unroll
-      for (int j = 0; j < kDispMaxE; ++j) {
-        ev[j] = -1;
-        wv[j] = 0.f;
-        const int p = c0 + j * NT + tid;
-        if (j < E && p < P) src(p, ev[j], wv[j]);
+    if (!one_chunk) disp_load<NT>(src, c0, P, E, ev, wv);
+    disp_scatter<NT>(L, ev, wv, c0, P, E, K, nbits, perm, perm_w, inv);
+  }
+}
+
+// Several workgroups (chip-wide sort, two launches).  Workgroup b owns pairs [b*C, (b+1)*C).
+// Launch 1: its histogram to bcnt[b][K].
+template <int NT, typename Src>
+__device__ void dispatch_hist_part(DispatchLds<NT>& L, Src src, int P, int K, int C, int32_t* __restrict__ bcnt) {
+  const int tid = threadIdx.x;
+  const int nbits = disp_nbits(K);
+  if (tid < 64) L.cnt[tid] = 0;
+  __syncthreads();
+  const int c0 = blockIdx.x * C, c1 = min(P, c0 + C);
+  int ev[kDispMaxE];
+  float wv[kDispMaxE];
+  for (int s0 = c0; s0 < c1; s0 += kDispMaxE * NT) {
+    disp_load<NT>(src, s0, c1, kDispMaxE, ev, wv);
+    disp_count<NT>(L, ev, kDispMaxE, K, nbits);
+  }
+  __syncthreads();
+  if (tid < K) bcnt[(size_t)blockIdx.x * K + tid] = L.cnt[tid];
+}
+
+// Launch 2: every workgroup sums the nb histograms (totals and the part before its own range),
+// scans the totals into offsets (workgroup 0 writes counts and offsets) and scatters its range.
+template <int NT, typename Src>
+__device__ void dispatch_scatter_part(DispatchLds<NT>& L, Src src, int P, int K, int C, int nb,
+                                      const int32_t* __restrict__ bcnt, int32_t* __restrict__ counts,
+                                      int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
+                                      float* __restrict__ perm_w, int32_t* __restrict__ inv) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nbits = disp_nbits(K);
+  const int b = blockIdx.x;
+  if (tid < 64) {
+    int tot = 0, pre = 0;
+    if (tid < K)
+      for (int j = 0; j < nb; ++j) {
+        const int c = bcnt[(size_t)j * K + tid];
+        tot += c;
+        pre += j < b ? c : 0;
       }
+    L.cnt[tid] = tot;
+    L.base[tid] = pre;
+  }
+  __syncthreads();
+  if (wave == 0) {
+    const int c = (lane < K) ? L.cnt[lane] : 0;
+    const int incl = wave_incl_scan(c, lane);
+    if (lane < K) L.offs[lane] = incl - c;
+    if (b == 0) {
+      if (lane < K) {
+        counts[lane] = c;
+        offsets[lane + 1] = incl;
+      }
+      if (lane == 0) offsets[0] = 0;
     }
-    __syncthreads();
-    int rk[kDispMaxE];
-#pragma unroll
-    for (int j = 0; j < kDispMaxE; ++j) {
-      rk[j] = 0;
-      if (j < E) {
-        const bool v = (ev[j] >= 0) && (ev[j] < K);
-        const uint64_t m = match_mask(ev[j], v, nbits);
-        if (v) {
-          rk[j] = __popcll(m & lt);
-          if (rk[j] == 0) L.wcnt[(j * NW + wave) * 64 + ev[j]] = __popcll(m);
-        } else {
-          ev[j] = -1;
-        }
-      }
-    }
-    __syncthreads();
-    {
-      // adapter ae's E*NW group sizes in (j, wave) order, split over TPA threads of one wave;
-      // thread pi takes the entries [pi * E * NW / TPA, (pi + 1) * E * NW / TPA)
-      const int ae = tid / TPA, pi = tid % TPA;
-      constexpr int PER = kDispMaxE * NW / TPA;  // upper bound of entries per thread
-      const int per = E * NW / TPA;
-      int loc[PER];
-      int sum = 0;
-#pragma unroll
-      for (int i = 0; i < PER; ++i) {
-        loc[i] = 0;
-        if (i < per) {
-          loc[i] = L.wcnt[(pi * per + i) * 64 + ae];
-          sum += loc[i];
-        }
-      }
-      int incl = sum;
-#pragma unroll
-      for (int d = 1; d < TPA; d <<= 1) {
-        const int o = __shfl_up(incl, d, TPA);
-        if (pi >= d) incl += o;
-      }
-      const int b0 = (ae < K) ? L.offs[ae] + L.base[ae] : 0;
-      int run = b0 + incl - sum;
-#pragma unroll
-      for (int i = 0; i < PER; ++i) {
-        if (i < per) {
-          L.wcnt[(pi * per + i) * 64 + ae] = run;
-          run += loc[i];
-        }
-      }
-      if (pi == TPA - 1 && ae < K) L.base[ae] = L.base[ae] + incl;  // same wave read base[ae] above
-    }
-    __syncthreads();
-#pragma unroll
-    for (int j = 0; j < kDispMaxE; ++j) {
-      if (j < E) {
-        const int p = c0 + j * NT + tid;
-        if (ev[j] >= 0) {
-          const int pos = L.wcnt[(j * NW + wave) * 64 + ev[j]] + rk[j];
-          perm[pos] = p;
-          perm_w[pos] = wv[j];
-          if (inv != nullptr) inv[p] = pos;
-        } else if (p < P && inv != nullptr) {
-          inv[p] = -1;
-        }
-      }
-    }
-    __syncthreads();
+  }
+  __syncthreads();
+  const int c0 = b * C, c1 = min(P, c0 + C);
+  int ev[kDispMaxE];
+  float wv[kDispMaxE];
+  for (int s0 = c0; s0 < c1; s0 += kDispMaxE * NT) {
+    disp_load<NT>(src, s0, c1, kDispMaxE, ev, wv);
+    disp_scatter<NT>(L, ev, wv, s0, c1, kDispMaxE, K, nbits, perm, perm_w, inv);
   }
 }
 

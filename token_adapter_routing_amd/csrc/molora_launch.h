@@ -27,9 +27,16 @@ hipError_t launch_route_topk(const uint16_t* x, int N, int d, const uint16_t* W1
                              const uint16_t* W2, const float* b2, float* logits, int K, int k,
                              int32_t* idx, float* w, uint8_t* flags, hipStream_t s);
 
-hipError_t launch_dispatch(const int32_t* idx, const float* w, int P, int K, int32_t* counts,
-                           int32_t* offsets, int32_t* perm, float* perm_w, int32_t* inv,
-                           hipStream_t s);
+// Chip-wide dispatch split: nb workgroups of C pairs (nb == 1: one workgroup sorts all).
+struct DispatchSplit {
+  int nb, C;
+};
+constexpr int kDispMaxParts = 128;
+DispatchSplit dispatch_split(long long P);
+size_t dispatch_ws_bytes(long long P, int K);  // per-workgroup counts of the chip-wide sort
+// ws: at least dispatch_ws_bytes(P, K) bytes, or nullptr (then one workgroup sorts all pairs)
+hipError_t launch_dispatch(const int32_t* idx, const float* w, int P, int K, int32_t* counts, int32_t* offsets,
+                           int32_t* perm, float* perm_w, int32_t* inv, void* ws, hipStream_t s);
 
 hipError_t launch_relayout(const uint16_t* A, const uint16_t* B, int d_in, int d_out, int r,
                            int r_pad, uint16_t* At, uint16_t* Bt, hipStream_t s);
