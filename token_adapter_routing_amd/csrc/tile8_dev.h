@@ -379,6 +379,37 @@ __device__ __forceinline__ void t8_main(const T8Args& a, T8Lds<RB>& L, T8Stream<
     }
     return;
   }
+  if (JB == 8 && nU == 2 && myunits <= 2) {
+    // two adapters (a tile across a run boundary), at most two units: b0 already holds the
+    // first unit's pieces of the first adapter; each next batch is requested before the
+    // current batch's MFMAs
+    const uint16_t* Bf = adapter_B<INDIRECT>(a.tgt, e0);
+    const uint16_t* Bs = adapter_B<INDIRECT>(a.tgt, __builtin_ctz(used & (used - 1)));
+    const int cba = st.c0 + wave * kT8Unit, cbb = cba + NW * kT8Unit;
+    const bool two = myunits > 1;
+    bf16x8_t hh[RB], hl[RB];
+    f32x4_t o[8];
+    t8_load_b<RB, JB>(b1, Bs, r_pad, cba, st.cend, lane, 0);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) o[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    t8_h_operands<RB>(L, 0, cba + kT8Unit > st.cend, lane, hh, hl);
+    t8_expand_mfma<RB, JB>(o, hh, hl, b0, 0);
+    t8_load_b<RB, JB>(b0, Bf, r_pad, two ? cbb : cba, st.cend, lane, 0);
+    t8_h_operands<RB>(L, 1, cba + kT8Unit > st.cend, lane, hh, hl);
+    t8_expand_mfma<RB, JB>(o, hh, hl, b1, 0);
+    t8_store_y<Y0F32, YF32>(o, y0c0, a, st.trow, t8_block_col(cba, st.cend, G), n);
+    if (two) {
+      t8_load_b<RB, JB>(b1, Bs, r_pad, cbb, st.cend, lane, 0);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) o[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      t8_h_operands<RB>(L, 0, cbb + kT8Unit > st.cend, lane, hh, hl);
+      t8_expand_mfma<RB, JB>(o, hh, hl, b0, 0);
+      t8_h_operands<RB>(L, 1, cbb + kT8Unit > st.cend, lane, hh, hl);
+      t8_expand_mfma<RB, JB>(o, hh, hl, b1, 0);
+      t8_store_y<Y0F32, YF32>(o, y0c1, a, st.trow, t8_block_col(cbb, st.cend, G), n);
+    }
+    return;
+  }
   // several adapters (or large ranks): per unit, every adapter's pieces in batches of JB MFMA
   // columns
   for (int ui = 0; ui < myunits; ++ui) {
