@@ -210,7 +210,7 @@ int molora_dispatch(const int32_t *idx, const float *w, int N, int k, int K,
  *           _BLOCK (64 consecutive tokens per block, two launches: the shrink
  *           split over workgroups by 512-wide slices of d_in, writing partial
  *           sums to the workspace, then the expand split by 512-wide slices of
- *           d_out; needs K <= 16 and r <= 32)
+ *           d_out; needs K <= 16)
  *   ws      device workspace of at least molora_apply_workspace() bytes for
  *           the same N, k, y_dtype and path (no initial contents needed; for
  *           k > 1 on the grouped path with a bf16 y it holds an fp32 [N][d_out]

@@ -129,6 +129,7 @@ SHAPES = [
     (700, 512, 512, 64, 64, 1),   # 64-row grouped tiles over 64 adapters
     (90, 256, 2048, 16, 48, 2),   # few tiles: output columns split over workgroups
     (4100, 128, 256, 2, 16, 2),   # one reduction step, long segments
+    (256, 2048, 6144, 16, 64, 2), # decode batch of the 28-layer stack, down-projection shape
 ]
 
 
@@ -138,8 +139,6 @@ def test_apply_shapes_paths(N, d_in, d_out, K, r, k, path):
     m = need_gpu()
     if path in (3, 4) and K > 16:
         pytest.skip("the tile and block paths take K <= 16")
-    if path == 4 and r > 32:
-        pytest.skip("the block path takes r <= 32")
     g = np.random.default_rng(N * 31 + d_in + K * 7 + r + k)
     xb = synth.to_bf16_bits(g.standard_normal((N, d_in)).astype(np.float32))
     Ab = synth.to_bf16_bits((g.standard_normal((K, d_in, r)) / np.sqrt(d_in)).astype(np.float32))
@@ -166,11 +165,13 @@ def test_apply_shapes_paths(N, d_in, d_out, K, r, k, path):
     check_bf16_output(host(yb16), ref)
 
 
+@pytest.mark.parametrize("path", [1, 2])
 @pytest.mark.parametrize("k,r", [(2, 16), (3, 64), (1, 64)])
 @pytest.mark.parametrize("y_dtype", [torch.float32, torch.bfloat16])
-def test_grouped_in_place_multi_slot(k, r, y_dtype):
-    """In-place grouped apply (y0 is y) on the 64-row tiles: per-slot passes and the fp32 carry
-    must leave unrouted tokens untouched and give the out-of-place result bit for bit."""
+def test_grouped_in_place_multi_slot(k, r, y_dtype, path):
+    """In-place grouped apply (y0 is y) on the 64-row tiles (path 1) and the split-shrink
+    grouped expand (path 2): per-rank passes and the fp32 carry must leave unrouted tokens
+    untouched and give the out-of-place result bit for bit."""
     m = need_gpu()
     N, d_in, d_out, K = 333, 384, 768, 8
     g = np.random.default_rng(7 * k + r)
@@ -187,9 +188,9 @@ def test_grouped_in_place_multi_slot(k, r, y_dtype):
     counts, offsets, perm, perm_w, inv = m.molora_dispatch(dev(idx), dev(w), K, k)
     ref = oracle_from_gpu_routing(tg, 2.0, idx, w, K, k)
     y0 = dev_bf16(yb).to(y_dtype)
-    out = m.molora_apply(hs, dev_bf16(xb), y0, offsets, perm, perm_w, inv, k=k, y_dtype=y_dtype, path=1)
+    out = m.molora_apply(hs, dev_bf16(xb), y0, offsets, perm, perm_w, inv, k=k, y_dtype=y_dtype, path=path)
     yin = y0.clone()
-    m.molora_apply(hs, dev_bf16(xb), yin, offsets, perm, perm_w, inv, k=k, y=yin, path=1)
+    m.molora_apply(hs, dev_bf16(xb), yin, offsets, perm, perm_w, inv, k=k, y=yin, path=path)
     np.testing.assert_array_equal(host(yin), host(out))
     np.testing.assert_array_equal(host(yin)[::11], f64(yb)[::11])
     if y_dtype == torch.float32:

@@ -261,7 +261,7 @@ __global__ __launch_bounds__(kT8Threads) void step_vocab(StepArgs a) {
 }
 
 // --------------------------------------------------------------------------------------
-// 64-token blocks, shrink launch then expand launch (any k, K <= 16, r <= 32): routing from
+// 64-token blocks, shrink launch then expand launch (any k, K <= 16): routing from
 // the dispatch outputs.  Lane i of a wave holds offsets[i]; the adapter of grouped position q
 // is the number of segment starts offsets[1 .. K-1] at or below q.
 struct BlockApplyArgs {
@@ -680,7 +680,9 @@ struct ExpandArgs {
   TargetDev tgt;
   const void* y0;
   void* y;
-  const int32_t* offsets;
+  const int32_t* offsets;  // expand_grouped_k1: grouped start of each key (key0 .. key0 + K)
+  const int32_t* order;    // expand_grouped_k1: row -> grouped position of the shrink (nullptr: the row)
+  int key0;
   const int32_t* perm;
   const int32_t* inv;
   const float* hpart;
@@ -692,7 +694,9 @@ struct ExpandArgs {
   int main_blocks;
 };
 
-// k = 1, small batches: grid = tile slots * col_groups (+ copy blocks).
+// One adapter per token (k = 1), or one pass over the j-th routed pairs of the tokens (k > 1:
+// keys key0 .. key0 + K of the rank-sorted order, rows mapped to the shrink's grouped positions
+// by `order`): grid = tile slots * col_groups (+ copy blocks).
 template <int RB, bool INDIRECT, bool Y0F32, bool YF32>
 __global__ __launch_bounds__(256) void expand_grouped_k1(ExpandArgs a) {
   constexpr size_t y0b = Y0F32 ? 4 : 2, yb = YF32 ? 4 : 2;
@@ -704,11 +708,12 @@ __global__ __launch_bounds__(256) void expand_grouped_k1(ExpandArgs a) {
   }
   const int g = b % a.col_groups, T = b / a.col_groups;
   int e, row0, nrows;
-  if (!find_tile(a.offsets, a.K, T, lane, e, row0, nrows)) return;
+  if (!find_tile(a.offsets + a.key0, a.K, T, lane, e, row0, nrows)) return;
   const int n = lane & 15, G = lane >> 4;
   const bool valid = n < nrows;
-  const int q = row0 + (valid ? n : 0);
-  const int tok = a.perm[q];
+  const int qr = row0 + (valid ? n : 0);
+  const int q = a.order != nullptr ? a.order[qr] : qr;  // the row's grouped position in the shrink
+  const int tok = a.perm[q] / a.k;
   const uint16_t* Bt = adapter_B<INDIRECT>(a.tgt, e);
   const int d_out = a.tgt.d_out;
   const int cols = d_out / a.col_groups;
@@ -818,7 +823,7 @@ int apply_resolve_path(int N, int k, int path, int K, int r_pad) {
   // few, small adapters: tile-local.  Ranks <= 32: grouped (faster than the split-reduction
   // skinny path at every decode batch measured, 1 .. 2048 tokens).  Ranks above 32: the 64-row
   // grouped tiles from 1024 pairs on; below that their serial per-tile pipeline is slower than
-  // the skinny path's d_in split.
+  // the skinny path's split reductions (the 64-token blocks give too few workgroups there).
   if (K <= kT8MaxU && r_pad <= 32 && P >= 192) return 3;
   if (r_pad <= 32) return 1;
   return P >= 1024 ? 1 : 2;
@@ -863,7 +868,9 @@ size_t apply_ws_bytes(int N, int k, int K, int r_pad, int d_in, int d_out, bool 
   if (p == 1 && use_gm(k, K, r_pad)) return gm_ws_bytes(N, k, K, d_out, y_f32);
   if (p == 3 || (k == 1 && p == 1)) return 0;
   const int ns = (p == 2) ? skinny_splits(d_in) : 1;
-  return (size_t)ns * (size_t)N * (size_t)k * (size_t)r_pad * sizeof(float);
+  const size_t hpart = ((size_t)ns * (size_t)N * (size_t)k * (size_t)r_pad * sizeof(float) + 255) / 256 * 256;
+  if (p == 2 && k > 1 && k * K <= 64) return hpart + gm_ws_bytes(N, k, K, d_out, y_f32);  // rank passes
+  return hpart;
 }
 
 static int env_int(const char* name, int dflt) {
@@ -986,15 +993,40 @@ static hipError_t launch_expand_tok_t(const ExpandArgs& ea, int grid, hipStream_
     case 4: { constexpr int RB = 4; __VA_ARGS__; } break; \
     default: return hipErrorInvalidValue;                 \
   }
-// Runtime RB -> instance for the kernels limited to ranks <= 32.
-#define MOLORA_DISPATCH_RB12(RBV, ...)                    \
-  switch (RBV) {                                          \
-    case 1: { constexpr int RB = 1; __VA_ARGS__; } break; \
-    case 2: { constexpr int RB = 2; __VA_ARGS__; } break; \
-    default: return hipErrorInvalidValue;                 \
-  }
 #define MOLORA_DISPATCH_BOOL(V, NAME, ...) \
   if (V) { constexpr bool NAME = true; __VA_ARGS__; } else { constexpr bool NAME = false; __VA_ARGS__; }
+
+// Rank sort of the grouped pairs for k > 1 passes, in the workspace at wsb: counts2 and offsets2
+// (256-byte block), perm2 and w2 (the order and weights), the chip-wide sort's counts; z is the
+// fp32 carry of the passes (y itself when y is fp32, else the buffer after the sort).
+struct RankSort {
+  int32_t* offsets2;
+  int32_t* perm2;
+  float* w2;
+  float* z;
+};
+static hipError_t launch_rank_sort(const ApplyLaunch& a, char* wsb, long long P, hipStream_t s, RankSort& o) {
+  int32_t* counts2 = reinterpret_cast<int32_t*>(wsb);
+  o.offsets2 = counts2 + a.k * a.K;
+  const size_t head = gm_head_bytes(a.k, a.K);
+  o.perm2 = reinterpret_cast<int32_t*>(wsb + head);
+  o.w2 = reinterpret_cast<float*>(wsb + head + (size_t)P * sizeof(int32_t));
+  int32_t* bcnt = reinterpret_cast<int32_t*>(wsb + head + gm_order_bytes(P));
+  o.z = a.y_f32 ? reinterpret_cast<float*>(a.y) : reinterpret_cast<float*>(wsb + gm_sort_bytes(P, a.k, a.K));
+  const DispatchSplit ds = dispatch_split(P);
+  if (ds.nb > 1) {
+    hipLaunchKernelGGL(slot_hist, dim3(ds.nb), dim3(1024), 0, s, a.offsets, a.perm, a.perm_w, a.inv, a.k, a.K, ds.C,
+                       bcnt);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(slot_scatter, dim3(ds.nb), dim3(1024), 0, s, a.offsets, a.perm, a.perm_w, a.inv, a.k, a.K, ds.C,
+                       ds.nb, bcnt, counts2, o.offsets2, o.perm2, o.w2);
+  } else {
+    hipLaunchKernelGGL(slot_sort, dim3(1), dim3(1024), 0, s, a.offsets, a.perm, a.perm_w, a.inv, a.k, a.K, counts2,
+                       o.offsets2, o.perm2, o.w2);
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_apply(const ApplyLaunch& a, hipStream_t s) {
   const long long P = (long long)a.N * a.k;
@@ -1017,7 +1049,7 @@ hipError_t launch_apply(const ApplyLaunch& a, hipStream_t s) {
     BlockApplyArgs ba;
     ba.b = block_args(a, a.ws);
     ba.offsets = a.offsets; ba.perm_w = a.perm_w; ba.inv = a.inv;
-    MOLORA_DISPATCH_RB12(RBv, MOLORA_DISPATCH_BOOL(a.indirect, IND, MOLORA_DISPATCH_BOOL(a.y0_f32, Y0F,
+    MOLORA_DISPATCH_RB(RBv, MOLORA_DISPATCH_BOOL(a.indirect, IND, MOLORA_DISPATCH_BOOL(a.y0_f32, Y0F,
         MOLORA_DISPATCH_BOOL(a.y_f32, YF, err = (launch_block_t<RB, IND, Y0F, YF>(ba, s))))));
     return err;
   }
@@ -1058,28 +1090,13 @@ hipError_t launch_apply(const ApplyLaunch& a, hipStream_t s) {
           err = (launch_finish_t<Y0F, YF>(a.y0, nullptr, a.y, a.inv, a.N, 1, a.tgt.d_out, true, false, s))));
       return err;
     }
-    char* wsb = reinterpret_cast<char*>(a.ws);
-    int32_t* counts2 = reinterpret_cast<int32_t*>(wsb);
-    int32_t* offsets2 = counts2 + a.k * a.K;
-    const size_t head = gm_head_bytes(a.k, a.K);
-    int32_t* perm2 = reinterpret_cast<int32_t*>(wsb + head);
-    float* w2 = reinterpret_cast<float*>(wsb + head + (size_t)P * sizeof(int32_t));
-    int32_t* bcnt = reinterpret_cast<int32_t*>(wsb + head + gm_order_bytes(P));
-    float* z = a.y_f32 ? reinterpret_cast<float*>(a.y) : reinterpret_cast<float*>(wsb + gm_sort_bytes(P, a.k, a.K));
-    const DispatchSplit ds = dispatch_split(P);
-    if (ds.nb > 1) {
-      hipLaunchKernelGGL(slot_hist, dim3(ds.nb), dim3(1024), 0, s, a.offsets, a.perm, a.perm_w, a.inv, a.k, a.K, ds.C,
-                         bcnt);
-      err = hipGetLastError();
-      if (err != hipSuccess) return err;
-      hipLaunchKernelGGL(slot_scatter, dim3(ds.nb), dim3(1024), 0, s, a.offsets, a.perm, a.perm_w, a.inv, a.k, a.K,
-                         ds.C, ds.nb, bcnt, counts2, offsets2, perm2, w2);
-    } else {
-      hipLaunchKernelGGL(slot_sort, dim3(1), dim3(1024), 0, s, a.offsets, a.perm, a.perm_w, a.inv, a.k, a.K, counts2,
-                         offsets2, perm2, w2);
-    }
-    err = hipGetLastError();
+    RankSort rs;
+    err = launch_rank_sort(a, reinterpret_cast<char*>(a.ws), P, s, rs);
     if (err != hipSuccess) return err;
+    int32_t* offsets2 = rs.offsets2;
+    int32_t* perm2 = rs.perm2;
+    float* w2 = rs.w2;
+    float* z = rs.z;
     ga.offsets = offsets2; ga.order = perm2; ga.wts = w2;
     for (int j = 0; j < a.k; ++j) {
       ga.key0 = j * a.K;
@@ -1120,6 +1137,8 @@ hipError_t launch_apply(const ApplyLaunch& a, hipStream_t s) {
   ExpandArgs ea;
   ea.tgt = a.tgt; ea.y0 = a.y0; ea.y = a.y; ea.offsets = a.offsets; ea.perm = a.perm; ea.inv = a.inv;
   ea.hpart = a.ws; ea.P = P; ea.nsplit = nsplit; ea.N = a.N; ea.K = a.K; ea.k = a.k;
+  ea.order = nullptr;
+  ea.key0 = 0;
   if (a.k == 1) {
     ea.col_groups = choose_col_groups(tiles, a.tgt.d_out, 512, 4);
     ea.main_blocks = (int)tiles * ea.col_groups;
@@ -1127,6 +1146,36 @@ hipError_t launch_apply(const ApplyLaunch& a, hipStream_t s) {
     const int grid = ea.main_blocks + ea.copy_blocks;
     MOLORA_DISPATCH_RB(RBv, MOLORA_DISPATCH_BOOL(a.indirect, IND, MOLORA_DISPATCH_BOOL(a.y0_f32, Y0F,
         MOLORA_DISPATCH_BOOL(a.y_f32, YF, err = (launch_expand_k1_t<RB, IND, Y0F, YF>(ea, grid, s))))));
+    return err;
+  }
+  if (a.path == 2 && a.k * a.K <= 64) {
+    // one grouped expand pass per rank of the routed pairs (as on the 64-row tiles), over
+    // (adapter, 16-row tile, column group) workgroups, the sum carried in fp32
+    const size_t hpart = ((size_t)nsplit * (size_t)P * (size_t)a.tgt.r_pad * sizeof(float) + 255) / 256 * 256;
+    RankSort rs;
+    err = launch_rank_sort(a, reinterpret_cast<char*>(a.ws) + hpart, P, s, rs);
+    if (err != hipSuccess) return err;
+    const long long ptiles = (a.N + 15) / 16 + a.K;  // 16-row tiles of one pass
+    ea.offsets = rs.offsets2;
+    ea.order = rs.perm2;
+    ea.col_groups = choose_col_groups(ptiles, a.tgt.d_out, 512, 4);
+    ea.main_blocks = (int)(ptiles * ea.col_groups);
+    ea.copy_blocks = 0;
+    const int grid = ea.main_blocks;
+    for (int j = 0; j < a.k; ++j) {
+      const bool last = j == a.k - 1;
+      ea.key0 = j * a.K;
+      ea.y0 = j == 0 ? a.y0 : static_cast<const void*>(rs.z);
+      ea.y = last ? a.y : static_cast<void*>(rs.z);
+      const bool y0f = j == 0 ? (bool)a.y0_f32 : true, yf = last ? (bool)a.y_f32 : true;
+      MOLORA_DISPATCH_RB(RBv, MOLORA_DISPATCH_BOOL(a.indirect, IND, MOLORA_DISPATCH_BOOL(y0f, Y0F,
+          MOLORA_DISPATCH_BOOL(yf, YF, err = (launch_expand_k1_t<RB, IND, Y0F, YF>(ea, grid, s))))));
+      if (err != hipSuccess) return err;
+    }
+    const bool copy_z = static_cast<void*>(rs.z) != a.y;
+    if (in_place && !copy_z) return err;
+    MOLORA_DISPATCH_BOOL(a.y0_f32, Y0F, MOLORA_DISPATCH_BOOL(a.y_f32, YF,
+        err = (launch_finish_t<Y0F, YF>(a.y0, rs.z, a.y, a.inv, a.N, a.k, a.tgt.d_out, !in_place, copy_z, s))));
     return err;
   }
   const long long ttiles = (a.N + 15) / 16;
@@ -1159,7 +1208,7 @@ hipError_t launch_step_vocab(const StepVocabLaunch& a, hipStream_t s) {
   hipError_t err = hipSuccess;
   if (a.ws != nullptr) {
     const BlockArgs b = block_args(a.apply, a.ws);
-    MOLORA_DISPATCH_RB12(RBv, MOLORA_DISPATCH_BOOL(a.apply.indirect, IND, MOLORA_DISPATCH_BOOL(a.apply.y0_f32, Y0F,
+    MOLORA_DISPATCH_RB(RBv, MOLORA_DISPATCH_BOOL(a.apply.indirect, IND, MOLORA_DISPATCH_BOOL(a.apply.y0_f32, Y0F,
         MOLORA_DISPATCH_BOOL(a.apply.y_f32, YF, err = (launch_step_block_t<RB, IND, Y0F, YF>(sa, b, s))))));
     return err;
   }

@@ -29,7 +29,11 @@ constexpr int kBSlice = 512;      // reduction or output columns per workgroup
 constexpr int kBWaves = 8;
 constexpr int kBThreads = kBWaves * kWave;
 constexpr int kBMaxU = 16;        // adapters per block (K <= 16)
-constexpr int kBGroup = 2;        // adapters whose pieces are staged in LDS at once
+// adapters whose pieces are staged in LDS at once (one at ranks above 32: LDS size)
+template <int RB>
+constexpr int block_group() {
+  return RB <= 2 ? 2 : 1;
+}
 
 struct BlockArgs {
   TargetDev tgt;
@@ -52,9 +56,9 @@ __host__ __device__ inline size_t block_part_floats(int nblocks, int slotmax, in
 template <int RB>
 struct BlockLds {
   // shrink: A pieces [slot][step][chunk][u][64 lanes x 16 B]; expand: B^T rows [slot][512][r_pad]
-  alignas(16) uint16_t ab[kBGroup][kBSlice * RB * 16];
+  alignas(16) uint16_t ab[block_group<RB>()][kBSlice * RB * 16];
   float red[2][4][16][RB * 16 + 4];          // shrink: the two reduction halves of each row block
-  alignas(16) uint16_t hb[kBGroup][2][kBTok][RB * 16];  // expand: h hi / lo [slot][part][token][rank]
+  alignas(16) uint16_t hb[block_group<RB>()][2][kBTok][RB * 16];  // expand: h hi / lo [slot][part][token][rank]
   float wt[kBMaxU][kBTok];                    // expand: weight of (slot, token)
 };
 
@@ -117,8 +121,8 @@ __device__ void block_shrink(const BlockArgs& a, BlockLds<RB>& L, const Route& r
   const int nU = __popc(used);
   const size_t piece = (size_t)RB * 16 * kStepK;  // elements of one step's pieces (4 chunks x RB)
   uint32_t rem = used;
-  for (int base = 0; base < nU; base += kBGroup) {
-    const int ng = min(kBGroup, nU - base);
+  for (int base = 0; base < nU; base += block_group<RB>()) {
+    const int ng = min(block_group<RB>(), nU - base);
     // stage the group's A pieces of the slice: [g][step][chunk][u][1 KB]
     uint32_t r2 = rem;
     for (int g = 0; g < ng; ++g) {
@@ -208,7 +212,7 @@ __device__ void block_expand(const BlockArgs& a, BlockLds<RB>& L, const Route& r
   // first group's B^T rows of the slice, straight into LDS
   {
     uint32_t r2 = used;
-    for (int g = 0; g < min(kBGroup, nU); ++g) {
+    for (int g = 0; g < min(block_group<RB>(), nU); ++g) {
       lds_copy_1k(L.ab[g], adapter_B<INDIRECT>(a.tgt, __builtin_ctz(r2)) + (size_t)c0 * r_pad,
                   (c1 - c0) * r_pad * 2);
       r2 &= r2 - 1;
@@ -223,8 +227,8 @@ __device__ void block_expand(const BlockArgs& a, BlockLds<RB>& L, const Route& r
     o1[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
   uint32_t rem = used;
-  for (int base = 0; base < nU; base += kBGroup) {
-    const int ng = min(kBGroup, nU - base);
+  for (int base = 0; base < nU; base += block_group<RB>()) {
+    const int ng = min(block_group<RB>(), nU - base);
     if (base > 0) {
       uint32_t r2 = rem;
       for (int g = 0; g < ng; ++g) {

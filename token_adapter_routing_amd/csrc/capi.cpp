@@ -295,7 +295,6 @@ int molora_apply(const molora_hotset* hs, int target, const void* x, const void*
   if (path < MOLORA_PATH_AUTO || path > MOLORA_PATH_BLOCK) return fail(MOLORA_EINVAL, "unknown path %d", path);
   if ((path == MOLORA_PATH_TILE || path == MOLORA_PATH_BLOCK) && hs->K > molora::kApplyTileMaxAdapters)
     return fail(MOLORA_ENOTSUP, "the tile and block paths support K <= %d", molora::kApplyTileMaxAdapters);
-  if (path == MOLORA_PATH_BLOCK && hs->r_pad > 32) return fail(MOLORA_ENOTSUP, "the block path supports r <= 32");
   if (y0 == y && y0_dtype != y_dtype) return fail(MOLORA_EINVAL, "in-place apply needs y0_dtype == y_dtype");
   if (N == 0) return ok();
   if (x == nullptr || y0 == nullptr || y == nullptr) return fail(MOLORA_EINVAL, "x, y0 or y is NULL");
@@ -366,7 +365,6 @@ int molora_step_vocab(const molora_hotset* hs, int target, const int32_t* ids, i
   if (!aligned(ids, 4) || !aligned(idx, 4) || !aligned(w, 4) || !aligned(counts, 4) || !aligned(offsets, 4) ||
       !aligned(perm, 4) || !aligned(perm_w, 4) || !aligned(inv, 4))
     return fail(MOLORA_EINVAL, "misaligned pointer");
-  if (ws != nullptr && hs->r_pad > 32) return fail(MOLORA_ENOTSUP, "the block step supports r <= 32 (pass no workspace)");
   if (ws != nullptr) {
     const size_t need = molora::step_ws_bytes(N, hs->K, hs->r_pad, hs->tg[target].d_in);
     if (ws_bytes < need || !aligned(ws, 256))
