@@ -726,15 +726,24 @@ __global__ __launch_bounds__(256) void expand_grouped_k1(ExpandArgs a) {
   unsigned vmask = 0;
 #pragma unroll
   for (int i = 0; i < 4; ++i) vmask |= ((4 * G + i) < nrows ? 1u : 0u) << i;
+  // the first block's y0 rows and B pieces do not depend on h: they go out before the partials
+  RowChunk<Y0F32> cur;
+  u32x4_t bv[8][RB];
+  const int blk0 = min(wave, nblk - 1);
+  load_row_chunk<Y0F32>(cur, y0rows, c0 + blk0 * kColBlock, n);
+  expand_load_b<RB>(bv, Bt, a.tgt.r_pad, c0 + blk0 * kColBlock, lane);
+  __builtin_amdgcn_sched_barrier(0);
   bf16x8_t hb[RB];
   h_operand_from_ws<RB>(hb, a.hpart, a.P, a.nsplit, q, valid, lane);
   for (int blk = wave; blk < nblk; blk += 4) {
-    RowChunk<Y0F32> cur;
-    load_row_chunk<Y0F32>(cur, y0rows, c0 + blk * kColBlock, n);
+    if (blk != wave) {
+      load_row_chunk<Y0F32>(cur, y0rows, c0 + blk * kColBlock, n);
+      expand_load_b<RB>(bv, Bt, a.tgt.r_pad, c0 + blk * kColBlock, lane);
+    }
     f32x4_t o[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) o[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    expand_mfma<RB>(o, hb, Bt, a.tgt.r_pad, c0 + blk * kColBlock, lane);
+    expand_mfma_regs<RB>(o, hb, bv);
     epilogue_store<Y0F32, YF32>(o, cur, yrows, c0 + blk * kColBlock, n, vmask);
   }
 }

@@ -186,20 +186,29 @@ __device__ __forceinline__ void h_operand_from_lds(bf16x8_t (&hb)[RB], const flo
 // Expand of one 128-column block at colbase (a multiple of 128) of the slab's B^T.  All of
 // the block's B pieces are requested before the first MFMA (8 * RB loads in flight).
 template <int RB>
-__device__ __forceinline__ void expand_mfma(f32x4_t (&acc)[8], const bf16x8_t (&hb)[RB],
-                                            const uint16_t* __restrict__ Bt, int r_pad, int colbase, int lane) {
+__device__ __forceinline__ void expand_load_b(u32x4_t (&bv)[8][RB], const uint16_t* __restrict__ Bt, int r_pad,
+                                              int colbase, int lane) {
   const int n = lane & 15, G = lane >> 4;
   const uint16_t* bp = Bt + (size_t)(colbase + n) * r_pad + (G & 1) * 8;
-  u32x4_t bv[8][RB];
 #pragma unroll
   for (int j = 0; j < 8; ++j)
 #pragma unroll
     for (int u = 0; u < RB; ++u) bv[j][u] = ld16(bp + (size_t)j * 16 * r_pad + u * 16);
-  __builtin_amdgcn_sched_barrier(0);  // keep every load of the block ahead of the MFMAs
+}
+template <int RB>
+__device__ __forceinline__ void expand_mfma_regs(f32x4_t (&acc)[8], const bf16x8_t (&hb)[RB], const u32x4_t (&bv)[8][RB]) {
 #pragma unroll
   for (int j = 0; j < 8; ++j)
 #pragma unroll
     for (int u = 0; u < RB; ++u) acc[j] = mfma16x16x32(hb[u], as_bf16x8(bv[j][u]), acc[j]);
+}
+template <int RB>
+__device__ __forceinline__ void expand_mfma(f32x4_t (&acc)[8], const bf16x8_t (&hb)[RB],
+                                            const uint16_t* __restrict__ Bt, int r_pad, int colbase, int lane) {
+  u32x4_t bv[8][RB];
+  expand_load_b<RB>(bv, Bt, r_pad, colbase, lane);
+  __builtin_amdgcn_sched_barrier(0);  // keep every load of the block ahead of the MFMAs
+  expand_mfma_regs<RB>(acc, hb, bv);
 }
 
 // 8 contiguous columns (colbase + 8n ..) of the 4 token rows 4G..4G+3 of one block.
