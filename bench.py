@@ -79,6 +79,7 @@ def parse():
     p.add_argument("--rows", default="C0,C2,C3,C4,C4stack",
                    help="other configurations to measure beside the headline (comma list, or 'none')")
     p.add_argument("--row-reps", type=int, default=100, help="graph replays per timed row entry")
+    p.add_argument("--stack-replays", type=int, default=1000, help="single-graph replays of the 28-layer stack row")
     return p.parse_args()
 
 
@@ -273,7 +274,7 @@ def main():
     if rows:
         del sets, g_all, g_one
         torch.cuda.synchronize()
-        out["rows"] = measure_rows(m, torch, dev, rows, args.row_reps)
+        out["rows"] = measure_rows(m, torch, dev, rows, args.row_reps, args.stack_replays)
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
@@ -311,7 +312,7 @@ def graph_ms(torch, fn, reps, warm=5, inner=1):
     return e0.elapsed_time(e1) / (reps * inner), g, stream
 
 
-def measure_rows(m, torch, dev, rows, reps):
+def measure_rows(m, torch, dev, rows, reps, stack_replays=1000):
     import synth
 
     def bf(bits):
@@ -348,7 +349,7 @@ def measure_rows(m, torch, dev, rows, reps):
     if "C4" in rows:
         res["C4_stress"] = row_stress(m, torch, dev, bf, f32, max(20, reps // 4))
     if "C4stack" in rows:
-        res["C4_stack"] = row_stack(m, torch, dev)
+        res["C4_stack"] = row_stack(m, torch, dev, replays=stack_replays)
     torch.cuda.synchronize()
     return res
 
