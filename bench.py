@@ -538,20 +538,20 @@ def row_stack(m, torch, dev, layers=28, B=256, K=16, r=64, k=2, replays=1000):
         meta = (torch.empty(K, dtype=torch.int32, device=dev), torch.empty(K + 1, dtype=torch.int32, device=dev),
                 torch.empty(B * k, dtype=torch.int32, device=dev), torch.empty(B * k, dtype=torch.float32, device=dev),
                 torch.empty(B * k, dtype=torch.int32, device=dev))
-        wss = [torch.zeros(max(1, m.molora_apply_workspace(hs, ti, B, k, m.PATH_AUTO, torch.bfloat16)), dtype=torch.uint8, device=dev)
-               for ti in range(len(targets))]
-        layer_objs.append((hs, xs, ys, logits, idx, w, meta, wss))
+        tids = list(range(len(targets)))
+        ws = torch.zeros(max(1, m.molora_apply_multi_workspace(hs, tids, B, k, m.PATH_AUTO, torch.bfloat16)),
+                         dtype=torch.uint8, device=dev)
+        layer_objs.append((hs, xs, ys, logits, idx, w, meta, ws))
         nbytes += (3 * B * 2048 + B * 6144) * 2 + sum(2 * B * d_out * 2 for (_, _, d_out) in targets)
         nbytes += sum(K * (d_in + d_out) * r * 2 for (_, d_in, d_out) in targets) + logits.numel() * 4
     torch.cuda.synchronize()
 
     def step():
-        for (hs, xs, ys, logits, idx, w, meta, wss) in layer_objs:
+        # per layer: routing, dispatch, then the 7 projections in one multi-target apply
+        for (hs, xs, ys, logits, idx, w, meta, ws) in layer_objs:
             m.molora_route_topk(k, K, logits=logits, idx=idx, w=w, want_flags=False)
             m.molora_dispatch(idx, w, K, k, out=meta)
-            for ti in range(len(xs)):
-                m.molora_apply(hs, xs[ti], ys[ti], meta[1], meta[2], meta[3], meta[4], k=k, target=ti, y=ys[ti],
-                               ws=wss[ti])
+            m.molora_apply_multi(hs, xs, ys, meta[1], meta[2], meta[3], meta[4], k=k, ys=ys, ws=ws)
 
     ms, g, stream = graph_ms(torch, step, 20)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(replays)]

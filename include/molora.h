@@ -227,6 +227,30 @@ int molora_apply(const molora_hotset *hs, int target, const void *x, const void 
                  void *ws, size_t ws_bytes, void *stream);
 
 /* ------------------------------------------------------------------------
+ * Several projections sharing one routing (thelatestinai.com, Table 10: the
+ * adapter targets of a layer, q/k/v/o/gate/up/down, all follow the token's
+ * routing decision): the apply of molora_apply for n <= 8 distinct targets,
+ * with one launch per phase for all of them on the skinny path (and the
+ * rank sort of k > 1 done once); other paths apply the targets in turn.
+ *   targets host int [n]: hot-set target of each projection (distinct)
+ *   x, y0, y host arrays [n] of device pointers, as in molora_apply for
+ *           targets[i] (y[i] distinct; y0[i] may equal y[i]); one y0_dtype
+ *           and one y_dtype for all
+ *   N, k, offsets, perm, perm_w, inv, path: as in molora_apply (shared)
+ *   ws      device workspace of at least molora_apply_multi_workspace()
+ *           bytes, 256-byte aligned (no initial contents needed)
+ * Results equal n molora_apply calls bit for bit.  Errors as molora_apply;
+ * MOLORA_ENOTSUP for n outside [1, 8].
+ * ------------------------------------------------------------------------ */
+int molora_apply_multi_workspace(const molora_hotset *hs, int n, const int *targets, int N,
+                                 int k, int y_dtype, int path, size_t *bytes);
+int molora_apply_multi(const molora_hotset *hs, int n, const int *targets,
+                       const void *const *x, const void *const *y0, int y0_dtype,
+                       void *const *y, int y_dtype, int N, int k, const int32_t *offsets,
+                       const int32_t *perm, const float *perm_w, const int32_t *inv, int path,
+                       void *ws, size_t ws_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
  * The whole vocabulary-routed step in one launch (thelatestinai.com, Table 1:
  * routing decision, histogram, pointer arrays and grouped dispatch; Figure 2:
  * per-token weighted sum; Table 4 "Per-token + Graph": the step as few

@@ -28,7 +28,7 @@ def lib():
 def test_every_declared_symbol_is_exported_and_bound():
     L = lib()
     names = declared_functions()
-    assert len(names) == 13, names
+    assert len(names) == 15, names
     for n in names:
         assert hasattr(L, n), n
     assert sorted(m.exported_symbols()) == names
@@ -82,6 +82,9 @@ def test_host_validation_without_launch():
     assert L.molora_dispatch_workspace(2048, 4, 16, ctypes.byref(sz)) == 0 and sz.value == 0  # 8192 pairs: one workgroup
     assert L.molora_dispatch_workspace(16384, 4, 16, ctypes.byref(sz)) == 0 and sz.value == 8 * 16 * 4
     assert L.molora_apply_workspace(nul, 0, 4, 1, 0, 0, ctypes.byref(sz)) == 1
+    # multi-target apply: NULL hot set
+    assert L.molora_apply_multi_workspace(nul, 2, nul, 4, 1, 0, 0, ctypes.byref(sz)) == 1
+    assert L.molora_apply_multi(nul, 2, nul, nul, nul, 0, nul, 0, 4, 1, nul, nul, nul, nul, 0, nul, 0, nul) == 1
     # hotset_init: unaligned slab is rejected before any launch
     tg = (MoloraTarget * 1)(MoloraTarget(128, 128, 2, 2))
     h = ctypes.c_void_p()

@@ -329,3 +329,48 @@ def test_zero_tokens_is_noop():
     y = m.molora_apply(hs, x, x.clone(), torch.zeros(5, dtype=torch.int32, device="cuda"), empty, empty.float(),
                        empty, k=1)
     assert y.shape == (0, 512)
+
+
+@pytest.mark.parametrize("k,r,path", [(2, 64, 0), (1, 64, 0), (2, 16, 2), (3, 32, 1), (2, 16, 3)])
+@pytest.mark.parametrize("y_dtype", [torch.float32, torch.bfloat16])
+def test_apply_multi_equals_single_calls(k, r, path, y_dtype):
+    """Several projections sharing one routing in one call (the skinny path fuses the phases
+    over the targets; other paths loop): bit-identical to one molora_apply per target, and
+    within the bars of the oracle."""
+    m = need_gpu()
+    N, K = 256, 16
+    dims = [(512, 512), (512, 256), (512, 1536), (1536, 512)]
+    g = np.random.default_rng(100 + 10 * k + r + path)
+    tgs = []
+    for di, do in dims:
+        xb = synth.to_bf16_bits(g.standard_normal((N, di)).astype(np.float32))
+        Ab = synth.to_bf16_bits((g.standard_normal((K, di, r)) / np.sqrt(di)).astype(np.float32))
+        Bb = synth.to_bf16_bits((g.standard_normal((K, r, do)) / np.sqrt(r)).astype(np.float32))
+        yb = synth.to_bf16_bits(g.standard_normal((N, do)).astype(np.float32))
+        tgs.append(synth.Target("p", di, do, Ab, Bb, xb, yb))
+    oi, ow, _ = route_topk(g.standard_normal((N, K)), k)
+    idx, w = oi.astype(np.int32), ow.astype(np.float32)
+    idx[::9, 0] = -1
+    idx[::13, :] = -1
+    hs = m.molora_hotset_init([(dev_bf16(t.A), dev_bf16(t.B)) for t in tgs], 2.0)
+    counts, offsets, perm, perm_w, inv = m.molora_dispatch(dev(idx), dev(w), K, k)
+    xs = [dev_bf16(t.x) for t in tgs]
+    y0s = [dev_bf16(t.y0).to(y_dtype) for t in tgs]
+    order = [2, 0, 3, 1]  # targets in any order
+    ys = m.molora_apply_multi(hs, [xs[i] for i in order], [y0s[i] for i in order], offsets, perm, perm_w, inv, k=k,
+                              targets=order, y_dtype=y_dtype, path=path)
+    for j, i in enumerate(order):
+        single = m.molora_apply(hs, xs[i], y0s[i], offsets, perm, perm_w, inv, k=k, target=i, y_dtype=y_dtype,
+                                path=path)
+        np.testing.assert_array_equal(host(ys[j]), host(single))
+    t = tgs[3]
+    ref = oracle_from_gpu_routing(t, 2.0, idx, w, K, k)
+    if y_dtype == torch.float32:
+        check_float_output(host(ys[2]), ref, f64(t.y0))
+    else:
+        check_bf16_output(host(ys[2]), ref)
+    # in place: y0 is y for every target
+    yin = [v.clone() for v in y0s]
+    m.molora_apply_multi(hs, xs, yin, offsets, perm, perm_w, inv, k=k, ys=yin, path=path)
+    for i in range(len(dims)):
+        np.testing.assert_array_equal(host(yin[i]), host(ys[order.index(i)]))

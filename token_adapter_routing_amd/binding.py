@@ -50,6 +50,9 @@ _SIGS = {
     "molora_apply_workspace": (_c_i, [_c_p, _c_i, _c_i, _c_i, _c_i, _c_i, ctypes.POINTER(_c_sz)]),
     "molora_apply": (_c_i, [_c_p, _c_i, _c_p, _c_p, _c_i, _c_p, _c_i, _c_i, _c_i, _c_p, _c_p, _c_p, _c_p, _c_i,
                             _c_p, _c_sz, _c_p]),
+    "molora_apply_multi_workspace": (_c_i, [_c_p, _c_i, _c_p, _c_i, _c_i, _c_i, _c_i, ctypes.POINTER(_c_sz)]),
+    "molora_apply_multi": (_c_i, [_c_p, _c_i, _c_p, _c_p, _c_p, _c_i, _c_p, _c_i, _c_i, _c_i,  # hs .. k
+                                  _c_p, _c_p, _c_p, _c_p, _c_i, _c_p, _c_sz, _c_p]),
     "molora_seqpass_meta": (_c_i, [_c_p, _c_i, _c_i, _c_p, _c_p, _c_p, _c_p]),
     "molora_step_vocab": (_c_i, [_c_p, _c_i, _c_p, _c_i, _c_p, _c_p, _c_p, _c_i, _c_p, _c_i,  # hs .. y_dtype
                                  _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p,  # idx, w, counts, offsets, perm, perm_w, inv
@@ -282,6 +285,42 @@ def molora_apply(hs: HotSet, x: torch.Tensor, y0: torch.Tensor, offsets: torch.T
         _ptr(perm_w, torch.float32, "perm_w"), _ptr(inv, torch.int32, "inv"), path,
         _ptr(ws, None, "ws") if ws is not None else None, ws.numel() if ws is not None else 0, _stream(stream)))
     return y
+
+
+def molora_apply_multi_workspace(hs: HotSet, targets: Sequence[int], N: int, k: int, path: int = PATH_AUTO,
+                                 y_dtype=torch.float32) -> int:
+    out = _c_sz()
+    tg = (ctypes.c_int * len(targets))(*targets)
+    code = F32 if y_dtype == torch.float32 else BF16
+    _check(load_library().molora_apply_multi_workspace(hs.handle, len(targets), tg, N, k, code, path,
+                                                       ctypes.byref(out)))
+    return out.value
+
+
+def molora_apply_multi(hs: HotSet, xs: Sequence[torch.Tensor], y0s: Sequence[torch.Tensor], offsets: torch.Tensor,
+                       perm: torch.Tensor, perm_w: torch.Tensor, inv: torch.Tensor, k: int = 1,
+                       targets: Optional[Sequence[int]] = None, ys: Optional[Sequence[torch.Tensor]] = None,
+                       y_dtype=None, path: int = PATH_AUTO, ws: Optional[torch.Tensor] = None, stream=None):
+    """molora_apply for several targets that share one routing (one launch per phase)."""
+    n = len(xs)
+    targets = list(range(n)) if targets is None else list(targets)
+    N = xs[0].shape[0]
+    if ys is None:
+        ys = [torch.empty(N, hs.dims[t][1], dtype=y_dtype or y0s[i].dtype, device=xs[0].device)
+              for i, t in enumerate(targets)]
+    need = molora_apply_multi_workspace(hs, targets, N, k, path, ys[0].dtype)
+    if need and (ws is None or ws.numel() < need):
+        ws = torch.zeros(need, dtype=torch.uint8, device=xs[0].device)
+    tg = (ctypes.c_int * n)(*targets)
+    xp = (_c_p * n)(*[_ptr(x, torch.bfloat16, "x") for x in xs])
+    y0p = (_c_p * n)(*[_ptr(v, None, "y0") for v in y0s])
+    yp = (_c_p * n)(*[_ptr(v, None, "y") for v in ys])
+    _check(load_library().molora_apply_multi(
+        hs.handle, n, tg, xp, y0p, _dtype_code(y0s[0]), yp, _dtype_code(ys[0]), N, k,
+        _ptr(offsets, torch.int32, "offsets"), _ptr(perm, torch.int32, "perm"), _ptr(perm_w, torch.float32, "perm_w"),
+        _ptr(inv, torch.int32, "inv"), path, _ptr(ws, None, "ws") if ws is not None else None,
+        ws.numel() if ws is not None else 0, _stream(stream)))
+    return ys
 
 
 def molora_step_workspace(hs: HotSet, target: int, N: int) -> int:

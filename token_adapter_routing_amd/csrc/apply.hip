@@ -455,11 +455,10 @@ __global__ __launch_bounds__(1024) void slot_scatter(const int32_t* __restrict__
 // y = z (the fp32 pass buffer) for tokens whose last routed pair came before the last pass
 // (copy_z, when z is not y itself).  One wave per 64 tokens.
 template <bool Y0F32, bool YF32>
-__global__ __launch_bounds__(256) void finish_tokens(const void* y0, const float* z, void* y,
-                                                     const int32_t* __restrict__ inv, int N, int k, int d_out,
-                                                     int copy_y0, int copy_z) {
+__device__ __forceinline__ void finish_body(const void* y0, const float* z, void* y, const int32_t* __restrict__ inv,
+                                            int N, int k, int d_out, int copy_y0, int copy_z, int blk) {
   const int lane = threadIdx.x & 63;
-  const int base = (blockIdx.x * 4 + (threadIdx.x >> 6)) * kWave;
+  const int base = (blk * 4 + (threadIdx.x >> 6)) * kWave;
   const int t = base + lane;
   int c = 0;
   if (t < N)
@@ -498,6 +497,12 @@ __global__ __launch_bounds__(256) void finish_tokens(const void* y0, const float
       }
     }
   }
+}
+template <bool Y0F32, bool YF32>
+__global__ __launch_bounds__(256) void finish_tokens(const void* y0, const float* z, void* y,
+                                                     const int32_t* __restrict__ inv, int N, int k, int d_out,
+                                                     int copy_y0, int copy_z) {
+  finish_body<Y0F32, YF32>(y0, z, y, inv, N, k, d_out, copy_y0, copy_z, blockIdx.x);
 }
 
 // --------------------------------------------------------------------------------------
@@ -608,11 +613,9 @@ struct ShrinkArgs {
 
 // grid (tile slots, nsplit).  Writes perm_w * scale * (partial h) for valid rows only.
 template <int RB, bool INDIRECT>
-__global__ __launch_bounds__(256) void shrink_grouped(ShrinkArgs a) {
-  __shared__ float red[RedLds<RB>::kFloats];
+__device__ __forceinline__ void shrink_grouped_body(const ShrinkArgs& a, float* red, int T, int sp) {
   constexpr int RS = RedLds<RB>::RS;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int T = blockIdx.x, sp = blockIdx.y;
   int e, row0, nrows;
   if (!find_tile(a.offsets, a.K, T, lane, e, row0, nrows)) return;
   const int n = lane & 15, G = lane >> 4;
@@ -649,6 +652,11 @@ __global__ __launch_bounds__(256) void shrink_grouped(ShrinkArgs a) {
       st16(dst + i, v);
     }
   }
+}
+template <int RB, bool INDIRECT>
+__global__ __launch_bounds__(256) void shrink_grouped(ShrinkArgs a) {
+  __shared__ float red[RedLds<RB>::kFloats];
+  shrink_grouped_body<RB, INDIRECT>(a, red, blockIdx.x, blockIdx.y);
 }
 
 // Sum the nsplit partials of grouped row q for the lane's rank pieces and split hi/lo.
@@ -698,10 +706,9 @@ struct ExpandArgs {
 // keys key0 .. key0 + K of the rank-sorted order, rows mapped to the shrink's grouped positions
 // by `order`): grid = tile slots * col_groups (+ copy blocks).
 template <int RB, bool INDIRECT, bool Y0F32, bool YF32>
-__global__ __launch_bounds__(256) void expand_grouped_k1(ExpandArgs a) {
+__device__ __forceinline__ void expand_grouped_body(const ExpandArgs& a, int b) {
   constexpr size_t y0b = Y0F32 ? 4 : 2, yb = YF32 ? 4 : 2;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int b = blockIdx.x;
   if (b >= a.main_blocks) {
     copy_unrouted<Y0F32, YF32, 4>(a.y0, a.y, a.inv, a.N, a.tgt.d_out, b - a.main_blocks, a.copy_blocks);
     return;
@@ -746,6 +753,47 @@ __global__ __launch_bounds__(256) void expand_grouped_k1(ExpandArgs a) {
     expand_mfma_regs<RB>(o, hb, bv);
     epilogue_store<Y0F32, YF32>(o, cur, yrows, c0 + blk * kColBlock, n, vmask);
   }
+}
+template <int RB, bool INDIRECT, bool Y0F32, bool YF32>
+__global__ __launch_bounds__(256) void expand_grouped_k1(ExpandArgs a) {
+  expand_grouped_body<RB, INDIRECT, Y0F32, YF32>(a, blockIdx.x);
+}
+
+// Several projections that share one routing (the targets of a layer), one launch per phase:
+// target i's arguments are entry i of an array passed by value; the grid's last dimension
+// selects the entry and workgroups past a target's own grid return.
+constexpr int kMaxMulti = 8;
+struct ShrinkMulti {
+  ShrinkArgs a[kMaxMulti];
+};
+struct ExpandMulti {
+  ExpandArgs a[kMaxMulti];
+};
+struct FinishMulti {
+  const void* y0[kMaxMulti];
+  const float* z[kMaxMulti];
+  void* y[kMaxMulti];
+  int d_out[kMaxMulti];
+  const int32_t* inv;
+  int N, k, copy_y0[kMaxMulti], copy_z[kMaxMulti];
+};
+template <int RB, bool INDIRECT>
+__global__ __launch_bounds__(256) void shrink_grouped_multi(ShrinkMulti m) {
+  __shared__ float red[RedLds<RB>::kFloats];
+  const ShrinkArgs& a = m.a[blockIdx.z];
+  if ((int)blockIdx.y >= a.nsplit) return;
+  shrink_grouped_body<RB, INDIRECT>(a, red, blockIdx.x, blockIdx.y);
+}
+template <int RB, bool INDIRECT, bool Y0F32, bool YF32>
+__global__ __launch_bounds__(256) void expand_grouped_multi(ExpandMulti m) {
+  const ExpandArgs& a = m.a[blockIdx.y];
+  if ((int)blockIdx.x >= a.main_blocks + a.copy_blocks) return;
+  expand_grouped_body<RB, INDIRECT, Y0F32, YF32>(a, blockIdx.x);
+}
+template <bool Y0F32, bool YF32>
+__global__ __launch_bounds__(256) void finish_tokens_multi(FinishMulti m) {
+  const int i = blockIdx.y;
+  finish_body<Y0F32, YF32>(m.y0[i], m.z[i], m.y[i], m.inv, m.N, m.k, m.d_out[i], m.copy_y0[i], m.copy_z[i], blockIdx.x);
 }
 
 // k > 1: grid = ceil(N/16) token tiles * col_groups.  KMAX bounds k (register arrays).
@@ -1200,6 +1248,141 @@ hipError_t launch_apply(const ApplyLaunch& a, hipStream_t s) {
   else { MOLORA_TOK(8) }
 #undef MOLORA_TOK
   return err;
+}
+
+// Several targets sharing one routing.  The skinny path runs each phase for all targets in one
+// launch (the rank sort once); other paths apply the targets in turn, each with its own slice of
+// the workspace.  Workspace: [rank sort] then per target [h partials][fp32 carry].
+static size_t align256(size_t b) { return (b + 255) / 256 * 256; }
+static bool multi_fused(int p, int k, int K) { return p == 2 && (k == 1 || k * K <= 64); }
+
+size_t apply_multi_ws_bytes(int n, const int* d_in, const int* d_out, int N, int k, int K, int r_pad, bool y_f32,
+                            int path) {
+  const int p = apply_resolve_path(N, k, path, K, r_pad);
+  size_t b = 0;
+  if (!multi_fused(p, k, K)) {
+    for (int i = 0; i < n; ++i) b += align256(apply_ws_bytes(N, k, K, r_pad, d_in[i], d_out[i], y_f32, path));
+    return b;
+  }
+  const long long P = (long long)N * k;
+  if (k > 1) b += align256(gm_sort_bytes(P, k, K));
+  for (int i = 0; i < n; ++i) {
+    b += align256((size_t)skinny_splits(d_in[i]) * (size_t)P * (size_t)r_pad * sizeof(float));
+    if (k > 1 && !y_f32) b += align256((size_t)N * d_out[i] * sizeof(float));
+  }
+  return b;
+}
+
+hipError_t launch_apply_multi(const ApplyLaunch* as, int n, hipStream_t s) {
+  const ApplyLaunch& a0 = as[0];
+  hipError_t err = hipSuccess;
+  char* wsb = reinterpret_cast<char*>(a0.ws);
+  if (!multi_fused(a0.path, a0.k, a0.K)) {
+    size_t off = 0;
+    for (int i = 0; i < n; ++i) {
+      ApplyLaunch b = as[i];
+      b.ws = reinterpret_cast<float*>(wsb + off);
+      off += align256(apply_ws_bytes(b.N, b.k, b.K, b.tgt.r_pad, b.tgt.d_in, b.tgt.d_out, b.y_f32, b.path));
+      err = launch_apply(b, s);
+      if (err != hipSuccess) return err;
+    }
+    return err;
+  }
+  const long long P = (long long)a0.N * a0.k;
+  const long long tiles = P / kTileRows + a0.K + 1;
+  const int RBv = a0.tgt.r_pad / 16;
+  size_t off = a0.k > 1 ? align256(gm_sort_bytes(P, a0.k, a0.K)) : 0;
+  ShrinkMulti sm;
+  float* z[kMaxMulti];
+  int max_split = 1;
+  for (int i = 0; i < n; ++i) {
+    const ApplyLaunch& a = as[i];
+    ShrinkArgs& sa = sm.a[i];
+    sa.tgt = a.tgt; sa.x = a.x; sa.offsets = a.offsets; sa.perm = a.perm; sa.perm_w = a.perm_w;
+    sa.K = a.K; sa.k = a.k; sa.scale = a.scale; sa.P = P; sa.nsplit = skinny_splits(a.tgt.d_in);
+    sa.hpart = reinterpret_cast<float*>(wsb + off);
+    off += align256((size_t)sa.nsplit * (size_t)P * (size_t)a.tgt.r_pad * sizeof(float));
+    z[i] = a.y_f32 ? reinterpret_cast<float*>(a.y) : nullptr;
+    if (a.k > 1 && !a.y_f32) {
+      z[i] = reinterpret_cast<float*>(wsb + off);
+      off += align256((size_t)a.N * a.tgt.d_out * sizeof(float));
+    }
+    max_split = std::max(max_split, sa.nsplit);
+  }
+  MOLORA_DISPATCH_RB(RBv, MOLORA_DISPATCH_BOOL(a0.indirect, IND,
+      hipLaunchKernelGGL((shrink_grouped_multi<RB, IND>), dim3((int)tiles, max_split, n), dim3(256), 0, s, sm)));
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+
+  ExpandMulti em;
+  auto expand_args = [&](int i, long long t) {
+    const ApplyLaunch& a = as[i];
+    ExpandArgs& ea = em.a[i];
+    ea.tgt = a.tgt; ea.y0 = a.y0; ea.y = a.y; ea.offsets = a.offsets; ea.perm = a.perm; ea.inv = a.inv;
+    ea.hpart = sm.a[i].hpart; ea.P = P; ea.nsplit = sm.a[i].nsplit; ea.N = a.N; ea.K = a.K; ea.k = a.k;
+    ea.order = nullptr;
+    ea.key0 = 0;
+    ea.col_groups = choose_col_groups(t, a.tgt.d_out, 512, 4);
+    ea.main_blocks = (int)(t * ea.col_groups);
+    ea.copy_blocks = 0;
+    return ea.main_blocks;
+  };
+  if (a0.k == 1) {
+    int gx = 1;
+    for (int i = 0; i < n; ++i) {
+      expand_args(i, tiles);
+      ExpandArgs& ea = em.a[i];
+      ea.copy_blocks = as[i].y0 == as[i].y ? 0 : (int)std::min<long long>((as[i].N + 255) / 256, 64);
+      gx = std::max(gx, ea.main_blocks + ea.copy_blocks);
+    }
+    MOLORA_DISPATCH_RB(RBv, MOLORA_DISPATCH_BOOL(a0.indirect, IND, MOLORA_DISPATCH_BOOL(a0.y0_f32, Y0F,
+        MOLORA_DISPATCH_BOOL(a0.y_f32, YF,
+            hipLaunchKernelGGL((expand_grouped_multi<RB, IND, Y0F, YF>), dim3(gx, n), dim3(256), 0, s, em)))));
+    return hipGetLastError();
+  }
+  // k > 1: the rank sort once (shared routing), then one pass per rank over all targets
+  RankSort rs;
+  err = launch_rank_sort(a0, wsb, P, s, rs);
+  if (err != hipSuccess) return err;
+  const long long ptiles = (a0.N + 15) / 16 + a0.K;
+  int gx = 1;
+  for (int i = 0; i < n; ++i) gx = std::max(gx, expand_args(i, ptiles));
+  for (int i = 0; i < n; ++i) {
+    em.a[i].offsets = rs.offsets2;
+    em.a[i].order = rs.perm2;
+  }
+  for (int j = 0; j < a0.k; ++j) {
+    const bool last = j == a0.k - 1;
+    for (int i = 0; i < n; ++i) {
+      em.a[i].key0 = j * a0.K;
+      em.a[i].y0 = j == 0 ? as[i].y0 : static_cast<const void*>(z[i]);
+      em.a[i].y = last ? as[i].y : static_cast<void*>(z[i]);
+    }
+    const bool y0f = j == 0 ? (bool)a0.y0_f32 : true, yf = last ? (bool)a0.y_f32 : true;
+    MOLORA_DISPATCH_RB(RBv, MOLORA_DISPATCH_BOOL(a0.indirect, IND, MOLORA_DISPATCH_BOOL(y0f, Y0F,
+        MOLORA_DISPATCH_BOOL(yf, YF,
+            hipLaunchKernelGGL((expand_grouped_multi<RB, IND, Y0F, YF>), dim3(gx, n), dim3(256), 0, s, em)))));
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  FinishMulti fm;
+  bool any = false;
+  for (int i = 0; i < n; ++i) {
+    fm.y0[i] = as[i].y0;
+    fm.z[i] = z[i];
+    fm.y[i] = as[i].y;
+    fm.d_out[i] = as[i].tgt.d_out;
+    fm.copy_y0[i] = as[i].y0 != as[i].y;
+    fm.copy_z[i] = static_cast<void*>(z[i]) != as[i].y;
+    any = any || fm.copy_y0[i] || fm.copy_z[i];
+  }
+  if (!any) return err;
+  fm.inv = a0.inv;
+  fm.N = a0.N;
+  fm.k = a0.k;
+  MOLORA_DISPATCH_BOOL(a0.y0_f32, Y0F, MOLORA_DISPATCH_BOOL(a0.y_f32, YF,
+      hipLaunchKernelGGL((finish_tokens_multi<Y0F, YF>), dim3((a0.N + 255) / 256, n), dim3(256), 0, s, fm)));
+  return hipGetLastError();
 }
 
 bool step_vocab_fused(int N) { return N <= kStepMaxN; }

@@ -330,6 +330,92 @@ int molora_apply(const molora_hotset* hs, int target, const void* x, const void*
   return e == hipSuccess ? ok() : hip_fail(e, "apply launch");
 }
 
+static int check_multi_targets(const molora_hotset* hs, int n, const int* targets, int* d_in, int* d_out) {
+  if (hs == nullptr) return fail(MOLORA_EINVAL, "hot set is NULL");
+  if (n < 1 || n > molora::kApplyMaxMulti) return fail(MOLORA_ENOTSUP, "n=%d outside [1, %d]", n, molora::kApplyMaxMulti);
+  if (targets == nullptr) return fail(MOLORA_EINVAL, "targets is NULL");
+  for (int i = 0; i < n; ++i) {
+    if (targets[i] < 0 || targets[i] >= hs->n_targets)
+      return fail(MOLORA_EINVAL, "targets[%d]=%d outside [0, %d)", i, targets[i], hs->n_targets);
+    d_in[i] = hs->tg[targets[i]].d_in;
+    d_out[i] = hs->tg[targets[i]].d_out;
+  }
+  return MOLORA_OK;
+}
+
+int molora_apply_multi_workspace(const molora_hotset* hs, int n, const int* targets, int N, int k, int y_dtype,
+                                 int path, size_t* bytes) {
+  if (bytes == nullptr) return fail(MOLORA_EINVAL, "bytes is NULL");
+  int d_in[molora::kApplyMaxMulti], d_out[molora::kApplyMaxMulti];
+  const int rc = check_multi_targets(hs, n, targets, d_in, d_out);
+  if (rc != MOLORA_OK) return rc;
+  if (N < 0 || k < 1 || k > MOLORA_MAX_TOPK || k > hs->K) return fail(MOLORA_EINVAL, "bad N=%d or k=%d", N, k);
+  if (path < MOLORA_PATH_AUTO || path > MOLORA_PATH_BLOCK) return fail(MOLORA_EINVAL, "unknown path %d", path);
+  if (y_dtype != MOLORA_BF16 && y_dtype != MOLORA_F32) return fail(MOLORA_EINVAL, "unknown dtype");
+  *bytes = molora::apply_multi_ws_bytes(n, d_in, d_out, N, k, hs->K, hs->r_pad, y_dtype == MOLORA_F32, path);
+  return ok();
+}
+
+int molora_apply_multi(const molora_hotset* hs, int n, const int* targets, const void* const* x,
+                       const void* const* y0, int y0_dtype, void* const* y, int y_dtype, int N, int k,
+                       const int32_t* offsets, const int32_t* perm, const float* perm_w, const int32_t* inv, int path,
+                       void* ws, size_t ws_bytes, void* stream) {
+  int d_in[molora::kApplyMaxMulti], d_out[molora::kApplyMaxMulti];
+  const int rc = check_multi_targets(hs, n, targets, d_in, d_out);
+  if (rc != MOLORA_OK) return rc;
+  if (N < 0) return fail(MOLORA_EINVAL, "N=%d < 0", N);
+  if (k < 1 || k > MOLORA_MAX_TOPK || k > hs->K) return fail(MOLORA_ENOTSUP, "k=%d outside [1, min(K, %d)]", k, MOLORA_MAX_TOPK);
+  if ((long long)N * k >= (1ll << 31)) return fail(MOLORA_ENOTSUP, "N*k too large");
+  if ((y0_dtype != MOLORA_BF16 && y0_dtype != MOLORA_F32) || (y_dtype != MOLORA_BF16 && y_dtype != MOLORA_F32))
+    return fail(MOLORA_EINVAL, "unknown dtype");
+  if (path < MOLORA_PATH_AUTO || path > MOLORA_PATH_BLOCK) return fail(MOLORA_EINVAL, "unknown path %d", path);
+  if ((path == MOLORA_PATH_TILE || path == MOLORA_PATH_BLOCK) && hs->K > molora::kApplyTileMaxAdapters)
+    return fail(MOLORA_ENOTSUP, "the tile and block paths support K <= %d", molora::kApplyTileMaxAdapters);
+  if (x == nullptr || y0 == nullptr || y == nullptr) return fail(MOLORA_EINVAL, "x, y0 or y array is NULL");
+  if (N == 0) return ok();
+  for (int i = 0; i < n; ++i) {
+    if (x[i] == nullptr || y0[i] == nullptr || y[i] == nullptr) return fail(MOLORA_EINVAL, "x, y0 or y [%d] is NULL", i);
+    if (!aligned(x[i], 16) || !aligned(y0[i], 16) || !aligned(y[i], 16))
+      return fail(MOLORA_EINVAL, "x, y0 and y [%d] must be 16-byte aligned", i);
+    if (y0[i] == y[i] && y0_dtype != y_dtype) return fail(MOLORA_EINVAL, "in-place apply needs y0_dtype == y_dtype");
+    for (int j = 0; j < i; ++j)
+      if (targets[j] == targets[i] || y[j] == y[i]) return fail(MOLORA_EINVAL, "targets and outputs must be distinct");
+  }
+  if (offsets == nullptr || perm == nullptr || perm_w == nullptr || inv == nullptr)
+    return fail(MOLORA_EINVAL, "offsets, perm, perm_w and inv are required");
+  if (!aligned(offsets, 4) || !aligned(perm, 4) || !aligned(perm_w, 4) || !aligned(inv, 4))
+    return fail(MOLORA_EINVAL, "misaligned pointer");
+  const size_t need = molora::apply_multi_ws_bytes(n, d_in, d_out, N, k, hs->K, hs->r_pad, y_dtype == MOLORA_F32, path);
+  if (need > 0 && (ws == nullptr || ws_bytes < need || !aligned(ws, 256)))
+    return fail(MOLORA_ENOSPC, "workspace of %zu bytes (256-byte aligned) needed, %zu given", need, ws_bytes);
+  molora::ApplyLaunch as[molora::kApplyMaxMulti];
+  const int rp = molora::apply_resolve_path(N, k, path, hs->K, hs->r_pad);
+  for (int i = 0; i < n; ++i) {
+    molora::ApplyLaunch& a = as[i];
+    a = molora::ApplyLaunch{};
+    a.tgt = hs->tg[targets[i]];
+    a.indirect = hs->layout == MOLORA_LAYOUT_INDIRECT;
+    a.x = reinterpret_cast<const uint16_t*>(x[i]);
+    a.y0 = y0[i];
+    a.y = y[i];
+    a.y0_f32 = y0_dtype == MOLORA_F32;
+    a.y_f32 = y_dtype == MOLORA_F32;
+    a.N = N;
+    a.k = k;
+    a.K = hs->K;
+    a.scale = hs->scale;
+    a.offsets = offsets;
+    a.perm = perm;
+    a.perm_w = perm_w;
+    a.inv = inv;
+    a.path = rp;
+    a.ws = reinterpret_cast<float*>(ws);
+    a.col_groups = 0;
+  }
+  const hipError_t e = molora::launch_apply_multi(as, n, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ok() : hip_fail(e, "apply launch");
+}
+
 int molora_step_workspace(const molora_hotset* hs, int target, int N, size_t* bytes) {
   if (bytes == nullptr) return fail(MOLORA_EINVAL, "bytes is NULL");
   if (hs == nullptr) return fail(MOLORA_EINVAL, "hot set is NULL");
