@@ -404,6 +404,22 @@ def row_qwen_layer(m, torch, dev, bf, f32, reps):
                               "pairs_per_s": N * k / (ms * 1e-3),
                               "roofline_frac": compulsory / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9)}
         del g, wss
+    # the 7 projections in one multi-target apply (one launch per phase on the fused paths)
+    tids = list(range(len(c.targets)))
+    for name, path in (("multi_auto", m.PATH_AUTO), ("multi_skinny", m.PATH_SKINNY)):
+        mws = torch.zeros(max(1, m.molora_apply_multi_workspace(hs, tids, N, k, path, torch.bfloat16)),
+                          dtype=torch.uint8, device=dev)
+
+        def step():
+            m.molora_route_topk(k, K, x=tx[0], W1=W1, b1=b1, W2=W2, b2=b2, logits=logits, idx=idx, w=w, flags=flags)
+            m.molora_dispatch(idx, w, K, k, out=meta)
+            m.molora_apply_multi(hs, tx, y0, meta[1], meta[2], meta[3], meta[4], k=k, ys=y, path=path, ws=mws)
+
+        ms, g, _ = graph_ms(torch, step, reps)
+        out["paths"][name] = {"ms_per_step": ms, "routed_tokens_per_s": N / (ms * 1e-3),
+                              "pairs_per_s": N * k / (ms * 1e-3),
+                              "roofline_frac": compulsory / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9)}
+        del g, mws
     best = min(out["paths"].items(), key=lambda kv: kv[1]["ms_per_step"])
     out["best_path"] = best[0]
     out["routed_tokens_per_s"] = best[1]["routed_tokens_per_s"]

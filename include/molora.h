@@ -230,13 +230,16 @@ int molora_apply(const molora_hotset *hs, int target, const void *x, const void 
  * Several projections sharing one routing (thelatestinai.com, Table 10: the
  * adapter targets of a layer, q/k/v/o/gate/up/down, all follow the token's
  * routing decision): the apply of molora_apply for n <= 8 distinct targets,
- * with one launch per phase for all of them on the skinny path (and the
- * rank sort of k > 1 done once); other paths apply the targets in turn.
+ * with one launch per phase for all of them on the skinny path (the rank
+ * sort of k > 1 done once) and on the block path; the grouped and tile
+ * paths apply the targets in turn.
  *   targets host int [n]: hot-set target of each projection (distinct)
  *   x, y0, y host arrays [n] of device pointers, as in molora_apply for
  *           targets[i] (y[i] distinct; y0[i] may equal y[i]); one y0_dtype
  *           and one y_dtype for all
- *   N, k, offsets, perm, perm_w, inv, path: as in molora_apply (shared)
+ *   N, k, offsets, perm, perm_w, inv, path: as in molora_apply (shared);
+ *           AUTO as in molora_apply, except _BLOCK instead of _TILE when
+ *           k > 1 and n > 1
  *   ws      device workspace of at least molora_apply_multi_workspace()
  *           bytes, 256-byte aligned (no initial contents needed)
  * Results equal n molora_apply calls bit for bit.  Errors as molora_apply;

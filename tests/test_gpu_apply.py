@@ -331,7 +331,7 @@ def test_zero_tokens_is_noop():
     assert y.shape == (0, 512)
 
 
-@pytest.mark.parametrize("k,r,path", [(2, 64, 0), (1, 64, 0), (2, 16, 2), (3, 32, 1), (2, 16, 3)])
+@pytest.mark.parametrize("k,r,path", [(2, 64, 0), (1, 64, 0), (2, 16, 2), (3, 32, 1), (2, 16, 3), (2, 16, 4), (1, 64, 4)])
 @pytest.mark.parametrize("y_dtype", [torch.float32, torch.bfloat16])
 def test_apply_multi_equals_single_calls(k, r, path, y_dtype):
     """Several projections sharing one routing in one call (the skinny path fuses the phases

@@ -302,6 +302,30 @@ __global__ __launch_bounds__(kBThreads, 2) void expand_block(BlockApplyArgs a) {
   block_expand<RB, INDIRECT, Y0F32, YF32>(a.b, L, rt, blockIdx.x / a.b.cslices, blockIdx.x % a.b.cslices, [] {});
 }
 
+// Several targets sharing one routing: entry blockIdx.y of the array, workgroups past that
+// target's own grid return.
+struct BlockMulti {
+  BlockApplyArgs a[8];
+};
+template <int RB, bool INDIRECT>
+__global__ __launch_bounds__(kBThreads, 2) void shrink_block_multi(BlockMulti m) {
+  __shared__ BlockLds<RB> L;
+  const BlockApplyArgs& a = m.a[blockIdx.y];
+  if ((int)blockIdx.x >= a.b.nblocks * a.b.kslices) return;
+  const int lane = threadIdx.x & 63;
+  const DispatchRoute rt{a.inv, a.perm_w, a.b.k, a.b.K, a.b.scale, a.offsets[min(lane, a.b.K)]};
+  block_shrink<RB, INDIRECT>(a.b, L, rt, blockIdx.x / a.b.kslices, blockIdx.x % a.b.kslices);
+}
+template <int RB, bool INDIRECT, bool Y0F32, bool YF32>
+__global__ __launch_bounds__(kBThreads, 2) void expand_block_multi(BlockMulti m) {
+  __shared__ BlockLds<RB> L;
+  const BlockApplyArgs& a = m.a[blockIdx.y];
+  if ((int)blockIdx.x >= a.b.nblocks * a.b.cslices) return;
+  const int lane = threadIdx.x & 63;
+  const DispatchRoute rt{a.inv, a.perm_w, a.b.k, a.b.K, a.b.scale, a.offsets[min(lane, a.b.K)]};
+  block_expand<RB, INDIRECT, Y0F32, YF32>(a.b, L, rt, blockIdx.x / a.b.cslices, blockIdx.x % a.b.cslices, [] {});
+}
+
 // The vocabulary-routed step on 64-token blocks (k = 1), as two launches: the shrink routes
 // its block from the ids; the expand does too, and its workgroups of column slice 0 write their
 // block's share of the dispatch outputs (adapter counts over all N ids and over the ids before
@@ -1256,12 +1280,20 @@ hipError_t launch_apply(const ApplyLaunch& a, hipStream_t s) {
 static size_t align256(size_t b) { return (b + 255) / 256 * 256; }
 static bool multi_fused(int p, int k, int K) { return p == 2 && (k == 1 || k * K <= 64); }
 
+// AUTO for several targets: as for one, except that tile-local applies with k > 1 become the
+// 64-token blocks, whose two launches then cover every target (measured faster on a 7-target
+// layer with top-2 routing).
+int apply_multi_resolve_path(int n, int N, int k, int path, int K, int r_pad) {
+  const int p = apply_resolve_path(N, k, path, K, r_pad);
+  return (path == 0 && p == 3 && k > 1 && n > 1) ? 4 : p;
+}
+
 size_t apply_multi_ws_bytes(int n, const int* d_in, const int* d_out, int N, int k, int K, int r_pad, bool y_f32,
                             int path) {
-  const int p = apply_resolve_path(N, k, path, K, r_pad);
+  const int p = apply_multi_resolve_path(n, N, k, path, K, r_pad);
   size_t b = 0;
   if (!multi_fused(p, k, K)) {
-    for (int i = 0; i < n; ++i) b += align256(apply_ws_bytes(N, k, K, r_pad, d_in[i], d_out[i], y_f32, path));
+    for (int i = 0; i < n; ++i) b += align256(apply_ws_bytes(N, k, K, r_pad, d_in[i], d_out[i], y_f32, p));
     return b;
   }
   const long long P = (long long)N * k;
@@ -1277,6 +1309,32 @@ hipError_t launch_apply_multi(const ApplyLaunch* as, int n, hipStream_t s) {
   const ApplyLaunch& a0 = as[0];
   hipError_t err = hipSuccess;
   char* wsb = reinterpret_cast<char*>(a0.ws);
+  if (a0.path == 4) {
+    // 64-token blocks: one shrink launch and one expand launch for all targets
+    static_assert(sizeof(BlockMulti) / sizeof(BlockApplyArgs) == kMaxMulti, "multi size");
+    BlockMulti bm;
+    size_t off = 0;
+    int gs = 1, ge = 1;
+    for (int i = 0; i < n; ++i) {
+      const ApplyLaunch& b = as[i];
+      bm.a[i].b = block_args(b, wsb + off);
+      bm.a[i].offsets = b.offsets;
+      bm.a[i].perm_w = b.perm_w;
+      bm.a[i].inv = b.inv;
+      off += align256(apply_ws_bytes(b.N, b.k, b.K, b.tgt.r_pad, b.tgt.d_in, b.tgt.d_out, b.y_f32, b.path));
+      gs = std::max(gs, bm.a[i].b.nblocks * bm.a[i].b.kslices);
+      ge = std::max(ge, bm.a[i].b.nblocks * bm.a[i].b.cslices);
+    }
+    const int RBv = a0.tgt.r_pad / 16;
+    MOLORA_DISPATCH_RB(RBv, MOLORA_DISPATCH_BOOL(a0.indirect, IND,
+        hipLaunchKernelGGL((shrink_block_multi<RB, IND>), dim3(gs, n), dim3(kBThreads), 0, s, bm)));
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    MOLORA_DISPATCH_RB(RBv, MOLORA_DISPATCH_BOOL(a0.indirect, IND, MOLORA_DISPATCH_BOOL(a0.y0_f32, Y0F,
+        MOLORA_DISPATCH_BOOL(a0.y_f32, YF,
+            hipLaunchKernelGGL((expand_block_multi<RB, IND, Y0F, YF>), dim3(ge, n), dim3(kBThreads), 0, s, bm)))));
+    return hipGetLastError();
+  }
   if (!multi_fused(a0.path, a0.k, a0.K)) {
     size_t off = 0;
     for (int i = 0; i < n; ++i) {

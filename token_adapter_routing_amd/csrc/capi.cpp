@@ -389,7 +389,7 @@ int molora_apply_multi(const molora_hotset* hs, int n, const int* targets, const
   if (need > 0 && (ws == nullptr || ws_bytes < need || !aligned(ws, 256)))
     return fail(MOLORA_ENOSPC, "workspace of %zu bytes (256-byte aligned) needed, %zu given", need, ws_bytes);
   molora::ApplyLaunch as[molora::kApplyMaxMulti];
-  const int rp = molora::apply_resolve_path(N, k, path, hs->K, hs->r_pad);
+  const int rp = molora::apply_multi_resolve_path(n, N, k, path, hs->K, hs->r_pad);
   for (int i = 0; i < n; ++i) {
     molora::ApplyLaunch& a = as[i];
     a = molora::ApplyLaunch{};

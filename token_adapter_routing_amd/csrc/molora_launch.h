@@ -67,6 +67,7 @@ hipError_t launch_apply(const ApplyLaunch& a, hipStream_t s);
 // Targets sharing one routing (same N, k, K, rank, path and dtypes); as[0].ws holds the
 // whole workspace of apply_multi_ws_bytes bytes.
 constexpr int kApplyMaxMulti = 8;
+int apply_multi_resolve_path(int n, int N, int k, int path, int K, int r_pad);
 size_t apply_multi_ws_bytes(int n, const int* d_in, const int* d_out, int N, int k, int K, int r_pad, bool y_f32,
                             int path);
 hipError_t launch_apply_multi(const ApplyLaunch* as, int n, hipStream_t s);
