@@ -331,7 +331,8 @@ def test_zero_tokens_is_noop():
     assert y.shape == (0, 512)
 
 
-@pytest.mark.parametrize("k,r,path", [(2, 64, 0), (1, 64, 0), (2, 16, 2), (3, 32, 1), (2, 16, 3), (2, 16, 4), (1, 64, 4)])
+@pytest.mark.parametrize("k,r,path", [(2, 64, 0), (1, 64, 0), (2, 16, 0), (2, 16, 2), (3, 32, 1), (2, 16, 3), (2, 16, 4),
+                                      (1, 64, 4)])
 @pytest.mark.parametrize("y_dtype", [torch.float32, torch.bfloat16])
 def test_apply_multi_equals_single_calls(k, r, path, y_dtype):
     """Several projections sharing one routing in one call (the skinny path fuses the phases
@@ -359,9 +360,19 @@ def test_apply_multi_equals_single_calls(k, r, path, y_dtype):
     order = [2, 0, 3, 1]  # targets in any order
     ys = m.molora_apply_multi(hs, [xs[i] for i in order], [y0s[i] for i in order], offsets, perm, perm_w, inv, k=k,
                               targets=order, y_dtype=y_dtype, path=path)
+    # the documented AUTO rule: tile-local for K <= 16, r <= 32, N*k >= 192, except blocks for
+    # several targets with k > 1; else grouped, or skinny for r > 32 below 1024 pairs
+    single_path = path
+    if path == 0:
+        if K <= 16 and r <= 32 and N * k >= 192:
+            single_path = 4 if k > 1 else 3
+        elif r <= 32 or N * k >= 1024:
+            single_path = 1
+        else:
+            single_path = 2
     for j, i in enumerate(order):
         single = m.molora_apply(hs, xs[i], y0s[i], offsets, perm, perm_w, inv, k=k, target=i, y_dtype=y_dtype,
-                                path=path)
+                                path=single_path)
         np.testing.assert_array_equal(host(ys[j]), host(single))
     t = tgs[3]
     ref = oracle_from_gpu_routing(t, 2.0, idx, w, K, k)
