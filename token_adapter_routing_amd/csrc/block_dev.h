@@ -93,6 +93,26 @@ __device__ __forceinline__ void lds_copy_1k(void* dst, const void* src, int byte
                                      reinterpret_cast<char*>(dst) + off, 16, 0, 0);
 }
 
+// Copy `bytes` (a multiple of 1 KB, at most 2 RB KB per wave) from global src to LDS dst through
+// registers: wave w's 1 KB pieces w, w + 8, ..; the loads are unconditional (clamped), the
+// stores only for pieces inside `bytes`.
+template <int RB>
+__device__ __forceinline__ void lds_stage_regs(void* dst, const void* src, int bytes) {
+  constexpr int C = (kBSlice * RB * 16 * 2) / (kBWaves * 1024);
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  u32x4_t v[C];
+#pragma unroll
+  for (int c = 0; c < C; ++c) {
+    const int off = min((wave + kBWaves * c) * 1024, bytes - 1024);
+    v[c] = ld16(reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(src) + off) + 8 * lane);
+  }
+#pragma unroll
+  for (int c = 0; c < C; ++c) {
+    const int off = (wave + kBWaves * c) * 1024;
+    if (off < bytes) *reinterpret_cast<u32x4_t*>(reinterpret_cast<char*>(dst) + off + 16 * lane) = v[c];
+  }
+}
+
 // ------------------------------------------------------------------------------------------
 // shrink workgroup: block tb, reduction slice sl.  Wave w: row block rb = w % 4 (16 tokens),
 // reduction half kh = w / 4 (two steps of 128).
@@ -195,8 +215,6 @@ __device__ void block_expand(const BlockArgs& a, BlockLds<RB>& L, const Route& r
     yrows[i] = reinterpret_cast<char*>(a.y) + (size_t)t * d_out * yb;
   }
   RowChunk<Y0F32> yc0, yc1;
-  load_row_chunk<Y0F32>(yc0, y0rows, c0 + b0 * kColBlock, n);
-  load_row_chunk<Y0F32>(yc1, y0rows, c0 + b1 * kColBlock, n);
   // routing: used adapters and the (slot, token) weights; token thread t sums its pairs in order
   const uint32_t used = block_used(rt, t0, a.N, a.k, a.K);
   const int nU = __popc(used);
@@ -209,35 +227,17 @@ __device__ void block_expand(const BlockArgs& a, BlockLds<RB>& L, const Route& r
       if (e >= 0) L.wt[slot_of(used, e)][threadIdx.x] += w;
     }
   }
-  // first group's B^T rows of the slice, straight into LDS
-  {
-    uint32_t r2 = used;
-    for (int g = 0; g < min(block_group<RB>(), nU); ++g) {
-      lds_copy_1k(L.ab[g], adapter_B<INDIRECT>(a.tgt, __builtin_ctz(r2)) + (size_t)c0 * r_pad,
-                  (c1 - c0) * r_pad * 2);
+  constexpr int BG = block_group<RB>();
+  const int bbytes = (c1 - c0) * r_pad * 2;  // B^T rows of the slice, one adapter
+  // a group's B^T rows into LDS through registers (the waits then name exactly these loads)
+  auto stage_b = [&](uint32_t r2, int ng) {
+    for (int g = 0; g < ng; ++g) {
+      lds_stage_regs<RB>(L.ab[g], adapter_B<INDIRECT>(a.tgt, __builtin_ctz(r2)) + (size_t)c0 * r_pad, bbytes);
       r2 &= r2 - 1;
     }
-  }
-  hook();
-  __syncthreads();  // the weight table is complete
-  f32x4_t o0[8], o1[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    o0[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    o1[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  }
-  uint32_t rem = used;
-  for (int base = 0; base < nU; base += block_group<RB>()) {
-    const int ng = min(block_group<RB>(), nU - base);
-    if (base > 0) {
-      uint32_t r2 = rem;
-      for (int g = 0; g < ng; ++g) {
-        lds_copy_1k(L.ab[g], adapter_B<INDIRECT>(a.tgt, __builtin_ctz(r2)) + (size_t)c0 * r_pad,
-                    (c1 - c0) * r_pad * 2);
-        r2 &= r2 - 1;
-      }
-    }
-    // h of the group's slots: sum the slices in order, weight, split into hi / lo
+  };
+  // h of a group's slots: sum the slices in order, weight, split into hi / lo
+  auto group_h = [&](int base, int ng) {
     for (int v = threadIdx.x; v < ng * kBTok * RB * 16; v += kBThreads) {
       const int g = v / (kBTok * RB * 16), vi = v % (kBTok * RB * 16);
       const int tok = vi / (RB * 16), rk = vi % (RB * 16);
@@ -250,8 +250,14 @@ __device__ void block_expand(const BlockArgs& a, BlockLds<RB>& L, const Route& r
       L.hb[g][0][tok][rk] = __builtin_bit_cast(uint16_t, hi);
       L.hb[g][1][tok][rk] = __builtin_bit_cast(uint16_t, lo);
     }
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+  };
+  f32x4_t o0[8], o1[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    o0[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    o1[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+  auto group_mfma = [&](int ng) {
     for (int g = 0; g < ng; ++g) {
       // A operand: row n of the row block; groups 0, 1 carry hi of ranks 16u + 8(G & 1) ..,
       // groups 2, 3 lo of the same ranks
@@ -273,8 +279,28 @@ __device__ void block_expand(const BlockArgs& a, BlockLds<RB>& L, const Route& r
           o1[j] = mfma16x16x32(hb[u], as_bf16x8(v1), o1[j]);
         }
     }
-    for (int g = 0; g < ng; ++g) rem &= rem - 1;
+  };
+  // first group: B rows and h before the y0 rows are requested, so that waiting for them does
+  // not wait for HBM; the y0 rows are needed only by the epilogue
+  const int ng0 = min(BG, nU);
+  stage_b(used, ng0);
+  hook();
+  __syncthreads();  // the weight table is complete
+  group_h(0, ng0);
+  load_row_chunk<Y0F32>(yc0, y0rows, c0 + b0 * kColBlock, n);
+  load_row_chunk<Y0F32>(yc1, y0rows, c0 + b1 * kColBlock, n);
+  __syncthreads();  // B rows and h of the group are in LDS
+  group_mfma(ng0);
+  uint32_t rem = used;
+  for (int g = 0; g < ng0; ++g) rem &= rem - 1;
+  for (int base = BG; base < nU; base += BG) {
+    const int ng = min(BG, nU - base);
     __syncthreads();  // LDS pieces free for the next group
+    stage_b(rem, ng);
+    group_h(base, ng);
+    __syncthreads();
+    group_mfma(ng);
+    for (int g = 0; g < ng; ++g) rem &= rem - 1;
   }
   if (has0) epilogue_store<Y0F32, YF32>(o0, yc0, yrows, c0 + b0 * kColBlock, n, 0xFu);
   if (has1) epilogue_store<Y0F32, YF32>(o1, yc1, yrows, c0 + b1 * kColBlock, n, 0xFu);
