@@ -19,6 +19,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import os
 import statistics
@@ -39,7 +40,12 @@ COUNTER_SUMMARY = "step_vocab_modality4.md"
 
 
 def kernel_source_hash() -> str:
+    """Hash of the kernel sources' code (comments and whitespace removed, so that editing a
+    comment does not mark the recorded counters stale)."""
     src = "".join(open(os.path.join(ROOT, f)).read() for f in KERNEL_SOURCES)
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", " ", src)
+    src = " ".join(src.split())
     return hashlib.sha256(src.encode()).hexdigest()[:16]
 
 

@@ -6,21 +6,31 @@
 // Figure 4 / Table 2 (hot-set adapters at fixed addresses, direct or indirect layout),
 // Figure 5 / Figure 9 (a matrix-core kernel for large batches, a skinny kernel for small ones).
 //
-// Kernels:
-//   apply_tile         token-major tiles with grouping inside the tile (any k, K <= 16): a
-//                      workgroup owns 16 consecutive tokens and a slice of output columns;
-//                      its x / y0 / y rows depend only on the token index, so those streams
-//                      start as soon as the (small) routing loads are done; for every adapter
-//                      used in the tile (ascending) one MFMA shrink over the 16 rows and one
-//                      masked MFMA expand, summed in registers; y is written once.
-//   apply_fused_k1     globally grouped tiles, one adapter per token: a workgroup owns 16
-//                      grouped rows of one adapter (gathered through perm) and a slice of the
-//                      output columns; shrink and expand fused; each token written once.
-//   shrink_grouped     the grouped shrink into an fp32 workspace (weighted by gate and
-//                      alpha/r), optionally split over d_in (the skinny path), for
-//   expand_grouped_k1  (one adapter per token) and
-//   expand_tokens      (k > 1: token-major, every adapter of the tile, fixed order).
-//   copy_unrouted      y = y0 for tokens that no adapter was applied to (out-of-place calls).
+// Kernels (paths of molora_apply in brackets):
+//   step_vocab         the whole vocabulary-routed step in one launch (k = 1): every workgroup
+//                      routes its 8 tokens, applies them as apply_t8 does and writes its share
+//                      of the dispatch outputs, counting all ids itself (no grid barrier).
+//   apply_t8           [TILE] 8 consecutive tokens per workgroup (tile8_dev.h), every adapter
+//                      the tile uses applied in turn; x / y0 / y rows depend only on the token
+//                      index, so those streams start before the routing is known.
+//   shrink_block, expand_block
+//                      [BLOCK] 64-token blocks in two launches (block_dev.h): partial shrinks
+//                      per 512-wide d_in slice into the workspace, then expands per 512-wide
+//                      column slice; step_shrink_block / step_expand_block route from the ids.
+//   apply_gm           [GROUPED, rank > 32 or k > 1] equal row ranges of the grouped order in
+//                      64-row sub-tiles (gm_dev.h); k > 1: slot_sort (or slot_hist +
+//                      slot_scatter) orders the pairs by (rank among the token's pairs,
+//                      adapter), one pass per rank carries the sum in fp32, finish_tokens
+//                      writes the tokens the last pass does not reach.
+//   apply_fused_k1     [GROUPED, k = 1, rank <= 32] 16 grouped rows of one adapter (gathered
+//                      through perm) and a slice of output columns; shrink and expand fused.
+//   shrink_grouped     [SKINNY, GROUPED k > 1 with k*K > 64] the grouped shrink into an fp32
+//                      workspace (weighted by gate and alpha/r), split over d_in, then
+//   expand_grouped_k1  one adapter per token, or one pass per rank (k*K <= 64), or
+//   expand_tokens      token-major over every adapter of a 16-token tile (k*K > 64).
+//   *_multi            the same phases for several targets sharing one routing, one launch
+//                      per phase (molora_apply_multi).
+//   relayout_A / _B, seqpass_meta: hot-set layout and the per-sequence comparator's metadata.
 //
 // The shrink result h stays fp32 and enters the expand MFMA as a bf16 hi/lo pair
 // (h = hi + lo to about 2^-17 relative).  Workgroups that share x rows are numbered so that
