@@ -33,7 +33,18 @@ def cases():
     odd.ids = odd.ids.copy()
     odd.ids[::37] = -5        # unrouted
     odd.ids[5::41] = 10 ** 6  # unrouted
-    return [("tiny", tiny), ("modality4", mod), ("ragged_unrouted", odd)]
+    # whole tiles of unrouted tokens (they apply no adapter and copy y0 to y), two 256-column
+    # units per wave, rank blocks 1 and 2, and tiles with up to four adapters
+    holes = []
+    for r in (16, 32):
+        h = synth.vocab_case(N=520, d=4096, K=4, r=r, case_id=12, runs=False)
+        h.ids = h.ids.copy()
+        h.ids[16:40] = -5
+        h.ids[500:] = 10 ** 6
+        holes.append((f"unrouted_tiles_r{r}", h))
+    dead = synth.vocab_case(N=100, d=4096, K=4, r=32, case_id=13, runs=False)
+    dead.ids = np.full_like(dead.ids, -1)
+    return [("tiny", tiny), ("modality4", mod), ("ragged_unrouted", odd), *holes, ("all_unrouted", dead)]
 
 
 @pytest.mark.parametrize("block", [False, True])

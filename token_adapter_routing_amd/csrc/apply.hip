@@ -336,85 +336,326 @@ __global__ __launch_bounds__(kBThreads, 2) void expand_block_multi(BlockMulti m)
   block_expand<RB, INDIRECT, Y0F32, YF32>(a.b, L, rt, blockIdx.x / a.b.cslices, blockIdx.x % a.b.cslices, [] {});
 }
 
-// The vocabulary-routed step on 64-token blocks (k = 1), as two launches: the shrink routes
-// its block from the ids; the expand does too, and its workgroups of column slice 0 write their
-// block's share of the dispatch outputs (adapter counts over all N ids and over the ids before
-// the block give the offsets and each token's grouped position).
-struct VocabRoute {
-  const int32_t* ids;
-  StepBounds bd;
-  float scale;
-  __device__ __forceinline__ int operator()(int t, int s, float& w) const {
-    (void)s;
-    const int e = step_owner(ids[t], bd);
-    w = e >= 0 ? scale : 0.f;
-    return e;
-  }
+// The vocabulary-routed step split over the reduction and output dimensions, in two launches
+// (k = 1).  Every token's h is the sum of per-slice partials, so a workgroup reads only a
+// 512-wide slice of each adapter it uses (A: 16 KB, B: 16 KB per adapter at rank 16) instead of
+// the whole matrices: an 8-token tile reads 256 KB of adapter data per adapter for 192 KB of
+// its own rows, and a tile that spans a run boundary reads it twice.
+//   split_shrink  (64-token block, d_in slice of 512): routes the block's tokens from their
+//                 ids, stages the A slices of the adapters the block uses in LDS, and writes
+//                 the partial h of every token against its own adapter (rows of other adapters
+//                 are discarded, so the partial workspace does not grow with the adapters in a
+//                 block).  Workgroups of slice 0 also write the block's share of the dispatch
+//                 outputs (they count the adapters of all ids and of the ids before the block).
+//   split_expand  (64-token block, d_out slice of 512): sums the partials in slice order,
+//                 scales, stages the B slices in LDS and writes y = y0 + sum_e mask_e(h) B_e.
+// The launch boundary orders the partials' writes before their reads.  Workgroup b takes block
+// b / slices and slice b % slices: with 8 slices, slice s runs on XCD s (workgroups are dispatched
+// round robin over the 8 XCDs), so each XCD's L2 holds one slice of every adapter.
+constexpr int kSTok = 64;
+constexpr int kSSlice = 512;
+constexpr int kSWaves = 8;
+constexpr int kSThreads = kSWaves * kWave;
+// adapters whose slices are staged in LDS together (64 KB)
+template <int RB>
+constexpr int split_group() {
+  return RB == 1 ? 4 : (RB == 2 ? 2 : 1);
+}
+
+struct SplitGeom {
+  int nblocks, kslices, cslices;
+  float* part;  // [nblocks][kslices][64][r_pad] fp32: partial h of each token on its own adapter
 };
 
+__host__ __device__ inline size_t split_part_floats(int N, int d_in, int r_pad) {
+  return (size_t)((N + kSTok - 1) / kSTok) * ((d_in + kSSlice - 1) / kSSlice) * kSTok * r_pad;
+}
+
 template <int RB, bool INDIRECT>
-__global__ __launch_bounds__(kBThreads, 2) void step_shrink_block(StepArgs a, BlockArgs b) {
-  __shared__ BlockLds<RB> L;
-  const VocabRoute rt{a.ids, a.bounds, b.scale};
-  block_shrink<RB, INDIRECT>(b, L, rt, blockIdx.x / b.kslices, blockIdx.x % b.kslices);
+__global__ __launch_bounds__(kSThreads) void split_shrink(StepArgs a, SplitGeom g) {
+  constexpr int GA = split_group<RB>();
+  constexpr int piece = RB * 16 * kStepK;  // elements of one reduction step's A pieces
+  __shared__ alignas(16) uint16_t As[GA][4 * piece];
+  __shared__ float red[4][16][RB * 16 + 4];
+  __shared__ StepLds S;
+  const int tb = blockIdx.x / g.kslices, sl = blockIdx.x % g.kslices;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n = lane & 15, G = lane >> 4, rb = wave & 3, kh = wave >> 2;
+  const int N = a.t.N, K = a.t.K, d_in = a.t.tgt.d_in, r_pad = a.t.tgt.r_pad;
+  const int t0 = tb * kSTok;
+  const bool disp = sl == 0;  // this workgroup writes the block's dispatch outputs
+  if (disp && threadIdx.x < 64) {
+    S.gcnt[threadIdx.x] = 0;
+    S.pcnt[threadIdx.x] = 0;
+  }
+  // loads in use order: the block's ids (lane l: token t0 + l, clones of N - 1 past the end),
+  // this thread's share of the first 2048 ids (dispatch workgroups), then the x rows
+  const int myid = a.ids[min(t0 + lane, N - 1)];
+  int dv[kStepIdsPerThread];
+  if (disp) {
+#pragma unroll
+    for (int j = 0; j < kStepIdsPerThread; ++j) dv[j] = a.ids[min(j * kSThreads + (int)threadIdx.x, N - 1)];
+  }
+  const int S_all = d_in / kStepK;
+  const int s0 = sl * (kSSlice / kStepK), s1 = min(s0 + kSSlice / kStepK, S_all);
+  const int w0 = min(s0 + 2 * kh, s1), w1 = min(w0 + 2, s1);  // this wave's steps
+  const int row = min(t0 + 16 * rb + n, N - 1);
+  const uint16_t* xp = a.t.x + (size_t)row * d_in + 8 * G;
+  u32x4_t xv[2][4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int st = max(min(w0 + i, w1 - 1), s0);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) xv[i][c] = ld16_nt(xp + st * kStepK + 32 * c);
+  }
+  const int pe = step_owner(myid, a.bounds);
+  uint32_t used = 0;
+#pragma unroll
+  for (int e = 0; e < kT8MaxU; ++e)
+    if (e < K && __ballot(pe == e) != 0) used |= 1u << e;
+  const int nU = __popc(used);
+  // adapters of the lane's four MFMA rows (tokens 16 rb + 4G + i)
+  int erow[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) erow[i] = __shfl(pe, 16 * rb + 4 * G + i, kWave);
+  int nbits = 0;
+  while ((1 << nbits) < K) ++nbits;
+
+  f32x4_t hs[RB];
+#pragma unroll
+  for (int u = 0; u < RB; ++u) hs[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const int ns = s1 - s0;
+  uint32_t rem = used;
+  for (int base = 0; base < max(nU, 1); base += GA) {
+    const int ng = min(GA, nU - base);
+    if (base > 0) __syncthreads();  // the previous group's slices are consumed
+    uint32_t r2 = rem;
+    for (int gi = 0; gi < ng; ++gi) {
+      lds_copy_1k(As[gi], adapter_A<INDIRECT>(a.t.tgt, __builtin_ctz(r2)) + (size_t)s0 * piece, ns * piece * 2);
+      r2 &= r2 - 1;
+    }
+    if (base == 0 && disp) {
+      // dispatch counts while the x rows and A slices are in flight
+      __syncthreads();  // counters cleared
+      step_count(S, a.bounds, dv, 0, N, nbits, t0);
+      for (int c0 = kStepIdsPerThread * kSThreads; c0 < N; c0 += kStepIdsPerThread * kSThreads) {
+#pragma unroll
+        for (int j = 0; j < kStepIdsPerThread; ++j) dv[j] = a.ids[min(c0 + j * kSThreads + (int)threadIdx.x, N - 1)];
+        step_count(S, a.bounds, dv, c0, N, nbits, t0);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    for (int gi = 0; gi < ng; ++gi) {
+      const int e = __builtin_ctz(rem);
+      rem &= rem - 1;
+      f32x4_t acc[RB];
+#pragma unroll
+      for (int u = 0; u < RB; ++u) acc[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        if (w0 + i < w1) {
+          const uint16_t* ap = As[gi] + (size_t)(w0 + i - s0) * piece;
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+#pragma unroll
+            for (int u = 0; u < RB; ++u) {
+              // lane (n, G) takes its 16 bytes at position 4n + G of the 1 KB piece (slab swizzle)
+              const u32x4_t av = *reinterpret_cast<const u32x4_t*>(ap + ((c * RB + u) * 64 + 4 * n + G) * 8);
+              acc[u] = mfma16x16x32(as_bf16x8(xv[i][c]), as_bf16x8(av), acc[u]);
+            }
+        }
+      }
+      // keep the rows whose token uses this adapter (adding to zero: exact)
+#pragma unroll
+      for (int u = 0; u < RB; ++u)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) hs[u][i] += (erow[i] == e) ? acc[u][i] : 0.f;
+    }
+  }
+  // the two reduction halves of a row block meet in LDS; the first half stores the sums
+  if (kh == 1) {
+#pragma unroll
+    for (int u = 0; u < RB; ++u)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) red[rb][4 * G + i][u * 16 + n] = hs[u][i];
+  }
+  __syncthreads();
+  if (kh == 0) {
+    float* dst = g.part + (((size_t)tb * g.kslices + sl) * kSTok + 16 * rb) * r_pad;
+#pragma unroll
+    for (int u = 0; u < RB; ++u)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dst[(size_t)(4 * G + i) * r_pad + u * 16 + n] = hs[u][i] + red[rb][4 * G + i][u * 16 + n];
+  }
+  if (!disp) return;
+  // dispatch share of the block: offsets, then the block's tokens' grouped positions
+  if (wave == 0) {
+    const int c = lane < K ? S.gcnt[lane] : 0;
+    const int incl = wave_incl_scan(c, lane);
+    if (lane < K) S.offs[lane] = incl - c;
+    if (tb == 0) {
+      if (lane < K) {
+        a.counts[lane] = c;
+        a.offsets[lane + 1] = incl;
+      }
+      if (lane == 0) a.offsets[0] = 0;
+    }
+  }
+  __syncthreads();
+  if (wave == 0) {
+    // one token per lane: rank among the block's earlier tokens of the same adapter
+    const int tok = t0 + lane;
+    const bool real = tok < N;
+    const bool valid = real && pe >= 0;
+    const uint64_t m = match_mask(pe, valid, nbits);
+    if (real) {
+      a.idx[tok] = pe;
+      a.w[tok] = valid ? 1.0f : 0.0f;
+      if (valid) {
+        const int pos = S.offs[pe] + S.pcnt[pe] + __popcll(m & lanemask_lt(lane));
+        a.inv[tok] = pos;
+        a.perm[pos] = tok;
+        a.perm_w[pos] = 1.0f;
+      } else {
+        a.inv[tok] = -1;
+      }
+    }
+  }
 }
 
 template <int RB, bool INDIRECT, bool Y0F32, bool YF32>
-__global__ __launch_bounds__(kBThreads, 2) void step_expand_block(StepArgs a, BlockArgs b) {
-  __shared__ BlockLds<RB> L;
-  __shared__ StepLds S;
-  const VocabRoute rt{a.ids, a.bounds, b.scale};
-  const int tb = blockIdx.x / b.cslices, cs = blockIdx.x % b.cslices;
+__global__ __launch_bounds__(kSThreads) void split_expand(StepArgs a, SplitGeom g) {
+  constexpr int GB = split_group<RB>();
+  constexpr int RP = RB * 16;
+  constexpr size_t y0b = Y0F32 ? 4 : 2, yb = YF32 ? 4 : 2;
+  __shared__ alignas(16) uint16_t Bs[GB][kSSlice * RP];  // B^T rows of the slice [512][r_pad]
+  __shared__ alignas(16) uint16_t hb[2][kSTok][RP];      // h hi / lo [part][token][rank]
+  const int tb = blockIdx.x / g.cslices, cs = blockIdx.x % g.cslices;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int N = b.N, K = b.K, t0 = tb * kBTok;
-  block_expand<RB, INDIRECT, Y0F32, YF32>(b, L, rt, tb, cs, [&] {
-    if (cs != 0) return;
-    if (threadIdx.x < 64) {
-      S.gcnt[threadIdx.x] = 0;
-      S.pcnt[threadIdx.x] = 0;
-    }
-    __syncthreads();
-    int nbits = 0;
-    while ((1 << nbits) < K) ++nbits;
-    int dv[kStepIdsPerThread];
-    for (int c0 = 0; c0 < N; c0 += kStepIdsPerThread * kT8Threads) {
+  const int n = lane & 15, G = lane >> 4, rb = wave & 3, ch = wave >> 2;
+  const int N = a.t.N, K = a.t.K, d_out = a.t.tgt.d_out;
+  const int t0 = tb * kSTok;
+  const int c0 = cs * kSSlice, c1 = min(c0 + kSSlice, d_out);
+  const int nb = (c1 - c0) / kColBlock;  // 128-column blocks in the slice
+  const int b0 = min(2 * ch, nb - 1), b1 = min(2 * ch + 1, nb - 1);
+  const bool has0 = 2 * ch < nb, has1 = 2 * ch + 1 < nb;
+  // loads: the ids, the y0 rows of the first column block, the partials (every thread 16 bytes
+  // of each slice), the first group's B slices (straight into LDS, once the routing is known),
+  // then the y0 rows of the second column block.  Loads return in issue order: the first
+  // block's output is stored while the second block's y0 rows are still arriving.
+  const int myid = a.ids[min(t0 + lane, N - 1)];
+  const char* y0rows[4];
+  char* yrows[4];
 #pragma unroll
-      for (int j = 0; j < kStepIdsPerThread; ++j) dv[j] = a.ids[min(c0 + j * kT8Threads + (int)threadIdx.x, N - 1)];
-      step_count(S, a.bounds, dv, c0, N, nbits, t0);
-    }
-    __syncthreads();
-    if (wave == 0) {
-      const int c = lane < K ? S.gcnt[lane] : 0;
-      const int incl = wave_incl_scan(c, lane);
-      if (lane < K) S.offs[lane] = incl - c;
-      if (tb == 0) {
-        if (lane < K) {
-          a.counts[lane] = c;
-          a.offsets[lane + 1] = incl;
-        }
-        if (lane == 0) a.offsets[0] = 0;
+  for (int i = 0; i < 4; ++i) {
+    const int t = min(t0 + 16 * rb + 4 * G + i, N - 1);
+    y0rows[i] = reinterpret_cast<const char*>(a.t.y0) + (size_t)t * d_out * y0b;
+    yrows[i] = reinterpret_cast<char*>(a.t.y) + (size_t)t * d_out * yb;
+  }
+  RowChunk<Y0F32> yc0, yc1;
+  load_row_chunk<Y0F32>(yc0, y0rows, c0 + b0 * kColBlock, n);
+  constexpr int QPT = (kSTok * RP / 4 + kSThreads - 1) / kSThreads;  // 16-byte quads per thread
+  constexpr int KSMAX = 8;  // slices loaded up front (the rest, d_in > 4096, at the sum)
+  u32x4_t pv[QPT][KSMAX];
+  const float* pbase = g.part + (size_t)tb * g.kslices * kSTok * RP;
+#pragma unroll
+  for (int q = 0; q < QPT; ++q) {
+    const int qi = min(q * kSThreads + (int)threadIdx.x, kSTok * RP / 4 - 1);
+#pragma unroll
+    for (int s = 0; s < KSMAX; ++s)
+      if (s < g.kslices) pv[q][s] = ld16(pbase + (size_t)s * kSTok * RP + 4 * qi);
+  }
+  const int pe = step_owner(myid, a.bounds);
+  uint32_t used = 0;
+#pragma unroll
+  for (int e = 0; e < kT8MaxU; ++e)
+    if (e < K && __ballot(pe == e) != 0) used |= 1u << e;
+  const int nU = __popc(used);
+  const int bbytes = (c1 - c0) * RP * 2;
+  uint32_t r2 = used;
+  for (int gi = 0; gi < min(GB, nU); ++gi) {
+    lds_copy_1k(Bs[gi], adapter_B<INDIRECT>(a.t.tgt, __builtin_ctz(r2)) + (size_t)c0 * RP, bbytes);
+    r2 &= r2 - 1;
+  }
+  load_row_chunk<Y0F32>(yc1, y0rows, c0 + b1 * kColBlock, n);
+  // everything but the second block's y0 rows has arrived (vmcnt = that block's loads)
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (Y0F32 ? 8 : 4));
+  // h = scale x (sum of the slices in order), split into bf16 hi / lo; unrouted tokens get 0
+#pragma unroll
+  for (int q = 0; q < QPT; ++q) {
+    const int qi = q * kSThreads + (int)threadIdx.x;
+    const int tok = min(qi, kSTok * RP / 4 - 1) / (RP / 4), rk = 4 * (qi % (RP / 4));
+    const float wt = __shfl(pe, tok, kWave) >= 0 ? a.t.scale : 0.f;
+    if (qi < kSTok * RP / 4) {
+      float sum[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < KSMAX; ++s)
+        if (s < g.kslices)
+#pragma unroll
+          for (int c = 0; c < 4; ++c) sum[c] += __uint_as_float(pv[q][s][c]);
+      for (int s = KSMAX; s < g.kslices; ++s) {
+        const u32x4_t v = ld16(pbase + (size_t)s * kSTok * RP + 4 * qi);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) sum[c] += __uint_as_float(v[c]);
       }
-      // the block's tokens, one per lane: rank among the block's earlier tokens of the adapter
-      const int tok = t0 + lane;
-      const bool real = tok < N;
-      float w;
-      const int pe = rt(min(tok, N - 1), 0, w);
-      const bool valid = real && pe >= 0;
-      const uint64_t m = match_mask(pe, valid, nbits);
-      if (real) {
-        a.idx[tok] = pe;
-        a.w[tok] = valid ? 1.0f : 0.0f;
-        if (valid) {
-          const int pos = S.offs[pe] + S.pcnt[pe] + __popcll(m & lanemask_lt(lane));
-          a.inv[tok] = pos;
-          a.perm[pos] = tok;
-          a.perm_w[pos] = 1.0f;
-        } else {
-          a.inv[tok] = -1;
-        }
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const float h = sum[c] * wt;
+        const __bf16 hi = (__bf16)h;
+        const __bf16 lo = (__bf16)(h - (float)hi);
+        hb[0][tok][rk + c] = __builtin_bit_cast(uint16_t, hi);
+        hb[1][tok][rk + c] = __builtin_bit_cast(uint16_t, lo);
       }
     }
-  });
+  }
+  f32x4_t o0[8], o1[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    o0[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    o1[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+  const int erow = __shfl(pe, 16 * rb + n, kWave);  // adapter of the lane's A-operand row
+  uint32_t rem = used;
+  for (int base = 0; base < nU; base += GB) {
+    const int ng = min(GB, nU - base);
+    if (base > 0) {
+      __syncthreads();  // the previous group's slices are consumed
+      uint32_t r3 = rem;
+      for (int gi = 0; gi < ng; ++gi) {
+        lds_copy_1k(Bs[gi], adapter_B<INDIRECT>(a.t.tgt, __builtin_ctz(r3)) + (size_t)c0 * RP, bbytes);
+        r3 &= r3 - 1;
+      }
+    }
+    if (base > 0) __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();  // the group's B slices and h are in LDS
+    for (int gi = 0; gi < ng; ++gi) {
+      const int e = __builtin_ctz(rem);
+      rem &= rem - 1;
+      // A operand: row n of the row block, kept only if that token uses adapter e; k-slot
+      // groups 0, 1 carry hi of ranks 16u + 8(G & 1) .., groups 2, 3 lo of the same ranks
+      bf16x8_t hv[RB];
+#pragma unroll
+      for (int u = 0; u < RB; ++u) {
+        u32x4_t v = *reinterpret_cast<const u32x4_t*>(&hb[G >> 1][16 * rb + n][u * 16 + 8 * (G & 1)]);
+        if (erow != e) v = u32x4_t{0u, 0u, 0u, 0u};
+        hv[u] = as_bf16x8(v);
+      }
+      const uint16_t* bp0 = Bs[gi] + (size_t)(b0 * kColBlock + n) * RP + 8 * (G & 1);
+      const uint16_t* bp1 = Bs[gi] + (size_t)(b1 * kColBlock + n) * RP + 8 * (G & 1);
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+#pragma unroll
+        for (int u = 0; u < RB; ++u) {
+          const u32x4_t v0 = *reinterpret_cast<const u32x4_t*>(bp0 + (size_t)16 * j * RP + 16 * u);
+          const u32x4_t v1 = *reinterpret_cast<const u32x4_t*>(bp1 + (size_t)16 * j * RP + 16 * u);
+          o0[j] = mfma16x16x32(hv[u], as_bf16x8(v0), o0[j]);
+          o1[j] = mfma16x16x32(hv[u], as_bf16x8(v1), o1[j]);
+        }
+    }
+  }
+  if (has0) epilogue_store<Y0F32, YF32>(o0, yc0, yrows, c0 + b0 * kColBlock, n, 0xFu);
+  if (has1) epilogue_store<Y0F32, YF32>(o1, yc1, yrows, c0 + b1 * kColBlock, n, 0xFu);
 }
 
 // --------------------------------------------------------------------------------------
@@ -936,7 +1177,10 @@ static size_t block_ws(int N, int k, int K, int r_pad, int d_in) {
   return block_part_floats(nblocks, slotmax, kslices, r_pad) * sizeof(float);
 }
 
-size_t step_ws_bytes(int N, int K, int r_pad, int d_in) { return block_ws(N, 1, K, r_pad, d_in); }
+size_t step_ws_bytes(int N, int K, int r_pad, int d_in) {
+  (void)K;
+  return split_part_floats(N, d_in, r_pad) * sizeof(float);
+}
 
 // Grouped path on 64-row tiles: used for k > 1 (passes over ranked slots) or ranks above 32.
 // k > 1 workspace: the slot sort (counts and offsets in a 256-byte block, then the order and
@@ -1057,11 +1301,11 @@ static hipError_t launch_block_t(const BlockApplyArgs& ba, hipStream_t s) {
   return hipGetLastError();
 }
 template <int RB, bool IND, bool Y0F, bool YF>
-static hipError_t launch_step_block_t(const StepArgs& sa, const BlockArgs& b, hipStream_t s) {
-  hipLaunchKernelGGL((step_shrink_block<RB, IND>), dim3(b.nblocks * b.kslices), dim3(kBThreads), 0, s, sa, b);
+static hipError_t launch_split_t(const StepArgs& sa, const SplitGeom& g, hipStream_t s) {
+  hipLaunchKernelGGL((split_shrink<RB, IND>), dim3(g.nblocks * g.kslices), dim3(kSThreads), 0, s, sa, g);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((step_expand_block<RB, IND, Y0F, YF>), dim3(b.nblocks * b.cslices), dim3(kBThreads), 0, s, sa, b);
+  hipLaunchKernelGGL((split_expand<RB, IND, Y0F, YF>), dim3(g.nblocks * g.cslices), dim3(kSThreads), 0, s, sa, g);
   return hipGetLastError();
 }
 template <int RB, bool IND, bool Y0F, bool YF>
@@ -1467,9 +1711,13 @@ hipError_t launch_step_vocab(const StepVocabLaunch& a, hipStream_t s) {
   const int RBv = a.apply.tgt.r_pad / 16;
   hipError_t err = hipSuccess;
   if (a.ws != nullptr) {
-    const BlockArgs b = block_args(a.apply, a.ws);
+    SplitGeom g;
+    g.nblocks = (a.apply.N + kSTok - 1) / kSTok;
+    g.kslices = (a.apply.tgt.d_in + kSSlice - 1) / kSSlice;
+    g.cslices = (a.apply.tgt.d_out + kSSlice - 1) / kSSlice;
+    g.part = reinterpret_cast<float*>(a.ws);
     MOLORA_DISPATCH_RB(RBv, MOLORA_DISPATCH_BOOL(a.apply.indirect, IND, MOLORA_DISPATCH_BOOL(a.apply.y0_f32, Y0F,
-        MOLORA_DISPATCH_BOOL(a.apply.y_f32, YF, err = (launch_step_block_t<RB, IND, Y0F, YF>(sa, b, s))))));
+        MOLORA_DISPATCH_BOOL(a.apply.y_f32, YF, err = (launch_split_t<RB, IND, Y0F, YF>(sa, g, s))))));
     return err;
   }
   const int grid = 8 * sa.t.tiles_per_xcd * sa.t.col_groups;

@@ -292,10 +292,18 @@ __device__ __forceinline__ void t8_main(const T8Args& a, T8Lds<RB>& L, T8Stream<
     }
     // the next adapter's first A pieces stream during this adapter's reduction
     if (base + 1 < nU) load_a(adapter_A<INDIRECT>(a.tgt, __builtin_ctz(rem)), st.s0);
-    if (base == 0) {
-      // the second unit's pieces and y0 rows stream during the reductions
-      if (nU == 1) t8_load_b<RB, JB>(b1, adapter_B<INDIRECT>(a.tgt, e0), r_pad, cb1, st.cend, lane, 0);
+    if (base == nU - 1) {
+      // the expand's second batch of B pieces, then the second unit's y0 rows, stream during
+      // the last reduction.  Loads return in issue order, so every piece that the expand needs
+      // before the second unit's store must be requested ahead of those rows: with one adapter
+      // that is the second unit's pieces, with several (rank block 1) the first unit's pieces
+      // of the second adapter.
+      if (nU == 1 || JB == 8)
+        t8_load_b<RB, JB>(b1, adapter_B<INDIRECT>(a.tgt, nU == 1 ? e0 : __builtin_ctz(used & (used - 1))), r_pad,
+                          nU == 1 ? cb1 : cb0, st.cend, lane, 0);
       t8_load_y0<Y0F32>(y0c1, a, st.trow, t8_block_col(cb1, st.cend, G), n);
+    }
+    if (base == 0) {
       // weight table (slot, token): the sum of the token's gate weights on the slot's adapter;
       // the shuffles run with every lane of wave 0 active
       if (wave == 0) {
@@ -341,6 +349,9 @@ __device__ __forceinline__ void t8_main(const T8Args& a, T8Lds<RB>& L, T8Stream<
     __syncthreads();
   }
 
+  // a tile of unrouted tokens skipped the shrink, where the second unit's y0 rows are requested
+  if (nU == 0) t8_load_y0<Y0F32>(y0c1, a, st.trow, t8_block_col(cb1, st.cend, G), n);
+
   // expand, y = y0 + sum over the used adapters (ascending) of h_e B_e
   if (myunits == 0) return;
   if (nU <= 1 && JB == 8) {
@@ -379,64 +390,68 @@ __device__ __forceinline__ void t8_main(const T8Args& a, T8Lds<RB>& L, T8Stream<
     }
     return;
   }
-  if (JB == 8 && nU == 2 && myunits <= 2) {
-    // two adapters (a tile across a run boundary), at most two units: b0 already holds the
-    // first unit's pieces of the first adapter; each next batch is requested before the
-    // current batch's MFMAs
-    const uint16_t* Bf = adapter_B<INDIRECT>(a.tgt, e0);
-    const uint16_t* Bs = adapter_B<INDIRECT>(a.tgt, __builtin_ctz(used & (used - 1)));
-    const int cba = st.c0 + wave * kT8Unit, cbb = cba + NW * kT8Unit;
-    const bool two = myunits > 1;
-    bf16x8_t hh[RB], hl[RB];
-    f32x4_t o[8];
-    t8_load_b<RB, JB>(b1, Bs, r_pad, cba, st.cend, lane, 0);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) o[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    t8_h_operands<RB>(L, 0, cba + kT8Unit > st.cend, lane, hh, hl);
-    t8_expand_mfma<RB, JB>(o, hh, hl, b0, 0);
-    t8_load_b<RB, JB>(b0, Bf, r_pad, two ? cbb : cba, st.cend, lane, 0);
-    t8_h_operands<RB>(L, 1, cba + kT8Unit > st.cend, lane, hh, hl);
-    t8_expand_mfma<RB, JB>(o, hh, hl, b1, 0);
-    t8_store_y<Y0F32, YF32>(o, y0c0, a, st.trow, t8_block_col(cba, st.cend, G), n);
-    if (two) {
-      t8_load_b<RB, JB>(b1, Bs, r_pad, cbb, st.cend, lane, 0);
+  // several adapters (or large ranks): batch i = (unit, adapter slot, JB-column batch) in that
+  // order, two B buffers in ping-pong: batch i + 1 is requested before batch i's MFMAs, so every
+  // L2 round trip after the first overlaps the previous batch.  b0 holds batch 0 (requested
+  // before the shrink).  Requests past the last batch repeat it (their data is not used), so
+  // the number of loads in flight at every wait is the same on all paths.
+  if (nU == 0) {
+    // no routed token: y = y0
+    for (int ui = 0; ui < myunits; ++ui) {
+      const int cb = st.c0 + (wave + ui * NW) * kT8Unit;
+      RowChunk<Y0F32> yc;
+      if (ui == 0) yc = y0c0;
+      else if (ui == 1) yc = y0c1;
+      else t8_load_y0<Y0F32>(yc, a, st.trow, t8_block_col(cb, st.cend, G), n);
+      f32x4_t o[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) o[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      t8_h_operands<RB>(L, 0, cbb + kT8Unit > st.cend, lane, hh, hl);
-      t8_expand_mfma<RB, JB>(o, hh, hl, b0, 0);
-      t8_h_operands<RB>(L, 1, cbb + kT8Unit > st.cend, lane, hh, hl);
-      t8_expand_mfma<RB, JB>(o, hh, hl, b1, 0);
-      t8_store_y<Y0F32, YF32>(o, y0c1, a, st.trow, t8_block_col(cbb, st.cend, G), n);
+      t8_store_y<Y0F32, YF32>(o, yc, a, st.trow, t8_block_col(cb, st.cend, G), n);
     }
     return;
   }
-  // several adapters (or large ranks): per unit, every adapter's pieces in batches of JB MFMA
-  // columns
-  for (int ui = 0; ui < myunits; ++ui) {
+  constexpr int NBP = 8 / JB;  // batches per (unit, adapter)
+  const int per_unit = nU * NBP;
+  const int total = myunits * per_unit;
+  auto batch_load = [&](u32x4_t (&bv)[JB][RB], int i) {
+    i = min(i, total - 1);
+    const int ui = i / per_unit, rem = i - ui * per_unit, sl = rem / NBP, jb = rem - sl * NBP;
+    uint32_t m = used;
+    for (int q = 0; q < sl; ++q) m &= m - 1;
     const int cb = st.c0 + (wave + ui * NW) * kT8Unit;
-    const bool half = cb + kT8Unit > st.cend;
-    RowChunk<Y0F32> yc;
-    if (ui == 0) yc = y0c0;
-    else if (ui == 1) yc = y0c1;
-    else t8_load_y0<Y0F32>(yc, a, st.trow, t8_block_col(cb, st.cend, G), n);
-    f32x4_t o[8];
+    t8_load_b<RB, JB>(bv, adapter_B<INDIRECT>(a.tgt, __builtin_ctz(m)), r_pad, cb, st.cend, lane, jb * JB);
+  };
+  f32x4_t o[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) o[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    uint32_t r2 = used;
-    for (int sl = 0; sl < nU; ++sl) {
-      const uint16_t* Bt = adapter_B<INDIRECT>(a.tgt, __builtin_ctz(r2));
-      r2 &= r2 - 1;
-      bf16x8_t hh[RB], hl[RB];
-      t8_h_operands<RB>(L, sl, half, lane, hh, hl);
+  for (int j = 0; j < 8; ++j) o[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  RowChunk<Y0F32> yc = y0c0;
+  auto consume = [&](const u32x4_t (&bv)[JB][RB], int i) {
+    const int ui = i / per_unit, rem = i - ui * per_unit, sl = rem / NBP, jb = rem - sl * NBP;
+    const int cb = st.c0 + (wave + ui * NW) * kT8Unit;
+    bf16x8_t hh[RB], hl[RB];
+    t8_h_operands<RB>(L, sl, cb + kT8Unit > st.cend, lane, hh, hl);
+    __builtin_amdgcn_sched_barrier(0);
+    if (NBP == 1 || jb == 0) t8_expand_mfma<RB, JB>(o, hh, hl, bv, 0);
+    else t8_expand_mfma<RB, JB>(o, hh, hl, bv, JB);
+    __builtin_amdgcn_sched_barrier(0);
+    if (rem == per_unit - 1) {
+      t8_store_y<Y0F32, YF32>(o, yc, a, st.trow, t8_block_col(cb, st.cend, G), n);
 #pragma unroll
-      for (int j0 = 0; j0 < 8; j0 += JB) {
-        t8_load_b<RB, JB>(b1, Bt, r_pad, cb, st.cend, lane, j0);
-        __builtin_amdgcn_sched_barrier(0);
-        t8_expand_mfma<RB, JB>(o, hh, hl, b1, j0);
-        __builtin_amdgcn_sched_barrier(0);
-      }
+      for (int j = 0; j < 8; ++j) o[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      if (ui + 1 == 1) yc = y0c1;
+      else if (ui + 1 < myunits) t8_load_y0<Y0F32>(yc, a, st.trow, t8_block_col(cb + NW * kT8Unit, st.cend, G), n);
     }
-    t8_store_y<Y0F32, YF32>(o, yc, a, st.trow, t8_block_col(cb, st.cend, G), n);
+  };
+  // first pair of batches: with rank block 1, b1 already holds batch 1
+  if constexpr (JB != 8) batch_load(b1, 1);
+  consume(b0, 0);
+  batch_load(b0, 2);
+  if (1 < total) consume(b1, 1);
+  for (int i = 2; i < total; i += 2) {
+    batch_load(b1, i + 1);
+    consume(b0, i);
+    batch_load(b0, i + 2);
+    if (i + 1 < total) consume(b1, i + 1);
   }
 }
 
