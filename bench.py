@@ -6,9 +6,11 @@ accumulation; modality runs with geometric lengths (mean 64) and mix 0.4/0.3/0.1
 
 One step = one pass of the whole hot path over one batch: vocabulary routing, dispatch
 (histogram, offsets, stable permutation) and the LoRA apply (shrink, expand, gate-weighted
-alpha/r add into y) on adapters held in a hot-set slab.  The headline step is the one-launch
-form (`molora_step_vocab`); the three-launch form (route, dispatch, apply) and the
-per-sequence comparator (K masked dense passes) are timed beside it.  Inputs are resident in
+alpha/r add into y) on adapters held in a hot-set slab.  The headline step is
+`molora_step_vocab` with a workspace: two launches that split the reduction and the output
+columns into 512-wide slices (routing and the dispatch outputs happen inside them).  The
+one-launch tile form, the three-launch form (route, dispatch, apply) and the per-sequence
+comparator (K masked dense passes) are timed beside it.  Inputs are resident in
 HBM; S buffer sets (about 410 MB in all, above the 256 MB Infinity Cache) rotate so that
 every step streams x / y0 / y from HBM.  Timed steps are replayed from one HIP graph that
 holds one step per buffer set.
@@ -36,7 +38,7 @@ KERNEL_SOURCES = ("token_adapter_routing_amd/csrc/apply.hip", "token_adapter_rou
                   "token_adapter_routing_amd/csrc/molora_dev.h", "token_adapter_routing_amd/csrc/dispatch_dev.h",
                   "token_adapter_routing_amd/csrc/tile8_dev.h", "token_adapter_routing_amd/csrc/block_dev.h",
                   "token_adapter_routing_amd/csrc/gm_dev.h")
-COUNTER_SUMMARY = "step_vocab_modality4.md"
+COUNTER_SUMMARY = "step_split_modality4.md"
 
 
 def kernel_source_hash() -> str:
@@ -125,6 +127,8 @@ def main():
 
     hs = m.molora_hotset_init([(bf(t.A), bf(t.B))], case.scale)
     bounds = case.bounds.tolist()
+    # partial-sum workspace of the split step (written by its first launch, read by its second)
+    ws = torch.zeros(m.molora_step_workspace(hs, 0, N), dtype=torch.uint8, device=dev)
     S = args.sets
     sets = []
     ids_h = torch.from_numpy(case.ids)
@@ -140,7 +144,11 @@ def main():
                   torch.empty(N, dtype=torch.int32, device=dev))))
     del x_h, y0_h
 
-    def step(s):  # one launch: route + dispatch + apply
+    def step(s):  # two launches: route + shrink slices + dispatch, then expand slices
+        b = sets[s]
+        m.molora_step_vocab(hs, b["ids"], bounds, b["x"], b["y0"], y=b["y"], route=b["route"], meta=b["meta"], ws=ws)
+
+    def step1(s):  # one launch: route + dispatch + 8-token tile apply
         b = sets[s]
         m.molora_step_vocab(hs, b["ids"], bounds, b["x"], b["y0"], y=b["y"], route=b["route"], meta=b["meta"])
 
@@ -154,6 +162,7 @@ def main():
 
     for s in range(S):
         step(s)
+        step1(s)
         step3(s)
     torch.cuda.synchronize()
 
@@ -193,7 +202,7 @@ def main():
     ms_per_step, wall = time_graph(g_all)
     value = N / (ms_per_step * 1e-3)
 
-    # ---------------- dominant kernel: the one-launch step, back to back on `stream`
+    # ---------------- the step's kernels (split_shrink + split_expand), back to back on `stream`
     kreps = max(S, args.kernel_reps // S * S)
     ka = torch.cuda.Event(enable_timing=True)
     kb = torch.cuda.Event(enable_timing=True)
@@ -244,17 +253,20 @@ def main():
         "config": {"workload": "4-modality vocab routing N=2048 d=4096 K=4 r=16 k=1", "N": N, "d": d_in, "K": K,
                    "r": r, "k": k, "alpha_over_r": case.scale, "buffer_sets": S,
                    "launch": "hipGraph, one step per buffer set",
-                   "step": "molora_step_vocab (route + dispatch + tile-local apply in one launch)"},
+                   "step": "molora_step_vocab with a workspace (split_shrink: routing, 512-wide d_in slices, "
+                           "dispatch outputs; split_expand: 512-wide output slices)"},
         "step_roofline_frac": step_bytes / (ms_per_step * 1e-3) / (HBM_PEAK_GBS * 1e9),
         "step_latency_us": {"p50": p50, "p99": p99, "cv": cv, "replays": len(lat), "graph": "single step"},
         "wall_s_timed_region": wall,
         "roofline": {"bound": "hbm", "achieved": kernel_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": kernel_gbs / HBM_PEAK_GBS, "traffic": counter_traffic(COUNTER_SUMMARY),
-                     "kernel": "step_vocab", "kernel_us": kernel_us, "algorithmic_bytes": step_bytes},
+                     "kernel": "split_shrink + split_expand (the two launches of one step)",
+                     "kernel_us": kernel_us, "algorithmic_bytes": step_bytes},
     }
 
     if not args.no_extras:
-        # three launches per step (route_vocab, dispatch, apply)
+        # the one-launch step (tile apply) and three launches per step (route_vocab, dispatch, apply)
+        ms1, _ = time_graph(graph_of(step1, range(S)))
         ms3, _ = time_graph(graph_of(step3, range(S)))
         # per-sequence comparator: K masked dense passes over all N tokens (metadata from the routing)
         seq = []
@@ -272,6 +284,7 @@ def main():
                 m.molora_apply(hs, b["x"], b["y"], offs[e], perm, pw[e], perm, k=1, y=b["y"], path=m.PATH_GROUPED)
 
         seq_ms, _ = time_graph(graph_of(seq_step, range(S)))
+        out["one_launch_tile_step"] = {"ms_per_step": ms1, "routed_tokens_per_s": N / (ms1 * 1e-3)}
         out["three_launch_step"] = {"ms_per_step": ms3, "routed_tokens_per_s": N / (ms3 * 1e-3)}
         out["per_sequence_comparator"] = {"ms_per_step": seq_ms, "passes": K,
                                           "speedup_per_token": seq_ms / ms_per_step}

@@ -146,6 +146,7 @@ __global__ __launch_bounds__(kT8Threads) void apply_t8(T8ApplyArgs a) {
 // idx / w / inv / perm / perm_w; the first tile writes counts and offsets.
 constexpr int kStepIdsPerThread = 4;  // ids held from the start: N <= 512 * 4 in one pass
 constexpr int kStepMaxN = 4096;       // larger batches take the three-launch step
+constexpr int kSWavesMax = 8;         // waves of the workgroups that count ids
 
 // Vocabulary ranges as kernel arguments: [lo, hi) is routed; the owner of v is the number of
 // interior bounds b[1..K-1] at or below v (mid[i - 1] = b[i]; unused entries hold INT_MAX).
@@ -194,6 +195,38 @@ __device__ __forceinline__ void step_count(StepLds& S, const StepBounds& bd, con
     if (valid && (m & lt) == 0) atomicAdd(&S.gcnt[e], __popcll(m));
     const uint64_t mp = m & __ballot(t < t0);
     if (valid && t < t0 && (mp & lt) == 0) atomicAdd(&S.pcnt[e], __popcll(mp));
+  }
+}
+
+// The same counts as step_count, with per-wave ballots per adapter (no LDS atomics while the
+// ids are counted): wave w's counts of ids [c0 .. c0 + 512 * kStepIdsPerThread) land in
+// wg[w][e] / wp[w][e] (tokens below t0); the caller sums the waves in order.
+__device__ __forceinline__ void step_count_waves(int (&wg)[kSWavesMax][kT8MaxU], int (&wp)[kSWavesMax][kT8MaxU],
+                                                 const StepBounds& bd, const int (&v)[kStepIdsPerThread], int c0,
+                                                 int N, int K, int t0) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int e[kStepIdsPerThread];
+  uint64_t below[kStepIdsPerThread];
+#pragma unroll
+  for (int j = 0; j < kStepIdsPerThread; ++j) {
+    const int t = c0 + j * (int)blockDim.x + (int)threadIdx.x;
+    e[j] = t < N ? step_owner(v[j], bd) : -1;
+    below[j] = __ballot(t < t0);
+  }
+#pragma unroll
+  for (int ee = 0; ee < kT8MaxU; ++ee) {
+    if (ee >= K) break;
+    int cg = 0, cp = 0;
+#pragma unroll
+    for (int j = 0; j < kStepIdsPerThread; ++j) {
+      const uint64_t m = __ballot(e[j] == ee);
+      cg += __popcll(m);
+      cp += __popcll(m & below[j]);
+    }
+    if (lane == 0) {
+      wg[wave][ee] += cg;
+      wp[wave][ee] += cp;
+    }
   }
 }
 
@@ -349,9 +382,10 @@ __global__ __launch_bounds__(kBThreads, 2) void expand_block_multi(BlockMulti m)
 //                 outputs (they count the adapters of all ids and of the ids before the block).
 //   split_expand  (64-token block, d_out slice of 512): sums the partials in slice order,
 //                 scales, stages the B slices in LDS and writes y = y0 + sum_e mask_e(h) B_e.
-// The launch boundary orders the partials' writes before their reads.  Workgroup b takes block
-// b / slices and slice b % slices: with 8 slices, slice s runs on XCD s (workgroups are dispatched
-// round robin over the 8 XCDs), so each XCD's L2 holds one slice of every adapter.
+// The launch boundary orders the partials' writes before their reads.  Workgroups are dispatched
+// round robin over the 8 XCDs (workgroup b runs on XCD b % 8); both launches place every slice of
+// block tb on XCD tb % 8, so the partials that the shrink writes are still in that XCD's L2 when
+// the expand reads them.
 constexpr int kSTok = 64;
 constexpr int kSSlice = 512;
 constexpr int kSWaves = 8;
@@ -363,7 +397,7 @@ constexpr int split_group() {
 }
 
 struct SplitGeom {
-  int nblocks, kslices, cslices;
+  int nblocks, kslices, cslices;  // grid of a launch: 8 * ceil(nblocks / 8) * slices
   float* part;  // [nblocks][kslices][64][r_pad] fp32: partial h of each token on its own adapter
 };
 
@@ -378,15 +412,18 @@ __global__ __launch_bounds__(kSThreads) void split_shrink(StepArgs a, SplitGeom 
   __shared__ alignas(16) uint16_t As[GA][4 * piece];
   __shared__ float red[4][16][RB * 16 + 4];
   __shared__ StepLds S;
-  const int tb = blockIdx.x / g.kslices, sl = blockIdx.x % g.kslices;
+  __shared__ int wgc[kSWavesMax][kT8MaxU], wpc[kSWavesMax][kT8MaxU];
+  const int q = blockIdx.x >> 3;
+  const int tb = (q / g.kslices) * 8 + (blockIdx.x & 7), sl = q % g.kslices;
+  if (tb >= g.nblocks) return;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15, G = lane >> 4, rb = wave & 3, kh = wave >> 2;
   const int N = a.t.N, K = a.t.K, d_in = a.t.tgt.d_in, r_pad = a.t.tgt.r_pad;
   const int t0 = tb * kSTok;
   const bool disp = sl == 0;  // this workgroup writes the block's dispatch outputs
-  if (disp && threadIdx.x < 64) {
-    S.gcnt[threadIdx.x] = 0;
-    S.pcnt[threadIdx.x] = 0;
+  if (disp && threadIdx.x < kSWavesMax * kT8MaxU) {
+    (&wgc[0][0])[threadIdx.x] = 0;
+    (&wpc[0][0])[threadIdx.x] = 0;
   }
   // loads in use order: the block's ids (lane l: token t0 + l, clones of N - 1 past the end),
   // this thread's share of the first 2048 ids (dispatch workgroups), then the x rows
@@ -396,6 +433,7 @@ __global__ __launch_bounds__(kSThreads) void split_shrink(StepArgs a, SplitGeom 
 #pragma unroll
     for (int j = 0; j < kStepIdsPerThread; ++j) dv[j] = a.ids[min(j * kSThreads + (int)threadIdx.x, N - 1)];
   }
+  __builtin_amdgcn_sched_barrier(0);  // keep the issue order (data returns in issue order)
   const int S_all = d_in / kStepK;
   const int s0 = sl * (kSSlice / kStepK), s1 = min(s0 + kSSlice / kStepK, S_all);
   const int w0 = min(s0 + 2 * kh, s1), w1 = min(w0 + 2, s1);  // this wave's steps
@@ -408,6 +446,7 @@ __global__ __launch_bounds__(kSThreads) void split_shrink(StepArgs a, SplitGeom 
 #pragma unroll
     for (int c = 0; c < 4; ++c) xv[i][c] = ld16_nt(xp + st * kStepK + 32 * c);
   }
+  __builtin_amdgcn_sched_barrier(0);
   const int pe = step_owner(myid, a.bounds);
   uint32_t used = 0;
 #pragma unroll
@@ -420,6 +459,16 @@ __global__ __launch_bounds__(kSThreads) void split_shrink(StepArgs a, SplitGeom 
   for (int i = 0; i < 4; ++i) erow[i] = __shfl(pe, 16 * rb + 4 * G + i, kWave);
   int nbits = 0;
   while ((1 << nbits) < K) ++nbits;
+  if (disp) {
+    // dispatch counts while the x rows are in flight (the ids were requested before them)
+    __syncthreads();  // counters cleared
+    step_count_waves(wgc, wpc, a.bounds, dv, 0, N, K, t0);
+    for (int c0 = kStepIdsPerThread * kSThreads; c0 < N; c0 += kStepIdsPerThread * kSThreads) {
+#pragma unroll
+      for (int j = 0; j < kStepIdsPerThread; ++j) dv[j] = a.ids[min(c0 + j * kSThreads + (int)threadIdx.x, N - 1)];
+      step_count_waves(wgc, wpc, a.bounds, dv, c0, N, K, t0);
+    }
+  }
 
   f32x4_t hs[RB];
 #pragma unroll
@@ -433,16 +482,6 @@ __global__ __launch_bounds__(kSThreads) void split_shrink(StepArgs a, SplitGeom 
     for (int gi = 0; gi < ng; ++gi) {
       lds_copy_1k(As[gi], adapter_A<INDIRECT>(a.t.tgt, __builtin_ctz(r2)) + (size_t)s0 * piece, ns * piece * 2);
       r2 &= r2 - 1;
-    }
-    if (base == 0 && disp) {
-      // dispatch counts while the x rows and A slices are in flight
-      __syncthreads();  // counters cleared
-      step_count(S, a.bounds, dv, 0, N, nbits, t0);
-      for (int c0 = kStepIdsPerThread * kSThreads; c0 < N; c0 += kStepIdsPerThread * kSThreads) {
-#pragma unroll
-        for (int j = 0; j < kStepIdsPerThread; ++j) dv[j] = a.ids[min(c0 + j * kSThreads + (int)threadIdx.x, N - 1)];
-        step_count(S, a.bounds, dv, c0, N, nbits, t0);
-      }
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -491,7 +530,15 @@ __global__ __launch_bounds__(kSThreads) void split_shrink(StepArgs a, SplitGeom 
   if (!disp) return;
   // dispatch share of the block: offsets, then the block's tokens' grouped positions
   if (wave == 0) {
-    const int c = lane < K ? S.gcnt[lane] : 0;
+    int c = 0, cp = 0;
+    if (lane < K) {
+#pragma unroll
+      for (int w = 0; w < kSWaves; ++w) {
+        c += wgc[w][lane];
+        cp += wpc[w][lane];
+      }
+      S.pcnt[lane] = cp;
+    }
     const int incl = wave_incl_scan(c, lane);
     if (lane < K) S.offs[lane] = incl - c;
     if (tb == 0) {
@@ -524,15 +571,22 @@ __global__ __launch_bounds__(kSThreads) void split_shrink(StepArgs a, SplitGeom 
   }
 }
 
-template <int RB, bool INDIRECT, bool Y0F32, bool YF32>
+// ALLB (rank block 1, K <= 4): the B slices of all K adapters fit in LDS and are requested
+// before the y0 rows without waiting for the routing, so h and the MFMAs run while the y0 rows
+// are still arriving.  Otherwise the used adapters' slices are requested once the ids are in.
+template <int RB, bool INDIRECT, bool Y0F32, bool YF32, bool ALLB>
 __global__ __launch_bounds__(kSThreads) void split_expand(StepArgs a, SplitGeom g) {
   constexpr int GB = split_group<RB>();
   constexpr int RP = RB * 16;
   constexpr size_t y0b = Y0F32 ? 4 : 2, yb = YF32 ? 4 : 2;
   __shared__ alignas(16) uint16_t Bs[GB][kSSlice * RP];  // B^T rows of the slice [512][r_pad]
   __shared__ alignas(16) uint16_t hb[2][kSTok][RP];      // h hi / lo [part][token][rank]
-  const int tb = blockIdx.x / g.cslices, cs = blockIdx.x % g.cslices;
+  const int q = blockIdx.x >> 3;
+  const int tb = (q / g.cslices) * 8 + (blockIdx.x & 7), cs = q % g.cslices;
+  if (tb >= g.nblocks) return;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // wave: row block rb (16 tokens) x two 128-column blocks of the slice (512 contiguous bytes
+  // of each y0 / y row)
   const int n = lane & 15, G = lane >> 4, rb = wave & 3, ch = wave >> 2;
   const int N = a.t.N, K = a.t.K, d_out = a.t.tgt.d_out;
   const int t0 = tb * kSTok;
@@ -540,11 +594,13 @@ __global__ __launch_bounds__(kSThreads) void split_expand(StepArgs a, SplitGeom 
   const int nb = (c1 - c0) / kColBlock;  // 128-column blocks in the slice
   const int b0 = min(2 * ch, nb - 1), b1 = min(2 * ch + 1, nb - 1);
   const bool has0 = 2 * ch < nb, has1 = 2 * ch + 1 < nb;
-  // loads: the ids, the y0 rows of the first column block, the partials (every thread 16 bytes
-  // of each slice), the first group's B slices (straight into LDS, once the routing is known),
-  // then the y0 rows of the second column block.  Loads return in issue order: the first
-  // block's output is stored while the second block's y0 rows are still arriving.
+  // loads: the ids, the y0 rows of the first column block (ALLB: after the B slices), the
+  // partials (every thread 16 bytes of each slice), the B slices (straight into LDS), then the
+  // y0 rows of the second column block.  Loads return in issue order: the first block's output
+  // is stored while the second block's y0 rows are still arriving.
+  static_assert(!ALLB || RB == 1, "all-adapter staging holds four rank-16 slices");
   const int myid = a.ids[min(t0 + lane, N - 1)];
+  __builtin_amdgcn_sched_barrier(0);  // keep the issue order (data returns in issue order)
   const char* y0rows[4];
   char* yrows[4];
 #pragma unroll
@@ -554,7 +610,8 @@ __global__ __launch_bounds__(kSThreads) void split_expand(StepArgs a, SplitGeom 
     yrows[i] = reinterpret_cast<char*>(a.t.y) + (size_t)t * d_out * yb;
   }
   RowChunk<Y0F32> yc0, yc1;
-  load_row_chunk<Y0F32>(yc0, y0rows, c0 + b0 * kColBlock, n);
+  if constexpr (!ALLB) load_row_chunk<Y0F32>(yc0, y0rows, c0 + b0 * kColBlock, n);
+  __builtin_amdgcn_sched_barrier(0);
   constexpr int QPT = (kSTok * RP / 4 + kSThreads - 1) / kSThreads;  // 16-byte quads per thread
   constexpr int KSMAX = 8;  // slices loaded up front (the rest, d_in > 4096, at the sum)
   u32x4_t pv[QPT][KSMAX];
@@ -566,21 +623,33 @@ __global__ __launch_bounds__(kSThreads) void split_expand(StepArgs a, SplitGeom 
     for (int s = 0; s < KSMAX; ++s)
       if (s < g.kslices) pv[q][s] = ld16(pbase + (size_t)s * kSTok * RP + 4 * qi);
   }
+  __builtin_amdgcn_sched_barrier(0);
+  const int bbytes = (c1 - c0) * RP * 2;
+  if constexpr (ALLB) {
+    for (int e2 = 0; e2 < K; ++e2)
+      lds_copy_1k(Bs[e2], adapter_B<INDIRECT>(a.t.tgt, e2) + (size_t)c0 * RP, bbytes);
+    __builtin_amdgcn_sched_barrier(0);
+    load_row_chunk<Y0F32>(yc0, y0rows, c0 + b0 * kColBlock, n);
+  }
   const int pe = step_owner(myid, a.bounds);
   uint32_t used = 0;
 #pragma unroll
   for (int e = 0; e < kT8MaxU; ++e)
     if (e < K && __ballot(pe == e) != 0) used |= 1u << e;
   const int nU = __popc(used);
-  const int bbytes = (c1 - c0) * RP * 2;
-  uint32_t r2 = used;
-  for (int gi = 0; gi < min(GB, nU); ++gi) {
-    lds_copy_1k(Bs[gi], adapter_B<INDIRECT>(a.t.tgt, __builtin_ctz(r2)) + (size_t)c0 * RP, bbytes);
-    r2 &= r2 - 1;
+  if constexpr (!ALLB) {
+    uint32_t r2 = used;
+    for (int gi = 0; gi < min(GB, nU); ++gi) {
+      lds_copy_1k(Bs[gi], adapter_B<INDIRECT>(a.t.tgt, __builtin_ctz(r2)) + (size_t)c0 * RP, bbytes);
+      r2 &= r2 - 1;
+    }
   }
+  __builtin_amdgcn_sched_barrier(0);
   load_row_chunk<Y0F32>(yc1, y0rows, c0 + b1 * kColBlock, n);
-  // everything but the second block's y0 rows has arrived (vmcnt = that block's loads)
-  __builtin_amdgcn_s_waitcnt(0x0F70 | (Y0F32 ? 8 : 4));
+  __builtin_amdgcn_sched_barrier(0);
+  // everything before the y0 rows still to come has arrived (vmcnt = those rows' loads)
+  if constexpr (ALLB) __builtin_amdgcn_s_waitcnt(0x0F70 | (Y0F32 ? 16 : 8));
+  else __builtin_amdgcn_s_waitcnt(0x0F70 | (Y0F32 ? 8 : 4));
   // h = scale x (sum of the slices in order), split into bf16 hi / lo; unrouted tokens get 0
 #pragma unroll
   for (int q = 0; q < QPT; ++q) {
@@ -619,7 +688,7 @@ __global__ __launch_bounds__(kSThreads) void split_expand(StepArgs a, SplitGeom 
   uint32_t rem = used;
   for (int base = 0; base < nU; base += GB) {
     const int ng = min(GB, nU - base);
-    if (base > 0) {
+    if (!ALLB && base > 0) {
       __syncthreads();  // the previous group's slices are consumed
       uint32_t r3 = rem;
       for (int gi = 0; gi < ng; ++gi) {
@@ -632,6 +701,7 @@ __global__ __launch_bounds__(kSThreads) void split_expand(StepArgs a, SplitGeom 
     for (int gi = 0; gi < ng; ++gi) {
       const int e = __builtin_ctz(rem);
       rem &= rem - 1;
+      const uint16_t* Bl = Bs[ALLB ? e : gi];
       // A operand: row n of the row block, kept only if that token uses adapter e; k-slot
       // groups 0, 1 carry hi of ranks 16u + 8(G & 1) .., groups 2, 3 lo of the same ranks
       bf16x8_t hv[RB];
@@ -641,8 +711,8 @@ __global__ __launch_bounds__(kSThreads) void split_expand(StepArgs a, SplitGeom 
         if (erow != e) v = u32x4_t{0u, 0u, 0u, 0u};
         hv[u] = as_bf16x8(v);
       }
-      const uint16_t* bp0 = Bs[gi] + (size_t)(b0 * kColBlock + n) * RP + 8 * (G & 1);
-      const uint16_t* bp1 = Bs[gi] + (size_t)(b1 * kColBlock + n) * RP + 8 * (G & 1);
+      const uint16_t* bp0 = Bl + (size_t)(b0 * kColBlock + n) * RP + 8 * (G & 1);
+      const uint16_t* bp1 = Bl + (size_t)(b1 * kColBlock + n) * RP + 8 * (G & 1);
 #pragma unroll
       for (int j = 0; j < 8; ++j)
 #pragma unroll
@@ -1302,10 +1372,17 @@ static hipError_t launch_block_t(const BlockApplyArgs& ba, hipStream_t s) {
 }
 template <int RB, bool IND, bool Y0F, bool YF>
 static hipError_t launch_split_t(const StepArgs& sa, const SplitGeom& g, hipStream_t s) {
-  hipLaunchKernelGGL((split_shrink<RB, IND>), dim3(g.nblocks * g.kslices), dim3(kSThreads), 0, s, sa, g);
+  const int nb8 = 8 * ((g.nblocks + 7) / 8);
+  hipLaunchKernelGGL((split_shrink<RB, IND>), dim3(nb8 * g.kslices), dim3(kSThreads), 0, s, sa, g);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((split_expand<RB, IND, Y0F, YF>), dim3(g.nblocks * g.cslices), dim3(kSThreads), 0, s, sa, g);
+  if constexpr (RB == 1) {
+    if (sa.t.K <= split_group<1>()) {
+      hipLaunchKernelGGL((split_expand<RB, IND, Y0F, YF, true>), dim3(nb8 * g.cslices), dim3(kSThreads), 0, s, sa, g);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((split_expand<RB, IND, Y0F, YF, false>), dim3(nb8 * g.cslices), dim3(kSThreads), 0, s, sa, g);
   return hipGetLastError();
 }
 template <int RB, bool IND, bool Y0F, bool YF>
