@@ -446,6 +446,7 @@ __global__ __launch_bounds__(kSThreads) void split_shrink(StepArgs a, SplitGeom 
 #pragma unroll
     for (int c = 0; c < 4; ++c) xv[i][c] = ld16_nt(xp + st * kStepK + 32 * c);
   }
+  const int ns = s1 - s0;
   __builtin_amdgcn_sched_barrier(0);
   const int pe = step_owner(myid, a.bounds);
   uint32_t used = 0;
@@ -473,10 +474,11 @@ __global__ __launch_bounds__(kSThreads) void split_shrink(StepArgs a, SplitGeom 
   f32x4_t hs[RB];
 #pragma unroll
   for (int u = 0; u < RB; ++u) hs[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  const int ns = s1 - s0;
   uint32_t rem = used;
   for (int base = 0; base < max(nU, 1); base += GA) {
     const int ng = min(GA, nU - base);
+    // the used adapters' slices of this group (requested once the routing is known: staging
+    // every adapter's slice up front costs more in extra traffic than it saves in latency)
     if (base > 0) __syncthreads();  // the previous group's slices are consumed
     uint32_t r2 = rem;
     for (int gi = 0; gi < ng; ++gi) {
@@ -488,6 +490,7 @@ __global__ __launch_bounds__(kSThreads) void split_shrink(StepArgs a, SplitGeom 
     for (int gi = 0; gi < ng; ++gi) {
       const int e = __builtin_ctz(rem);
       rem &= rem - 1;
+      if (__ballot(erow[0] == e || erow[1] == e || erow[2] == e || erow[3] == e) == 0) continue;
       f32x4_t acc[RB];
 #pragma unroll
       for (int u = 0; u < RB; ++u) acc[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
