@@ -259,18 +259,25 @@ int molora_apply_multi(const molora_hotset *hs, int n, const int *targets,
  * per-token weighted sum; Table 4 "Per-token + Graph": the step as few
  * launches as possible).  Equivalent to molora_route_vocab, molora_dispatch
  * and molora_apply with k = 1, producing bit-identical idx, w, counts,
- * offsets, perm, perm_w, inv and y: with a workspace of
- * molora_step_workspace() bytes the apply is MOLORA_PATH_BLOCK (a shrink
- * launch and an expand launch), without one (ws NULL) MOLORA_PATH_TILE (one
- * launch).  Every workgroup routes its own tokens from their ids and derives
- * its share of the dispatch outputs by counting all N ids.  Batches above
- * 4096 tokens run route, dispatch and apply as separate launches.
+ * offsets, perm, perm_w, inv and y.  With a workspace of
+ * molora_step_workspace() bytes the step is two launches over 512-wide
+ * slices: the first routes 64-token blocks, writes each token's partial
+ * x A_e per d_in slice (its own adapter only) and the dispatch outputs, the
+ * second sums the partials in slice order and writes y per output slice; y
+ * equals MOLORA_PATH_BLOCK's bit for bit.  Without one (ws NULL) the step is
+ * one launch of MOLORA_PATH_TILE.  Every workgroup routes its own tokens from
+ * their ids and derives its share of the dispatch outputs by counting all N
+ * ids.  Batches above 4096 tokens run route, dispatch and apply as separate
+ * launches.
  *   hs, target    hot set with K = hs->K adapters (K <= 16) and the projection
  *   ids, bounds   as molora_route_vocab (bounds: host int32 [K+1])
  *   x, y0, y      as molora_apply (y0 may equal y)
  *   idx, w        device [N] out, as molora_route_vocab
  *   counts..inv   device out, as molora_dispatch with k = 1 (inv required)
- *   ws            NULL, or device workspace of molora_step_workspace() bytes
+ *   ws            NULL, or device workspace of molora_step_workspace() bytes,
+ *                 256-byte aligned, owned by the caller; its contents need no
+ *                 initialisation and are scratch for the call (fp32 partial
+ *                 sums [ceil(N/64)][ceil(d_in/512)][64][r_pad])
  * ------------------------------------------------------------------------ */
 int molora_step_workspace(const molora_hotset *hs, int target, int N, size_t *bytes);
 int molora_step_vocab(const molora_hotset *hs, int target, const int32_t *ids, int N,

@@ -332,10 +332,12 @@ def molora_step_workspace(hs: HotSet, target: int, N: int) -> int:
 def molora_step_vocab(hs: HotSet, ids: torch.Tensor, bounds: Sequence[int], x: torch.Tensor, y0: torch.Tensor,
                       target: int = 0, y: Optional[torch.Tensor] = None, y_dtype=None, route=None, meta=None,
                       ws: Optional[torch.Tensor] = None, stream=None):
-    """One launch of route_vocab + dispatch + apply (k = 1).  Returns (y, (idx, w),
+    """route_vocab + dispatch + apply (k = 1) in one call.  Returns (y, (idx, w),
     (counts, offsets, perm, perm_w, inv)); `route` and `meta` may supply those buffers.
-    `ws` (uint8, zero-filled, at least molora_step_workspace bytes) selects the block apply;
-    without it the tile apply runs."""
+    `ws` (uint8, 256-byte aligned, at least molora_step_workspace bytes; no initialisation
+    needed) selects the two-launch split step over 512-wide slices; without it the one-launch
+    tile step runs.
+    """
     N = ids.numel()
     K = len(bounds) - 1
     dev = ids.device
