@@ -44,7 +44,13 @@ def cases():
         holes.append((f"unrouted_tiles_r{r}", h))
     dead = synth.vocab_case(N=100, d=4096, K=4, r=32, case_id=13, runs=False)
     dead.ids = np.full_like(dead.ids, -1)
-    return [("tiny", tiny), ("modality4", mod), ("ragged_unrouted", odd), *holes, ("all_unrouted", dead)]
+    # rank blocks 3 and 4, and more adapters than the split expand stages at once (groups)
+    wide = [
+        ("k16_r64", synth.vocab_case(N=300, d=1024, K=16, r=64, case_id=14, runs=True, probs=(1 / 16,) * 16)),
+        ("k9_r16", synth.vocab_case(N=777, d=2048, K=9, r=16, case_id=15, runs=True, probs=(1 / 9,) * 9)),
+        ("k3_r48", synth.vocab_case(N=200, d=1536, K=3, r=48, case_id=16, runs=False)),
+    ]
+    return [("tiny", tiny), ("modality4", mod), ("ragged_unrouted", odd), *holes, ("all_unrouted", dead), *wide]
 
 
 @pytest.mark.parametrize("block", [False, True])
