@@ -275,9 +275,14 @@ int molora_apply_multi(const molora_hotset *hs, int n, const int *targets,
  *   idx, w        device [N] out, as molora_route_vocab
  *   counts..inv   device out, as molora_dispatch with k = 1 (inv required)
  *   ws            NULL, or device workspace of molora_step_workspace() bytes,
- *                 256-byte aligned, owned by the caller; its contents need no
- *                 initialisation and are scratch for the call (fp32 partial
- *                 sums [ceil(N/64)][ceil(d_in/512)][64][r_pad])
+ *                 256-byte aligned, owned by the caller, zero-filled before its
+ *                 first use with a given N and left alone between calls: it
+ *                 starts with control words (an epoch and per-(block, slice)
+ *                 flags) used when the environment sets MOLORA_SPLIT_FUSED=1,
+ *                 which runs the split step as one launch (each workgroup
+ *                 publishes its slice's partials and waits, bounded, for its
+ *                 block's others, else computes them itself); then the fp32
+ *                 partial sums [ceil(N/64)][ceil(d_in/512)][64][r_pad]
  * ------------------------------------------------------------------------ */
 int molora_step_workspace(const molora_hotset *hs, int target, int N, size_t *bytes);
 int molora_step_vocab(const molora_hotset *hs, int target, const int32_t *ids, int N,

@@ -19,11 +19,11 @@ def three_calls(m, hs, ids, bounds, K, x, y0, y_dtype, path):
 
 
 def step_ws(m, hs, N, block):
-    """A step workspace (block apply), or None (tile apply); filled with NaN bytes, so that a
-    partial sum read before it is written would show."""
+    """A step workspace (split step), or None (tile step): zero-filled, as the fused launch's
+    control words at its start must be before the first call."""
     if not block:
         return None
-    return torch.full((m.molora_step_workspace(hs, 0, N),), 0xFF, dtype=torch.uint8, device="cuda")
+    return torch.zeros((m.molora_step_workspace(hs, 0, N),), dtype=torch.uint8, device="cuda")
 
 
 def cases():
@@ -181,3 +181,69 @@ def test_block_step_reuses_workspace_across_inputs_and_graph_replays():
         g.replay()
         torch.cuda.synchronize()
         np.testing.assert_array_equal(host(y), eager)
+
+
+def _split_env(fused, spin=None):
+    import os
+    old = {k: os.environ.get(k) for k in ("MOLORA_SPLIT_FUSED", "MOLORA_SPLIT_SPIN")}
+    os.environ["MOLORA_SPLIT_FUSED"] = "1" if fused else "0"
+    if spin is None:
+        os.environ.pop("MOLORA_SPLIT_SPIN", None)
+    else:
+        os.environ["MOLORA_SPLIT_SPIN"] = str(spin)
+    return old
+
+
+def _restore_env(old):
+    import os
+    for k, v in old.items():
+        if v is None:
+            os.environ.pop(k, None)
+        else:
+            os.environ[k] = v
+
+
+@pytest.mark.parametrize("name", ["modality4", "k9_r16", "k3_r48"])
+def test_split_fused_equals_two_launches(name):
+    """The fused split launch (partials published per block inside one launch) gives the same
+    bits as the two-launch split step, on calls in a row that alternate two inputs (a partial
+    left from the previous call would show), under graph replays, and with every workgroup
+    forced onto the fallback that recomputes the block's other slices itself."""
+    m = need_gpu()
+    case = dict(cases())[name]
+    t = case.targets[0]
+    hs = m.molora_hotset_init([(dev_bf16(t.A), dev_bf16(t.B))], case.scale)
+    ids = dev(case.ids)
+    bounds = case.bounds.tolist()
+    xa, y0 = dev_bf16(t.x), dev_bf16(t.y0)
+    xb = torch.flip(xa, dims=[0]).contiguous()
+    old = _split_env(False)
+    try:
+        refs = [m.molora_step_vocab(hs, ids, bounds, x, y0, ws=step_ws(m, hs, case.N, True))[0] for x in (xa, xb)]
+        for spin in (None, -1):
+            _split_env(True, spin)
+            ws = step_ws(m, hs, case.N, True)
+            for i in range(5):
+                y, r, meta = m.molora_step_vocab(hs, ids, bounds, (xa, xb)[i % 2], y0, ws=ws)
+                np.testing.assert_array_equal(host(y), host(refs[i % 2]))
+        # graph replays (fused, default wait), eager calls in between
+        _split_env(True)
+        ws = step_ws(m, hs, case.N, True)
+        out = torch.empty_like(y0)
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            m.molora_step_vocab(hs, ids, bounds, xa, y0, y=out, ws=ws)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            m.molora_step_vocab(hs, ids, bounds, xa, y0, y=out, ws=ws)
+        for _ in range(3):
+            out.fill_(0)
+            g.replay()
+            torch.cuda.synchronize()
+            np.testing.assert_array_equal(host(out), host(refs[0]))
+            yb, _, _ = m.molora_step_vocab(hs, ids, bounds, xb, y0, ws=ws)
+            np.testing.assert_array_equal(host(yb), host(refs[1]))
+    finally:
+        _restore_env(old)

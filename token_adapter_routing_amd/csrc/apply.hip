@@ -405,22 +405,31 @@ __host__ __device__ inline size_t split_part_floats(int N, int d_in, int r_pad) 
   return (size_t)((N + kSTok - 1) / kSTok) * ((d_in + kSSlice - 1) / kSSlice) * kSTok * r_pad;
 }
 
-template <int RB, bool INDIRECT>
-__global__ __launch_bounds__(kSThreads) void split_shrink(StepArgs a, SplitGeom g) {
+template <int RB>
+struct ShrinkLds {
+  alignas(16) uint16_t As[split_group<RB>()][4 * RB * 16 * kStepK];
+  float red[4][16][RB * 16 + 4];
+  StepLds S;
+  int wgc[kSWavesMax][kT8MaxU], wpc[kSWavesMax][kT8MaxU];
+};
+
+// Partial h of block tb, reduction slice sl (and, when disp, the block's dispatch outputs).
+// `pre(used)` runs once the first group's A slices are requested and before their data is
+// awaited: the fused launch requests its expand's loads there.
+template <int RB, bool INDIRECT, typename Pre>
+__device__ __forceinline__ void shrink_slice(const StepArgs& a, const SplitGeom& g, int tb, int sl, bool disp,
+                                             ShrinkLds<RB>& L, Pre pre) {
   constexpr int GA = split_group<RB>();
   constexpr int piece = RB * 16 * kStepK;  // elements of one reduction step's A pieces
-  __shared__ alignas(16) uint16_t As[GA][4 * piece];
-  __shared__ float red[4][16][RB * 16 + 4];
-  __shared__ StepLds S;
-  __shared__ int wgc[kSWavesMax][kT8MaxU], wpc[kSWavesMax][kT8MaxU];
-  const int q = blockIdx.x >> 3;
-  const int tb = (q / g.kslices) * 8 + (blockIdx.x & 7), sl = q % g.kslices;
-  if (tb >= g.nblocks) return;
+  auto& As = L.As;
+  auto& red = L.red;
+  auto& S = L.S;
+  auto& wgc = L.wgc;
+  auto& wpc = L.wpc;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15, G = lane >> 4, rb = wave & 3, kh = wave >> 2;
   const int N = a.t.N, K = a.t.K, d_in = a.t.tgt.d_in, r_pad = a.t.tgt.r_pad;
   const int t0 = tb * kSTok;
-  const bool disp = sl == 0;  // this workgroup writes the block's dispatch outputs
   if (disp && threadIdx.x < kSWavesMax * kT8MaxU) {
     (&wgc[0][0])[threadIdx.x] = 0;
     (&wpc[0][0])[threadIdx.x] = 0;
@@ -485,6 +494,7 @@ __global__ __launch_bounds__(kSThreads) void split_shrink(StepArgs a, SplitGeom 
       lds_copy_1k(As[gi], adapter_A<INDIRECT>(a.t.tgt, __builtin_ctz(r2)) + (size_t)s0 * piece, ns * piece * 2);
       r2 &= r2 - 1;
     }
+    if (base == 0) pre(used);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     for (int gi = 0; gi < ng; ++gi) {
@@ -570,6 +580,256 @@ __global__ __launch_bounds__(kSThreads) void split_shrink(StepArgs a, SplitGeom 
       } else {
         a.inv[tok] = -1;
       }
+    }
+  }
+}
+
+template <int RB, bool INDIRECT>
+__global__ __launch_bounds__(kSThreads) void split_shrink(StepArgs a, SplitGeom g) {
+  __shared__ ShrinkLds<RB> L;
+  const int q = blockIdx.x >> 3;
+  const int tb = (q / g.kslices) * 8 + (blockIdx.x & 7), sl = q % g.kslices;
+  if (tb >= g.nblocks) return;
+  shrink_slice<RB, INDIRECT>(a, g, tb, sl, sl == 0, L, [](uint32_t) {});  // slice 0: dispatch outputs
+}
+
+// The same step as one launch (split_shrink + split_expand fused).  Workgroup (block tb, slice
+// j) computes shrink slice j, publishes it, then expands output slice j once the block's partials
+// are all published; the y0 rows and B slices of its expand are requested before it waits, so
+// they stream during the other workgroups' shrinks.  All slices of block tb run on XCD tb mod 8
+// (workgroups are dispatched round robin over the XCDs), so the partials and the flags that
+// publish them meet in that XCD's L2.  Publication: after its partial stores have completed a
+// workgroup writes the launch's epoch into flag[tb][j]; the epoch is read from the workspace
+// header at the start and advanced by the last workgroup to finish, so a flag equal to it was
+// written by this launch.  The wait is bounded: a workgroup that is not answered within
+// `spin` polls (a workgroup of its block not resident, or running on another XCD) computes
+// every other slice's partial itself, with the same code and so the same bits, and goes on;
+// the launch therefore always completes and always produces the same y.
+template <int RB>
+struct ExpandLds {
+  alignas(16) uint16_t Bs[split_group<RB>()][kSSlice * RB * 16];
+  alignas(16) uint16_t hb[2][kSTok][RB * 16];
+};
+struct FusedHdr {  // workspace words after the partials
+  unsigned epoch;  // epoch of the last completed launch
+  unsigned done;   // workgroups of the current launch that have finished
+};
+constexpr int kSMaxSlices = 64;  // d <= 32768
+
+// The shrink's and the expand's LDS side by side (rank blocks 1..3: at most 145 KB), else shared.
+template <int RB>
+struct FusedLdsT {
+  static constexpr bool kSeparate = true;
+  ShrinkLds<RB> s;
+  ExpandLds<RB> e;
+};
+template <>
+struct FusedLdsT<4> {
+  static constexpr bool kSeparate = false;
+  union {
+    ShrinkLds<4> s;
+    ExpandLds<4> e;
+  };
+};
+
+template <int RB, bool INDIRECT, bool Y0F32, bool YF32, bool ALLB>
+__global__ __launch_bounds__(kSThreads) void split_fused(StepArgs a, SplitGeom g, FusedHdr* hdr, unsigned* flags,
+                                                         int spin) {
+  constexpr int GB = split_group<RB>();
+  constexpr int RP = RB * 16;
+  constexpr size_t y0b = Y0F32 ? 4 : 2, yb = YF32 ? 4 : 2;
+  static_assert(!ALLB || RB == 1, "all-adapter staging holds four rank-16 slices");
+  __shared__ FusedLdsT<RB> L;
+  constexpr bool EARLY_B = FusedLdsT<RB>::kSeparate;  // the expand's B slices load with the shrink's
+  __shared__ unsigned epoch_s;
+  __shared__ int fallback_s, stray_s;
+  const int SL = max(g.kslices, g.cslices);
+  const int q = blockIdx.x >> 3;
+  const int tb = (q / SL) * 8 + (blockIdx.x & 7), j = q % SL;
+  if (tb >= g.nblocks) return;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n = lane & 15, G = lane >> 4, rb = wave & 3, ch = wave >> 2;
+  const int N = a.t.N, K = a.t.K, d_out = a.t.tgt.d_out;
+  const int t0 = tb * kSTok;
+  if (threadIdx.x == 0) {
+    epoch_s = __hip_atomic_load(&hdr->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
+    // a workgroup off the XCD that its block's slices share publishes nothing (its partial is
+    // not in that XCD's L2) and computes the other slices itself
+    stray_s = (__builtin_amdgcn_s_getreg((31 << 11) | 20) & 15) != (int)(blockIdx.x & 7);
+  }
+  const bool expand = j < g.cslices;
+  const int c0 = expand ? j * kSSlice : 0, c1 = min(c0 + kSSlice, d_out);
+  const int nb = (c1 - c0) / kColBlock;
+  const int b0 = min(2 * ch, nb - 1), b1 = min(2 * ch + 1, nb - 1);
+  const bool has0 = expand && 2 * ch < nb, has1 = expand && 2 * ch + 1 < nb;
+  const int bbytes = (c1 - c0) * RP * 2;
+  const char* y0rows[4];
+  char* yrows[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int t = min(t0 + 16 * rb + 4 * G + i, N - 1);
+    y0rows[i] = reinterpret_cast<const char*>(a.t.y0) + (size_t)t * d_out * y0b;
+    yrows[i] = reinterpret_cast<char*>(a.t.y) + (size_t)t * d_out * yb;
+  }
+  RowChunk<Y0F32> yc0, yc1;
+  auto stage_b = [&](uint32_t used_) {
+    if (!expand) return;
+    if constexpr (ALLB) {
+      for (int e2 = 0; e2 < K; ++e2)
+        lds_copy_1k(L.e.Bs[e2], adapter_B<INDIRECT>(a.t.tgt, e2) + (size_t)c0 * RP, bbytes);
+    } else {
+      uint32_t r2 = used_;
+      for (int gi = 0; gi < min(GB, __popc(used_)); ++gi) {
+        lds_copy_1k(L.e.Bs[gi], adapter_B<INDIRECT>(a.t.tgt, __builtin_ctz(r2)) + (size_t)c0 * RP, bbytes);
+        r2 &= r2 - 1;
+      }
+    }
+  };
+  // the expand's loads that do not need the other slices (B slices when their LDS is separate,
+  // y0 rows), requested with the shrink's so that HBM streams them together
+  auto prefetch = [&](uint32_t used_) {
+    if constexpr (EARLY_B) stage_b(used_);
+    __builtin_amdgcn_sched_barrier(0);
+    load_row_chunk<Y0F32>(yc0, y0rows, c0 + b0 * kColBlock, n);
+    load_row_chunk<Y0F32>(yc1, y0rows, c0 + b1 * kColBlock, n);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // ---- shrink slice j (publishes nothing yet)
+  const int myid = a.ids[min(t0 + lane, N - 1)];
+  const int pe = step_owner(myid, a.bounds);
+  uint32_t used = 0;
+#pragma unroll
+  for (int e = 0; e < kT8MaxU; ++e)
+    if (e < K && __ballot(pe == e) != 0) used |= 1u << e;
+  const int nU = __popc(used);
+  if (j < g.kslices) shrink_slice<RB, INDIRECT>(a, g, tb, j, j == 0, L.s, prefetch);
+  else prefetch(used);
+  __syncthreads();  // the shrink's LDS is free
+  const unsigned E = epoch_s;
+  if constexpr (!EARLY_B) stage_b(used);
+  // the partial stores (and every load above) have completed
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  // ---- publish slice j, then wait for the block's other slices
+  if (threadIdx.x == 0) {
+    const int stray = stray_s;
+    if (!stray) __hip_atomic_store(&flags[(size_t)tb * kSMaxSlices + j], E, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    int fb = stray;
+    if (expand && !fb && spin < 0) fb = 1;  // forced (tests of the fallback)
+    if (expand && !fb) {
+      for (int it = 0;; ++it) {
+        bool all = true;
+        for (int s2 = 0; s2 < SL; ++s2)
+          all = all && __hip_atomic_load(&flags[(size_t)tb * kSMaxSlices + s2], __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT) == E;
+        if (all) break;
+        if (it >= spin) {
+          fb = 1;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(2);
+      }
+    }
+    fallback_s = fb;
+  }
+  __syncthreads();
+  if (expand) {
+    if (fallback_s) {
+      // not answered in time: compute the other slices' partials here (same code, same bits);
+      // they overwrite the workspace with the values their own workgroups write
+      for (int s2 = 0; s2 < g.kslices; ++s2) {
+        if (s2 == j) continue;
+        shrink_slice<RB, INDIRECT>(a, g, tb, s2, false, L.s, [](uint32_t) {});
+        __syncthreads();
+      }
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      // the B slices again when the shrink reused their LDS
+      if constexpr (!EARLY_B) {
+        stage_b(used);
+        __builtin_amdgcn_s_waitcnt(0);
+      }
+    }
+    // h = scale x (sum of the slices in order), split into bf16 hi / lo; unrouted tokens get 0
+    constexpr int QPT = (kSTok * RP / 4 + kSThreads - 1) / kSThreads;
+    const float* pbase = g.part + (size_t)tb * g.kslices * kSTok * RP;
+#pragma unroll
+    for (int qq = 0; qq < QPT; ++qq) {
+      const int qi = qq * kSThreads + (int)threadIdx.x;
+      const int tok = min(qi, kSTok * RP / 4 - 1) / (RP / 4), rk = 4 * (qi % (RP / 4));
+      const float wt = __shfl(pe, tok, kWave) >= 0 ? a.t.scale : 0.f;
+      if (qi < kSTok * RP / 4) {
+        float sum[4] = {0.f, 0.f, 0.f, 0.f};
+        for (int s2 = 0; s2 < g.kslices; ++s2) {
+          const u32x4_t v = ld16(pbase + (size_t)s2 * kSTok * RP + 4 * qi);
+#pragma unroll
+          for (int c = 0; c < 4; ++c) sum[c] += __uint_as_float(v[c]);
+        }
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const float h = sum[c] * wt;
+          const __bf16 hi = (__bf16)h;
+          const __bf16 lo = (__bf16)(h - (float)hi);
+          L.e.hb[0][tok][rk + c] = __builtin_bit_cast(uint16_t, hi);
+          L.e.hb[1][tok][rk + c] = __builtin_bit_cast(uint16_t, lo);
+        }
+      }
+    }
+    f32x4_t o0[8], o1[8];
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+      o0[jj] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      o1[jj] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+    const int erow = __shfl(pe, 16 * rb + n, kWave);
+    uint32_t rem = used;
+    for (int base = 0; base < nU; base += GB) {
+      const int ng = min(GB, nU - base);
+      if (!ALLB && base > 0) {
+        __syncthreads();
+        uint32_t r3 = rem;
+        for (int gi = 0; gi < ng; ++gi) {
+          lds_copy_1k(L.e.Bs[gi], adapter_B<INDIRECT>(a.t.tgt, __builtin_ctz(r3)) + (size_t)c0 * RP, bbytes);
+          r3 &= r3 - 1;
+        }
+        __builtin_amdgcn_s_waitcnt(0);
+      }
+      __syncthreads();  // the group's B slices and h are in LDS
+      for (int gi = 0; gi < ng; ++gi) {
+        const int e = __builtin_ctz(rem);
+        rem &= rem - 1;
+        const uint16_t* Bl = L.e.Bs[ALLB ? e : gi];
+        bf16x8_t hv[RB];
+#pragma unroll
+        for (int u = 0; u < RB; ++u) {
+          u32x4_t v = *reinterpret_cast<const u32x4_t*>(&L.e.hb[G >> 1][16 * rb + n][u * 16 + 8 * (G & 1)]);
+          if (erow != e) v = u32x4_t{0u, 0u, 0u, 0u};
+          hv[u] = as_bf16x8(v);
+        }
+        const uint16_t* bp0 = Bl + (size_t)(b0 * kColBlock + n) * RP + 8 * (G & 1);
+        const uint16_t* bp1 = Bl + (size_t)(b1 * kColBlock + n) * RP + 8 * (G & 1);
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj)
+#pragma unroll
+          for (int u = 0; u < RB; ++u) {
+            const u32x4_t v0 = *reinterpret_cast<const u32x4_t*>(bp0 + (size_t)16 * jj * RP + 16 * u);
+            const u32x4_t v1 = *reinterpret_cast<const u32x4_t*>(bp1 + (size_t)16 * jj * RP + 16 * u);
+            o0[jj] = mfma16x16x32(hv[u], as_bf16x8(v0), o0[jj]);
+            o1[jj] = mfma16x16x32(hv[u], as_bf16x8(v1), o1[jj]);
+          }
+      }
+    }
+    if (has0) epilogue_store<Y0F32, YF32>(o0, yc0, yrows, c0 + b0 * kColBlock, n, 0xFu);
+    if (has1) epilogue_store<Y0F32, YF32>(o1, yc1, yrows, c0 + b1 * kColBlock, n, 0xFu);
+  }
+  // the last workgroup to finish advances the epoch for the next launch
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const unsigned total = (unsigned)(g.nblocks * SL);
+    const unsigned d = __hip_atomic_fetch_add(&hdr->done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (d == total - 1) {
+      __hip_atomic_store(&hdr->done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&hdr->epoch, E, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 }
@@ -1250,9 +1510,11 @@ static size_t block_ws(int N, int k, int K, int r_pad, int d_in) {
   return block_part_floats(nblocks, slotmax, kslices, r_pad) * sizeof(float);
 }
 
+static size_t split_ws_bytes(int N, int d_in, int r_pad);
+static size_t split_ctrl_bytes(int N);
 size_t step_ws_bytes(int N, int K, int r_pad, int d_in) {
   (void)K;
-  return split_part_floats(N, d_in, r_pad) * sizeof(float);
+  return split_ws_bytes(N, d_in, r_pad);
 }
 
 // Grouped path on 64-row tiles: used for k > 1 (passes over ranked slots) or ranks above 32.
@@ -1373,14 +1635,43 @@ static hipError_t launch_block_t(const BlockApplyArgs& ba, hipStream_t s) {
   hipLaunchKernelGGL((expand_block<RB, IND, Y0F, YF>), dim3(ba.b.nblocks * ba.b.cslices), dim3(kBThreads), 0, s, ba);
   return hipGetLastError();
 }
+// Split step workspace: control words of the fused launch (the header, then one flag per
+// (block, slice)), which must be zero before the first call, then the partials.
+static size_t split_ctrl_bytes(int N) {
+  const size_t nblocks = (N + kSTok - 1) / kSTok;
+  return 256 + (nblocks * kSMaxSlices * sizeof(unsigned) + 255) / 256 * 256;
+}
+static size_t split_ws_bytes(int N, int d_in, int r_pad) {
+  return split_ctrl_bytes(N) + split_part_floats(N, d_in, r_pad) * sizeof(float);
+}
+
 template <int RB, bool IND, bool Y0F, bool YF>
-static hipError_t launch_split_t(const StepArgs& sa, const SplitGeom& g, hipStream_t s) {
+static hipError_t launch_split_t(const StepArgs& sa, const SplitGeom& g, void* ctrl, hipStream_t s) {
   const int nb8 = 8 * ((g.nblocks + 7) / 8);
+  const int SL = std::max(g.kslices, g.cslices);
+  const bool allb = RB == 1 && sa.t.K <= split_group<1>();
+  // the fused single launch is opt-in: its publish-and-wait costs more than the launch boundary
+  // it removes (4-modality step: 17.8 us fused against 15.0 us in two launches)
+  if (env_int("MOLORA_SPLIT_FUSED", 0) != 0 && SL <= kSMaxSlices) {
+    FusedHdr* hdr = reinterpret_cast<FusedHdr*>(ctrl);
+    unsigned* flags = reinterpret_cast<unsigned*>(reinterpret_cast<char*>(ctrl) + 256);
+    const int spin = env_int("MOLORA_SPLIT_SPIN", 20000);
+    if constexpr (RB == 1) {
+      if (allb) {
+        hipLaunchKernelGGL((split_fused<RB, IND, Y0F, YF, true>), dim3(nb8 * SL), dim3(kSThreads), 0, s, sa, g, hdr,
+                           flags, spin);
+        return hipGetLastError();
+      }
+    }
+    hipLaunchKernelGGL((split_fused<RB, IND, Y0F, YF, false>), dim3(nb8 * SL), dim3(kSThreads), 0, s, sa, g, hdr, flags,
+                       spin);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL((split_shrink<RB, IND>), dim3(nb8 * g.kslices), dim3(kSThreads), 0, s, sa, g);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if constexpr (RB == 1) {
-    if (sa.t.K <= split_group<1>()) {
+    if (allb) {
       hipLaunchKernelGGL((split_expand<RB, IND, Y0F, YF, true>), dim3(nb8 * g.cslices), dim3(kSThreads), 0, s, sa, g);
       return hipGetLastError();
     }
@@ -1795,9 +2086,9 @@ hipError_t launch_step_vocab(const StepVocabLaunch& a, hipStream_t s) {
     g.nblocks = (a.apply.N + kSTok - 1) / kSTok;
     g.kslices = (a.apply.tgt.d_in + kSSlice - 1) / kSSlice;
     g.cslices = (a.apply.tgt.d_out + kSSlice - 1) / kSSlice;
-    g.part = reinterpret_cast<float*>(a.ws);
+    g.part = reinterpret_cast<float*>(reinterpret_cast<char*>(a.ws) + split_ctrl_bytes(a.apply.N));
     MOLORA_DISPATCH_RB(RBv, MOLORA_DISPATCH_BOOL(a.apply.indirect, IND, MOLORA_DISPATCH_BOOL(a.apply.y0_f32, Y0F,
-        MOLORA_DISPATCH_BOOL(a.apply.y_f32, YF, err = (launch_split_t<RB, IND, Y0F, YF>(sa, g, s))))));
+        MOLORA_DISPATCH_BOOL(a.apply.y_f32, YF, err = (launch_split_t<RB, IND, Y0F, YF>(sa, g, a.ws, s))))));
     return err;
   }
   const int grid = 8 * sa.t.tiles_per_xcd * sa.t.col_groups;
