@@ -964,6 +964,7 @@ __global__ __launch_bounds__(kSThreads) void split_expand(StepArgs a, SplitGeom 
     for (int gi = 0; gi < ng; ++gi) {
       const int e = __builtin_ctz(rem);
       rem &= rem - 1;
+      if (__ballot(erow == e) == 0) continue;  // no token of this row block uses adapter e
       const uint16_t* Bl = Bs[ALLB ? e : gi];
       // A operand: row n of the row block, kept only if that token uses adapter e; k-slot
       // groups 0, 1 carry hi of ranks 16u + 8(G & 1) .., groups 2, 3 lo of the same ranks
