@@ -214,7 +214,13 @@ __device__ void block_expand(const BlockArgs& a, BlockLds<RB>& L, const Route& r
     y0rows[i] = reinterpret_cast<const char*>(a.y0) + (size_t)t * d_out * y0b;
     yrows[i] = reinterpret_cast<char*>(a.y) + (size_t)t * d_out * yb;
   }
+  // the y0 rows first: they do not depend on the routing and are the HBM stream of this launch
+  // (everything requested after them returns after them, and is needed before them only by
+  // work that is short next to their latency)
   RowChunk<Y0F32> yc0, yc1;
+  load_row_chunk<Y0F32>(yc0, y0rows, c0 + b0 * kColBlock, n);
+  load_row_chunk<Y0F32>(yc1, y0rows, c0 + b1 * kColBlock, n);
+  __builtin_amdgcn_sched_barrier(0);
   // routing: used adapters and the (slot, token) weights; token thread t sums its pairs in order
   const uint32_t used = block_used(rt, t0, a.N, a.k, a.K);
   const int nU = __popc(used);
@@ -236,19 +242,35 @@ __device__ void block_expand(const BlockArgs& a, BlockLds<RB>& L, const Route& r
       r2 &= r2 - 1;
     }
   };
-  // h of a group's slots: sum the slices in order, weight, split into hi / lo
+  // h of a group's slots: sum the slices in order, weight, split into hi / lo.  A thread takes
+  // 4 consecutive ranks (16 bytes) of one (slot, token) and requests all its slices at once.
   auto group_h = [&](int base, int ng) {
-    for (int v = threadIdx.x; v < ng * kBTok * RB * 16; v += kBThreads) {
-      const int g = v / (kBTok * RB * 16), vi = v % (kBTok * RB * 16);
-      const int tok = vi / (RB * 16), rk = vi % (RB * 16);
+    constexpr int KS = 8;  // slices requested together
+    for (int v = threadIdx.x; v < ng * kBTok * RB * 4; v += kBThreads) {
+      const int g = v / (kBTok * RB * 4), vi = v % (kBTok * RB * 4);
+      const int tok = vi / (RB * 4), rk = 4 * (vi % (RB * 4));
       const float* src = a.part + (((size_t)tb * a.slotmax + base + g) * a.kslices * kBTok + tok) * r_pad + rk;
-      float sum = 0.f;
-      for (int s = 0; s < a.kslices; ++s) sum += src[(size_t)s * kBTok * r_pad];
-      const float h = sum * L.wt[base + g][tok];
-      const __bf16 hi = (__bf16)h;
-      const __bf16 lo = (__bf16)(h - (float)hi);
-      L.hb[g][0][tok][rk] = __builtin_bit_cast(uint16_t, hi);
-      L.hb[g][1][tok][rk] = __builtin_bit_cast(uint16_t, lo);
+      float sum[4] = {0.f, 0.f, 0.f, 0.f};
+      for (int s0 = 0; s0 < a.kslices; s0 += KS) {
+        u32x4_t pv[KS];
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+          if (s0 + s < a.kslices) pv[s] = ld16(src + (size_t)(s0 + s) * kBTok * r_pad);
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+          if (s0 + s < a.kslices)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) sum[c] += __uint_as_float(pv[s][c]);
+      }
+      const float wgt = L.wt[base + g][tok];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const float h = sum[c] * wgt;
+        const __bf16 hi = (__bf16)h;
+        const __bf16 lo = (__bf16)(h - (float)hi);
+        L.hb[g][0][tok][rk + c] = __builtin_bit_cast(uint16_t, hi);
+        L.hb[g][1][tok][rk + c] = __builtin_bit_cast(uint16_t, lo);
+      }
     }
   };
   f32x4_t o0[8], o1[8];
@@ -280,15 +302,12 @@ __device__ void block_expand(const BlockArgs& a, BlockLds<RB>& L, const Route& r
         }
     }
   };
-  // first group: B rows and h before the y0 rows are requested, so that waiting for them does
-  // not wait for HBM; the y0 rows are needed only by the epilogue
+  // first group: B rows and h (requested behind the y0 rows)
   const int ng0 = min(BG, nU);
   stage_b(used, ng0);
   hook();
   __syncthreads();  // the weight table is complete
   group_h(0, ng0);
-  load_row_chunk<Y0F32>(yc0, y0rows, c0 + b0 * kColBlock, n);
-  load_row_chunk<Y0F32>(yc1, y0rows, c0 + b1 * kColBlock, n);
   __syncthreads();  // B rows and h of the group are in LDS
   group_mfma(ng0);
   uint32_t rem = used;
