@@ -277,7 +277,7 @@ def molora_apply(hs: HotSet, x: torch.Tensor, y0: torch.Tensor, offsets: torch.T
         y = torch.empty(N, d_out, dtype=y_dtype or y0.dtype, device=x.device)
     need = molora_apply_workspace(hs, target, N, k, path, y.dtype)
     if need and (ws is None or ws.numel() < need):
-        # zero-filled: the block path keeps control words at the start that must begin at zero
+        # a fresh workspace for this call (zero-filled, so that its contents are defined)
         ws = torch.zeros(need, dtype=torch.uint8, device=x.device)
     _check(load_library().molora_apply(
         hs.handle, target, _ptr(x, torch.bfloat16, "x"), _ptr(y0, None, "y0"), _dtype_code(y0), _ptr(y, None, "y"),

@@ -329,12 +329,25 @@ struct DispatchRoute {
   }
 };
 
+// Block and slice of workgroup b: every slice of block tb runs on XCD tb mod 8 (workgroups are
+// dispatched round robin over the XCDs; a launch has 8 * ceil(nblocks / 8) * slices of them),
+// so the expand finds the partials that the shrink wrote in the same L2.
+__device__ __forceinline__ bool block_slice_of(int b, int nblocks, int slices, int& tb, int& sl) {
+  const int q = b >> 3;
+  tb = (q / slices) * 8 + (b & 7);
+  sl = q % slices;
+  return tb < nblocks;
+}
+__host__ inline int block_grid(int nblocks, int slices) { return 8 * ((nblocks + 7) / 8) * slices; }
+
 template <int RB, bool INDIRECT>
 __global__ __launch_bounds__(kBThreads, 2) void shrink_block(BlockApplyArgs a) {
   __shared__ BlockLds<RB> L;
   const int lane = threadIdx.x & 63;
   const DispatchRoute rt{a.inv, a.perm_w, a.b.k, a.b.K, a.b.scale, a.offsets[min(lane, a.b.K)]};
-  block_shrink<RB, INDIRECT>(a.b, L, rt, blockIdx.x / a.b.kslices, blockIdx.x % a.b.kslices);
+  int tb, sl;
+  if (!block_slice_of(blockIdx.x, a.b.nblocks, a.b.kslices, tb, sl)) return;
+  block_shrink<RB, INDIRECT>(a.b, L, rt, tb, sl);
 }
 
 template <int RB, bool INDIRECT, bool Y0F32, bool YF32>
@@ -342,7 +355,9 @@ __global__ __launch_bounds__(kBThreads, 2) void expand_block(BlockApplyArgs a) {
   __shared__ BlockLds<RB> L;
   const int lane = threadIdx.x & 63;
   const DispatchRoute rt{a.inv, a.perm_w, a.b.k, a.b.K, a.b.scale, a.offsets[min(lane, a.b.K)]};
-  block_expand<RB, INDIRECT, Y0F32, YF32>(a.b, L, rt, blockIdx.x / a.b.cslices, blockIdx.x % a.b.cslices, [] {});
+  int tb, cs;
+  if (!block_slice_of(blockIdx.x, a.b.nblocks, a.b.cslices, tb, cs)) return;
+  block_expand<RB, INDIRECT, Y0F32, YF32>(a.b, L, rt, tb, cs, [] {});
 }
 
 // Several targets sharing one routing: entry blockIdx.y of the array, workgroups past that
@@ -354,19 +369,21 @@ template <int RB, bool INDIRECT>
 __global__ __launch_bounds__(kBThreads, 2) void shrink_block_multi(BlockMulti m) {
   __shared__ BlockLds<RB> L;
   const BlockApplyArgs& a = m.a[blockIdx.y];
-  if ((int)blockIdx.x >= a.b.nblocks * a.b.kslices) return;
+  int tb, sl;
+  if (!block_slice_of(blockIdx.x, a.b.nblocks, a.b.kslices, tb, sl)) return;
   const int lane = threadIdx.x & 63;
   const DispatchRoute rt{a.inv, a.perm_w, a.b.k, a.b.K, a.b.scale, a.offsets[min(lane, a.b.K)]};
-  block_shrink<RB, INDIRECT>(a.b, L, rt, blockIdx.x / a.b.kslices, blockIdx.x % a.b.kslices);
+  block_shrink<RB, INDIRECT>(a.b, L, rt, tb, sl);
 }
 template <int RB, bool INDIRECT, bool Y0F32, bool YF32>
 __global__ __launch_bounds__(kBThreads, 2) void expand_block_multi(BlockMulti m) {
   __shared__ BlockLds<RB> L;
   const BlockApplyArgs& a = m.a[blockIdx.y];
-  if ((int)blockIdx.x >= a.b.nblocks * a.b.cslices) return;
+  int tb, cs;
+  if (!block_slice_of(blockIdx.x, a.b.nblocks, a.b.cslices, tb, cs)) return;
   const int lane = threadIdx.x & 63;
   const DispatchRoute rt{a.inv, a.perm_w, a.b.k, a.b.K, a.b.scale, a.offsets[min(lane, a.b.K)]};
-  block_expand<RB, INDIRECT, Y0F32, YF32>(a.b, L, rt, blockIdx.x / a.b.cslices, blockIdx.x % a.b.cslices, [] {});
+  block_expand<RB, INDIRECT, Y0F32, YF32>(a.b, L, rt, tb, cs, [] {});
 }
 
 // The vocabulary-routed step split over the reduction and output dimensions, in two launches
@@ -1630,10 +1647,11 @@ static hipError_t launch_finish_t(const void* y0, const float* z, void* y, const
 }
 template <int RB, bool IND, bool Y0F, bool YF>
 static hipError_t launch_block_t(const BlockApplyArgs& ba, hipStream_t s) {
-  hipLaunchKernelGGL((shrink_block<RB, IND>), dim3(ba.b.nblocks * ba.b.kslices), dim3(kBThreads), 0, s, ba);
+  hipLaunchKernelGGL((shrink_block<RB, IND>), dim3(block_grid(ba.b.nblocks, ba.b.kslices)), dim3(kBThreads), 0, s, ba);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((expand_block<RB, IND, Y0F, YF>), dim3(ba.b.nblocks * ba.b.cslices), dim3(kBThreads), 0, s, ba);
+  hipLaunchKernelGGL((expand_block<RB, IND, Y0F, YF>), dim3(block_grid(ba.b.nblocks, ba.b.cslices)), dim3(kBThreads), 0, s,
+                     ba);
   return hipGetLastError();
 }
 // Split step workspace: control words of the fused launch (the header, then one flag per
@@ -1948,8 +1966,8 @@ hipError_t launch_apply_multi(const ApplyLaunch* as, int n, hipStream_t s) {
       bm.a[i].perm_w = b.perm_w;
       bm.a[i].inv = b.inv;
       off += align256(apply_ws_bytes(b.N, b.k, b.K, b.tgt.r_pad, b.tgt.d_in, b.tgt.d_out, b.y_f32, b.path));
-      gs = std::max(gs, bm.a[i].b.nblocks * bm.a[i].b.kslices);
-      ge = std::max(ge, bm.a[i].b.nblocks * bm.a[i].b.cslices);
+      gs = std::max(gs, block_grid(bm.a[i].b.nblocks, bm.a[i].b.kslices));
+      ge = std::max(ge, block_grid(bm.a[i].b.nblocks, bm.a[i].b.cslices));
     }
     const int RBv = a0.tgt.r_pad / 16;
     MOLORA_DISPATCH_RB(RBv, MOLORA_DISPATCH_BOOL(a0.indirect, IND,

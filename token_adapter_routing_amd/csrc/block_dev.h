@@ -11,9 +11,9 @@
 // slice (A: 16 KB, B: 16 KB per adapter at rank 16) are read once per workgroup, straight into
 // LDS, and shared by the four row-block waves, so the per-CU load volume is dominated by the x
 // and y0 streams (an 8-token tile reads every adapter's whole A and B: twice its own stream).
-// Workgroup b takes block b / slices and slice b % slices: with 8 slices, slice s always runs
-// on XCD s (workgroups are dispatched round robin over the 8 XCDs), so each XCD's L2 holds one
-// slice of each adapter.
+// Every slice of block tb runs on XCD tb mod 8 (workgroups are dispatched round robin over the
+// 8 XCDs; the kernels map workgroup ids accordingly), so the expand finds the partials that the
+// shrink wrote in the same L2.
 //
 // MFMA layouts (v_mfma_f32_16x16x32_bf16): the shrink uses the swizzled A pieces with rows =
 // 16 tokens; the expand uses h as a bf16 hi/lo pair stacked along k and the slab's permuted
