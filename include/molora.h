@@ -281,8 +281,10 @@ int molora_apply_multi(const molora_hotset *hs, int n, const int *targets,
  *                 flags) used when the environment sets MOLORA_SPLIT_FUSED=1,
  *                 which runs the split step as one launch (each workgroup
  *                 publishes its slice's partials and waits, bounded, for its
- *                 block's others, else computes them itself); then the fp32
- *                 partial sums [ceil(N/64)][ceil(d_in/512)][64][r_pad]
+ *                 block's others, else computes them itself; MOLORA_SPLIT_SPIN
+ *                 sets the bound in polls, default 20000, negative forces the
+ *                 local computation); then the fp32 partial sums
+ *                 [ceil(N/64)][ceil(d_in/512)][64][r_pad]
  * ------------------------------------------------------------------------ */
 int molora_step_workspace(const molora_hotset *hs, int target, int N, size_t *bytes);
 int molora_step_vocab(const molora_hotset *hs, int target, const int32_t *ids, int N,
