@@ -85,7 +85,7 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run plain device copies of known size (for HBM counter scaling)")
-    p.add_argument("--rows", default="C0,C2,C3,C4,C4stack",
+    p.add_argument("--rows", default="C0,C2,C3,C4,C4stack,paging",
                    help="other configurations to measure beside the headline (comma list, or 'none')")
     p.add_argument("--row-reps", type=int, default=100, help="graph replays per timed row entry")
     p.add_argument("--stack-replays", type=int, default=1000, help="single-graph replays of the 28-layer stack row")
@@ -361,7 +361,78 @@ def measure_rows(m, torch, dev, rows, reps, stack_replays=1000):
         res["C4_stress"] = row_stress(m, torch, dev, bf, f32, max(20, reps // 4))
     if "C4stack" in rows:
         res["C4_stack"] = row_stack(m, torch, dev, replays=stack_replays)
+    if "paging" in rows:
+        res["C1_paging"] = row_paging(m, torch, dev, bf, i32, max(200, reps * 2))
     torch.cuda.synchronize()
+    return res
+
+
+def row_paging(m, torch, dev, bf, i32, steps):
+    """Hot set against on-demand paging on the 4-modality workload (the pages' Table 4 runs the
+    Table 3 configuration; Figures 7 and 8 compare latencies).  Paging step: every adapter the
+    batch uses is copied from pinned host memory into a device staging buffer, written into its
+    slot with molora_hotset_load, then the split step runs; launched eagerly, as paging rules out
+    a captured graph.  Hot-set steps: the split step alone, eager and as a single-step graph.
+    Each step is timed on its own with HIP events on the launch stream."""
+    import statistics
+    import synth
+    c = synth.modality4()
+    t = c.targets[0]
+    N, K, r = c.N, c.K, c.r
+    hs = m.molora_hotset_init([(bf(t.A), bf(t.B))], c.scale)
+    ids, x, y0 = i32(c.ids), bf(t.x), bf(t.y0)
+    y = torch.empty(N, t.d_out, dtype=torch.bfloat16, device=dev)
+    route = (torch.empty(N, dtype=torch.int32, device=dev), torch.empty(N, dtype=torch.float32, device=dev))
+    meta = (torch.empty(K, dtype=torch.int32, device=dev), torch.empty(K + 1, dtype=torch.int32, device=dev),
+            torch.empty(N, dtype=torch.int32, device=dev), torch.empty(N, dtype=torch.float32, device=dev),
+            torch.empty(N, dtype=torch.int32, device=dev))
+    ws = torch.zeros(m.molora_step_workspace(hs, 0, N), dtype=torch.uint8, device=dev)
+    hostA = torch.from_numpy(t.A.view(np.int16)).view(torch.bfloat16).pin_memory()
+    hostB = torch.from_numpy(t.B.view(np.int16)).view(torch.bfloat16).pin_memory()
+    stA, stB = torch.empty_like(hostA, device=dev), torch.empty_like(hostB, device=dev)
+    # adapters the batch uses, decided on the host from its token ids before the timed steps
+    used = sorted(set(int(e) for e in np.searchsorted(c.bounds, c.ids, side="right") - 1 if 0 <= e < K))
+    bounds = c.bounds.tolist()
+    stream = torch.cuda.Stream()
+
+    def step():
+        m.molora_step_vocab(hs, ids, bounds, x, y0, y=y, route=route, meta=meta, ws=ws, stream=stream)
+
+    def paged():
+        for e in used:
+            stA[e].copy_(hostA[e], non_blocking=True)
+            stB[e].copy_(hostB[e], non_blocking=True)
+        for e in used:
+            m.molora_hotset_load(hs, 0, e, stA[e], stB[e], stream=stream)
+        step()
+
+    def timed(fn, n):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        with torch.cuda.stream(stream):
+            for _ in range(10):
+                fn()
+            torch.cuda.synchronize()
+            for a, b in evs:
+                a.record(stream)
+                fn()
+                b.record(stream)
+        torch.cuda.synchronize()
+        lat = sorted(a.elapsed_time(b) * 1e3 for a, b in evs)
+        return {"p50_us": lat[len(lat) // 2], "p99_us": lat[min(len(lat) - 1, int(0.99 * len(lat)))],
+                "mean_us": statistics.mean(lat), "cv": statistics.pstdev(lat) / statistics.mean(lat), "steps": n}
+
+    res = {"workload": "4-modality vocab routing N=2048 d=4096 K=4 r=16 k=1",
+           "adapters_paged_per_step": len(used), "host_to_device_bytes_per_step": len(used) * (hostA[0].numel() +
+                                                                                               hostB[0].numel()) * 2,
+           "paging_eager": timed(paged, steps), "hot_set_eager": timed(step, steps)}
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        step()
+    res["hot_set_graph"] = timed(g.replay, steps)
+    res["paging_over_hot_set_eager_p50"] = res["paging_eager"]["p50_us"] / res["hot_set_eager"]["p50_us"]
+    res["paging_over_hot_set_graph_p50"] = res["paging_eager"]["p50_us"] / res["hot_set_graph"]["p50_us"]
+    res["paging_over_hot_set_graph_p99"] = res["paging_eager"]["p99_us"] / res["hot_set_graph"]["p99_us"]
+    del g, hs
     return res
 
 

@@ -111,6 +111,24 @@ int molora_hotset_init(molora_hotset **out, int K, int r, float scale, int n_tar
                        const molora_target *targets, int layout, void *slab,
                        size_t slab_bytes, void *stream);
 
+/* Page one adapter into its hot-set slot (thelatestinai.com, Figure 4 and
+ * Table 4: the paging baseline copies adapters from host memory on demand,
+ * the hot set keeps them resident at fixed addresses; Figures 7 and 8 compare
+ * the two under different access patterns).  Writes adapter e of target
+ * `target` into the slot molora_hotset_init gave it, in the same internal
+ * layout and bit for bit what init writes for the same weights; the slot's
+ * address does not change, so graphs captured over molora_apply stay valid.
+ *   A  device bf16 [d_in][r]  row-major (adapter e's A; read by the kernels)
+ *   B  device bf16 [r][d_out] row-major (adapter e's B; read by the kernels)
+ * Asynchronous: enqueues two copy kernels on `stream` and returns; A and B
+ * must stay valid until they have run.  Nothing is synchronised, so the call
+ * may be captured in a graph.  Kernels on other streams that read adapter e
+ * while the load runs race with it: order them through `stream`.
+ * Errors (nothing enqueued): NULL hs, A or B, target or e out of range, or a
+ * pointer not 2-byte aligned -> MOLORA_EINVAL; a launch failure -> MOLORA_EHIP. */
+int molora_hotset_load(molora_hotset *hs, int target, int e, const void *A, const void *B,
+                       void *stream);
+
 /* Free the descriptor (not the slab).  NULL is accepted. */
 int molora_hotset_destroy(molora_hotset *hs);
 

@@ -28,7 +28,7 @@ def lib():
 def test_every_declared_symbol_is_exported_and_bound():
     L = lib()
     names = declared_functions()
-    assert len(names) == 15, names
+    assert len(names) == 16, names
     for n in names:
         assert hasattr(L, n), n
     assert sorted(m.exported_symbols()) == names
@@ -91,6 +91,8 @@ def test_host_validation_without_launch():
     assert L.molora_hotset_init(ctypes.byref(h), 4, 16, 2.0, 1, tg, 0, ctypes.c_void_p(16), 1 << 20, nul) == 1
     assert L.molora_hotset_init(ctypes.byref(h), 4, 16, 2.0, 1, tg, 0, ctypes.c_void_p(256), 16, nul) == 3
     assert L.molora_hotset_destroy(nul) == 0
+    # hotset_load: NULL hot set is rejected before any launch
+    assert L.molora_hotset_load(nul, 0, 0, ctypes.c_void_p(256), ctypes.c_void_p(256), nul) == 1
     assert L.molora_seqpass_meta(nul, 0, 4, nul, nul, nul, nul) == 0
 
 

@@ -9,6 +9,6 @@ from .binding import (  # noqa: F401
     HotSet, MoloraError, exported_symbols, load_library, LIB_PATH,
     molora_apply, molora_apply_multi, molora_apply_multi_workspace, molora_apply_workspace, molora_dispatch,
     molora_dispatch_workspace,
-    molora_hotset_bytes, molora_hotset_destroy, molora_hotset_init, molora_route_topk,
+    molora_hotset_bytes, molora_hotset_destroy, molora_hotset_init, molora_hotset_load, molora_route_topk,
     molora_route_vocab, molora_seqpass_meta, molora_step_vocab, molora_step_workspace,
 )

@@ -42,6 +42,7 @@ _SIGS = {
     "molora_hotset_bytes": (_c_i, [_c_i, _c_i, _c_i, ctypes.POINTER(MoloraTarget), _c_i, ctypes.POINTER(_c_sz)]),
     "molora_hotset_init": (_c_i, [ctypes.POINTER(_c_p), _c_i, _c_i, _c_f, _c_i, ctypes.POINTER(MoloraTarget), _c_i,
                                   _c_p, _c_sz, _c_p]),
+    "molora_hotset_load": (_c_i, [_c_p, _c_i, _c_i, _c_p, _c_p, _c_p]),
     "molora_hotset_destroy": (_c_i, [_c_p]),
     "molora_route_vocab": (_c_i, [_c_p, _c_i, _c_p, _c_i, _c_p, _c_p, _c_p]),
     "molora_route_topk": (_c_i, [_c_p, _c_i, _c_i, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i, _c_i, _c_p, _c_p, _c_p, _c_p]),
@@ -175,6 +176,16 @@ def molora_hotset_init(targets, scale: float, layout: int = LAYOUT_DIRECT, slab:
     _check(lib.molora_hotset_init(ctypes.byref(h), int(K), int(r), float(scale), len(dims), arr, layout,
                                   _ptr(slab, torch.uint8, "slab"), slab.numel(), _stream(stream)))
     return HotSet(h.value, slab, int(K), int(r), float(scale), dims, layout)
+
+
+def molora_hotset_load(hs: HotSet, target: int, e: int, A: torch.Tensor, B: torch.Tensor, stream=None):
+    """Write adapter e of `target` into its slot: A bf16 [d_in][r], B bf16 [r][d_out], device tensors.
+    Only enqueues on `stream`; A and B must stay alive until the copy kernels have run."""
+    d_in, d_out = hs.dims[target] if 0 <= target < len(hs.dims) else (None, None)
+    if d_in is not None and (tuple(A.shape) != (d_in, hs.r) or tuple(B.shape) != (hs.r, d_out)):
+        raise ValueError(f"A must be [{d_in}][{hs.r}] and B [{hs.r}][{d_out}]")
+    _check(load_library().molora_hotset_load(hs.handle, int(target), int(e), _ptr(A, torch.bfloat16, "A"),
+                                             _ptr(B, torch.bfloat16, "B"), _stream(stream)))
 
 
 def molora_hotset_destroy(hs: HotSet):

@@ -19,6 +19,8 @@ struct molora_hotset {
   std::vector<molora::TargetDev> tg;
   void* slab = nullptr;
   size_t slab_bytes = 0;
+  // host copies of every adapter's slot addresses, [target][adapter] (both layouts)
+  std::vector<std::vector<uint16_t*>> slotA, slotB;
 };
 
 namespace {
@@ -187,6 +189,12 @@ int molora_hotset_init(molora_hotset** out, int K, int r, float scale, int n_tar
       }
     }
     hs->tg.push_back(d);
+    hs->slotA.emplace_back();
+    hs->slotB.emplace_back();
+    for (int e = 0; e < K; ++e) {
+      hs->slotA.back().push_back(const_cast<uint16_t*>(static_cast<const uint16_t*>(tablesA[t][e])));
+      hs->slotB.back().push_back(const_cast<uint16_t*>(static_cast<const uint16_t*>(tablesB[t][e])));
+    }
   }
   const hipError_t err = hipStreamSynchronize(s);  // host tables above must outlive the copies
   if (err != hipSuccess) {
@@ -195,6 +203,21 @@ int molora_hotset_init(molora_hotset** out, int K, int r, float scale, int n_tar
   }
   *out = hs;
   return ok();
+}
+
+int molora_hotset_load(molora_hotset* hs, int target, int e, const void* A, const void* B, void* stream) {
+  if (hs == nullptr) return fail(MOLORA_EINVAL, "hs is NULL");
+  if (target < 0 || target >= hs->n_targets)
+    return fail(MOLORA_EINVAL, "target %d outside [0, %d)", target, hs->n_targets);
+  if (e < 0 || e >= hs->K) return fail(MOLORA_EINVAL, "adapter %d outside [0, %d)", e, hs->K);
+  if (A == nullptr || B == nullptr) return fail(MOLORA_EINVAL, "A or B is NULL");
+  if (!aligned(A, 2) || !aligned(B, 2)) return fail(MOLORA_EINVAL, "misaligned pointer");
+  const molora::TargetDev& d = hs->tg[target];
+  const hipError_t err =
+      molora::launch_relayout(static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(B), d.d_in, d.d_out,
+                              hs->r, hs->r_pad, hs->slotA[target][e], hs->slotB[target][e],
+                              reinterpret_cast<hipStream_t>(stream));
+  return err == hipSuccess ? ok() : hip_fail(err, "hot-set load");
 }
 
 int molora_hotset_destroy(molora_hotset* hs) {
