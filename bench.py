@@ -432,7 +432,63 @@ def row_paging(m, torch, dev, bf, i32, steps):
     res["paging_over_hot_set_eager_p50"] = res["paging_eager"]["p50_us"] / res["hot_set_eager"]["p50_us"]
     res["paging_over_hot_set_graph_p50"] = res["paging_eager"]["p50_us"] / res["hot_set_graph"]["p50_us"]
     res["paging_over_hot_set_graph_p99"] = res["paging_eager"]["p99_us"] / res["hot_set_graph"]["p99_us"]
-    del g, hs
+    del g
+    res["access_patterns"] = paging_patterns(m, torch, dev, hs, c, step, timed, stream, steps)
+    del hs
+    return res
+
+
+def paging_patterns(m, torch, dev, hs, c, step, timed, stream, steps, L=16, burst=8):
+    """Paging under access patterns (the pages' Figure 8): L logical adapters live in pinned host
+    memory behind the hot set's K slots, one slot per modality of the batch (a direct-mapped cache:
+    slot s keeps the adapter modality s used last); each step's batch (the 4-modality ids) needs
+    K of them.  bursty: the same K for `burst` steps, then K others; uniform: K distinct adapters
+    drawn at random each step; adversarial: the K slots cycle through all L adapters, so every
+    access misses.  A miss pages the adapter into its slot (2 copies + molora_hotset_load)."""
+    import synth
+    t = c.targets[0]
+    K = c.K
+    A, B = synth._lora_weights(16, 0, L, t.d_in, t.d_out, c.r)
+    hostA = torch.from_numpy(A.view(np.int16)).view(torch.bfloat16).pin_memory()
+    hostB = torch.from_numpy(B.view(np.int16)).view(torch.bfloat16).pin_memory()
+    stA = torch.empty(K, t.d_in, c.r, dtype=torch.bfloat16, device=dev)
+    stB = torch.empty(K, c.r, t.d_out, dtype=torch.bfloat16, device=dev)
+    g = np.random.default_rng(np.random.SeedSequence([20260316, 1, 99]))
+    n = steps + 10
+
+    def sets(kind):
+        if kind == "bursty":
+            out = []
+            for i in range(n):
+                if i % burst == 0:
+                    cur = [int(v) for v in g.choice(L, K, replace=False)]
+                out.append(cur)
+            return out
+        if kind == "uniform":
+            return [[int(v) for v in g.choice(L, K, replace=False)] for _ in range(n)]
+        return [[(K * i + j) % L for j in range(K)] for i in range(n)]  # adversarial: cycles all L
+
+    res = {"logical_adapters": L, "slots": K}
+    for kind in ("bursty", "uniform", "adversarial"):
+        seq = sets(kind)
+        resident = [-1] * K  # logical adapter held by each slot (slot = modality of the batch)
+        misses = [0]
+        it = iter(seq)
+
+        def paged():
+            need = next(it)
+            for s_, a in enumerate(need):
+                if resident[s_] != a:
+                    stA[s_].copy_(hostA[a], non_blocking=True)
+                    stB[s_].copy_(hostB[a], non_blocking=True)
+                    m.molora_hotset_load(hs, 0, s_, stA[s_], stB[s_], stream=stream)
+                    resident[s_] = a
+                    misses[0] += 1
+            step()
+
+        r_ = timed(paged, steps)
+        r_["page_ins_per_step"] = misses[0] / len(seq)
+        res[kind] = r_
     return res
 
 
