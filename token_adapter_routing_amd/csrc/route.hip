@@ -6,7 +6,9 @@
 //   route_vocab_k   one thread per token: binary search of the id in the K+1 range bounds (LDS).
 //   route_topk_k    a workgroup owns 16 tokens.  Router mode: the first layer x W1^T (d -> 64)
 //                   is an MFMA product with the same gather/shrink core as the LoRA shrink,
-//                   the 4 waves splitting d and meeting in LDS; bias and ReLU follow in LDS;
+//                   8 waves splitting d (every workgroup reads all of W1, so more loads in
+//                   flight per CU is what shortens it) and meeting in LDS; bias and ReLU
+//                   follow in LDS;
 //                   the second layer (64 -> K) runs on the VALU with one lane per adapter.
 //                   Selection: one wave per token holds the K logits in its lanes; k rounds of
 //                   (wave max, ballot of lanes equal to it, lowest lane wins) pick the top-k
@@ -83,11 +85,18 @@ struct TopkArgs {
   uint8_t* flags;
 };
 
+// Waves per workgroup: 8 with the router MLP (splitting d), 4 with given logits.
 template <bool ROUTER>
-__global__ __launch_bounds__(256) void route_topk_k(TopkArgs a) {
+struct TopkWaves {
+  static constexpr int NW = ROUTER ? 8 : 4;
+};
+
+template <bool ROUTER>
+__global__ __launch_bounds__(TopkWaves<ROUTER>::NW * 64) void route_topk_k(TopkArgs a) {
+  constexpr int NW = TopkWaves<ROUTER>::NW;
   constexpr int RB = 4;  // 64 hidden units = 4 blocks of 16
-  constexpr int RS = RedLds<RB>::RS;
-  __shared__ float red[ROUTER ? RedLds<RB>::kFloats : 1];
+  constexpr int RS = RedLds<RB, NW>::RS;
+  __shared__ float red[ROUTER ? RedLds<RB, NW>::kFloats : 1];
   __shared__ float hid[ROUTER ? 16 * 64 : 1];
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int t0 = blockIdx.x * 16;
@@ -98,21 +107,23 @@ __global__ __launch_bounds__(256) void route_topk_k(TopkArgs a) {
 #pragma unroll
     for (int u = 0; u < RB; ++u) acc[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     const int S = a.d / kStepK;
-    shrink_steps_batched<RB, false>(acc, a.x + (size_t)tok * a.d, a.W1, a.d, (S * wave) / 4, (S * (wave + 1)) / 4, lane);
-    shrink_to_lds<RB>(acc, red, wave, lane);
+    shrink_steps_batched<RB, false>(acc, a.x + (size_t)tok * a.d, a.W1, a.d, (S * wave) / NW, (S * (wave + 1)) / NW,
+                                    lane);
+    shrink_to_lds<RB, NW>(acc, red, wave, lane);
     __syncthreads();
-    for (int i = threadIdx.x; i < 16 * 64; i += 256) {
+    for (int i = threadIdx.x; i < 16 * 64; i += NW * 64) {
       const int row = i >> 6, j = i & 63;
       float v = 0.f;
 #pragma unroll
-      for (int w = 0; w < 4; ++w) v += red[(w * 16 + row) * RS + j];
+      for (int w = 0; w < NW; ++w) v += red[(w * 16 + row) * RS + j];
       if (a.b1 != nullptr) v += a.b1[j];
       hid[i] = v > 0.f ? v : 0.f;
     }
     __syncthreads();
   }
-  for (int r = 0; r < 4; ++r) {
-    const int row = wave * 4 + r;
+  constexpr int RPW = 16 / NW;  // tokens per wave in the selection
+  for (int r = 0; r < RPW; ++r) {
+    const int row = wave * RPW + r;
     const int tok = t0 + row;
     if (tok >= a.N) break;  // uniform per wave
     float l = -INFINITY;
@@ -139,8 +150,8 @@ hipError_t launch_route_topk(const uint16_t* x, int N, int d, const uint16_t* W1
                              float* w, uint8_t* flags, hipStream_t s) {
   TopkArgs a{x, N, d, W1, b1, W2, b2, logits, K, k, idx, w, flags};
   const dim3 grid((N + 15) / 16);
-  if (W1 != nullptr) hipLaunchKernelGGL(route_topk_k<true>, grid, dim3(256), 0, s, a);
-  else hipLaunchKernelGGL(route_topk_k<false>, grid, dim3(256), 0, s, a);
+  if (W1 != nullptr) hipLaunchKernelGGL(route_topk_k<true>, grid, dim3(TopkWaves<true>::NW * 64), 0, s, a);
+  else hipLaunchKernelGGL(route_topk_k<false>, grid, dim3(TopkWaves<false>::NW * 64), 0, s, a);
   return hipGetLastError();
 }
 
