@@ -272,37 +272,38 @@ int molora_apply_multi(const molora_hotset *hs, int n, const int *targets,
                        void *ws, size_t ws_bytes, void *stream);
 
 /* ------------------------------------------------------------------------
- * The whole vocabulary-routed step in one launch (thelatestinai.com, Table 1:
- * routing decision, histogram, pointer arrays and grouped dispatch; Figure 2:
- * per-token weighted sum; Table 4 "Per-token + Graph": the step as few
+ * The whole vocabulary-routed step (thelatestinai.com, Table 1: routing
+ * decision, histogram, pointer arrays and grouped dispatch; Figure 2:
+ * per-token weighted sum; Table 4 "Per-token + Graph": the step in as few
  * launches as possible).  Equivalent to molora_route_vocab, molora_dispatch
  * and molora_apply with k = 1, producing bit-identical idx, w, counts,
- * offsets, perm, perm_w, inv and y.  With a workspace of
- * molora_step_workspace() bytes the step is two launches over 512-wide
- * slices: the first routes 64-token blocks, writes each token's partial
- * x A_e per d_in slice (its own adapter only) and the dispatch outputs, the
- * second sums the partials in slice order and writes y per output slice; y
- * equals MOLORA_PATH_BLOCK's bit for bit.  Without one (ws NULL) the step is
- * one launch of MOLORA_PATH_TILE.  Every workgroup routes its own tokens from
- * their ids and derives its share of the dispatch outputs by counting all N
- * ids.  Batches above 4096 tokens run route, dispatch and apply as separate
- * launches.
+ * offsets, perm, perm_w and inv, and y as below.
+ *   With a workspace (ws != NULL): two launches over 512-wide slices; the
+ *   first routes 64-token blocks from their ids and writes each token's
+ *   partial x A_e per d_in slice (its own adapter only), the second sums the
+ *   partials in slice order and writes y per output slice; y equals
+ *   MOLORA_PATH_BLOCK's bit for bit.  Up to 4096 tokens these two launches
+ *   also write the dispatch outputs (no other launch); above that, route and
+ *   a chip-wide dispatch run first as launches of their own.
+ *   Without a workspace (ws == NULL): up to 4096 tokens one launch of the
+ *   8-token tile apply (MOLORA_PATH_TILE's arithmetic) that also routes and
+ *   writes the dispatch outputs; above that route, a one-workgroup dispatch
+ *   and the tile apply as three launches.
  *   hs, target    hot set with K = hs->K adapters (K <= 16) and the projection
  *   ids, bounds   as molora_route_vocab (bounds: host int32 [K+1])
  *   x, y0, y      as molora_apply (y0 may equal y)
  *   idx, w        device [N] out, as molora_route_vocab
  *   counts..inv   device out, as molora_dispatch with k = 1 (inv required)
- *   ws            NULL, or device workspace of molora_step_workspace() bytes,
- *                 256-byte aligned, owned by the caller, zero-filled before its
- *                 first use with a given N and left alone between calls: it
- *                 starts with control words (an epoch and per-(block, slice)
- *                 flags) used when the environment sets MOLORA_SPLIT_FUSED=1,
- *                 which runs the split step as one launch (each workgroup
- *                 publishes its slice's partials and waits, bounded, for its
- *                 block's others, else computes them itself; MOLORA_SPLIT_SPIN
- *                 sets the bound in polls, default 20000, negative forces the
- *                 local computation); then the fp32 partial sums
- *                 [ceil(N/64)][ceil(d_in/512)][64][r_pad]
+ *   ws            NULL, or a device workspace of at least
+ *                 molora_step_workspace() bytes for the same hot set, target
+ *                 and N, 256-byte aligned, owned by the caller (no initial
+ *                 contents needed): the chip-wide dispatch's counts (above
+ *                 4096 tokens), then the fp32 partial sums
+ *                 [ceil(N/64)][ceil(d_in/512)][64][r_pad].  Calls that share
+ *                 a workspace must not run concurrently.
+ * Errors: K > 16 -> MOLORA_ENOTSUP; a workspace smaller than required or
+ * misaligned -> MOLORA_ENOSPC; NULL or misaligned buffers -> MOLORA_EINVAL;
+ * nothing is enqueued on any error.
  * ------------------------------------------------------------------------ */
 int molora_step_workspace(const molora_hotset *hs, int target, int N, size_t *bytes);
 int molora_step_vocab(const molora_hotset *hs, int target, const int32_t *ids, int N,

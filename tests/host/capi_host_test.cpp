@@ -1,0 +1,469 @@
+// CPU test of the C ABI's host layer, built with AddressSanitizer and UndefinedBehaviorSanitizer.
+//
+// capi.cpp and plan.cpp are compiled as shipped.  The kernel launchers and the three HIP runtime
+// calls that capi.cpp makes are replaced by stand-ins that launch nothing; instead each stand-in
+// performs, on host memory, every workspace and slab write the replaced kernels make (from the
+// same index helpers the kernels use), so a workspace or slab that the *_workspace / *_bytes
+// queries size too small, or a plan whose regions overlap, shows up as a sanitizer error or a
+// failed check.  "Device" buffers are host allocations of exactly the queried size.
+#include <algorithm>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+#include <utility>
+#include <vector>
+
+#include "molora.h"
+#include "molora_launch.h"
+
+using namespace molora;
+
+static int g_fail = 0;
+static int g_checks = 0;
+#define CHECK(c, ...)                                             \
+  do {                                                            \
+    ++g_checks;                                                   \
+    if (!(c)) {                                                   \
+      ++g_fail;                                                   \
+      fprintf(stderr, "FAIL %s:%d: ", __FILE__, __LINE__);        \
+      fprintf(stderr, __VA_ARGS__);                               \
+      fprintf(stderr, " [%s]\n", molora_last_error());            \
+    }                                                             \
+  } while (0)
+
+// ------------------------------------------------------------------ write recording
+// Byte ranges written into the current workspace by the stand-in kernels of one call, with the
+// name of the array they belong to; ranges of different arrays must not overlap.
+struct Range {
+  size_t lo, hi;
+  std::string what;
+};
+static std::vector<Range> g_ranges;
+static char* g_ws_base = nullptr;
+static size_t g_ws_bytes = 0;
+
+// Write `count` elements of T at base[first ..] (every element: the sanitizer checks each).
+template <typename T>
+static void write_span(void* base, size_t first, size_t count, const char* what) {
+  if (count == 0) return;
+  T* p = static_cast<T*>(base);
+  for (size_t i = 0; i < count; ++i) p[first + i] = T(1);
+  char* lo = reinterpret_cast<char*>(p + first);
+  if (g_ws_base != nullptr && lo >= g_ws_base && lo < g_ws_base + g_ws_bytes + 1)
+    g_ranges.push_back({(size_t)(lo - g_ws_base), (size_t)(lo - g_ws_base) + count * sizeof(T), what});
+}
+
+static void check_disjoint(const char* call) {
+  std::vector<Range> r = g_ranges;
+  std::sort(r.begin(), r.end(), [](const Range& a, const Range& b) { return a.lo < b.lo; });
+  for (size_t i = 1; i < r.size(); ++i)
+    CHECK(r[i].lo >= r[i - 1].hi || r[i].what == r[i - 1].what, "%s: %s [%zu, %zu) overlaps %s [%zu, %zu)", call,
+          r[i].what.c_str(), r[i].lo, r[i].hi, r[i - 1].what.c_str(), r[i - 1].lo, r[i - 1].hi);
+  for (const Range& x : r) CHECK(x.hi <= g_ws_bytes, "%s: %s ends at %zu > %zu", call, x.what.c_str(), x.hi, g_ws_bytes);
+}
+
+// ------------------------------------------------------------------ stand-in kernels
+static int g_launches = 0;
+static int g_last_apply_path = -1;
+
+static void rank_sort_writes(char* region, long long P, int k, int K) {
+  const RankSortPlan rp = rank_sort_plan(P, k, K);
+  write_span<int32_t>(region + rp.counts2_off, 0, (size_t)k * K, "counts2");
+  write_span<int32_t>(region + rp.offsets2_off, 0, (size_t)k * K + 1, "offsets2");
+  write_span<int32_t>(region + rp.perm2_off, 0, (size_t)P, "perm2");
+  write_span<float>(region + rp.w2_off, 0, (size_t)P, "w2");
+  const DispatchSplit ds = dispatch_split(P);
+  if (ds.nb > 1) write_span<int32_t>(region + rp.bcnt_off, 0, (size_t)ds.nb * k * K, "rank bcnt");
+}
+
+static void block_writes(const ApplyLaunch& a, char* base) {
+  const BlockGeom g = block_geom(a.N, a.k, a.K, a.tgt.d_in, a.tgt.d_out);
+  for (int tb = 0; tb < g.nblocks; ++tb)
+    for (int slot = 0; slot < g.slotmax; ++slot)
+      for (int sl = 0; sl < g.kslices; ++sl)
+        write_span<float>(base, block_part_index(tb, slot, sl, g.slotmax, g.kslices, a.tgt.r_pad),
+                          (size_t)kBTok * a.tgt.r_pad, "block partials");
+}
+
+// What launch_apply's kernels write into a.ws for a's resolved path (apply.hip, launch_apply).
+static void apply_writes(const ApplyLaunch& a) {
+  const ApplyPlan p = apply_plan(a.N, a.k, a.K, a.tgt.r_pad, a.tgt.d_in, a.tgt.d_out, a.y_f32, a.path);
+  CHECK(p.path == a.path, "resolved path %d vs plan %d", a.path, p.path);
+  char* ws = reinterpret_cast<char*>(a.ws);
+  const long long P = (long long)a.N * a.k;
+  if (p.total > 0) CHECK(ws != nullptr, "path %d needs a workspace of %zu bytes", a.path, p.total);
+  if (ws == nullptr) return;
+  if (a.path == kPathBlock) {
+    block_writes(a, ws + p.block_off);
+    return;
+  }
+  if (a.path == kPathTile || (a.path == kPathGrouped && a.k == 1)) return;  // no workspace
+  if (a.path == kPathGrouped && use_gm(a.k, a.K, a.tgt.r_pad)) {
+    rank_sort_writes(ws + p.sort_off, P, a.k, a.K);
+    if (!a.y_f32) write_span<float>(ws + p.z_off, 0, (size_t)a.N * a.tgt.d_out, "z");
+    return;
+  }
+  const int ns = a.path == kPathSkinny ? skinny_splits(a.tgt.d_in) : 1;
+  write_span<float>(ws + p.hpart_off, 0, (size_t)ns * P * a.tgt.r_pad, "hpart");
+  if (a.path == kPathSkinny && a.k > 1 && a.k * a.K <= 64) {
+    rank_sort_writes(ws + p.sort_off, P, a.k, a.K);
+    if (!a.y_f32) write_span<float>(ws + p.z_off, 0, (size_t)a.N * a.tgt.d_out, "z");
+  }
+}
+
+namespace molora {
+
+hipError_t launch_route_vocab(const int32_t*, int, const VocabBounds&, int, int32_t*, float*, hipStream_t) {
+  ++g_launches;
+  return hipSuccess;
+}
+hipError_t launch_route_topk(const uint16_t*, int, int, const uint16_t*, const float*, const uint16_t*, const float*,
+                             float*, int, int, int32_t*, float*, uint8_t*, hipStream_t) {
+  ++g_launches;
+  return hipSuccess;
+}
+hipError_t launch_dispatch(const int32_t*, const float*, int P, int K, int32_t*, int32_t*, int32_t*, float*, int32_t*,
+                           void* ws, hipStream_t) {
+  ++g_launches;
+  const DispatchSplit d = dispatch_split(P);
+  if (d.nb > 1 && ws != nullptr) write_span<int32_t>(ws, 0, (size_t)d.nb * K, "dispatch bcnt");
+  return hipSuccess;
+}
+hipError_t launch_relayout(const uint16_t*, const uint16_t*, int d_in, int d_out, int, int r_pad, uint16_t* At,
+                           uint16_t* Bt, hipStream_t) {
+  ++g_launches;
+  write_span<uint16_t>(At, 0, (size_t)r_pad * d_in, "A slot");
+  write_span<uint16_t>(Bt, 0, (size_t)d_out * r_pad, "B slot");
+  return hipSuccess;
+}
+hipError_t launch_apply(const ApplyLaunch& a, hipStream_t) {
+  ++g_launches;
+  g_last_apply_path = a.path;
+  apply_writes(a);
+  return hipSuccess;
+}
+hipError_t launch_apply_multi(const ApplyLaunch* as, int n, hipStream_t) {
+  ++g_launches;
+  const ApplyLaunch& a0 = as[0];
+  g_last_apply_path = a0.path;
+  int d_in[kApplyMaxMulti], d_out[kApplyMaxMulti];
+  for (int i = 0; i < n; ++i) {
+    d_in[i] = as[i].tgt.d_in;
+    d_out[i] = as[i].tgt.d_out;
+  }
+  const MultiPlan mp = apply_multi_plan(n, d_in, d_out, a0.N, a0.k, a0.K, a0.tgt.r_pad, a0.y_f32, a0.path);
+  char* ws = reinterpret_cast<char*>(a0.ws);
+  if (mp.total > 0) CHECK(ws != nullptr, "multi needs %zu bytes", mp.total);
+  if (ws == nullptr) return hipSuccess;
+  if (!mp.fused) {
+    for (int i = 0; i < n; ++i) {
+      ApplyLaunch b = as[i];
+      b.ws = reinterpret_cast<float*>(ws + mp.tgt_off[i]);
+      apply_writes(b);
+    }
+    return hipSuccess;
+  }
+  const long long P = (long long)a0.N * a0.k;
+  if (a0.k > 1) rank_sort_writes(ws + mp.sort_off, P, a0.k, a0.K);
+  for (int i = 0; i < n; ++i) {
+    write_span<float>(ws + mp.hpart_off[i], 0, (size_t)skinny_splits(d_in[i]) * P * a0.tgt.r_pad, "hpart (multi)");
+    if (a0.k > 1 && !a0.y_f32) write_span<float>(ws + mp.z_off[i], 0, (size_t)a0.N * d_out[i], "z (multi)");
+  }
+  return hipSuccess;
+}
+hipError_t launch_step_vocab(const StepVocabLaunch& a, hipStream_t) {
+  ++g_launches;
+  CHECK(a.apply.N <= kStepMaxN || !a.dispatch_share, "fused dispatch share above %d tokens (N=%d)", kStepMaxN,
+        a.apply.N);
+  if (a.ws == nullptr) return hipSuccess;  // the one-launch tile step writes no workspace
+  const int nblocks = (a.apply.N + kSTok - 1) / kSTok;
+  const int kslices = (a.apply.tgt.d_in + kSSlice - 1) / kSSlice;
+  for (int tb = 0; tb < nblocks; ++tb)
+    for (int sl = 0; sl < kslices; ++sl)
+      write_span<float>(a.ws, split_part_index(tb, sl, kslices, a.apply.tgt.r_pad), (size_t)kSTok * a.apply.tgt.r_pad,
+                        "split partials");
+  return hipSuccess;
+}
+hipError_t launch_seqpass_meta(const int32_t*, int, int, int32_t*, int32_t*, float*, hipStream_t) {
+  ++g_launches;
+  return hipSuccess;
+}
+
+}  // namespace molora
+
+extern "C" {
+hipError_t hipMemcpyAsync(void* dst, const void* src, size_t n, hipMemcpyKind, hipStream_t) {
+  std::memcpy(dst, src, n);  // the indirect layout's pointer tables, written into the host "slab"
+  return hipSuccess;
+}
+hipError_t hipStreamSynchronize(hipStream_t) { return hipSuccess; }
+const char* hipGetErrorString(hipError_t) { return "stand-in"; }
+}
+
+// ------------------------------------------------------------------ helpers
+static void* fake(size_t addr) { return reinterpret_cast<void*>(addr); }  // aligned, never dereferenced
+
+struct HostHotset {
+  molora_hotset* hs = nullptr;
+  std::vector<char> slab;
+};
+
+static bool make_hotset(HostHotset& h, int K, int r, const std::vector<std::pair<int, int>>& dims, int layout) {
+  std::vector<molora_target> tg;
+  for (auto& d : dims) tg.push_back({d.first, d.second, fake(0x10000), fake(0x20000)});
+  size_t bytes = 0;
+  int rc = molora_hotset_bytes(K, r, (int)tg.size(), tg.data(), layout, &bytes);
+  CHECK(rc == MOLORA_OK, "hotset_bytes K=%d r=%d", K, r);
+  if (rc != MOLORA_OK) return false;
+  h.slab.assign(bytes + 256, 0);  // + room to align the base to 256 bytes
+  char* base = h.slab.data();
+  base += (256 - reinterpret_cast<uintptr_t>(base) % 256) % 256;
+  // a slab one byte short is refused before anything is written
+  rc = molora_hotset_init(&h.hs, K, r, 2.0f, (int)tg.size(), tg.data(), layout, base, bytes - 1, nullptr);
+  CHECK(rc == MOLORA_ENOSPC && h.hs == nullptr, "short slab accepted");
+  g_ws_base = base;  // slot and table writes must land inside [base, base + bytes)
+  g_ws_bytes = bytes;
+  g_ranges.clear();
+  rc = molora_hotset_init(&h.hs, K, r, 2.0f, (int)tg.size(), tg.data(), layout, base, bytes, nullptr);
+  CHECK(rc == MOLORA_OK, "hotset_init K=%d r=%d layout=%d", K, r, layout);
+  for (const Range& x : g_ranges) CHECK(x.hi <= bytes, "slab write %s ends at %zu > %zu", x.what.c_str(), x.hi, bytes);
+  g_ws_base = nullptr;
+  return rc == MOLORA_OK;
+}
+
+// Host buffer of exactly n bytes, 256-byte aligned (n == 0: none); the sanitizer flags any
+// access past its n-th byte.
+static void* exact_alloc(size_t n) {
+  if (n == 0) return nullptr;
+  void* p = nullptr;
+  if (posix_memalign(&p, 256, n) != 0) return nullptr;
+  return p;
+}
+
+static const size_t kMaxBuf = 192ull << 20;  // skip combinations whose workspace exceeds this
+
+// ------------------------------------------------------------------ tests
+static void test_step(int K, int r, int d_in, int d_out, int N, int layout) {
+  HostHotset h;
+  if (!make_hotset(h, K, r, {{d_in, d_out}}, layout)) return;
+  std::vector<int32_t> bounds(K + 1);
+  for (int e = 0; e <= K; ++e) bounds[e] = 8192 * e;
+  size_t need = 0;
+  CHECK(molora_step_workspace(h.hs, 0, N, &need) == MOLORA_OK, "step_workspace N=%d", N);
+  const StepPlan sp = step_plan(N, K, (r + 15) / 16 * 16, d_in);
+  CHECK(need == sp.total, "step_workspace %zu vs plan %zu", need, sp.total);
+  if (need > kMaxBuf) {
+    molora_hotset_destroy(h.hs);
+    return;
+  }
+  // exact-size workspace: every write the launches make must land inside it
+  char* ws = static_cast<char*>(exact_alloc(need));
+  g_ws_base = ws;
+  g_ws_bytes = need;
+  g_ranges.clear();
+  const int l0 = g_launches;
+  int rc = molora_step_vocab(h.hs, 0, (int32_t*)fake(0x1000), N, bounds.data(), fake(0x2000), fake(0x3000),
+                             MOLORA_BF16, fake(0x4000), MOLORA_BF16, (int32_t*)fake(0x5000), (float*)fake(0x6000),
+                             (int32_t*)fake(0x7000), (int32_t*)fake(0x8000), (int32_t*)fake(0x9000),
+                             (float*)fake(0xa000), (int32_t*)fake(0xb000), ws, need, nullptr);
+  if (K <= kApplyTileMaxAdapters) {
+    CHECK(rc == MOLORA_OK, "step N=%d K=%d r=%d d=%d", N, K, r, d_in);
+    const int launches = g_launches - l0;
+    if (N == 0) CHECK(launches == 0, "N=0 launched %d", launches);
+    else if (N <= kStepMaxN) CHECK(launches == 1, "N=%d: %d launch calls", N, launches);
+    else CHECK(launches == 3, "N=%d: %d launch calls (route, dispatch, split)", N, launches);
+    check_disjoint("step");
+    // one byte short: refused, nothing launched
+    if (need > 0 && N > 0) {
+      const int l1 = g_launches;
+      rc = molora_step_vocab(h.hs, 0, (int32_t*)fake(0x1000), N, bounds.data(), fake(0x2000), fake(0x3000), MOLORA_BF16,
+                             fake(0x4000), MOLORA_BF16, (int32_t*)fake(0x5000), (float*)fake(0x6000),
+                             (int32_t*)fake(0x7000), (int32_t*)fake(0x8000), (int32_t*)fake(0x9000),
+                             (float*)fake(0xa000), (int32_t*)fake(0xb000), ws, need - 1, nullptr);
+      CHECK(rc == MOLORA_ENOSPC && g_launches == l1, "short step workspace accepted (N=%d)", N);
+    }
+    // without a workspace: the tile step (no workspace writes)
+    g_ranges.clear();
+    rc = molora_step_vocab(h.hs, 0, (int32_t*)fake(0x1000), N, bounds.data(), fake(0x2000), fake(0x3000), MOLORA_BF16,
+                           fake(0x4000), MOLORA_BF16, (int32_t*)fake(0x5000), (float*)fake(0x6000),
+                           (int32_t*)fake(0x7000), (int32_t*)fake(0x8000), (int32_t*)fake(0x9000), (float*)fake(0xa000),
+                           (int32_t*)fake(0xb000), nullptr, 0, nullptr);
+    CHECK(rc == MOLORA_OK && g_ranges.empty(), "tile step N=%d", N);
+  } else {
+    CHECK(rc == MOLORA_ENOTSUP, "step with K=%d accepted", K);
+  }
+  g_ws_base = nullptr;
+  free(ws);
+  molora_hotset_destroy(h.hs);
+}
+
+static void test_apply(int K, int r, int d_in, int d_out, int N, int k, int path, int y_dtype) {
+  HostHotset h;
+  if (!make_hotset(h, K, r, {{d_in, d_out}}, MOLORA_LAYOUT_DIRECT)) return;
+  size_t need = 0;
+  int rc = molora_apply_workspace(h.hs, 0, N, k, y_dtype, path, &need);
+  if (k > K) {
+    CHECK(rc != MOLORA_OK, "k > K accepted");
+    molora_hotset_destroy(h.hs);
+    return;
+  }
+  CHECK(rc == MOLORA_OK, "apply_workspace");
+  if (need > kMaxBuf) {
+    molora_hotset_destroy(h.hs);
+    return;
+  }
+  char* ws = static_cast<char*>(exact_alloc(need));
+  g_ws_base = ws;
+  g_ws_bytes = need;
+  g_ranges.clear();
+  g_last_apply_path = -1;
+  rc = molora_apply(h.hs, 0, fake(0x2000), fake(0x3000), y_dtype, fake(0x4000), y_dtype, N, k, (int32_t*)fake(0x8000),
+                    (int32_t*)fake(0x9000), (float*)fake(0xa000), (int32_t*)fake(0xb000), path, ws, need, nullptr);
+  const bool tile_like = path == MOLORA_PATH_TILE || path == MOLORA_PATH_BLOCK;
+  if (tile_like && K > kApplyTileMaxAdapters) {
+    CHECK(rc == MOLORA_ENOTSUP, "tile/block with K=%d accepted", K);
+  } else {
+    CHECK(rc == MOLORA_OK, "apply N=%d k=%d K=%d r=%d path=%d", N, k, K, r, path);
+    if (N > 0) CHECK(g_last_apply_path == apply_resolve_path(N, k, path, K, (r + 15) / 16 * 16), "path");
+    check_disjoint("apply");
+    if (need > 0 && N > 0) {
+      const int l1 = g_launches;
+      rc = molora_apply(h.hs, 0, fake(0x2000), fake(0x3000), y_dtype, fake(0x4000), y_dtype, N, k,
+                        (int32_t*)fake(0x8000), (int32_t*)fake(0x9000), (float*)fake(0xa000), (int32_t*)fake(0xb000),
+                        path, ws, need - 1, nullptr);
+      CHECK(rc == MOLORA_ENOSPC && g_launches == l1, "short apply workspace accepted");
+    }
+  }
+  g_ws_base = nullptr;
+  free(ws);
+  molora_hotset_destroy(h.hs);
+}
+
+static void test_multi(int K, int r, int N, int k, int path, int y_dtype) {
+  const std::vector<std::pair<int, int>> qwen = {{2048, 2048}, {2048, 1024}, {2048, 1024}, {2048, 2048},
+                                                 {2048, 6144}, {2048, 6144}, {6144, 2048}};
+  HostHotset h;
+  if (!make_hotset(h, K, r, qwen, MOLORA_LAYOUT_INDIRECT)) return;
+  const int n = 7;
+  int targets[n];
+  const void* xs[n];
+  const void* y0s[n];
+  void* ys[n];
+  for (int i = 0; i < n; ++i) {
+    targets[i] = i;
+    xs[i] = fake(0x100000 + 0x1000 * i);
+    y0s[i] = fake(0x200000 + 0x1000 * i);
+    ys[i] = fake(0x300000 + 0x1000 * i);
+  }
+  size_t need = 0;
+  int rc = molora_apply_multi_workspace(h.hs, n, targets, N, k, y_dtype, path, &need);
+  CHECK(rc == MOLORA_OK, "multi_workspace");
+  if (need > kMaxBuf) {
+    molora_hotset_destroy(h.hs);
+    return;
+  }
+  char* ws = static_cast<char*>(exact_alloc(need));
+  g_ws_base = ws;
+  g_ws_bytes = need;
+  g_ranges.clear();
+  rc = molora_apply_multi(h.hs, n, targets, xs, y0s, y_dtype, ys, y_dtype, N, k, (int32_t*)fake(0x8000),
+                          (int32_t*)fake(0x9000), (float*)fake(0xa000), (int32_t*)fake(0xb000), path, ws, need, nullptr);
+  CHECK(rc == MOLORA_OK, "multi N=%d k=%d path=%d", N, k, path);
+  check_disjoint("apply_multi");
+  if (need > 0) {
+    rc = molora_apply_multi(h.hs, n, targets, xs, y0s, y_dtype, ys, y_dtype, N, k, (int32_t*)fake(0x8000),
+                            (int32_t*)fake(0x9000), (float*)fake(0xa000), (int32_t*)fake(0xb000), path, ws, need - 1,
+                            nullptr);
+    CHECK(rc == MOLORA_ENOSPC, "short multi workspace accepted");
+  }
+  g_ws_base = nullptr;
+  free(ws);
+  molora_hotset_destroy(h.hs);
+}
+
+static void test_dispatch() {
+  for (long long N : {1LL, 8192LL, 8193LL, 16384LL, 100000LL, 1048579LL})
+    for (int k : {1, 2, 4})
+      for (int K : {1, 4, 16, 64}) {
+        size_t need = 0;
+        CHECK(molora_dispatch_workspace((int)N, k, K, &need) == MOLORA_OK, "dispatch_workspace");
+        char* ws = static_cast<char*>(exact_alloc(need));
+        g_ws_base = ws;
+        g_ws_bytes = need;
+        g_ranges.clear();
+        int rc = molora_dispatch((int32_t*)fake(0x1000), (float*)fake(0x2000), (int)N, k, K, (int32_t*)fake(0x3000),
+                                 (int32_t*)fake(0x4000), (int32_t*)fake(0x5000), (float*)fake(0x6000),
+                                 (int32_t*)fake(0x7000), ws, need, nullptr);
+        CHECK(rc == MOLORA_OK, "dispatch N=%lld k=%d K=%d", N, k, K);
+        check_disjoint("dispatch");
+        if (need > 0) {
+          rc = molora_dispatch((int32_t*)fake(0x1000), (float*)fake(0x2000), (int)N, k, K, (int32_t*)fake(0x3000),
+                               (int32_t*)fake(0x4000), (int32_t*)fake(0x5000), (float*)fake(0x6000),
+                               (int32_t*)fake(0x7000), ws, need - 4, nullptr);
+          CHECK(rc == MOLORA_ENOSPC, "short dispatch workspace accepted");
+        }
+        g_ws_base = nullptr;
+        free(ws);
+      }
+}
+
+static void test_validation() {
+  // argument errors are reported before anything is launched
+  const int l0 = g_launches;
+  int32_t b[3] = {0, 10, 5};
+  CHECK(molora_route_vocab((int32_t*)fake(0x1000), 4, b, 2, (int32_t*)fake(0x2000), (float*)fake(0x3000), nullptr) ==
+            MOLORA_EINVAL && std::strstr(molora_last_error(), "non-decreasing") != nullptr,
+        "decreasing bounds");
+  CHECK(molora_route_vocab((int32_t*)fake(0x1002), 4, b + 0, 1, (int32_t*)fake(0x2000), (float*)fake(0x3000),
+                           nullptr) == MOLORA_EINVAL,
+        "misaligned ids");
+  CHECK(molora_route_topk(nullptr, 4, 0, nullptr, nullptr, nullptr, nullptr, (float*)fake(0x1000), 4, 5,
+                          (int32_t*)fake(0x2000), (float*)fake(0x3000), nullptr, nullptr) == MOLORA_ENOTSUP,
+        "k > K");
+  CHECK(molora_dispatch((int32_t*)fake(0x1000), (float*)fake(0x2000), 1 << 29, 8, 4, (int32_t*)fake(0x3000),
+                        (int32_t*)fake(0x4000), (int32_t*)fake(0x5000), (float*)fake(0x6000), nullptr, nullptr, 0,
+                        nullptr) == MOLORA_ENOTSUP,
+        "N*k overflow");
+  HostHotset h;
+  if (make_hotset(h, 4, 16, {{512, 512}}, MOLORA_LAYOUT_DIRECT)) {
+    size_t sz = 0;
+    CHECK(molora_apply_workspace(h.hs, 1, 4, 1, 0, 0, &sz) == MOLORA_EINVAL, "target out of range");
+    CHECK(molora_apply_workspace(h.hs, 0, 4, 5, 0, 0, &sz) == MOLORA_EINVAL, "k > K");
+    CHECK(molora_apply(h.hs, 0, fake(0x2008), fake(0x3000), 0, fake(0x4000), 0, 4, 1, (int32_t*)fake(0x8000),
+                       (int32_t*)fake(0x9000), (float*)fake(0xa000), (int32_t*)fake(0xb000), 0, nullptr, 0,
+                       nullptr) == MOLORA_EINVAL,
+          "misaligned x");
+    CHECK(molora_apply(h.hs, 0, fake(0x2000), fake(0x3000), 0, fake(0x3000), 1, 4, 1, (int32_t*)fake(0x8000),
+                       (int32_t*)fake(0x9000), (float*)fake(0xa000), (int32_t*)fake(0xb000), 0, nullptr, 0,
+                       nullptr) == MOLORA_EINVAL,
+          "in place with two dtypes");
+    CHECK(molora_hotset_load(h.hs, 0, 4, fake(0x10), fake(0x10), nullptr) == MOLORA_EINVAL, "adapter out of range");
+    molora_hotset_destroy(h.hs);
+  }
+  CHECK(g_launches == l0 + 4, "launches during validation: %d", g_launches - l0);  // init: one relayout per adapter
+}
+
+int main() {
+  test_validation();
+  test_dispatch();
+  for (int layout : {MOLORA_LAYOUT_DIRECT, MOLORA_LAYOUT_INDIRECT})
+    for (int K : {1, 4, 16, 17})
+      for (int r : {8, 16, 64})
+        for (int N : {0, 1, 63, 64, 2048, 4096, 4097, 8192, 8193, 65536})
+          test_step(K, r, 4096, 4096, N, layout);
+  test_step(4, 16, 512, 1536, 5000, MOLORA_LAYOUT_DIRECT);
+  for (int path : {MOLORA_PATH_AUTO, MOLORA_PATH_GROUPED, MOLORA_PATH_SKINNY, MOLORA_PATH_TILE, MOLORA_PATH_BLOCK})
+    for (int K : {1, 4, 16, 64})
+      for (int r : {8, 16, 48, 64})
+        for (int k : {1, 2, 3, 4, 8})
+          for (int N : {0, 1, 100, 1024, 4097})
+            for (int yd : {MOLORA_BF16, MOLORA_F32}) test_apply(K, r, 1024, 2048, N, k, path, yd);
+  for (int N : {16384}) test_apply(16, 64, 4096, 4096, N, 4, MOLORA_PATH_AUTO, MOLORA_BF16);
+  for (int path : {MOLORA_PATH_AUTO, MOLORA_PATH_SKINNY, MOLORA_PATH_BLOCK, MOLORA_PATH_GROUPED})
+    for (int k : {1, 2})
+      for (int N : {1, 256, 4096})
+        for (int yd : {MOLORA_BF16, MOLORA_F32}) test_multi(4, 16, N, k, path, yd);
+  fprintf(stderr, "%d checks, %d failures\n", g_checks, g_fail);
+  return g_fail == 0 ? 0 : 1;
+}

@@ -60,9 +60,11 @@ def test_host_validation_without_launch():
     # route_vocab: K out of range, decreasing bounds, negative N
     b = (ctypes.c_int32 * 3)(0, 10, 5)
     assert L.molora_route_vocab(nul, 4, ctypes.cast(b, ctypes.c_void_p), 2, nul, nul, nul) == 1
+    assert b"non-decreasing" in L.molora_last_error()
     assert L.molora_route_vocab(nul, 4, ctypes.cast(b, ctypes.c_void_p), 0, nul, nul, nul) == 2
+    assert b"K=0" in L.molora_last_error()
     assert L.molora_route_vocab(nul, -1, ctypes.cast(b, ctypes.c_void_p), 2, nul, nul, nul) == 1
-    assert b"non-decreasing" in L.molora_last_error() or True
+    assert b"N=-1" in L.molora_last_error()
     ok = (ctypes.c_int32 * 3)(0, 5, 10)
     assert L.molora_route_vocab(nul, 0, ctypes.cast(ok, ctypes.c_void_p), 2, nul, nul, nul) == 0  # N=0 no-op
     assert L.molora_route_vocab(nul, 3, ctypes.cast(ok, ctypes.c_void_p), 2, nul, nul, nul) == 1  # NULL buffers

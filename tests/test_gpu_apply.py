@@ -257,21 +257,49 @@ def test_qwen_layer_all_targets():
 
 @pytest.mark.parametrize("k", [1, 2, 3, 4])
 def test_stress_full_size(k):
+    """The stress workload at full size (N=16384, d=4096, K=16, r=64, Zipf logits), k = 1..4, on
+    the AUTO path the bench times: every one of the 16384 rows against the oracle, for an fp32
+    and a bf16 y (the bf16 y goes through the fp32 carry of the k > 1 passes)."""
     m = need_gpu()
     c = synth.stress(k)
     t = c.targets[0]
     _, idx, w, _ = m.molora_route_topk(k, c.K, logits=dev(c.logits))
     counts, offsets, perm, perm_w, inv = m.molora_dispatch(idx, w, c.K, k)
     hs = make_hotset(m, c.targets, c.scale)
-    y = m.molora_apply(hs, dev_bf16(t.x), dev_bf16(t.y0), offsets, perm, perm_w, inv, k=k, y_dtype=torch.float32)
+    x, y0 = dev_bf16(t.x), dev_bf16(t.y0)
+    y32 = m.molora_apply(hs, x, y0, offsets, perm, perm_w, inv, k=k, y_dtype=torch.float32)
+    y16 = m.molora_apply(hs, x, y0, offsets, perm, perm_w, inv, k=k, y_dtype=torch.bfloat16)
     gi, gw = host(idx), host(w)
     oi, _, _ = route_topk(c.logits.astype(np.float64), k)
     np.testing.assert_array_equal(gi, oi)
-    # full-size oracle on a sample of tokens (all of their pairs), to keep the CPU time bounded
-    rows = np.random.default_rng(k).choice(c.N, 2048, replace=False)
-    sub = synth.Target("s", t.d_in, t.d_out, t.A, t.B, t.x[rows], t.y0[rows])
-    ref = oracle_from_gpu_routing(sub, c.scale, gi[rows], gw[rows], c.K, k)
-    check_float_output(host(y)[rows], ref, f64(t.y0[rows]))
+    ref = oracle_from_gpu_routing(t, c.scale, gi, gw, c.K, k)
+    check_float_output(host(y32), ref, f64(t.y0))
+    check_bf16_output(host(y16), ref)
+
+
+def test_qwen_layer_multi_auto_all_targets():
+    """The Qwen3-1.7B-shaped layer as the bench runs it: router MLP, top-2, dispatch, then one
+    molora_apply_multi over all 7 targets on AUTO (which resolves to the 64-token block path for
+    several targets with k > 1), bf16 and fp32 y; every target against the oracle."""
+    m = need_gpu()
+    c = synth.qwen_layer()
+    r = c.router
+    logits, idx, w, flags = m.molora_route_topk(
+        c.k, c.K, x=dev_bf16(c.targets[0].x), W1=dev_bf16(np.ascontiguousarray(r["W1"].T)), b1=dev(r["b1"]),
+        W2=dev_bf16(np.ascontiguousarray(r["W2"].T)), b2=dev(r["b2"]))
+    counts, offsets, perm, perm_w, inv = m.molora_dispatch(idx, w, c.K, c.k)
+    gi, gw = host(idx), host(w)
+    hs = make_hotset(m, c.targets, c.scale)
+    xs = [dev_bf16(t.x) for t in c.targets]
+    y0s = [dev_bf16(t.y0) for t in c.targets]
+    assert m.molora_apply_multi_workspace(hs, list(range(7)), c.N, c.k, m.PATH_AUTO, torch.bfloat16) == \
+        m.molora_apply_multi_workspace(hs, list(range(7)), c.N, c.k, m.PATH_BLOCK, torch.bfloat16)
+    y16 = m.molora_apply_multi(hs, xs, y0s, offsets, perm, perm_w, inv, k=c.k, y_dtype=torch.bfloat16)
+    y32 = m.molora_apply_multi(hs, xs, y0s, offsets, perm, perm_w, inv, k=c.k, y_dtype=torch.float32)
+    for ti, t in enumerate(c.targets):
+        ref = oracle_from_gpu_routing(t, c.scale, gi, gw, c.K, c.k)
+        check_bf16_output(host(y16[ti]), ref)
+        check_float_output(host(y32[ti]), ref, f64(t.y0))
 
 
 @pytest.mark.parametrize("path", [0, 4])

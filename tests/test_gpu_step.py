@@ -19,11 +19,11 @@ def three_calls(m, hs, ids, bounds, K, x, y0, y_dtype, path):
 
 
 def step_ws(m, hs, N, block):
-    """A step workspace (split step), or None (tile step): zero-filled, as the fused launch's
-    control words at its start must be before the first call."""
+    """A step workspace (split step), or None (tile step).  It needs no initial contents, so it
+    starts as 0xFF bytes (NaN floats): a partial read before it is written would show."""
     if not block:
         return None
-    return torch.zeros((m.molora_step_workspace(hs, 0, N),), dtype=torch.uint8, device="cuda")
+    return torch.full((max(1, m.molora_step_workspace(hs, 0, N)),), 0xFF, dtype=torch.uint8, device="cuda")
 
 
 def cases():
@@ -183,67 +183,53 @@ def test_block_step_reuses_workspace_across_inputs_and_graph_replays():
         np.testing.assert_array_equal(host(y), eager)
 
 
-def _split_env(fused, spin=None):
-    import os
-    old = {k: os.environ.get(k) for k in ("MOLORA_SPLIT_FUSED", "MOLORA_SPLIT_SPIN")}
-    os.environ["MOLORA_SPLIT_FUSED"] = "1" if fused else "0"
-    if spin is None:
-        os.environ.pop("MOLORA_SPLIT_SPIN", None)
-    else:
-        os.environ["MOLORA_SPLIT_SPIN"] = str(spin)
-    return old
+def large_cases():
+    # above 4096 tokens: route, the chip-wide dispatch (8193 pairs and more) and the split launches
+    out = []
+    for N, cid in ((4097, 31), (8192, 32), (8193, 33)):
+        c = synth.vocab_case(N=N, d=4096, K=4, r=16, case_id=cid, runs=True, probs=(0.4, 0.3, 0.15, 0.15))
+        c.ids = c.ids.copy()
+        c.ids[7::1001] = -3  # a few unrouted tokens
+        out.append((f"n{N}", c))
+    out.append(("n5000_k16_r64", synth.vocab_case(N=5000, d=1024, K=16, r=64, case_id=34, runs=True,
+                                                  probs=(1 / 16,) * 16)))
+    return out
 
 
-def _restore_env(old):
-    import os
-    for k, v in old.items():
-        if v is None:
-            os.environ.pop(k, None)
-        else:
-            os.environ[k] = v
-
-
-@pytest.mark.parametrize("name", ["modality4", "k9_r16", "k3_r48"])
-def test_split_fused_equals_two_launches(name):
-    """The fused split launch (partials published per block inside one launch) gives the same
-    bits as the two-launch split step, on calls in a row that alternate two inputs (a partial
-    left from the previous call would show), under graph replays, and with every workgroup
-    forced onto the fallback that recomputes the block's other slices itself."""
+@pytest.mark.parametrize("block", [False, True])
+@pytest.mark.parametrize("name,case", large_cases())
+def test_step_above_4096_tokens(name, case, block):
+    """molora_step_vocab above 4096 tokens, with and without a workspace: routing and dispatch
+    bit-exact against the oracle, y within the output bars, and (with a workspace) y bit-identical
+    to the block path on the same dispatch, as the header states."""
     m = need_gpu()
-    case = dict(cases())[name]
     t = case.targets[0]
     hs = m.molora_hotset_init([(dev_bf16(t.A), dev_bf16(t.B))], case.scale)
     ids = dev(case.ids)
     bounds = case.bounds.tolist()
-    xa, y0 = dev_bf16(t.x), dev_bf16(t.y0)
-    xb = torch.flip(xa, dims=[0]).contiguous()
-    old = _split_env(False)
-    try:
-        refs = [m.molora_step_vocab(hs, ids, bounds, x, y0, ws=step_ws(m, hs, case.N, True))[0] for x in (xa, xb)]
-        for spin in (None, -1):
-            _split_env(True, spin)
-            ws = step_ws(m, hs, case.N, True)
-            for i in range(5):
-                y, r, meta = m.molora_step_vocab(hs, ids, bounds, (xa, xb)[i % 2], y0, ws=ws)
-                np.testing.assert_array_equal(host(y), host(refs[i % 2]))
-        # graph replays (fused, default wait), eager calls in between
-        _split_env(True)
-        ws = step_ws(m, hs, case.N, True)
-        out = torch.empty_like(y0)
-        s = torch.cuda.Stream()
-        s.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(s):
-            m.molora_step_vocab(hs, ids, bounds, xa, y0, y=out, ws=ws)
-        torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=s):
-            m.molora_step_vocab(hs, ids, bounds, xa, y0, y=out, ws=ws)
-        for _ in range(3):
-            out.fill_(0)
-            g.replay()
-            torch.cuda.synchronize()
-            np.testing.assert_array_equal(host(out), host(refs[0]))
-            yb, _, _ = m.molora_step_vocab(hs, ids, bounds, xb, y0, ws=ws)
-            np.testing.assert_array_equal(host(yb), host(refs[1]))
-    finally:
-        _restore_env(old)
+    x, y0 = dev_bf16(t.x), dev_bf16(t.y0)
+    ws = step_ws(m, hs, case.N, block)
+    y, r, meta = m.molora_step_vocab(hs, ids, bounds, x, y0, y_dtype=torch.float32, ws=ws)
+    torch.cuda.synchronize()
+    N = case.N
+    ri, rw = route_vocab(case.ids, case.bounds)
+    np.testing.assert_array_equal(host(r[0])[:N], ri)
+    np.testing.assert_array_equal(host(r[1])[:N], rw.astype(np.float32))
+    oc, oo, op, opw, oinv = dispatch(ri, rw, case.K)
+    np.testing.assert_array_equal(host(meta[0]), oc)
+    np.testing.assert_array_equal(host(meta[1]), oo)
+    np.testing.assert_array_equal(host(meta[2])[:oo[-1]], op)
+    np.testing.assert_array_equal(host(meta[3])[:oo[-1]], opw.astype(np.float32))
+    np.testing.assert_array_equal(host(meta[4])[:N], oinv)
+    ref = apply(f64(t.y0), f64(t.x), f64(t.A), f64(t.B), case.scale, op, opw, oo, 1)
+    check_float_output(host(y), ref, f64(t.y0))
+    if block:
+        yb = m.molora_apply(hs, x, y0, meta[1], meta[2], meta[3], meta[4], k=1, y_dtype=torch.float32,
+                            path=m.PATH_BLOCK)
+        np.testing.assert_array_equal(host(y), host(yb))
+        # the same workspace again, after a smaller batch used it: same bits
+        n_small = 1000
+        m.molora_step_vocab(hs, ids[:n_small].contiguous(), bounds, x[:n_small].contiguous(),
+                            torch.flip(y0[:n_small], dims=[0]).contiguous(), ws=ws)
+        y2, _, _ = m.molora_step_vocab(hs, ids, bounds, x, y0, y_dtype=torch.float32, ws=ws)
+        np.testing.assert_array_equal(host(y2), host(y))

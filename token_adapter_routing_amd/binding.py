@@ -345,9 +345,10 @@ def molora_step_vocab(hs: HotSet, ids: torch.Tensor, bounds: Sequence[int], x: t
                       ws: Optional[torch.Tensor] = None, stream=None):
     """route_vocab + dispatch + apply (k = 1) in one call.  Returns (y, (idx, w),
     (counts, offsets, perm, perm_w, inv)); `route` and `meta` may supply those buffers.
-    `ws` (uint8, 256-byte aligned, at least molora_step_workspace bytes, zero-filled before its
-    first use and kept between calls) selects the split step over 512-wide slices (two
-    launches; one with MOLORA_SPLIT_FUSED=1); without it the one-launch tile step runs.
+    `ws` (uint8, 256-byte aligned, at least molora_step_workspace bytes, no initial contents
+    needed) selects the split step over 512-wide slices (two launches); without it the
+    one-launch tile step runs.  Above 4096 tokens routing and dispatch run as launches of their
+    own first.
     """
     N = ids.numel()
     K = len(bounds) - 1

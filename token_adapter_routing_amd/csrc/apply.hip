@@ -145,7 +145,6 @@ __global__ __launch_bounds__(kT8Threads) void apply_t8(T8ApplyArgs a) {
 // the apply body, while its stores drain.  Workgroups of column group 0 write their tokens'
 // idx / w / inv / perm / perm_w; the first tile writes counts and offsets.
 constexpr int kStepIdsPerThread = 4;  // ids held from the start: N <= 512 * 4 in one pass
-constexpr int kStepMaxN = 4096;       // larger batches take the three-launch step
 constexpr int kSWavesMax = 8;         // waves of the workgroups that count ids
 
 // Vocabulary ranges as kernel arguments: [lo, hi) is routed; the owner of v is the number of
@@ -172,6 +171,7 @@ struct StepArgs {
   int32_t* perm;
   float* perm_w;
   int32_t* inv;
+  int dispatch_share;  // the launch writes idx .. inv (every workgroup of slice 0 counts all N ids)
 };
 
 struct StepLds {
@@ -403,8 +403,6 @@ __global__ __launch_bounds__(kBThreads, 2) void expand_block_multi(BlockMulti m)
 // round robin over the 8 XCDs (workgroup b runs on XCD b % 8); both launches place every slice of
 // block tb on XCD tb % 8, so the partials that the shrink writes are still in that XCD's L2 when
 // the expand reads them.
-constexpr int kSTok = 64;
-constexpr int kSSlice = 512;
 constexpr int kSWaves = 8;
 constexpr int kSThreads = kSWaves * kWave;
 // adapters whose slices are staged in LDS together (64 KB)
@@ -417,10 +415,6 @@ struct SplitGeom {
   int nblocks, kslices, cslices;  // grid of a launch: 8 * ceil(nblocks / 8) * slices
   float* part;  // [nblocks][kslices][64][r_pad] fp32: partial h of each token on its own adapter
 };
-
-__host__ __device__ inline size_t split_part_floats(int N, int d_in, int r_pad) {
-  return (size_t)((N + kSTok - 1) / kSTok) * ((d_in + kSSlice - 1) / kSSlice) * kSTok * r_pad;
-}
 
 template <int RB>
 struct ShrinkLds {
@@ -551,7 +545,7 @@ __device__ __forceinline__ void shrink_slice(const StepArgs& a, const SplitGeom&
   }
   __syncthreads();
   if (kh == 0) {
-    float* dst = g.part + (((size_t)tb * g.kslices + sl) * kSTok + 16 * rb) * r_pad;
+    float* dst = g.part + split_part_index(tb, sl, g.kslices, r_pad) + (size_t)16 * rb * r_pad;
 #pragma unroll
     for (int u = 0; u < RB; ++u)
 #pragma unroll
@@ -607,248 +601,7 @@ __global__ __launch_bounds__(kSThreads) void split_shrink(StepArgs a, SplitGeom 
   const int q = blockIdx.x >> 3;
   const int tb = (q / g.kslices) * 8 + (blockIdx.x & 7), sl = q % g.kslices;
   if (tb >= g.nblocks) return;
-  shrink_slice<RB, INDIRECT>(a, g, tb, sl, sl == 0, L, [](uint32_t) {});  // slice 0: dispatch outputs
-}
-
-// The same step as one launch (split_shrink + split_expand fused).  Workgroup (block tb, slice
-// j) computes shrink slice j, publishes it, then expands output slice j once the block's partials
-// are all published; the y0 rows and B slices of its expand are requested before it waits, so
-// they stream during the other workgroups' shrinks.  All slices of block tb run on XCD tb mod 8
-// (workgroups are dispatched round robin over the XCDs), so the partials and the flags that
-// publish them meet in that XCD's L2.  Publication: after its partial stores have completed a
-// workgroup writes the launch's epoch into flag[tb][j]; the epoch is read from the workspace
-// header at the start and advanced by the last workgroup to finish, so a flag equal to it was
-// written by this launch.  The wait is bounded: a workgroup that is not answered within
-// `spin` polls (a workgroup of its block not resident, or running on another XCD) computes
-// every other slice's partial itself, with the same code and so the same bits, and goes on;
-// the launch therefore always completes and always produces the same y.
-template <int RB>
-struct ExpandLds {
-  alignas(16) uint16_t Bs[split_group<RB>()][kSSlice * RB * 16];
-  alignas(16) uint16_t hb[2][kSTok][RB * 16];
-};
-struct FusedHdr {  // workspace words after the partials
-  unsigned epoch;  // epoch of the last completed launch
-  unsigned done;   // workgroups of the current launch that have finished
-};
-constexpr int kSMaxSlices = 64;  // d <= 32768
-
-// The shrink's and the expand's LDS side by side (rank blocks 1..3: at most 145 KB), else shared.
-template <int RB>
-struct FusedLdsT {
-  static constexpr bool kSeparate = true;
-  ShrinkLds<RB> s;
-  ExpandLds<RB> e;
-};
-template <>
-struct FusedLdsT<4> {
-  static constexpr bool kSeparate = false;
-  union {
-    ShrinkLds<4> s;
-    ExpandLds<4> e;
-  };
-};
-
-template <int RB, bool INDIRECT, bool Y0F32, bool YF32, bool ALLB>
-__global__ __launch_bounds__(kSThreads) void split_fused(StepArgs a, SplitGeom g, FusedHdr* hdr, unsigned* flags,
-                                                         int spin) {
-  constexpr int GB = split_group<RB>();
-  constexpr int RP = RB * 16;
-  constexpr size_t y0b = Y0F32 ? 4 : 2, yb = YF32 ? 4 : 2;
-  static_assert(!ALLB || RB == 1, "all-adapter staging holds four rank-16 slices");
-  __shared__ FusedLdsT<RB> L;
-  constexpr bool EARLY_B = FusedLdsT<RB>::kSeparate;  // the expand's B slices load with the shrink's
-  __shared__ unsigned epoch_s;
-  __shared__ int fallback_s, stray_s;
-  const int SL = max(g.kslices, g.cslices);
-  const int q = blockIdx.x >> 3;
-  const int tb = (q / SL) * 8 + (blockIdx.x & 7), j = q % SL;
-  if (tb >= g.nblocks) return;
-  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int n = lane & 15, G = lane >> 4, rb = wave & 3, ch = wave >> 2;
-  const int N = a.t.N, K = a.t.K, d_out = a.t.tgt.d_out;
-  const int t0 = tb * kSTok;
-  if (threadIdx.x == 0) {
-    epoch_s = __hip_atomic_load(&hdr->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
-    // a workgroup off the XCD that its block's slices share publishes nothing (its partial is
-    // not in that XCD's L2) and computes the other slices itself
-    stray_s = (__builtin_amdgcn_s_getreg((31 << 11) | 20) & 15) != (int)(blockIdx.x & 7);
-  }
-  const bool expand = j < g.cslices;
-  const int c0 = expand ? j * kSSlice : 0, c1 = min(c0 + kSSlice, d_out);
-  const int nb = (c1 - c0) / kColBlock;
-  const int b0 = min(2 * ch, nb - 1), b1 = min(2 * ch + 1, nb - 1);
-  const bool has0 = expand && 2 * ch < nb, has1 = expand && 2 * ch + 1 < nb;
-  const int bbytes = (c1 - c0) * RP * 2;
-  const char* y0rows[4];
-  char* yrows[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int t = min(t0 + 16 * rb + 4 * G + i, N - 1);
-    y0rows[i] = reinterpret_cast<const char*>(a.t.y0) + (size_t)t * d_out * y0b;
-    yrows[i] = reinterpret_cast<char*>(a.t.y) + (size_t)t * d_out * yb;
-  }
-  RowChunk<Y0F32> yc0, yc1;
-  auto stage_b = [&](uint32_t used_) {
-    if (!expand) return;
-    if constexpr (ALLB) {
-      for (int e2 = 0; e2 < K; ++e2)
-        lds_copy_1k(L.e.Bs[e2], adapter_B<INDIRECT>(a.t.tgt, e2) + (size_t)c0 * RP, bbytes);
-    } else {
-      uint32_t r2 = used_;
-      for (int gi = 0; gi < min(GB, __popc(used_)); ++gi) {
-        lds_copy_1k(L.e.Bs[gi], adapter_B<INDIRECT>(a.t.tgt, __builtin_ctz(r2)) + (size_t)c0 * RP, bbytes);
-        r2 &= r2 - 1;
-      }
-    }
-  };
-  // the expand's loads that do not need the other slices (B slices when their LDS is separate,
-  // y0 rows), requested with the shrink's so that HBM streams them together
-  auto prefetch = [&](uint32_t used_) {
-    if constexpr (EARLY_B) stage_b(used_);
-    __builtin_amdgcn_sched_barrier(0);
-    load_row_chunk<Y0F32>(yc0, y0rows, c0 + b0 * kColBlock, n);
-    load_row_chunk<Y0F32>(yc1, y0rows, c0 + b1 * kColBlock, n);
-    __builtin_amdgcn_sched_barrier(0);
-  };
-  // ---- shrink slice j (publishes nothing yet)
-  const int myid = a.ids[min(t0 + lane, N - 1)];
-  const int pe = step_owner(myid, a.bounds);
-  uint32_t used = 0;
-#pragma unroll
-  for (int e = 0; e < kT8MaxU; ++e)
-    if (e < K && __ballot(pe == e) != 0) used |= 1u << e;
-  const int nU = __popc(used);
-  if (j < g.kslices) shrink_slice<RB, INDIRECT>(a, g, tb, j, j == 0, L.s, prefetch);
-  else prefetch(used);
-  __syncthreads();  // the shrink's LDS is free
-  const unsigned E = epoch_s;
-  if constexpr (!EARLY_B) stage_b(used);
-  // the partial stores (and every load above) have completed
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  // ---- publish slice j, then wait for the block's other slices
-  if (threadIdx.x == 0) {
-    const int stray = stray_s;
-    if (!stray) __hip_atomic_store(&flags[(size_t)tb * kSMaxSlices + j], E, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    int fb = stray;
-    if (expand && !fb && spin < 0) fb = 1;  // forced (tests of the fallback)
-    if (expand && !fb) {
-      for (int it = 0;; ++it) {
-        bool all = true;
-        for (int s2 = 0; s2 < SL; ++s2)
-          all = all && __hip_atomic_load(&flags[(size_t)tb * kSMaxSlices + s2], __ATOMIC_RELAXED,
-                                         __HIP_MEMORY_SCOPE_AGENT) == E;
-        if (all) break;
-        if (it >= spin) {
-          fb = 1;
-          break;
-        }
-        __builtin_amdgcn_s_sleep(2);
-      }
-    }
-    fallback_s = fb;
-  }
-  __syncthreads();
-  if (expand) {
-    if (fallback_s) {
-      // not answered in time: compute the other slices' partials here (same code, same bits);
-      // they overwrite the workspace with the values their own workgroups write
-      for (int s2 = 0; s2 < g.kslices; ++s2) {
-        if (s2 == j) continue;
-        shrink_slice<RB, INDIRECT>(a, g, tb, s2, false, L.s, [](uint32_t) {});
-        __syncthreads();
-      }
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-      // the B slices again when the shrink reused their LDS
-      if constexpr (!EARLY_B) {
-        stage_b(used);
-        __builtin_amdgcn_s_waitcnt(0);
-      }
-    }
-    // h = scale x (sum of the slices in order), split into bf16 hi / lo; unrouted tokens get 0
-    constexpr int QPT = (kSTok * RP / 4 + kSThreads - 1) / kSThreads;
-    const float* pbase = g.part + (size_t)tb * g.kslices * kSTok * RP;
-#pragma unroll
-    for (int qq = 0; qq < QPT; ++qq) {
-      const int qi = qq * kSThreads + (int)threadIdx.x;
-      const int tok = min(qi, kSTok * RP / 4 - 1) / (RP / 4), rk = 4 * (qi % (RP / 4));
-      const float wt = __shfl(pe, tok, kWave) >= 0 ? a.t.scale : 0.f;
-      if (qi < kSTok * RP / 4) {
-        float sum[4] = {0.f, 0.f, 0.f, 0.f};
-        for (int s2 = 0; s2 < g.kslices; ++s2) {
-          const u32x4_t v = ld16(pbase + (size_t)s2 * kSTok * RP + 4 * qi);
-#pragma unroll
-          for (int c = 0; c < 4; ++c) sum[c] += __uint_as_float(v[c]);
-        }
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const float h = sum[c] * wt;
-          const __bf16 hi = (__bf16)h;
-          const __bf16 lo = (__bf16)(h - (float)hi);
-          L.e.hb[0][tok][rk + c] = __builtin_bit_cast(uint16_t, hi);
-          L.e.hb[1][tok][rk + c] = __builtin_bit_cast(uint16_t, lo);
-        }
-      }
-    }
-    f32x4_t o0[8], o1[8];
-#pragma unroll
-    for (int jj = 0; jj < 8; ++jj) {
-      o0[jj] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      o1[jj] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    }
-    const int erow = __shfl(pe, 16 * rb + n, kWave);
-    uint32_t rem = used;
-    for (int base = 0; base < nU; base += GB) {
-      const int ng = min(GB, nU - base);
-      if (!ALLB && base > 0) {
-        __syncthreads();
-        uint32_t r3 = rem;
-        for (int gi = 0; gi < ng; ++gi) {
-          lds_copy_1k(L.e.Bs[gi], adapter_B<INDIRECT>(a.t.tgt, __builtin_ctz(r3)) + (size_t)c0 * RP, bbytes);
-          r3 &= r3 - 1;
-        }
-        __builtin_amdgcn_s_waitcnt(0);
-      }
-      __syncthreads();  // the group's B slices and h are in LDS
-      for (int gi = 0; gi < ng; ++gi) {
-        const int e = __builtin_ctz(rem);
-        rem &= rem - 1;
-        const uint16_t* Bl = L.e.Bs[ALLB ? e : gi];
-        bf16x8_t hv[RB];
-#pragma unroll
-        for (int u = 0; u < RB; ++u) {
-          u32x4_t v = *reinterpret_cast<const u32x4_t*>(&L.e.hb[G >> 1][16 * rb + n][u * 16 + 8 * (G & 1)]);
-          if (erow != e) v = u32x4_t{0u, 0u, 0u, 0u};
-          hv[u] = as_bf16x8(v);
-        }
-        const uint16_t* bp0 = Bl + (size_t)(b0 * kColBlock + n) * RP + 8 * (G & 1);
-        const uint16_t* bp1 = Bl + (size_t)(b1 * kColBlock + n) * RP + 8 * (G & 1);
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj)
-#pragma unroll
-          for (int u = 0; u < RB; ++u) {
-            const u32x4_t v0 = *reinterpret_cast<const u32x4_t*>(bp0 + (size_t)16 * jj * RP + 16 * u);
-            const u32x4_t v1 = *reinterpret_cast<const u32x4_t*>(bp1 + (size_t)16 * jj * RP + 16 * u);
-            o0[jj] = mfma16x16x32(hv[u], as_bf16x8(v0), o0[jj]);
-            o1[jj] = mfma16x16x32(hv[u], as_bf16x8(v1), o1[jj]);
-          }
-      }
-    }
-    if (has0) epilogue_store<Y0F32, YF32>(o0, yc0, yrows, c0 + b0 * kColBlock, n, 0xFu);
-    if (has1) epilogue_store<Y0F32, YF32>(o1, yc1, yrows, c0 + b1 * kColBlock, n, 0xFu);
-  }
-  // the last workgroup to finish advances the epoch for the next launch
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const unsigned total = (unsigned)(g.nblocks * SL);
-    const unsigned d = __hip_atomic_fetch_add(&hdr->done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (d == total - 1) {
-      __hip_atomic_store(&hdr->done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(&hdr->epoch, E, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-  }
+  shrink_slice<RB, INDIRECT>(a, g, tb, sl, sl == 0 && a.dispatch_share, L, [](uint32_t) {});  // slice 0: dispatch outputs
 }
 
 // ALLB (rank block 1, K <= 4): the B slices of all K adapters fit in LDS and are requested
@@ -895,7 +648,7 @@ __global__ __launch_bounds__(kSThreads) void split_expand(StepArgs a, SplitGeom 
   constexpr int QPT = (kSTok * RP / 4 + kSThreads - 1) / kSThreads;  // 16-byte quads per thread
   constexpr int KSMAX = 8;  // slices loaded up front (the rest, d_in > 4096, at the sum)
   u32x4_t pv[QPT][KSMAX];
-  const float* pbase = g.part + (size_t)tb * g.kslices * kSTok * RP;
+  const float* pbase = g.part + split_part_index(tb, 0, g.kslices, RP);
 #pragma unroll
   for (int q = 0; q < QPT; ++q) {
     const int qi = min(q * kSThreads + (int)threadIdx.x, kSTok * RP / 4 - 1);
@@ -1388,20 +1141,19 @@ __global__ __launch_bounds__(256) void expand_grouped_k1(ExpandArgs a) {
 // Several projections that share one routing (the targets of a layer), one launch per phase:
 // target i's arguments are entry i of an array passed by value; the grid's last dimension
 // selects the entry and workgroups past a target's own grid return.
-constexpr int kMaxMulti = 8;
 struct ShrinkMulti {
-  ShrinkArgs a[kMaxMulti];
+  ShrinkArgs a[kApplyMaxMulti];
 };
 struct ExpandMulti {
-  ExpandArgs a[kMaxMulti];
+  ExpandArgs a[kApplyMaxMulti];
 };
 struct FinishMulti {
-  const void* y0[kMaxMulti];
-  const float* z[kMaxMulti];
-  void* y[kMaxMulti];
-  int d_out[kMaxMulti];
+  const void* y0[kApplyMaxMulti];
+  const float* z[kApplyMaxMulti];
+  void* y[kApplyMaxMulti];
+  int d_out[kApplyMaxMulti];
   const int32_t* inv;
-  int N, k, copy_y0[kMaxMulti], copy_z[kMaxMulti];
+  int N, k, copy_y0[kApplyMaxMulti], copy_z[kApplyMaxMulti];
 };
 template <int RB, bool INDIRECT>
 __global__ __launch_bounds__(256) void shrink_grouped_multi(ShrinkMulti m) {
@@ -1500,72 +1252,6 @@ __global__ __launch_bounds__(256) void expand_tokens(ExpandArgs a) {
 // --------------------------------------------------------------------------------------
 // host side
 
-int apply_resolve_path(int N, int k, int path, int K, int r_pad) {
-  if (path != 0) return path;
-  const long long P = (long long)N * k;
-  // few, small adapters: tile-local.  Ranks <= 32: grouped (faster than the split-reduction
-  // skinny path at every decode batch measured, 1 .. 2048 tokens).  Ranks above 32: the 64-row
-  // grouped tiles from 1024 pairs on; below that their serial per-tile pipeline is slower than
-  // the skinny path's split reductions (the 64-token blocks give too few workgroups there).
-  if (K <= kT8MaxU && r_pad <= 32 && P >= 192) return 3;
-  if (r_pad <= 32) return 1;
-  return P >= 1024 ? 1 : 2;
-}
-
-static int skinny_splits(int d_in) {
-  const int S = d_in / kStepK;  // steps of 128
-  int ns = S / 4;               // 512 reduction elements per split
-  if (ns < 1) ns = 1;
-  if (ns > 16) ns = 16;
-  return ns;
-}
-
-// Block path workspace: the partial sums of the shrink launch.
-static size_t block_ws(int N, int k, int K, int r_pad, int d_in) {
-  const int nblocks = (N + kBTok - 1) / kBTok;
-  const int kslices = (d_in + kBSlice - 1) / kBSlice;
-  const int slotmax = std::min(K, kBTok * k);
-  return block_part_floats(nblocks, slotmax, kslices, r_pad) * sizeof(float);
-}
-
-static size_t split_ws_bytes(int N, int d_in, int r_pad);
-static size_t split_ctrl_bytes(int N);
-size_t step_ws_bytes(int N, int K, int r_pad, int d_in) {
-  (void)K;
-  return split_ws_bytes(N, d_in, r_pad);
-}
-
-// Grouped path on 64-row tiles: used for k > 1 (passes over ranked slots) or ranks above 32.
-// k > 1 workspace: the slot sort (counts and offsets in a 256-byte block, then the order and
-// the weights, then the per-workgroup counts of a chip-wide sort), then, for a bf16 y, the
-// fp32 pass buffer z [N][d_out].
-static bool use_gm(int k, int K, int r_pad) { return (k > 1 && k * K <= 64) || (k == 1 && r_pad > 32); }
-static size_t gm_head_bytes(int k, int K) { return ((size_t)(2 * k * K + 1) * sizeof(int32_t) + 255) / 256 * 256; }
-static size_t gm_order_bytes(long long P) { return ((size_t)P * (sizeof(int32_t) + sizeof(float)) + 255) / 256 * 256; }
-static size_t gm_sort_bytes(long long P, int k, int K) {
-  return gm_head_bytes(k, K) + gm_order_bytes(P) + (dispatch_ws_bytes(P, k * K) + 255) / 256 * 256;
-}
-static size_t gm_ws_bytes(int N, int k, int K, int d_out, bool y_f32) {
-  if (k == 1) return 0;
-  return gm_sort_bytes((long long)N * k, k, K) + (y_f32 ? 0 : (size_t)N * d_out * sizeof(float));
-}
-
-size_t apply_ws_bytes(int N, int k, int K, int r_pad, int d_in, int d_out, bool y_f32, int path) {
-  const int p = apply_resolve_path(N, k, path, K, r_pad);
-  if (p == 4) return block_ws(N, k, K, r_pad, d_in);
-  if (p == 1 && use_gm(k, K, r_pad)) return gm_ws_bytes(N, k, K, d_out, y_f32);
-  if (p == 3 || (k == 1 && p == 1)) return 0;
-  const int ns = (p == 2) ? skinny_splits(d_in) : 1;
-  const size_t hpart = ((size_t)ns * (size_t)N * (size_t)k * (size_t)r_pad * sizeof(float) + 255) / 256 * 256;
-  if (p == 2 && k > 1 && k * K <= 64) return hpart + gm_ws_bytes(N, k, K, d_out, y_f32);  // rank passes
-  return hpart;
-}
-
-static int env_int(const char* name, int dflt) {
-  const char* s = getenv(name);
-  return (s && *s) ? atoi(s) : dflt;
-}
-
 // Column groups: enough workgroups to cover the chip while every wave keeps output blocks.
 static int choose_col_groups(long long tiles, int d_out, int target_blocks, int min_blocks_per_group) {
   const int nblk = d_out / kColBlock;
@@ -1575,18 +1261,16 @@ static int choose_col_groups(long long tiles, int d_out, int target_blocks, int 
 }
 
 static int col_groups_for(int requested, long long tiles, int d_out, int target, int minb) {
-  int cg = requested > 0 ? requested : env_int("MOLORA_APPLY_COLGROUPS", 0);
-  if (cg <= 0 || (d_out / kColBlock) % cg != 0) cg = choose_col_groups(tiles, d_out, target, minb);
-  return cg;
+  if (requested > 0 && (d_out / kColBlock) % requested == 0) return requested;
+  return choose_col_groups(tiles, d_out, target, minb);
 }
 
 // Column groups of the 8-token tiles: more workgroups while there are fewer tiles than compute
 // units, as long as every wave of a group keeps a 256-column unit.
 static int t8_col_groups(int requested, long long tiles, int d_out) {
   const int nblk = d_out / kColBlock;
-  int cg = requested > 0 ? requested : env_int("MOLORA_APPLY_COLGROUPS", 0);
-  if (cg > 0 && nblk % cg == 0) return cg;
-  cg = 1;
+  if (requested > 0 && nblk % requested == 0) return requested;
+  int cg = 1;
   while (tiles * cg < 256 && nblk % (2 * cg) == 0 && nblk / (2 * cg) >= 2 * kT8Waves) cg *= 2;
   return cg;
 }
@@ -1595,10 +1279,11 @@ static BlockArgs block_args(const ApplyLaunch& a, void* ws) {
   BlockArgs b;
   b.tgt = a.tgt; b.x = a.x; b.y0 = a.y0; b.y = a.y;
   b.N = a.N; b.K = a.K; b.k = a.k; b.scale = a.scale;
-  b.nblocks = (a.N + kBTok - 1) / kBTok;
-  b.kslices = (a.tgt.d_in + kBSlice - 1) / kBSlice;
-  b.cslices = (a.tgt.d_out + kBSlice - 1) / kBSlice;
-  b.slotmax = std::min(a.K, kBTok * a.k);
+  const BlockGeom g = block_geom(a.N, a.k, a.K, a.tgt.d_in, a.tgt.d_out);
+  b.nblocks = g.nblocks;
+  b.kslices = g.kslices;
+  b.cslices = g.cslices;
+  b.slotmax = g.slotmax;
   b.part = reinterpret_cast<float*>(ws);
   return b;
 }
@@ -1654,38 +1339,10 @@ static hipError_t launch_block_t(const BlockApplyArgs& ba, hipStream_t s) {
                      ba);
   return hipGetLastError();
 }
-// Split step workspace: control words of the fused launch (the header, then one flag per
-// (block, slice)), which must be zero before the first call, then the partials.
-static size_t split_ctrl_bytes(int N) {
-  const size_t nblocks = (N + kSTok - 1) / kSTok;
-  return 256 + (nblocks * kSMaxSlices * sizeof(unsigned) + 255) / 256 * 256;
-}
-static size_t split_ws_bytes(int N, int d_in, int r_pad) {
-  return split_ctrl_bytes(N) + split_part_floats(N, d_in, r_pad) * sizeof(float);
-}
-
 template <int RB, bool IND, bool Y0F, bool YF>
-static hipError_t launch_split_t(const StepArgs& sa, const SplitGeom& g, void* ctrl, hipStream_t s) {
+static hipError_t launch_split_t(const StepArgs& sa, const SplitGeom& g, hipStream_t s) {
   const int nb8 = 8 * ((g.nblocks + 7) / 8);
-  const int SL = std::max(g.kslices, g.cslices);
   const bool allb = RB == 1 && sa.t.K <= split_group<1>();
-  // the fused single launch is opt-in: its publish-and-wait costs more than the launch boundary
-  // it removes (4-modality step: 17.8 us fused against 15.0 us in two launches)
-  if (env_int("MOLORA_SPLIT_FUSED", 0) != 0 && SL <= kSMaxSlices) {
-    FusedHdr* hdr = reinterpret_cast<FusedHdr*>(ctrl);
-    unsigned* flags = reinterpret_cast<unsigned*>(reinterpret_cast<char*>(ctrl) + 256);
-    const int spin = env_int("MOLORA_SPLIT_SPIN", 20000);
-    if constexpr (RB == 1) {
-      if (allb) {
-        hipLaunchKernelGGL((split_fused<RB, IND, Y0F, YF, true>), dim3(nb8 * SL), dim3(kSThreads), 0, s, sa, g, hdr,
-                           flags, spin);
-        return hipGetLastError();
-      }
-    }
-    hipLaunchKernelGGL((split_fused<RB, IND, Y0F, YF, false>), dim3(nb8 * SL), dim3(kSThreads), 0, s, sa, g, hdr, flags,
-                       spin);
-    return hipGetLastError();
-  }
   hipLaunchKernelGGL((split_shrink<RB, IND>), dim3(nb8 * g.kslices), dim3(kSThreads), 0, s, sa, g);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -1721,23 +1378,20 @@ static hipError_t launch_expand_tok_t(const ExpandArgs& ea, int grid, hipStream_
 #define MOLORA_DISPATCH_BOOL(V, NAME, ...) \
   if (V) { constexpr bool NAME = true; __VA_ARGS__; } else { constexpr bool NAME = false; __VA_ARGS__; }
 
-// Rank sort of the grouped pairs for k > 1 passes, in the workspace at wsb: counts2 and offsets2
-// (256-byte block), perm2 and w2 (the order and weights), the chip-wide sort's counts; z is the
-// fp32 carry of the passes (y itself when y is fp32, else the buffer after the sort).
+// Rank sort of the grouped pairs for k > 1 passes, in the region of rank_sort_plan() at wsb
+// (counts2 and offsets2, perm2 and w2 = the order and weights, the chip-wide sort's counts).
 struct RankSort {
   int32_t* offsets2;
   int32_t* perm2;
   float* w2;
-  float* z;
 };
 static hipError_t launch_rank_sort(const ApplyLaunch& a, char* wsb, long long P, hipStream_t s, RankSort& o) {
-  int32_t* counts2 = reinterpret_cast<int32_t*>(wsb);
-  o.offsets2 = counts2 + a.k * a.K;
-  const size_t head = gm_head_bytes(a.k, a.K);
-  o.perm2 = reinterpret_cast<int32_t*>(wsb + head);
-  o.w2 = reinterpret_cast<float*>(wsb + head + (size_t)P * sizeof(int32_t));
-  int32_t* bcnt = reinterpret_cast<int32_t*>(wsb + head + gm_order_bytes(P));
-  o.z = a.y_f32 ? reinterpret_cast<float*>(a.y) : reinterpret_cast<float*>(wsb + gm_sort_bytes(P, a.k, a.K));
+  const RankSortPlan rp = rank_sort_plan(P, a.k, a.K);
+  int32_t* counts2 = reinterpret_cast<int32_t*>(wsb + rp.counts2_off);
+  o.offsets2 = reinterpret_cast<int32_t*>(wsb + rp.offsets2_off);
+  o.perm2 = reinterpret_cast<int32_t*>(wsb + rp.perm2_off);
+  o.w2 = reinterpret_cast<float*>(wsb + rp.w2_off);
+  int32_t* bcnt = reinterpret_cast<int32_t*>(wsb + rp.bcnt_off);
   const DispatchSplit ds = dispatch_split(P);
   if (ds.nb > 1) {
     hipLaunchKernelGGL(slot_hist, dim3(ds.nb), dim3(1024), 0, s, a.offsets, a.perm, a.perm_w, a.inv, a.k, a.K, ds.C,
@@ -1755,6 +1409,10 @@ static hipError_t launch_rank_sort(const ApplyLaunch& a, char* wsb, long long P,
 
 hipError_t launch_apply(const ApplyLaunch& a, hipStream_t s) {
   const long long P = (long long)a.N * a.k;
+  const ApplyPlan plan = apply_plan(a.N, a.k, a.K, a.tgt.r_pad, a.tgt.d_in, a.tgt.d_out, a.y_f32, a.path);
+  char* const wsb = reinterpret_cast<char*>(a.ws);
+  // fp32 carry of the k > 1 passes: y itself when y is fp32, else the plan's buffer
+  float* const zbuf = a.y_f32 ? reinterpret_cast<float*>(a.y) : reinterpret_cast<float*>(wsb + plan.z_off);
   const int RBv = a.tgt.r_pad / 16;
   const long long tiles = P / kTileRows + a.K + 1;  // upper bound on tiles of any grouping
   const bool in_place = (a.y0 == a.y);
@@ -1772,7 +1430,7 @@ hipError_t launch_apply(const ApplyLaunch& a, hipStream_t s) {
 
   if (a.path == 4) {
     BlockApplyArgs ba;
-    ba.b = block_args(a, a.ws);
+    ba.b = block_args(a, wsb + plan.block_off);
     ba.offsets = a.offsets; ba.perm_w = a.perm_w; ba.inv = a.inv;
     MOLORA_DISPATCH_RB(RBv, MOLORA_DISPATCH_BOOL(a.indirect, IND, MOLORA_DISPATCH_BOOL(a.y0_f32, Y0F,
         MOLORA_DISPATCH_BOOL(a.y_f32, YF, err = (launch_block_t<RB, IND, Y0F, YF>(ba, s))))));
@@ -1816,12 +1474,12 @@ hipError_t launch_apply(const ApplyLaunch& a, hipStream_t s) {
       return err;
     }
     RankSort rs;
-    err = launch_rank_sort(a, reinterpret_cast<char*>(a.ws), P, s, rs);
+    err = launch_rank_sort(a, wsb + plan.sort_off, P, s, rs);
     if (err != hipSuccess) return err;
     int32_t* offsets2 = rs.offsets2;
     int32_t* perm2 = rs.perm2;
     float* w2 = rs.w2;
-    float* z = rs.z;
+    float* z = zbuf;
     ga.offsets = offsets2; ga.order = perm2; ga.wts = w2;
     for (int j = 0; j < a.k; ++j) {
       ga.key0 = j * a.K;
@@ -1855,13 +1513,14 @@ hipError_t launch_apply(const ApplyLaunch& a, hipStream_t s) {
   const int nsplit = (a.path == 2) ? skinny_splits(a.tgt.d_in) : 1;
   ShrinkArgs sa;
   sa.tgt = a.tgt; sa.x = a.x; sa.offsets = a.offsets; sa.perm = a.perm; sa.perm_w = a.perm_w;
-  sa.K = a.K; sa.k = a.k; sa.scale = a.scale; sa.hpart = a.ws; sa.P = P; sa.nsplit = nsplit;
+  sa.K = a.K; sa.k = a.k; sa.scale = a.scale; sa.P = P; sa.nsplit = nsplit;
+  sa.hpart = reinterpret_cast<float*>(wsb + plan.hpart_off);
   MOLORA_DISPATCH_RB(RBv, MOLORA_DISPATCH_BOOL(a.indirect, IND, err = (launch_shrink_t<RB, IND>(sa, (int)tiles, s))));
   if (err != hipSuccess) return err;
 
   ExpandArgs ea;
   ea.tgt = a.tgt; ea.y0 = a.y0; ea.y = a.y; ea.offsets = a.offsets; ea.perm = a.perm; ea.inv = a.inv;
-  ea.hpart = a.ws; ea.P = P; ea.nsplit = nsplit; ea.N = a.N; ea.K = a.K; ea.k = a.k;
+  ea.hpart = sa.hpart; ea.P = P; ea.nsplit = nsplit; ea.N = a.N; ea.K = a.K; ea.k = a.k;
   ea.order = nullptr;
   ea.key0 = 0;
   if (a.k == 1) {
@@ -1876,9 +1535,8 @@ hipError_t launch_apply(const ApplyLaunch& a, hipStream_t s) {
   if (a.path == 2 && a.k * a.K <= 64) {
     // one grouped expand pass per rank of the routed pairs (as on the 64-row tiles), over
     // (adapter, 16-row tile, column group) workgroups, the sum carried in fp32
-    const size_t hpart = ((size_t)nsplit * (size_t)P * (size_t)a.tgt.r_pad * sizeof(float) + 255) / 256 * 256;
     RankSort rs;
-    err = launch_rank_sort(a, reinterpret_cast<char*>(a.ws) + hpart, P, s, rs);
+    err = launch_rank_sort(a, wsb + plan.sort_off, P, s, rs);
     if (err != hipSuccess) return err;
     const long long ptiles = (a.N + 15) / 16 + a.K;  // 16-row tiles of one pass
     ea.offsets = rs.offsets2;
@@ -1890,17 +1548,17 @@ hipError_t launch_apply(const ApplyLaunch& a, hipStream_t s) {
     for (int j = 0; j < a.k; ++j) {
       const bool last = j == a.k - 1;
       ea.key0 = j * a.K;
-      ea.y0 = j == 0 ? a.y0 : static_cast<const void*>(rs.z);
-      ea.y = last ? a.y : static_cast<void*>(rs.z);
+      ea.y0 = j == 0 ? a.y0 : static_cast<const void*>(zbuf);
+      ea.y = last ? a.y : static_cast<void*>(zbuf);
       const bool y0f = j == 0 ? (bool)a.y0_f32 : true, yf = last ? (bool)a.y_f32 : true;
       MOLORA_DISPATCH_RB(RBv, MOLORA_DISPATCH_BOOL(a.indirect, IND, MOLORA_DISPATCH_BOOL(y0f, Y0F,
           MOLORA_DISPATCH_BOOL(yf, YF, err = (launch_expand_k1_t<RB, IND, Y0F, YF>(ea, grid, s))))));
       if (err != hipSuccess) return err;
     }
-    const bool copy_z = static_cast<void*>(rs.z) != a.y;
+    const bool copy_z = static_cast<void*>(zbuf) != a.y;
     if (in_place && !copy_z) return err;
     MOLORA_DISPATCH_BOOL(a.y0_f32, Y0F, MOLORA_DISPATCH_BOOL(a.y_f32, YF,
-        err = (launch_finish_t<Y0F, YF>(a.y0, rs.z, a.y, a.inv, a.N, a.k, a.tgt.d_out, !in_place, copy_z, s))));
+        err = (launch_finish_t<Y0F, YF>(a.y0, zbuf, a.y, a.inv, a.N, a.k, a.tgt.d_out, !in_place, copy_z, s))));
     return err;
   }
   const long long ttiles = (a.N + 15) / 16;
@@ -1921,51 +1579,27 @@ hipError_t launch_apply(const ApplyLaunch& a, hipStream_t s) {
 // Several targets sharing one routing.  The skinny path runs each phase for all targets in one
 // launch (the rank sort once); other paths apply the targets in turn, each with its own slice of
 // the workspace.  Workspace: [rank sort] then per target [h partials][fp32 carry].
-static size_t align256(size_t b) { return (b + 255) / 256 * 256; }
-static bool multi_fused(int p, int k, int K) { return p == 2 && (k == 1 || k * K <= 64); }
-
-// AUTO for several targets: as for one, except that tile-local applies with k > 1 become the
-// 64-token blocks, whose two launches then cover every target (measured faster on a 7-target
-// layer with top-2 routing).
-int apply_multi_resolve_path(int n, int N, int k, int path, int K, int r_pad) {
-  const int p = apply_resolve_path(N, k, path, K, r_pad);
-  return (path == 0 && p == 3 && k > 1 && n > 1) ? 4 : p;
-}
-
-size_t apply_multi_ws_bytes(int n, const int* d_in, const int* d_out, int N, int k, int K, int r_pad, bool y_f32,
-                            int path) {
-  const int p = apply_multi_resolve_path(n, N, k, path, K, r_pad);
-  size_t b = 0;
-  if (!multi_fused(p, k, K)) {
-    for (int i = 0; i < n; ++i) b += align256(apply_ws_bytes(N, k, K, r_pad, d_in[i], d_out[i], y_f32, p));
-    return b;
-  }
-  const long long P = (long long)N * k;
-  if (k > 1) b += align256(gm_sort_bytes(P, k, K));
-  for (int i = 0; i < n; ++i) {
-    b += align256((size_t)skinny_splits(d_in[i]) * (size_t)P * (size_t)r_pad * sizeof(float));
-    if (k > 1 && !y_f32) b += align256((size_t)N * d_out[i] * sizeof(float));
-  }
-  return b;
-}
-
 hipError_t launch_apply_multi(const ApplyLaunch* as, int n, hipStream_t s) {
   const ApplyLaunch& a0 = as[0];
   hipError_t err = hipSuccess;
   char* wsb = reinterpret_cast<char*>(a0.ws);
+  int d_in[kApplyMaxMulti], d_out[kApplyMaxMulti];
+  for (int i = 0; i < n; ++i) {
+    d_in[i] = as[i].tgt.d_in;
+    d_out[i] = as[i].tgt.d_out;
+  }
+  const MultiPlan mp = apply_multi_plan(n, d_in, d_out, a0.N, a0.k, a0.K, a0.tgt.r_pad, a0.y_f32, a0.path);
   if (a0.path == 4) {
     // 64-token blocks: one shrink launch and one expand launch for all targets
-    static_assert(sizeof(BlockMulti) / sizeof(BlockApplyArgs) == kMaxMulti, "multi size");
+    static_assert(sizeof(BlockMulti) / sizeof(BlockApplyArgs) == kApplyMaxMulti, "multi size");
     BlockMulti bm;
-    size_t off = 0;
     int gs = 1, ge = 1;
     for (int i = 0; i < n; ++i) {
       const ApplyLaunch& b = as[i];
-      bm.a[i].b = block_args(b, wsb + off);
+      bm.a[i].b = block_args(b, wsb + mp.tgt_off[i]);
       bm.a[i].offsets = b.offsets;
       bm.a[i].perm_w = b.perm_w;
       bm.a[i].inv = b.inv;
-      off += align256(apply_ws_bytes(b.N, b.k, b.K, b.tgt.r_pad, b.tgt.d_in, b.tgt.d_out, b.y_f32, b.path));
       gs = std::max(gs, block_grid(bm.a[i].b.nblocks, bm.a[i].b.kslices));
       ge = std::max(ge, block_grid(bm.a[i].b.nblocks, bm.a[i].b.cslices));
     }
@@ -1979,12 +1613,10 @@ hipError_t launch_apply_multi(const ApplyLaunch* as, int n, hipStream_t s) {
             hipLaunchKernelGGL((expand_block_multi<RB, IND, Y0F, YF>), dim3(ge, n), dim3(kBThreads), 0, s, bm)))));
     return hipGetLastError();
   }
-  if (!multi_fused(a0.path, a0.k, a0.K)) {
-    size_t off = 0;
+  if (!mp.fused) {
     for (int i = 0; i < n; ++i) {
       ApplyLaunch b = as[i];
-      b.ws = reinterpret_cast<float*>(wsb + off);
-      off += align256(apply_ws_bytes(b.N, b.k, b.K, b.tgt.r_pad, b.tgt.d_in, b.tgt.d_out, b.y_f32, b.path));
+      b.ws = reinterpret_cast<float*>(wsb + mp.tgt_off[i]);
       err = launch_apply(b, s);
       if (err != hipSuccess) return err;
     }
@@ -1993,22 +1625,17 @@ hipError_t launch_apply_multi(const ApplyLaunch* as, int n, hipStream_t s) {
   const long long P = (long long)a0.N * a0.k;
   const long long tiles = P / kTileRows + a0.K + 1;
   const int RBv = a0.tgt.r_pad / 16;
-  size_t off = a0.k > 1 ? align256(gm_sort_bytes(P, a0.k, a0.K)) : 0;
   ShrinkMulti sm;
-  float* z[kMaxMulti];
+  float* z[kApplyMaxMulti];
   int max_split = 1;
   for (int i = 0; i < n; ++i) {
     const ApplyLaunch& a = as[i];
     ShrinkArgs& sa = sm.a[i];
     sa.tgt = a.tgt; sa.x = a.x; sa.offsets = a.offsets; sa.perm = a.perm; sa.perm_w = a.perm_w;
     sa.K = a.K; sa.k = a.k; sa.scale = a.scale; sa.P = P; sa.nsplit = skinny_splits(a.tgt.d_in);
-    sa.hpart = reinterpret_cast<float*>(wsb + off);
-    off += align256((size_t)sa.nsplit * (size_t)P * (size_t)a.tgt.r_pad * sizeof(float));
+    sa.hpart = reinterpret_cast<float*>(wsb + mp.hpart_off[i]);
     z[i] = a.y_f32 ? reinterpret_cast<float*>(a.y) : nullptr;
-    if (a.k > 1 && !a.y_f32) {
-      z[i] = reinterpret_cast<float*>(wsb + off);
-      off += align256((size_t)a.N * a.tgt.d_out * sizeof(float));
-    }
+    if (a.k > 1 && !a.y_f32) z[i] = reinterpret_cast<float*>(wsb + mp.z_off[i]);
     max_split = std::max(max_split, sa.nsplit);
   }
   MOLORA_DISPATCH_RB(RBv, MOLORA_DISPATCH_BOOL(a0.indirect, IND,
@@ -2044,7 +1671,7 @@ hipError_t launch_apply_multi(const ApplyLaunch* as, int n, hipStream_t s) {
   }
   // k > 1: the rank sort once (shared routing), then one pass per rank over all targets
   RankSort rs;
-  err = launch_rank_sort(a0, wsb, P, s, rs);
+  err = launch_rank_sort(a0, wsb + mp.sort_off, P, s, rs);
   if (err != hipSuccess) return err;
   const long long ptiles = (a0.N + 15) / 16 + a0.K;
   int gx = 1;
@@ -2087,8 +1714,6 @@ hipError_t launch_apply_multi(const ApplyLaunch* as, int n, hipStream_t s) {
   return hipGetLastError();
 }
 
-bool step_vocab_fused(int N) { return N <= kStepMaxN; }
-
 hipError_t launch_step_vocab(const StepVocabLaunch& a, hipStream_t s) {
   StepArgs sa;
   sa.t = t8_args(a.apply);
@@ -2098,6 +1723,7 @@ hipError_t launch_step_vocab(const StepVocabLaunch& a, hipStream_t s) {
   for (int i = 0; i < kT8MaxU - 1; ++i) sa.bounds.mid[i] = (i + 1 < K) ? a.bounds.b[i + 1] : INT_MAX;
   sa.ids = a.ids; sa.idx = a.idx; sa.w = a.w; sa.counts = a.counts; sa.offsets = a.offsets; sa.perm = a.perm;
   sa.perm_w = a.perm_w; sa.inv = a.inv;
+  sa.dispatch_share = a.dispatch_share ? 1 : 0;
   const int RBv = a.apply.tgt.r_pad / 16;
   hipError_t err = hipSuccess;
   if (a.ws != nullptr) {
@@ -2105,9 +1731,9 @@ hipError_t launch_step_vocab(const StepVocabLaunch& a, hipStream_t s) {
     g.nblocks = (a.apply.N + kSTok - 1) / kSTok;
     g.kslices = (a.apply.tgt.d_in + kSSlice - 1) / kSSlice;
     g.cslices = (a.apply.tgt.d_out + kSSlice - 1) / kSSlice;
-    g.part = reinterpret_cast<float*>(reinterpret_cast<char*>(a.ws) + split_ctrl_bytes(a.apply.N));
+    g.part = reinterpret_cast<float*>(a.ws);
     MOLORA_DISPATCH_RB(RBv, MOLORA_DISPATCH_BOOL(a.apply.indirect, IND, MOLORA_DISPATCH_BOOL(a.apply.y0_f32, Y0F,
-        MOLORA_DISPATCH_BOOL(a.apply.y_f32, YF, err = (launch_split_t<RB, IND, Y0F, YF>(sa, g, a.ws, s))))));
+        MOLORA_DISPATCH_BOOL(a.apply.y_f32, YF, err = (launch_split_t<RB, IND, Y0F, YF>(sa, g, s))))));
     return err;
   }
   const int grid = 8 * sa.t.tiles_per_xcd * sa.t.col_groups;

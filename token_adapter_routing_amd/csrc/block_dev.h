@@ -24,8 +24,6 @@
 
 namespace molora {
 
-constexpr int kBTok = 64;         // tokens per block
-constexpr int kBSlice = 512;      // reduction or output columns per workgroup
 constexpr int kBWaves = 8;
 constexpr int kBThreads = kBWaves * kWave;
 constexpr int kBMaxU = 16;        // adapters per block (K <= 16)
@@ -48,10 +46,6 @@ struct BlockArgs {
   int slotmax;   // partial slots per block: min(K, 64 k)
   float* part;   // [nblocks][slotmax][kslices][64][r_pad] fp32
 };
-
-__host__ __device__ inline size_t block_part_floats(int nblocks, int slotmax, int kslices, int r_pad) {
-  return (size_t)nblocks * slotmax * kslices * kBTok * r_pad;
-}
 
 template <int RB>
 struct BlockLds {
@@ -177,7 +171,7 @@ __device__ void block_shrink(const BlockArgs& a, BlockLds<RB>& L, const Route& r
         for (int i = 0; i < 4; ++i) L.red[kh][rb][4 * G + i][u * 16 + n] = acc[u][i];
       __syncthreads();
       const int slot = base + g;
-      float* dst = a.part + ((((size_t)tb * a.slotmax + slot) * a.kslices + sl) * kBTok) * r_pad;
+      float* dst = a.part + block_part_index(tb, slot, sl, a.slotmax, a.kslices, r_pad);
       for (int v = threadIdx.x; v < kBTok * RB * 16; v += kBThreads) {
         const int tok = v / (RB * 16), rk = v % (RB * 16);
         const int rbv = tok >> 4, rw = tok & 15;
@@ -249,7 +243,7 @@ __device__ void block_expand(const BlockArgs& a, BlockLds<RB>& L, const Route& r
     for (int v = threadIdx.x; v < ng * kBTok * RB * 4; v += kBThreads) {
       const int g = v / (kBTok * RB * 4), vi = v % (kBTok * RB * 4);
       const int tok = vi / (RB * 4), rk = 4 * (vi % (RB * 4));
-      const float* src = a.part + (((size_t)tb * a.slotmax + base + g) * a.kslices * kBTok + tok) * r_pad + rk;
+      const float* src = a.part + block_part_index(tb, base + g, 0, a.slotmax, a.kslices, r_pad) + (size_t)tok * r_pad + rk;
       float sum[4] = {0.f, 0.f, 0.f, 0.f};
       for (int s0 = 0; s0 < a.kslices; s0 += KS) {
         u32x4_t pv[KS];

@@ -375,7 +375,7 @@ int molora_apply_multi_workspace(const molora_hotset* hs, int n, const int* targ
   if (N < 0 || k < 1 || k > MOLORA_MAX_TOPK || k > hs->K) return fail(MOLORA_EINVAL, "bad N=%d or k=%d", N, k);
   if (path < MOLORA_PATH_AUTO || path > MOLORA_PATH_BLOCK) return fail(MOLORA_EINVAL, "unknown path %d", path);
   if (y_dtype != MOLORA_BF16 && y_dtype != MOLORA_F32) return fail(MOLORA_EINVAL, "unknown dtype");
-  *bytes = molora::apply_multi_ws_bytes(n, d_in, d_out, N, k, hs->K, hs->r_pad, y_dtype == MOLORA_F32, path);
+  *bytes = molora::apply_multi_plan(n, d_in, d_out, N, k, hs->K, hs->r_pad, y_dtype == MOLORA_F32, path).total;
   return ok();
 }
 
@@ -408,7 +408,8 @@ int molora_apply_multi(const molora_hotset* hs, int n, const int* targets, const
     return fail(MOLORA_EINVAL, "offsets, perm, perm_w and inv are required");
   if (!aligned(offsets, 4) || !aligned(perm, 4) || !aligned(perm_w, 4) || !aligned(inv, 4))
     return fail(MOLORA_EINVAL, "misaligned pointer");
-  const size_t need = molora::apply_multi_ws_bytes(n, d_in, d_out, N, k, hs->K, hs->r_pad, y_dtype == MOLORA_F32, path);
+  const size_t need =
+      molora::apply_multi_plan(n, d_in, d_out, N, k, hs->K, hs->r_pad, y_dtype == MOLORA_F32, path).total;
   if (need > 0 && (ws == nullptr || ws_bytes < need || !aligned(ws, 256)))
     return fail(MOLORA_ENOSPC, "workspace of %zu bytes (256-byte aligned) needed, %zu given", need, ws_bytes);
   molora::ApplyLaunch as[molora::kApplyMaxMulti];
@@ -444,7 +445,7 @@ int molora_step_workspace(const molora_hotset* hs, int target, int N, size_t* by
   if (hs == nullptr) return fail(MOLORA_EINVAL, "hot set is NULL");
   if (target < 0 || target >= hs->n_targets) return fail(MOLORA_EINVAL, "target %d outside [0, %d)", target, hs->n_targets);
   if (N < 0) return fail(MOLORA_EINVAL, "N=%d < 0", N);
-  *bytes = molora::step_ws_bytes(N, hs->K, hs->r_pad, hs->tg[target].d_in);
+  *bytes = molora::step_plan(N, hs->K, hs->r_pad, hs->tg[target].d_in).total;
   return ok();
 }
 
@@ -474,11 +475,9 @@ int molora_step_vocab(const molora_hotset* hs, int target, const int32_t* ids, i
   if (!aligned(ids, 4) || !aligned(idx, 4) || !aligned(w, 4) || !aligned(counts, 4) || !aligned(offsets, 4) ||
       !aligned(perm, 4) || !aligned(perm_w, 4) || !aligned(inv, 4))
     return fail(MOLORA_EINVAL, "misaligned pointer");
-  if (ws != nullptr) {
-    const size_t need = molora::step_ws_bytes(N, hs->K, hs->r_pad, hs->tg[target].d_in);
-    if (ws_bytes < need || !aligned(ws, 256))
-      return fail(MOLORA_ENOSPC, "step workspace of %zu bytes (256-byte aligned) needed, %zu given", need, ws_bytes);
-  }
+  const molora::StepPlan plan = molora::step_plan(N, hs->K, hs->r_pad, hs->tg[target].d_in);
+  if (ws != nullptr && (ws_bytes < plan.total || !aligned(ws, 256)))
+    return fail(MOLORA_ENOSPC, "step workspace of %zu bytes (256-byte aligned) needed, %zu given", plan.total, ws_bytes);
   molora::ApplyLaunch& a = st.apply;
   a.tgt = hs->tg[target];
   a.indirect = hs->layout == MOLORA_LAYOUT_INDIRECT;
@@ -495,10 +494,11 @@ int molora_step_vocab(const molora_hotset* hs, int target, const int32_t* ids, i
   a.perm = perm;
   a.perm_w = perm_w;
   a.inv = inv;
-  a.path = ws != nullptr ? 4 : 3;
-  a.ws = reinterpret_cast<float*>(ws);
+  a.path = molora::kPathTile;
+  a.ws = nullptr;
   a.col_groups = 0;
-  st.ws = ws;
+  st.ws = ws != nullptr ? static_cast<char*>(ws) + plan.part_off : nullptr;
+  st.dispatch_share = true;
   st.ids = ids;
   st.idx = idx;
   st.w = w;
@@ -508,13 +508,26 @@ int molora_step_vocab(const molora_hotset* hs, int target, const int32_t* ids, i
   st.perm_w = perm_w;
   st.inv = inv;
   const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  if (molora::step_vocab_fused(N)) {
+  if (N <= molora::kStepMaxN) {  // one or two launches that also route and write the dispatch outputs
     const hipError_t e = molora::launch_step_vocab(st, s);
     return e == hipSuccess ? ok() : hip_fail(e, "step launch");
   }
+  // Above kStepMaxN tokens the routing and the dispatch run as launches of their own (chip-wide
+  // with a workspace, else one workgroup); then the split launches apply (same arithmetic, so y
+  // is bit-identical at every N), or, without a workspace, the tile path.
+  char* wsb = static_cast<char*>(ws);
+  void* dws = (ws != nullptr && plan.disp_bytes > 0) ? wsb + plan.disp_off : nullptr;
   hipError_t e = molora::launch_route_vocab(ids, N, st.bounds, hs->K, idx, w, s);
-  if (e == hipSuccess) e = molora::launch_dispatch(idx, w, N, hs->K, counts, offsets, perm, perm_w, inv, nullptr, s);
-  if (e == hipSuccess) e = molora::launch_apply(a, s);
+  if (e == hipSuccess) e = molora::launch_dispatch(idx, w, N, hs->K, counts, offsets, perm, perm_w, inv, dws, s);
+  if (e == hipSuccess) {
+    if (ws != nullptr) {
+      st.ws = wsb + plan.part_off;
+      st.dispatch_share = false;
+      e = molora::launch_step_vocab(st, s);
+    } else {
+      e = molora::launch_apply(a, s);
+    }
+  }
   return e == hipSuccess ? ok() : hip_fail(e, "step launch");
 }
 

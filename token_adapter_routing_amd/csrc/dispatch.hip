@@ -46,22 +46,6 @@ __global__ __launch_bounds__(kDispThreads) void dispatch_scatter(const int32_t* 
   dispatch_scatter_part<kDispThreads>(L, ArraySource{idx, w}, P, K, C, nb, bcnt, counts, offsets, perm, perm_w, inv);
 }
 
-// Pairs per workgroup of the chip-wide sort: whole 8192-pair chunks, at most 128 workgroups.
-DispatchSplit dispatch_split(long long P) {
-  DispatchSplit d{1, (int)P};
-  if (P <= kDispChunk) return d;
-  long long C = (P + kDispMaxParts - 1) / kDispMaxParts;
-  C = (C + kDispChunk - 1) / kDispChunk * kDispChunk;
-  d.C = (int)C;
-  d.nb = (int)((P + C - 1) / C);
-  return d;
-}
-
-size_t dispatch_ws_bytes(long long P, int K) {
-  const DispatchSplit d = dispatch_split(P);
-  return d.nb > 1 ? (size_t)d.nb * K * sizeof(int32_t) : 0;
-}
-
 hipError_t launch_dispatch(const int32_t* idx, const float* w, int P, int K, int32_t* counts, int32_t* offsets,
                            int32_t* perm, float* perm_w, int32_t* inv, void* ws, hipStream_t s) {
   const DispatchSplit d = dispatch_split(P);

@@ -39,8 +39,6 @@ struct DispatchLds {
   int wcnt[kDispMaxE * NW * 64];
 };
 
-constexpr int kDispChunk = 8192;  // pairs per pass of one 1024-thread workgroup (8 per thread)
-
 // Pairs c0 + j*NT + tid (j < E, below c1) from the source: adapter (outside [0, K) = unrouted)
 // and gate weight; missing pairs get -1.
 template <int NT, typename Src>

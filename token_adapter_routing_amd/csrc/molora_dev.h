@@ -13,27 +13,13 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "molora_plan.h"
+
 namespace molora {
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
 typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4_t;
-
-constexpr int kWave = 64;
-constexpr int kTileRows = 16;    // rows (pairs) per MFMA tile
-constexpr int kStepK = 128;      // reduction elements one wave consumes per shrink step
-constexpr int kColBlock = 128;   // output columns one wave produces per expand block
-
-// Per-target adapter addressing, as the kernels see it.
-struct TargetDev {
-  const uint16_t* At;            // direct: A^T of adapter 0, [r_pad][d_in] bf16
-  const uint16_t* Bt;            // direct: B^T of adapter 0, [d_out][r_pad] bf16
-  long long strideA;             // elements between consecutive adapters' A^T
-  long long strideB;             // elements between consecutive adapters' B^T
-  const uint16_t* const* ptrA;   // indirect: device table of K A^T addresses
-  const uint16_t* const* ptrB;   // indirect: device table of K B^T addresses
-  int d_in, d_out, r_pad;
-};
 
 template <bool INDIRECT>
 __device__ __forceinline__ const uint16_t* adapter_A(const TargetDev& t, int e) {

@@ -1,0 +1,135 @@
+// Sizes and placements shared by the host launchers and the kernels: tile constants, the
+// workspace layout of every path, and the index formulas the kernels write partial sums with.
+// Plain C++ without HIP types, so the host-side arithmetic also builds for a CPU-only test
+// (under AddressSanitizer / UndefinedBehaviorSanitizer) that checks every workspace a kernel
+// writes against the bytes the entry points require.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__HIP__)
+#define MOLORA_HD __host__ __device__
+#else
+#define MOLORA_HD
+#endif
+
+namespace molora {
+
+constexpr int kWave = 64;
+constexpr int kTileRows = 16;    // rows (pairs) per MFMA tile
+constexpr int kStepK = 128;      // reduction elements one wave consumes per shrink step
+constexpr int kColBlock = 128;   // output columns one wave produces per expand block
+
+constexpr int kBTok = 64;        // block path: tokens per block
+constexpr int kBSlice = 512;     // block path: reduction or output columns per workgroup
+constexpr int kSTok = 64;        // split step: tokens per block
+constexpr int kSSlice = 512;     // split step: reduction or output columns per workgroup
+constexpr int kStepMaxN = 4096;  // the vocabulary step's fused launches handle N <= this
+constexpr int kDispChunk = 8192; // pairs one 1024-thread dispatch workgroup sorts per pass
+constexpr int kDispMaxParts = 128;
+constexpr int kApplyTileMaxAdapters = 16;  // tile and block paths: distinct adapters (K <= 16)
+constexpr int kApplyMaxMulti = 8;          // targets of one molora_apply_multi call
+
+enum { kPathAuto = 0, kPathGrouped = 1, kPathSkinny = 2, kPathTile = 3, kPathBlock = 4 };
+
+// Per-target adapter addressing, as the kernels see it.
+struct TargetDev {
+  const uint16_t* At;            // direct: A of adapter 0 in the slab's swizzled layout
+  const uint16_t* Bt;            // direct: B^T of adapter 0, [d_out][r_pad] bf16
+  long long strideA;             // elements between consecutive adapters' A
+  long long strideB;             // elements between consecutive adapters' B^T
+  const uint16_t* const* ptrA;   // indirect: device table of K A addresses
+  const uint16_t* const* ptrB;   // indirect: device table of K B^T addresses
+  int d_in, d_out, r_pad;
+};
+
+inline size_t align256(size_t b) { return (b + 255) / 256 * 256; }
+
+// ---- dispatch: above kDispChunk pairs the sort runs over nb workgroups of C pairs each, whose
+// per-adapter counts ([nb][K] int32) live in the workspace.
+struct DispatchSplit {
+  int nb, C;
+};
+DispatchSplit dispatch_split(long long P);
+size_t dispatch_ws_bytes(long long P, int K);
+
+// ---- block path: partial sums of the shrink launch, [nblocks][slotmax][kslices][64][r_pad]
+// fp32; (tb, slot, sl) starts at block_part_index and holds 64 rows of r_pad floats.
+MOLORA_HD inline size_t block_part_index(int tb, int slot, int sl, int slotmax, int kslices, int r_pad) {
+  return ((((size_t)tb * slotmax + slot) * kslices + sl) * kBTok) * r_pad;
+}
+MOLORA_HD inline size_t block_part_floats(int nblocks, int slotmax, int kslices, int r_pad) {
+  return (size_t)nblocks * slotmax * kslices * kBTok * r_pad;
+}
+struct BlockGeom {
+  int nblocks, kslices, cslices, slotmax;
+};
+BlockGeom block_geom(int N, int k, int K, int d_in, int d_out);
+size_t block_ws_bytes(int N, int k, int K, int r_pad, int d_in);
+
+// ---- split step (vocabulary routing, k = 1): partial h of every token on its own adapter,
+// [nblocks][kslices][64][r_pad] fp32; (tb, sl) starts at split_part_index.
+MOLORA_HD inline size_t split_part_index(int tb, int sl, int kslices, int r_pad) {
+  return (((size_t)tb * kslices + sl) * kSTok) * r_pad;
+}
+MOLORA_HD inline size_t split_part_floats(int N, int d_in, int r_pad) {
+  return (size_t)((N + kSTok - 1) / kSTok) * ((d_in + kSSlice - 1) / kSSlice) * kSTok * r_pad;
+}
+
+// Workspace of molora_step_vocab with a workspace: the split launches' partials at part_off.
+// N <= kStepMaxN: those launches also write the dispatch outputs (fused_dispatch).  Larger N:
+// route and a chip-wide dispatch (its per-workgroup counts at disp_off) run first.
+struct StepPlan {
+  bool fused_dispatch;
+  size_t disp_off, disp_bytes;
+  size_t part_off, part_bytes;
+  size_t total;
+};
+StepPlan step_plan(int N, int K, int r_pad, int d_in);
+
+// ---- apply paths
+int apply_resolve_path(int N, int k, int path, int K, int r_pad);
+int apply_multi_resolve_path(int n, int N, int k, int path, int K, int r_pad);
+int skinny_splits(int d_in);
+// 64-row grouped tiles (r > 32, or k > 1 with k*K <= 64)
+bool use_gm(int k, int K, int r_pad);
+
+// Rank sort of k > 1 (grouped and skinny paths): counts2 [k*K] and offsets2 [k*K+1] in a
+// 256-byte-aligned head, then perm2 [P] int32 and w2 [P] fp32, then the chip-wide sort's
+// per-workgroup counts; offsets relative to the start of the sort's region.
+struct RankSortPlan {
+  size_t counts2_off, offsets2_off, perm2_off, w2_off, bcnt_off, bytes;
+};
+RankSortPlan rank_sort_plan(long long P, int k, int K);
+
+// Workspace of one molora_apply on a resolved path: [skinny/grouped h partials][rank sort][z],
+// where z is the fp32 [N][d_out] carry of the k > 1 passes when y is bf16.
+struct ApplyPlan {
+  int path;
+  size_t hpart_off, hpart_bytes;  // shrink partials ([nsplit][P][r_pad] fp32), two-kernel paths
+  size_t block_off, block_bytes;  // block path partials
+  size_t sort_off;                // rank sort region (k > 1 on the grouped / skinny passes)
+  RankSortPlan sort;
+  size_t z_off, z_bytes;          // fp32 carry
+  size_t total;
+};
+ApplyPlan apply_plan(int N, int k, int K, int r_pad, int d_in, int d_out, bool y_f32, int path);
+size_t apply_ws_bytes(int N, int k, int K, int r_pad, int d_in, int d_out, bool y_f32, int path);
+
+// Workspace of molora_apply_multi (n targets sharing one routing): on the fused skinny path
+// [rank sort][per target: h partials, z]; otherwise one apply_plan region per target.
+struct MultiPlan {
+  int path;
+  bool fused;
+  size_t sort_off;
+  RankSortPlan sort;
+  size_t tgt_off[kApplyMaxMulti];   // start of target i's region
+  size_t hpart_off[kApplyMaxMulti]; // fused: its h partials
+  size_t z_off[kApplyMaxMulti];     // fused: its fp32 carry (bf16 y, k > 1), else 0
+  size_t total;
+};
+MultiPlan apply_multi_plan(int n, const int* d_in, const int* d_out, int N, int k, int K, int r_pad, bool y_f32,
+                           int path);
+
+}  // namespace molora

@@ -1,0 +1,159 @@
+// Host-side sizes and placements of every workspace (declared in molora_plan.h).  Plain C++:
+// the library builds it with the kernels, and a CPU-only test builds it with the sanitizers.
+#include "molora_plan.h"
+
+#include <algorithm>
+
+namespace molora {
+
+DispatchSplit dispatch_split(long long P) {
+  DispatchSplit d{1, (int)P};
+  if (P <= kDispChunk) return d;
+  long long C = (P + kDispMaxParts - 1) / kDispMaxParts;
+  C = (C + kDispChunk - 1) / kDispChunk * kDispChunk;
+  d.C = (int)C;
+  d.nb = (int)((P + C - 1) / C);
+  return d;
+}
+
+size_t dispatch_ws_bytes(long long P, int K) {
+  const DispatchSplit d = dispatch_split(P);
+  return d.nb > 1 ? (size_t)d.nb * K * sizeof(int32_t) : 0;
+}
+
+BlockGeom block_geom(int N, int k, int K, int d_in, int d_out) {
+  BlockGeom g;
+  g.nblocks = (N + kBTok - 1) / kBTok;
+  g.kslices = (d_in + kBSlice - 1) / kBSlice;
+  g.cslices = (d_out + kBSlice - 1) / kBSlice;
+  g.slotmax = std::min(K, kBTok * k);
+  return g;
+}
+
+size_t block_ws_bytes(int N, int k, int K, int r_pad, int d_in) {
+  const BlockGeom g = block_geom(N, k, K, d_in, kBSlice);
+  return block_part_floats(g.nblocks, g.slotmax, g.kslices, r_pad) * sizeof(float);
+}
+
+StepPlan step_plan(int N, int K, int r_pad, int d_in) {
+  StepPlan p{};
+  p.fused_dispatch = N <= kStepMaxN;
+  p.disp_off = 0;
+  p.disp_bytes = p.fused_dispatch ? 0 : dispatch_ws_bytes(N, K);
+  p.part_off = align256(p.disp_bytes);
+  p.part_bytes = split_part_floats(N, d_in, r_pad) * sizeof(float);
+  p.total = p.part_off + p.part_bytes;
+  return p;
+}
+
+int apply_resolve_path(int N, int k, int path, int K, int r_pad) {
+  if (path != kPathAuto) return path;
+  const long long P = (long long)N * k;
+  // few, small adapters: tile-local.  Ranks <= 32: grouped.  Ranks above 32: the 64-row
+  // grouped tiles from 1024 pairs on; below that their serial per-tile pipeline is slower than
+  // the skinny path's split reductions (the 64-token blocks give too few workgroups there).
+  if (K <= kApplyTileMaxAdapters && r_pad <= 32 && P >= 192) return kPathTile;
+  if (r_pad <= 32) return kPathGrouped;
+  return P >= 1024 ? kPathGrouped : kPathSkinny;
+}
+
+// AUTO for several targets: as for one, except that tile-local applies with k > 1 become the
+// 64-token blocks, whose two launches then cover every target.
+int apply_multi_resolve_path(int n, int N, int k, int path, int K, int r_pad) {
+  const int p = apply_resolve_path(N, k, path, K, r_pad);
+  return (path == kPathAuto && p == kPathTile && k > 1 && n > 1) ? kPathBlock : p;
+}
+
+int skinny_splits(int d_in) {
+  int ns = (d_in / kStepK) / 4;  // 512 reduction elements per split
+  if (ns < 1) ns = 1;
+  if (ns > 16) ns = 16;
+  return ns;
+}
+
+bool use_gm(int k, int K, int r_pad) { return (k > 1 && k * K <= 64) || (k == 1 && r_pad > 32); }
+
+RankSortPlan rank_sort_plan(long long P, int k, int K) {
+  RankSortPlan s{};
+  s.counts2_off = 0;
+  s.offsets2_off = (size_t)k * K * sizeof(int32_t);
+  const size_t head = align256((size_t)(2 * k * K + 1) * sizeof(int32_t));
+  s.perm2_off = head;
+  s.w2_off = head + (size_t)P * sizeof(int32_t);
+  s.bcnt_off = head + align256((size_t)P * (sizeof(int32_t) + sizeof(float)));
+  s.bytes = s.bcnt_off + align256(dispatch_ws_bytes(P, k * K));
+  return s;
+}
+
+ApplyPlan apply_plan(int N, int k, int K, int r_pad, int d_in, int d_out, bool y_f32, int path) {
+  ApplyPlan a{};
+  a.path = apply_resolve_path(N, k, path, K, r_pad);
+  const long long P = (long long)N * k;
+  const size_t zb = y_f32 ? 0 : (size_t)N * d_out * sizeof(float);
+  if (a.path == kPathBlock) {
+    a.block_bytes = block_ws_bytes(N, k, K, r_pad, d_in);
+    a.total = a.block_bytes;
+    return a;
+  }
+  if (a.path == kPathGrouped && use_gm(k, K, r_pad)) {
+    if (k == 1) return a;
+    a.sort_off = 0;
+    a.sort = rank_sort_plan(P, k, K);
+    a.z_off = a.sort.bytes;
+    a.z_bytes = zb;
+    a.total = a.z_off + a.z_bytes;
+    return a;
+  }
+  if (a.path == kPathTile || (k == 1 && a.path == kPathGrouped)) return a;
+  const int ns = a.path == kPathSkinny ? skinny_splits(d_in) : 1;
+  a.hpart_off = 0;
+  a.hpart_bytes = align256((size_t)ns * (size_t)P * (size_t)r_pad * sizeof(float));
+  a.total = a.hpart_bytes;
+  if (a.path == kPathSkinny && k > 1 && k * K <= 64) {  // one expand pass per rank of the pairs
+    a.sort_off = a.hpart_bytes;
+    a.sort = rank_sort_plan(P, k, K);
+    a.z_off = a.sort_off + a.sort.bytes;
+    a.z_bytes = zb;
+    a.total = a.z_off + a.z_bytes;
+  }
+  return a;
+}
+
+size_t apply_ws_bytes(int N, int k, int K, int r_pad, int d_in, int d_out, bool y_f32, int path) {
+  return apply_plan(N, k, K, r_pad, d_in, d_out, y_f32, path).total;
+}
+
+MultiPlan apply_multi_plan(int n, const int* d_in, const int* d_out, int N, int k, int K, int r_pad, bool y_f32,
+                           int path) {
+  MultiPlan m{};
+  m.path = apply_multi_resolve_path(n, N, k, path, K, r_pad);
+  m.fused = m.path == kPathSkinny && (k == 1 || k * K <= 64);
+  size_t off = 0;
+  if (!m.fused) {
+    for (int i = 0; i < n; ++i) {
+      m.tgt_off[i] = off;
+      off += align256(apply_ws_bytes(N, k, K, r_pad, d_in[i], d_out[i], y_f32, m.path));
+    }
+    m.total = off;
+    return m;
+  }
+  const long long P = (long long)N * k;
+  if (k > 1) {
+    m.sort_off = 0;
+    m.sort = rank_sort_plan(P, k, K);
+    off = align256(m.sort.bytes);
+  }
+  for (int i = 0; i < n; ++i) {
+    m.tgt_off[i] = off;
+    m.hpart_off[i] = off;
+    off += align256((size_t)skinny_splits(d_in[i]) * (size_t)P * (size_t)r_pad * sizeof(float));
+    if (k > 1 && !y_f32) {
+      m.z_off[i] = off;
+      off += align256((size_t)N * d_out[i] * sizeof(float));
+    }
+  }
+  m.total = off;
+  return m;
+}
+
+}  // namespace molora

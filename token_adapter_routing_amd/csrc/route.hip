@@ -21,6 +21,13 @@
 
 namespace molora {
 
+// Copy the K+1 bounds from kernel arguments into LDS (static indices only).
+__device__ __forceinline__ void bounds_to_lds(const VocabBounds& vb, int* lds, int K) {
+#pragma unroll
+  for (int i = 0; i < 65; ++i)
+    if ((int)threadIdx.x == i && i <= K) lds[i] = vb.b[i];
+}
+
 __global__ __launch_bounds__(256) void route_vocab_k(const int32_t* __restrict__ ids, int N, VocabBounds b,
                                                      int K, int32_t* __restrict__ idx, float* __restrict__ w) {
   __shared__ int bl[65];
