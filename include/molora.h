@@ -313,6 +313,28 @@ int molora_step_vocab(const molora_hotset *hs, int target, const int32_t *ids, i
                       void *ws, size_t ws_bytes, void *stream);
 
 /* ------------------------------------------------------------------------
+ * molora_step_vocab with a workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same arguments minus ws / ws_bytes, the same
+ * launches and bit-identical results.  The workspace is a scratch array of
+ * MOLORA_NOALLOC_SCRATCH_BYTES compiled into the library, one per GPU, held
+ * until the process ends; its address on the current device is looked up
+ * once (in molora_hotset_init, else on the first call on that device).  The
+ * call allocates nothing.  Every call on a GPU shares that GPU's array:
+ * calls that overlap on one GPU (several streams, several host threads) race
+ * and must be serialised by the caller.  The array needs no initial
+ * contents; it keeps the last call's partial sums.
+ * Errors: a step whose molora_step_workspace() exceeds the array ->
+ * MOLORA_ENOSPC (nothing enqueued); otherwise as molora_step_vocab.
+ * ------------------------------------------------------------------------ */
+#define MOLORA_NOALLOC_SCRATCH_BYTES (8u << 20)
+int molora_step_vocab_noalloc(const molora_hotset *hs, int target, const int32_t *ids, int N,
+                              const int32_t *bounds, const void *x, const void *y0,
+                              int y0_dtype, void *y, int y_dtype, int32_t *idx, float *w,
+                              int32_t *counts, int32_t *offsets, int32_t *perm, float *perm_w,
+                              int32_t *inv, void *stream);
+
+/* ------------------------------------------------------------------------
  * Per-sequence comparator metadata (thelatestinai.com, Table 3: per-sequence
  * routing needs K passes for a K-modality batch; the abstract: work K*N
  * versus N).  From a k = 1 routing idx [N], builds K one-hot dispatches: pass e

@@ -185,6 +185,16 @@ hipError_t launch_step_vocab(const StepVocabLaunch& a, hipStream_t) {
                         "split partials");
   return hipSuccess;
 }
+static char* g_scratch = nullptr;  // host stand-in of the device scratch array
+hipError_t scratch_setup(void** out) {
+  if (g_scratch == nullptr) {
+    void* p = nullptr;
+    if (posix_memalign(&p, 256, kScratchBytes) != 0) return hipErrorOutOfMemory;
+    g_scratch = static_cast<char*>(p);
+  }
+  if (out != nullptr) *out = g_scratch;
+  return hipSuccess;
+}
 hipError_t launch_seqpass_meta(const int32_t*, int, int, int32_t*, int32_t*, float*, hipStream_t) {
   ++g_launches;
   return hipSuccess;
@@ -444,7 +454,39 @@ static void test_validation() {
   CHECK(g_launches == l0 + 4, "launches during validation: %d", g_launches - l0);  // init: one relayout per adapter
 }
 
+// The allocation-free step: workspace from the scratch stand-in (exactly kScratchBytes), size
+// limit enforced before anything is launched.
+static void test_noalloc() {
+  HostHotset h;
+  if (!make_hotset(h, 4, 16, {{4096, 4096}}, MOLORA_LAYOUT_DIRECT)) return;
+  int32_t bounds[5] = {0, 8192, 16384, 24576, 32768};
+  void* sp = nullptr;
+  CHECK(scratch_setup(&sp) == hipSuccess, "scratch stand-in");
+  for (int N : {1, 2048, 4096, 4097, 8192, 16383, 16384, 65536}) {
+    const StepPlan plan = step_plan(N, 4, 16, 4096);
+    g_ws_base = static_cast<char*>(sp);
+    g_ws_bytes = kScratchBytes;
+    g_ranges.clear();
+    const int l0 = g_launches;
+    const int rc = molora_step_vocab_noalloc(h.hs, 0, (int32_t*)fake(0x1000), N, bounds, fake(0x2000), fake(0x3000),
+                                             MOLORA_BF16, fake(0x4000), MOLORA_BF16, (int32_t*)fake(0x5000),
+                                             (float*)fake(0x6000), (int32_t*)fake(0x7000), (int32_t*)fake(0x8000),
+                                             (int32_t*)fake(0x9000), (float*)fake(0xa000), (int32_t*)fake(0xb000),
+                                             nullptr);
+    if (plan.total <= kScratchBytes) {
+      CHECK(rc == MOLORA_OK, "noalloc N=%d", N);
+      check_disjoint("noalloc");
+    } else {
+      CHECK(rc == MOLORA_ENOSPC && g_launches == l0 && std::strstr(molora_last_error(), "scratch") != nullptr,
+            "noalloc N=%d above the scratch size accepted", N);
+    }
+  }
+  g_ws_base = nullptr;
+  molora_hotset_destroy(h.hs);
+}
+
 int main() {
+  test_noalloc();
   test_validation();
   test_dispatch();
   for (int layout : {MOLORA_LAYOUT_DIRECT, MOLORA_LAYOUT_INDIRECT})
@@ -464,6 +506,7 @@ int main() {
     for (int k : {1, 2})
       for (int N : {1, 256, 4096})
         for (int yd : {MOLORA_BF16, MOLORA_F32}) test_multi(4, 16, N, k, path, yd);
+  free(g_scratch);
   fprintf(stderr, "%d checks, %d failures\n", g_checks, g_fail);
   return g_fail == 0 ? 0 : 1;
 }

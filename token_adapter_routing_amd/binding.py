@@ -59,7 +59,11 @@ _SIGS = {
                                  _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p,  # idx, w, counts, offsets, perm, perm_w, inv
                                  _c_p, _c_sz, _c_p]),  # ws, ws_bytes, stream
     "molora_step_workspace": (_c_i, [_c_p, _c_i, _c_i, ctypes.POINTER(_c_sz)]),
+    "molora_step_vocab_noalloc": (_c_i, [_c_p, _c_i, _c_p, _c_i, _c_p, _c_p, _c_p, _c_i, _c_p, _c_i,  # hs .. y_dtype
+                                         _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p,  # idx .. inv
+                                         _c_p]),  # stream
 }
+NOALLOC_SCRATCH_BYTES = 8 << 20
 
 _lib = None
 
@@ -371,6 +375,36 @@ def molora_step_vocab(hs: HotSet, ids: torch.Tensor, bounds: Sequence[int], x: t
         _ptr(w, torch.float32, "w"), _ptr(counts, torch.int32, "counts"), _ptr(offsets, torch.int32, "offsets"),
         _ptr(perm, torch.int32, "perm"), _ptr(perm_w, torch.float32, "perm_w"), _ptr(inv, torch.int32, "inv"),
         _ptr(ws, None, "ws") if ws is not None else None, ws.numel() if ws is not None else 0, _stream(stream)))
+    return y, route, meta
+
+
+def molora_step_vocab_noalloc(hs: HotSet, ids: torch.Tensor, bounds: Sequence[int], x: torch.Tensor,
+                              y0: torch.Tensor, target: int = 0, y: Optional[torch.Tensor] = None, y_dtype=None,
+                              route=None, meta=None, stream=None):
+    """molora_step_vocab with the library's own device scratch instead of a caller workspace
+    (the entry point allocates nothing).  Outputs that are not supplied are allocated here, by
+    torch, before the call; pass all of them to keep the call allocation-free."""
+    N = ids.numel()
+    K = len(bounds) - 1
+    dev = ids.device
+    d_out = hs.dims[target][1]
+    if y is None:
+        y = torch.empty(N, d_out, dtype=y_dtype or y0.dtype, device=dev)
+    if route is None:
+        route = (torch.empty(max(N, 1), dtype=torch.int32, device=dev), torch.empty(max(N, 1), dtype=torch.float32, device=dev))
+    if meta is None:
+        meta = (torch.empty(K, dtype=torch.int32, device=dev), torch.empty(K + 1, dtype=torch.int32, device=dev),
+                torch.empty(max(N, 1), dtype=torch.int32, device=dev), torch.empty(max(N, 1), dtype=torch.float32, device=dev),
+                torch.empty(max(N, 1), dtype=torch.int32, device=dev))
+    b = (ctypes.c_int32 * len(bounds))(*[int(v) for v in bounds])
+    idx, w = route
+    counts, offsets, perm, perm_w, inv = meta
+    _check(load_library().molora_step_vocab_noalloc(
+        hs.handle, target, _ptr(ids, torch.int32, "ids"), N, ctypes.cast(b, _c_p), _ptr(x, torch.bfloat16, "x"),
+        _ptr(y0, None, "y0"), _dtype_code(y0), _ptr(y, None, "y"), _dtype_code(y), _ptr(idx, torch.int32, "idx"),
+        _ptr(w, torch.float32, "w"), _ptr(counts, torch.int32, "counts"), _ptr(offsets, torch.int32, "offsets"),
+        _ptr(perm, torch.int32, "perm"), _ptr(perm_w, torch.float32, "perm_w"), _ptr(inv, torch.int32, "inv"),
+        _stream(stream)))
     return y, route, meta
 
 

@@ -38,6 +38,8 @@
 #include <algorithm>
 #include <climits>
 #include <cstdlib>
+#include <mutex>
+#include <vector>
 
 #include "dispatch_dev.h"
 #include "molora_launch.h"
@@ -1803,6 +1805,35 @@ hipError_t launch_seqpass_meta(const int32_t* idx, int N, int K, int32_t* offset
   hipLaunchKernelGGL(seqpass_meta, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, idx, N, K, offsets, perm,
                      perm_w);
   return hipGetLastError();
+}
+
+// --------------------------------------------------------------------------------------
+// Scratch memory of the entry points that allocate nothing: a file-scope device array, one copy
+// per GPU, held until the process ends.  Host code never passes the array's name to a kernel
+// (on the host it is only a stand-in symbol); it takes each device's address once with
+// hipGetSymbolAddress, with that device current, and passes that address.
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+std::mutex g_scratch_mu;
+std::vector<void*> g_scratch_addr;  // per device ordinal; nullptr until looked up
+}  // namespace
+
+hipError_t scratch_setup(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if ((size_t)dev >= g_scratch_addr.size()) g_scratch_addr.resize((size_t)dev + 1, nullptr);
+  if (g_scratch_addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_addr[dev] = p;
+  }
+  if (out != nullptr) *out = g_scratch_addr[dev];
+  return hipSuccess;
 }
 
 }  // namespace molora

@@ -13,6 +13,8 @@
 #include "../../include/molora.h"
 #include "molora_launch.h"
 
+static_assert(MOLORA_NOALLOC_SCRATCH_BYTES == molora::kScratchBytes, "scratch size in the header and the library");
+
 struct molora_hotset {
   int K = 0, r = 0, r_pad = 0, layout = 0, n_targets = 0;
   float scale = 1.f;
@@ -196,7 +198,9 @@ int molora_hotset_init(molora_hotset** out, int K, int r, float scale, int n_tar
       hs->slotB.back().push_back(const_cast<uint16_t*>(static_cast<const uint16_t*>(tablesB[t][e])));
     }
   }
-  const hipError_t err = hipStreamSynchronize(s);  // host tables above must outlive the copies
+  hipError_t err = hipStreamSynchronize(s);  // host tables above must outlive the copies
+  // this device's scratch array (molora_step_vocab_noalloc), looked up once per device here
+  if (err == hipSuccess) err = molora::scratch_setup(nullptr);
   if (err != hipSuccess) {
     delete hs;
     return hip_fail(err, "hot-set init");
@@ -529,6 +533,24 @@ int molora_step_vocab(const molora_hotset* hs, int target, const int32_t* ids, i
     }
   }
   return e == hipSuccess ? ok() : hip_fail(e, "step launch");
+}
+
+int molora_step_vocab_noalloc(const molora_hotset* hs, int target, const int32_t* ids, int N, const int32_t* bounds,
+                              const void* x, const void* y0, int y0_dtype, void* y, int y_dtype, int32_t* idx,
+                              float* w, int32_t* counts, int32_t* offsets, int32_t* perm, float* perm_w,
+                              int32_t* inv, void* stream) {
+  if (hs == nullptr) return fail(MOLORA_EINVAL, "hot set is NULL");
+  if (target < 0 || target >= hs->n_targets) return fail(MOLORA_EINVAL, "target %d outside [0, %d)", target, hs->n_targets);
+  if (N < 0) return fail(MOLORA_EINVAL, "N=%d < 0", N);
+  const molora::StepPlan plan = molora::step_plan(N, hs->K, hs->r_pad, hs->tg[target].d_in);
+  if (plan.total > molora::kScratchBytes)
+    return fail(MOLORA_ENOSPC, "this step needs %zu bytes of scratch; the allocation-free step holds %zu", plan.total,
+                molora::kScratchBytes);
+  void* scratch = nullptr;
+  const hipError_t e = molora::scratch_setup(&scratch);
+  if (e != hipSuccess) return hip_fail(e, "scratch lookup");
+  return molora_step_vocab(hs, target, ids, N, bounds, x, y0, y0_dtype, y, y_dtype, idx, w, counts, offsets, perm,
+                           perm_w, inv, scratch, molora::kScratchBytes, stream);
 }
 
 int molora_seqpass_meta(const int32_t* idx, int N, int K, int32_t* offsets, int32_t* perm, float* perm_w, void* stream) {

@@ -68,6 +68,10 @@ struct StepVocabLaunch {
 };
 hipError_t launch_step_vocab(const StepVocabLaunch& a, hipStream_t s);
 
+// The calling thread's current device's scratch array (kScratchBytes, 256-byte aligned): looked
+// up once per device with hipGetSymbolAddress, then cached.  out may be NULL (set-up only).
+hipError_t scratch_setup(void** out);
+
 hipError_t launch_seqpass_meta(const int32_t* idx, int N, int K, int32_t* offsets, int32_t* perm,
                                float* perm_w, hipStream_t s);
 

@@ -30,6 +30,8 @@ constexpr int kDispChunk = 8192; // pairs one 1024-thread dispatch workgroup sor
 constexpr int kDispMaxParts = 128;
 constexpr int kApplyTileMaxAdapters = 16;  // tile and block paths: distinct adapters (K <= 16)
 constexpr int kApplyMaxMulti = 8;          // targets of one molora_apply_multi call
+constexpr size_t kScratchBytes = size_t(8) << 20;  // device scratch of the allocation-free step
+                                                   // (MOLORA_NOALLOC_SCRATCH_BYTES)
 
 enum { kPathAuto = 0, kPathGrouped = 1, kPathSkinny = 2, kPathTile = 3, kPathBlock = 4 };
 
