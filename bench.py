@@ -177,30 +177,32 @@ def main():
                 fn(s)
         return g
 
-    reps = max(1, args.steps // S)
-    steps = reps * S
-    wreps = max(1, args.warmup // S)
+    K_steps, W_steps = max(1, args.steps), max(0, args.warmup)
 
-    def time_graph(g):
-        with torch.cuda.stream(stream):
-            for _ in range(wreps):
-                g.replay()
-        torch.cuda.synchronize()
+    def time_steps(fn):
+        """Exactly W_steps untimed steps, then exactly K_steps timed steps, each run as one HIP
+        graph that cycles through the S buffer sets (step i uses set i mod S); HIP events on the
+        launch stream bracket the timed graph.  Returns (ms per step, wall seconds)."""
+        if W_steps:
+            gw = graph_of(fn, [i % S for i in range(W_steps)])
+            with torch.cuda.stream(stream):
+                gw.replay()
+            torch.cuda.synchronize()
+            del gw
+        g = graph_of(fn, [i % S for i in range(K_steps)])
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         with torch.cuda.stream(stream):
             e0.record(stream)
-            for _ in range(reps):
-                g.replay()
+            g.replay()
             e1.record(stream)
         torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / steps, time.perf_counter() - t0
+        return e0.elapsed_time(e1) / K_steps, time.perf_counter() - t0
 
-    # ---------------- timed region (headline): `steps` one-launch steps
-    g_all = graph_of(step, range(S))
-    ms_per_step, wall = time_graph(g_all)
+    # ---------------- timed region (headline): exactly `steps` split steps
+    ms_per_step, wall = time_steps(step)
     value = N / (ms_per_step * 1e-3)
 
     # ---------------- the step's kernels (split_shrink + split_expand): their time per step is the
@@ -215,7 +217,7 @@ def main():
     kernel_gbs = step_bytes / (kernel_us * 1e-6) / 1e9
 
     # ---------------- step latency percentiles over single-step graph replays
-    g_one = [graph_of(step, [s]) for s in range(S)]
+    g_one = [graph_of(step, [s_]) for s_ in range(S)]
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(args.latency_reps)]
     with torch.cuda.stream(stream):
@@ -234,8 +236,8 @@ def main():
         "value": value,
         "unit": "routed tokens/s",
         "n_gpus": 1,
-        "steps": steps,
-        "warmup": wreps * S,
+        "steps": K_steps,
+        "warmup": W_steps,
         "ms_per_step": ms_per_step,
         "higher_is_better": True,
         "scaling": "weak",
@@ -244,7 +246,7 @@ def main():
         "data": "synthetic (seeded; modality runs, bf16 N(0,1) activations, LoRA A~N(0,1/d), B~N(0,1/r))",
         "config": {"workload": "4-modality vocab routing N=2048 d=4096 K=4 r=16 k=1", "N": N, "d": d_in, "K": K,
                    "r": r, "k": k, "alpha_over_r": case.scale, "buffer_sets": S,
-                   "launch": "hipGraph, one step per buffer set",
+                   "launch": "one hipGraph of `steps` steps cycling through the buffer sets",
                    "step": "molora_step_vocab with a workspace (split_shrink: routing, 512-wide d_in slices, "
                            "dispatch outputs; split_expand: 512-wide output slices)"},
         "step_roofline_frac": step_bytes / (ms_per_step * 1e-3) / (HBM_PEAK_GBS * 1e9),
@@ -258,8 +260,8 @@ def main():
 
     if not args.no_extras:
         # the one-launch step (tile apply) and three launches per step (route_vocab, dispatch, apply)
-        ms1, _ = time_graph(graph_of(step1, range(S)))
-        ms3, _ = time_graph(graph_of(step3, range(S)))
+        ms1, _ = time_steps(step1)
+        ms3, _ = time_steps(step3)
         # per-sequence comparator: K masked dense passes over all N tokens (metadata from the routing)
         seq = []
         for s in range(S):
@@ -275,7 +277,7 @@ def main():
             for e in range(1, K):
                 m.molora_apply(hs, b["x"], b["y"], offs[e], perm, pw[e], perm, k=1, y=b["y"], path=m.PATH_GROUPED)
 
-        seq_ms, _ = time_graph(graph_of(seq_step, range(S)))
+        seq_ms, _ = time_steps(seq_step)
         out["one_launch_tile_step"] = {"ms_per_step": ms1, "routed_tokens_per_s": N / (ms1 * 1e-3)}
         out["three_launch_step"] = {"ms_per_step": ms3, "routed_tokens_per_s": N / (ms3 * 1e-3)}
         out["per_sequence_comparator"] = {"ms_per_step": seq_ms, "passes": K,
@@ -283,12 +285,13 @@ def main():
 
     rows = [r for r in args.rows.split(",") if r and r != "none"]
     if rows:
-        del sets, g_all, g_one
+        del sets, g_one
         torch.cuda.synchronize()
         out["rows"] = measure_rows(m, torch, dev, rows, args.row_reps, args.stack_replays)
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
+        out["cpu_baseline_1core"] = cpu_baseline(case, args.cpu_seconds, threads=1)
     print(json.dumps(out))
 
 
@@ -725,32 +728,39 @@ def row_stack(m, torch, dev, layers=28, B=256, K=16, r=64, k=2, replays=1000):
     return out
 
 
-def cpu_baseline(case, seconds):
+def cpu_baseline(case, seconds, threads=None):
     """The CPU oracle as it stands (fp64 numpy), timed on this host on the same workload:
-    route_vocab -> dispatch -> apply for the full batch, repeated for about `seconds`."""
+    route_vocab -> dispatch -> apply for the full batch, repeated for about `seconds`, with the
+    BLAS pool at `threads` threads (None: as configured, normally all cores)."""
+    import contextlib
     from oracle import apply, bf16_to_f64, dispatch, route_vocab
     t = case.targets[0]
     x, A, B, y0 = (bf16_to_f64(v) for v in (t.x, t.A, t.B, t.y0))  # conversion excluded
     try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        threads = os.cpu_count()
+        from threadpoolctl import threadpool_info, threadpool_limits
+    except Exception:  # pragma: no cover - threadpoolctl is installed here
+        threadpool_info = threadpool_limits = None
+    limit = threadpool_limits(limits=threads) if (threads and threadpool_limits) else contextlib.nullcontext()
+    with limit:
+        if threadpool_info is not None:
+            used = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        else:
+            used = threads or os.cpu_count()
 
-    def one():
-        idx, w = route_vocab(case.ids, case.bounds)
-        counts, offsets, perm, perm_w, inv = dispatch(idx, w, case.K)
-        return apply(y0, x, A, B, case.scale, perm, perm_w, offsets, 1)
+        def one():
+            idx, w = route_vocab(case.ids, case.bounds)
+            counts, offsets, perm, perm_w, inv = dispatch(idx, w, case.K)
+            return apply(y0, x, A, B, case.scale, perm, perm_w, offsets, 1)
 
-    one()  # warm-up
-    times = []
-    t_end = time.perf_counter() + seconds
-    while time.perf_counter() < t_end or len(times) < 3:
-        a = time.perf_counter()
-        one()
-        times.append(time.perf_counter() - a)
+        one()  # warm-up
+        times = []
+        t_end = time.perf_counter() + seconds
+        while time.perf_counter() < t_end or len(times) < 3:
+            a = time.perf_counter()
+            one()
+            times.append(time.perf_counter() - a)
     med = statistics.median(times)
-    return {"value": case.N / med, "unit": "routed tokens/s", "cores": threads, "kind": "oracle",
+    return {"value": case.N / med, "unit": "routed tokens/s", "cores": used, "kind": "oracle",
             "sample": f"full batch (N={case.N}) route+dispatch+apply, {len(times)} runs, median {med * 1e3:.1f} ms",
             "host_cpus": len(os.sched_getaffinity(0))}
 

@@ -176,13 +176,17 @@ hipError_t launch_step_vocab(const StepVocabLaunch& a, hipStream_t) {
   ++g_launches;
   CHECK(a.apply.N <= kStepMaxN || !a.dispatch_share, "fused dispatch share above %d tokens (N=%d)", kStepMaxN,
         a.apply.N);
-  if (a.ws == nullptr) return hipSuccess;  // the one-launch tile step writes no workspace
+  if (a.part == nullptr) return hipSuccess;  // the one-launch tile step writes no workspace
   const int nblocks = (a.apply.N + kSTok - 1) / kSTok;
   const int kslices = (a.apply.tgt.d_in + kSSlice - 1) / kSSlice;
   for (int tb = 0; tb < nblocks; ++tb)
     for (int sl = 0; sl < kslices; ++sl)
-      write_span<float>(a.ws, split_part_index(tb, sl, kslices, a.apply.tgt.r_pad), (size_t)kSTok * a.apply.tgt.r_pad,
+      write_span<float>(a.part, split_part_index(tb, sl, kslices, a.apply.tgt.r_pad), (size_t)kSTok * a.apply.tgt.r_pad,
                         "split partials");
+  if (a.dispatch_share) {  // the first launch's per-block adapter counts
+    CHECK(a.bcnt != nullptr, "per-block counts buffer missing");
+    if (a.bcnt != nullptr) write_span<int32_t>(a.bcnt, 0, (size_t)a.apply.K * split_count_stride(nblocks), "block counts");
+  }
   return hipSuccess;
 }
 static char* g_scratch = nullptr;  // host stand-in of the device scratch array

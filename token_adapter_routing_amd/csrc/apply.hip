@@ -173,7 +173,8 @@ struct StepArgs {
   int32_t* perm;
   float* perm_w;
   int32_t* inv;
-  int dispatch_share;  // the launch writes idx .. inv (every workgroup of slice 0 counts all N ids)
+  int dispatch_share;  // the launches write idx .. inv (split: from per-block counts; tile: every
+                       // workgroup counts all N ids itself)
 };
 
 struct StepLds {
@@ -397,10 +398,12 @@ __global__ __launch_bounds__(kBThreads, 2) void expand_block_multi(BlockMulti m)
 //                 ids, stages the A slices of the adapters the block uses in LDS, and writes
 //                 the partial h of every token against its own adapter (rows of other adapters
 //                 are discarded, so the partial workspace does not grow with the adapters in a
-//                 block).  Workgroups of slice 0 also write the block's share of the dispatch
-//                 outputs (they count the adapters of all ids and of the ids before the block).
+//                 block).  Workgroups of slice 0 also write the block's adapter counts.
 //   split_expand  (64-token block, d_out slice of 512): sums the partials in slice order,
-//                 scales, stages the B slices in LDS and writes y = y0 + sum_e mask_e(h) B_e.
+//                 scales, stages the B slices in LDS and writes y = y0 + sum_e mask_e(h) B_e;
+//                 and, from all blocks' adapter counts (offsets, and the tokens of earlier
+//                 blocks per adapter), the dispatch outputs of its share of the block's tokens
+//                 (the block's column slices split its 64 tokens).
 // The launch boundary orders the partials' writes before their reads.  Workgroups are dispatched
 // round robin over the 8 XCDs (workgroup b runs on XCD b % 8); both launches place every slice of
 // block tb on XCD tb % 8, so the partials that the shrink writes are still in that XCD's L2 when
@@ -416,45 +419,33 @@ constexpr int split_group() {
 struct SplitGeom {
   int nblocks, kslices, cslices;  // grid of a launch: 8 * ceil(nblocks / 8) * slices
   float* part;  // [nblocks][kslices][64][r_pad] fp32: partial h of each token on its own adapter
+  int32_t* bcnt;  // [K][split_count_stride(nblocks)]: routed tokens per adapter in each block
 };
+constexpr int kSMaxCounts = 1024;  // K * split_count_stride(nblocks) for N <= kStepMaxN, K <= 16
+static_assert(kSMaxCounts >= kApplyTileMaxAdapters * (kStepMaxN / kSTok) && kSMaxCounts % kSThreads == 0,
+              "per-block counts of the split step's dispatch share");
 
 template <int RB>
 struct ShrinkLds {
   alignas(16) uint16_t As[split_group<RB>()][4 * RB * 16 * kStepK];
   float red[4][16][RB * 16 + 4];
-  StepLds S;
-  int wgc[kSWavesMax][kT8MaxU], wpc[kSWavesMax][kT8MaxU];
 };
 
-// Partial h of block tb, reduction slice sl (and, when disp, the block's dispatch outputs).
-// `pre(used)` runs once the first group's A slices are requested and before their data is
-// awaited: the fused launch requests its expand's loads there.
-template <int RB, bool INDIRECT, typename Pre>
+// Partial h of block tb, reduction slice sl (and, when disp, the block's adapter counts).
+template <int RB, bool INDIRECT>
 __device__ __forceinline__ void shrink_slice(const StepArgs& a, const SplitGeom& g, int tb, int sl, bool disp,
-                                             ShrinkLds<RB>& L, Pre pre) {
+                                             ShrinkLds<RB>& L) {
   constexpr int GA = split_group<RB>();
   constexpr int piece = RB * 16 * kStepK;  // elements of one reduction step's A pieces
   auto& As = L.As;
   auto& red = L.red;
-  auto& S = L.S;
-  auto& wgc = L.wgc;
-  auto& wpc = L.wpc;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15, G = lane >> 4, rb = wave & 3, kh = wave >> 2;
   const int N = a.t.N, K = a.t.K, d_in = a.t.tgt.d_in, r_pad = a.t.tgt.r_pad;
   const int t0 = tb * kSTok;
-  if (disp && threadIdx.x < kSWavesMax * kT8MaxU) {
-    (&wgc[0][0])[threadIdx.x] = 0;
-    (&wpc[0][0])[threadIdx.x] = 0;
-  }
   // loads in use order: the block's ids (lane l: token t0 + l, clones of N - 1 past the end),
-  // this thread's share of the first 2048 ids (dispatch workgroups), then the x rows
+  // then the x rows
   const int myid = a.ids[min(t0 + lane, N - 1)];
-  int dv[kStepIdsPerThread];
-  if (disp) {
-#pragma unroll
-    for (int j = 0; j < kStepIdsPerThread; ++j) dv[j] = a.ids[min(j * kSThreads + (int)threadIdx.x, N - 1)];
-  }
   __builtin_amdgcn_sched_barrier(0);  // keep the issue order (data returns in issue order)
   const int S_all = d_in / kStepK;
   const int s0 = sl * (kSSlice / kStepK), s1 = min(s0 + kSSlice / kStepK, S_all);
@@ -480,17 +471,18 @@ __device__ __forceinline__ void shrink_slice(const StepArgs& a, const SplitGeom&
   int erow[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) erow[i] = __shfl(pe, 16 * rb + 4 * G + i, kWave);
-  int nbits = 0;
-  while ((1 << nbits) < K) ++nbits;
-  if (disp) {
-    // dispatch counts while the x rows are in flight (the ids were requested before them)
-    __syncthreads();  // counters cleared
-    step_count_waves(wgc, wpc, a.bounds, dv, 0, N, K, t0);
-    for (int c0 = kStepIdsPerThread * kSThreads; c0 < N; c0 += kStepIdsPerThread * kSThreads) {
+  if (disp && wave == 0) {
+    // the block's routed tokens per adapter (clones of token N - 1 past the end do not count),
+    // stored while the x rows are in flight
+    const bool real = t0 + lane < N;
+    int mine = 0;
 #pragma unroll
-      for (int j = 0; j < kStepIdsPerThread; ++j) dv[j] = a.ids[min(c0 + j * kSThreads + (int)threadIdx.x, N - 1)];
-      step_count_waves(wgc, wpc, a.bounds, dv, c0, N, K, t0);
-    }
+    for (int e = 0; e < kT8MaxU; ++e)
+      if (e < K) {
+        const int c = __popcll(__ballot(real && pe == e));
+        if (lane == e) mine = c;
+      }
+    if (lane < K) g.bcnt[(size_t)lane * split_count_stride(g.nblocks) + tb] = mine;
   }
 
   f32x4_t hs[RB];
@@ -507,7 +499,6 @@ __device__ __forceinline__ void shrink_slice(const StepArgs& a, const SplitGeom&
       lds_copy_1k(As[gi], adapter_A<INDIRECT>(a.t.tgt, __builtin_ctz(r2)) + (size_t)s0 * piece, ns * piece * 2);
       r2 &= r2 - 1;
     }
-    if (base == 0) pre(used);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     for (int gi = 0; gi < ng; ++gi) {
@@ -553,48 +544,6 @@ __device__ __forceinline__ void shrink_slice(const StepArgs& a, const SplitGeom&
 #pragma unroll
       for (int i = 0; i < 4; ++i) dst[(size_t)(4 * G + i) * r_pad + u * 16 + n] = hs[u][i] + red[rb][4 * G + i][u * 16 + n];
   }
-  if (!disp) return;
-  // dispatch share of the block: offsets, then the block's tokens' grouped positions
-  if (wave == 0) {
-    int c = 0, cp = 0;
-    if (lane < K) {
-#pragma unroll
-      for (int w = 0; w < kSWaves; ++w) {
-        c += wgc[w][lane];
-        cp += wpc[w][lane];
-      }
-      S.pcnt[lane] = cp;
-    }
-    const int incl = wave_incl_scan(c, lane);
-    if (lane < K) S.offs[lane] = incl - c;
-    if (tb == 0) {
-      if (lane < K) {
-        a.counts[lane] = c;
-        a.offsets[lane + 1] = incl;
-      }
-      if (lane == 0) a.offsets[0] = 0;
-    }
-  }
-  __syncthreads();
-  if (wave == 0) {
-    // one token per lane: rank among the block's earlier tokens of the same adapter
-    const int tok = t0 + lane;
-    const bool real = tok < N;
-    const bool valid = real && pe >= 0;
-    const uint64_t m = match_mask(pe, valid, nbits);
-    if (real) {
-      a.idx[tok] = pe;
-      a.w[tok] = valid ? 1.0f : 0.0f;
-      if (valid) {
-        const int pos = S.offs[pe] + S.pcnt[pe] + __popcll(m & lanemask_lt(lane));
-        a.inv[tok] = pos;
-        a.perm[pos] = tok;
-        a.perm_w[pos] = 1.0f;
-      } else {
-        a.inv[tok] = -1;
-      }
-    }
-  }
 }
 
 template <int RB, bool INDIRECT>
@@ -603,7 +552,7 @@ __global__ __launch_bounds__(kSThreads) void split_shrink(StepArgs a, SplitGeom 
   const int q = blockIdx.x >> 3;
   const int tb = (q / g.kslices) * 8 + (blockIdx.x & 7), sl = q % g.kslices;
   if (tb >= g.nblocks) return;
-  shrink_slice<RB, INDIRECT>(a, g, tb, sl, sl == 0 && a.dispatch_share, L, [](uint32_t) {});  // slice 0: dispatch outputs
+  shrink_slice<RB, INDIRECT>(a, g, tb, sl, sl == 0 && a.dispatch_share, L);  // slice 0: the block's counts
 }
 
 // ALLB (rank block 1, K <= 4): the B slices of all K adapters fit in LDS and are requested
@@ -616,6 +565,7 @@ __global__ __launch_bounds__(kSThreads) void split_expand(StepArgs a, SplitGeom 
   constexpr size_t y0b = Y0F32 ? 4 : 2, yb = YF32 ? 4 : 2;
   __shared__ alignas(16) uint16_t Bs[GB][kSSlice * RP];  // B^T rows of the slice [512][r_pad]
   __shared__ alignas(16) uint16_t hb[2][kSTok][RP];      // h hi / lo [part][token][rank]
+  __shared__ alignas(16) int cntl[kSMaxCounts];          // all blocks' adapter counts [K][cstride]
   const int q = blockIdx.x >> 3;
   const int tb = (q / g.cslices) * 8 + (blockIdx.x & 7), cs = q % g.cslices;
   if (tb >= g.nblocks) return;
@@ -635,6 +585,13 @@ __global__ __launch_bounds__(kSThreads) void split_expand(StepArgs a, SplitGeom 
   // is stored while the second block's y0 rows are still arriving.
   static_assert(!ALLB || RB == 1, "all-adapter staging holds four rank-16 slices");
   const int myid = a.ids[min(t0 + lane, N - 1)];
+  // dispatch share: all blocks' adapter counts, 2 per thread (unconditional, clamped loads)
+  const int cstride = split_count_stride(g.nblocks), ncnt = K * cstride;
+  int cv[kSMaxCounts / kSThreads];
+  if (a.dispatch_share) {
+#pragma unroll
+    for (int j = 0; j < kSMaxCounts / kSThreads; ++j) cv[j] = g.bcnt[min(j * kSThreads + (int)threadIdx.x, ncnt - 1)];
+  }
   __builtin_amdgcn_sched_barrier(0);  // keep the issue order (data returns in issue order)
   const char* y0rows[4];
   char* yrows[4];
@@ -719,6 +676,11 @@ __global__ __launch_bounds__(kSThreads) void split_expand(StepArgs a, SplitGeom 
     o0[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     o1[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
+  if (a.dispatch_share) {
+#pragma unroll
+    for (int j = 0; j < kSMaxCounts / kSThreads; ++j)
+      if (j * kSThreads + (int)threadIdx.x < ncnt) cntl[j * kSThreads + threadIdx.x] = cv[j];
+  }
   const int erow = __shfl(pe, 16 * rb + n, kWave);  // adapter of the lane's A-operand row
   uint32_t rem = used;
   for (int base = 0; base < nU; base += GB) {
@@ -732,7 +694,7 @@ __global__ __launch_bounds__(kSThreads) void split_expand(StepArgs a, SplitGeom 
       }
     }
     if (base > 0) __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();  // the group's B slices and h are in LDS
+    __syncthreads();  // the group's B slices and h (and the counts) are in LDS
     for (int gi = 0; gi < ng; ++gi) {
       const int e = __builtin_ctz(rem);
       rem &= rem - 1;
@@ -758,6 +720,62 @@ __global__ __launch_bounds__(kSThreads) void split_expand(StepArgs a, SplitGeom 
           o0[j] = mfma16x16x32(hv[u], as_bf16x8(v0), o0[j]);
           o1[j] = mfma16x16x32(hv[u], as_bf16x8(v1), o1[j]);
         }
+    }
+  }
+  if (nU == 0 && a.dispatch_share) __syncthreads();  // the counts are in LDS (no group loop ran)
+  if (a.dispatch_share && wave == 0) {
+    // dispatch share, before the y stores so that its own stores go out first (issued after
+    // them they would extend the launch): lane e < K sums adapter e's row of block counts (all
+    // blocks, and those before tb) with 16-byte LDS reads; a uniform loop over the adapters
+    // turns the totals into offsets.  A token's grouped position is its adapter's offset, plus
+    // that adapter's tokens in earlier blocks, plus its rank among the block's earlier tokens of
+    // the same adapter.  This workgroup writes the outputs of block tokens [l0, l1) (the column
+    // slices split the block).
+    int tot = 0, bef = 0;
+    if (lane < K) {
+      const int* row = cntl + lane * cstride;
+#pragma unroll
+      for (int j = 0; j < kStepMaxN / kSTok / 4; ++j) {
+        if (4 * j < cstride) {  // entries past nblocks are padding, never written
+          const int4 v = *reinterpret_cast<const int4*>(row + 4 * j);
+          const int nb = g.nblocks;
+          tot += (4 * j < nb ? v.x : 0) + (4 * j + 1 < nb ? v.y : 0) + (4 * j + 2 < nb ? v.z : 0) +
+                 (4 * j + 3 < nb ? v.w : 0);
+          bef += (4 * j < tb ? v.x : 0) + (4 * j + 1 < tb ? v.y : 0) + (4 * j + 2 < tb ? v.z : 0) +
+                 (4 * j + 3 < tb ? v.w : 0);
+        }
+      }
+    }
+    int start = 0, off = 0;
+    for (int e = 0; e < K; ++e) {
+      const int tot_e = __builtin_amdgcn_readlane(tot, e), bef_e = __builtin_amdgcn_readlane(bef, e);
+      if (pe == e) start = off + bef_e;
+      if (tb == 0 && cs == 0 && lane == e) {
+        a.counts[e] = tot_e;
+        a.offsets[e] = off;
+      }
+      off += tot_e;
+    }
+    if (tb == 0 && cs == 0 && lane == 0) a.offsets[K] = off;
+    int nbits = 0;
+    while ((1 << nbits) < K) ++nbits;
+    const int tok = t0 + lane;
+    const bool real = tok < N;
+    const bool valid = real && pe >= 0;
+    const uint64_t mm = match_mask(pe, valid, nbits);
+    const int tpw = (kSTok + g.cslices - 1) / g.cslices;
+    const int l0 = cs * tpw, l1 = min(kSTok, l0 + tpw);
+    if (real && lane >= l0 && lane < l1) {
+      a.idx[tok] = pe;
+      a.w[tok] = valid ? 1.0f : 0.0f;
+      if (valid) {
+        const int pos = start + __popcll(mm & lanemask_lt(lane));
+        a.inv[tok] = pos;
+        a.perm[pos] = tok;
+        a.perm_w[pos] = 1.0f;
+      } else {
+        a.inv[tok] = -1;
+      }
     }
   }
   if (has0) epilogue_store<Y0F32, YF32>(o0, yc0, yrows, c0 + b0 * kColBlock, n, 0xFu);
@@ -1728,12 +1746,13 @@ hipError_t launch_step_vocab(const StepVocabLaunch& a, hipStream_t s) {
   sa.dispatch_share = a.dispatch_share ? 1 : 0;
   const int RBv = a.apply.tgt.r_pad / 16;
   hipError_t err = hipSuccess;
-  if (a.ws != nullptr) {
+  if (a.part != nullptr) {
     SplitGeom g;
     g.nblocks = (a.apply.N + kSTok - 1) / kSTok;
     g.kslices = (a.apply.tgt.d_in + kSSlice - 1) / kSSlice;
     g.cslices = (a.apply.tgt.d_out + kSSlice - 1) / kSSlice;
-    g.part = reinterpret_cast<float*>(a.ws);
+    g.part = a.part;
+    g.bcnt = a.bcnt;
     MOLORA_DISPATCH_RB(RBv, MOLORA_DISPATCH_BOOL(a.apply.indirect, IND, MOLORA_DISPATCH_BOOL(a.apply.y0_f32, Y0F,
         MOLORA_DISPATCH_BOOL(a.apply.y_f32, YF, err = (launch_split_t<RB, IND, Y0F, YF>(sa, g, s))))));
     return err;

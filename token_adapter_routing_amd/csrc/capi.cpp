@@ -10,7 +10,7 @@
 #include <string>
 #include <vector>
 
-#include "../../include/molora.h"
+#include "molora.h"
 #include "molora_launch.h"
 
 static_assert(MOLORA_NOALLOC_SCRATCH_BYTES == molora::kScratchBytes, "scratch size in the header and the library");
@@ -501,7 +501,8 @@ int molora_step_vocab(const molora_hotset* hs, int target, const int32_t* ids, i
   a.path = molora::kPathTile;
   a.ws = nullptr;
   a.col_groups = 0;
-  st.ws = ws != nullptr ? static_cast<char*>(ws) + plan.part_off : nullptr;
+  st.part = ws != nullptr ? reinterpret_cast<float*>(static_cast<char*>(ws) + plan.part_off) : nullptr;
+  st.bcnt = ws != nullptr ? reinterpret_cast<int32_t*>(static_cast<char*>(ws) + plan.cnt_off) : nullptr;
   st.dispatch_share = true;
   st.ids = ids;
   st.idx = idx;
@@ -525,7 +526,8 @@ int molora_step_vocab(const molora_hotset* hs, int target, const int32_t* ids, i
   if (e == hipSuccess) e = molora::launch_dispatch(idx, w, N, hs->K, counts, offsets, perm, perm_w, inv, dws, s);
   if (e == hipSuccess) {
     if (ws != nullptr) {
-      st.ws = wsb + plan.part_off;
+      st.part = reinterpret_cast<float*>(wsb + plan.part_off);
+      st.bcnt = nullptr;
       st.dispatch_share = false;
       e = molora::launch_step_vocab(st, s);
     } else {

@@ -62,9 +62,9 @@ struct StepVocabLaunch {
   int32_t* perm;
   float* perm_w;
   int32_t* inv;
-  void* ws;           // NULL: the one-launch tile step; else the split launches' partials
-  bool dispatch_share;  // the launches write idx .. inv (N <= kStepMaxN: every workgroup that
-                        // writes a share reads all N ids); else they only apply
+  float* part;         // NULL: the one-launch tile step; else the split launches' partials
+  int32_t* bcnt;        // split launches with dispatch_share: per-block adapter counts
+  bool dispatch_share;  // the launches write idx .. inv (N <= kStepMaxN); else they only apply
 };
 hipError_t launch_step_vocab(const StepVocabLaunch& a, hipStream_t s);
 

@@ -79,13 +79,20 @@ MOLORA_HD inline size_t split_part_floats(int N, int d_in, int r_pad) {
   return (size_t)((N + kSTok - 1) / kSTok) * ((d_in + kSSlice - 1) / kSSlice) * kSTok * r_pad;
 }
 
+// Per-block adapter counts of the split step's dispatch share, adapter-major: [K][stride]
+// int32 with the block count rounded up to a multiple of 4 (rows read 16 bytes at a time; the
+// padding entries are never written and never counted).
+MOLORA_HD inline int split_count_stride(int nblocks) { return (nblocks + 3) / 4 * 4; }
+
 // Workspace of molora_step_vocab with a workspace: the split launches' partials at part_off.
-// N <= kStepMaxN: those launches also write the dispatch outputs (fused_dispatch).  Larger N:
-// route and a chip-wide dispatch (its per-workgroup counts at disp_off) run first.
+// N <= kStepMaxN: those launches also produce the dispatch outputs (fused_dispatch), through
+// per-block adapter counts (at cnt_off) that the first launch writes and the second scans.  Larger N: route and a chip-wide dispatch (its per-workgroup counts at disp_off)
+// run first.
 struct StepPlan {
   bool fused_dispatch;
   size_t disp_off, disp_bytes;
   size_t part_off, part_bytes;
+  size_t cnt_off, cnt_bytes;
   size_t total;
 };
 StepPlan step_plan(int N, int K, int r_pad, int d_in);

@@ -42,7 +42,9 @@ StepPlan step_plan(int N, int K, int r_pad, int d_in) {
   p.disp_bytes = p.fused_dispatch ? 0 : dispatch_ws_bytes(N, K);
   p.part_off = align256(p.disp_bytes);
   p.part_bytes = split_part_floats(N, d_in, r_pad) * sizeof(float);
-  p.total = p.part_off + p.part_bytes;
+  p.cnt_off = align256(p.part_off + p.part_bytes);
+  p.cnt_bytes = p.fused_dispatch ? (size_t)K * split_count_stride((N + kSTok - 1) / kSTok) * sizeof(int32_t) : 0;
+  p.total = p.cnt_off + p.cnt_bytes;
   return p;
 }
 
