@@ -179,6 +179,10 @@ def main():
 
     K_steps, W_steps = max(1, args.steps), max(0, args.warmup)
 
+    def spin(stream_):
+        with torch.cuda.stream(stream_):
+            torch.cuda._sleep(200000)
+
     def time_steps(fn):
         """Exactly W_steps untimed steps, then exactly K_steps timed steps, each run as one HIP
         graph that cycles through the S buffer sets (step i uses set i mod S); HIP events on the
@@ -195,6 +199,10 @@ def main():
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         with torch.cuda.stream(stream):
+            # a short spin kernel ahead of the start event keeps the GPU busy while the host submits
+            # the graph, so the events time the steps, not the submission (as in a serving loop
+            # whose next graph is queued while the previous one runs)
+            spin(stream)
             e0.record(stream)
             g.replay()
             e1.record(stream)
@@ -215,6 +223,13 @@ def main():
                   + N * 4                            # token ids
                   + N * (4 + 4 + 4 + 4 + 4) + (2 * K + 1) * 4)  # idx, w, perm, perm_w, inv, counts, offsets
     kernel_gbs = step_bytes / (kernel_us * 1e-6) / 1e9
+
+    # ---------------- a reference for the step's bytes: one torch elementwise kernel that reads two
+    # [N][d] bf16 tensors and writes one (the x, y0 and y streams of a step, without the adapters)
+    def stream_ref(s_):
+        b = sets[s_]
+        torch.add(b["x"], b["y0"], out=b["y"])
+    ref_ms, _ = time_steps(stream_ref)
 
     # ---------------- step latency percentiles over single-step graph replays
     g_one = [graph_of(step, [s_]) for s_ in range(S)]
@@ -252,6 +267,10 @@ def main():
         "step_roofline_frac": step_bytes / (ms_per_step * 1e-3) / (HBM_PEAK_GBS * 1e9),
         "step_latency_us": {"p50": p50, "p99": p99, "cv": cv, "replays": len(lat), "graph": "single step"},
         "wall_s_timed_region": wall,
+        "streaming_reference": {"what": "torch.add(x, y0, out=y) on the same buffer sets: 2 reads + 1 write of "
+                                        "[2048][4096] bf16 per step, one kernel, same graph timing",
+                                "us_per_step": ref_ms * 1e3,
+                                "GBps": 3 * N * d_in * 2 / (ref_ms * 1e-3) / 1e9},
         "roofline": {"bound": "hbm", "achieved": kernel_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": kernel_gbs / HBM_PEAK_GBS, "traffic": counter_traffic(COUNTER_SUMMARY),
                      "kernel": "split_shrink + split_expand (the two launches of one step)",
@@ -570,17 +589,22 @@ def row_qwen_layer(m, torch, dev, bf, f32, reps):
 
 def row_decode(m, torch, dev, bf, i32, reps):
     """Decode sweep: B tokens, 64 hot-set adapters of rank 16, one uniformly random adapter
-    per token (idx given): dispatch + apply, skinny vs grouped; then the slab layouts."""
+    per token (idx given): dispatch + apply on the skinny, grouped and AUTO paths (AUTO's choice
+    as the library reports it); then the slab layouts (direct vs indirect, identical operations,
+    AUTO path) at every B for 4 .. 64 adapters."""
     import synth
+    names = {m.PATH_GROUPED: "grouped", m.PATH_SKINNY: "skinny", m.PATH_TILE: "tile", m.PATH_BLOCK: "block"}
+    batches = (1, 16, 64, 160, 512, 2048)
     out = {"workload": "decode B in {1,16,64,160,512,2048}, d=4096, K=64 r=16 k=1; 20 steps per graph",
            "sweep": {}, "layouts": {}}
     per_adapter = 2 * 4096 * 16 * 2
     cache = {}
-    for B in (1, 16, 64, 160, 512, 2048):
+    for B in batches:
         c = synth.decode_batch(B)
         t = c.targets[0]
         if "hs" not in cache:
-            cache["hs"] = {lay: m.molora_hotset_init([(bf(t.A), bf(t.B))], c.scale, layout=lay) for lay in (0, 1)}
+            cache["hs"] = m.molora_hotset_init([(bf(t.A), bf(t.B))], c.scale)
+        hs = cache["hs"]
         x, y0 = bf(t.x), bf(t.y0)
         y = torch.empty(B, t.d_out, dtype=torch.bfloat16, device=dev)
         idx = i32(c.idx)
@@ -590,9 +614,9 @@ def row_decode(m, torch, dev, bf, i32, reps):
                 torch.empty(B, dtype=torch.int32, device=dev))
         used = len(np.unique(c.idx))
         nbytes = B * (t.d_in + 2 * t.d_out) * 2 + used * per_adapter
-        entry = {"distinct_adapters": used, "compulsory_bytes": nbytes}
-        for name, path in (("skinny", m.PATH_SKINNY), ("grouped", m.PATH_GROUPED)):
-            hs = cache["hs"][0]
+        entry = {"distinct_adapters": used, "compulsory_bytes": nbytes,
+                 "auto_path": names[m.molora_apply_path(hs, B, 1, m.PATH_AUTO)]}
+        for name, path in (("skinny", m.PATH_SKINNY), ("grouped", m.PATH_GROUPED), ("auto", m.PATH_AUTO)):
             ws = torch.zeros(max(1, m.molora_apply_workspace(hs, 0, B, 1, path, torch.bfloat16)), dtype=torch.uint8, device=dev)
 
             def step():
@@ -602,30 +626,35 @@ def row_decode(m, torch, dev, bf, i32, reps):
             ms, g, _ = graph_ms(torch, step, reps, inner=20)
             entry[name] = {"us_per_step": ms * 1e3, "GBps": nbytes / (ms * 1e-3) / 1e9}
             del g
-        entry["auto_path"] = "grouped"
         out["sweep"][str(B)] = entry
     sk = [int(b) for b, e in out["sweep"].items() if e["grouped"]["us_per_step"] < e["skinny"]["us_per_step"]]
     out["grouped_faster_from_B"] = min(sk) if sk else None
-    # direct vs indirect slab at 4/8/16/32/64 adapters, B = 512, identical operations
-    B = 512
-    for Kh in (4, 8, 16, 32, 64):
-        c = synth.decode_batch(B, K=Kh, case_id=30 + Kh)
-        t = c.targets[0]
-        x, y0 = bf(t.x), bf(t.y0)
-        y = torch.empty(B, t.d_out, dtype=torch.bfloat16, device=dev)
-        idx = i32(c.idx)
-        w = torch.ones(B, dtype=torch.float32, device=dev)
-        meta = m.molora_dispatch(idx, w, Kh, 1)
-        ent = {}
-        for lay, name in ((0, "direct"), (1, "indirect")):
-            hs = m.molora_hotset_init([(bf(t.A), bf(t.B))], c.scale, layout=lay)
-            ms, g, _ = graph_ms(torch, lambda: m.molora_apply(hs, x, y0, meta[1], meta[2], meta[3], meta[4], k=1, y=y),
-                                reps, inner=20)
-            ent[name + "_us"] = ms * 1e3
-            del g, hs
-        ent["indirect_over_direct"] = ent["indirect_us"] / ent["direct_us"]
-        out["layouts"][str(Kh)] = ent
     del cache
+    # direct vs indirect slab at 4/8/16/32/64 adapters and every B, identical operations (AUTO path)
+    for Kh in (4, 8, 16, 32, 64):
+        c0 = synth.decode_batch(1, K=Kh, case_id=30 + Kh)
+        t0 = c0.targets[0]
+        hss = {lay: m.molora_hotset_init([(bf(t0.A), bf(t0.B))], c0.scale, layout=lay) for lay in (0, 1)}
+        per_k = {}
+        for B in batches:
+            c = synth.decode_batch(B, K=Kh, case_id=30 + Kh)
+            t = c.targets[0]
+            x, y0 = bf(t.x), bf(t.y0)
+            y = torch.empty(B, t.d_out, dtype=torch.bfloat16, device=dev)
+            meta = m.molora_dispatch(i32(c.idx), torch.ones(B, dtype=torch.float32, device=dev), Kh, 1)
+            ent = {"path": names[m.molora_apply_path(hss[0], B, 1, m.PATH_AUTO)]}
+            for lay, name in ((0, "direct"), (1, "indirect")):
+                hs = hss[lay]
+                ms, g, _ = graph_ms(torch, lambda: m.molora_apply(hs, x, y0, meta[1], meta[2], meta[3], meta[4], k=1,
+                                                                  y=y), reps, inner=20)
+                ent[name + "_us"] = ms * 1e3
+                del g
+            ent["indirect_over_direct"] = ent["indirect_us"] / ent["direct_us"]
+            per_k[str(B)] = ent
+        out["layouts"][str(Kh)] = per_k
+        del hss
+    out["layout_mean_indirect_over_direct"] = statistics.mean(
+        e["indirect_over_direct"] for pk in out["layouts"].values() for e in pk.values())
     return out
 
 

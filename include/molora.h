@@ -217,8 +217,10 @@ int molora_dispatch(const int32_t *idx, const float *w, int N, int k, int K,
  *   y       device [N][d_out] out, dtype y_dtype
  *   offsets, perm, perm_w, inv: the outputs of molora_dispatch for this
  *           routing (all four required)
- *   path    MOLORA_PATH_AUTO (_TILE when K <= 16, r <= 32 and N*k >= 192;
- *           else _GROUPED, except _SKINNY for r > 32 below 1024 pairs),
+ *   path    MOLORA_PATH_AUTO (r <= 32: for k == 1 _TILE when N >= 1024 and
+ *           K <= 4, else _GROUPED; for k > 1 _TILE when K <= 16 and N*k >= 192,
+ *           else _GROUPED; r > 32: _GROUPED from 1024 pairs, else _SKINNY;
+ *           molora_apply_path reports the choice),
  *           _GROUPED (MFMA tiles of grouped rows of one adapter: 16 rows for
  *           k == 1 and r <= 32; otherwise 64 rows, and for k > 1 (k*K <= 64)
  *           one pass per routed pair of a token, the sum carried in fp32),
@@ -239,6 +241,9 @@ int molora_dispatch(const int32_t *idx, const float *w, int N, int k, int K,
  * ------------------------------------------------------------------------ */
 int molora_apply_workspace(const molora_hotset *hs, int target, int N, int k, int y_dtype,
                            int path, size_t *bytes);
+/* The path molora_apply runs for these arguments: `path` itself, or for MOLORA_PATH_AUTO the
+ * rule's choice (host arithmetic only, nothing enqueued).  Errors as molora_apply_workspace. */
+int molora_apply_path(const molora_hotset *hs, int target, int N, int k, int path, int *resolved);
 int molora_apply(const molora_hotset *hs, int target, const void *x, const void *y0,
                  int y0_dtype, void *y, int y_dtype, int N, int k, const int32_t *offsets,
                  const int32_t *perm, const float *perm_w, const int32_t *inv, int path,

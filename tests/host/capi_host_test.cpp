@@ -340,6 +340,10 @@ static void test_apply(int K, int r, int d_in, int d_out, int N, int k, int path
   } else {
     CHECK(rc == MOLORA_OK, "apply N=%d k=%d K=%d r=%d path=%d", N, k, K, r, path);
     if (N > 0) CHECK(g_last_apply_path == apply_resolve_path(N, k, path, K, (r + 15) / 16 * 16), "path");
+    int reported = -1;
+    CHECK(molora_apply_path(h.hs, 0, N, k, path, &reported) == MOLORA_OK &&
+              (N == 0 || reported == g_last_apply_path),
+          "molora_apply_path reports %d, the launch ran %d", reported, g_last_apply_path);
     check_disjoint("apply");
     if (need > 0 && N > 0) {
       const int l1 = g_launches;

@@ -388,16 +388,16 @@ def test_apply_multi_equals_single_calls(k, r, path, y_dtype):
     order = [2, 0, 3, 1]  # targets in any order
     ys = m.molora_apply_multi(hs, [xs[i] for i in order], [y0s[i] for i in order], offsets, perm, perm_w, inv, k=k,
                               targets=order, y_dtype=y_dtype, path=path)
-    # the documented AUTO rule: tile-local for K <= 16, r <= 32, N*k >= 192, except blocks for
-    # several targets with k > 1; else grouped, or skinny for r > 32 below 1024 pairs
+    # the documented AUTO rule (blocks instead of tiles for several targets with k > 1)
     single_path = path
     if path == 0:
-        if K <= 16 and r <= 32 and N * k >= 192:
-            single_path = 4 if k > 1 else 3
-        elif r <= 32 or N * k >= 1024:
-            single_path = 1
+        if r <= 32 and k > 1:
+            single_path = 4 if (K <= 16 and N * k >= 192) else 1  # tile, then blocks for several targets
+        elif r <= 32:
+            single_path = 3 if (N >= 1024 and K <= 4) else 1
         else:
-            single_path = 2
+            single_path = 1 if N * k >= 1024 else 2
+        assert m.molora_apply_path(hs, N, k, 0, target=0) == (3 if single_path == 4 else single_path)
     for j, i in enumerate(order):
         single = m.molora_apply(hs, xs[i], y0s[i], offsets, perm, perm_w, inv, k=k, target=i, y_dtype=y_dtype,
                                 path=single_path)

@@ -8,7 +8,7 @@ from .binding import (  # noqa: F401
     BF16, F32, LAYOUT_DIRECT, LAYOUT_INDIRECT, PATH_AUTO, PATH_BLOCK, PATH_GROUPED, PATH_SKINNY, PATH_TILE,
     HotSet, MoloraError, exported_symbols, load_library, LIB_PATH, NOALLOC_SCRATCH_BYTES,
     MOLORA_OK, MOLORA_EINVAL, MOLORA_ENOTSUP, MOLORA_ENOSPC, MOLORA_EHIP,
-    molora_apply, molora_apply_multi, molora_apply_multi_workspace, molora_apply_workspace, molora_dispatch,
+    molora_apply, molora_apply_multi, molora_apply_path, molora_apply_multi_workspace, molora_apply_workspace, molora_dispatch,
     molora_dispatch_workspace,
     molora_hotset_bytes, molora_hotset_destroy, molora_hotset_init, molora_hotset_load, molora_route_topk,
     molora_route_vocab, molora_seqpass_meta, molora_step_vocab, molora_step_vocab_noalloc, molora_step_workspace,

@@ -49,6 +49,7 @@ _SIGS = {
     "molora_dispatch_workspace": (_c_i, [_c_i, _c_i, _c_i, ctypes.POINTER(_c_sz)]),
     "molora_dispatch": (_c_i, [_c_p, _c_p, _c_i, _c_i, _c_i, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_sz, _c_p]),
     "molora_apply_workspace": (_c_i, [_c_p, _c_i, _c_i, _c_i, _c_i, _c_i, ctypes.POINTER(_c_sz)]),
+    "molora_apply_path": (_c_i, [_c_p, _c_i, _c_i, _c_i, _c_i, ctypes.POINTER(_c_i)]),
     "molora_apply": (_c_i, [_c_p, _c_i, _c_p, _c_p, _c_i, _c_p, _c_i, _c_i, _c_i, _c_p, _c_p, _c_p, _c_p, _c_i,
                             _c_p, _c_sz, _c_p]),
     "molora_apply_multi_workspace": (_c_i, [_c_p, _c_i, _c_p, _c_i, _c_i, _c_i, _c_i, ctypes.POINTER(_c_sz)]),
@@ -280,6 +281,13 @@ def molora_apply_workspace(hs: HotSet, target: int, N: int, k: int, path: int = 
     out = _c_sz()
     code = F32 if y_dtype == torch.float32 else BF16
     _check(load_library().molora_apply_workspace(hs.handle, target, N, k, code, path, ctypes.byref(out)))
+    return out.value
+
+
+def molora_apply_path(hs: HotSet, N: int, k: int = 1, path: int = PATH_AUTO, target: int = 0) -> int:
+    """The path molora_apply runs for these arguments (AUTO resolved by the library's rule)."""
+    out = _c_i()
+    _check(load_library().molora_apply_path(hs.handle, target, N, k, path, ctypes.byref(out)))
     return out.value
 
 

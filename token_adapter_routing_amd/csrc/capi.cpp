@@ -309,6 +309,16 @@ int molora_apply_workspace(const molora_hotset* hs, int target, int N, int k, in
   return ok();
 }
 
+int molora_apply_path(const molora_hotset* hs, int target, int N, int k, int path, int* resolved) {
+  if (resolved == nullptr) return fail(MOLORA_EINVAL, "resolved is NULL");
+  if (hs == nullptr) return fail(MOLORA_EINVAL, "hot set is NULL");
+  if (target < 0 || target >= hs->n_targets) return fail(MOLORA_EINVAL, "target %d outside [0, %d)", target, hs->n_targets);
+  if (N < 0 || k < 1 || k > MOLORA_MAX_TOPK || k > hs->K) return fail(MOLORA_EINVAL, "bad N=%d or k=%d", N, k);
+  if (path < MOLORA_PATH_AUTO || path > MOLORA_PATH_BLOCK) return fail(MOLORA_EINVAL, "unknown path %d", path);
+  *resolved = molora::apply_resolve_path(N, k, path, hs->K, hs->r_pad);
+  return ok();
+}
+
 int molora_apply(const molora_hotset* hs, int target, const void* x, const void* y0, int y0_dtype, void* y, int y_dtype,
                  int N, int k, const int32_t* offsets, const int32_t* perm, const float* perm_w, const int32_t* inv,
                  int path, void* ws, size_t ws_bytes, void* stream) {

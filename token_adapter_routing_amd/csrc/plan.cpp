@@ -51,11 +51,17 @@ StepPlan step_plan(int N, int K, int r_pad, int d_in) {
 int apply_resolve_path(int N, int k, int path, int K, int r_pad) {
   if (path != kPathAuto) return path;
   const long long P = (long long)N * k;
-  // few, small adapters: tile-local.  Ranks <= 32: grouped.  Ranks above 32: the 64-row
-  // grouped tiles from 1024 pairs on; below that their serial per-tile pipeline is slower than
-  // the skinny path's split reductions (the 64-token blocks give too few workgroups there).
-  if (K <= kApplyTileMaxAdapters && r_pad <= 32 && P >= 192) return kPathTile;
-  if (r_pad <= 32) return kPathGrouped;
+  // Measured at d = 4096, rank 16 (dispatch + apply, uniform routing, 1..2048 tokens, 4..64
+  // adapters): for k = 1 the grouped 16-row tiles win at every batch up to 512 tokens and for
+  // more than 4 adapters at every size (an 8-token tile reads every adapter its tokens use:
+  // 1.3-3.4x slower with 8-16 adapters); the tile path wins from 1024 pairs with at most 4
+  // adapters.  For k > 1 the tile path applies a token's pairs in one workgroup, where the
+  // grouped path would carry the sum through memory between rank passes.  Ranks above 32: the
+  // 64-row grouped tiles from 1024 pairs on; below that the skinny path's split reductions.
+  if (r_pad <= 32) {
+    if (k > 1) return (K <= kApplyTileMaxAdapters && P >= 192) ? kPathTile : kPathGrouped;
+    return (P >= 1024 && K <= 4) ? kPathTile : kPathGrouped;
+  }
   return P >= 1024 ? kPathGrouped : kPathSkinny;
 }
 
