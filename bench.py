@@ -85,7 +85,7 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run plain device copies of known size (for HBM counter scaling)")
-    p.add_argument("--rows", default="C0,C2,C3,C4,C4stack,paging",
+    p.add_argument("--rows", default="C0,C2,C3,C4,C4stack,paging,tiling",
                    help="other configurations to measure beside the headline (comma list, or 'none')")
     p.add_argument("--row-reps", type=int, default=100, help="graph replays per timed row entry")
     p.add_argument("--stack-replays", type=int, default=1000, help="single-graph replays of the 28-layer stack row")
@@ -383,6 +383,8 @@ def measure_rows(m, torch, dev, rows, reps, stack_replays=1000):
         res["C4_stress"] = row_stress(m, torch, dev, bf, f32, max(20, reps // 4))
     if "C4stack" in rows:
         res["C4_stack"] = row_stack(m, torch, dev, replays=stack_replays)
+    if "tiling" in rows:
+        res["tiling"] = row_tiling(m, torch, dev, bf, f32, i32, max(20, reps // 4))
     if "paging" in rows:
         res["C1_paging"] = row_paging(m, torch, dev, bf, i32, max(200, reps * 2))
     torch.cuda.synchronize()
@@ -691,6 +693,69 @@ def row_stress(m, torch, dev, bf, f32, reps):
                             "roofline_frac": compulsory / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9),
                             "mfma_utilisation_bf16": flops / (ms * 1e-3) / 2.5e15}
         del g, ws
+    return out
+
+
+def row_tiling(m, torch, dev, bf, f32, i32, reps):
+    """Fixed against adaptive tiling of the 64-row grouped kernel (the pages' Table 9): adapter
+    usage mixes 25% each, 80/10/5/5 and 95/2/2/1 (one adapter per token, 4 adapters of rank 64,
+    d=4096) at 2048 and 16384 tokens, and the stress workload's Zipf top-k (16 adapters of rank
+    64, 16384 tokens, k = 1..4).  Each entry: dispatch (and top-k) + apply as one graph."""
+    import synth
+    out = {"workload": "grouped 64-row kernel, MOLORA_PATH_GROUPED (adaptive) vs MOLORA_PATH_GROUPED_FIXED",
+           "mixes": {}, "zipf_stress": {}}
+    mixes = {"uniform_25": (0.25, 0.25, 0.25, 0.25), "80_10_5_5": (0.8, 0.1, 0.05, 0.05),
+             "95_2_2_1": (0.95, 0.02, 0.02, 0.01)}
+    for N in (2048, 16384):
+        for name, probs in mixes.items():
+            c = synth.mixed_batch(N, probs, case_id=6, sub=N)
+            t = c.targets[0]
+            hs = m.molora_hotset_init([(bf(t.A), bf(t.B))], c.scale)
+            x, y0 = bf(t.x), bf(t.y0)
+            y = torch.empty(N, t.d_out, dtype=torch.bfloat16, device=dev)
+            idx = i32(c.idx)
+            w = torch.ones(N, dtype=torch.float32, device=dev)
+            meta = m.molora_dispatch(idx, w, c.K, 1)
+            ent = {"segment_rows": [int(v) for v in np.bincount(c.idx, minlength=c.K)]}
+            for tname, path in (("adaptive", m.PATH_GROUPED), ("fixed64", m.PATH_GROUPED_FIXED)):
+                def step():
+                    m.molora_dispatch(idx, w, c.K, 1, out=meta)
+                    m.molora_apply(hs, x, y0, meta[1], meta[2], meta[3], meta[4], k=1, y=y, path=path)
+                ms, g, _ = graph_ms(torch, step, reps)
+                ent[tname + "_us"] = ms * 1e3
+                del g
+            ent["fixed_over_adaptive"] = ent["fixed64_us"] / ent["adaptive_us"]
+            out["mixes"][f"{name}_N{N}"] = ent
+            del hs
+    c = synth.stress(1)
+    t = c.targets[0]
+    N, K = c.N, c.K
+    x, y0 = bf(t.x), bf(t.y0)
+    y = torch.empty(N, t.d_out, dtype=torch.bfloat16, device=dev)
+    logits = f32(c.logits)
+    hs = m.molora_hotset_init([(bf(t.A), bf(t.B))], c.scale)
+    for k in (1, 2, 3, 4):
+        idx = torch.empty(N * k, dtype=torch.int32, device=dev)
+        w = torch.empty(N * k, dtype=torch.float32, device=dev)
+        meta = (torch.empty(K, dtype=torch.int32, device=dev), torch.empty(K + 1, dtype=torch.int32, device=dev),
+                torch.empty(N * k, dtype=torch.int32, device=dev), torch.empty(N * k, dtype=torch.float32, device=dev),
+                torch.empty(N * k, dtype=torch.int32, device=dev))
+        ent = {}
+        for tname, path in (("adaptive", m.PATH_GROUPED), ("fixed64", m.PATH_GROUPED_FIXED)):
+            ws = torch.zeros(max(1, m.molora_apply_workspace(hs, 0, N, k, path, torch.bfloat16)), dtype=torch.uint8,
+                             device=dev)
+
+            def step():
+                m.molora_route_topk(k, K, logits=logits, idx=idx, w=w, want_flags=False)
+                m.molora_dispatch(idx, w, K, k, out=meta)
+                m.molora_apply(hs, x, y0, meta[1], meta[2], meta[3], meta[4], k=k, y=y, path=path, ws=ws)
+
+            ms, g, _ = graph_ms(torch, step, reps)
+            ent[tname + "_us"] = ms * 1e3
+            del g, ws
+        ent["fixed_over_adaptive"] = ent["fixed64_us"] / ent["adaptive_us"]
+        out["zipf_stress"][f"k{k}"] = ent
+    del hs
     return out
 
 

@@ -54,7 +54,7 @@ enum {
 
 enum { MOLORA_LAYOUT_DIRECT = 0, MOLORA_LAYOUT_INDIRECT = 1 };
 enum { MOLORA_PATH_AUTO = 0, MOLORA_PATH_GROUPED = 1, MOLORA_PATH_SKINNY = 2, MOLORA_PATH_TILE = 3,
-       MOLORA_PATH_BLOCK = 4 };
+       MOLORA_PATH_BLOCK = 4, MOLORA_PATH_GROUPED_FIXED = 5 };
 enum { MOLORA_BF16 = 0, MOLORA_F32 = 1 };
 
 /* Limits of this build. */
@@ -222,8 +222,15 @@ int molora_dispatch(const int32_t *idx, const float *w, int N, int k, int K,
  *           else _GROUPED; r > 32: _GROUPED from 1024 pairs, else _SKINNY;
  *           molora_apply_path reports the choice),
  *           _GROUPED (MFMA tiles of grouped rows of one adapter: 16 rows for
- *           k == 1 and r <= 32; otherwise 64 rows, and for k > 1 (k*K <= 64)
- *           one pass per routed pair of a token, the sum carried in fp32),
+ *           k == 1 and r <= 32; otherwise up to 64 rows, the tile height chosen
+ *           per adapter segment on the device from the offsets (each segment cut
+ *           into equal tiles of at most a bound set by the pass's size, so no
+ *           tile spans two adapters: thelatestinai.com, Table 9, adaptive
+ *           tiling), and for k > 1 (k*K <= 64) one pass per routed pair of a
+ *           token, the sum carried in fp32),
+ *           _GROUPED_FIXED (the same 64-row kernel with fixed 64-row tiles per
+ *           segment, also for k == 1 and r <= 32: Table 9's fixed tiling, the
+ *           comparator of the adaptive one),
  *           _SKINNY (the grouped shrink split over d_in, for small batches), or
  *           _TILE (8 consecutive tokens per workgroup, every adapter the tile
  *           uses applied in turn; needs K <= 16), or

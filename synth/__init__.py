@@ -210,6 +210,19 @@ def decode_batch(B: int, K: int = 64, d: int = 4096, r: int = 16, case_id: int =
     return Case(f"decode_B{B}", case_id, B, K, r, 1, 2.0, [Target("proj", d, d, A, B_, x, y0)], idx=idx)
 
 
+def mixed_batch(N: int, probs, d: int = 4096, r: int = 64, case_id: int = 6, sub: int = 0) -> Case:
+    """Adapter-usage mix of the tiling comparison (thelatestinai.com, Table 9: 25% each,
+    80/10/5/5, 95/2/2/1): one adapter per token drawn i.i.d. from `probs` (K = len(probs))."""
+    K = len(probs)
+    g = rng_for(case_id, T_IDX, sub)
+    p = np.asarray(probs, dtype=np.float64)
+    idx = g.choice(K, size=N, p=p / p.sum()).astype(np.int32)
+    x = normal_bf16(case_id, T_X, (N, d), sub=sub)
+    y0 = normal_bf16(case_id, T_Y0, (N, d), sub=sub)
+    A, B = _lora_weights(case_id, 0, K, d, d, r)
+    return Case(f"mix_{K}_{N}", case_id, N, K, r, 1, 2.0, [Target("proj", d, d, A, B, x, y0)], idx=idx)
+
+
 def zipf_logits(case_id: int, N: int, K: int, s: float = 1.1, sub: int = 0) -> np.ndarray:
     """Biased random router: logits ln p_e + G with G ~ Gumbel(0,1) and p_e ~ (e+1)^-s."""
     p = (np.arange(1, K + 1, dtype=np.float64) ** -s)

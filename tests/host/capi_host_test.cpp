@@ -99,7 +99,8 @@ static void apply_writes(const ApplyLaunch& a) {
     return;
   }
   if (a.path == kPathTile || (a.path == kPathGrouped && a.k == 1)) return;  // no workspace
-  if (a.path == kPathGrouped && use_gm(a.k, a.K, a.tgt.r_pad)) {
+  if (gm_path(a.path, a.k, a.K, a.tgt.r_pad)) {
+    if (a.k == 1) return;  // one pass, no workspace
     rank_sort_writes(ws + p.sort_off, P, a.k, a.K);
     if (!a.y_f32) write_span<float>(ws + p.z_off, 0, (size_t)a.N * a.tgt.d_out, "z");
     return;
@@ -503,7 +504,8 @@ int main() {
         for (int N : {0, 1, 63, 64, 2048, 4096, 4097, 8192, 8193, 65536})
           test_step(K, r, 4096, 4096, N, layout);
   test_step(4, 16, 512, 1536, 5000, MOLORA_LAYOUT_DIRECT);
-  for (int path : {MOLORA_PATH_AUTO, MOLORA_PATH_GROUPED, MOLORA_PATH_SKINNY, MOLORA_PATH_TILE, MOLORA_PATH_BLOCK})
+  for (int path : {MOLORA_PATH_AUTO, MOLORA_PATH_GROUPED, MOLORA_PATH_SKINNY, MOLORA_PATH_TILE, MOLORA_PATH_BLOCK,
+                   MOLORA_PATH_GROUPED_FIXED})
     for (int K : {1, 4, 16, 64})
       for (int r : {8, 16, 48, 64})
         for (int k : {1, 2, 3, 4, 8})

@@ -5,7 +5,7 @@ and only marshal arguments.  The library must be built first (``__graft_entry__.
 importing the functions does not load it, calling one does, and a missing library raises.
 """
 from .binding import (  # noqa: F401
-    BF16, F32, LAYOUT_DIRECT, LAYOUT_INDIRECT, PATH_AUTO, PATH_BLOCK, PATH_GROUPED, PATH_SKINNY, PATH_TILE,
+    BF16, F32, LAYOUT_DIRECT, LAYOUT_INDIRECT, PATH_AUTO, PATH_BLOCK, PATH_GROUPED, PATH_SKINNY, PATH_TILE, PATH_GROUPED_FIXED,
     HotSet, MoloraError, exported_symbols, load_library, LIB_PATH, NOALLOC_SCRATCH_BYTES,
     MOLORA_OK, MOLORA_EINVAL, MOLORA_ENOTSUP, MOLORA_ENOSPC, MOLORA_EHIP,
     molora_apply, molora_apply_multi, molora_apply_path, molora_apply_multi_workspace, molora_apply_workspace, molora_dispatch,

@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_PKG, "libmolora.so")
 
 MOLORA_OK, MOLORA_EINVAL, MOLORA_ENOTSUP, MOLORA_ENOSPC, MOLORA_EHIP = range(5)
 LAYOUT_DIRECT, LAYOUT_INDIRECT = 0, 1
-PATH_AUTO, PATH_GROUPED, PATH_SKINNY, PATH_TILE, PATH_BLOCK = 0, 1, 2, 3, 4
+PATH_AUTO, PATH_GROUPED, PATH_SKINNY, PATH_TILE, PATH_BLOCK, PATH_GROUPED_FIXED = 0, 1, 2, 3, 4, 5
 BF16, F32 = 0, 1
 
 _c_p = ctypes.c_void_p

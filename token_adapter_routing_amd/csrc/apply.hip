@@ -1457,7 +1457,7 @@ hipError_t launch_apply(const ApplyLaunch& a, hipStream_t s) {
     return err;
   }
 
-  if (a.path == 1 && use_gm(a.k, a.K, a.tgt.r_pad)) {
+  if (gm_path(a.path, a.k, a.K, a.tgt.r_pad)) {
     // 64-row grouped tiles.  k > 1: pass j applies the j-th routed pair of every token, over
     // the (rank, adapter) order of the slot sort; pass 0 reads y0, the last pass writes y and
     // the passes in between carry the sum in fp32 (in y itself when y is fp32, else in z), so a
@@ -1465,17 +1465,18 @@ hipError_t launch_apply(const ApplyLaunch& a, hipStream_t s) {
     const bool in_place = (a.y0 == a.y);
     GMArgs ga;
     ga.tgt = a.tgt; ga.x = a.x; ga.N = a.N; ga.k = a.k; ga.scale = a.scale; ga.perm = a.perm; ga.nkeys = a.K;
-    // equal row ranges of at most 64 rows (at least 16 while that leaves CUs idle), a multiple
-    // of 8 for the XCD mapping; column slices while there are fewer than 256 workgroups
+    // row tiles per segment (a multiple of 8 workgroups for the XCD mapping); column slices
+    // while there are fewer than 256 workgroups
     const long long rows_max = a.k == 1 ? P : a.N;  // rows of one pass
-    long long nwg = (rows_max + kGMRows - 1) / kGMRows;
-    if (nwg < 256) nwg = std::min<long long>(256, (rows_max + 15) / 16);
-    nwg = (nwg + 7) / 8 * 8;
+    const GMTiling tl = gm_tiling(a.path, rows_max, a.K);
+    const long long nwg = (tl.max_tiles + 7) / 8 * 8;
     const int nblk = a.tgt.d_out / kColBlock;
     int cg = 1;
     while (nwg * cg < 256 && nblk % (2 * cg) == 0 && nblk / (2 * cg) >= 2) cg *= 2;
     ga.col_groups = cg;
     ga.nwg = (int)nwg;
+    ga.tile_rows = tl.rows;
+    ga.fixed = tl.fixed;
     const int grid = (int)nwg * cg;
     auto pass = [&](const void* src, bool src_f32, void* dst, bool dst_f32) {
       ga.y0 = src;

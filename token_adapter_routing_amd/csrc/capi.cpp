@@ -302,7 +302,7 @@ int molora_apply_workspace(const molora_hotset* hs, int target, int N, int k, in
   if (hs == nullptr) return fail(MOLORA_EINVAL, "hot set is NULL");
   if (target < 0 || target >= hs->n_targets) return fail(MOLORA_EINVAL, "target %d outside [0, %d)", target, hs->n_targets);
   if (N < 0 || k < 1 || k > MOLORA_MAX_TOPK || k > hs->K) return fail(MOLORA_EINVAL, "bad N=%d or k=%d", N, k);
-  if (path < MOLORA_PATH_AUTO || path > MOLORA_PATH_BLOCK) return fail(MOLORA_EINVAL, "unknown path %d", path);
+  if (path < MOLORA_PATH_AUTO || path > MOLORA_PATH_GROUPED_FIXED) return fail(MOLORA_EINVAL, "unknown path %d", path);
   if (y_dtype != MOLORA_BF16 && y_dtype != MOLORA_F32) return fail(MOLORA_EINVAL, "unknown dtype");
   *bytes = molora::apply_ws_bytes(N, k, hs->K, hs->r_pad, hs->tg[target].d_in, hs->tg[target].d_out,
                                   y_dtype == MOLORA_F32, path);
@@ -314,7 +314,7 @@ int molora_apply_path(const molora_hotset* hs, int target, int N, int k, int pat
   if (hs == nullptr) return fail(MOLORA_EINVAL, "hot set is NULL");
   if (target < 0 || target >= hs->n_targets) return fail(MOLORA_EINVAL, "target %d outside [0, %d)", target, hs->n_targets);
   if (N < 0 || k < 1 || k > MOLORA_MAX_TOPK || k > hs->K) return fail(MOLORA_EINVAL, "bad N=%d or k=%d", N, k);
-  if (path < MOLORA_PATH_AUTO || path > MOLORA_PATH_BLOCK) return fail(MOLORA_EINVAL, "unknown path %d", path);
+  if (path < MOLORA_PATH_AUTO || path > MOLORA_PATH_GROUPED_FIXED) return fail(MOLORA_EINVAL, "unknown path %d", path);
   *resolved = molora::apply_resolve_path(N, k, path, hs->K, hs->r_pad);
   return ok();
 }
@@ -329,7 +329,7 @@ int molora_apply(const molora_hotset* hs, int target, const void* x, const void*
   if ((long long)N * k >= (1ll << 31)) return fail(MOLORA_ENOTSUP, "N*k too large");
   if ((y0_dtype != MOLORA_BF16 && y0_dtype != MOLORA_F32) || (y_dtype != MOLORA_BF16 && y_dtype != MOLORA_F32))
     return fail(MOLORA_EINVAL, "unknown dtype");
-  if (path < MOLORA_PATH_AUTO || path > MOLORA_PATH_BLOCK) return fail(MOLORA_EINVAL, "unknown path %d", path);
+  if (path < MOLORA_PATH_AUTO || path > MOLORA_PATH_GROUPED_FIXED) return fail(MOLORA_EINVAL, "unknown path %d", path);
   if ((path == MOLORA_PATH_TILE || path == MOLORA_PATH_BLOCK) && hs->K > molora::kApplyTileMaxAdapters)
     return fail(MOLORA_ENOTSUP, "the tile and block paths support K <= %d", molora::kApplyTileMaxAdapters);
   if (y0 == y && y0_dtype != y_dtype) return fail(MOLORA_EINVAL, "in-place apply needs y0_dtype == y_dtype");
@@ -387,7 +387,7 @@ int molora_apply_multi_workspace(const molora_hotset* hs, int n, const int* targ
   const int rc = check_multi_targets(hs, n, targets, d_in, d_out);
   if (rc != MOLORA_OK) return rc;
   if (N < 0 || k < 1 || k > MOLORA_MAX_TOPK || k > hs->K) return fail(MOLORA_EINVAL, "bad N=%d or k=%d", N, k);
-  if (path < MOLORA_PATH_AUTO || path > MOLORA_PATH_BLOCK) return fail(MOLORA_EINVAL, "unknown path %d", path);
+  if (path < MOLORA_PATH_AUTO || path > MOLORA_PATH_GROUPED_FIXED) return fail(MOLORA_EINVAL, "unknown path %d", path);
   if (y_dtype != MOLORA_BF16 && y_dtype != MOLORA_F32) return fail(MOLORA_EINVAL, "unknown dtype");
   *bytes = molora::apply_multi_plan(n, d_in, d_out, N, k, hs->K, hs->r_pad, y_dtype == MOLORA_F32, path).total;
   return ok();
@@ -405,7 +405,7 @@ int molora_apply_multi(const molora_hotset* hs, int n, const int* targets, const
   if ((long long)N * k >= (1ll << 31)) return fail(MOLORA_ENOTSUP, "N*k too large");
   if ((y0_dtype != MOLORA_BF16 && y0_dtype != MOLORA_F32) || (y_dtype != MOLORA_BF16 && y_dtype != MOLORA_F32))
     return fail(MOLORA_EINVAL, "unknown dtype");
-  if (path < MOLORA_PATH_AUTO || path > MOLORA_PATH_BLOCK) return fail(MOLORA_EINVAL, "unknown path %d", path);
+  if (path < MOLORA_PATH_AUTO || path > MOLORA_PATH_GROUPED_FIXED) return fail(MOLORA_EINVAL, "unknown path %d", path);
   if ((path == MOLORA_PATH_TILE || path == MOLORA_PATH_BLOCK) && hs->K > molora::kApplyTileMaxAdapters)
     return fail(MOLORA_ENOTSUP, "the tile and block paths support K <= %d", molora::kApplyTileMaxAdapters);
   if (x == nullptr || y0 == nullptr || y == nullptr) return fail(MOLORA_EINVAL, "x, y0 or y array is NULL");

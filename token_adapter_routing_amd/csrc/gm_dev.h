@@ -2,10 +2,10 @@
 // right, tokens grouped by their selected adapter and one grouped GEMM per adapter; Table 10
 // shapes).
 //
-// The rows of a pass (a grouped order, adapter by adapter) are split into nwg equal ranges,
-// one per workgroup and column slice; a range that crosses a segment boundary is handled as
-// one sub-tile per adapter.  Equal ranges keep every workgroup's HBM traffic the same, so a
-// launch of 256 ranges finishes in one round on 256 CUs.
+// The rows of a pass (a grouped order, adapter by adapter) are cut into tiles of at most 64
+// rows, one per workgroup and column slice, that never span two adapters: each adapter's
+// segment gets ceil(count / bound) tiles of equal height (the bound aims at 256 tiles per pass,
+// one round on 256 CUs), or, for the fixed-tiling comparator, 64-row tiles.
 //
 // A workgroup (8 waves) takes a sub-tile: wave w works on row block rb = w % 4 (16 rows) and
 // half hf = w / 4.  In the shrink, half hf takes one half of the reduction steps; in the
@@ -42,7 +42,9 @@ struct GMArgs {
   const float* wts;         // row -> gate weight
   float scale;
   int col_groups;           // output-column slices
-  int nwg;                  // row ranges (a multiple of 8); grid = nwg * col_groups
+  int nwg;                  // row tiles (a multiple of 8, at least the tiles of a pass); grid = nwg * col_groups
+  int tile_rows;            // tile height bound (GMTiling::rows)
+  int fixed;                // GMTiling::fixed
 };
 
 template <int RB>
@@ -298,8 +300,10 @@ __device__ void gm_tile(const GMArgs& a, GMLds<RB>& L, int e, int row0, int nrow
   __syncthreads();  // the next sub-tile reuses the buffers
 }
 
-// The workgroup's row range and column slice; one sub-tile per segment the range crosses
-// (at most 64 rows each).
+// The workgroup's row tile and column slice.  Segment e (adapter e of the pass) of count c is
+// cut into nt = ceil(c / tile_rows) tiles: balanced (tile i: rows c*i/nt .. c*(i+1)/nt) or,
+// fixed, tile_rows rows each but the last; the tiles are numbered segment by segment, so
+// consecutive tiles (which run on one XCD) mostly share their adapter in its L2.
 template <int RB, bool INDIRECT, bool Y0F32, bool YF32>
 __device__ void gm_range(const GMArgs& a, GMLds<RB>& L) {
   const int lane = threadIdx.x & 63;
@@ -307,23 +311,26 @@ __device__ void gm_range(const GMArgs& a, GMLds<RB>& L) {
   const int per_xcd = a.nwg >> 3;
   const int g = slot % a.col_groups;
   const int w = xcd * per_xcd + slot / a.col_groups;
-  // segment starts of the pass's keys, one per lane (nkeys <= 64), and the pass's end
-  const int ov = lane < a.nkeys ? a.offsets[a.key0 + lane] : 0x7fffffff;
-  const int endv = a.offsets[a.key0 + a.nkeys];
-  const int base = __shfl(ov, 0, kWave), total = endv - base;
-  const int lo = base + (int)((long long)total * w / a.nwg);
-  const int hi = base + (int)((long long)total * (w + 1) / a.nwg);
-  const int cols = a.tgt.d_out / a.col_groups;
-  for (int r = lo; r < hi;) {
-    // adapter of row r: the number of segment starts 1 .. nkeys-1 at or below r
-    const uint64_t m = __ballot(lane >= 1 && lane < a.nkeys && ov <= r);
-    const int e = __popcll(m);
-    const int nxt = __shfl(ov, min(e + 1, kWave - 1), kWave);
-    const int seg_end = e + 1 < a.nkeys ? nxt : endv;
-    const int end = min(min(hi, seg_end), r + kGMRows);
-    gm_tile<RB, INDIRECT, Y0F32, YF32>(a, L, e, r, end - r, g * cols, cols);
-    r = end;
+  const int M = a.tile_rows;
+  const int s0l = lane < a.nkeys ? a.offsets[a.key0 + lane] : 0;
+  const int cl = lane < a.nkeys ? a.offsets[a.key0 + lane + 1] - s0l : 0;
+  const int ntl = (cl + M - 1) / M;
+  const int incl = wave_incl_scan(ntl, lane);
+  const uint64_t m = __ballot(lane < a.nkeys && w >= incl - ntl && w < incl);
+  if (m == 0) return;  // past the pass's tiles (the same answer in every wave)
+  const int e = __builtin_ctzll(m);
+  const int s0 = __shfl(s0l, e, kWave), c = __shfl(cl, e, kWave), nt = __shfl(ntl, e, kWave);
+  const int i = w - (__shfl(incl, e, kWave) - nt);
+  int r0, r1;
+  if (a.fixed) {
+    r0 = s0 + i * M;
+    r1 = min(s0 + c, r0 + M);
+  } else {
+    r0 = s0 + (int)((long long)c * i / nt);
+    r1 = s0 + (int)((long long)c * (i + 1) / nt);
   }
+  const int cols = a.tgt.d_out / a.col_groups;
+  gm_tile<RB, INDIRECT, Y0F32, YF32>(a, L, e, r0, r1 - r0, g * cols, cols);
 }
 
 }  // namespace molora

@@ -33,7 +33,7 @@ constexpr int kApplyMaxMulti = 8;          // targets of one molora_apply_multi 
 constexpr size_t kScratchBytes = size_t(8) << 20;  // device scratch of the allocation-free step
                                                    // (MOLORA_NOALLOC_SCRATCH_BYTES)
 
-enum { kPathAuto = 0, kPathGrouped = 1, kPathSkinny = 2, kPathTile = 3, kPathBlock = 4 };
+enum { kPathAuto = 0, kPathGrouped = 1, kPathSkinny = 2, kPathTile = 3, kPathBlock = 4, kPathGroupedFixed = 5 };
 
 // Per-target adapter addressing, as the kernels see it.
 struct TargetDev {
@@ -103,6 +103,17 @@ int apply_multi_resolve_path(int n, int N, int k, int path, int K, int r_pad);
 int skinny_splits(int d_in);
 // 64-row grouped tiles (r > 32, or k > 1 with k*K <= 64)
 bool use_gm(int k, int K, int r_pad);
+// The resolved path runs the 64-row grouped kernel: the grouped path where use_gm holds, and
+// the fixed-tiling comparator wherever its rank passes apply (k == 1 or k*K <= 64).
+bool gm_path(int path, int k, int K, int r_pad);
+// Row tiles of the 64-row grouped kernel: per segment (adapter) of a pass, ceil(count / rows)
+// tiles, balanced inside the segment (adaptive) or of exactly `rows` rows but the last (fixed).
+struct GMTiling {
+  int rows;      // tile height bound (16 .. 64)
+  int fixed;     // 1: fixed 64-row tiles per segment
+  long long max_tiles;  // upper bound on the tiles of a pass: ceil(rows_of_pass / rows) + keys
+};
+GMTiling gm_tiling(int path, long long rows_of_pass, int nkeys);
 
 // Rank sort of k > 1 (grouped and skinny paths): counts2 [k*K] and offsets2 [k*K+1] in a
 // 256-byte-aligned head, then perm2 [P] int32 and w2 [P] fp32, then the chip-wide sort's

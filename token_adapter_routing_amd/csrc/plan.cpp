@@ -81,6 +81,28 @@ int skinny_splits(int d_in) {
 
 bool use_gm(int k, int K, int r_pad) { return (k > 1 && k * K <= 64) || (k == 1 && r_pad > 32); }
 
+bool gm_path(int path, int k, int K, int r_pad) {
+  if (path == kPathGrouped) return use_gm(k, K, r_pad);
+  return path == kPathGroupedFixed && (k == 1 || k * K <= 64);
+}
+
+// Adaptive: the tile height bound aims at 256 tiles over the pass (one round on the chip),
+// between 16 and 64 rows; every segment is then cut into ceil(count / rows) tiles of equal
+// height, so no tile spans two adapters and a small segment gets one short tile.  Fixed: 64-row
+// tiles per segment whatever its size (the fixed-tiling comparator).
+GMTiling gm_tiling(int path, long long rows_of_pass, int nkeys) {
+  GMTiling t{};
+  t.fixed = path == kPathGroupedFixed ? 1 : 0;
+  if (t.fixed) {
+    t.rows = 64;
+  } else {
+    const long long per = (rows_of_pass + 255) / 256;
+    t.rows = (int)std::min<long long>(64, std::max<long long>(16, (per + 15) / 16 * 16));
+  }
+  t.max_tiles = (rows_of_pass + t.rows - 1) / t.rows + nkeys;
+  return t;
+}
+
 RankSortPlan rank_sort_plan(long long P, int k, int K) {
   RankSortPlan s{};
   s.counts2_off = 0;
@@ -103,7 +125,7 @@ ApplyPlan apply_plan(int N, int k, int K, int r_pad, int d_in, int d_out, bool y
     a.total = a.block_bytes;
     return a;
   }
-  if (a.path == kPathGrouped && use_gm(k, K, r_pad)) {
+  if (gm_path(a.path, k, K, r_pad)) {
     if (k == 1) return a;
     a.sort_off = 0;
     a.sort = rank_sort_plan(P, k, K);
