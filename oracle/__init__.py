@@ -13,4 +13,7 @@ from .molora_oracle import (  # noqa: F401
     apply,
     apply_masked_passes,
     pairs_of,
+    apply_backward,
+    route_topk_backward,
+    router_backward,
 )

@@ -23,6 +23,12 @@ Per-Token Adapter Routing"):
 * the abstract (all pages): per-token routing does work N for N tokens,
   per-sequence routing does K * N for K adapter types (one masked pass per
   adapter), giving the second formulation ``apply_masked_passes``.
+* thelatestinai.com, Figure 2 read backwards and Table 13 (the router is
+  trained without labels, so gradients reach the adapters, the gate weights
+  and the router): ``apply_backward``, ``route_topk_backward`` and
+  ``router_backward`` are the exact derivatives of ``apply``, of the
+  renormalised softmax of ``route_topk`` (selection held fixed) and of
+  ``router_logits``.
 
 Readings where the pages are silent (each is also listed in the design notes):
 half-open vocabulary ranges and unrouted ids outside them; ReLU in the router;
@@ -203,3 +209,83 @@ def apply_masked_passes(y0, x, A, B, scale: float, idx, w):
         mass = np.where(idx2 == e, w2, 0.0).sum(axis=1)
         y += (mass * scale)[:, None] * ((x @ A[e]) @ B[e])
     return y
+
+
+# --------------------------------------------------------------------------- backward
+
+def apply_backward(x, gy, A, B, scale: float, perm, perm_w, offsets, k: int):
+    """Derivatives of ``apply`` given dL/dy = ``gy`` (thelatestinai.com, Figure 2
+    with the grouping reused backwards; Table 13: adapters and router learn
+    from the loss).
+
+    For a routed pair p = (token t, adapter e, gate weight w_p) with
+    c_p = w_p * scale, the forward adds c_p * (x_t A_e) B_e to y_t.  With
+    h_p = x_t A_e and g_p = gy_t B_e^T (both [r]):
+      dL/dA_e  = sum over e's pairs of  outer(x_t, c_p g_p)      [d_in][r]
+      dL/dB_e  = sum over e's pairs of  outer(c_p h_p, gy_t)     [r][d_out]
+      dL/dx_t  = sum over t's pairs of  c_p g_p A_e^T            [d_in]
+                 (the adapters' part only; y0's own path is the caller's)
+      dL/dw_p  = scale * (h_p . g_p)
+    Unrouted pairs get dL/dw_p = 0.  All fp64.  Returns (dx [N][d_in],
+    dA [K][d_in][r], dB [K][r][d_out], dw [N*k] in pair order)."""
+    x = np.asarray(x, dtype=np.float64)
+    gy = np.asarray(gy, dtype=np.float64)
+    N = x.shape[0]
+    K = len(offsets) - 1
+    dx = np.zeros_like(x)
+    dA = np.zeros(np.shape(A), dtype=np.float64)
+    dB = np.zeros(np.shape(B), dtype=np.float64)
+    dw = np.zeros(N * k, dtype=np.float64)
+    for e in range(K):
+        q0, q1 = int(offsets[e]), int(offsets[e + 1])
+        if q1 == q0:
+            continue
+        pid = np.asarray(perm[q0:q1], dtype=np.int64)
+        t = pid // k
+        c = np.asarray(perm_w[q0:q1], dtype=np.float64) * scale
+        h = x[t] @ A[e]
+        g = gy[t] @ B[e].T
+        dB[e] = (c[:, None] * h).T @ gy[t]
+        dA[e] = x[t].T @ (c[:, None] * g)
+        np.add.at(dx, t, (c[:, None] * g) @ A[e].T)
+        dw[pid] = scale * np.sum(h * g, axis=1)
+    return dx, dA, dB, dw
+
+
+def route_topk_backward(w, idx, dw, K: int):
+    """dL/dlogits through the softmax over the k selected logits of
+    ``route_topk`` (thelatestinai.com, Table 1 TopK(g_theta(x)) and Figure 2's
+    weighted sum), with the selection held fixed (it is piecewise constant in
+    the logits).  For a token with selected weights w_j and incoming dL/dw_j,
+    the selected logit of slot j receives w_j * (dL/dw_j - sum_i w_i dL/dw_i);
+    unselected logits receive 0.  ``w``/``dw`` [N][k] fp64, ``idx`` [N][k].
+    Returns [N][K] fp64."""
+    w = np.asarray(w, dtype=np.float64)
+    dw = np.asarray(dw, dtype=np.float64)
+    idx = np.asarray(idx, dtype=np.int64)
+    N = w.shape[0]
+    mean = np.sum(w * dw, axis=1, keepdims=True)
+    dl = np.zeros((N, K), dtype=np.float64)
+    np.put_along_axis(dl, idx, w * (dw - mean), axis=1)
+    return dl
+
+
+def router_backward(x, W1, b1, W2, dlogits):
+    """Derivatives of ``router_logits`` (logits = ReLU(x W1 + b1) W2 + b2, the
+    MLP d -> H -> K read from Table 1's routing cost) given dL/dlogits.
+    ``x`` [N][d], ``W1`` [d][H], ``W2`` [H][K], fp64; ``b1`` may be None.  The
+    ReLU's derivative is taken as 1 where its input is > 0, else 0.
+    Returns (dW1 [d][H], db1 [H], dW2 [H][K], db2 [K], dx [N][d])."""
+    x = np.asarray(x, dtype=np.float64)
+    dl = np.asarray(dlogits, dtype=np.float64)
+    a = x @ W1
+    if b1 is not None:
+        a = a + b1
+    hdn = np.maximum(a, 0.0)
+    dW2 = hdn.T @ dl
+    db2 = dl.sum(axis=0)
+    da = (dl @ W2.T) * (a > 0.0)
+    dW1 = x.T @ da
+    db1 = da.sum(axis=0)
+    dx = da @ W1.T
+    return dW1, db1, dW2, db2, dx
