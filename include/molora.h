@@ -359,6 +359,58 @@ int molora_step_vocab_noalloc(const molora_hotset *hs, int target, const int32_t
 int molora_seqpass_meta(const int32_t *idx, int N, int K, int32_t *offsets, int32_t *perm,
                         float *perm_w, void *stream);
 
+/* ------------------------------------------------------------------------
+ * Backward of the routed LoRA (thelatestinai.com, Figure 2: the grouping by
+ * selected adapter serves the gradients too, read backwards; Table 13: the
+ * adapters and the router are trained from the loss, without routing labels).
+ *
+ * molora_hotset_init_transposed builds the transposed twin of a hot set: the
+ * same arguments as molora_hotset_init (the same targets, A and B in their
+ * forward layouts), but target t of the result maps d_out -> d_in with
+ * adapter e = (B_e^T, A_e^T).  molora_apply on it computes
+ * y0 + sum w * scale * (x B_e^T) A_e^T, which with x = dL/dy is the adapters'
+ * part of dL/dx.  molora_hotset_bytes of the forward targets sizes its slab
+ * (the same bytes); molora_hotset_load on the twin takes A and B in their
+ * forward layouts as well.  Errors as molora_hotset_init.
+ *
+ * molora_backward, for one target of a forward hot set `hs` and its twin
+ * `hs_t` (same K, r, scale), with the forward's routing (offsets, perm,
+ * perm_w, inv of molora_dispatch, as given to molora_apply) and gy = dL/dy:
+ *   x    device bf16 [N][d_in]   the forward's input
+ *   gy   device bf16 [N][d_out]  dL/dy
+ *   dx0  device [N][d_in] (dx0_dtype), the rest of dL/dx (e.g. the base
+ *        layer's); dx = dx0 + sum over the token's pairs of
+ *        w * scale * (gy B_e^T) A_e^T, written in dx_dtype (bf16 or fp32;
+ *        dx may equal dx0 when the dtypes agree).  dx NULL: skipped.
+ *   dA   device fp32 [K][d_in][r] out or NULL: sum over adapter e's pairs of
+ *        outer(x_t, w * scale * gy_t B_e^T); an adapter without pairs gets 0
+ *   dB   device fp32 [K][r][d_out] out or NULL: sum over e's pairs of
+ *        outer(w * scale * x_t A_e, gy_t)
+ *   dw   device fp32 [N*k] out or NULL: dL/dw of pair p = t*k + s, i.e.
+ *        scale * (x_t A_e) . (gy_t B_e^T); 0 for unrouted pairs.  Feed it to
+ *        molora_route_topk_backward for the router's gradient.
+ *   ws   device workspace of molora_backward_workspace() bytes, 256-byte
+ *        aligned, no initial contents (NULL allowed only when N = 0 and dA,
+ *        dB are NULL).  Calls sharing it must not overlap.
+ * Products are bf16 x bf16 with fp32 accumulation; the per-pair vectors
+ * w*scale*h and w*scale*g enter the weight gradients as bf16 hi + lo pairs
+ * (about fp32 accuracy).  Sums over pairs run in a fixed order: results are
+ * deterministic.  Asynchronous on `stream`, no allocation, capturable.
+ * Errors (nothing enqueued): mismatched hot sets, shapes or dtypes, NULL or
+ * misaligned required pointers -> MOLORA_EINVAL / MOLORA_ENOTSUP; a short
+ * workspace -> MOLORA_ENOSPC.
+ * ------------------------------------------------------------------------ */
+int molora_hotset_init_transposed(molora_hotset **out, int K, int r, float scale, int n_targets,
+                                  const molora_target *targets, int layout, void *slab,
+                                  size_t slab_bytes, void *stream);
+int molora_backward_workspace(const molora_hotset *hs, const molora_hotset *hs_t, int target,
+                              int N, int k, int dx_dtype, size_t *bytes);
+int molora_backward(const molora_hotset *hs, const molora_hotset *hs_t, int target,
+                    const void *x, const void *gy, const void *dx0, int dx0_dtype, void *dx,
+                    int dx_dtype, int N, int k, const int32_t *offsets, const int32_t *perm,
+                    const float *perm_w, const int32_t *inv, float *dA, float *dB, float *dw,
+                    void *ws, size_t ws_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -35,7 +35,7 @@ import numpy as np
 BASE_SEED = 20260316
 
 # tensor ids inside one case (stable: changing them changes every input)
-T_IDS, T_X, T_Y0, T_A, T_B, T_W1, T_B1, T_W2, T_B2, T_LOGITS, T_IDX, T_RUNS, T_CLUSTER = range(13)
+T_IDS, T_X, T_Y0, T_A, T_B, T_W1, T_B1, T_W2, T_B2, T_LOGITS, T_IDX, T_RUNS, T_CLUSTER, T_GY, T_DX0 = range(15)
 
 
 def rng_for(case_id: int, tensor_id: int, sub: int = 0) -> np.random.Generator:
@@ -251,3 +251,9 @@ def small_int_case(N: int, d_in: int, d_out: int, K: int, r: int, seed: int = 7,
     B = g.integers(lo, hi, size=(K, r, d_out)).astype(np.float32)
     y0 = g.integers(-8, 9, size=(N, d_out)).astype(np.float32)
     return to_bf16_bits(x), to_bf16_bits(A), to_bf16_bits(B), to_bf16_bits(y0)
+
+
+def grad_case(case_id: int, N: int, d_in: int, d_out: int, sub: int = 0):
+    """Upstream gradient dL/dy [N][d_out] and the rest of dL/dx [N][d_in] of a backward case,
+    bf16 bits, N(0, 1)."""
+    return (normal_bf16(case_id, T_GY, (N, d_out), sub=sub), normal_bf16(case_id, T_DX0, (N, d_in), sub=sub))

@@ -132,10 +132,42 @@ hipError_t launch_dispatch(const int32_t*, const float*, int P, int K, int32_t*,
   return hipSuccess;
 }
 hipError_t launch_relayout(const uint16_t*, const uint16_t*, int d_in, int d_out, int, int r_pad, uint16_t* At,
-                           uint16_t* Bt, hipStream_t) {
+                           uint16_t* Bt, hipStream_t, bool) {
   ++g_launches;
   write_span<uint16_t>(At, 0, (size_t)r_pad * d_in, "A slot");
   write_span<uint16_t>(Bt, 0, (size_t)d_out * r_pad, "B slot");
+  return hipSuccess;
+}
+hipError_t launch_pair_shrink(const TargetDev& tgt, bool, const uint16_t*, const int32_t*, const int32_t*, int, int,
+                              long long P, float* hpart, int nsplit, hipStream_t) {
+  ++g_launches;
+  write_span<float>(hpart, 0, (size_t)nsplit * P * tgt.r_pad, "pair shrink partials");
+  return hipSuccess;
+}
+// What launch_backward's kernels write into the workspace (backward.hip): the h and g
+// partials, the hi/lo chunk planes, and the weight-gradient partials (dA, then dB, in one
+// region the two reductions take in turn).
+static int g_last_backward_outputs = 0;
+hipError_t launch_backward(const BackwardLaunch& a, hipStream_t) {
+  ++g_launches;
+  const BwdPlan p = bwd_plan(a.N, a.k, a.K, a.tgt.r_pad, a.tgt.d_in, a.tgt.d_out, a.dx_f32, a.dx_path);
+  const long long P = (long long)a.N * a.k;
+  CHECK(a.tgt.d_in == a.tgt_t.d_out && a.tgt.d_out == a.tgt_t.d_in, "twin shapes");
+  g_last_backward_outputs = (a.dA != nullptr) + 2 * (a.dB != nullptr) + 4 * (a.dw != nullptr);
+  const bool need_h = a.dB != nullptr || a.dw != nullptr, need_g = a.dA != nullptr || a.dw != nullptr;
+  if (P > 0) {
+    if (need_h) write_span<float>(a.ws + p.h_off, 0, (size_t)p.nsh * P * a.tgt.r_pad, "bwd h");
+    if (need_g) write_span<float>(a.ws + p.g_off, 0, (size_t)p.nsg * P * a.tgt.r_pad, "bwd g");
+    const size_t planes = (size_t)p.nchunks * 2 * bwd_s_chunk_elems(a.tgt.r_pad, p.Qc);
+    if (a.dA != nullptr) write_span<uint16_t>(a.ws + p.sa_off, 0, planes, "bwd s for dA");
+    if (a.dB != nullptr) write_span<uint16_t>(a.ws + p.sb_off, 0, planes, "bwd s for dB");
+    CHECK(p.Qc % kWStep == 0 && p.Qc >= kWStep, "chunk of %d pairs", p.Qc);
+    CHECK(p.nchunks >= (P + p.Qc - 1) / p.Qc + a.K, "chunk bound");
+  }
+  if (a.dA != nullptr && P > 0)
+    write_span<float>(a.ws + p.part_off, 0, (size_t)p.nchunks * a.tgt.d_in * a.tgt.r_pad, "bwd wgrad part");
+  if (a.dB != nullptr && P > 0)
+    write_span<float>(a.ws + p.part_off, 0, (size_t)p.nchunks * a.tgt.d_out * a.tgt.r_pad, "bwd wgrad part");
   return hipSuccess;
 }
 hipError_t launch_apply(const ApplyLaunch& a, hipStream_t) {
@@ -224,7 +256,9 @@ struct HostHotset {
   std::vector<char> slab;
 };
 
-static bool make_hotset(HostHotset& h, int K, int r, const std::vector<std::pair<int, int>>& dims, int layout) {
+static bool make_hotset(HostHotset& h, int K, int r, const std::vector<std::pair<int, int>>& dims, int layout,
+                        bool transposed = false) {
+  auto init = transposed ? molora_hotset_init_transposed : molora_hotset_init;
   std::vector<molora_target> tg;
   for (auto& d : dims) tg.push_back({d.first, d.second, fake(0x10000), fake(0x20000)});
   size_t bytes = 0;
@@ -235,13 +269,13 @@ static bool make_hotset(HostHotset& h, int K, int r, const std::vector<std::pair
   char* base = h.slab.data();
   base += (256 - reinterpret_cast<uintptr_t>(base) % 256) % 256;
   // a slab one byte short is refused before anything is written
-  rc = molora_hotset_init(&h.hs, K, r, 2.0f, (int)tg.size(), tg.data(), layout, base, bytes - 1, nullptr);
+  rc = init(&h.hs, K, r, 2.0f, (int)tg.size(), tg.data(), layout, base, bytes - 1, nullptr);
   CHECK(rc == MOLORA_ENOSPC && h.hs == nullptr, "short slab accepted");
   g_ws_base = base;  // slot and table writes must land inside [base, base + bytes)
   g_ws_bytes = bytes;
   g_ranges.clear();
-  rc = molora_hotset_init(&h.hs, K, r, 2.0f, (int)tg.size(), tg.data(), layout, base, bytes, nullptr);
-  CHECK(rc == MOLORA_OK, "hotset_init K=%d r=%d layout=%d", K, r, layout);
+  rc = init(&h.hs, K, r, 2.0f, (int)tg.size(), tg.data(), layout, base, bytes, nullptr);
+  CHECK(rc == MOLORA_OK, "hotset_init K=%d r=%d layout=%d transposed=%d", K, r, layout, (int)transposed);
   for (const Range& x : g_ranges) CHECK(x.hi <= bytes, "slab write %s ends at %zu > %zu", x.what.c_str(), x.hi, bytes);
   g_ws_base = nullptr;
   return rc == MOLORA_OK;
@@ -357,6 +391,58 @@ static void test_apply(int K, int r, int d_in, int d_out, int N, int k, int path
   g_ws_base = nullptr;
   free(ws);
   molora_hotset_destroy(h.hs);
+}
+
+static void test_backward(int K, int r, int d_in, int d_out, int N, int k, int dx_dtype, int layout, int outputs) {
+  HostHotset f, t;
+  if (!make_hotset(f, K, r, {{d_in, d_out}}, layout)) return;
+  if (!make_hotset(t, K, r, {{d_in, d_out}}, layout, true)) {
+    molora_hotset_destroy(f.hs);
+    return;
+  }
+  size_t need = 0;
+  int rc = molora_backward_workspace(f.hs, t.hs, 0, N, k, dx_dtype, &need);
+  if (k > K) {
+    CHECK(rc != MOLORA_OK, "backward k > K accepted");
+  } else if (need <= kMaxBuf) {
+    CHECK(rc == MOLORA_OK, "backward_workspace K=%d r=%d N=%d k=%d", K, r, N, k);
+    // swapped or mismatched hot sets are refused before anything is enqueued
+    CHECK(molora_backward_workspace(t.hs, f.hs, 0, N, k, dx_dtype, &need) == MOLORA_EINVAL, "swapped pair accepted");
+    CHECK(molora_backward_workspace(f.hs, f.hs, 0, N, k, dx_dtype, &need) == MOLORA_EINVAL, "forward as twin accepted");
+    rc = molora_backward_workspace(f.hs, t.hs, 0, N, k, dx_dtype, &need);
+    char* ws = static_cast<char*>(exact_alloc(need));
+    g_ws_base = ws;
+    g_ws_bytes = need;
+    g_ranges.clear();
+    void* dx = (outputs & 8) ? fake(0x4000) : nullptr;
+    float* dA = (outputs & 1) ? (float*)fake(0xc000) : nullptr;
+    float* dB = (outputs & 2) ? (float*)fake(0xd000) : nullptr;
+    float* dw = (outputs & 4) ? (float*)fake(0xe000) : nullptr;
+    const int l0 = g_launches;
+    g_last_backward_outputs = -1;
+    rc = molora_backward(f.hs, t.hs, 0, fake(0x2000), fake(0x3000), fake(0x5000), dx_dtype, dx, dx_dtype, N, k,
+                         (int32_t*)fake(0x8000), (int32_t*)fake(0x9000), (float*)fake(0xa000), (int32_t*)fake(0xb000),
+                         dA, dB, dw, ws, need, nullptr);
+    if (outputs == 0) {
+      CHECK(rc == MOLORA_EINVAL && g_launches == l0, "backward without outputs accepted");
+    } else {
+      CHECK(rc == MOLORA_OK, "backward K=%d r=%d d=%d/%d N=%d k=%d outputs=%d", K, r, d_in, d_out, N, k, outputs);
+      const bool wgrads = (outputs & 7) != 0;
+      if (wgrads) CHECK(g_last_backward_outputs == (outputs & 7), "backward outputs %d", g_last_backward_outputs);
+      check_disjoint("backward");
+      if (need > 0 && N > 0) {
+        const int l1 = g_launches;
+        rc = molora_backward(f.hs, t.hs, 0, fake(0x2000), fake(0x3000), fake(0x5000), dx_dtype, dx, dx_dtype, N, k,
+                             (int32_t*)fake(0x8000), (int32_t*)fake(0x9000), (float*)fake(0xa000),
+                             (int32_t*)fake(0xb000), dA, dB, dw, ws, need - 1, nullptr);
+        CHECK(rc == MOLORA_ENOSPC && g_launches == l1, "short backward workspace accepted");
+      }
+    }
+    g_ws_base = nullptr;
+    free(ws);
+  }
+  molora_hotset_destroy(f.hs);
+  molora_hotset_destroy(t.hs);
 }
 
 static void test_multi(int K, int r, int N, int k, int path, int y_dtype) {
@@ -516,6 +602,14 @@ int main() {
     for (int k : {1, 2})
       for (int N : {1, 256, 4096})
         for (int yd : {MOLORA_BF16, MOLORA_F32}) test_multi(4, 16, N, k, path, yd);
+  for (int layout : {MOLORA_LAYOUT_DIRECT, MOLORA_LAYOUT_INDIRECT})
+    for (int K : {1, 4, 16, 64})
+      for (int r : {8, 16, 64})
+        for (int k : {1, 2, 4})
+          for (int N : {0, 1, 100, 2048, 16384})
+            test_backward(K, r, 1024, 2048, N, k, MOLORA_BF16, layout, 15);
+  for (int outputs = 0; outputs < 16; ++outputs) test_backward(4, 16, 512, 256, 777, 2, MOLORA_F32, MOLORA_LAYOUT_DIRECT, outputs);
+  test_backward(16, 64, 4096, 4096, 16384, 1, MOLORA_BF16, MOLORA_LAYOUT_DIRECT, 15);
   free(g_scratch);
   fprintf(stderr, "%d checks, %d failures\n", g_checks, g_fail);
   return g_fail == 0 ? 0 : 1;

@@ -28,7 +28,7 @@ def lib():
 def test_every_declared_symbol_is_exported_and_bound():
     L = lib()
     names = declared_functions()
-    assert len(names) == 18, names
+    assert len(names) == 21, names
     for n in names:
         assert hasattr(L, n), n
     assert sorted(m.exported_symbols()) == names
@@ -96,6 +96,14 @@ def test_host_validation_without_launch():
     # hotset_load: NULL hot set is rejected before any launch
     assert L.molora_hotset_load(nul, 0, 0, ctypes.c_void_p(256), ctypes.c_void_p(256), nul) == 1
     assert L.molora_seqpass_meta(nul, 0, 4, nul, nul, nul, nul) == 0
+    # backward: NULL hot sets; the transposed init refuses a misaligned slab before any launch
+    assert L.molora_backward_workspace(nul, nul, 0, 4, 1, 0, ctypes.byref(sz)) == 1
+    assert b"hot set is NULL" in L.molora_last_error()
+    assert L.molora_backward(nul, nul, 0, nul, nul, nul, 0, nul, 0, 4, 1, nul, nul, nul, nul, nul, nul, nul, nul, 0,
+                             nul) == 1
+    assert L.molora_hotset_init_transposed(ctypes.byref(h), 4, 16, 2.0, 1, tg, 0, ctypes.c_void_p(16), 1 << 20,
+                                           nul) == 1
+    assert b"256-byte" in L.molora_last_error()
 
 
 def test_binding_refuses_cpu_tensors():

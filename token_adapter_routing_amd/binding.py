@@ -60,6 +60,12 @@ _SIGS = {
                                  _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p,  # idx, w, counts, offsets, perm, perm_w, inv
                                  _c_p, _c_sz, _c_p]),  # ws, ws_bytes, stream
     "molora_step_workspace": (_c_i, [_c_p, _c_i, _c_i, ctypes.POINTER(_c_sz)]),
+    "molora_hotset_init_transposed": (_c_i, [ctypes.POINTER(_c_p), _c_i, _c_i, _c_f, _c_i, ctypes.POINTER(MoloraTarget),
+                                             _c_i, _c_p, _c_sz, _c_p]),
+    "molora_backward_workspace": (_c_i, [_c_p, _c_p, _c_i, _c_i, _c_i, _c_i, ctypes.POINTER(_c_sz)]),
+    "molora_backward": (_c_i, [_c_p, _c_p, _c_i, _c_p, _c_p, _c_p, _c_i, _c_p, _c_i, _c_i, _c_i,  # hs .. k
+                               _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p,  # offsets .. dw
+                               _c_p, _c_sz, _c_p]),  # ws, ws_bytes, stream
     "molora_step_vocab_noalloc": (_c_i, [_c_p, _c_i, _c_p, _c_i, _c_p, _c_p, _c_p, _c_i, _c_p, _c_i,  # hs .. y_dtype
                                          _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p,  # idx .. inv
                                          _c_p]),  # stream
@@ -128,10 +134,12 @@ def _dtype_code(t: torch.Tensor) -> int:
 class HotSet:
     """Owns a molora_hotset descriptor and the torch slab it points into."""
 
-    def __init__(self, handle: int, slab: torch.Tensor, K: int, r: int, scale: float, dims, layout: int):
+    def __init__(self, handle: int, slab: torch.Tensor, K: int, r: int, scale: float, dims, layout: int,
+                 transposed: bool = False):
         self.handle = handle
         self.slab = slab
         self.K, self.r, self.scale, self.dims, self.layout = K, r, scale, list(dims), layout
+        self.transposed = transposed  # dims are the forward (d_in, d_out); the twin maps d_out -> d_in
 
     def close(self):
         if self.handle:
@@ -181,6 +189,22 @@ def molora_hotset_init(targets, scale: float, layout: int = LAYOUT_DIRECT, slab:
     _check(lib.molora_hotset_init(ctypes.byref(h), int(K), int(r), float(scale), len(dims), arr, layout,
                                   _ptr(slab, torch.uint8, "slab"), slab.numel(), _stream(stream)))
     return HotSet(h.value, slab, int(K), int(r), float(scale), dims, layout)
+
+
+def molora_hotset_init_transposed(targets, scale: float, layout: int = LAYOUT_DIRECT,
+                                  slab: Optional[torch.Tensor] = None, stream=None) -> HotSet:
+    """The transposed twin of molora_hotset_init(targets): adapter e = (B_e^T, A_e^T), target t
+    mapping d_out -> d_in (the adapters' part of dL/dx is molora_apply on it with x = dL/dy)."""
+    lib = load_library()
+    arr, dims = _targets(targets)
+    K, _, r = targets[0][0].shape
+    nbytes = molora_hotset_bytes(int(K), int(r), dims, layout)
+    if slab is None:
+        slab = torch.empty(nbytes, dtype=torch.uint8, device=targets[0][0].device)
+    h = _c_p()
+    _check(lib.molora_hotset_init_transposed(ctypes.byref(h), int(K), int(r), float(scale), len(dims), arr, layout,
+                                             _ptr(slab, torch.uint8, "slab"), slab.numel(), _stream(stream)))
+    return HotSet(h.value, slab, int(K), int(r), float(scale), dims, layout, transposed=True)
 
 
 def molora_hotset_load(hs: HotSet, target: int, e: int, A: torch.Tensor, B: torch.Tensor, stream=None):
@@ -427,3 +451,49 @@ def molora_seqpass_meta(idx: torch.Tensor, K: int, stream=None):
                                               _ptr(perm, torch.int32, "perm"), _ptr(perm_w, torch.float32, "perm_w"),
                                               _stream(stream)))
     return offsets, perm, perm_w
+
+
+# ----------------------------------------------------------------------------------- backward
+
+def molora_backward_workspace(hs: HotSet, hs_t: HotSet, N: int, k: int = 1, target: int = 0,
+                              dx_dtype=torch.bfloat16) -> int:
+    n = _c_sz()
+    _check(load_library().molora_backward_workspace(hs.handle, hs_t.handle, int(target), int(N), int(k),
+                                                    BF16 if dx_dtype == torch.bfloat16 else F32, ctypes.byref(n)))
+    return n.value
+
+
+def molora_backward(hs: HotSet, hs_t: HotSet, x: torch.Tensor, gy: torch.Tensor, offsets: torch.Tensor,
+                    perm: torch.Tensor, perm_w: torch.Tensor, inv: torch.Tensor, k: int = 1, target: int = 0,
+                    dx0: Optional[torch.Tensor] = None, dx: Optional[torch.Tensor] = None,
+                    dA: Optional[torch.Tensor] = None, dB: Optional[torch.Tensor] = None,
+                    dw: Optional[torch.Tensor] = None, want=("dx", "dA", "dB", "dw"),
+                    ws: Optional[torch.Tensor] = None, stream=None):
+    """Gradients of molora_apply for one target: dx = dx0 + the adapters' part of dL/dx (dx0
+    defaults to zeros of gy's dtype), dA fp32 [K][d_in][r], dB fp32 [K][r][d_out], dw fp32 [N*k].
+    Outputs named in `want` and not given are allocated; the others are skipped."""
+    N = x.shape[0]
+    d_in, d_out = hs.dims[target]
+    dev = x.device
+    if "dx" in want and dx is None:
+        dx = torch.empty(N, d_in, dtype=dx0.dtype if dx0 is not None else gy.dtype, device=dev)
+    if dx is not None and dx0 is None:
+        dx0 = torch.zeros(N, d_in, dtype=dx.dtype, device=dev)
+    if "dA" in want and dA is None:
+        dA = torch.empty(hs.K, d_in, hs.r, dtype=torch.float32, device=dev)
+    if "dB" in want and dB is None:
+        dB = torch.empty(hs.K, hs.r, d_out, dtype=torch.float32, device=dev)
+    if "dw" in want and dw is None:
+        dw = torch.empty(N * k, dtype=torch.float32, device=dev)
+    dx_dtype = dx.dtype if dx is not None else torch.bfloat16
+    need = molora_backward_workspace(hs, hs_t, N, k, target, dx_dtype)
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _check(load_library().molora_backward(
+        hs.handle, hs_t.handle, int(target), _ptr(x, torch.bfloat16, "x"), _ptr(gy, torch.bfloat16, "gy"),
+        _ptr(dx0, None, "dx0"), _dtype_code(dx0) if dx0 is not None else BF16, _ptr(dx, None, "dx"),
+        _dtype_code(dx) if dx is not None else BF16, N, int(k), _ptr(offsets, torch.int32, "offsets"),
+        _ptr(perm, torch.int32, "perm"), _ptr(perm_w, torch.float32, "perm_w"), _ptr(inv, torch.int32, "inv"),
+        _ptr(dA, torch.float32, "dA"), _ptr(dB, torch.float32, "dB"), _ptr(dw, torch.float32, "dw"),
+        _ptr(ws, torch.uint8, "ws"), ws.numel(), _stream(stream)))
+    return dx, dA, dB, dw

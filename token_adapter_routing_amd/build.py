@@ -17,7 +17,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmolora.so")
-SOURCES = ["capi.cpp", "plan.cpp", "route.hip", "dispatch.hip", "apply.hip"]
+SOURCES = ["capi.cpp", "plan.cpp", "route.hip", "dispatch.hip", "apply.hip", "backward.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

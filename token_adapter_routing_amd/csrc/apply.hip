@@ -1002,7 +1002,7 @@ struct ShrinkArgs {
   const uint16_t* x;
   const int32_t* offsets;
   const int32_t* perm;
-  const float* perm_w;
+  const float* perm_w;  // nullptr: weight 1 (the backward's unscaled h and g)
   int K, k;
   float scale;
   float* hpart;  // [nsplit][P][r_pad] fp32, row q = grouped position
@@ -1035,7 +1035,7 @@ __device__ __forceinline__ void shrink_grouped_body(const ShrinkArgs& a, float* 
   __syncthreads();
   // lane (n, G) writes ranks [G * RB * 4, (G + 1) * RB * 4) of row n
   if (valid) {
-    const float wgt = a.perm_w[q] * a.scale;
+    const float wgt = (a.perm_w != nullptr ? a.perm_w[q] : 1.f) * a.scale;
     float* dst = a.hpart + ((long long)sp * a.P + q) * (RB * 16) + G * RB * 4;
 #pragma unroll
     for (int i = 0; i < RB * 4; i += 4) {
@@ -1765,11 +1765,31 @@ hipError_t launch_step_vocab(const StepVocabLaunch& a, hipStream_t s) {
 }
 
 // --------------------------------------------------------------------------------------
+// Per-pair shrink without gate weight or scale: hpart[sp][q] = partial (x_t A_e) of grouped
+// row q over split sp of the reduction (the backward's h and g).
+hipError_t launch_pair_shrink(const TargetDev& tgt, bool indirect, const uint16_t* x, const int32_t* offsets,
+                              const int32_t* perm, int K, int k, long long P, float* hpart, int nsplit,
+                              hipStream_t s) {
+  ShrinkArgs sa;
+  sa.tgt = tgt; sa.x = x; sa.offsets = offsets; sa.perm = perm; sa.perm_w = nullptr;
+  sa.K = K; sa.k = k; sa.scale = 1.f; sa.P = P; sa.nsplit = nsplit; sa.hpart = hpart;
+  const long long tiles = P / kTileRows + K + 1;
+  const int RBv = tgt.r_pad / 16;
+  hipError_t err = hipSuccess;
+  MOLORA_DISPATCH_RB(RBv, MOLORA_DISPATCH_BOOL(indirect, IND, err = (launch_shrink_t<RB, IND>(sa, (int)tiles, s))));
+  return err;
+}
+
+// --------------------------------------------------------------------------------------
 // Hot-set relayout of one adapter.
 //   A [d_in][r] -> swizzled slab blocks (see a_swz_index); ranks r..r_pad-1 are zero.
 //   B [r][d_out] -> B^T [d_out][r_pad] with the columns of each 128-column block permuted
 //   (slab row w holds column b_perm_col(w)); ranks r..r_pad-1 are zero.
-__global__ void relayout_A(const uint16_t* __restrict__ A, uint16_t* __restrict__ As, int d_in, int r, int r_pad) {
+//   Source strides: element (row, rank j) of the [d][r] matrix being laid out is read at
+//   src[row * s_row + j * s_j] (A itself: s_row = r, s_j = 1; the transposed twin's A = B^T
+//   of a forward adapter: s_row = 1, s_j = d).
+__global__ void relayout_A(const uint16_t* __restrict__ A, uint16_t* __restrict__ As, int d_in, int r, int r_pad,
+                           long long s_row, long long s_j) {
   const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= (long long)r_pad * d_in) return;
   const int RB = r_pad / 16;
@@ -1782,23 +1802,34 @@ __global__ void relayout_A(const uint16_t* __restrict__ A, uint16_t* __restrict_
   const int s = (int)v;
   const int j = u * 16 + n;
   const int col = s * kStepK + c * 32 + G * 8 + i;
-  As[idx] = (j < r) ? A[(long long)col * r + j] : (uint16_t)0;
+  As[idx] = (j < r) ? A[(long long)col * s_row + (long long)j * s_j] : (uint16_t)0;
 }
-__global__ void relayout_B(const uint16_t* __restrict__ B, uint16_t* __restrict__ Bt, int d_out, int r, int r_pad) {
+// Element (rank j, column col) of the [r][d] matrix is read at src[j * s_j + col * s_col] (B
+// itself: s_j = d_out, s_col = 1; the twin's B = A^T of a forward adapter: s_j = 1, s_col = r).
+__global__ void relayout_B(const uint16_t* __restrict__ B, uint16_t* __restrict__ Bt, int d_out, int r, int r_pad,
+                           long long s_j, long long s_col) {
   const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= (long long)d_out * r_pad) return;
   const int row = (int)(i / r_pad), j = (int)(i % r_pad);
   const int col = b_perm_col(row);
-  Bt[i] = (j < r) ? B[(long long)j * d_out + col] : (uint16_t)0;
+  Bt[i] = (j < r) ? B[(long long)j * s_j + (long long)col * s_col] : (uint16_t)0;
 }
 
 hipError_t launch_relayout(const uint16_t* A, const uint16_t* B, int d_in, int d_out, int r, int r_pad,
-                           uint16_t* At, uint16_t* Bt, hipStream_t s) {
+                           uint16_t* At, uint16_t* Bt, hipStream_t s, bool transposed) {
   const long long na = (long long)r_pad * d_in, nb = (long long)d_out * r_pad;
-  hipLaunchKernelGGL(relayout_A, dim3((unsigned)((na + 255) / 256)), dim3(256), 0, s, A, At, d_in, r, r_pad);
+  // transposed: the slab adapter (d_in x r, r x d_out) is (B^T, A^T) of the forward adapter
+  // whose A is [d_out][r] and B is [r][d_in]
+  const uint16_t* srcA = transposed ? B : A;
+  const uint16_t* srcB = transposed ? A : B;
+  const long long sa_row = transposed ? 1 : r, sa_j = transposed ? d_in : 1;
+  const long long sb_j = transposed ? 1 : d_out, sb_col = transposed ? r : 1;
+  hipLaunchKernelGGL(relayout_A, dim3((unsigned)((na + 255) / 256)), dim3(256), 0, s, srcA, At, d_in, r, r_pad,
+                     sa_row, sa_j);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(relayout_B, dim3((unsigned)((nb + 255) / 256)), dim3(256), 0, s, B, Bt, d_out, r, r_pad);
+  hipLaunchKernelGGL(relayout_B, dim3((unsigned)((nb + 255) / 256)), dim3(256), 0, s, srcB, Bt, d_out, r, r_pad,
+                     sb_j, sb_col);
   return hipGetLastError();
 }
 

@@ -1,0 +1,346 @@
+// Backward of the routed LoRA on gfx950 (MoLoRA pages, thelatestinai.com, Figure 2: tokens
+// grouped by their selected adapter, each group one grouped GEMM; the same grouping serves the
+// gradients, read backwards; Table 13: adapters and router are trained from the loss alone).
+//
+// For a routed pair q (token t, adapter e, gate weight w, LoRA scale s), with h = x_t A_e and
+// g = gy_t B_e^T:
+//   dA_e = sum_q x_t^T (s w g)      dB_e = sum_q (s w h)^T gy_t      dL/dw_q = s (h . g)
+// dx is the forward apply of the transposed adapters (B^T, A^T) on gy (launched by the C ABI).
+//
+//   pair shrinks  two grouped shrinks (the skinny path's kernel, unscaled) give h and g per pair
+//                 as split partials.
+//   bwd_pairs     a workgroup owns 64 consecutive pairs of one chunk: sums the partials, writes
+//                 dL/dw at the pair id and s w g, s w h as bf16 hi/lo planes [rank][pair] of
+//                 the chunk (pairs past the segment hold zeros).
+//   bwd_wgrad     a workgroup owns (chunk, 128 columns of x or gy): per step of 64 pairs it
+//                 stages the gathered rows transposed in LDS (pairs contiguous, 16-byte groups
+//                 XOR-swizzled by row), and the chunk's hi/lo planes; the 8 waves (16 columns
+//                 each) take D[rank][col] += S^T[rank][pair] X[pair][col] with
+//                 v_mfma_f32_16x16x32_bf16 (hi and lo: fp32-accurate S), and write the
+//                 chunk's partial [col][rank] in fp32.
+//   bwd_reduce    a workgroup owns (adapter, 128 columns): sums the adapter's chunk partials
+//                 in chunk order (deterministic) into dA [K][d_in][r] or dB [K][r][d_out];
+//                 an adapter without pairs gets zeros.
+#include "molora_launch.h"
+#include "molora_dev.h"
+
+namespace molora {
+
+// Chunk cg of the segments cut into ceil(count / Qc) chunks each, numbered segment by
+// segment: its adapter and pair range [q0, q1).  False past the last chunk (wave-uniform).
+__device__ __forceinline__ bool chunk_of(const int32_t* __restrict__ offsets, int K, int Qc, long long cg, int lane,
+                                         int& e, int& q0, int& q1) {
+  const int lo = lane < K ? offsets[lane] : 0;
+  const int cnt = lane < K ? offsets[lane + 1] - lo : 0;
+  const int nch = (cnt + Qc - 1) / Qc;
+  const int incl = wave_incl_scan(nch, lane);
+  const uint64_t m = __ballot(lane < K && cg >= incl - nch && cg < incl);
+  if (m == 0) return false;
+  e = __builtin_ctzll(m);
+  const int lo_e = __shfl(lo, e, kWave), cnt_e = __shfl(cnt, e, kWave);
+  const int first = __shfl(incl, e, kWave) - __shfl(nch, e, kWave);
+  q0 = lo_e + (int)(cg - first) * Qc;
+  q1 = min(lo_e + cnt_e, q0 + Qc);
+  return true;
+}
+
+// ------------------------------------------------------------------------------ pair pass
+struct BwdPairArgs {
+  const float* hp;  // [nsh][P][r_pad] unscaled h partials, or nullptr
+  const float* gp;  // [nsg][P][r_pad] unscaled g partials, or nullptr
+  int nsh, nsg;
+  long long P;
+  const int32_t* offsets;
+  const int32_t* perm;
+  const float* perm_w;
+  const int32_t* inv;
+  int K, r_pad, Qc;
+  float scale;
+  uint16_t* sa;  // chunks of s w g (dA), or nullptr
+  uint16_t* sb;  // chunks of s w h (dB), or nullptr
+  float* dw;     // [P] by pair id, or nullptr
+  long long chunk_blocks;
+  int zero_blocks;
+};
+
+__device__ __forceinline__ void sum_partials(float (&v)[16], const float* __restrict__ p, int ns, long long P, int q,
+                                             int r_pad, int j0, int nj) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) v[i] = 0.f;
+  for (int sp = 0; sp < ns; ++sp) {
+    const float* row = p + ((long long)sp * P + q) * r_pad + j0;
+#pragma unroll
+    for (int i = 0; i < 16; i += 4) {
+      if (i < nj) {
+        const u32x4_t x = ld16(row + i);
+        v[i] += __uint_as_float(x[0]);
+        v[i + 1] += __uint_as_float(x[1]);
+        v[i + 2] += __uint_as_float(x[2]);
+        v[i + 3] += __uint_as_float(x[3]);
+      }
+    }
+  }
+}
+
+__device__ __forceinline__ void put_hilo(uint16_t* __restrict__ plane, size_t lo_off, int Qc, int j, int col,
+                                         float v) {
+  const __bf16 hi = (__bf16)v;
+  const __bf16 lo = (__bf16)(v - (float)hi);
+  plane[(size_t)j * Qc + col] = __builtin_bit_cast(uint16_t, hi);
+  plane[lo_off + (size_t)j * Qc + col] = __builtin_bit_cast(uint16_t, lo);
+}
+
+__global__ __launch_bounds__(256) void bwd_pairs(BwdPairArgs a) {
+  __shared__ float dot[4][64];
+  const int lane = threadIdx.x & 63, jg = threadIdx.x >> 6;
+  if ((long long)blockIdx.x >= a.chunk_blocks) {
+    if (a.dw == nullptr) return;
+    const long long stride = (long long)a.zero_blocks * 256;
+    for (long long p = ((long long)blockIdx.x - a.chunk_blocks) * 256 + threadIdx.x; p < a.P; p += stride)
+      if (a.inv[p] < 0) a.dw[p] = 0.f;
+    return;
+  }
+  const int spc = a.Qc / kWStep;
+  const long long cg = (long long)blockIdx.x / spc;
+  const int col = (int)((long long)blockIdx.x % spc) * kWStep + lane;
+  int e, q0, q1;
+  if (!chunk_of(a.offsets, a.K, a.Qc, cg, lane, e, q0, q1)) return;
+  const int q = q0 + col;
+  const bool valid = q < q1;
+  const int nj = a.r_pad / 4, j0 = jg * nj;
+  float h[16], g[16];
+  if (valid && a.hp != nullptr) sum_partials(h, a.hp, a.nsh, a.P, q, a.r_pad, j0, nj);
+  else
+#pragma unroll
+    for (int i = 0; i < 16; ++i) h[i] = 0.f;
+  if (valid && a.gp != nullptr) sum_partials(g, a.gp, a.nsg, a.P, q, a.r_pad, j0, nj);
+  else
+#pragma unroll
+    for (int i = 0; i < 16; ++i) g[i] = 0.f;
+  const float c = valid ? a.scale * a.perm_w[q] : 0.f;
+  const size_t plane = bwd_s_chunk_elems(a.r_pad, a.Qc);
+  const size_t base = (size_t)cg * 2 * plane;
+  float d = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    if (i < nj) {
+      d += h[i] * g[i];
+      if (a.sa != nullptr) put_hilo(a.sa + base, plane, a.Qc, j0 + i, col, c * g[i]);
+      if (a.sb != nullptr) put_hilo(a.sb + base, plane, a.Qc, j0 + i, col, c * h[i]);
+    }
+  }
+  if (a.dw == nullptr) return;
+  dot[jg][lane] = d;
+  __syncthreads();
+  if (jg == 0 && valid) a.dw[a.perm[q]] = a.scale * (((dot[0][lane] + dot[1][lane]) + dot[2][lane]) + dot[3][lane]);
+}
+
+// ------------------------------------------------------------------------------ weight gradient
+struct BwdWgradArgs {
+  const uint16_t* X;  // [rows][D] bf16 (x for dA, gy for dB)
+  int D;
+  const int32_t* offsets;
+  const int32_t* perm;  // grouped position -> pair id; nullptr: the position is the row
+  int k, K;
+  const uint16_t* S;    // chunks [nchunks][2][r_pad][Qc] bf16 hi / lo
+  int Qc, r_pad, ncb;
+  float* part;          // [nchunks][ncb][128][r_pad] fp32
+};
+
+constexpr int kWThreads = 512;
+
+template <int RB>
+struct WgradLds {
+  uint32_t xt[kWCols][kWStep / 2];        // X^T: row = column of X, dword = two pairs; 16-byte
+                                          // groups (8 pairs) at group ^ (row & 7)
+  u32x4_t st[2][RB * 16][kWStep / 8];     // S^T hi / lo: row = rank, groups at g ^ (row & 7)
+};
+
+template <int RB>
+__global__ __launch_bounds__(kWThreads) void bwd_wgrad(BwdWgradArgs a) {
+  __shared__ WgradLds<RB> L;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const long long cg = (long long)blockIdx.x / a.ncb;
+  const int b = (int)((long long)blockIdx.x % a.ncb);
+  int e, q0, q1;
+  if (!chunk_of(a.offsets, a.K, a.Qc, cg, lane, e, q0, q1)) return;
+  const int n = lane & 15, G = lane >> 4;
+  // staging roles: X rows (2p, 2p+1) of the step, columns [8c, 8c + 8) of the block
+  const int p = threadIdx.x & 31, c = threadIdx.x >> 5;
+  const uint16_t* xcol = a.X + (size_t)b * kWCols + 8 * c;
+  const uint16_t* schunk = a.S + (size_t)cg * 2 * bwd_s_chunk_elems(a.r_pad, a.Qc);
+  constexpr int kSPieces = 2 * RB * 16 * (kWStep / 8);  // 16-byte pieces of S per step
+  auto row_of = [&](int q) {
+    q = min(q, q1 - 1);  // rows past the range: any valid row (their S is zero)
+    return a.perm != nullptr ? a.perm[q] / a.k : q;
+  };
+  u32x4_t xv[2], sv[2];
+  auto load = [&](int qs) {
+    xv[0] = ld16(xcol + (size_t)row_of(qs + 2 * p) * a.D);
+    xv[1] = ld16(xcol + (size_t)row_of(qs + 2 * p + 1) * a.D);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int v = threadIdx.x + i * kWThreads;
+      if (v < kSPieces) {
+        const int pl = v / (RB * 16 * 8), rem = v % (RB * 16 * 8);
+        const int j = rem >> 3, gq = rem & 7;
+        sv[i] = ld16(schunk + (size_t)pl * bwd_s_chunk_elems(a.r_pad, a.Qc) + (size_t)j * a.Qc + (qs - q0) + 8 * gq);
+      }
+    }
+  };
+  auto store = [&]() {
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const int row = 8 * c + s;
+      const uint32_t lo = (s & 1) ? (xv[0][s >> 1] >> 16) : (xv[0][s >> 1] & 0xffffu);
+      const uint32_t hi = (s & 1) ? (xv[1][s >> 1] >> 16) : (xv[1][s >> 1] & 0xffffu);
+      L.xt[row][4 * ((p >> 2) ^ s) + (p & 3)] = lo | (hi << 16);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int v = threadIdx.x + i * kWThreads;
+      if (v < kSPieces) {
+        const int pl = v / (RB * 16 * 8), rem = v % (RB * 16 * 8);
+        const int j = rem >> 3, gq = rem & 7;
+        L.st[pl][j][gq ^ (j & 7)] = sv[i];
+      }
+    }
+  };
+  f32x4_t acc[RB];
+#pragma unroll
+  for (int u = 0; u < RB; ++u) acc[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const int xrow = 16 * wave + n;
+  load(q0);
+  for (int qs = q0; qs < q1; qs += kWStep) {
+    __syncthreads();  // the previous step's operands are consumed
+    store();
+    __syncthreads();
+    if (qs + kWStep < q1) load(qs + kWStep);  // next step's rows land during the products
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const int gq = 4 * ks + G;
+      const u32x4_t xb = *reinterpret_cast<const u32x4_t*>(&L.xt[xrow][4 * (gq ^ (xrow & 7))]);
+#pragma unroll
+      for (int u = 0; u < RB; ++u) {
+        const int j = 16 * u + n;
+        const u32x4_t sh = L.st[0][j][gq ^ (j & 7)];
+        const u32x4_t sl = L.st[1][j][gq ^ (j & 7)];
+        acc[u] = mfma16x16x32(as_bf16x8(sh), as_bf16x8(xb), acc[u]);
+        acc[u] = mfma16x16x32(as_bf16x8(sl), as_bf16x8(xb), acc[u]);
+      }
+    }
+  }
+  // D[rank 16u + 4G + i][column 16 wave + n]
+  float* dst = a.part + (((size_t)cg * a.ncb + b) * kWCols + 16 * wave + n) * a.r_pad + 4 * G;
+#pragma unroll
+  for (int u = 0; u < RB; ++u) {
+    u32x4_t v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = __float_as_uint(acc[u][i]);
+    st16(dst + 16 * u, v);
+  }
+}
+
+// ------------------------------------------------------------------------------ reduction
+struct BwdReduceArgs {
+  const float* part;
+  const int32_t* offsets;
+  int K, Qc, r, r_pad, ncb, D;
+  float* out;
+  int rank_major;  // 0: out [K][D][r] (dA); 1: out [K][r][D] (dB)
+};
+
+__global__ __launch_bounds__(256) void bwd_reduce(BwdReduceArgs a) {
+  const int e = blockIdx.x / a.ncb, b = blockIdx.x % a.ncb;
+  const int lane = threadIdx.x & 63;
+  // chunks of adapter e: [first, first + nch) (every wave computes the same)
+  const int cnt = lane < a.K ? a.offsets[lane + 1] - a.offsets[lane] : 0;
+  const int nchl = (cnt + a.Qc - 1) / a.Qc;
+  const int incl = wave_incl_scan(nchl, lane);
+  const int nch = __shfl(nchl, e, kWave);
+  const int first = __shfl(incl, e, kWave) - nch;
+  const int total = kWCols * a.r;
+  for (int v = threadIdx.x; v < total; v += 256) {
+    int col, j;
+    if (a.rank_major) {
+      j = v / kWCols;
+      col = v % kWCols;
+    } else {
+      col = v / a.r;
+      j = v % a.r;
+    }
+    float sum = 0.f;
+    for (int i = 0; i < nch; ++i)
+      sum += a.part[(((size_t)(first + i) * a.ncb + b) * kWCols + col) * a.r_pad + j];
+    const size_t gcol = (size_t)b * kWCols + col;
+    if (a.rank_major) a.out[((size_t)e * a.r + j) * a.D + gcol] = sum;
+    else a.out[((size_t)e * a.D + gcol) * a.r + j] = sum;
+  }
+}
+
+// ------------------------------------------------------------------------------ host side
+static hipError_t launch_wgrad_reduce(const BackwardLaunch& a, const BwdPlan& plan, const uint16_t* X, int D,
+                                      const uint16_t* S, float* out, int rank_major, hipStream_t s) {
+  const int ncb = D / kWCols;
+  float* part = reinterpret_cast<float*>(a.ws + plan.part_off);
+  if (a.N > 0) {
+    BwdWgradArgs w;
+    w.X = X; w.D = D; w.offsets = a.offsets; w.perm = a.perm; w.k = a.k; w.K = a.K;
+    w.S = S; w.Qc = plan.Qc; w.r_pad = a.tgt.r_pad; w.ncb = ncb; w.part = part;
+    const long long grid = plan.nchunks * ncb;
+    switch (a.tgt.r_pad / 16) {
+      case 1: hipLaunchKernelGGL(bwd_wgrad<1>, dim3((unsigned)grid), dim3(kWThreads), 0, s, w); break;
+      case 2: hipLaunchKernelGGL(bwd_wgrad<2>, dim3((unsigned)grid), dim3(kWThreads), 0, s, w); break;
+      case 3: hipLaunchKernelGGL(bwd_wgrad<3>, dim3((unsigned)grid), dim3(kWThreads), 0, s, w); break;
+      case 4: hipLaunchKernelGGL(bwd_wgrad<4>, dim3((unsigned)grid), dim3(kWThreads), 0, s, w); break;
+      default: return hipErrorInvalidValue;
+    }
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  BwdReduceArgs r;
+  r.part = part; r.offsets = a.offsets; r.K = a.K; r.Qc = plan.Qc; r.r = a.r; r.r_pad = a.tgt.r_pad;
+  r.ncb = ncb; r.D = D; r.out = out; r.rank_major = rank_major;
+  hipLaunchKernelGGL(bwd_reduce, dim3((unsigned)(a.K * ncb)), dim3(256), 0, s, r);
+  return hipGetLastError();
+}
+
+hipError_t launch_backward(const BackwardLaunch& a, hipStream_t s) {
+  const BwdPlan plan = bwd_plan(a.N, a.k, a.K, a.tgt.r_pad, a.tgt.d_in, a.tgt.d_out, a.dx_f32, a.dx_path);
+  const long long P = (long long)a.N * a.k;
+  const bool need_h = a.dB != nullptr || a.dw != nullptr;
+  const bool need_g = a.dA != nullptr || a.dw != nullptr;
+  float* hp = need_h ? reinterpret_cast<float*>(a.ws + plan.h_off) : nullptr;
+  float* gp = need_g ? reinterpret_cast<float*>(a.ws + plan.g_off) : nullptr;
+  uint16_t* sa = a.dA != nullptr ? reinterpret_cast<uint16_t*>(a.ws + plan.sa_off) : nullptr;
+  uint16_t* sb = a.dB != nullptr ? reinterpret_cast<uint16_t*>(a.ws + plan.sb_off) : nullptr;
+  hipError_t err = hipSuccess;
+  if (P > 0) {
+    if (need_h) {
+      err = launch_pair_shrink(a.tgt, a.indirect, a.x, a.offsets, a.perm, a.K, a.k, P, hp, plan.nsh, s);
+      if (err != hipSuccess) return err;
+    }
+    if (need_g) {
+      err = launch_pair_shrink(a.tgt_t, a.indirect_t, a.gy, a.offsets, a.perm, a.K, a.k, P, gp, plan.nsg, s);
+      if (err != hipSuccess) return err;
+    }
+    BwdPairArgs pa;
+    pa.hp = hp; pa.gp = gp; pa.nsh = plan.nsh; pa.nsg = plan.nsg; pa.P = P;
+    pa.offsets = a.offsets; pa.perm = a.perm; pa.perm_w = a.perm_w; pa.inv = a.inv;
+    pa.K = a.K; pa.r_pad = a.tgt.r_pad; pa.Qc = plan.Qc; pa.scale = a.scale;
+    pa.sa = sa; pa.sb = sb; pa.dw = a.dw;
+    pa.chunk_blocks = plan.nchunks * (plan.Qc / kWStep);
+    pa.zero_blocks = a.dw != nullptr ? (int)std::min<long long>((P + 255) / 256, 64) : 0;
+    hipLaunchKernelGGL(bwd_pairs, dim3((unsigned)(pa.chunk_blocks + pa.zero_blocks)), dim3(256), 0, s, pa);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  if (a.dA != nullptr) {
+    err = launch_wgrad_reduce(a, plan, a.x, a.tgt.d_in, sa, a.dA, 0, s);
+    if (err != hipSuccess) return err;
+  }
+  if (a.dB != nullptr) err = launch_wgrad_reduce(a, plan, a.gy, a.tgt.d_out, sb, a.dB, 1, s);
+  return err;
+}
+
+}  // namespace molora

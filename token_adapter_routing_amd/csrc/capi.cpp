@@ -6,6 +6,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <utility>
 #include <new>
 #include <string>
 #include <vector>
@@ -18,6 +19,7 @@ static_assert(MOLORA_NOALLOC_SCRATCH_BYTES == molora::kScratchBytes, "scratch si
 struct molora_hotset {
   int K = 0, r = 0, r_pad = 0, layout = 0, n_targets = 0;
   float scale = 1.f;
+  bool transposed = false;  // holds (B^T, A^T) of the given adapters (molora_hotset_init_transposed)
   std::vector<molora::TargetDev> tg;
   void* slab = nullptr;
   size_t slab_bytes = 0;
@@ -127,8 +129,12 @@ int molora_hotset_bytes(int K, int r, int n_targets, const molora_target* target
   return ok();
 }
 
-int molora_hotset_init(molora_hotset** out, int K, int r, float scale, int n_targets, const molora_target* targets,
-                       int layout, void* slab, size_t slab_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+int hotset_init_impl(molora_hotset** out, int K, int r, float scale, int n_targets, const molora_target* targets,
+                     int layout, void* slab, size_t slab_bytes, void* stream, bool transposed) {
   if (out == nullptr) return fail(MOLORA_EINVAL, "out is NULL");
   *out = nullptr;
   if (layout != MOLORA_LAYOUT_DIRECT && layout != MOLORA_LAYOUT_INDIRECT)
@@ -136,7 +142,11 @@ int molora_hotset_init(molora_hotset** out, int K, int r, float scale, int n_tar
   int rc = check_targets(K, r, n_targets, targets, true);
   if (rc != MOLORA_OK) return rc;
   if (slab == nullptr || !aligned(slab, 256)) return fail(MOLORA_EINVAL, "slab is NULL or not 256-byte aligned");
-  const SlabPlan plan = plan_slab(K, r, n_targets, targets, layout);
+  // the slab's own targets: the twin's target t maps d_out -> d_in
+  std::vector<molora_target> slab_targets(targets, targets + n_targets);
+  if (transposed)
+    for (molora_target& g : slab_targets) std::swap(g.d_in, g.d_out);
+  const SlabPlan plan = plan_slab(K, r, n_targets, slab_targets.data(), layout);
   if (slab_bytes < plan.total)
     return fail(MOLORA_ENOSPC, "slab holds %zu bytes, %zu needed", slab_bytes, plan.total);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
@@ -150,14 +160,15 @@ int molora_hotset_init(molora_hotset** out, int K, int r, float scale, int n_tar
   hs->scale = scale;
   hs->slab = slab;
   hs->slab_bytes = slab_bytes;
+  hs->transposed = transposed;
   char* base = reinterpret_cast<char*>(slab);
   std::vector<std::vector<const void*>> tablesA(n_targets), tablesB(n_targets);
   for (int t = 0; t < n_targets; ++t) {
     const molora_target& g = targets[t];
     const SlabPlan::T& p = plan.t[t];
     molora::TargetDev d{};
-    d.d_in = g.d_in;
-    d.d_out = g.d_out;
+    d.d_in = slab_targets[t].d_in;
+    d.d_out = slab_targets[t].d_out;
     d.r_pad = hs->r_pad;
     for (int e = 0; e < K; ++e) {
       const int slot = (layout == MOLORA_LAYOUT_DIRECT) ? e : indirect_slot(e, K);
@@ -165,7 +176,7 @@ int molora_hotset_init(molora_hotset** out, int K, int r, float scale, int n_tar
       uint16_t* Bt = reinterpret_cast<uint16_t*>(base + p.offB + (size_t)slot * p.sizeB);
       const uint16_t* A = reinterpret_cast<const uint16_t*>(g.A) + (size_t)e * g.d_in * r;
       const uint16_t* B = reinterpret_cast<const uint16_t*>(g.B) + (size_t)e * r * g.d_out;
-      hipError_t err = molora::launch_relayout(A, B, g.d_in, g.d_out, r, hs->r_pad, At, Bt, s);
+      hipError_t err = molora::launch_relayout(A, B, d.d_in, d.d_out, r, hs->r_pad, At, Bt, s, transposed);
       if (err != hipSuccess) {
         delete hs;
         return hip_fail(err, "hot-set relayout");
@@ -209,6 +220,21 @@ int molora_hotset_init(molora_hotset** out, int K, int r, float scale, int n_tar
   return ok();
 }
 
+}  // namespace
+
+extern "C" {
+
+int molora_hotset_init(molora_hotset** out, int K, int r, float scale, int n_targets, const molora_target* targets,
+                       int layout, void* slab, size_t slab_bytes, void* stream) {
+  return hotset_init_impl(out, K, r, scale, n_targets, targets, layout, slab, slab_bytes, stream, false);
+}
+
+int molora_hotset_init_transposed(molora_hotset** out, int K, int r, float scale, int n_targets,
+                                  const molora_target* targets, int layout, void* slab, size_t slab_bytes,
+                                  void* stream) {
+  return hotset_init_impl(out, K, r, scale, n_targets, targets, layout, slab, slab_bytes, stream, true);
+}
+
 int molora_hotset_load(molora_hotset* hs, int target, int e, const void* A, const void* B, void* stream) {
   if (hs == nullptr) return fail(MOLORA_EINVAL, "hs is NULL");
   if (target < 0 || target >= hs->n_targets)
@@ -220,7 +246,7 @@ int molora_hotset_load(molora_hotset* hs, int target, int e, const void* A, cons
   const hipError_t err =
       molora::launch_relayout(static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(B), d.d_in, d.d_out,
                               hs->r, hs->r_pad, hs->slotA[target][e], hs->slotB[target][e],
-                              reinterpret_cast<hipStream_t>(stream));
+                              reinterpret_cast<hipStream_t>(stream), hs->transposed);
   return err == hipSuccess ? ok() : hip_fail(err, "hot-set load");
 }
 
@@ -563,6 +589,126 @@ int molora_step_vocab_noalloc(const molora_hotset* hs, int target, const int32_t
   if (e != hipSuccess) return hip_fail(e, "scratch lookup");
   return molora_step_vocab(hs, target, ids, N, bounds, x, y0, y0_dtype, y, y_dtype, idx, w, counts, offsets, perm,
                            perm_w, inv, scratch, molora::kScratchBytes, stream);
+}
+
+namespace {
+
+// Checks shared by molora_backward_workspace and molora_backward.
+int check_backward_pair(const molora_hotset* hs, const molora_hotset* hs_t, int target, int N, int k) {
+  if (hs == nullptr || hs_t == nullptr) return fail(MOLORA_EINVAL, "hot set is NULL");
+  if (hs->transposed || !hs_t->transposed)
+    return fail(MOLORA_EINVAL, "hs must be a forward hot set and hs_t one built by molora_hotset_init_transposed");
+  if (hs->K != hs_t->K || hs->r != hs_t->r || hs->n_targets != hs_t->n_targets || hs->scale != hs_t->scale)
+    return fail(MOLORA_EINVAL, "hs and hs_t differ in K, r, targets or scale");
+  if (target < 0 || target >= hs->n_targets) return fail(MOLORA_EINVAL, "target %d outside [0, %d)", target, hs->n_targets);
+  if (hs->tg[target].d_in != hs_t->tg[target].d_out || hs->tg[target].d_out != hs_t->tg[target].d_in)
+    return fail(MOLORA_EINVAL, "hs_t's target %d is not the transpose of hs's", target);
+  if (N < 0) return fail(MOLORA_EINVAL, "N=%d < 0", N);
+  if (k < 1 || k > MOLORA_MAX_TOPK || k > hs->K) return fail(MOLORA_ENOTSUP, "k=%d outside [1, min(K, %d)]", k, MOLORA_MAX_TOPK);
+  if ((long long)N * k >= (1ll << 31)) return fail(MOLORA_ENOTSUP, "N*k too large");
+  return MOLORA_OK;
+}
+
+molora::BwdPlan backward_plan(const molora_hotset* hs, int target, int N, int k, bool dx_f32, int* dx_path) {
+  const molora::TargetDev& tg = hs->tg[target];
+  const int path = molora::apply_resolve_path(N, k, MOLORA_PATH_AUTO, hs->K, hs->r_pad);
+  if (dx_path != nullptr) *dx_path = path;
+  return molora::bwd_plan(N, k, hs->K, hs->r_pad, tg.d_in, tg.d_out, dx_f32, path);
+}
+
+}  // namespace
+
+int molora_backward_workspace(const molora_hotset* hs, const molora_hotset* hs_t, int target, int N, int k,
+                              int dx_dtype, size_t* bytes) {
+  if (bytes == nullptr) return fail(MOLORA_EINVAL, "bytes is NULL");
+  const int rc = check_backward_pair(hs, hs_t, target, N, k);
+  if (rc != MOLORA_OK) return rc;
+  if (dx_dtype != MOLORA_BF16 && dx_dtype != MOLORA_F32) return fail(MOLORA_EINVAL, "unknown dtype");
+  *bytes = backward_plan(hs, target, N, k, dx_dtype == MOLORA_F32, nullptr).total;
+  return ok();
+}
+
+int molora_backward(const molora_hotset* hs, const molora_hotset* hs_t, int target, const void* x, const void* gy,
+                    const void* dx0, int dx0_dtype, void* dx, int dx_dtype, int N, int k, const int32_t* offsets,
+                    const int32_t* perm, const float* perm_w, const int32_t* inv, float* dA, float* dB, float* dw,
+                    void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_backward_pair(hs, hs_t, target, N, k);
+  if (rc != MOLORA_OK) return rc;
+  if ((dx0_dtype != MOLORA_BF16 && dx0_dtype != MOLORA_F32) || (dx_dtype != MOLORA_BF16 && dx_dtype != MOLORA_F32))
+    return fail(MOLORA_EINVAL, "unknown dtype");
+  if (dx != nullptr && dx0 == dx && dx0_dtype != dx_dtype) return fail(MOLORA_EINVAL, "in-place dx needs dx0_dtype == dx_dtype");
+  if (dx == nullptr && dA == nullptr && dB == nullptr && dw == nullptr)
+    return fail(MOLORA_EINVAL, "dx, dA, dB and dw are all NULL");
+  if ((dA != nullptr && !aligned(dA, 4)) || (dB != nullptr && !aligned(dB, 4)) || (dw != nullptr && !aligned(dw, 4)))
+    return fail(MOLORA_EINVAL, "misaligned pointer");
+  const bool any_pairs = N > 0;
+  if (any_pairs) {
+    if (x == nullptr || gy == nullptr) return fail(MOLORA_EINVAL, "x or gy is NULL");
+    if (!aligned(x, 16) || !aligned(gy, 16)) return fail(MOLORA_EINVAL, "x and gy must be 16-byte aligned");
+    if (offsets == nullptr || perm == nullptr || perm_w == nullptr || inv == nullptr)
+      return fail(MOLORA_EINVAL, "offsets, perm, perm_w and inv are required");
+    if (!aligned(offsets, 4) || !aligned(perm, 4) || !aligned(perm_w, 4) || !aligned(inv, 4))
+      return fail(MOLORA_EINVAL, "misaligned pointer");
+    if (dx != nullptr && (dx0 == nullptr || !aligned(dx0, 16) || !aligned(dx, 16)))
+      return fail(MOLORA_EINVAL, "dx needs dx0; both 16-byte aligned");
+  } else if ((dA != nullptr || dB != nullptr) && offsets == nullptr) {
+    return fail(MOLORA_EINVAL, "offsets is required");
+  }
+  int dx_path = 0;
+  const molora::BwdPlan plan = backward_plan(hs, target, N, k, dx_dtype == MOLORA_F32, &dx_path);
+  const bool need_ws = any_pairs || dA != nullptr || dB != nullptr;
+  if (need_ws && (ws == nullptr || ws_bytes < plan.total || !aligned(ws, 256)))
+    return fail(MOLORA_ENOSPC, "workspace of %zu bytes (256-byte aligned) needed, %zu given", plan.total, ws_bytes);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  char* wsb = reinterpret_cast<char*>(ws);
+  if (dx != nullptr && any_pairs) {
+    molora::ApplyLaunch a{};
+    a.tgt = hs_t->tg[target];
+    a.indirect = hs_t->layout == MOLORA_LAYOUT_INDIRECT;
+    a.x = reinterpret_cast<const uint16_t*>(gy);
+    a.y0 = dx0;
+    a.y = dx;
+    a.y0_f32 = dx0_dtype == MOLORA_F32;
+    a.y_f32 = dx_dtype == MOLORA_F32;
+    a.N = N;
+    a.k = k;
+    a.K = hs->K;
+    a.scale = hs->scale;
+    a.offsets = offsets;
+    a.perm = perm;
+    a.perm_w = perm_w;
+    a.inv = inv;
+    a.path = dx_path;
+    a.ws = reinterpret_cast<float*>(wsb + plan.apply_off);
+    a.col_groups = 0;
+    const hipError_t e = molora::launch_apply(a, s);
+    if (e != hipSuccess) return hip_fail(e, "backward dx launch");
+  }
+  if (dA == nullptr && dB == nullptr && dw == nullptr) return ok();
+  molora::BackwardLaunch b{};
+  b.tgt = hs->tg[target];
+  b.tgt_t = hs_t->tg[target];
+  b.indirect = hs->layout == MOLORA_LAYOUT_INDIRECT;
+  b.indirect_t = hs_t->layout == MOLORA_LAYOUT_INDIRECT;
+  b.x = reinterpret_cast<const uint16_t*>(x);
+  b.gy = reinterpret_cast<const uint16_t*>(gy);
+  b.offsets = offsets;
+  b.perm = perm;
+  b.perm_w = perm_w;
+  b.inv = inv;
+  b.N = N;
+  b.k = k;
+  b.K = hs->K;
+  b.r = hs->r;
+  b.scale = hs->scale;
+  b.dA = dA;
+  b.dB = dB;
+  b.dw = dw;
+  b.ws = wsb;
+  b.dx_f32 = dx_dtype == MOLORA_F32;
+  b.dx_path = dx_path;
+  const hipError_t e = molora::launch_backward(b, s);
+  return e == hipSuccess ? ok() : hip_fail(e, "backward launch");
 }
 
 int molora_seqpass_meta(const int32_t* idx, int N, int K, int32_t* offsets, int32_t* perm, float* perm_w, void* stream) {

@@ -24,8 +24,8 @@ hipError_t launch_route_topk(const uint16_t* x, int N, int d, const uint16_t* W1
 hipError_t launch_dispatch(const int32_t* idx, const float* w, int P, int K, int32_t* counts, int32_t* offsets,
                            int32_t* perm, float* perm_w, int32_t* inv, void* ws, hipStream_t s);
 
-hipError_t launch_relayout(const uint16_t* A, const uint16_t* B, int d_in, int d_out, int r,
-                           int r_pad, uint16_t* At, uint16_t* Bt, hipStream_t s);
+hipError_t launch_relayout(const uint16_t* A, const uint16_t* B, int d_in, int d_out, int r, int r_pad,
+                           uint16_t* At, uint16_t* Bt, hipStream_t s, bool transposed);
 
 struct ApplyLaunch {
   TargetDev tgt;
@@ -44,6 +44,33 @@ struct ApplyLaunch {
   float* ws;         // workspace of apply_plan() for this apply (NULL when it needs none)
   int col_groups;    // 0 = choose
 };
+
+// Grouped shrink per pair without gate weight or scale into hpart [nsplit][P][r_pad] fp32.
+hipError_t launch_pair_shrink(const TargetDev& tgt, bool indirect, const uint16_t* x, const int32_t* offsets,
+                              const int32_t* perm, int K, int k, long long P, float* hpart, int nsplit,
+                              hipStream_t s);
+
+// Backward of the routed LoRA except dx: dA, dB, dw (any may be NULL) from x, gy and the
+// forward routing; ws holds bwd_plan() for these shapes.
+struct BackwardLaunch {
+  TargetDev tgt, tgt_t;  // forward adapters and their transposed twin (same target)
+  bool indirect, indirect_t;
+  const uint16_t* x;
+  const uint16_t* gy;
+  const int32_t* offsets;
+  const int32_t* perm;
+  const float* perm_w;
+  const int32_t* inv;
+  int N, k, K, r;
+  float scale;
+  float* dA;
+  float* dB;
+  float* dw;
+  char* ws;
+  bool dx_f32;  // the plan's dx apply (placement of the later regions only)
+  int dx_path;
+};
+hipError_t launch_backward(const BackwardLaunch& a, hipStream_t s);
 
 // a.ws: the workspace of apply_plan() for a's shape and resolved path.
 hipError_t launch_apply(const ApplyLaunch& a, hipStream_t s);

@@ -152,4 +152,27 @@ struct MultiPlan {
 MultiPlan apply_multi_plan(int n, const int* d_in, const int* d_out, int N, int k, int K, int r_pad, bool y_f32,
                            int path);
 
+// ---- backward (molora_backward): per-pair h = x A_e and g = gy B_e^T from two grouped
+// shrinks (split over the reduction like the skinny path, unscaled), a pair pass that writes
+// dL/dw and the scaled h, g as bf16 hi/lo chunks [nchunks][2][r_pad][Qc] (rank-major, pairs
+// contiguous, zero past the segment), then the weight-gradient reductions over each
+// segment's pairs: partials [nchunks][D / 128][128][r_pad] fp32, summed chunk by chunk.
+constexpr int kWStep = 64;   // pairs per LDS step of the weight-gradient kernel
+constexpr int kWCols = 128;  // columns of x / gy per weight-gradient workgroup
+struct BwdPlan {
+  int nsh, nsg;            // splits of the h shrink (over d_in) and the g shrink (over d_out)
+  int Qc;                  // pairs per chunk, a multiple of kWStep
+  long long nchunks;       // upper bound on chunks: ceil(P / Qc) + K
+  size_t h_off, h_bytes;   // h partials [nsh][P][r_pad] fp32
+  size_t g_off, g_bytes;   // g partials [nsg][P][r_pad] fp32
+  size_t sa_off, sb_off, s_bytes;  // hi/lo chunks of scale*w*g (for dA) and scale*w*h (for dB)
+  size_t part_off, part_bytes;     // weight-gradient partials, shared by dA then dB
+  size_t apply_off, apply_bytes;   // dx: the apply on the transposed adapters
+  size_t total;
+};
+// dx_path: the resolved path of the dx apply (apply_resolve_path on the transposed shapes).
+BwdPlan bwd_plan(int N, int k, int K, int r_pad, int d_in, int d_out, bool dx_f32, int dx_path);
+// bf16 elements of one chunk's hi (or lo) plane; the lo plane follows the hi plane.
+MOLORA_HD inline size_t bwd_s_chunk_elems(int r_pad, int Qc) { return (size_t)r_pad * Qc; }
+
 }  // namespace molora

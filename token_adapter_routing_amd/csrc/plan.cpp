@@ -186,4 +186,44 @@ MultiPlan apply_multi_plan(int n, const int* d_in, const int* d_out, int N, int 
   return m;
 }
 
+// Splits: enough shrink workgroups to cover the chip (about 1024) without more partial
+// traffic than needed.  Chunks: about 512 weight-gradient workgroups over the narrower of the
+// two widths, between 64 and 2048 pairs each.
+BwdPlan bwd_plan(int N, int k, int K, int r_pad, int d_in, int d_out, bool dx_f32, int dx_path) {
+  BwdPlan b{};
+  const long long P = (long long)N * k;
+  const long long tiles = P / kTileRows + K + 1;
+  auto splits = [&](int d) {
+    const long long want = (1024 + tiles - 1) / tiles;
+    return (int)std::max<long long>(1, std::min<long long>(want, skinny_splits(d)));
+  };
+  b.nsh = splits(d_in);
+  b.nsg = splits(d_out);
+  const long long ncb = std::min(d_in, d_out) / kWCols;
+  const long long steps = std::max<long long>(1, std::min<long long>(32, P * ncb / (512LL * kWStep)));
+  b.Qc = (int)(steps * kWStep);
+  b.nchunks = (P + b.Qc - 1) / b.Qc + K;
+  size_t off = 0;
+  b.h_off = off;
+  b.h_bytes = align256((size_t)b.nsh * P * r_pad * sizeof(float));
+  off += b.h_bytes;
+  b.g_off = off;
+  b.g_bytes = align256((size_t)b.nsg * P * r_pad * sizeof(float));
+  off += b.g_bytes;
+  b.s_bytes = align256((size_t)b.nchunks * 2 * bwd_s_chunk_elems(r_pad, b.Qc) * sizeof(uint16_t));
+  b.sa_off = off;
+  off += b.s_bytes;
+  b.sb_off = off;
+  off += b.s_bytes;
+  const int D = std::max(d_in, d_out);
+  b.part_off = off;
+  b.part_bytes = align256((size_t)b.nchunks * D * r_pad * sizeof(float));
+  off += b.part_bytes;
+  b.apply_off = off;
+  b.apply_bytes = align256(apply_ws_bytes(N, k, K, r_pad, d_out, d_in, dx_f32, dx_path));
+  off += b.apply_bytes;
+  b.total = off;
+  return b;
+}
+
 }  // namespace molora
