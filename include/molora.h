@@ -388,7 +388,7 @@ int molora_seqpass_meta(const int32_t *idx, int N, int K, int32_t *offsets, int3
  *        outer(w * scale * x_t A_e, gy_t)
  *   dw   device fp32 [N*k] out or NULL: dL/dw of pair p = t*k + s, i.e.
  *        scale * (x_t A_e) . (gy_t B_e^T); 0 for unrouted pairs.  Feed it to
- *        molora_route_topk_backward for the router's gradient.
+ *        molora_route_topk_backward (below) for the router's gradient.
  *   ws   device workspace of molora_backward_workspace() bytes, 256-byte
  *        aligned, no initial contents (NULL allowed only when N = 0 and dA,
  *        dB are NULL).  Calls sharing it must not overlap.
@@ -410,6 +410,48 @@ int molora_backward(const molora_hotset *hs, const molora_hotset *hs_t, int targ
                     int dx_dtype, int N, int k, const int32_t *offsets, const int32_t *perm,
                     const float *perm_w, const int32_t *inv, float *dA, float *dB, float *dw,
                     void *ws, size_t ws_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
+ * Router gradient (thelatestinai.com, Table 1 TopK(g_theta(x)) with the MLP
+ * d -> 64 -> K; Figure 2's weighted sum; Table 13: the router learns from
+ * the loss without labels).
+ *
+ * molora_route_topk_backward: dL/dlogits through the softmax over the k
+ * selected logits, the selection held fixed (it is piecewise constant):
+ *   idx, w  device int32 / fp32 [N][k]: molora_route_topk's outputs
+ *   dw      device fp32 [N][k]: dL/dw (molora_backward's dw of every target,
+ *           summed by the caller when several targets share the routing)
+ *   dlogits device fp32 [N][K] out: slot j's logit gets
+ *           w_j (dw_j - sum_i w_i dw_i); unselected logits get 0.
+ *   Slots whose idx lies outside [0, K) receive nothing.
+ *
+ * molora_router_backward: the MLP's gradients given dlogits, for the
+ * router of molora_route_topk (W1 bf16 [64][d] and W2 bf16 [K][64] in
+ * nn.Linear layout, b1 fp32 [64] or NULL; b2 does not enter).  The
+ * pre-activation x W1^T + b1 is recomputed with the forward's own kernel
+ * code, so the ReLU's mask (derivative 1 where the pre-activation is > 0)
+ * is the forward's fp32 decision.
+ *   dW1 fp32 [64][d], db1 fp32 [64], dW2 fp32 [K][64], db2 fp32 [K]: out or
+ *       NULL (sums over the N tokens; zeros when N = 0)
+ *   dx  fp32 [N][d] out or NULL: dx0 + dL/d(pre-activation) W1, dx0 fp32
+ *       [N][d] or NULL (= 0); dx may equal dx0
+ *   ws  device workspace of molora_router_backward_workspace() bytes,
+ *       256-byte aligned, no initial contents.
+ * dW1 comes from the same MFMA weight-gradient reduction as molora_backward's
+ * dA (fixed order); dW2, db1, db2 from per-64-token partial sums added in
+ * block order; dx on the vector ALU.  Deterministic, asynchronous,
+ * capturable, no allocation.  Supported: 1 <= K <= 64, d a multiple of 128.
+ * Errors (nothing enqueued): shapes -> MOLORA_ENOTSUP; NULL or misaligned
+ * required pointers, every output NULL -> MOLORA_EINVAL; short workspace ->
+ * MOLORA_ENOSPC.
+ * ------------------------------------------------------------------------ */
+int molora_route_topk_backward(const int32_t *idx, const float *w, const float *dw, int N, int K,
+                               int k, float *dlogits, void *stream);
+int molora_router_backward_workspace(int N, int d, int K, size_t *bytes);
+int molora_router_backward(const void *x, int N, int d, const void *W1, const float *b1,
+                           const void *W2, int K, const float *dlogits, float *dW1, float *db1,
+                           float *dW2, float *db2, const float *dx0, float *dx, void *ws,
+                           size_t ws_bytes, void *stream);
 
 #ifdef __cplusplus
 }

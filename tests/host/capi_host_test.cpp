@@ -170,6 +170,28 @@ hipError_t launch_backward(const BackwardLaunch& a, hipStream_t) {
     write_span<float>(a.ws + p.part_off, 0, (size_t)p.nchunks * a.tgt.d_out * a.tgt.r_pad, "bwd wgrad part");
   return hipSuccess;
 }
+hipError_t launch_route_topk_backward(const int32_t*, const float*, const float*, int, int, int, float*, hipStream_t) {
+  ++g_launches;
+  return hipSuccess;
+}
+// What launch_router_backward's kernels write into the workspace (backward.hip).
+hipError_t launch_router_backward(const RouterBackwardLaunch& a, hipStream_t) {
+  ++g_launches;
+  const RouterBwdPlan p = router_bwd_plan(a.N, a.d, a.K);
+  write_span<float>(a.ws + p.pre_off, 0, (size_t)a.N * kRouterHidden, "router pre");
+  write_span<float>(a.ws + p.da_off, 0, (size_t)a.N * kRouterHidden, "router da");
+  if (a.N > 0) {
+    // the planes of every token block's chunk, up to the block-rounded token count
+    const long long last = ((long long)p.ntb * kRouterTokBlock - 1) / p.Qc;
+    CHECK(last < p.nchunks, "router chunk %lld of %lld", last, p.nchunks);
+    write_span<uint16_t>(a.ws + p.s_off, 0, (size_t)(last + 1) * 2 * bwd_s_chunk_elems(kRouterHidden, p.Qc),
+                         "router s");
+    write_span<float>(a.ws + p.part_off, 0, (size_t)p.nchunks * a.d * kRouterHidden, "router part");
+  }
+  write_span<float>(a.ws + p.small_off, 0, (size_t)p.ntb * router_small_floats(a.K), "router small");
+  write_span<int32_t>(a.ws + p.offs_off, 0, 2, "router offsets");
+  return hipSuccess;
+}
 hipError_t launch_apply(const ApplyLaunch& a, hipStream_t) {
   ++g_launches;
   g_last_apply_path = a.path;
@@ -445,6 +467,35 @@ static void test_backward(int K, int r, int d_in, int d_out, int N, int k, int d
   molora_hotset_destroy(t.hs);
 }
 
+static void test_router_backward(int N, int d, int K) {
+  size_t need = 0;
+  CHECK(molora_router_backward_workspace(N, d, K, &need) == MOLORA_OK, "router_backward_workspace");
+  if (need > kMaxBuf) return;
+  char* ws = static_cast<char*>(exact_alloc(need));
+  g_ws_base = ws;
+  g_ws_bytes = need;
+  g_ranges.clear();
+  const int l0 = g_launches;
+  int rc = molora_router_backward(fake(0x1000), N, d, fake(0x2000), (float*)fake(0x3000), fake(0x4000), K,
+                                  (float*)fake(0x5000), (float*)fake(0x6000), (float*)fake(0x7000),
+                                  (float*)fake(0x8000), (float*)fake(0x9000), nullptr, (float*)fake(0xa000), ws, need,
+                                  nullptr);
+  CHECK(rc == MOLORA_OK && g_launches == l0 + 1, "router_backward N=%d d=%d K=%d", N, d, K);
+  check_disjoint("router_backward");
+  const int l1 = g_launches;
+  rc = molora_router_backward(fake(0x1000), N, d, fake(0x2000), nullptr, fake(0x4000), K, (float*)fake(0x5000),
+                              (float*)fake(0x6000), nullptr, nullptr, nullptr, nullptr, nullptr, ws, need - 1, nullptr);
+  CHECK(rc == MOLORA_ENOSPC && g_launches == l1, "short router workspace accepted");
+  rc = molora_router_backward(fake(0x1000), N, d, fake(0x2000), nullptr, fake(0x4000), K, (float*)fake(0x5000),
+                              nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, ws, need, nullptr);
+  CHECK(rc == MOLORA_EINVAL && g_launches == l1, "router backward without outputs accepted");
+  g_ws_base = nullptr;
+  free(ws);
+  CHECK(molora_router_backward_workspace(N, 100, K, &need) == MOLORA_ENOTSUP, "d=100 accepted");
+  CHECK(molora_route_topk_backward(nullptr, nullptr, nullptr, 4, K, K + 1, nullptr, nullptr) == MOLORA_ENOTSUP,
+        "k > K accepted");
+}
+
 static void test_multi(int K, int r, int N, int k, int path, int y_dtype) {
   const std::vector<std::pair<int, int>> qwen = {{2048, 2048}, {2048, 1024}, {2048, 1024}, {2048, 2048},
                                                  {2048, 6144}, {2048, 6144}, {6144, 2048}};
@@ -610,6 +661,9 @@ int main() {
             test_backward(K, r, 1024, 2048, N, k, MOLORA_BF16, layout, 15);
   for (int outputs = 0; outputs < 16; ++outputs) test_backward(4, 16, 512, 256, 777, 2, MOLORA_F32, MOLORA_LAYOUT_DIRECT, outputs);
   test_backward(16, 64, 4096, 4096, 16384, 1, MOLORA_BF16, MOLORA_LAYOUT_DIRECT, 15);
+  for (int N : {0, 1, 63, 64, 65, 4096, 5000, 65536})
+    for (int d : {128, 2048, 4096})
+      for (int K : {1, 4, 64}) test_router_backward(N, d, K);
   free(g_scratch);
   fprintf(stderr, "%d checks, %d failures\n", g_checks, g_fail);
   return g_fail == 0 ? 0 : 1;

@@ -63,6 +63,11 @@ _SIGS = {
     "molora_hotset_init_transposed": (_c_i, [ctypes.POINTER(_c_p), _c_i, _c_i, _c_f, _c_i, ctypes.POINTER(MoloraTarget),
                                              _c_i, _c_p, _c_sz, _c_p]),
     "molora_backward_workspace": (_c_i, [_c_p, _c_p, _c_i, _c_i, _c_i, _c_i, ctypes.POINTER(_c_sz)]),
+    "molora_route_topk_backward": (_c_i, [_c_p, _c_p, _c_p, _c_i, _c_i, _c_i, _c_p, _c_p]),
+    "molora_router_backward_workspace": (_c_i, [_c_i, _c_i, _c_i, ctypes.POINTER(_c_sz)]),
+    "molora_router_backward": (_c_i, [_c_p, _c_i, _c_i, _c_p, _c_p, _c_p, _c_i, _c_p,  # x .. dlogits
+                                      _c_p, _c_p, _c_p, _c_p, _c_p, _c_p,  # dW1, db1, dW2, db2, dx0, dx
+                                      _c_p, _c_sz, _c_p]),
     "molora_backward": (_c_i, [_c_p, _c_p, _c_i, _c_p, _c_p, _c_p, _c_i, _c_p, _c_i, _c_i, _c_i,  # hs .. k
                                _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p,  # offsets .. dw
                                _c_p, _c_sz, _c_p]),  # ws, ws_bytes, stream
@@ -497,3 +502,47 @@ def molora_backward(hs: HotSet, hs_t: HotSet, x: torch.Tensor, gy: torch.Tensor,
         _ptr(dA, torch.float32, "dA"), _ptr(dB, torch.float32, "dB"), _ptr(dw, torch.float32, "dw"),
         _ptr(ws, torch.uint8, "ws"), ws.numel(), _stream(stream)))
     return dx, dA, dB, dw
+
+
+def molora_route_topk_backward(idx: torch.Tensor, w: torch.Tensor, dw: torch.Tensor, K: int,
+                               dlogits: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """dL/dlogits [N][K] fp32 through the softmax over the selected logits (idx, w, dw [N][k])."""
+    N, k = idx.shape if idx.dim() == 2 else (idx.numel(), 1)
+    if dlogits is None:
+        dlogits = torch.empty(N, K, dtype=torch.float32, device=idx.device)
+    _check(load_library().molora_route_topk_backward(
+        _ptr(idx, torch.int32, "idx"), _ptr(w, torch.float32, "w"), _ptr(dw, torch.float32, "dw"), int(N), int(K),
+        int(k), _ptr(dlogits, torch.float32, "dlogits"), _stream(stream)))
+    return dlogits
+
+
+def molora_router_backward_workspace(N: int, d: int, K: int) -> int:
+    n = _c_sz()
+    _check(load_library().molora_router_backward_workspace(int(N), int(d), int(K), ctypes.byref(n)))
+    return n.value
+
+
+def molora_router_backward(x: torch.Tensor, W1: torch.Tensor, b1: Optional[torch.Tensor], W2: torch.Tensor,
+                           dlogits: torch.Tensor, dx0: Optional[torch.Tensor] = None,
+                           want=("dW1", "db1", "dW2", "db2", "dx"), out=None, ws: Optional[torch.Tensor] = None,
+                           stream=None):
+    """Router MLP gradients (W1 [64][d], W2 [K][64] bf16): returns dict of the requested fp32
+    outputs dW1 [64][d], db1 [64], dW2 [K][64], db2 [K], dx [N][d] (= dx0 + router part)."""
+    N, d = x.shape
+    K = W2.shape[0]
+    o = dict(out or {})
+    shapes = {"dW1": (64, d), "db1": (64,), "dW2": (K, 64), "db2": (K,), "dx": (N, d)}
+    for name in want:
+        if name not in o:
+            o[name] = torch.empty(*shapes[name], dtype=torch.float32, device=x.device)
+    need = molora_router_backward_workspace(N, d, K)
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(need, dtype=torch.uint8, device=x.device)
+    g = o.get
+    _check(load_library().molora_router_backward(
+        _ptr(x, torch.bfloat16, "x"), int(N), int(d), _ptr(W1, torch.bfloat16, "W1"), _ptr(b1, torch.float32, "b1"),
+        _ptr(W2, torch.bfloat16, "W2"), int(K), _ptr(dlogits, torch.float32, "dlogits"),
+        _ptr(g("dW1"), torch.float32, "dW1"), _ptr(g("db1"), torch.float32, "db1"), _ptr(g("dW2"), torch.float32, "dW2"),
+        _ptr(g("db2"), torch.float32, "db2"), _ptr(dx0, torch.float32, "dx0"), _ptr(g("dx"), torch.float32, "dx"),
+        _ptr(ws, torch.uint8, "ws"), ws.numel(), _stream(stream)))
+    return o

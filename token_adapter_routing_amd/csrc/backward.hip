@@ -44,6 +44,11 @@ __device__ __forceinline__ bool chunk_of(const int32_t* __restrict__ offsets, in
   return true;
 }
 
+__global__ __launch_bounds__(256) void fill_zero_k(float* __restrict__ p, long long n) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = 0.f;
+}
+
 // ------------------------------------------------------------------------------ pair pass
 struct BwdPairArgs {
   const float* hp;  // [nsh][P][r_pad] unscaled h partials, or nullptr
@@ -340,6 +345,219 @@ hipError_t launch_backward(const BackwardLaunch& a, hipStream_t s) {
     if (err != hipSuccess) return err;
   }
   if (a.dB != nullptr) err = launch_wgrad_reduce(a, plan, a.gy, a.tgt.d_out, sb, a.dB, 1, s);
+  return err;
+}
+
+// ------------------------------------------------------------------------------ router
+// dL/dlogits through the softmax over the selected logits: the selected logit of slot j gets
+// w_j (dw_j - sum_i w_i dw_i), every other logit 0.  One thread per (token, adapter).
+__global__ __launch_bounds__(256) void route_topk_bwd_k(const int32_t* __restrict__ idx, const float* __restrict__ w,
+                                                        const float* __restrict__ dw, int N, int K, int k,
+                                                        float* __restrict__ dl) {
+  const long long v = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (v >= (long long)N * K) return;
+  const int t = (int)(v / K), e = (int)(v % K);
+  const int32_t* ir = idx + (size_t)t * k;
+  const float* wr = w + (size_t)t * k;
+  const float* dr = dw + (size_t)t * k;
+  float mean = 0.f, mine = 0.f, wmine = 0.f;
+  bool sel = false;
+  for (int j = 0; j < k; ++j) {
+    mean += wr[j] * dr[j];
+    if (ir[j] == e) {
+      sel = true;
+      mine = dr[j];
+      wmine = wr[j];
+    }
+  }
+  dl[v] = sel ? wmine * (mine - mean) : 0.f;
+}
+
+hipError_t launch_route_topk_backward(const int32_t* idx, const float* w, const float* dw, int N, int K, int k,
+                                      float* dl, hipStream_t s) {
+  const long long n = (long long)N * K;
+  hipLaunchKernelGGL(route_topk_bwd_k, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, idx, w, dw, N, K, k, dl);
+  return hipGetLastError();
+}
+
+// Per 64-token block: dL/d(hidden) = dlogits W2, masked by the ReLU of the recomputed
+// pre-activation (the forward's own fp32 decision), written fp32 [N][64] and as the dW1
+// reduction's hi/lo planes; the block's partial sums of dW2 = sum dlogits^T relu(pre),
+// db2 = sum dlogits and db1 = sum dL/d(pre) go to `small` [block][K*64 + K + 64].
+struct RouterTokArgs {
+  const float* pre;
+  const float* dl;
+  const uint16_t* W2;  // [K][64] bf16
+  int N, K, Qc;
+  float* da;
+  uint16_t* S;
+  float* small;
+  int32_t* offs;
+};
+
+__global__ __launch_bounds__(256) void router_bwd_tok_k(RouterTokArgs a) {
+  constexpr int H = kRouterHidden, T = kRouterTokBlock;
+  __shared__ float w2[64][H];
+  __shared__ float dls[T][65];
+  __shared__ float hid[T][H + 1];
+  __shared__ float das[T][H + 1];
+  const int t0 = blockIdx.x * T;
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    a.offs[0] = 0;
+    a.offs[1] = a.N;
+  }
+  for (int v = threadIdx.x; v < a.K * H; v += 256) w2[v / H][v % H] = bf16_to_f32(a.W2[v]);
+  for (int v = threadIdx.x; v < T * a.K; v += 256) {
+    const int tl = v / a.K, e = v % a.K;
+    dls[tl][e] = t0 + tl < a.N ? a.dl[(size_t)(t0 + tl) * a.K + e] : 0.f;
+  }
+  __syncthreads();
+  const int tl = threadIdx.x & 63, hg = threadIdx.x >> 6;
+  const int t = t0 + tl;
+  const bool valid = t < a.N;
+  const size_t plane = bwd_s_chunk_elems(H, a.Qc);
+  uint16_t* sc = a.S + (size_t)(t / a.Qc) * 2 * plane;
+  const int col = t % a.Qc;
+#pragma unroll 4
+  for (int i = 0; i < 16; ++i) {
+    const int h = hg * 16 + i;
+    float dh = 0.f;
+    for (int e = 0; e < a.K; ++e) dh = fmaf(dls[tl][e], w2[e][h], dh);
+    const float p = valid ? a.pre[(size_t)t * H + h] : 0.f;
+    const float g = (valid && p > 0.f) ? dh : 0.f;
+    hid[tl][h] = p > 0.f ? p : 0.f;
+    das[tl][h] = g;
+    if (valid) a.da[(size_t)t * H + h] = g;
+    const __bf16 hi = (__bf16)g;
+    const __bf16 lo = (__bf16)(g - (float)hi);
+    sc[(size_t)h * a.Qc + col] = __builtin_bit_cast(uint16_t, hi);
+    sc[plane + (size_t)h * a.Qc + col] = __builtin_bit_cast(uint16_t, lo);
+  }
+  __syncthreads();
+  float* out = a.small + (size_t)blockIdx.x * router_small_floats(a.K);
+  for (int v = threadIdx.x; v < router_small_floats(a.K); v += 256) {
+    float sum = 0.f;
+    if (v < a.K * H) {
+      const int e = v / H, h = v % H;
+      for (int i = 0; i < T; ++i) sum = fmaf(dls[i][e], hid[i][h], sum);
+    } else if (v < a.K * H + a.K) {
+      const int e = v - a.K * H;
+      for (int i = 0; i < T; ++i) sum += dls[i][e];
+    } else {
+      const int h = v - a.K * H - a.K;
+      for (int i = 0; i < T; ++i) sum += das[i][h];
+    }
+    out[v] = sum;
+  }
+}
+
+// Sum the blocks' partials in block order into dW2 [K][64], db2 [K], db1 [64].
+__global__ __launch_bounds__(256) void router_bwd_small_k(const float* __restrict__ small, int ntb, int K,
+                                                          float* __restrict__ dW2, float* __restrict__ db2,
+                                                          float* __restrict__ db1) {
+  const int v = blockIdx.x * 256 + threadIdx.x;
+  const int n = router_small_floats(K);
+  if (v >= n) return;
+  float sum = 0.f;
+  for (int b = 0; b < ntb; ++b) sum += small[(size_t)b * n + v];
+  if (v < K * kRouterHidden) {
+    if (dW2 != nullptr) dW2[v] = sum;
+  } else if (v < K * kRouterHidden + K) {
+    if (db2 != nullptr) db2[v - K * kRouterHidden] = sum;
+  } else if (db1 != nullptr) {
+    db1[v - K * kRouterHidden - K] = sum;
+  }
+}
+
+// dx = dx0 + dL/d(pre) W1 on the VALU: a workgroup owns 16 tokens x 512 columns, two columns
+// per thread, the 16 tokens' gradients in LDS.
+__global__ __launch_bounds__(256) void router_bwd_dx_k(const float* __restrict__ da, const uint16_t* __restrict__ W1,
+                                                       const float* __restrict__ dx0, float* __restrict__ dx, int N,
+                                                       int d) {
+  constexpr int H = kRouterHidden;
+  __shared__ float g[16][H];
+  const int t0 = blockIdx.x * 16;
+  for (int v = threadIdx.x; v < 16 * H; v += 256) {
+    const int tl = v / H;
+    g[tl][v % H] = t0 + tl < N ? da[(size_t)(t0 + tl) * H + v % H] : 0.f;
+  }
+  __syncthreads();
+  const int c = blockIdx.y * 512 + 2 * threadIdx.x;
+  if (c >= d) return;
+  float acc[16][2];
+#pragma unroll
+  for (int t = 0; t < 16; ++t) acc[t][0] = acc[t][1] = 0.f;
+  for (int h = 0; h < H; ++h) {
+    const uint32_t wv = *reinterpret_cast<const uint32_t*>(W1 + (size_t)h * d + c);
+    const float w0 = bf16_to_f32(wv & 0xffffu), w1 = bf16_to_f32(wv >> 16);
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      acc[t][0] = fmaf(g[t][h], w0, acc[t][0]);
+      acc[t][1] = fmaf(g[t][h], w1, acc[t][1]);
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < 16; ++t) {
+    if (t0 + t >= N) break;
+    const size_t o = (size_t)(t0 + t) * d + c;
+    const float b0 = dx0 != nullptr ? dx0[o] : 0.f, b1v = dx0 != nullptr ? dx0[o + 1] : 0.f;
+    dx[o] = b0 + acc[t][0];
+    dx[o + 1] = b1v + acc[t][1];
+  }
+}
+
+hipError_t launch_router_backward(const RouterBackwardLaunch& a, hipStream_t s) {
+  const RouterBwdPlan p = router_bwd_plan(a.N, a.d, a.K);
+  float* pre = reinterpret_cast<float*>(a.ws + p.pre_off);
+  float* da = reinterpret_cast<float*>(a.ws + p.da_off);
+  uint16_t* S = reinterpret_cast<uint16_t*>(a.ws + p.s_off);
+  float* part = reinterpret_cast<float*>(a.ws + p.part_off);
+  float* small = reinterpret_cast<float*>(a.ws + p.small_off);
+  int32_t* offs = reinterpret_cast<int32_t*>(a.ws + p.offs_off);
+  hipError_t err = hipSuccess;
+  if (a.N > 0) {
+    err = launch_router_pre(a.x, a.N, a.d, a.W1, a.b1, pre, s);
+    if (err != hipSuccess) return err;
+    RouterTokArgs t{pre, a.dl, a.W2, a.N, a.K, p.Qc, da, S, small, offs};
+    hipLaunchKernelGGL(router_bwd_tok_k, dim3((unsigned)p.ntb), dim3(256), 0, s, t);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
+  if (a.dW2 != nullptr || a.db2 != nullptr || a.db1 != nullptr) {
+    if (a.N > 0) {
+      const int n = router_small_floats(a.K);
+      hipLaunchKernelGGL(router_bwd_small_k, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, small, p.ntb, a.K,
+                         a.dW2, a.db2, a.db1);
+    } else {
+      // no tokens: the parameter gradients are zero (a fill kernel, capturable)
+      hipLaunchKernelGGL(router_bwd_small_k, dim3((unsigned)((router_small_floats(a.K) + 255) / 256)), dim3(256), 0,
+                         s, small, 0, a.K, a.dW2, a.db2, a.db1);
+    }
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
+  if (a.dW1 != nullptr) {
+    const int ncb = a.d / kWCols;
+    if (a.N > 0) {
+      BwdWgradArgs w;
+      w.X = a.x; w.D = a.d; w.offsets = offs; w.perm = nullptr; w.k = 1; w.K = 1;
+      w.S = S; w.Qc = p.Qc; w.r_pad = kRouterHidden; w.ncb = ncb; w.part = part;
+      hipLaunchKernelGGL(bwd_wgrad<4>, dim3((unsigned)(p.nchunks * ncb)), dim3(kWThreads), 0, s, w);
+      if ((err = hipGetLastError()) != hipSuccess) return err;
+      BwdReduceArgs r;
+      r.part = part; r.offsets = offs; r.K = 1; r.Qc = p.Qc; r.r = kRouterHidden; r.r_pad = kRouterHidden;
+      r.ncb = ncb; r.D = a.d; r.out = a.dW1; r.rank_major = 1;
+      hipLaunchKernelGGL(bwd_reduce, dim3((unsigned)ncb), dim3(256), 0, s, r);
+      if ((err = hipGetLastError()) != hipSuccess) return err;
+    } else {
+      hipLaunchKernelGGL(fill_zero_k, dim3((unsigned)(((size_t)kRouterHidden * a.d + 255) / 256)), dim3(256), 0, s,
+                         a.dW1, (long long)kRouterHidden * a.d);
+      if ((err = hipGetLastError()) != hipSuccess) return err;
+    }
+  }
+  if (a.dx != nullptr && a.N > 0) {
+    hipLaunchKernelGGL(router_bwd_dx_k, dim3((unsigned)((a.N + 15) / 16), (unsigned)((a.d + 511) / 512)), dim3(256), 0,
+                       s, da, a.W1, a.dx0, a.dx, a.N, a.d);
+    err = hipGetLastError();
+  }
   return err;
 }
 

@@ -711,6 +711,69 @@ int molora_backward(const molora_hotset* hs, const molora_hotset* hs_t, int targ
   return e == hipSuccess ? ok() : hip_fail(e, "backward launch");
 }
 
+int molora_route_topk_backward(const int32_t* idx, const float* w, const float* dw, int N, int K, int k,
+                               float* dlogits, void* stream) {
+  if (N < 0) return fail(MOLORA_EINVAL, "N=%d < 0", N);
+  if (K < 1 || K > MOLORA_MAX_ADAPTERS) return fail(MOLORA_ENOTSUP, "K=%d outside [1, %d]", K, MOLORA_MAX_ADAPTERS);
+  if (k < 1 || k > K || k > MOLORA_MAX_TOPK) return fail(MOLORA_ENOTSUP, "k=%d outside [1, min(K, %d)]", k, MOLORA_MAX_TOPK);
+  if (N == 0) return ok();
+  if (idx == nullptr || w == nullptr || dw == nullptr || dlogits == nullptr)
+    return fail(MOLORA_EINVAL, "idx, w, dw or dlogits is NULL");
+  if (!aligned(idx, 4) || !aligned(w, 4) || !aligned(dw, 4) || !aligned(dlogits, 4))
+    return fail(MOLORA_EINVAL, "misaligned pointer");
+  const hipError_t e = molora::launch_route_topk_backward(idx, w, dw, N, K, k, dlogits, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ok() : hip_fail(e, "route_topk_backward launch");
+}
+
+int molora_router_backward_workspace(int N, int d, int K, size_t* bytes) {
+  if (bytes == nullptr) return fail(MOLORA_EINVAL, "bytes is NULL");
+  if (N < 0) return fail(MOLORA_EINVAL, "N=%d < 0", N);
+  if (d <= 0 || d % 128 != 0) return fail(MOLORA_ENOTSUP, "d=%d must be a positive multiple of 128", d);
+  if (K < 1 || K > MOLORA_MAX_ADAPTERS) return fail(MOLORA_ENOTSUP, "K=%d outside [1, %d]", K, MOLORA_MAX_ADAPTERS);
+  *bytes = molora::router_bwd_plan(N, d, K).total;
+  return ok();
+}
+
+int molora_router_backward(const void* x, int N, int d, const void* W1, const float* b1, const void* W2, int K,
+                           const float* dlogits, float* dW1, float* db1, float* dW2, float* db2, const float* dx0,
+                           float* dx, void* ws, size_t ws_bytes, void* stream) {
+  size_t need = 0;
+  int rc = molora_router_backward_workspace(N, d, K, &need);
+  if (rc != MOLORA_OK) return rc;
+  if (dW1 == nullptr && db1 == nullptr && dW2 == nullptr && db2 == nullptr && dx == nullptr)
+    return fail(MOLORA_EINVAL, "every output is NULL");
+  if (W1 == nullptr || W2 == nullptr) return fail(MOLORA_EINVAL, "W1 or W2 is NULL");
+  if (!aligned(W1, 16) || !aligned(W2, 16)) return fail(MOLORA_EINVAL, "W1 and W2 must be 16-byte aligned");
+  if (N > 0) {
+    if (x == nullptr || dlogits == nullptr) return fail(MOLORA_EINVAL, "x or dlogits is NULL");
+    if (!aligned(x, 16) || !aligned(dlogits, 4)) return fail(MOLORA_EINVAL, "misaligned x or dlogits");
+  }
+  if ((b1 != nullptr && !aligned(b1, 4)) || (dW1 != nullptr && !aligned(dW1, 4)) || (db1 != nullptr && !aligned(db1, 4)) ||
+      (dW2 != nullptr && !aligned(dW2, 4)) || (db2 != nullptr && !aligned(db2, 4)) || (dx0 != nullptr && !aligned(dx0, 8)) ||
+      (dx != nullptr && !aligned(dx, 8)))
+    return fail(MOLORA_EINVAL, "misaligned pointer");
+  if (ws == nullptr || ws_bytes < need || !aligned(ws, 256))
+    return fail(MOLORA_ENOSPC, "workspace of %zu bytes (256-byte aligned) needed, %zu given", need, ws_bytes);
+  molora::RouterBackwardLaunch a{};
+  a.x = reinterpret_cast<const uint16_t*>(x);
+  a.N = N;
+  a.d = d;
+  a.K = K;
+  a.W1 = reinterpret_cast<const uint16_t*>(W1);
+  a.b1 = b1;
+  a.W2 = reinterpret_cast<const uint16_t*>(W2);
+  a.dl = dlogits;
+  a.dW1 = dW1;
+  a.db1 = db1;
+  a.dW2 = dW2;
+  a.db2 = db2;
+  a.dx0 = dx0;
+  a.dx = dx;
+  a.ws = reinterpret_cast<char*>(ws);
+  const hipError_t e = molora::launch_router_backward(a, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ok() : hip_fail(e, "router_backward launch");
+}
+
 int molora_seqpass_meta(const int32_t* idx, int N, int K, int32_t* offsets, int32_t* perm, float* perm_w, void* stream) {
   if (N < 0) return fail(MOLORA_EINVAL, "N=%d < 0", N);
   if (K < 1 || K > MOLORA_MAX_ADAPTERS) return fail(MOLORA_ENOTSUP, "K=%d outside [1, %d]", K, MOLORA_MAX_ADAPTERS);

@@ -72,6 +72,28 @@ struct BackwardLaunch {
 };
 hipError_t launch_backward(const BackwardLaunch& a, hipStream_t s);
 
+// Router backward: dL/dlogits of the top-k softmax; the MLP's parameter gradients and dx.
+hipError_t launch_route_topk_backward(const int32_t* idx, const float* w, const float* dw, int N, int K, int k,
+                                      float* dl, hipStream_t s);
+hipError_t launch_router_pre(const uint16_t* x, int N, int d, const uint16_t* W1, const float* b1, float* pre,
+                             hipStream_t s);
+struct RouterBackwardLaunch {
+  const uint16_t* x;   // [N][d] bf16
+  int N, d, K;
+  const uint16_t* W1;  // [64][d] bf16
+  const float* b1;     // [64] or NULL
+  const uint16_t* W2;  // [K][64] bf16
+  const float* dl;     // dL/dlogits [N][K] fp32
+  float* dW1;          // [64][d] or NULL
+  float* db1;          // [64] or NULL
+  float* dW2;          // [K][64] or NULL
+  float* db2;          // [K] or NULL
+  const float* dx0;    // [N][d] fp32 or NULL
+  float* dx;           // [N][d] fp32 or NULL
+  char* ws;            // router_bwd_plan()
+};
+hipError_t launch_router_backward(const RouterBackwardLaunch& a, hipStream_t s);
+
 // a.ws: the workspace of apply_plan() for a's shape and resolved path.
 hipError_t launch_apply(const ApplyLaunch& a, hipStream_t s);
 // Targets sharing one routing (same N, k, K, rank, path and dtypes); as[0].ws holds the

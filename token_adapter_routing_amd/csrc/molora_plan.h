@@ -175,4 +175,19 @@ BwdPlan bwd_plan(int N, int k, int K, int r_pad, int d_in, int d_out, bool dx_f3
 // bf16 elements of one chunk's hi (or lo) plane; the lo plane follows the hi plane.
 MOLORA_HD inline size_t bwd_s_chunk_elems(int r_pad, int Qc) { return (size_t)r_pad * Qc; }
 
+// ---- router backward (molora_router_backward), hidden width kRouterHidden: the
+// pre-activation [N][64] fp32, dL/d(pre-activation) [N][64] fp32, its hi/lo chunk planes for
+// the dW1 reduction (one segment: all tokens in order), that reduction's partials, per
+// 64-token block partial sums of dW2, db2, db1, and the two-entry segment offsets.
+constexpr int kRouterHidden = 64;
+constexpr int kRouterTokBlock = 64;
+struct RouterBwdPlan {
+  int Qc;
+  long long nchunks;
+  int ntb;  // 64-token blocks
+  size_t pre_off, da_off, s_off, part_off, small_off, offs_off, total;
+};
+RouterBwdPlan router_bwd_plan(int N, int d, int K);
+MOLORA_HD inline int router_small_floats(int K) { return K * kRouterHidden + K + kRouterHidden; }
+
 }  // namespace molora

@@ -226,4 +226,28 @@ BwdPlan bwd_plan(int N, int k, int K, int r_pad, int d_in, int d_out, bool dx_f3
   return b;
 }
 
+RouterBwdPlan router_bwd_plan(int N, int d, int K) {
+  RouterBwdPlan p{};
+  const long long ncb = d / kWCols;
+  const long long steps = std::max<long long>(1, std::min<long long>(32, (long long)N * ncb / (512LL * kWStep)));
+  p.Qc = (int)(steps * kWStep);
+  p.nchunks = ((long long)N + p.Qc - 1) / p.Qc + 1;
+  p.ntb = (N + kRouterTokBlock - 1) / kRouterTokBlock;
+  size_t off = 0;
+  p.pre_off = off;
+  off += align256((size_t)N * kRouterHidden * sizeof(float));
+  p.da_off = off;
+  off += align256((size_t)N * kRouterHidden * sizeof(float));
+  p.s_off = off;
+  off += align256((size_t)p.nchunks * 2 * bwd_s_chunk_elems(kRouterHidden, p.Qc) * sizeof(uint16_t));
+  p.part_off = off;
+  off += align256((size_t)p.nchunks * d * kRouterHidden * sizeof(float));
+  p.small_off = off;
+  off += align256((size_t)p.ntb * router_small_floats(K) * sizeof(float));
+  p.offs_off = off;
+  off += 256;
+  p.total = off;
+  return p;
+}
+
 }  // namespace molora

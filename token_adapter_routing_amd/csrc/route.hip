@@ -92,6 +92,33 @@ struct TopkArgs {
   uint8_t* flags;
 };
 
+// First router layer x W1^T (+ b1) of tokens [t0, t0 + 16) into out[16][64] (LDS): 8 waves
+// split d (the same MFMA shrink core as the LoRA shrink) and meet in LDS.  relu: apply the
+// ReLU.  Ends with a barrier; `red` holds RedLds<4, 8>::kFloats floats.
+__device__ __forceinline__ void router_layer1(const uint16_t* x, int N, int d, const uint16_t* W1, const float* b1,
+                                              int t0, float* red, float* out, bool relu) {
+  constexpr int NW = 8, RB = 4;
+  constexpr int RS = RedLds<RB, NW>::RS;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int tok = min(t0 + (lane & 15), N - 1);
+  f32x4_t acc[RB];
+#pragma unroll
+  for (int u = 0; u < RB; ++u) acc[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const int S = d / kStepK;
+  shrink_steps_batched<RB, false>(acc, x + (size_t)tok * d, W1, d, (S * wave) / NW, (S * (wave + 1)) / NW, lane);
+  shrink_to_lds<RB, NW>(acc, red, wave, lane);
+  __syncthreads();
+  for (int i = threadIdx.x; i < 16 * 64; i += NW * 64) {
+    const int row = i >> 6, j = i & 63;
+    float v = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) v += red[(w * 16 + row) * RS + j];
+    if (b1 != nullptr) v += b1[j];
+    out[i] = relu ? (v > 0.f ? v : 0.f) : v;
+  }
+  __syncthreads();
+}
+
 // Waves per workgroup: 8 with the router MLP (splitting d), 4 with given logits.
 template <bool ROUTER>
 struct TopkWaves {
@@ -101,33 +128,11 @@ struct TopkWaves {
 template <bool ROUTER>
 __global__ __launch_bounds__(TopkWaves<ROUTER>::NW * 64) void route_topk_k(TopkArgs a) {
   constexpr int NW = TopkWaves<ROUTER>::NW;
-  constexpr int RB = 4;  // 64 hidden units = 4 blocks of 16
-  constexpr int RS = RedLds<RB, NW>::RS;
-  __shared__ float red[ROUTER ? RedLds<RB, NW>::kFloats : 1];
+  __shared__ float red[ROUTER ? RedLds<4, 8>::kFloats : 1];
   __shared__ float hid[ROUTER ? 16 * 64 : 1];
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int t0 = blockIdx.x * 16;
-  if constexpr (ROUTER) {
-    const int n = lane & 15;
-    const int tok = min(t0 + n, a.N - 1);
-    f32x4_t acc[RB];
-#pragma unroll
-    for (int u = 0; u < RB; ++u) acc[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    const int S = a.d / kStepK;
-    shrink_steps_batched<RB, false>(acc, a.x + (size_t)tok * a.d, a.W1, a.d, (S * wave) / NW, (S * (wave + 1)) / NW,
-                                    lane);
-    shrink_to_lds<RB, NW>(acc, red, wave, lane);
-    __syncthreads();
-    for (int i = threadIdx.x; i < 16 * 64; i += NW * 64) {
-      const int row = i >> 6, j = i & 63;
-      float v = 0.f;
-#pragma unroll
-      for (int w = 0; w < NW; ++w) v += red[(w * 16 + row) * RS + j];
-      if (a.b1 != nullptr) v += a.b1[j];
-      hid[i] = v > 0.f ? v : 0.f;
-    }
-    __syncthreads();
-  }
+  if constexpr (ROUTER) router_layer1(a.x, a.N, a.d, a.W1, a.b1, t0, red, hid, true);
   constexpr int RPW = 16 / NW;  // tokens per wave in the selection
   for (int r = 0; r < RPW; ++r) {
     const int row = wave * RPW + r;
@@ -159,6 +164,24 @@ hipError_t launch_route_topk(const uint16_t* x, int N, int d, const uint16_t* W1
   const dim3 grid((N + 15) / 16);
   if (W1 != nullptr) hipLaunchKernelGGL(route_topk_k<true>, grid, dim3(TopkWaves<true>::NW * 64), 0, s, a);
   else hipLaunchKernelGGL(route_topk_k<false>, grid, dim3(TopkWaves<false>::NW * 64), 0, s, a);
+  return hipGetLastError();
+}
+
+// Pre-activation x W1^T + b1 of every token, fp32 [N][64] (the router's backward).
+__global__ __launch_bounds__(512) void router_pre_k(const uint16_t* __restrict__ x, int N, int d,
+                                                    const uint16_t* __restrict__ W1, const float* __restrict__ b1,
+                                                    float* __restrict__ pre) {
+  __shared__ float red[RedLds<4, 8>::kFloats];
+  __shared__ float out[16 * 64];
+  const int t0 = blockIdx.x * 16;
+  router_layer1(x, N, d, W1, b1, t0, red, out, false);
+  for (int i = threadIdx.x; i < 16 * 64; i += 512)
+    if (t0 + (i >> 6) < N) pre[(size_t)t0 * 64 + i] = out[i];
+}
+
+hipError_t launch_router_pre(const uint16_t* x, int N, int d, const uint16_t* W1, const float* b1, float* pre,
+                             hipStream_t s) {
+  hipLaunchKernelGGL(router_pre_k, dim3((N + 15) / 16), dim3(512), 0, s, x, N, d, W1, b1, pre);
   return hipGetLastError();
 }
 
