@@ -85,7 +85,7 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run plain device copies of known size (for HBM counter scaling)")
-    p.add_argument("--rows", default="C0,C2,C3,C4,C4stack,paging,tiling",
+    p.add_argument("--rows", default="C0,C2,C3,C4,C4stack,paging,tiling,backward",
                    help="other configurations to measure beside the headline (comma list, or 'none')")
     p.add_argument("--row-reps", type=int, default=100, help="graph replays per timed row entry")
     p.add_argument("--stack-replays", type=int, default=1000, help="single-graph replays of the 28-layer stack row")
@@ -385,6 +385,8 @@ def measure_rows(m, torch, dev, rows, reps, stack_replays=1000):
         res["C4_stack"] = row_stack(m, torch, dev, replays=stack_replays)
     if "tiling" in rows:
         res["tiling"] = row_tiling(m, torch, dev, bf, f32, i32, max(20, reps // 4))
+    if "backward" in rows:
+        res["backward"] = row_backward(m, torch, dev, bf, f32, max(20, reps // 4))
     if "paging" in rows:
         res["C1_paging"] = row_paging(m, torch, dev, bf, i32, max(200, reps * 2))
     torch.cuda.synchronize()
@@ -756,6 +758,84 @@ def row_tiling(m, torch, dev, bf, f32, i32, reps):
         ent["fixed_over_adaptive"] = ent["fixed64_us"] / ent["adaptive_us"]
         out["zipf_stress"][f"k{k}"] = ent
     del hs
+    return out
+
+
+def row_backward(m, torch, dev, bf, f32, reps):
+    """Backward of the routed LoRA (dx through the transposed hot set, dA, dB, dL/dw) on the
+    4-modality shape and the stress shape, and the router chain (dL/dlogits, router MLP
+    gradients) on the Qwen-shaped layer; each one graph replayed.  Compulsory bytes: read x,
+    dL/dy and dx0, write dx (bf16), read A and B, write dA, dB (fp32) and dL/dw."""
+    import synth
+    out = {}
+
+    def lora(name, N, d, K, r, k, cid, idx=None, w=None):
+        A = bf(synth.normal_bf16(cid, synth.T_A, (K, d, r), std=1.0 / np.sqrt(d)))
+        B = bf(synth.normal_bf16(cid, synth.T_B, (K, r, d), std=1.0 / np.sqrt(r)))
+        x = bf(synth.normal_bf16(cid, synth.T_X, (N, d)))
+        gy_b, dx0_b = synth.grad_case(cid, N, d, d)
+        gy, dx0 = bf(gy_b), bf(dx0_b)
+        if idx is None:
+            g = np.random.default_rng(cid)
+            idx = g.integers(0, K, size=N * k).astype(np.int32)
+            w = np.full(N * k, 1.0 / k, np.float32)
+        hs = m.molora_hotset_init([(A, B)], 2.0)
+        hs_t = m.molora_hotset_init_transposed([(A, B)], 2.0)
+        meta = m.molora_dispatch(torch.from_numpy(idx).to(dev), torch.from_numpy(w).to(dev), K, k)
+        dx = torch.empty(N, d, dtype=torch.bfloat16, device=dev)
+        dA = torch.empty(K, d, r, dtype=torch.float32, device=dev)
+        dB = torch.empty(K, r, d, dtype=torch.float32, device=dev)
+        dw = torch.empty(N * k, dtype=torch.float32, device=dev)
+        ws = torch.zeros(m.molora_backward_workspace(hs, hs_t, N, k), dtype=torch.uint8, device=dev)
+
+        def step():
+            m.molora_backward(hs, hs_t, x, gy, meta[1], meta[2], meta[3], meta[4], k=k, dx0=dx0, dx=dx, dA=dA, dB=dB,
+                              dw=dw, ws=ws)
+
+        ms, g, _ = graph_ms(torch, step, reps)
+        compulsory = 4 * N * d * 2 + K * 2 * d * r * (2 + 4) + N * k * 4
+        out[name] = {"workload": f"backward N={N} d={d} K={K} r={r} k={k}", "us": ms * 1e3,
+                     "compulsory_bytes": compulsory,
+                     "roofline_frac": compulsory / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9),
+                     "workspace_bytes": int(ws.numel())}
+        del g
+
+    lora("modality4_k1", 2048, 4096, 4, 16, 1, 54)
+    c = synth.stress(1)
+    for k in (1, 2):
+        lg = c.logits.astype(np.float64)
+        order = np.argsort(-lg, axis=1, kind="stable")[:, :k]
+        sel = np.sort(order, axis=1)
+        ex = np.exp(np.take_along_axis(lg, sel, 1) - np.take_along_axis(lg, sel, 1).max(1, keepdims=True))
+        w = (ex / ex.sum(1, keepdims=True)).astype(np.float32)
+        lora(f"stress_k{k}", c.N, 4096, 16, 64, k, 4, sel.reshape(-1).astype(np.int32), w.reshape(-1))
+    # router chain on the Qwen-shaped layer
+    q = synth.qwen_layer()
+    r = q.router
+    N, K, k, d = q.N, q.K, q.k, q.targets[0].d_in
+    xq = bf(q.targets[0].x)
+    W1, W2 = bf(np.ascontiguousarray(r["W1"].T)), bf(np.ascontiguousarray(r["W2"].T))
+    b1 = f32(r["b1"])
+    g = np.random.default_rng(9)
+    idx = torch.from_numpy(np.sort(np.stack([g.choice(K, k, replace=False) for _ in range(N)]), axis=1).astype(np.int32)).to(dev)
+    wq = torch.full((N, k), 1.0 / k, dtype=torch.float32, device=dev)
+    dwq = f32(g.standard_normal((N, k)).astype(np.float32))
+    dl = torch.empty(N, K, dtype=torch.float32, device=dev)
+    o = {n: torch.empty(sh, dtype=torch.float32, device=dev) for n, sh in (("dW1", (64, d)), ("db1", (64,)),
+                                                                            ("dW2", (K, 64)), ("db2", (K,)),
+                                                                            ("dx", (N, d)))}
+    wsr = torch.zeros(m.molora_router_backward_workspace(N, d, K), dtype=torch.uint8, device=dev)
+
+    def rstep():
+        m.molora_route_topk_backward(idx, wq, dwq, K, dlogits=dl)
+        m.molora_router_backward(xq, W1, b1, W2, dl, want=(), out=o, ws=wsr)
+
+    ms, gr, _ = graph_ms(torch, rstep, reps)
+    rbytes = N * d * 2 + 64 * d * 2 + N * d * 4 + 64 * d * 4 + N * K * 4 * 2
+    out["router_qwen"] = {"workload": f"router backward N={N} d={d} K={K} k={k} (dlogits, dW1, db1, dW2, db2, dx fp32)",
+                          "us": ms * 1e3, "compulsory_bytes": rbytes,
+                          "roofline_frac": rbytes / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9)}
+    del gr
     return out
 
 

@@ -138,12 +138,6 @@ hipError_t launch_relayout(const uint16_t*, const uint16_t*, int d_in, int d_out
   write_span<uint16_t>(Bt, 0, (size_t)d_out * r_pad, "B slot");
   return hipSuccess;
 }
-hipError_t launch_pair_shrink(const TargetDev& tgt, bool, const uint16_t*, const int32_t*, const int32_t*, int, int,
-                              long long P, float* hpart, int nsplit, hipStream_t) {
-  ++g_launches;
-  write_span<float>(hpart, 0, (size_t)nsplit * P * tgt.r_pad, "pair shrink partials");
-  return hipSuccess;
-}
 // What launch_backward's kernels write into the workspace (backward.hip): the h and g
 // partials, the hi/lo chunk planes, and the weight-gradient partials (dA, then dB, in one
 // region the two reductions take in turn).

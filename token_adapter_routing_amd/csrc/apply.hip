@@ -792,6 +792,12 @@ __global__ __launch_bounds__(kGMThreads) void apply_gm(GMArgs a) {
   __shared__ GMLds<RB> L;
   gm_range<RB, INDIRECT, Y0F32, YF32>(a, L);
 }
+// Shrink only: unscaled h of every grouped pair (the backward's h and g).
+template <int RB, bool INDIRECT>
+__global__ __launch_bounds__(kGMThreads) void shrink_gm(GMArgs a) {
+  __shared__ GMLds<RB> L;
+  gm_range<RB, INDIRECT, false, false, true>(a, L);
+}
 
 // Key of grouped position q: (rank of its pair among the token's routed pairs) * K + adapter;
 // weight: its gate weight.  Ranking the routed pairs (instead of using the slot index) makes
@@ -1002,7 +1008,7 @@ struct ShrinkArgs {
   const uint16_t* x;
   const int32_t* offsets;
   const int32_t* perm;
-  const float* perm_w;  // nullptr: weight 1 (the backward's unscaled h and g)
+  const float* perm_w;
   int K, k;
   float scale;
   float* hpart;  // [nsplit][P][r_pad] fp32, row q = grouped position
@@ -1035,7 +1041,7 @@ __device__ __forceinline__ void shrink_grouped_body(const ShrinkArgs& a, float* 
   __syncthreads();
   // lane (n, G) writes ranks [G * RB * 4, (G + 1) * RB * 4) of row n
   if (valid) {
-    const float wgt = (a.perm_w != nullptr ? a.perm_w[q] : 1.f) * a.scale;
+    const float wgt = a.perm_w[q] * a.scale;
     float* dst = a.hpart + ((long long)sp * a.P + q) * (RB * 16) + G * RB * 4;
 #pragma unroll
     for (int i = 0; i < RB * 4; i += 4) {
@@ -1463,7 +1469,7 @@ hipError_t launch_apply(const ApplyLaunch& a, hipStream_t s) {
     // the passes in between carry the sum in fp32 (in y itself when y is fp32, else in z), so a
     // bf16 y is rounded once.
     const bool in_place = (a.y0 == a.y);
-    GMArgs ga;
+    GMArgs ga{};
     ga.tgt = a.tgt; ga.x = a.x; ga.N = a.N; ga.k = a.k; ga.scale = a.scale; ga.perm = a.perm; ga.nkeys = a.K;
     // row tiles per segment (a multiple of 8 workgroups for the XCD mapping); column slices
     // while there are fewer than 256 workgroups
@@ -1765,20 +1771,25 @@ hipError_t launch_step_vocab(const StepVocabLaunch& a, hipStream_t s) {
 }
 
 // --------------------------------------------------------------------------------------
-// Per-pair shrink without gate weight or scale: hpart[sp][q] = partial (x_t A_e) of grouped
-// row q over split sp of the reduction (the backward's h and g).
-hipError_t launch_pair_shrink(const TargetDev& tgt, bool indirect, const uint16_t* x, const int32_t* offsets,
-                              const int32_t* perm, int K, int k, long long P, float* hpart, int nsplit,
-                              hipStream_t s) {
-  ShrinkArgs sa;
-  sa.tgt = tgt; sa.x = x; sa.offsets = offsets; sa.perm = perm; sa.perm_w = nullptr;
-  sa.K = K; sa.k = k; sa.scale = 1.f; sa.P = P; sa.nsplit = nsplit; sa.hpart = hpart;
-  const long long tiles = P / kTileRows + K + 1;
+// Per-pair shrink without gate weight or scale on the 64-row grouped tiles: hout[q] = x_t A_e
+// of grouped position q (the backward's h and g).
+hipError_t launch_pair_shrink_gm(const TargetDev& tgt, bool indirect, const uint16_t* x, const int32_t* offsets,
+                                 const int32_t* perm, int K, int k, long long P, float* hout, hipStream_t s) {
+  GMArgs ga{};
+  ga.tgt = tgt; ga.x = x; ga.k = k; ga.perm = perm; ga.offsets = offsets; ga.key0 = 0; ga.nkeys = K;
+  ga.order = nullptr; ga.wts = nullptr; ga.scale = 1.f; ga.hout = hout;
+  const GMTiling tl = gm_tiling(kPathGrouped, P, K);
+  ga.tile_rows = tl.rows; ga.fixed = tl.fixed; ga.col_groups = 1;
+  ga.nwg = (int)((tl.max_tiles + 7) / 8 * 8);
   const int RBv = tgt.r_pad / 16;
   hipError_t err = hipSuccess;
-  MOLORA_DISPATCH_RB(RBv, MOLORA_DISPATCH_BOOL(indirect, IND, err = (launch_shrink_t<RB, IND>(sa, (int)tiles, s))));
+  MOLORA_DISPATCH_RB(RBv, MOLORA_DISPATCH_BOOL(indirect, IND, {
+    hipLaunchKernelGGL((shrink_gm<RB, IND>), dim3(ga.nwg), dim3(kGMThreads), 0, s, ga);
+    err = hipGetLastError();
+  }));
   return err;
 }
+
 
 // --------------------------------------------------------------------------------------
 // Hot-set relayout of one adapter.

@@ -7,8 +7,8 @@
 //   dA_e = sum_q x_t^T (s w g)      dB_e = sum_q (s w h)^T gy_t      dL/dw_q = s (h . g)
 // dx is the forward apply of the transposed adapters (B^T, A^T) on gy (launched by the C ABI).
 //
-//   pair shrinks  two grouped shrinks (the skinny path's kernel, unscaled) give h and g per pair
-//                 as split partials.
+//   pair shrinks  the 64-row grouped kernel in shrink-only mode (A staged in LDS once per tile)
+//                 gives unscaled h and g per grouped pair.
 //   bwd_pairs     a workgroup owns 64 consecutive pairs of one chunk: sums the partials, writes
 //                 dL/dw at the pair id and s w g, s w h as bf16 hi/lo planes [rank][pair] of
 //                 the chunk (pairs past the segment hold zeros).
@@ -179,26 +179,30 @@ __global__ __launch_bounds__(kWThreads) void bwd_wgrad(BwdWgradArgs a) {
     q = min(q, q1 - 1);  // rows past the range: any valid row (their S is zero)
     return a.perm != nullptr ? a.perm[q] / a.k : q;
   };
-  u32x4_t xv[2], sv[2];
-  auto load = [&](int qs) {
-    xv[0] = ld16(xcol + (size_t)row_of(qs + 2 * p) * a.D);
-    xv[1] = ld16(xcol + (size_t)row_of(qs + 2 * p + 1) * a.D);
+  // two steps of rows in flight: register sets A and B alternate
+  struct Regs {
+    u32x4_t xv[2], sv[2];
+  };
+  Regs ra, rb;
+  auto load = [&](Regs& R, int qs) {
+    R.xv[0] = ld16(xcol + (size_t)row_of(qs + 2 * p) * a.D);
+    R.xv[1] = ld16(xcol + (size_t)row_of(qs + 2 * p + 1) * a.D);
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int v = threadIdx.x + i * kWThreads;
       if (v < kSPieces) {
         const int pl = v / (RB * 16 * 8), rem = v % (RB * 16 * 8);
         const int j = rem >> 3, gq = rem & 7;
-        sv[i] = ld16(schunk + (size_t)pl * bwd_s_chunk_elems(a.r_pad, a.Qc) + (size_t)j * a.Qc + (qs - q0) + 8 * gq);
+        R.sv[i] = ld16(schunk + (size_t)pl * bwd_s_chunk_elems(a.r_pad, a.Qc) + (size_t)j * a.Qc + (qs - q0) + 8 * gq);
       }
     }
   };
-  auto store = [&]() {
+  auto store = [&](const Regs& R) {
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
       const int row = 8 * c + s;
-      const uint32_t lo = (s & 1) ? (xv[0][s >> 1] >> 16) : (xv[0][s >> 1] & 0xffffu);
-      const uint32_t hi = (s & 1) ? (xv[1][s >> 1] >> 16) : (xv[1][s >> 1] & 0xffffu);
+      const uint32_t lo = (s & 1) ? (R.xv[0][s >> 1] >> 16) : (R.xv[0][s >> 1] & 0xffffu);
+      const uint32_t hi = (s & 1) ? (R.xv[1][s >> 1] >> 16) : (R.xv[1][s >> 1] & 0xffffu);
       L.xt[row][4 * ((p >> 2) ^ s) + (p & 3)] = lo | (hi << 16);
     }
 #pragma unroll
@@ -207,7 +211,7 @@ __global__ __launch_bounds__(kWThreads) void bwd_wgrad(BwdWgradArgs a) {
       if (v < kSPieces) {
         const int pl = v / (RB * 16 * 8), rem = v % (RB * 16 * 8);
         const int j = rem >> 3, gq = rem & 7;
-        L.st[pl][j][gq ^ (j & 7)] = sv[i];
+        L.st[pl][j][gq ^ (j & 7)] = R.sv[i];
       }
     }
   };
@@ -215,12 +219,7 @@ __global__ __launch_bounds__(kWThreads) void bwd_wgrad(BwdWgradArgs a) {
 #pragma unroll
   for (int u = 0; u < RB; ++u) acc[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   const int xrow = 16 * wave + n;
-  load(q0);
-  for (int qs = q0; qs < q1; qs += kWStep) {
-    __syncthreads();  // the previous step's operands are consumed
-    store();
-    __syncthreads();
-    if (qs + kWStep < q1) load(qs + kWStep);  // next step's rows land during the products
+  auto products = [&]() {
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       const int gq = 4 * ks + G;
@@ -234,6 +233,20 @@ __global__ __launch_bounds__(kWThreads) void bwd_wgrad(BwdWgradArgs a) {
         acc[u] = mfma16x16x32(as_bf16x8(sl), as_bf16x8(xb), acc[u]);
       }
     }
+  };
+  // one step: its rows go to LDS, the step two ahead is loaded into the freed registers
+  auto step = [&](Regs& R, int qs) {
+    __syncthreads();  // the previous step's operands are consumed
+    store(R);
+    __syncthreads();
+    if (qs + 2 * kWStep < q1) load(R, qs + 2 * kWStep);
+    products();
+  };
+  load(ra, q0);
+  if (q0 + kWStep < q1) load(rb, q0 + kWStep);
+  for (int qs = q0; qs < q1; qs += 2 * kWStep) {
+    step(ra, qs);
+    if (qs + kWStep < q1) step(rb, qs + kWStep);
   }
   // D[rank 16u + 4G + i][column 16 wave + n]
   float* dst = a.part + (((size_t)cg * a.ncb + b) * kWCols + 16 * wave + n) * a.r_pad + 4 * G;
@@ -255,31 +268,44 @@ struct BwdReduceArgs {
   int rank_major;  // 0: out [K][D][r] (dA); 1: out [K][r][D] (dB)
 };
 
+// A workgroup owns (adapter e, 128 columns, 16 ranks): each thread sums 8 (column, rank)
+// elements over e's chunks in chunk order (reads 64-byte rank runs of the partials), then
+// writes them rank-contiguous (dA) or, through an LDS transpose, column-contiguous (dB).
 __global__ __launch_bounds__(256) void bwd_reduce(BwdReduceArgs a) {
-  const int e = blockIdx.x / a.ncb, b = blockIdx.x % a.ncb;
+  __shared__ float tr[16][kWCols + 1];
+  const int RBv = a.r_pad / 16;
+  const int u = blockIdx.x % RBv;
+  const int b = (blockIdx.x / RBv) % a.ncb;
+  const int e = blockIdx.x / (RBv * a.ncb);
   const int lane = threadIdx.x & 63;
-  // chunks of adapter e: [first, first + nch) (every wave computes the same)
   const int cnt = lane < a.K ? a.offsets[lane + 1] - a.offsets[lane] : 0;
   const int nchl = (cnt + a.Qc - 1) / a.Qc;
   const int incl = wave_incl_scan(nchl, lane);
   const int nch = __shfl(nchl, e, kWave);
   const int first = __shfl(incl, e, kWave) - nch;
-  const int total = kWCols * a.r;
-  for (int v = threadIdx.x; v < total; v += 256) {
-    int col, j;
-    if (a.rank_major) {
-      j = v / kWCols;
-      col = v % kWCols;
-    } else {
-      col = v / a.r;
-      j = v % a.r;
-    }
-    float sum = 0.f;
-    for (int i = 0; i < nch; ++i)
-      sum += a.part[(((size_t)(first + i) * a.ncb + b) * kWCols + col) * a.r_pad + j];
-    const size_t gcol = (size_t)b * kWCols + col;
-    if (a.rank_major) a.out[((size_t)e * a.r + j) * a.D + gcol] = sum;
-    else a.out[((size_t)e * a.D + gcol) * a.r + j] = sum;
+  const int jj = threadIdx.x & 15, c0 = threadIdx.x >> 4;  // rank 16u + jj, columns c0 + 16 i
+  const int j = 16 * u + jj;
+  float sum[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) sum[i] = 0.f;
+  for (int ch = 0; ch < nch; ++ch) {
+    const float* src = a.part + ((size_t)(first + ch) * a.ncb + b) * kWCols * a.r_pad + j;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) sum[i] += src[(size_t)(c0 + 16 * i) * a.r_pad];
+  }
+  const size_t gcol0 = (size_t)b * kWCols;
+  if (!a.rank_major) {
+    if (j < a.r)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) a.out[((size_t)e * a.D + gcol0 + c0 + 16 * i) * a.r + j] = sum[i];
+    return;
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) tr[jj][c0 + 16 * i] = sum[i];
+  __syncthreads();
+  for (int v = threadIdx.x; v < 16 * kWCols; v += 256) {
+    const int jr = v / kWCols, col = v % kWCols;
+    if (16 * u + jr < a.r) a.out[((size_t)e * a.r + 16 * u + jr) * a.D + gcol0 + col] = tr[jr][col];
   }
 }
 
@@ -306,7 +332,7 @@ static hipError_t launch_wgrad_reduce(const BackwardLaunch& a, const BwdPlan& pl
   BwdReduceArgs r;
   r.part = part; r.offsets = a.offsets; r.K = a.K; r.Qc = plan.Qc; r.r = a.r; r.r_pad = a.tgt.r_pad;
   r.ncb = ncb; r.D = D; r.out = out; r.rank_major = rank_major;
-  hipLaunchKernelGGL(bwd_reduce, dim3((unsigned)(a.K * ncb)), dim3(256), 0, s, r);
+  hipLaunchKernelGGL(bwd_reduce, dim3((unsigned)(a.K * ncb * (a.tgt.r_pad / 16))), dim3(256), 0, s, r);
   return hipGetLastError();
 }
 
@@ -322,11 +348,11 @@ hipError_t launch_backward(const BackwardLaunch& a, hipStream_t s) {
   hipError_t err = hipSuccess;
   if (P > 0) {
     if (need_h) {
-      err = launch_pair_shrink(a.tgt, a.indirect, a.x, a.offsets, a.perm, a.K, a.k, P, hp, plan.nsh, s);
+      err = launch_pair_shrink_gm(a.tgt, a.indirect, a.x, a.offsets, a.perm, a.K, a.k, P, hp, s);
       if (err != hipSuccess) return err;
     }
     if (need_g) {
-      err = launch_pair_shrink(a.tgt_t, a.indirect_t, a.gy, a.offsets, a.perm, a.K, a.k, P, gp, plan.nsg, s);
+      err = launch_pair_shrink_gm(a.tgt_t, a.indirect_t, a.gy, a.offsets, a.perm, a.K, a.k, P, gp, s);
       if (err != hipSuccess) return err;
     }
     BwdPairArgs pa;
@@ -545,7 +571,7 @@ hipError_t launch_router_backward(const RouterBackwardLaunch& a, hipStream_t s) 
       BwdReduceArgs r;
       r.part = part; r.offsets = offs; r.K = 1; r.Qc = p.Qc; r.r = kRouterHidden; r.r_pad = kRouterHidden;
       r.ncb = ncb; r.D = a.d; r.out = a.dW1; r.rank_major = 1;
-      hipLaunchKernelGGL(bwd_reduce, dim3((unsigned)ncb), dim3(256), 0, s, r);
+      hipLaunchKernelGGL(bwd_reduce, dim3((unsigned)(ncb * (kRouterHidden / 16))), dim3(256), 0, s, r);
       if ((err = hipGetLastError()) != hipSuccess) return err;
     } else {
       hipLaunchKernelGGL(fill_zero_k, dim3((unsigned)(((size_t)kRouterHidden * a.d + 255) / 256)), dim3(256), 0, s,

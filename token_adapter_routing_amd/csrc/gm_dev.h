@@ -45,6 +45,7 @@ struct GMArgs {
   int nwg;                  // row tiles (a multiple of 8, at least the tiles of a pass); grid = nwg * col_groups
   int tile_rows;            // tile height bound (GMTiling::rows)
   int fixed;                // GMTiling::fixed
+  float* hout;              // shrink-only mode: unscaled h of grouped position q at [q][r_pad]
 };
 
 template <int RB>
@@ -122,7 +123,9 @@ struct GMExpandSet {
 };
 
 // One sub-tile: rows [row0, row0 + nrows) of adapter e, output columns [c0, c0 + cols).
-template <int RB, bool INDIRECT, bool Y0F32, bool YF32>
+// SHRINK_ONLY: stop after the reduction and write the rows' unscaled h to a.hout (the
+// backward's per-pair h and g).
+template <int RB, bool INDIRECT, bool Y0F32, bool YF32, bool SHRINK_ONLY = false>
 __device__ void gm_tile(const GMArgs& a, GMLds<RB>& L, int e, int row0, int nrows, int c0, int cols) {
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15, G = lane >> 4;
@@ -136,7 +139,8 @@ __device__ void gm_tile(const GMArgs& a, GMLds<RB>& L, int e, int row0, int nrow
     const int q = a.order != nullptr ? a.order[rr] : rr;
     tokl = a.perm[q] / a.k;
   }
-  if (threadIdx.x < kGMRows) L.wt[threadIdx.x] = a.wts[row0 + ((int)threadIdx.x < nrows ? (int)threadIdx.x : 0)] * a.scale;
+  if (!SHRINK_ONLY && threadIdx.x < kGMRows)
+    L.wt[threadIdx.x] = a.wts[row0 + ((int)threadIdx.x < nrows ? (int)threadIdx.x : 0)] * a.scale;
   const uint16_t* At = adapter_A<INDIRECT>(a.tgt, e);
   const uint16_t* Bt = adapter_B<INDIRECT>(a.tgt, e);
 
@@ -236,12 +240,14 @@ __device__ void gm_tile(const GMArgs& a, GMLds<RB>& L, int e, int row0, int nrow
     }
   }
   // the expand's first stages and y0 chunks go out now and land during the reduction
-  load_b(e0, 0);
-  load_y(e0, 0);
-  load_b(e1, 1);
-  load_y(e1, 1);
-  load_b(e2, 2);
-  load_y(e2, 2);
+  if constexpr (!SHRINK_ONLY) {
+    load_b(e0, 0);
+    load_y(e0, 0);
+    load_b(e1, 1);
+    load_y(e1, 1);
+    load_b(e2, 2);
+    load_y(e2, 2);
+  }
   __syncthreads();  // every wave is done with the stage buffers: the partial sums go there
   float* red = L.red();
   constexpr int kRS = RB * 16 + 4;
@@ -250,6 +256,19 @@ __device__ void gm_tile(const GMArgs& a, GMLds<RB>& L, int e, int row0, int nrow
 #pragma unroll
     for (int i = 0; i < 4; ++i) red[((hf * 4 + rb) * 16 + 4 * G + i) * kRS + u * 16 + n] = acc[u][i];
   __syncthreads();
+  if constexpr (SHRINK_ONLY) {
+    for (int v = threadIdx.x; v < kGMRows * RB * 16; v += kGMThreads) {
+      const int row = v / (RB * 16), rk = v % (RB * 16);
+      if (row < nrows) {
+        const int rbv = row >> 4, rw = row & 15;
+        const int rr = row0 + row;
+        const int q = a.order != nullptr ? a.order[rr] : rr;
+        a.hout[(size_t)q * (RB * 16) + rk] = red[(rbv * 16 + rw) * kRS + rk] + red[((4 + rbv) * 16 + rw) * kRS + rk];
+      }
+    }
+    __syncthreads();  // the next sub-tile reuses the buffers
+    return;
+  }
   for (int v = threadIdx.x; v < kGMRows * RB * 16; v += kGMThreads) {
     const int row = v / (RB * 16), rk = v % (RB * 16);
     const int rbv = row >> 4, rw = row & 15;
@@ -304,7 +323,7 @@ __device__ void gm_tile(const GMArgs& a, GMLds<RB>& L, int e, int row0, int nrow
 // cut into nt = ceil(c / tile_rows) tiles: balanced (tile i: rows c*i/nt .. c*(i+1)/nt) or,
 // fixed, tile_rows rows each but the last; the tiles are numbered segment by segment, so
 // consecutive tiles (which run on one XCD) mostly share their adapter in its L2.
-template <int RB, bool INDIRECT, bool Y0F32, bool YF32>
+template <int RB, bool INDIRECT, bool Y0F32, bool YF32, bool SHRINK_ONLY = false>
 __device__ void gm_range(const GMArgs& a, GMLds<RB>& L) {
   const int lane = threadIdx.x & 63;
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
@@ -330,7 +349,7 @@ __device__ void gm_range(const GMArgs& a, GMLds<RB>& L) {
     r1 = s0 + (int)((long long)c * (i + 1) / nt);
   }
   const int cols = a.tgt.d_out / a.col_groups;
-  gm_tile<RB, INDIRECT, Y0F32, YF32>(a, L, e, r0, r1 - r0, g * cols, cols);
+  gm_tile<RB, INDIRECT, Y0F32, YF32, SHRINK_ONLY>(a, L, e, r0, r1 - r0, g * cols, cols);
 }
 
 }  // namespace molora

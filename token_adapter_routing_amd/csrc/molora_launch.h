@@ -45,10 +45,9 @@ struct ApplyLaunch {
   int col_groups;    // 0 = choose
 };
 
-// Grouped shrink per pair without gate weight or scale into hpart [nsplit][P][r_pad] fp32.
-hipError_t launch_pair_shrink(const TargetDev& tgt, bool indirect, const uint16_t* x, const int32_t* offsets,
-                              const int32_t* perm, int K, int k, long long P, float* hpart, int nsplit,
-                              hipStream_t s);
+// Per-pair shrink without gate weight or scale (64-row grouped tiles) into hout [P][r_pad] fp32.
+hipError_t launch_pair_shrink_gm(const TargetDev& tgt, bool indirect, const uint16_t* x, const int32_t* offsets,
+                                 const int32_t* perm, int K, int k, long long P, float* hout, hipStream_t s);
 
 // Backward of the routed LoRA except dx: dA, dB, dw (any may be NULL) from x, gy and the
 // forward routing; ws holds bwd_plan() for these shapes.

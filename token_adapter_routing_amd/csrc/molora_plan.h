@@ -153,7 +153,7 @@ MultiPlan apply_multi_plan(int n, const int* d_in, const int* d_out, int N, int 
                            int path);
 
 // ---- backward (molora_backward): per-pair h = x A_e and g = gy B_e^T from two grouped
-// shrinks (split over the reduction like the skinny path, unscaled), a pair pass that writes
+// shrinks (unscaled, one partial each), a pair pass that writes
 // dL/dw and the scaled h, g as bf16 hi/lo chunks [nchunks][2][r_pad][Qc] (rank-major, pairs
 // contiguous, zero past the segment), then the weight-gradient reductions over each
 // segment's pairs: partials [nchunks][D / 128][128][r_pad] fp32, summed chunk by chunk.
@@ -170,6 +170,7 @@ struct BwdPlan {
   size_t apply_off, apply_bytes;   // dx: the apply on the transposed adapters
   size_t total;
 };
+int wgrad_chunk(long long P, int D);
 // dx_path: the resolved path of the dx apply (apply_resolve_path on the transposed shapes).
 BwdPlan bwd_plan(int N, int k, int K, int r_pad, int d_in, int d_out, bool dx_f32, int dx_path);
 // bf16 elements of one chunk's hi (or lo) plane; the lo plane follows the hi plane.

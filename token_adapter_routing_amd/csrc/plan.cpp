@@ -186,22 +186,21 @@ MultiPlan apply_multi_plan(int n, const int* d_in, const int* d_out, int N, int 
   return m;
 }
 
-// Splits: enough shrink workgroups to cover the chip (about 1024) without more partial
-// traffic than needed.  Chunks: about 512 weight-gradient workgroups over the narrower of the
-// two widths, between 64 and 2048 pairs each.
+// Pairs per weight-gradient chunk: about 512 workgroups of (chunk, 128 columns), two per
+// compute unit, between 256 and 4096 pairs each.  A chunk's fp32 partial (128 x r_pad) costs
+// 2 r_pad / Qc of the bf16 rows it reads, written and read once, so chunks stay long.
+int wgrad_chunk(long long P, int D) {
+  const long long ncb = D / kWCols;
+  const long long steps = std::max<long long>(4, std::min<long long>(64, P * ncb / (512LL * kWStep)));
+  return (int)(steps * kWStep);
+}
+
 BwdPlan bwd_plan(int N, int k, int K, int r_pad, int d_in, int d_out, bool dx_f32, int dx_path) {
   BwdPlan b{};
   const long long P = (long long)N * k;
-  const long long tiles = P / kTileRows + K + 1;
-  auto splits = [&](int d) {
-    const long long want = (1024 + tiles - 1) / tiles;
-    return (int)std::max<long long>(1, std::min<long long>(want, skinny_splits(d)));
-  };
-  b.nsh = splits(d_in);
-  b.nsg = splits(d_out);
-  const long long ncb = std::min(d_in, d_out) / kWCols;
-  const long long steps = std::max<long long>(1, std::min<long long>(32, P * ncb / (512LL * kWStep)));
-  b.Qc = (int)(steps * kWStep);
+  b.nsh = 1;  // the grouped shrink-only kernel reduces d whole per tile
+  b.nsg = 1;
+  b.Qc = wgrad_chunk(P, std::min(d_in, d_out));
   b.nchunks = (P + b.Qc - 1) / b.Qc + K;
   size_t off = 0;
   b.h_off = off;
@@ -228,9 +227,7 @@ BwdPlan bwd_plan(int N, int k, int K, int r_pad, int d_in, int d_out, bool dx_f3
 
 RouterBwdPlan router_bwd_plan(int N, int d, int K) {
   RouterBwdPlan p{};
-  const long long ncb = d / kWCols;
-  const long long steps = std::max<long long>(1, std::min<long long>(32, (long long)N * ncb / (512LL * kWStep)));
-  p.Qc = (int)(steps * kWStep);
+  p.Qc = wgrad_chunk(N, d);
   p.nchunks = ((long long)N + p.Qc - 1) / p.Qc + 1;
   p.ntb = (N + kRouterTokBlock - 1) / kRouterTokBlock;
   size_t off = 0;
