@@ -2,7 +2,8 @@
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and the benchmark's CPU-baseline leg
 may import this package.  The GPU library never calls it and shares no code
-with it.  See ``oracle/molora_oracle.py`` for the functions and their sources.
+with it.  See ``oracle/molora_oracle.py`` for the functions and their sources, and
+``oracle/transformer.py`` for the synthetic decoder with per-token LoRA.
 """
 from .molora_oracle import (  # noqa: F401
     bf16_to_f64,
@@ -17,3 +18,4 @@ from .molora_oracle import (  # noqa: F401
     route_topk_backward,
     router_backward,
 )
+from . import transformer  # noqa: F401,E402

@@ -35,7 +35,7 @@ import numpy as np
 BASE_SEED = 20260316
 
 # tensor ids inside one case (stable: changing them changes every input)
-T_IDS, T_X, T_Y0, T_A, T_B, T_W1, T_B1, T_W2, T_B2, T_LOGITS, T_IDX, T_RUNS, T_CLUSTER, T_GY, T_DX0 = range(15)
+T_IDS, T_X, T_Y0, T_A, T_B, T_W1, T_B1, T_W2, T_B2, T_LOGITS, T_IDX, T_RUNS, T_CLUSTER, T_GY, T_DX0, T_BASE, T_NORM = range(17)
 
 
 def rng_for(case_id: int, tensor_id: int, sub: int = 0) -> np.random.Generator:
@@ -257,3 +257,52 @@ def grad_case(case_id: int, N: int, d_in: int, d_out: int, sub: int = 0):
     """Upstream gradient dL/dy [N][d_out] and the rest of dL/dx [N][d_in] of a backward case,
     bf16 bits, N(0, 1)."""
     return (normal_bf16(case_id, T_GY, (N, d_out), sub=sub), normal_bf16(case_id, T_DX0, (N, d_in), sub=sub))
+
+
+XF_TARGETS = ("q", "k", "v", "o", "gate", "up", "down")
+
+
+def xf_mlp_width(d: int) -> int:
+    """MLP width of the synthetic decoder: 8d/3 rounded up to a multiple of 128."""
+    return -(-(8 * d) // (3 * 128)) * 128
+
+
+def xf_dims(d: int, f: int):
+    """(d_in, d_out) of the seven LoRA targets, in XF_TARGETS order."""
+    return [(d, d), (d, d), (d, d), (d, d), (d, f), (d, f), (f, d)]
+
+
+def xf_layers(case_id: int, d: int, L: int, K: int, r: int, f: int = None):
+    """Random decoder weights as bf16 bits: RMSNorm weights 1 + N(0, 0.1^2); base projections
+    N(0, 1/fan_in) in nn.Linear layout [out][in]; per target K LoRA adapters
+    A [K][d_in][r] ~ N(0, 1/d_in), B [K][r][d_out] ~ N(0, 1/(16 r)) (deltas about a quarter of
+    the base output)."""
+    f = f or xf_mlp_width(d)
+    layers = []
+    for l in range(L):
+        sub = 1000 * (l + 1)
+        lay = {"norm1": normal_bf16(case_id, T_NORM, (d,), std=0.1, mean=1.0, sub=sub),
+               "norm2": normal_bf16(case_id, T_NORM, (d,), std=0.1, mean=1.0, sub=sub + 1)}
+        for i, (name, (din, dout)) in enumerate(zip(("Wq", "Wk", "Wv", "Wo", "Wgate", "Wup", "Wdown"),
+                                                    xf_dims(d, f))):
+            lay[name] = normal_bf16(case_id, T_BASE, (dout, din), std=1.0 / np.sqrt(din), sub=sub + i)
+        lay["A"], lay["B"] = [], []
+        for i, (din, dout) in enumerate(xf_dims(d, f)):
+            lay["A"].append(normal_bf16(case_id, T_A, (K, din, r), std=1.0 / np.sqrt(din), sub=sub + i))
+            lay["B"].append(normal_bf16(case_id, T_B, (K, r, dout), std=0.25 / np.sqrt(r), sub=sub + i))
+        layers.append(lay)
+    return layers
+
+
+def xf_batch(case_id: int, n_seq: int, seq_len: int, d: int, K: int, mean_run: float = 64.0, probs=None):
+    """Interleaved mixed-modality batch (Tables 7 and 8): per-token modality labels in runs of
+    mean length `mean_run` (uniform over the K modalities unless `probs`), the token ids of
+    those labels under vocabulary ranges of 8192 ids each, and N(0, 1) input activations
+    [N][d] (the embedding lookup is not part of the measured path)."""
+    N = n_seq * seq_len
+    p = probs if probs is not None else [1.0 / K] * K
+    labels = modality_runs(case_id, N, p, mean_run)
+    bounds = vocab_bounds(K)
+    ids = ids_for_labels(case_id, labels, bounds)
+    x = normal_bf16(case_id, T_X, (N, d), sub=7)
+    return x, ids, bounds, labels
