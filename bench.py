@@ -85,7 +85,7 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run plain device copies of known size (for HBM counter scaling)")
-    p.add_argument("--rows", default="C0,C2,C3,C4,C4stack,paging,tiling,backward",
+    p.add_argument("--rows", default="C0,C2,C3,C4,C4stack,paging,tiling,backward,xf",
                    help="other configurations to measure beside the headline (comma list, or 'none')")
     p.add_argument("--row-reps", type=int, default=100, help="graph replays per timed row entry")
     p.add_argument("--stack-replays", type=int, default=1000, help="single-graph replays of the 28-layer stack row")
@@ -387,6 +387,8 @@ def measure_rows(m, torch, dev, rows, reps, stack_replays=1000):
         res["tiling"] = row_tiling(m, torch, dev, bf, f32, i32, max(20, reps // 4))
     if "backward" in rows:
         res["backward"] = row_backward(m, torch, dev, bf, f32, max(20, reps // 4))
+    if "xf" in rows:
+        res["xf_end_to_end"] = row_xf(m, torch, dev, max(5, reps // 20))
     if "paging" in rows:
         res["C1_paging"] = row_paging(m, torch, dev, bf, i32, max(200, reps * 2))
     torch.cuda.synchronize()
@@ -836,6 +838,77 @@ def row_backward(m, torch, dev, bf, f32, reps):
                           "us": ms * 1e3, "compulsory_bytes": rbytes,
                           "roofline_frac": rbytes / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9)}
     del gr
+    return out
+
+
+def row_xf(m, torch, dev, reps):
+    """The synthetic decoder with per-token LoRA on all seven projections (the pages' Table 7:
+    d = 1024 / 2048 / 4096, L = 2 / 4, batches 16x512, 4x512, 16x512, K = 4; Table 8: d = 2048,
+    L = 4, K = 2, interleaved modalities), rank 16, vocabulary routing of interleaved modality
+    runs (mean run 64 tokens).  Per token: one forward with the per-token routing.  Per
+    sequence (the pages' simulation): K forwards, pass e with every token on adapter e.  Base:
+    one forward without adapters.  Eager launches (the base GEMMs are rocBLAS calls), timed
+    with events around `reps` repetitions after a warmup."""
+    import synth
+    gen = torch.Generator(device=dev)
+    out = {}
+    configs = [("table7_d1024_L2", 1024, 2, 16, 512, 4), ("table7_d2048_L4", 2048, 4, 4, 512, 4),
+               ("table7_d4096_L4", 4096, 4, 16, 512, 4), ("table8_d2048_L4_K2", 2048, 4, 4, 512, 2)]
+    for name, d, L, n_seq, seq_len, K in configs:
+        gen.manual_seed(1000 + d + L + K)
+        f = synth.xf_mlp_width(d)
+        r = 16
+        dims = synth.xf_dims(d, f)
+
+        def randn(*shape, std):
+            return (torch.randn(*shape, generator=gen, device=dev) * std).to(torch.bfloat16)
+
+        layers, bare = [], []
+        for _ in range(L):
+            W = [randn(dout, din, std=din ** -0.5) for din, dout in dims]
+            n1 = (1 + randn(d, std=0.1).float()).to(torch.bfloat16)
+            n2 = (1 + randn(d, std=0.1).float()).to(torch.bfloat16)
+            hs = m.molora_hotset_init([(randn(K, din, r, std=din ** -0.5), randn(K, r, dout, std=0.25 / r ** 0.5))
+                                       for din, dout in dims], 2.0)
+            layers.append({"norm1": n1, "norm2": n2, "W": W, "lora": hs})
+            bare.append({"norm1": n1, "norm2": n2, "W": W, "lora": None})
+        model, base = m.XfModel(d, f, layers), m.XfModel(d, f, bare)
+        N = n_seq * seq_len
+        labels = synth.modality_runs(1000 + d, N, [1.0 / K] * K, 64.0)
+        bounds = synth.vocab_bounds(K)
+        ids = torch.from_numpy(synth.ids_for_labels(1000 + d, labels, bounds)).to(dev)
+        idx, w = m.molora_route_vocab(ids, [int(b) for b in bounds])
+        route = m.molora_dispatch(idx, w, K, 1)[1:]
+        passes = []
+        for e in range(K):
+            ie = torch.full((N,), e, dtype=torch.int32, device=dev)
+            passes.append(m.molora_dispatch(ie, torch.ones(N, device=dev), K, 1)[1:])
+        x = randn(N, d, std=1.0)
+        y = torch.empty_like(x)
+        ws = torch.empty(m.molora_xf_workspace(model, n_seq, seq_len), dtype=torch.uint8, device=dev)
+
+        def timed(fn):
+            for _ in range(2):
+                fn()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / reps
+
+        per_token = timed(lambda: m.molora_xf_forward(model, x, n_seq, seq_len, route=route, out=y, ws=ws))
+        per_seq = timed(lambda: [m.molora_xf_forward(model, x, n_seq, seq_len, route=p, out=y, ws=ws) for p in passes])
+        base_ms = timed(lambda: m.molora_xf_forward(base, x, n_seq, seq_len, out=y, ws=ws))
+        flops = 2 * N * L * sum(a * b for a, b in dims) + 4 * n_seq * L * (d // 128) * seq_len * seq_len * 128
+        out[name] = {"workload": f"decoder d={d} f={f} L={L} batch {n_seq}x{seq_len} K={K} r={r} (7 LoRA targets)",
+                     "per_token_ms": per_token, "per_sequence_sim_ms": per_seq, "speedup": per_seq / per_token,
+                     "base_only_ms": base_ms, "lora_overhead_frac": per_token / base_ms - 1.0,
+                     "base_tflops_per_token_pass": flops / (per_token * 1e-3) / 1e12}
+        del ws, layers, bare, model, base
+        torch.cuda.empty_cache()
     return out
 
 

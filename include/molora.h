@@ -453,6 +453,51 @@ int molora_router_backward(const void *x, int N, int d, const void *W1, const fl
                            float *dW2, float *db2, const float *dx0, float *dx, void *ws,
                            size_t ws_bytes, void *stream);
 
+/* ------------------------------------------------------------------------
+ * Synthetic decoder with per-token LoRA (thelatestinai.com, Table 7: an
+ * end-to-end transformer, d = 1024/2048/4096, L = 2/4, whose per-token pass is
+ * compared with a per-sequence simulation of one forward pass per adapter;
+ * Table 8: an interleaved two-modality batch, d = 2048, L = 4, K = 2).  The
+ * pages fix only d, L, K and the batch; this layer is a plain pre-norm
+ * decoder:
+ *   x += o(attn(rmsnorm1(x)));   x += down(silu(gate(h)) * up(h)), h = rmsnorm2(x)
+ * RMSNorm with a learned weight and eps 1e-6; causal softmax attention inside
+ * each sequence, heads of width 128 (d / 128 heads), scores scaled by
+ * 1/sqrt(128), no positional encoding; no biases.  Each of the seven
+ * projections q, k, v, o, gate, up, down is base + per-token LoRA: the base
+ * product (rocBLAS, bf16 operands, fp32 accumulation, stored bf16) then the
+ * grouped per-token delta of molora_apply added in place, all projections
+ * sharing one routing (offsets, perm, perm_w, inv of molora_dispatch for the
+ * N = n_seq * seq_len tokens, token t of sequence b being row b * seq_len + t).
+ * Activations are stored bf16 between kernels.
+ *   layer.norm1, norm2  device bf16 [d]
+ *   layer.W[7]          device bf16, nn.Linear layout [out][in]: q, k, v, o
+ *                       [d][d]; gate, up [f][d]; down [d][f]
+ *   layer.lora          a forward hot set of exactly these 7 targets (in that
+ *                       order and those shapes), or NULL: no adapters on that
+ *                       layer.  Every LoRA layer has the same K.
+ *   x_in, x_out         device bf16 [N][d] (x_out may equal x_in)
+ *   ws                  molora_xf_workspace() bytes, 256-byte aligned, no
+ *                       initial contents (activations, scores, the applies'
+ *                       workspace and rocBLAS's; the first call on a device
+ *                       creates that device's rocBLAS handle).
+ * Supported: d, f multiples of 128; 1 <= k <= 8.  Asynchronous on `stream`.
+ * Errors (nothing enqueued): shapes -> MOLORA_ENOTSUP; NULL, misaligned or
+ * mismatched arguments -> MOLORA_EINVAL; short workspace -> MOLORA_ENOSPC; a
+ * failed launch or GEMM -> MOLORA_EHIP.
+ * ------------------------------------------------------------------------ */
+typedef struct {
+  const void *norm1, *norm2;
+  const void *W[7];
+  const molora_hotset *lora;
+} molora_xf_layer;
+int molora_xf_workspace(int d, int f, int n_layers, const molora_xf_layer *layers, int n_seq,
+                        int seq_len, int k, size_t *bytes);
+int molora_xf_forward(int d, int f, int n_layers, const molora_xf_layer *layers, int n_seq,
+                      int seq_len, const void *x_in, void *x_out, int k, const int32_t *offsets,
+                      const int32_t *perm, const float *perm_w, const int32_t *inv, void *ws,
+                      size_t ws_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -186,6 +186,48 @@ hipError_t launch_router_backward(const RouterBackwardLaunch& a, hipStream_t) {
   write_span<int32_t>(a.ws + p.offs_off, 0, 2, "router offsets");
   return hipSuccess;
 }
+// What launch_xf_forward writes into the workspace (xfmr.cpp): every activation region, the
+// LoRA applies' workspace of each call and the GEMM library's workspace.
+hipError_t launch_xf_forward(const XfLaunch& a, hipStream_t) {
+  ++g_launches;
+  const XfPlan p = xf_plan(a.n_seq, a.seq_len, a.d, a.f, a.lora_bytes);
+  const size_t N = (size_t)a.n_seq * a.seq_len, H = a.d / kXfHeadDim, ss = (size_t)a.n_seq * H * a.seq_len * a.seq_len;
+  write_span<uint16_t>(a.ws + p.h_off, 0, N * a.d, "xf h");
+  write_span<uint16_t>(a.ws + p.q_off, 0, N * a.d, "xf q");
+  write_span<uint16_t>(a.ws + p.k_off, 0, N * a.d, "xf k");
+  write_span<uint16_t>(a.ws + p.v_off, 0, N * a.d, "xf v");
+  write_span<uint16_t>(a.ws + p.att_off, 0, N * a.d, "xf att");
+  write_span<uint16_t>(a.ws + p.o_off, 0, N * a.d, "xf o");
+  write_span<uint16_t>(a.ws + p.g_off, 0, N * a.f, "xf gate");
+  write_span<uint16_t>(a.ws + p.u_off, 0, N * a.f, "xf up");
+  write_span<float>(a.ws + p.s_off, 0, ss, "xf scores");
+  write_span<uint16_t>(a.ws + p.p_off, 0, ss, "xf probs");
+  write_span<char>(a.ws + p.blas_off, 0, p.blas_bytes, "xf blas");
+  for (int l = 0; l < a.n_layers; ++l) {
+    const XfLayerDev& L = a.layers[l];
+    if (!L.lora) continue;
+    ApplyLaunch m{};
+    m.N = (int)N; m.k = a.k; m.K = a.K; m.y_f32 = 0; m.ws = reinterpret_cast<float*>(a.ws + p.lora_off);
+    // the single-target applies (o, down) at their own shapes; the multi applies' plans
+    for (int t : {kXfO, kXfDown}) {
+      m.tgt = L.tgt[t];
+      m.path = t == kXfO ? a.path_o : a.path_down;
+      const size_t before = g_ranges.size();
+      apply_writes(m);
+      // the applies run one after another in the same region: one array for the overlap check
+      for (size_t i = before; i < g_ranges.size(); ++i) g_ranges[i].what = "xf lora";
+    }
+    int din[3], dout[3];
+    for (int i = 0; i < 3; ++i) { din[i] = L.tgt[i].d_in; dout[i] = L.tgt[i].d_out; }
+    const MultiPlan mq = apply_multi_plan(3, din, dout, (int)N, a.k, a.K, L.tgt[0].r_pad, false, kPathAuto);
+    CHECK(mq.path == a.path_qkv, "q/k/v path %d vs %d", mq.path, a.path_qkv);
+    write_span<char>(a.ws + p.lora_off, 0, mq.total, "xf lora");
+    for (int i = 0; i < 2; ++i) { din[i] = L.tgt[kXfGate + i].d_in; dout[i] = L.tgt[kXfGate + i].d_out; }
+    const MultiPlan mg = apply_multi_plan(2, din, dout, (int)N, a.k, a.K, L.tgt[0].r_pad, false, kPathAuto);
+    write_span<char>(a.ws + p.lora_off, 0, mg.total, "xf lora");
+  }
+  return hipSuccess;
+}
 hipError_t launch_apply(const ApplyLaunch& a, hipStream_t) {
   ++g_launches;
   g_last_apply_path = a.path;
@@ -490,6 +532,60 @@ static void test_router_backward(int N, int d, int K) {
         "k > K accepted");
 }
 
+static void test_xf(int d, int f, int L, int n_seq, int seq_len, int K, int r, int k, bool lora) {
+  std::vector<HostHotset> hsv(L);
+  std::vector<molora_xf_layer> layers(L);
+  for (int l = 0; l < L; ++l) {
+    molora_xf_layer& X = layers[l];
+    X.norm1 = fake(0x1000);
+    X.norm2 = fake(0x1100);
+    for (int t = 0; t < 7; ++t) X.W[t] = fake(0x2000 + 0x100 * t);
+    X.lora = nullptr;
+    if (lora) {
+      if (!make_hotset(hsv[l], K, r, {{d, d}, {d, d}, {d, d}, {d, d}, {d, f}, {d, f}, {f, d}}, MOLORA_LAYOUT_DIRECT)) return;
+      X.lora = hsv[l].hs;
+    }
+  }
+  size_t need = 0;
+  int rc = molora_xf_workspace(d, f, L, layers.data(), n_seq, seq_len, k, &need);
+  if (lora && k > K) {
+    CHECK(rc == MOLORA_ENOTSUP, "xf k > K accepted");
+  } else {
+    CHECK(rc == MOLORA_OK, "xf_workspace d=%d f=%d L=%d N=%dx%d", d, f, L, n_seq, seq_len);
+    if (need <= kMaxBuf) {
+      char* ws = static_cast<char*>(exact_alloc(need));
+      g_ws_base = ws;
+      g_ws_bytes = need;
+      g_ranges.clear();
+      const int l0 = g_launches;
+      rc = molora_xf_forward(d, f, L, layers.data(), n_seq, seq_len, fake(0x3000), fake(0x4000), k,
+                             (int32_t*)fake(0x8000), (int32_t*)fake(0x9000), (float*)fake(0xa000),
+                             (int32_t*)fake(0xb000), ws, need, nullptr);
+      CHECK(rc == MOLORA_OK && g_launches == l0 + 1, "xf_forward");
+      check_disjoint("xf_forward");
+      rc = molora_xf_forward(d, f, L, layers.data(), n_seq, seq_len, fake(0x3000), fake(0x4000), k,
+                             (int32_t*)fake(0x8000), (int32_t*)fake(0x9000), (float*)fake(0xa000),
+                             (int32_t*)fake(0xb000), ws, need - 1, nullptr);
+      CHECK(rc == MOLORA_ENOSPC, "short xf workspace accepted");
+      g_ws_base = nullptr;
+      free(ws);
+    }
+    // a LoRA layer with the wrong shapes is refused
+    if (lora) {
+      HostHotset bad;
+      if (make_hotset(bad, K, r, {{d, d}, {d, d}, {d, d}, {d, d}, {d, f}, {d, f}, {d, f}}, MOLORA_LAYOUT_DIRECT)) {
+        const molora_hotset* keep = layers[0].lora;
+        layers[0].lora = bad.hs;
+        CHECK(molora_xf_workspace(d, f, L, layers.data(), n_seq, seq_len, k, &need) == MOLORA_EINVAL,
+              "mismatched LoRA targets accepted");
+        layers[0].lora = keep;
+        molora_hotset_destroy(bad.hs);
+      }
+    }
+  }
+  for (auto& h : hsv) molora_hotset_destroy(h.hs);
+}
+
 static void test_multi(int K, int r, int N, int k, int path, int y_dtype) {
   const std::vector<std::pair<int, int>> qwen = {{2048, 2048}, {2048, 1024}, {2048, 1024}, {2048, 2048},
                                                  {2048, 6144}, {2048, 6144}, {6144, 2048}};
@@ -658,6 +754,11 @@ int main() {
   for (int N : {0, 1, 63, 64, 65, 4096, 5000, 65536})
     for (int d : {128, 2048, 4096})
       for (int K : {1, 4, 64}) test_router_backward(N, d, K);
+  test_xf(256, 768, 2, 2, 64, 4, 8, 1, true);
+  test_xf(256, 768, 1, 3, 17, 2, 16, 2, true);
+  test_xf(256, 768, 2, 2, 64, 4, 8, 1, false);
+  test_xf(1024, 2816, 2, 16, 512, 4, 16, 1, true);
+  test_xf(512, 1408, 1, 1, 100, 2, 16, 3, true);
   free(g_scratch);
   fprintf(stderr, "%d checks, %d failures\n", g_checks, g_fail);
   return g_fail == 0 ? 0 : 1;

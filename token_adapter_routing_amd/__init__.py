@@ -14,4 +14,5 @@ from .binding import (  # noqa: F401
     molora_route_vocab, molora_seqpass_meta, molora_step_vocab, molora_step_vocab_noalloc, molora_step_workspace,
     molora_hotset_init_transposed, molora_backward, molora_backward_workspace,
     molora_route_topk_backward, molora_router_backward, molora_router_backward_workspace,
+    XfModel, XF_TARGETS, molora_xf_workspace, molora_xf_forward,
 )

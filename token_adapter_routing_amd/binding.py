@@ -37,6 +37,10 @@ class MoloraTarget(ctypes.Structure):
     _fields_ = [("d_in", _c_i), ("d_out", _c_i), ("A", _c_p), ("B", _c_p)]
 
 
+class MoloraXfLayer(ctypes.Structure):
+    _fields_ = [("norm1", _c_p), ("norm2", _c_p), ("W", _c_p * 7), ("lora", _c_p)]
+
+
 _SIGS = {
     "molora_last_error": (ctypes.c_char_p, []),
     "molora_hotset_bytes": (_c_i, [_c_i, _c_i, _c_i, ctypes.POINTER(MoloraTarget), _c_i, ctypes.POINTER(_c_sz)]),
@@ -64,6 +68,10 @@ _SIGS = {
                                              _c_i, _c_p, _c_sz, _c_p]),
     "molora_backward_workspace": (_c_i, [_c_p, _c_p, _c_i, _c_i, _c_i, _c_i, ctypes.POINTER(_c_sz)]),
     "molora_route_topk_backward": (_c_i, [_c_p, _c_p, _c_p, _c_i, _c_i, _c_i, _c_p, _c_p]),
+    "molora_xf_workspace": (_c_i, [_c_i, _c_i, _c_i, ctypes.POINTER(MoloraXfLayer), _c_i, _c_i, _c_i,
+                                   ctypes.POINTER(_c_sz)]),
+    "molora_xf_forward": (_c_i, [_c_i, _c_i, _c_i, ctypes.POINTER(MoloraXfLayer), _c_i, _c_i, _c_p, _c_p, _c_i,
+                                 _c_p, _c_p, _c_p, _c_p, _c_p, _c_sz, _c_p]),
     "molora_router_backward_workspace": (_c_i, [_c_i, _c_i, _c_i, ctypes.POINTER(_c_sz)]),
     "molora_router_backward": (_c_i, [_c_p, _c_i, _c_i, _c_p, _c_p, _c_p, _c_i, _c_p,  # x .. dlogits
                                       _c_p, _c_p, _c_p, _c_p, _c_p, _c_p,  # dW1, db1, dW2, db2, dx0, dx
@@ -546,3 +554,50 @@ def molora_router_backward(x: torch.Tensor, W1: torch.Tensor, b1: Optional[torch
         _ptr(g("db2"), torch.float32, "db2"), _ptr(dx0, torch.float32, "dx0"), _ptr(g("dx"), torch.float32, "dx"),
         _ptr(ws, torch.uint8, "ws"), ws.numel(), _stream(stream)))
     return o
+
+
+# ----------------------------------------------------------------------------------- decoder
+
+XF_TARGETS = ("q", "k", "v", "o", "gate", "up", "down")
+
+
+class XfModel:
+    """Device weights of the synthetic decoder: per layer norm1, norm2 (bf16 [d]), the seven
+    base projections (bf16, nn.Linear layout) and an optional 7-target LoRA hot set."""
+
+    def __init__(self, d: int, f: int, layers):
+        self.d, self.f = d, f
+        self.layers = layers  # list of dicts: norm1, norm2, W (list of 7), lora (HotSet or None)
+        arr = (MoloraXfLayer * len(layers))()
+        for i, L in enumerate(layers):
+            arr[i].norm1 = _ptr(L["norm1"], torch.bfloat16, "norm1")
+            arr[i].norm2 = _ptr(L["norm2"], torch.bfloat16, "norm2")
+            for t in range(7):
+                arr[i].W[t] = _ptr(L["W"][t], torch.bfloat16, f"W[{t}]")
+            arr[i].lora = L["lora"].handle if L.get("lora") is not None else None
+        self._arr = arr
+
+
+def molora_xf_workspace(model: XfModel, n_seq: int, seq_len: int, k: int = 1) -> int:
+    n = _c_sz()
+    _check(load_library().molora_xf_workspace(model.d, model.f, len(model.layers), model._arr, int(n_seq),
+                                              int(seq_len), int(k), ctypes.byref(n)))
+    return n.value
+
+
+def molora_xf_forward(model: XfModel, x: torch.Tensor, n_seq: int, seq_len: int, route=None, k: int = 1,
+                      out: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None, stream=None):
+    """Decoder forward; route = (offsets, perm, perm_w, inv) of molora_dispatch (None when no
+    layer has LoRA)."""
+    if out is None:
+        out = torch.empty_like(x)
+    need = molora_xf_workspace(model, n_seq, seq_len, k)
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(need, dtype=torch.uint8, device=x.device)
+    offsets, perm, perm_w, inv = route if route is not None else (None, None, None, None)
+    _check(load_library().molora_xf_forward(
+        model.d, model.f, len(model.layers), model._arr, int(n_seq), int(seq_len), _ptr(x, torch.bfloat16, "x"),
+        _ptr(out, torch.bfloat16, "out"), int(k), _ptr(offsets, torch.int32, "offsets"), _ptr(perm, torch.int32, "perm"),
+        _ptr(perm_w, torch.float32, "perm_w"), _ptr(inv, torch.int32, "inv"), _ptr(ws, torch.uint8, "ws"), ws.numel(),
+        _stream(stream)))
+    return out

@@ -17,7 +17,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmolora.so")
-SOURCES = ["capi.cpp", "plan.cpp", "route.hip", "dispatch.hip", "apply.hip", "backward.hip"]
+SOURCES = ["capi.cpp", "plan.cpp", "route.hip", "dispatch.hip", "apply.hip", "backward.hip", "xf.hip", "xfmr.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
@@ -55,7 +55,8 @@ def build(verbose: bool = False) -> str:
         if rc != 0:
             raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{out}")
     tmp = LIB + ".tmp"
-    rc, out = _run([HIPCC, "-shared", f"--offload-arch={ARCH}", "-o", tmp, *objs])
+    rc, out = _run([HIPCC, "-shared", f"--offload-arch={ARCH}", "-o", tmp, *objs, "-L/opt/rocm/lib", "-lrocblas",
+                    "-Wl,-rpath,/opt/rocm/lib"])
     if rc != 0:
         raise RuntimeError(f"link failed\n{out}")
     os.replace(tmp, LIB)

@@ -3,6 +3,7 @@
 // is enqueued; kernels then assume valid shapes.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -772,6 +773,132 @@ int molora_router_backward(const void* x, int N, int d, const void* W1, const fl
   a.ws = reinterpret_cast<char*>(ws);
   const hipError_t e = molora::launch_router_backward(a, reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? ok() : hip_fail(e, "router_backward launch");
+}
+
+namespace {
+
+// Shapes of the decoder's seven LoRA targets (q, k, v, o, gate, up, down).
+void xf_dims(int d, int f, int* din, int* dout) {
+  const int di[molora::kXfTargets] = {d, d, d, d, d, d, f};
+  const int dn[molora::kXfTargets] = {d, d, d, d, f, f, d};
+  for (int t = 0; t < molora::kXfTargets; ++t) {
+    din[t] = di[t];
+    dout[t] = dn[t];
+  }
+}
+
+// Validates the model description; on success *K is the adapters per target (0: no layer
+// has LoRA) and *lora_bytes the largest workspace of one layer's applies.
+int xf_check(int d, int f, int n_layers, const molora_xf_layer* layers, int n_seq, int seq_len, int k, int* K,
+             size_t* lora_bytes, int* paths) {
+  if (d <= 0 || f <= 0 || d % 128 != 0 || f % 128 != 0)
+    return fail(MOLORA_ENOTSUP, "d=%d and f=%d must be positive multiples of 128", d, f);
+  if (n_layers < 1 || n_layers > 1024 || layers == nullptr) return fail(MOLORA_EINVAL, "n_layers=%d or layers", n_layers);
+  if (n_seq < 1 || seq_len < 1) return fail(MOLORA_EINVAL, "n_seq=%d seq_len=%d", n_seq, seq_len);
+  const long long N = (long long)n_seq * seq_len;
+  if (N * std::max(d, f) >= (1ll << 31) || (long long)n_seq * (d / 128) * seq_len * (long long)seq_len >= (1ll << 31))
+    return fail(MOLORA_ENOTSUP, "batch too large");
+  if (k < 1 || k > MOLORA_MAX_TOPK) return fail(MOLORA_ENOTSUP, "k=%d outside [1, %d]", k, MOLORA_MAX_TOPK);
+  int din[molora::kXfTargets], dout[molora::kXfTargets];
+  xf_dims(d, f, din, dout);
+  *K = 0;
+  *lora_bytes = 0;
+  for (int l = 0; l < n_layers; ++l) {
+    const molora_xf_layer& L = layers[l];
+    if (L.norm1 == nullptr || L.norm2 == nullptr || !aligned(L.norm1, 16) || !aligned(L.norm2, 16))
+      return fail(MOLORA_EINVAL, "layer %d: norm weights NULL or misaligned", l);
+    for (int t = 0; t < molora::kXfTargets; ++t)
+      if (L.W[t] == nullptr || !aligned(L.W[t], 16)) return fail(MOLORA_EINVAL, "layer %d: W[%d] NULL or misaligned", l, t);
+    const molora_hotset* hs = L.lora;
+    if (hs == nullptr) continue;
+    if (hs->transposed || hs->n_targets != molora::kXfTargets)
+      return fail(MOLORA_EINVAL, "layer %d: the LoRA hot set needs the 7 forward targets", l);
+    for (int t = 0; t < molora::kXfTargets; ++t)
+      if (hs->tg[t].d_in != din[t] || hs->tg[t].d_out != dout[t])
+        return fail(MOLORA_EINVAL, "layer %d: LoRA target %d is %dx%d, %dx%d needed", l, t, hs->tg[t].d_in,
+                    hs->tg[t].d_out, din[t], dout[t]);
+    if (*K != 0 && hs->K != *K) return fail(MOLORA_EINVAL, "layer %d: K=%d differs from %d", l, hs->K, *K);
+    *K = hs->K;
+    if (k > hs->K) return fail(MOLORA_ENOTSUP, "k=%d > K=%d", k, hs->K);
+    const int rp = hs->r_pad;
+    const int pq = molora::apply_multi_resolve_path(3, (int)N, k, MOLORA_PATH_AUTO, hs->K, rp);
+    const int pg = molora::apply_multi_resolve_path(2, (int)N, k, MOLORA_PATH_AUTO, hs->K, rp);
+    const int po = molora::apply_resolve_path((int)N, k, MOLORA_PATH_AUTO, hs->K, rp);
+    if (paths != nullptr) {
+      paths[0] = pq; paths[1] = po; paths[2] = pg; paths[3] = po;
+    }
+    const size_t b[4] = {
+        molora::apply_multi_plan(3, din, dout, (int)N, k, hs->K, rp, false, MOLORA_PATH_AUTO).total,
+        molora::apply_ws_bytes((int)N, k, hs->K, rp, d, d, false, MOLORA_PATH_AUTO),
+        molora::apply_multi_plan(2, din + molora::kXfGate, dout + molora::kXfGate, (int)N, k, hs->K, rp, false,
+                                 MOLORA_PATH_AUTO).total,
+        molora::apply_ws_bytes((int)N, k, hs->K, rp, f, d, false, MOLORA_PATH_AUTO)};
+    for (size_t v : b) *lora_bytes = std::max(*lora_bytes, v);
+  }
+  return MOLORA_OK;
+}
+
+}  // namespace
+
+int molora_xf_workspace(int d, int f, int n_layers, const molora_xf_layer* layers, int n_seq, int seq_len, int k,
+                        size_t* bytes) {
+  if (bytes == nullptr) return fail(MOLORA_EINVAL, "bytes is NULL");
+  int K = 0;
+  size_t lb = 0;
+  const int rc = xf_check(d, f, n_layers, layers, n_seq, seq_len, k, &K, &lb, nullptr);
+  if (rc != MOLORA_OK) return rc;
+  *bytes = molora::xf_plan(n_seq, seq_len, d, f, lb).total;
+  return ok();
+}
+
+int molora_xf_forward(int d, int f, int n_layers, const molora_xf_layer* layers, int n_seq, int seq_len,
+                      const void* x_in, void* x_out, int k, const int32_t* offsets, const int32_t* perm,
+                      const float* perm_w, const int32_t* inv, void* ws, size_t ws_bytes, void* stream) {
+  int K = 0;
+  size_t lb = 0;
+  int paths[4] = {0, 0, 0, 0};
+  int rc = xf_check(d, f, n_layers, layers, n_seq, seq_len, k, &K, &lb, paths);
+  if (rc != MOLORA_OK) return rc;
+  if (x_in == nullptr || x_out == nullptr || !aligned(x_in, 16) || !aligned(x_out, 16))
+    return fail(MOLORA_EINVAL, "x_in or x_out NULL or not 16-byte aligned");
+  if (K > 0) {
+    if (offsets == nullptr || perm == nullptr || perm_w == nullptr || inv == nullptr)
+      return fail(MOLORA_EINVAL, "offsets, perm, perm_w and inv are required with LoRA layers");
+    if (!aligned(offsets, 4) || !aligned(perm, 4) || !aligned(perm_w, 4) || !aligned(inv, 4))
+      return fail(MOLORA_EINVAL, "misaligned pointer");
+  }
+  const molora::XfPlan plan = molora::xf_plan(n_seq, seq_len, d, f, lb);
+  if (ws == nullptr || ws_bytes < plan.total || !aligned(ws, 256))
+    return fail(MOLORA_ENOSPC, "workspace of %zu bytes (256-byte aligned) needed, %zu given", plan.total, ws_bytes);
+  std::vector<molora::XfLayerDev> dev(n_layers);
+  for (int l = 0; l < n_layers; ++l) {
+    const molora_xf_layer& L = layers[l];
+    molora::XfLayerDev& D = dev[l];
+    D.norm1 = static_cast<const uint16_t*>(L.norm1);
+    D.norm2 = static_cast<const uint16_t*>(L.norm2);
+    for (int t = 0; t < molora::kXfTargets; ++t) D.W[t] = static_cast<const uint16_t*>(L.W[t]);
+    D.lora = L.lora != nullptr;
+    if (D.lora) {
+      for (int t = 0; t < molora::kXfTargets; ++t) D.tgt[t] = L.lora->tg[t];
+      D.indirect = L.lora->layout == MOLORA_LAYOUT_INDIRECT;
+      D.scale = L.lora->scale;
+    }
+  }
+  const char* what = "";
+  molora::XfLaunch a{};
+  a.d = d; a.f = f; a.n_seq = n_seq; a.seq_len = seq_len; a.n_layers = n_layers; a.K = K; a.k = k;
+  a.eps = 1e-6f;
+  a.layers = dev.data();
+  a.x_in = static_cast<const uint16_t*>(x_in);
+  a.x_out = static_cast<uint16_t*>(x_out);
+  a.offsets = offsets; a.perm = perm; a.perm_w = perm_w; a.inv = inv;
+  a.path_qkv = paths[0]; a.path_o = paths[1]; a.path_gu = paths[2]; a.path_down = paths[3];
+  a.lora_bytes = lb;
+  a.ws = static_cast<char*>(ws);
+  a.what = &what;
+  const hipError_t e = molora::launch_xf_forward(a, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(MOLORA_EHIP, "decoder forward (%s): %s", what, hipGetErrorString(e));
+  return ok();
 }
 
 int molora_seqpass_meta(const int32_t* idx, int N, int K, int32_t* offsets, int32_t* perm, float* perm_w, void* stream) {

@@ -93,6 +93,39 @@ struct RouterBackwardLaunch {
 };
 hipError_t launch_router_backward(const RouterBackwardLaunch& a, hipStream_t s);
 
+// Synthetic decoder forward (xfmr.cpp): base projections on the GEMM library, norms,
+// attention softmax, SwiGLU and residual adds on this library's kernels (xf.hip), the
+// per-token LoRA of each projection through launch_apply / launch_apply_multi.
+enum { kXfQ, kXfK, kXfV, kXfO, kXfGate, kXfUp, kXfDown, kXfTargets };
+struct XfLayerDev {
+  const uint16_t* norm1;
+  const uint16_t* norm2;
+  const uint16_t* W[kXfTargets];  // nn.Linear layout [out][in]
+  TargetDev tgt[kXfTargets];
+  bool lora, indirect;
+  float scale;
+};
+struct XfLaunch {
+  int d, f, n_seq, seq_len, n_layers, K, k;
+  float eps;
+  const XfLayerDev* layers;
+  const uint16_t* x_in;
+  uint16_t* x_out;
+  const int32_t* offsets;
+  const int32_t* perm;
+  const float* perm_w;
+  const int32_t* inv;
+  int path_qkv, path_o, path_gu, path_down;  // resolved apply paths
+  size_t lora_bytes;                         // the LoRA applies' workspace (xf_plan's lora region)
+  char* ws;                                  // xf_plan(n_seq, seq_len, d, f, lora_bytes)
+  const char** what;                         // out: what failed
+};
+hipError_t launch_xf_forward(const XfLaunch& a, hipStream_t s);
+hipError_t launch_xf_rmsnorm(const uint16_t* x, const uint16_t* w, uint16_t* y, int N, int d, float eps, hipStream_t s);
+hipError_t launch_xf_softmax_causal(const float* S, uint16_t* P, int seq, long long rows, hipStream_t s);
+hipError_t launch_xf_swiglu(uint16_t* g, const uint16_t* u, long long n, hipStream_t s);
+hipError_t launch_xf_add(const uint16_t* a, const uint16_t* b, uint16_t* y, long long n, hipStream_t s);
+
 // a.ws: the workspace of apply_plan() for a's shape and resolved path.
 hipError_t launch_apply(const ApplyLaunch& a, hipStream_t s);
 // Targets sharing one routing (same N, k, K, rank, path and dtypes); as[0].ws holds the

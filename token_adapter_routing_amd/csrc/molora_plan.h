@@ -191,4 +191,16 @@ struct RouterBwdPlan {
 RouterBwdPlan router_bwd_plan(int N, int d, int K);
 MOLORA_HD inline int router_small_floats(int K) { return K * kRouterHidden + K + kRouterHidden; }
 
+// ---- synthetic decoder (molora_xf_forward): per forward, bf16 activations h (norm output),
+// q, k, v, attention output, o (projection output), gate and up [N][f] (the product written
+// into gate), the scores [n_seq][heads][S][S] fp32 and probabilities (bf16), the LoRA applies'
+// workspace and the GEMM library's workspace.
+constexpr int kXfHeadDim = 128;
+constexpr size_t kXfBlasBytes = size_t(64) << 20;
+struct XfPlan {
+  size_t h_off, q_off, k_off, v_off, att_off, o_off, g_off, u_off, s_off, p_off;
+  size_t lora_off, lora_bytes, blas_off, blas_bytes, total;
+};
+XfPlan xf_plan(int n_seq, int seq_len, int d, int f, size_t lora_bytes);
+
 }  // namespace molora

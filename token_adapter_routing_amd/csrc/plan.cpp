@@ -247,4 +247,31 @@ RouterBwdPlan router_bwd_plan(int N, int d, int K) {
   return p;
 }
 
+XfPlan xf_plan(int n_seq, int seq_len, int d, int f, size_t lora_bytes) {
+  XfPlan p{};
+  const size_t N = (size_t)n_seq * seq_len;
+  const size_t H = (size_t)d / kXfHeadDim;
+  const size_t nd = align256(N * d * sizeof(uint16_t)), nf = align256(N * f * sizeof(uint16_t));
+  const size_t ss = (size_t)n_seq * H * seq_len * seq_len;
+  size_t off = 0;
+  p.h_off = off; off += nd;
+  p.q_off = off; off += nd;
+  p.k_off = off; off += nd;
+  p.v_off = off; off += nd;
+  p.att_off = off; off += nd;
+  p.o_off = off; off += nd;
+  p.g_off = off; off += nf;
+  p.u_off = off; off += nf;
+  p.s_off = off; off += align256(ss * sizeof(float));
+  p.p_off = off; off += align256(ss * sizeof(uint16_t));
+  p.lora_off = off;
+  p.lora_bytes = align256(lora_bytes);
+  off += p.lora_bytes;
+  p.blas_off = off;
+  p.blas_bytes = kXfBlasBytes;
+  off += p.blas_bytes;
+  p.total = off;
+  return p;
+}
+
 }  // namespace molora
