@@ -46,6 +46,8 @@ struct GMArgs {
   int tile_rows;            // tile height bound (GMTiling::rows)
   int fixed;                // GMTiling::fixed
   float* hout;              // shrink-only mode: unscaled h of grouped position q at [q][r_pad]
+  uint16_t* hs_out;         // shrink-only mode, instead: bf16 hi / lo of wts * scale * h at
+                            // [q][2][r_pad] (the token-block expand's MFMA operand rows)
 };
 
 template <int RB>
@@ -263,7 +265,15 @@ __device__ void gm_tile(const GMArgs& a, GMLds<RB>& L, int e, int row0, int nrow
         const int rbv = row >> 4, rw = row & 15;
         const int rr = row0 + row;
         const int q = a.order != nullptr ? a.order[rr] : rr;
-        a.hout[(size_t)q * (RB * 16) + rk] = red[(rbv * 16 + rw) * kRS + rk] + red[((4 + rbv) * 16 + rw) * kRS + rk];
+        const float h = red[(rbv * 16 + rw) * kRS + rk] + red[((4 + rbv) * 16 + rw) * kRS + rk];
+        if (a.hs_out != nullptr) {
+          const float v = h * a.wts[rr] * a.scale;
+          const __bf16 hi = (__bf16)v;
+          a.hs_out[(size_t)q * (2 * RB * 16) + rk] = __builtin_bit_cast(uint16_t, hi);
+          a.hs_out[(size_t)q * (2 * RB * 16) + RB * 16 + rk] = __builtin_bit_cast(uint16_t, (__bf16)(v - (float)hi));
+        } else {
+          a.hout[(size_t)q * (RB * 16) + rk] = h;
+        }
       }
     }
     __syncthreads();  // the next sub-tile reuses the buffers

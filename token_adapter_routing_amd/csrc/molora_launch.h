@@ -46,8 +46,11 @@ struct ApplyLaunch {
 };
 
 // Per-pair shrink without gate weight or scale (64-row grouped tiles) into hout [P][r_pad] fp32.
+// hs_out != NULL: write bf16 hi / lo of perm_w * scale * h at [q][2][r_pad] instead of hout.
 hipError_t launch_pair_shrink_gm(const TargetDev& tgt, bool indirect, const uint16_t* x, const int32_t* offsets,
-                                 const int32_t* perm, int K, int k, long long P, float* hout, hipStream_t s);
+                                 const int32_t* perm, int K, int k, long long P, float* hout, hipStream_t s,
+                                 bool fixed_tiles = false, uint16_t* hs_out = nullptr,
+                                 const float* perm_w = nullptr, float scale = 1.f);
 
 // Backward of the routed LoRA except dx: dA, dB, dw (any may be NULL) from x, gy and the
 // forward routing; ws holds bwd_plan() for these shapes.

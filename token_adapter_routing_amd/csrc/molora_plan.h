@@ -106,6 +106,11 @@ bool use_gm(int k, int K, int r_pad);
 // The resolved path runs the 64-row grouped kernel: the grouped path where use_gm holds, and
 // the fixed-tiling comparator wherever its rank passes apply (k == 1 or k*K <= 64).
 bool gm_path(int path, int k, int K, int r_pad);
+// k > 1 on the 64-row grouped tiles: the token-block expand (y0 read once, y written once) from
+// k = 4 on; one pass per pair rank with an fp32 carry below (measured at K = 16, rank 64,
+// 16384 tokens: 534 / 852 us for the passes at k = 2 / 3 against 792 / 889 us; 983 against
+// 1147 us at k = 4).
+bool gm_tokblock(int k);
 // Row tiles of the 64-row grouped kernel: per segment (adapter) of a pass, ceil(count / rows)
 // tiles, balanced inside the segment (adaptive) or of exactly `rows` rows but the last (fixed).
 struct GMTiling {
@@ -127,7 +132,8 @@ RankSortPlan rank_sort_plan(long long P, int k, int K);
 // where z is the fp32 [N][d_out] carry of the k > 1 passes when y is bf16.
 struct ApplyPlan {
   int path;
-  size_t hpart_off, hpart_bytes;  // shrink partials ([nsplit][P][r_pad] fp32), two-kernel paths
+  size_t hpart_off, hpart_bytes;  // shrink partials ([nsplit][P][r_pad] fp32): two-kernel paths,
+                                  // and h of every pair for k > 1 on the 64-row grouped tiles
   size_t block_off, block_bytes;  // block path partials
   size_t sort_off;                // rank sort region (k > 1 on the grouped / skinny passes)
   RankSortPlan sort;
