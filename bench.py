@@ -211,6 +211,9 @@ def main():
 
     # ---------------- timed region (headline): exactly `steps` split steps
     ms_per_step, wall = time_steps(step)
+    consistency = {"steps_requested": args.steps, "steps_timed": K_steps, "steps_match": K_steps == args.steps,
+                   "warmup_requested": args.warmup, "warmup_run": W_steps, "warmup_match": W_steps == args.warmup,
+                   "buffer_sets": S}
     value = N / (ms_per_step * 1e-3)
 
     # ---------------- the step's kernels (split_shrink + split_expand): their time per step is the
@@ -267,6 +270,7 @@ def main():
         "step_roofline_frac": step_bytes / (ms_per_step * 1e-3) / (HBM_PEAK_GBS * 1e9),
         "step_latency_us": {"p50": p50, "p99": p99, "cv": cv, "replays": len(lat), "graph": "single step"},
         "wall_s_timed_region": wall,
+        "consistency": consistency,
         "streaming_reference": {"what": "torch.add(x, y0, out=y) on the same buffer sets: 2 reads + 1 write of "
                                         "[2048][4096] bf16 per step, one kernel, same graph timing",
                                 "us_per_step": ref_ms * 1e3,
