@@ -725,7 +725,46 @@ static void test_noalloc() {
   molora_hotset_destroy(h.hs);
 }
 
+// Work items of the dense-slot block kernels: every (target, slice) exactly once; shrink items
+// of one x group interleaved per slice; the table's capacity enforced.
+static void test_dense_items() {
+  using namespace molora;
+  CHECK(dense_block_ok(4, 16) && dense_block_ok(2, 32) && dense_block_ok(1, 64) && !dense_block_ok(5, 16) &&
+            !dense_block_ok(2, 48) && !dense_block_ok(0, 16),
+        "dense_block_ok");
+  // a transformer layer's 7 projections: q, k, v, gate, up read x; o and down their own rows
+  const int xg[7] = {0, 0, 0, 3, 0, 0, 6};
+  const int ks[7] = {4, 4, 4, 4, 4, 4, 12}, cs[7] = {4, 2, 2, 4, 12, 12, 4};
+  const DenseItems d = dense_items(7, xg, ks, cs);
+  CHECK(d.ok && d.n_s == 36 && d.n_e == 40, "dense items %d %d", d.n_s, d.n_e);
+  int seen_s[7][256] = {}, seen_e[7][256] = {};
+  for (int i = 0; i < d.n_s; ++i) ++seen_s[d.s[i] >> 8][d.s[i] & 255];
+  for (int i = 0; i < d.n_e; ++i) ++seen_e[d.e[i] >> 8][d.e[i] & 255];
+  for (int t = 0; t < 7; ++t) {
+    for (int sl = 0; sl < 256; ++sl) CHECK(seen_s[t][sl] == (sl < ks[t] ? 1 : 0), "shrink item (%d, %d)", t, sl);
+    for (int c = 0; c < 256; ++c) CHECK(seen_e[t][c] == (c < cs[t] ? 1 : 0), "expand item (%d, %d)", t, c);
+  }
+  // the x group of target 0 comes first, slice by slice: q, k, v, gate, up of slice 0, ...
+  const int first[5] = {0, 1, 2, 4, 5};
+  for (int sl = 0; sl < 4; ++sl)
+    for (int j = 0; j < 5; ++j)
+      CHECK(d.s[5 * sl + j] == ((first[j] << 8) | sl), "group order at %d: %04x", 5 * sl + j, d.s[5 * sl + j]);
+  // capacity: 8 targets of 33 slices overflow the shrink table
+  int xg8[8], ks8[8], cs8[8];
+  for (int i = 0; i < 8; ++i) {
+    xg8[i] = i;
+    ks8[i] = 33;
+    cs8[i] = 1;
+  }
+  CHECK(!dense_items(8, xg8, ks8, cs8).ok, "shrink table overflow accepted");
+  ks8[0] = 256;
+  CHECK(!dense_items(1, xg8, ks8, cs8).ok, "256 slices accepted");
+  const int bad[2] = {1, 1};
+  CHECK(!dense_items(2, bad, ks, cs).ok, "x group pointing forward accepted");
+}
+
 int main() {
+  test_dense_items();
   test_noalloc();
   test_validation();
   test_dispatch();

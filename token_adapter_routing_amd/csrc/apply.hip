@@ -1704,6 +1704,10 @@ hipError_t launch_apply(const ApplyLaunch& a, hipStream_t s) {
   }
 
   if (a.path == 4) {
+    bool taken = false;
+    const size_t off = plan.block_off;
+    err = launch_dense_block(&a, 1, &off, s, &taken);
+    if (taken || err != hipSuccess) return err;
     BlockApplyArgs ba;
     ba.b = block_args(a, wsb + plan.block_off);
     ba.offsets = a.offsets; ba.perm_w = a.perm_w; ba.inv = a.inv;
@@ -1886,6 +1890,9 @@ hipError_t launch_apply_multi(const ApplyLaunch* as, int n, hipStream_t s) {
   const MultiPlan mp = apply_multi_plan(n, d_in, d_out, a0.N, a0.k, a0.K, a0.tgt.r_pad, a0.y_f32, a0.path);
   if (a0.path == 4) {
     // 64-token blocks: one shrink launch and one expand launch for all targets
+    bool taken = false;
+    err = launch_dense_block(as, n, mp.tgt_off, s, &taken);
+    if (taken || err != hipSuccess) return err;
     static_assert(sizeof(BlockMulti) / sizeof(BlockApplyArgs) == kApplyMaxMulti, "multi size");
     BlockMulti bm;
     int gs = 1, ge = 1;

@@ -45,6 +45,12 @@ struct ApplyLaunch {
   int col_groups;    // 0 = choose
 };
 
+// Block path (64-token blocks) for small hot sets (dense_block_ok): n targets sharing one
+// routing, target i's partials at (char*)as[0].ws + ws_off[i] (block_ws_bytes each).  Sets
+// *taken = false and enqueues nothing when the hot set or the targets' slices do not fit the
+// dense kernels.
+hipError_t launch_dense_block(const ApplyLaunch* as, int n, const size_t* ws_off, hipStream_t s, bool* taken);
+
 // Per-pair shrink without gate weight or scale (64-row grouped tiles) into hout [P][r_pad] fp32.
 // hs_out != NULL: write bf16 hi / lo of perm_w * scale * h at [q][2][r_pad] instead of hout.
 hipError_t launch_pair_shrink_gm(const TargetDev& tgt, bool indirect, const uint16_t* x, const int32_t* offsets,

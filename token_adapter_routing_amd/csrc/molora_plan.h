@@ -70,6 +70,21 @@ struct BlockGeom {
 BlockGeom block_geom(int N, int k, int K, int d_in, int d_out);
 size_t block_ws_bytes(int N, int k, int K, int r_pad, int d_in);
 
+// ---- dense-slot blocks: when the 512-wide slices of all K adapters fit in LDS together
+// (K * r_pad <= 64) the block path keeps a partial for every adapter (slot = adapter index, the
+// same region size since slotmax = K) and runs from a table of (target, slice) work items:
+// shrink items grouped by the x they read (per slice, the group's targets in turn), expand
+// items per target in slice order.  An item is (target << 8) | slice.
+constexpr int kDenseMaxItems = 256;
+MOLORA_HD inline bool dense_block_ok(int K, int r_pad) { return K >= 1 && K * r_pad <= 64; }
+struct DenseItems {
+  bool ok;    // false: more items than the table holds, or a target with more than 255 slices
+  int n_s, n_e;
+  uint16_t s[kDenseMaxItems], e[kDenseMaxItems];
+};
+// x_group[i]: index of the first target that reads the same x rows as target i.
+DenseItems dense_items(int n, const int* x_group, const int* kslices, const int* cslices);
+
 // ---- split step (vocabulary routing, k = 1): partial h of every token on its own adapter,
 // [nblocks][kslices][64][r_pad] fp32; (tb, sl) starts at split_part_index.
 MOLORA_HD inline size_t split_part_index(int tb, int sl, int kslices, int r_pad) {

@@ -35,6 +35,37 @@ size_t block_ws_bytes(int N, int k, int K, int r_pad, int d_in) {
   return block_part_floats(g.nblocks, g.slotmax, g.kslices, r_pad) * sizeof(float);
 }
 
+DenseItems dense_items(int n, const int* x_group, const int* kslices, const int* cslices) {
+  DenseItems d{};
+  d.ok = n >= 1 && n <= kApplyMaxMulti;
+  for (int i = 0; i < n && d.ok; ++i)
+    if (kslices[i] < 1 || kslices[i] > 255 || cslices[i] < 1 || cslices[i] > 255 || x_group[i] < 0 ||
+        x_group[i] > i || x_group[x_group[i]] != x_group[i])
+      d.ok = false;
+  if (!d.ok) return d;
+  for (int g = 0; g < n; ++g) {
+    if (x_group[g] != g) continue;  // not the first target of its group
+    for (int sl = 0; sl < kslices[g]; ++sl)
+      for (int i = g; i < n; ++i)
+        if (x_group[i] == g && sl < kslices[i]) {
+          if (d.n_s == kDenseMaxItems) {
+            d.ok = false;
+            return d;
+          }
+          d.s[d.n_s++] = (uint16_t)((i << 8) | sl);
+        }
+  }
+  for (int i = 0; i < n; ++i)
+    for (int cs = 0; cs < cslices[i]; ++cs) {
+      if (d.n_e == kDenseMaxItems) {
+        d.ok = false;
+        return d;
+      }
+      d.e[d.n_e++] = (uint16_t)((i << 8) | cs);
+    }
+  return d;
+}
+
 StepPlan step_plan(int N, int K, int r_pad, int d_in) {
   StepPlan p{};
   p.fused_dispatch = N <= kStepMaxN;
