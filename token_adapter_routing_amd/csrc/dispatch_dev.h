@@ -261,4 +261,79 @@ __device__ void dispatch_scatter_part(DispatchLds<NT>& L, Src src, int P, int K,
   }
 }
 
+// One launch over several workgroups for few adapters (K <= kDispWideMaxK): workgroup b owns
+// the pairs [b*C, min(P, (b+1)*C)), C <= kDispMaxE * NT.  Every workgroup counts all P pairs per
+// adapter -- one ballot per adapter and wave load, no atomics -- both in total (-> offsets)
+// and before its own range (-> where its pairs of each adapter start), then scatters its range
+// stably.  Workgroup 0 writes counts and offsets.
+constexpr int kDispWideMaxK = 16;
+template <int NT, typename Src>
+__device__ void dispatch_wide_part(DispatchLds<NT>& L, Src src, int P, int K, int C, int32_t* __restrict__ counts,
+                                   int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
+                                   float* __restrict__ perm_w, int32_t* __restrict__ inv) {
+  constexpr int NW = NT / kWave;
+  static_assert(2 * NW * 64 <= kDispMaxE * NW * 64, "per-wave count table");
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int b = blockIdx.x, c0 = b * C, c1 = min(P, c0 + C);
+  int tot[kDispWideMaxK], pre[kDispWideMaxK];
+#pragma unroll
+  for (int e = 0; e < kDispWideMaxK; ++e) tot[e] = pre[e] = 0;
+  for (int s0 = 0; s0 < P; s0 += kDispMaxE * NT) {
+    int ev[kDispMaxE];
+#pragma unroll
+    for (int j = 0; j < kDispMaxE; ++j) {
+      const int p = s0 + j * NT + tid;
+      float wd;
+      ev[j] = -1;
+      if (p < P) src(p, ev[j], wd);
+    }
+#pragma unroll
+    for (int j = 0; j < kDispMaxE; ++j) {
+      const uint64_t before = __ballot(s0 + j * NT + tid < c0);
+#pragma unroll
+      for (int e = 0; e < kDispWideMaxK; ++e)
+        if (e < K) {
+          const uint64_t m = __ballot(ev[j] == e);
+          tot[e] += __popcll(m);
+          pre[e] += __popcll(m & before);
+        }
+    }
+  }
+  int mt = 0, mp = 0;
+#pragma unroll
+  for (int e = 0; e < kDispWideMaxK; ++e)
+    if (lane == e) {
+      mt = tot[e];
+      mp = pre[e];
+    }
+  L.wcnt[wave * 64 + lane] = mt;
+  L.wcnt[(NW + wave) * 64 + lane] = mp;
+  __syncthreads();
+  if (wave == 0) {
+    int c = 0, pr = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      c += L.wcnt[w * 64 + lane];
+      pr += L.wcnt[(NW + w) * 64 + lane];
+    }
+    if (lane >= K) c = pr = 0;
+    const int incl = wave_incl_scan(c, lane);
+    L.offs[lane] = incl - c;
+    L.base[lane] = pr;
+    if (b == 0) {
+      if (lane < K) {
+        counts[lane] = c;
+        offsets[lane + 1] = incl;
+      }
+      if (lane == 0) offsets[0] = 0;
+    }
+  }
+  __syncthreads();
+  const int E = min(kDispMaxE, max(1, (c1 - c0 + NT - 1) / NT));
+  int ev[kDispMaxE];
+  float wv[kDispMaxE];
+  disp_load<NT>(src, c0, c1, E, ev, wv);
+  disp_scatter<NT>(L, ev, wv, c0, c1, E, K, disp_nbits(K), perm, perm_w, inv);
+}
+
 }  // namespace molora
