@@ -547,6 +547,8 @@ def row_qwen_layer(m, torch, dev, bf, f32, reps):
     idx = torch.empty(N * k, dtype=torch.int32, device=dev)
     w = torch.empty(N * k, dtype=torch.float32, device=dev)
     flags = torch.empty(N, dtype=torch.uint8, device=dev)
+    # the router's first layer split over d (a workspace; the same bits as one launch)
+    rws = torch.empty(max(256, m.molora_route_topk_workspace(N, c.targets[0].d_in)), dtype=torch.uint8, device=dev)
     meta = (torch.empty(K, dtype=torch.int32, device=dev), torch.empty(K + 1, dtype=torch.int32, device=dev),
             torch.empty(N * k, dtype=torch.int32, device=dev), torch.empty(N * k, dtype=torch.float32, device=dev),
             torch.empty(N * k, dtype=torch.int32, device=dev))
@@ -563,7 +565,8 @@ def row_qwen_layer(m, torch, dev, bf, f32, reps):
                for ti in range(len(c.targets))]
 
         def step():
-            m.molora_route_topk(k, K, x=tx[0], W1=W1, b1=b1, W2=W2, b2=b2, logits=logits, idx=idx, w=w, flags=flags)
+            m.molora_route_topk(k, K, x=tx[0], W1=W1, b1=b1, W2=W2, b2=b2, logits=logits, idx=idx, w=w, flags=flags,
+                                ws=rws)
             m.molora_dispatch(idx, w, K, k, out=meta)
             for ti in range(len(c.targets)):
                 m.molora_apply(hs, tx[ti], y0[ti], meta[1], meta[2], meta[3], meta[4], k=k, target=ti, y=y[ti],
@@ -581,7 +584,8 @@ def row_qwen_layer(m, torch, dev, bf, f32, reps):
                           dtype=torch.uint8, device=dev)
 
         def step():
-            m.molora_route_topk(k, K, x=tx[0], W1=W1, b1=b1, W2=W2, b2=b2, logits=logits, idx=idx, w=w, flags=flags)
+            m.molora_route_topk(k, K, x=tx[0], W1=W1, b1=b1, W2=W2, b2=b2, logits=logits, idx=idx, w=w, flags=flags,
+                                ws=rws)
             m.molora_dispatch(idx, w, K, k, out=meta)
             m.molora_apply_multi(hs, tx, y0, meta[1], meta[2], meta[3], meta[4], k=k, ys=y, path=path, ws=mws)
 

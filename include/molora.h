@@ -166,12 +166,24 @@ int molora_route_vocab(const int32_t *ids, int N, const int32_t *bounds, int K,
  *     w      device fp32 [N][k] out: softmax over the k selected logits
  *     flags  device uint8 [N] out or NULL: 1 when k < K and the k-th largest
  *            logit exceeds the (k+1)-th by less than 1e-4 (a near tie)
+ *   ws       NULL, or a device workspace (256-byte aligned, no initial
+ *            contents) of molora_route_topk_workspace() bytes.  In router
+ *            mode with d <= 4096 it holds the first layer's sums over eighths
+ *            of d, computed in a launch of its own that reads W1 once per 128
+ *            tokens; the selection launch then adds them in the order the
+ *            one-launch path uses, so every output is the same bit for bit
+ *            with or without it.  Ignored in logits mode and for larger d.
+ *            Calls that share a workspace must not run concurrently.
+ *   ws_bytes its size
  * Supported: 1 <= K <= 64, 1 <= k <= min(K, 8); router mode needs
- * d a multiple of 128.
+ * d a multiple of 128.  Errors: a workspace smaller than required ->
+ * MOLORA_ENOSPC.
  * ------------------------------------------------------------------------ */
+int molora_route_topk_workspace(int N, int d, size_t *bytes);
 int molora_route_topk(const void *x, int N, int d, const void *W1, const float *b1,
                       const void *W2, const float *b2, float *logits, int K, int k,
-                      int32_t *idx, float *w, uint8_t *flags, void *stream);
+                      int32_t *idx, float *w, uint8_t *flags, void *ws, size_t ws_bytes,
+                      void *stream);
 
 /* ------------------------------------------------------------------------
  * Dispatch: histogram, offsets and grouping permutation (thelatestinai.com,

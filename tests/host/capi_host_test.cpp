@@ -123,9 +123,14 @@ hipError_t launch_route_vocab(const int32_t*, int, const VocabBounds&, int, int3
   ++g_launches;
   return hipSuccess;
 }
-hipError_t launch_route_topk(const uint16_t*, int, int, const uint16_t*, const float*, const uint16_t*, const float*,
-                             float*, int, int, int32_t*, float*, uint8_t*, hipStream_t) {
+hipError_t launch_route_topk(const uint16_t*, int N, int d, const uint16_t* W1, const float*, const uint16_t*,
+                             const float*, float*, int, int, int32_t*, float*, uint8_t*, float* part, hipStream_t) {
   ++g_launches;
+  // the split first layer writes kRouterChunks x N x 64 floats into the workspace
+  if (part != nullptr) {
+    CHECK(W1 != nullptr && router_chunked(d), "split router layer for d=%d", d);
+    write_span<float>(part, 0, (size_t)kRouterChunks * N * 64, "route part");
+  }
   return hipSuccess;
 }
 hipError_t launch_dispatch(const int32_t*, const float*, int P, int K, int32_t*, int32_t*, int32_t*, float*, int32_t*,
@@ -536,6 +541,32 @@ static void test_router_backward(int N, int d, int K) {
         "k > K accepted");
 }
 
+// molora_route_topk with a workspace: the split first layer writes only inside it, for the d
+// it covers; larger d and logits mode leave it alone; a short workspace is refused.
+static void test_route_topk_ws(int N, int d) {
+  size_t need = 1;
+  CHECK(molora_route_topk_workspace(N, d, &need) == MOLORA_OK, "route_topk_workspace N=%d d=%d", N, d);
+  CHECK(need == (molora::router_chunked(d) ? (size_t)8 * N * 64 * 4 : 0), "route_topk workspace %zu", need);
+  const size_t alloc = std::max<size_t>(need, 256);
+  if (alloc > kMaxBuf) return;
+  char* ws = static_cast<char*>(exact_alloc(alloc));
+  g_ws_base = ws;
+  g_ws_bytes = need;
+  g_ranges.clear();
+  const int l0 = g_launches;
+  int rc = molora_route_topk(fake(0x1000), N, d, fake(0x2000), nullptr, fake(0x4000), nullptr, (float*)fake(0x5000),
+                             4, 2, (int32_t*)fake(0x6000), (float*)fake(0x7000), nullptr, ws, need, nullptr);
+  CHECK(rc == MOLORA_OK && g_launches == l0 + (N > 0 ? 1 : 0), "route_topk with workspace N=%d d=%d", N, d);
+  check_disjoint("route_topk");
+  if (need > 0) {
+    rc = molora_route_topk(fake(0x1000), N, d, fake(0x2000), nullptr, fake(0x4000), nullptr, (float*)fake(0x5000), 4,
+                           2, (int32_t*)fake(0x6000), (float*)fake(0x7000), nullptr, ws, need - 1, nullptr);
+    CHECK(rc == MOLORA_ENOSPC, "short route_topk workspace accepted");
+  }
+  g_ws_base = nullptr;
+  free(ws);
+}
+
 static void test_xf(int d, int f, int L, int n_seq, int seq_len, int K, int r, int k, bool lora) {
   std::vector<HostHotset> hsv(L);
   std::vector<molora_xf_layer> layers(L);
@@ -669,7 +700,7 @@ static void test_validation() {
                            nullptr) == MOLORA_EINVAL,
         "misaligned ids");
   CHECK(molora_route_topk(nullptr, 4, 0, nullptr, nullptr, nullptr, nullptr, (float*)fake(0x1000), 4, 5,
-                          (int32_t*)fake(0x2000), (float*)fake(0x3000), nullptr, nullptr) == MOLORA_ENOTSUP,
+                          (int32_t*)fake(0x2000), (float*)fake(0x3000), nullptr, nullptr, 0, nullptr) == MOLORA_ENOTSUP,
         "k > K");
   CHECK(molora_dispatch((int32_t*)fake(0x1000), (float*)fake(0x2000), 1 << 29, 8, 4, (int32_t*)fake(0x3000),
                         (int32_t*)fake(0x4000), (int32_t*)fake(0x5000), (float*)fake(0x6000), nullptr, nullptr, 0,
@@ -765,6 +796,8 @@ static void test_dense_items() {
 
 int main() {
   test_dense_items();
+  for (int N : {0, 1, 100, 4096, 4097})
+    for (int d : {128, 640, 2048, 4096, 4224, 8192}) test_route_topk_ws(N, d);
   test_noalloc();
   test_validation();
   test_dispatch();

@@ -28,7 +28,7 @@ def lib():
 def test_every_declared_symbol_is_exported_and_bound():
     L = lib()
     names = declared_functions()
-    assert len(names) == 26, names
+    assert len(names) == 27, names
     for n in names:
         assert hasattr(L, n), n
     assert sorted(m.exported_symbols()) == names
@@ -69,10 +69,15 @@ def test_host_validation_without_launch():
     assert L.molora_route_vocab(nul, 0, ctypes.cast(ok, ctypes.c_void_p), 2, nul, nul, nul) == 0  # N=0 no-op
     assert L.molora_route_vocab(nul, 3, ctypes.cast(ok, ctypes.c_void_p), 2, nul, nul, nul) == 1  # NULL buffers
     # route_topk: k > K, k > 8, router mode with d not a multiple of 128
-    assert L.molora_route_topk(nul, 4, 0, nul, nul, nul, nul, nul, 4, 5, nul, nul, nul, nul) == 2
-    assert L.molora_route_topk(nul, 4, 0, nul, nul, nul, nul, nul, 16, 9, nul, nul, nul, nul) == 2
+    assert L.molora_route_topk(nul, 4, 0, nul, nul, nul, nul, nul, 4, 5, nul, nul, nul, nul, 0, nul) == 2
+    assert L.molora_route_topk(nul, 4, 0, nul, nul, nul, nul, nul, 16, 9, nul, nul, nul, nul, 0, nul) == 2
     assert L.molora_route_topk(nul, 4, 100, ctypes.c_void_p(256), nul, ctypes.c_void_p(256), nul, nul, 4, 2,
-                               nul, nul, nul, nul) == 2
+                               nul, nul, nul, nul, 0, nul) == 2
+    # route_topk workspace: eighths of d in fp32 per token up to d = 4096, none above
+    sz = ctypes.c_size_t(0)
+    assert L.molora_route_topk_workspace(4096, 2048, ctypes.byref(sz)) == 0 and sz.value == 8 * 4096 * 64 * 4
+    assert L.molora_route_topk_workspace(100, 8192, ctypes.byref(sz)) == 0 and sz.value == 0
+    assert L.molora_route_topk_workspace(100, 100, ctypes.byref(sz)) == 2
     # dispatch: k out of range, K out of range, N=0 no-op, NULL outputs
     assert L.molora_dispatch(nul, nul, 4, 0, 4, nul, nul, nul, nul, nul, nul, 0, nul) == 2
     assert L.molora_dispatch(nul, nul, 4, 1, 65, nul, nul, nul, nul, nul, nul, 0, nul) == 2

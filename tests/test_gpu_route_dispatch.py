@@ -101,6 +101,35 @@ def test_route_topk_router_ragged_small():
     _check_selection(host(logits), host(idx), host(w), host(flags), k)
 
 
+@pytest.mark.parametrize("N,d,K,k,bias", [(4096, 2048, 4, 2, True), (37, 256, 6, 3, True), (129, 128, 4, 1, False),
+                                          (300, 640, 8, 2, True), (1000, 4096, 16, 4, True), (64, 4224, 4, 2, True)])
+def test_route_topk_workspace_same_bits(N, d, K, k, bias):
+    """The first layer split over eighths of d (a workspace) gives the one-launch path's bits:
+    logits, idx, w and flags; d above 4096 ignores the workspace.  The workspace starts as NaN
+    bytes, so a chunk read before it is written would show.  Logits against the oracle too."""
+    m = need_gpu()
+    g = np.random.default_rng(N + d + K)
+    xb = synth.to_bf16_bits(g.standard_normal((N, d)).astype(np.float32))
+    W1 = synth.to_bf16_bits((g.standard_normal((d, 64)) / np.sqrt(d)).astype(np.float32))
+    W2 = synth.to_bf16_bits((g.standard_normal((64, K)) / 8).astype(np.float32))
+    b1 = (g.standard_normal(64) / 10).astype(np.float32) if bias else None
+    b2 = (g.standard_normal(K) / 10).astype(np.float32) if bias else None
+    args = dict(x=dev_bf16(xb), W1=dev_bf16(np.ascontiguousarray(W1.T)), b1=dev(b1) if bias else None,
+                W2=dev_bf16(np.ascontiguousarray(W2.T)), b2=dev(b2) if bias else None)
+    one = [host(t) for t in m.molora_route_topk(k, K, **args)]
+    need = m.molora_route_topk_workspace(N, d)
+    assert need == (8 * N * 64 * 4 if d <= 4096 else 0)
+    ws = torch.full((max(need, 256),), 0xFF, dtype=torch.uint8, device="cuda")
+    for _ in range(2):
+        two = [host(t) for t in m.molora_route_topk(k, K, ws=ws, **args)]
+        for a, b in zip(one, two):
+            np.testing.assert_array_equal(a, b)
+    ref = router_logits(f64(xb), f64(W1), b1.astype(np.float64) if bias else None, f64(W2),
+                        b2.astype(np.float64) if bias else None)
+    assert np.max(np.abs(two[0] - ref)) <= 1e-4
+    _check_selection(two[0], two[1], two[2], two[3], k)
+
+
 # ----------------------------------------------------------------------------- dispatch
 
 def _check_dispatch(idx_np, w_np, K, k, out):

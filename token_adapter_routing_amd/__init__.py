@@ -10,7 +10,7 @@ from .binding import (  # noqa: F401
     MOLORA_OK, MOLORA_EINVAL, MOLORA_ENOTSUP, MOLORA_ENOSPC, MOLORA_EHIP,
     molora_apply, molora_apply_multi, molora_apply_path, molora_apply_multi_workspace, molora_apply_workspace, molora_dispatch,
     molora_dispatch_workspace,
-    molora_hotset_bytes, molora_hotset_destroy, molora_hotset_init, molora_hotset_load, molora_route_topk,
+    molora_hotset_bytes, molora_hotset_destroy, molora_hotset_init, molora_hotset_load, molora_route_topk, molora_route_topk_workspace,
     molora_route_vocab, molora_seqpass_meta, molora_step_vocab, molora_step_vocab_noalloc, molora_step_workspace,
     molora_hotset_init_transposed, molora_backward, molora_backward_workspace,
     molora_route_topk_backward, molora_router_backward, molora_router_backward_workspace,

@@ -49,7 +49,9 @@ _SIGS = {
     "molora_hotset_load": (_c_i, [_c_p, _c_i, _c_i, _c_p, _c_p, _c_p]),
     "molora_hotset_destroy": (_c_i, [_c_p]),
     "molora_route_vocab": (_c_i, [_c_p, _c_i, _c_p, _c_i, _c_p, _c_p, _c_p]),
-    "molora_route_topk": (_c_i, [_c_p, _c_i, _c_i, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i, _c_i, _c_p, _c_p, _c_p, _c_p]),
+    "molora_route_topk_workspace": (_c_i, [_c_i, _c_i, _c_p]),
+    "molora_route_topk": (_c_i, [_c_p, _c_i, _c_i, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i, _c_i, _c_p, _c_p, _c_p, _c_p,
+                                 _c_sz, _c_p]),
     "molora_dispatch_workspace": (_c_i, [_c_i, _c_i, _c_i, ctypes.POINTER(_c_sz)]),
     "molora_dispatch": (_c_i, [_c_p, _c_p, _c_i, _c_i, _c_i, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_sz, _c_p]),
     "molora_apply_workspace": (_c_i, [_c_p, _c_i, _c_i, _c_i, _c_i, _c_i, ctypes.POINTER(_c_sz)]),
@@ -251,12 +253,20 @@ def molora_route_vocab(ids: torch.Tensor, bounds: Sequence[int], idx: Optional[t
     return idx, w
 
 
+def molora_route_topk_workspace(N: int, d: int) -> int:
+    out = _c_sz()
+    _check(load_library().molora_route_topk_workspace(N, d, ctypes.byref(out)))
+    return out.value
+
+
 def molora_route_topk(k: int, K: int, x: Optional[torch.Tensor] = None, W1: Optional[torch.Tensor] = None,
                       b1: Optional[torch.Tensor] = None, W2: Optional[torch.Tensor] = None,
                       b2: Optional[torch.Tensor] = None, logits: Optional[torch.Tensor] = None,
                       idx: Optional[torch.Tensor] = None, w: Optional[torch.Tensor] = None,
-                      flags: Optional[torch.Tensor] = None, want_flags: bool = True, stream=None):
-    """Router mode when W1 is given (W1 [64][d], W2 [K][64], nn.Linear layout), else logits mode."""
+                      flags: Optional[torch.Tensor] = None, want_flags: bool = True,
+                      ws: Optional[torch.Tensor] = None, stream=None):
+    """Router mode when W1 is given (W1 [64][d], W2 [K][64], nn.Linear layout), else logits mode.
+    ``ws`` (uint8, molora_route_topk_workspace bytes) selects the two-launch first layer."""
     router = W1 is not None
     if router:
         N, d = x.shape
@@ -278,7 +288,8 @@ def molora_route_topk(k: int, K: int, x: Optional[torch.Tensor] = None, W1: Opti
         _ptr(W1, torch.bfloat16, "W1") if router else None, _ptr(b1, torch.float32, "b1") if router else None,
         _ptr(W2, torch.bfloat16, "W2") if router else None, _ptr(b2, torch.float32, "b2") if router else None,
         _ptr(logits, torch.float32, "logits"), K, k, _ptr(idx, torch.int32, "idx"), _ptr(w, torch.float32, "w"),
-        _ptr(flags, torch.uint8, "flags"), _stream(stream)))
+        _ptr(flags, torch.uint8, "flags"), _ptr(ws, None, "ws") if ws is not None else None,
+        ws.numel() if ws is not None else 0, _stream(stream)))
     return logits, idx, w, flags
 
 

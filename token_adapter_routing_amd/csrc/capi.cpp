@@ -273,8 +273,17 @@ int molora_route_vocab(const int32_t* ids, int N, const int32_t* bounds, int K, 
   return e == hipSuccess ? ok() : hip_fail(e, "route_vocab launch");
 }
 
+int molora_route_topk_workspace(int N, int d, size_t* bytes) {
+  if (bytes == nullptr) return fail(MOLORA_EINVAL, "bytes is NULL");
+  if (N < 0) return fail(MOLORA_EINVAL, "N=%d < 0", N);
+  if (d <= 0 || d % 128 != 0) return fail(MOLORA_ENOTSUP, "d=%d must be a positive multiple of 128", d);
+  *bytes = molora::route_topk_ws_bytes(N, d);
+  return ok();
+}
+
 int molora_route_topk(const void* x, int N, int d, const void* W1, const float* b1, const void* W2, const float* b2,
-                      float* logits, int K, int k, int32_t* idx, float* w, uint8_t* flags, void* stream) {
+                      float* logits, int K, int k, int32_t* idx, float* w, uint8_t* flags, void* ws, size_t ws_bytes,
+                      void* stream) {
   if (N < 0) return fail(MOLORA_EINVAL, "N=%d < 0", N);
   if (K < 1 || K > MOLORA_MAX_ADAPTERS) return fail(MOLORA_ENOTSUP, "K=%d outside [1, %d]", K, MOLORA_MAX_ADAPTERS);
   if (k < 1 || k > K || k > MOLORA_MAX_TOPK) return fail(MOLORA_ENOTSUP, "k=%d outside [1, min(K, %d)]", k, MOLORA_MAX_TOPK);
@@ -287,12 +296,21 @@ int molora_route_topk(const void* x, int N, int d, const void* W1, const float* 
     if ((b1 != nullptr && !aligned(b1, 4)) || (b2 != nullptr && !aligned(b2, 4)))
       return fail(MOLORA_EINVAL, "misaligned bias");
   }
+  // the split first layer: router mode, a workspace, and d within its range
+  float* part = nullptr;
+  if (W1 != nullptr && ws != nullptr && molora::router_chunked(d)) {
+    const size_t need = molora::route_topk_ws_bytes(N, d);
+    if (ws_bytes < need) return fail(MOLORA_ENOSPC, "route_topk workspace %zu < %zu bytes", ws_bytes, need);
+    if (!aligned(ws, 256)) return fail(MOLORA_EINVAL, "workspace must be 256-byte aligned");
+    part = static_cast<float*>(ws);
+  }
   if (N == 0) return ok();
   if (logits == nullptr || idx == nullptr || w == nullptr) return fail(MOLORA_EINVAL, "logits, idx or w is NULL");
   if (!aligned(logits, 4) || !aligned(idx, 4) || !aligned(w, 4)) return fail(MOLORA_EINVAL, "misaligned pointer");
   const hipError_t e = molora::launch_route_topk(
       reinterpret_cast<const uint16_t*>(x), N, d, reinterpret_cast<const uint16_t*>(W1), b1,
-      reinterpret_cast<const uint16_t*>(W2), b2, logits, K, k, idx, w, flags, reinterpret_cast<hipStream_t>(stream));
+      reinterpret_cast<const uint16_t*>(W2), b2, logits, K, k, idx, w, flags, part,
+      reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? ok() : hip_fail(e, "route_topk launch");
 }
 

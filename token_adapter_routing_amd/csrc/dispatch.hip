@@ -10,10 +10,10 @@
 namespace molora {
 
 constexpr int kDispThreads = 1024;
-// Up to kDispChunk pairs: above kDispWideMin pairs (few adapters) one launch of a workgroup per
-// kDispWideChunk pairs, below that one workgroup.
+// Up to kDispMaxE * kDispThreads (= kDispChunk) pairs: above kDispWideMin pairs (few adapters)
+// one launch of a workgroup per kDispThreads pairs, below that one workgroup.
 constexpr int kDispWideMin = 1024;
-constexpr int kDispWideChunk = 1024;
+static_assert(kDispMaxE * kDispThreads == kDispChunk, "one load per thread and chunk covers a dispatch chunk");
 
 struct ArraySource {
   const int32_t* idx;
@@ -53,13 +53,13 @@ __global__ __launch_bounds__(kDispThreads) void dispatch_scatter(const int32_t* 
 }
 
 __global__ __launch_bounds__(kDispThreads) void dispatch_wide(const int32_t* __restrict__ idx,
-                                                              const float* __restrict__ w, int P, int K, int C,
+                                                              const float* __restrict__ w, int P, int K,
                                                               int32_t* __restrict__ counts,
                                                               int32_t* __restrict__ offsets,
                                                               int32_t* __restrict__ perm, float* __restrict__ perm_w,
                                                               int32_t* __restrict__ inv) {
   __shared__ DispatchLds<kDispThreads> L;
-  dispatch_wide_part<kDispThreads>(L, ArraySource{idx, w}, P, K, C, counts, offsets, perm, perm_w, inv);
+  dispatch_wide_part<kDispThreads>(L, ArraySource{idx, w}, P, K, counts, offsets, perm, perm_w, inv);
 }
 
 hipError_t launch_dispatch(const int32_t* idx, const float* w, int P, int K, int32_t* counts, int32_t* offsets,
@@ -74,10 +74,10 @@ hipError_t launch_dispatch(const int32_t* idx, const float* w, int P, int K, int
                        offsets, perm, perm_w, inv);
     return hipGetLastError();
   }
-  if (P > kDispWideMin && P <= kDispChunk && K <= kDispWideMaxK) {
-    // a workgroup per kDispWideChunk pairs, each counting all of them
-    const int nb = (P + kDispWideChunk - 1) / kDispWideChunk;
-    hipLaunchKernelGGL(dispatch_wide, dim3(nb), dim3(kDispThreads), 0, s, idx, w, P, K, kDispWideChunk, counts,
+  if (P > kDispWideMin && P <= kDispMaxE * kDispThreads && K <= kDispWideMaxK) {
+    // a workgroup per kDispThreads pairs, each counting all of them
+    const int nb = (P + kDispThreads - 1) / kDispThreads;
+    hipLaunchKernelGGL(dispatch_wide, dim3(nb), dim3(kDispThreads), 0, s, idx, w, P, K, counts,
                        offsets, perm, perm_w, inv);
     return hipGetLastError();
   }

@@ -16,9 +16,11 @@ struct VocabBounds {
 hipError_t launch_route_vocab(const int32_t* ids, int N, const VocabBounds& bounds, int K,
                               int32_t* idx, float* w, hipStream_t s);
 
+// part != NULL (router mode, router_chunked(d)): the first layer split over d into part,
+// route_topk_ws_bytes(N, d) bytes; the same results.
 hipError_t launch_route_topk(const uint16_t* x, int N, int d, const uint16_t* W1, const float* b1,
                              const uint16_t* W2, const float* b2, float* logits, int K, int k,
-                             int32_t* idx, float* w, uint8_t* flags, hipStream_t s);
+                             int32_t* idx, float* w, uint8_t* flags, float* part, hipStream_t s);
 
 // ws: at least dispatch_ws_bytes(P, K) bytes, or nullptr (then one workgroup sorts all pairs)
 hipError_t launch_dispatch(const int32_t* idx, const float* w, int P, int K, int32_t* counts, int32_t* offsets,

@@ -197,6 +197,18 @@ BwdPlan bwd_plan(int N, int k, int K, int r_pad, int d_in, int d_out, bool dx_f3
 // bf16 elements of one chunk's hi (or lo) plane; the lo plane follows the hi plane.
 MOLORA_HD inline size_t bwd_s_chunk_elems(int r_pad, int Qc) { return (size_t)r_pad * Qc; }
 
+// ---- router first layer split over d (molora_route_topk with a workspace): chunk c of the
+// S = d / 128 reduction steps is [S c / 8, S (c + 1) / 8); the workspace holds each chunk's
+// sum, [kRouterChunks][N][64] fp32.  Used for d <= 128 * 8 * kRouterMaxChunkSteps.
+constexpr int kRouterChunks = 8;
+constexpr int kRouterMaxChunkSteps = 4;  // d <= 4096: at most 64 KB of W1 pieces in LDS
+MOLORA_HD inline bool router_chunked(int d) {
+  return d > 0 && (d / 128 + kRouterChunks - 1) / kRouterChunks <= kRouterMaxChunkSteps;
+}
+inline size_t route_topk_ws_bytes(int N, int d) {
+  return router_chunked(d) ? (size_t)kRouterChunks * N * 64 * sizeof(float) : 0;
+}
+
 // ---- router backward (molora_router_backward), hidden width kRouterHidden: the
 // pre-activation [N][64] fp32, dL/d(pre-activation) [N][64] fp32, its hi/lo chunk planes for
 // the dW1 reduction (one segment: all tokens in order), that reduction's partials, per
