@@ -594,6 +594,20 @@ def row_qwen_layer(m, torch, dev, bf, f32, reps):
                               "pairs_per_s": N * k / (ms * 1e-3),
                               "roofline_frac": compulsory / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9)}
         del g, mws
+    # dispatch and the 7 projections in one call (the dispatch rides in the block shrink's launch)
+    fws = torch.zeros(max(1, m.molora_dispatch_apply_multi_workspace(hs, tids, N, k, m.PATH_AUTO, torch.bfloat16)),
+                      dtype=torch.uint8, device=dev)
+
+    def step():
+        m.molora_route_topk(k, K, x=tx[0], W1=W1, b1=b1, W2=W2, b2=b2, logits=logits, idx=idx, w=w, flags=flags,
+                            ws=rws)
+        m.molora_dispatch_apply_multi(hs, tx, y0, idx, w, K, k, ys=y, path=m.PATH_AUTO, meta=meta, ws=fws)
+
+    ms, g, _ = graph_ms(torch, step, reps)
+    out["paths"]["multi_fused_dispatch"] = {"ms_per_step": ms, "routed_tokens_per_s": N / (ms * 1e-3),
+                                            "pairs_per_s": N * k / (ms * 1e-3),
+                                            "roofline_frac": compulsory / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9)}
+    del g, fws
     best = min(out["paths"].items(), key=lambda kv: kv[1]["ms_per_step"])
     out["best_path"] = best[0]
     out["routed_tokens_per_s"] = best[1]["routed_tokens_per_s"]

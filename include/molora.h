@@ -296,6 +296,33 @@ int molora_apply_multi(const molora_hotset *hs, int n, const int *targets,
                        void *ws, size_t ws_bytes, void *stream);
 
 /* ------------------------------------------------------------------------
+ * Dispatch and a multi-target apply in one call (thelatestinai.com, Table 1
+ * rows "Histogram computation", "Pointer arrays" and the grouped apply;
+ * Table 10: every target of a layer follows the token's routing): equals
+ * molora_dispatch(idx, w) followed by molora_apply_multi on its outputs, bit
+ * for bit, in fewer launches.  For hot sets whose adapters' 512-wide slices
+ * fit in LDS together (K * r_pad <= 64) on the block path, with at most 8192
+ * pairs, the block shrink reads each token's adapters and weights from idx
+ * and w directly and its launch also runs the dispatch: two launches in all.
+ * Otherwise the dispatch runs first.
+ *   targets, x, y0, y0_dtype, y, y_dtype, N, k, path: as molora_apply_multi
+ *   idx, w   device int32 / fp32 [N*k]: the routing, as molora_dispatch
+ *   counts, offsets, perm, perm_w, inv: molora_dispatch's outputs (all
+ *            required here)
+ *   ws       device workspace of molora_dispatch_apply_multi_workspace()
+ *            bytes, 256-byte aligned (no initial contents needed)
+ * Errors as molora_dispatch and molora_apply_multi.
+ * ------------------------------------------------------------------------ */
+int molora_dispatch_apply_multi_workspace(const molora_hotset *hs, int n, const int *targets,
+                                          int N, int k, int y_dtype, int path, size_t *bytes);
+int molora_dispatch_apply_multi(const molora_hotset *hs, int n, const int *targets,
+                                const void *const *x, const void *const *y0, int y0_dtype,
+                                void *const *y, int y_dtype, int N, int k, const int32_t *idx,
+                                const float *w, int32_t *counts, int32_t *offsets, int32_t *perm,
+                                float *perm_w, int32_t *inv, int path, void *ws, size_t ws_bytes,
+                                void *stream);
+
+/* ------------------------------------------------------------------------
  * The whole vocabulary-routed step (thelatestinai.com, Table 1: routing
  * decision, histogram, pointer arrays and grouped dispatch; Figure 2:
  * per-token weighted sum; Table 4 "Per-token + Graph": the step in as few

@@ -272,6 +272,39 @@ hipError_t launch_apply_multi(const ApplyLaunch* as, int n, hipStream_t) {
   }
   return hipSuccess;
 }
+hipError_t launch_dense_block(const ApplyLaunch* as, int n, const size_t* ws_off, hipStream_t, bool* taken,
+                              const DenseFuse* fuse) {
+  // the device side's own conditions, then the two launches' workspace writes (partials of
+  // every adapter per block and slice for each target)
+  const ApplyLaunch& a0 = as[0];
+  *taken = false;
+  if (!dense_block_ok(a0.K, a0.tgt.r_pad) || a0.k > 4) return hipSuccess;
+  if (fuse != nullptr && ((long long)a0.N * a0.k > kDenseFuseMaxPairs || a0.K > 16)) return hipSuccess;
+  int xg[kApplyMaxMulti], ks[kApplyMaxMulti], cs[kApplyMaxMulti];
+  for (int i = 0; i < n; ++i) {
+    xg[i] = i;
+    for (int j = 0; j < i; ++j)
+      if (as[j].x == as[i].x && as[j].tgt.d_in == as[i].tgt.d_in) {
+        xg[i] = xg[j];
+        break;
+      }
+    const BlockGeom g = block_geom(as[i].N, as[i].k, as[i].K, as[i].tgt.d_in, as[i].tgt.d_out);
+    ks[i] = g.kslices;
+    cs[i] = g.cslices;
+  }
+  if (!dense_items(n, xg, ks, cs).ok) return hipSuccess;
+  *taken = true;
+  g_launches += 2;
+  g_last_apply_path = a0.path;
+  if (fuse != nullptr) CHECK(fuse->idx != nullptr && fuse->w != nullptr && fuse->inv != nullptr, "fused routing arrays");
+  for (int i = 0; i < n; ++i) {
+    const BlockGeom g = block_geom(as[i].N, as[i].k, as[i].K, as[i].tgt.d_in, as[i].tgt.d_out);
+    CHECK(g.slotmax == as[i].K, "dense partials need one slot per adapter");
+    write_span<float>(reinterpret_cast<char*>(a0.ws) + ws_off[i], 0,
+                      block_part_floats(g.nblocks, g.slotmax, g.kslices, as[i].tgt.r_pad), "dense partials");
+  }
+  return hipSuccess;
+}
 hipError_t launch_step_vocab(const StepVocabLaunch& a, hipStream_t) {
   ++g_launches;
   CHECK(a.apply.N <= kStepMaxN || !a.dispatch_share, "fused dispatch share above %d tokens (N=%d)", kStepMaxN,
@@ -660,6 +693,38 @@ static void test_multi(int K, int r, int N, int k, int path, int y_dtype) {
   }
   g_ws_base = nullptr;
   free(ws);
+  // dispatch + apply in one call: the apply's regions, then the dispatch's counts
+  size_t need2 = 0;
+  rc = molora_dispatch_apply_multi_workspace(h.hs, n, targets, N, k, y_dtype, path, &need2);
+  CHECK(rc == MOLORA_OK && need2 == align256(need) + dispatch_ws_bytes((long long)N * k, K),
+        "dispatch_apply_multi_workspace %zu", need2);
+  if (need2 <= kMaxBuf) {
+    char* ws2 = static_cast<char*>(exact_alloc(std::max<size_t>(need2, 1)));
+    g_ws_base = ws2;
+    g_ws_bytes = need2;
+    g_ranges.clear();
+    const int l0 = g_launches;
+    rc = molora_dispatch_apply_multi(h.hs, n, targets, xs, y0s, y_dtype, ys, y_dtype, N, k, (int32_t*)fake(0x7000),
+                                     (float*)fake(0x7800), (int32_t*)fake(0x8000), (int32_t*)fake(0x8800),
+                                     (int32_t*)fake(0x9000), (float*)fake(0xa000), (int32_t*)fake(0xb000), path, ws2,
+                                     need2, nullptr);
+    CHECK(rc == MOLORA_OK && g_launches == l0 + (N > 0 ? 2 : 0), "dispatch_apply_multi N=%d k=%d path=%d (%d launches)",
+          N, k, path, g_launches - l0);
+    check_disjoint("dispatch_apply_multi");
+    if (need2 > 0) {
+      rc = molora_dispatch_apply_multi(h.hs, n, targets, xs, y0s, y_dtype, ys, y_dtype, N, k, (int32_t*)fake(0x7000),
+                                       (float*)fake(0x7800), (int32_t*)fake(0x8000), (int32_t*)fake(0x8800),
+                                       (int32_t*)fake(0x9000), (float*)fake(0xa000), (int32_t*)fake(0xb000), path,
+                                       ws2, need2 - 1, nullptr);
+      CHECK(rc == MOLORA_ENOSPC, "short dispatch_apply_multi workspace accepted");
+    }
+    rc = molora_dispatch_apply_multi(h.hs, n, targets, xs, y0s, y_dtype, ys, y_dtype, N, k, (int32_t*)fake(0x7000),
+                                     (float*)fake(0x7800), (int32_t*)fake(0x8000), (int32_t*)fake(0x8800),
+                                     (int32_t*)fake(0x9000), (float*)fake(0xa000), nullptr, path, ws2, need2, nullptr);
+    CHECK(rc == MOLORA_EINVAL || N == 0, "dispatch_apply_multi without inv accepted");
+    g_ws_base = nullptr;
+    free(ws2);
+  }
   molora_hotset_destroy(h.hs);
 }
 
@@ -819,6 +884,8 @@ int main() {
     for (int k : {1, 2})
       for (int N : {1, 256, 4096})
         for (int yd : {MOLORA_BF16, MOLORA_F32}) test_multi(4, 16, N, k, path, yd);
+  test_multi(16, 16, 4096, 2, MOLORA_PATH_BLOCK, MOLORA_BF16);  // no dense kernels: dispatch, then apply
+  test_multi(4, 16, 8192, 2, MOLORA_PATH_BLOCK, MOLORA_BF16);   // 16384 pairs: dispatch, then apply
   for (int layout : {MOLORA_LAYOUT_DIRECT, MOLORA_LAYOUT_INDIRECT})
     for (int K : {1, 4, 16, 64})
       for (int r : {8, 16, 64})

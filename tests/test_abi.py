@@ -28,7 +28,7 @@ def lib():
 def test_every_declared_symbol_is_exported_and_bound():
     L = lib()
     names = declared_functions()
-    assert len(names) == 27, names
+    assert len(names) == 29, names
     for n in names:
         assert hasattr(L, n), n
     assert sorted(m.exported_symbols()) == names

@@ -114,3 +114,52 @@ def test_dense_block_deterministic_and_repeat_routing():
     np.testing.assert_array_equal(outs[0], outs[1])
     ref = _oracle(t, 1.5, e, (w1.astype(np.float64) + w2), K, 1)
     check_float_output(outs[0], ref, f64(t.y0))
+
+
+@pytest.mark.parametrize("N,K,r,k,path,layout", [
+    (4096, 4, 16, 2, 0, 0),    # the Qwen-layer shape: dispatch inside the shrink launch
+    (300, 3, 16, 2, 4, 1),
+    (1, 2, 32, 1, 4, 0),
+    (5000, 4, 16, 2, 4, 0),    # 10000 pairs: dispatch first, then the dense kernels
+    (700, 16, 16, 2, 4, 0),    # no dense kernels: dispatch, then the general block path
+    (513, 4, 16, 3, 1, 1),     # grouped path
+])
+def test_dispatch_apply_multi_equals_two_calls(N, K, r, k, path, layout):
+    """molora_dispatch_apply_multi = molora_dispatch + molora_apply_multi bit for bit (every
+    dispatch output and every y), with unrouted and out-of-range adapters, in place too;
+    and within the oracle's bars."""
+    m = need_gpu()
+    g = np.random.default_rng(N + 3 * K + r + k + path)
+    t0 = _target(g, N, 512, 640, K, r)
+    t1 = _target(g, N, 512, 384, K, r, x=t0.x)
+    t2 = _target(g, N, 1024, 512, K, r)
+    tgs = [t0, t1, t2]
+    idx, w = _routing(g, N, K, k)
+    idx[5::17] = K + 2  # outside [0, K): unrouted
+    hs = m.molora_hotset_init([(dev_bf16(t.A), dev_bf16(t.B)) for t in tgs], 1.5, layout=layout)
+    xs = [dev_bf16(t.x) for t in tgs]
+    xs[1] = xs[0]
+    y0s = [dev_bf16(t.y0) for t in tgs]
+    di, dw = dev(idx), dev(w)
+    meta2 = m.molora_dispatch(di, dw, K, k)
+    ref_ys = m.molora_apply_multi(hs, xs, y0s, meta2[1], meta2[2], meta2[3], meta2[4], k=k, path=path)
+    ws = torch.full((max(1, m.molora_dispatch_apply_multi_workspace(hs, [0, 1, 2], N, k, path, torch.bfloat16)),),
+                    0xFF, dtype=torch.uint8, device="cuda")
+    for _ in range(2):
+        ys, meta1 = m.molora_dispatch_apply_multi(hs, xs, y0s, di, dw, K, k, path=path, ws=ws)
+        torch.cuda.synchronize()
+        n_routed = int(host(meta2[1])[-1])
+        for a, b, full in zip(meta1, meta2, (True, True, False, False, True)):
+            if full:
+                np.testing.assert_array_equal(host(a), host(b))
+            else:
+                np.testing.assert_array_equal(host(a)[:n_routed], host(b)[:n_routed])
+        for a, b in zip(ys, ref_ys):
+            np.testing.assert_array_equal(host(a), host(b))
+    yin = [v.clone() for v in y0s]
+    m.molora_dispatch_apply_multi(hs, xs, yin, di, dw, K, k, ys=yin, path=path, ws=ws)
+    torch.cuda.synchronize()
+    for a, b in zip(yin, ref_ys):
+        np.testing.assert_array_equal(host(a), host(b))
+    for i, t in enumerate(tgs):
+        check_bf16_output(host(ys[i]), _oracle(t, 1.5, idx, w, K, k))

@@ -9,7 +9,7 @@ from .binding import (  # noqa: F401
     HotSet, MoloraError, exported_symbols, load_library, LIB_PATH, NOALLOC_SCRATCH_BYTES,
     MOLORA_OK, MOLORA_EINVAL, MOLORA_ENOTSUP, MOLORA_ENOSPC, MOLORA_EHIP,
     molora_apply, molora_apply_multi, molora_apply_path, molora_apply_multi_workspace, molora_apply_workspace, molora_dispatch,
-    molora_dispatch_workspace,
+    molora_dispatch_workspace, molora_dispatch_apply_multi, molora_dispatch_apply_multi_workspace,
     molora_hotset_bytes, molora_hotset_destroy, molora_hotset_init, molora_hotset_load, molora_route_topk, molora_route_topk_workspace,
     molora_route_vocab, molora_seqpass_meta, molora_step_vocab, molora_step_vocab_noalloc, molora_step_workspace,
     molora_hotset_init_transposed, molora_backward, molora_backward_workspace,

@@ -61,6 +61,11 @@ _SIGS = {
     "molora_apply_multi_workspace": (_c_i, [_c_p, _c_i, _c_p, _c_i, _c_i, _c_i, _c_i, ctypes.POINTER(_c_sz)]),
     "molora_apply_multi": (_c_i, [_c_p, _c_i, _c_p, _c_p, _c_p, _c_i, _c_p, _c_i, _c_i, _c_i,  # hs .. k
                                   _c_p, _c_p, _c_p, _c_p, _c_i, _c_p, _c_sz, _c_p]),
+    "molora_dispatch_apply_multi_workspace": (_c_i, [_c_p, _c_i, _c_p, _c_i, _c_i, _c_i, _c_i,
+                                                     ctypes.POINTER(_c_sz)]),
+    "molora_dispatch_apply_multi": (_c_i, [_c_p, _c_i, _c_p, _c_p, _c_p, _c_i, _c_p, _c_i, _c_i, _c_i,  # hs .. k
+                                           _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p,  # idx, w, counts .. inv
+                                           _c_i, _c_p, _c_sz, _c_p]),
     "molora_seqpass_meta": (_c_i, [_c_p, _c_i, _c_i, _c_p, _c_p, _c_p, _c_p]),
     "molora_step_vocab": (_c_i, [_c_p, _c_i, _c_p, _c_i, _c_p, _c_p, _c_p, _c_i, _c_p, _c_i,  # hs .. y_dtype
                                  _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p,  # idx, w, counts, offsets, perm, perm_w, inv
@@ -392,6 +397,50 @@ def molora_apply_multi(hs: HotSet, xs: Sequence[torch.Tensor], y0s: Sequence[tor
         _ptr(inv, torch.int32, "inv"), path, _ptr(ws, None, "ws") if ws is not None else None,
         ws.numel() if ws is not None else 0, _stream(stream)))
     return ys
+
+
+def molora_dispatch_apply_multi_workspace(hs: HotSet, targets: Sequence[int], N: int, k: int, path: int = PATH_AUTO,
+                                          y_dtype=torch.float32) -> int:
+    out = _c_sz()
+    tg = (ctypes.c_int * len(targets))(*targets)
+    code = F32 if y_dtype == torch.float32 else BF16
+    _check(load_library().molora_dispatch_apply_multi_workspace(hs.handle, len(targets), tg, N, k, code, path,
+                                                                ctypes.byref(out)))
+    return out.value
+
+
+def molora_dispatch_apply_multi(hs: HotSet, xs: Sequence[torch.Tensor], y0s: Sequence[torch.Tensor], idx: torch.Tensor,
+                                w: torch.Tensor, K: int, k: int = 1, targets: Optional[Sequence[int]] = None,
+                                ys: Optional[Sequence[torch.Tensor]] = None, y_dtype=None, path: int = PATH_AUTO,
+                                meta=None, ws: Optional[torch.Tensor] = None, stream=None):
+    """molora_dispatch of (idx, w) then molora_apply_multi on its outputs, in one call.
+    Returns (ys, (counts, offsets, perm, perm_w, inv)); ``meta`` may supply those five."""
+    n = len(xs)
+    targets = list(range(n)) if targets is None else list(targets)
+    N = xs[0].shape[0]
+    dev = xs[0].device
+    if ys is None:
+        ys = [torch.empty(N, hs.dims[t][1], dtype=y_dtype or y0s[i].dtype, device=dev) for i, t in enumerate(targets)]
+    if meta is None:
+        P = N * k
+        meta = (torch.empty(K, dtype=torch.int32, device=dev), torch.empty(K + 1, dtype=torch.int32, device=dev),
+                torch.empty(P, dtype=torch.int32, device=dev), torch.empty(P, dtype=torch.float32, device=dev),
+                torch.empty(P, dtype=torch.int32, device=dev))
+    counts, offsets, perm, perm_w, inv = meta
+    need = molora_dispatch_apply_multi_workspace(hs, targets, N, k, path, ys[0].dtype)
+    if need and (ws is None or ws.numel() < need):
+        ws = torch.zeros(need, dtype=torch.uint8, device=dev)
+    tg = (ctypes.c_int * n)(*targets)
+    xp = (_c_p * n)(*[_ptr(x, torch.bfloat16, "x") for x in xs])
+    y0p = (_c_p * n)(*[_ptr(v, None, "y0") for v in y0s])
+    yp = (_c_p * n)(*[_ptr(v, None, "y") for v in ys])
+    _check(load_library().molora_dispatch_apply_multi(
+        hs.handle, n, tg, xp, y0p, _dtype_code(y0s[0]), yp, _dtype_code(ys[0]), N, k,
+        _ptr(idx, torch.int32, "idx"), _ptr(w, torch.float32, "w"), _ptr(counts, torch.int32, "counts"),
+        _ptr(offsets, torch.int32, "offsets"), _ptr(perm, torch.int32, "perm"), _ptr(perm_w, torch.float32, "perm_w"),
+        _ptr(inv, torch.int32, "inv"), path, _ptr(ws, None, "ws") if ws is not None else None,
+        ws.numel() if ws is not None else 0, _stream(stream)))
+    return ys, meta
 
 
 def molora_step_workspace(hs: HotSet, target: int, N: int) -> int:

@@ -438,11 +438,11 @@ int molora_apply_multi_workspace(const molora_hotset* hs, int n, const int* targ
   return ok();
 }
 
-int molora_apply_multi(const molora_hotset* hs, int n, const int* targets, const void* const* x,
-                       const void* const* y0, int y0_dtype, void* const* y, int y_dtype, int N, int k,
-                       const int32_t* offsets, const int32_t* perm, const float* perm_w, const int32_t* inv, int path,
-                       void* ws, size_t ws_bytes, void* stream) {
-  int d_in[molora::kApplyMaxMulti], d_out[molora::kApplyMaxMulti];
+// Arguments of an n-target apply other than the routing arrays and the workspace; fills the
+// launch records (routing and workspace pointers left for the caller).  *empty: N == 0.
+static int check_multi_io(const molora_hotset* hs, int n, const int* targets, const void* const* x,
+                          const void* const* y0, int y0_dtype, void* const* y, int y_dtype, int N, int k, int path,
+                          int* d_in, int* d_out, molora::ApplyLaunch* as, bool* empty) {
   const int rc = check_multi_targets(hs, n, targets, d_in, d_out);
   if (rc != MOLORA_OK) return rc;
   if (N < 0) return fail(MOLORA_EINVAL, "N=%d < 0", N);
@@ -454,7 +454,8 @@ int molora_apply_multi(const molora_hotset* hs, int n, const int* targets, const
   if ((path == MOLORA_PATH_TILE || path == MOLORA_PATH_BLOCK) && hs->K > molora::kApplyTileMaxAdapters)
     return fail(MOLORA_ENOTSUP, "the tile and block paths support K <= %d", molora::kApplyTileMaxAdapters);
   if (x == nullptr || y0 == nullptr || y == nullptr) return fail(MOLORA_EINVAL, "x, y0 or y array is NULL");
-  if (N == 0) return ok();
+  *empty = N == 0;
+  if (N == 0) return MOLORA_OK;
   for (int i = 0; i < n; ++i) {
     if (x[i] == nullptr || y0[i] == nullptr || y[i] == nullptr) return fail(MOLORA_EINVAL, "x, y0 or y [%d] is NULL", i);
     if (!aligned(x[i], 16) || !aligned(y0[i], 16) || !aligned(y[i], 16))
@@ -463,15 +464,6 @@ int molora_apply_multi(const molora_hotset* hs, int n, const int* targets, const
     for (int j = 0; j < i; ++j)
       if (targets[j] == targets[i] || y[j] == y[i]) return fail(MOLORA_EINVAL, "targets and outputs must be distinct");
   }
-  if (offsets == nullptr || perm == nullptr || perm_w == nullptr || inv == nullptr)
-    return fail(MOLORA_EINVAL, "offsets, perm, perm_w and inv are required");
-  if (!aligned(offsets, 4) || !aligned(perm, 4) || !aligned(perm_w, 4) || !aligned(inv, 4))
-    return fail(MOLORA_EINVAL, "misaligned pointer");
-  const size_t need =
-      molora::apply_multi_plan(n, d_in, d_out, N, k, hs->K, hs->r_pad, y_dtype == MOLORA_F32, path).total;
-  if (need > 0 && (ws == nullptr || ws_bytes < need || !aligned(ws, 256)))
-    return fail(MOLORA_ENOSPC, "workspace of %zu bytes (256-byte aligned) needed, %zu given", need, ws_bytes);
-  molora::ApplyLaunch as[molora::kApplyMaxMulti];
   const int rp = molora::apply_multi_resolve_path(n, N, k, path, hs->K, hs->r_pad);
   for (int i = 0; i < n; ++i) {
     molora::ApplyLaunch& a = as[i];
@@ -487,15 +479,92 @@ int molora_apply_multi(const molora_hotset* hs, int n, const int* targets, const
     a.k = k;
     a.K = hs->K;
     a.scale = hs->scale;
-    a.offsets = offsets;
-    a.perm = perm;
-    a.perm_w = perm_w;
-    a.inv = inv;
     a.path = rp;
-    a.ws = reinterpret_cast<float*>(ws);
     a.col_groups = 0;
   }
+  return MOLORA_OK;
+}
+
+int molora_apply_multi(const molora_hotset* hs, int n, const int* targets, const void* const* x,
+                       const void* const* y0, int y0_dtype, void* const* y, int y_dtype, int N, int k,
+                       const int32_t* offsets, const int32_t* perm, const float* perm_w, const int32_t* inv, int path,
+                       void* ws, size_t ws_bytes, void* stream) {
+  int d_in[molora::kApplyMaxMulti], d_out[molora::kApplyMaxMulti];
+  molora::ApplyLaunch as[molora::kApplyMaxMulti];
+  bool empty = false;
+  const int rc = check_multi_io(hs, n, targets, x, y0, y0_dtype, y, y_dtype, N, k, path, d_in, d_out, as, &empty);
+  if (rc != MOLORA_OK || empty) return rc == MOLORA_OK ? ok() : rc;
+  if (offsets == nullptr || perm == nullptr || perm_w == nullptr || inv == nullptr)
+    return fail(MOLORA_EINVAL, "offsets, perm, perm_w and inv are required");
+  if (!aligned(offsets, 4) || !aligned(perm, 4) || !aligned(perm_w, 4) || !aligned(inv, 4))
+    return fail(MOLORA_EINVAL, "misaligned pointer");
+  const size_t need =
+      molora::apply_multi_plan(n, d_in, d_out, N, k, hs->K, hs->r_pad, y_dtype == MOLORA_F32, path).total;
+  if (need > 0 && (ws == nullptr || ws_bytes < need || !aligned(ws, 256)))
+    return fail(MOLORA_ENOSPC, "workspace of %zu bytes (256-byte aligned) needed, %zu given", need, ws_bytes);
+  for (int i = 0; i < n; ++i) {
+    as[i].offsets = offsets;
+    as[i].perm = perm;
+    as[i].perm_w = perm_w;
+    as[i].inv = inv;
+    as[i].ws = reinterpret_cast<float*>(ws);
+  }
   const hipError_t e = molora::launch_apply_multi(as, n, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ok() : hip_fail(e, "apply launch");
+}
+
+int molora_dispatch_apply_multi_workspace(const molora_hotset* hs, int n, const int* targets, int N, int k,
+                                          int y_dtype, int path, size_t* bytes) {
+  size_t apply_bytes = 0;
+  const int rc = molora_apply_multi_workspace(hs, n, targets, N, k, y_dtype, path, &apply_bytes);
+  if (rc != MOLORA_OK) return rc;
+  *bytes = molora::align256(apply_bytes) + molora::dispatch_ws_bytes((long long)N * k, hs->K);
+  return ok();
+}
+
+int molora_dispatch_apply_multi(const molora_hotset* hs, int n, const int* targets, const void* const* x,
+                                const void* const* y0, int y0_dtype, void* const* y, int y_dtype, int N, int k,
+                                const int32_t* idx, const float* w, int32_t* counts, int32_t* offsets, int32_t* perm,
+                                float* perm_w, int32_t* inv, int path, void* ws, size_t ws_bytes, void* stream) {
+  int d_in[molora::kApplyMaxMulti], d_out[molora::kApplyMaxMulti];
+  molora::ApplyLaunch as[molora::kApplyMaxMulti];
+  bool empty = false;
+  const int rc = check_multi_io(hs, n, targets, x, y0, y0_dtype, y, y_dtype, N, k, path, d_in, d_out, as, &empty);
+  if (rc != MOLORA_OK || empty) return rc == MOLORA_OK ? ok() : rc;
+  if (idx == nullptr || w == nullptr || counts == nullptr || offsets == nullptr || perm == nullptr ||
+      perm_w == nullptr || inv == nullptr)
+    return fail(MOLORA_EINVAL, "idx, w, counts, offsets, perm, perm_w and inv are required");
+  if (!aligned(idx, 4) || !aligned(w, 4) || !aligned(counts, 4) || !aligned(offsets, 4) || !aligned(perm, 4) ||
+      !aligned(perm_w, 4) || !aligned(inv, 4))
+    return fail(MOLORA_EINVAL, "misaligned pointer");
+  const long long P = (long long)N * k;
+  const molora::MultiPlan mp =
+      molora::apply_multi_plan(n, d_in, d_out, N, k, hs->K, hs->r_pad, y_dtype == MOLORA_F32, path);
+  const size_t disp_off = molora::align256(mp.total);
+  const size_t need = disp_off + molora::dispatch_ws_bytes(P, hs->K);
+  if (need > 0 && (ws == nullptr || ws_bytes < need || !aligned(ws, 256)))
+    return fail(MOLORA_ENOSPC, "workspace of %zu bytes (256-byte aligned) needed, %zu given", need, ws_bytes);
+  for (int i = 0; i < n; ++i) {
+    as[i].offsets = offsets;
+    as[i].perm = perm;
+    as[i].perm_w = perm_w;
+    as[i].inv = inv;
+    as[i].ws = reinterpret_cast<float*>(ws);
+  }
+  const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (as[0].path == MOLORA_PATH_BLOCK) {
+    // small hot sets: the dispatch rides in the block shrink's launch, which reads the routing
+    // as given
+    const molora::DenseFuse f{idx, w, counts, offsets, perm, perm_w, inv};
+    bool taken = false;
+    const hipError_t e = molora::launch_dense_block(as, n, mp.tgt_off, s, &taken, &f);
+    if (e != hipSuccess) return hip_fail(e, "dispatch + apply launch");
+    if (taken) return ok();
+  }
+  char* dws = need > disp_off ? static_cast<char*>(ws) + disp_off : nullptr;
+  hipError_t e = molora::launch_dispatch(idx, w, (int)P, hs->K, counts, offsets, perm, perm_w, inv, dws, s);
+  if (e != hipSuccess) return hip_fail(e, "dispatch launch");
+  e = molora::launch_apply_multi(as, n, s);
   return e == hipSuccess ? ok() : hip_fail(e, "apply launch");
 }
 

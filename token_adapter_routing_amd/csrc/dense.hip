@@ -28,6 +28,7 @@
 // dispatched round robin over the 8 XCDs) and the later ones find the rows in its L2.  Every
 // item of pair block pb runs on XCD pb mod 8 in both kernels, where the expand finds the
 // partials the shrink wrote.
+#include "dispatch_dev.h"
 #include "molora_launch.h"
 #include "molora_mfma.h"
 
@@ -55,12 +56,24 @@ struct DenseArgs {
   const int32_t* offsets;
   const float* perm_w;
   const int32_t* inv;
+  DenseFuse fuse;  // routing as (idx, w) and, from disp_wgs leading workgroups, the dispatch
+  int disp_wgs;
   int N, K, k;
   float scale;
   int nblocks, npairs;  // 64-token blocks, 128-token pair blocks
   int items_s, items_e;
   uint16_t item_s[kDenseMaxItems];  // shrink items: (target << 8) | d_in slice
   uint16_t item_e[kDenseMaxItems];  // expand items: (target << 8) | d_out slice
+};
+
+// (adapter, gate weight) of pair p from the routing arrays (the dispatch's source)
+struct PairSource {
+  const int32_t* idx;
+  const float* w;
+  __device__ __forceinline__ void operator()(int p, int& e, float& wv) const {
+    e = idx[p];
+    wv = w[p];
+  }
 };
 
 // s_waitcnt immediate for "at most n vector memory operations outstanding" (gfx9 encoding:
@@ -75,10 +88,25 @@ __device__ __forceinline__ void dense_lds_copy(void* dst, const void* src, int b
                                      reinterpret_cast<char*>(dst) + off, 16, 0, 0);
 }
 
-template <int RB, bool INDIRECT, int KM>
+// DIRECT: the pairs' adapters and weights come from the routing arrays (idx, w); the leading
+// a.disp_wgs workgroups run the dispatch of those pairs instead of a shrink item.
+template <int RB, bool INDIRECT, int KM, bool DIRECT>
 __global__ __launch_bounds__(kDThreads, 2) void shrink_dense(const DenseArgs a) {
   __shared__ alignas(16) uint16_t As[kDLdsElems];  // [adapter][step][chunk][u][64 lanes x 16 B]
-  const int xcd = blockIdx.x & 7, qb = blockIdx.x >> 3;
+  int bid = blockIdx.x;
+  if constexpr (DIRECT) {
+    if (bid < a.disp_wgs) {
+      const int P = a.N * a.k;
+      if (bid * kDThreads >= P) return;  // past the pairs (the count rounds up to whole XCD rounds)
+      static_assert(sizeof(DispatchLds<kDThreads>) <= sizeof(As), "dispatch tables in the shrink's LDS");
+      dispatch_wide_part<kDThreads, PairSource, 4>(*reinterpret_cast<DispatchLds<kDThreads>*>(As),
+                                                   PairSource{a.fuse.idx, a.fuse.w}, P, a.K, bid, a.fuse.counts,
+                                                   a.fuse.offsets, a.fuse.perm, a.fuse.perm_w, a.fuse.inv);
+      return;
+    }
+    bid -= a.disp_wgs;  // a multiple of 8: the XCD of every item is unchanged
+  }
+  const int xcd = bid & 7, qb = bid >> 3;
   const int pb = (qb / a.items_s) * 8 + xcd;
   if (pb >= a.npairs) return;
   const int item = a.item_s[qb % a.items_s];
@@ -98,14 +126,25 @@ __global__ __launch_bounds__(kDThreads, 2) void shrink_dense(const DenseArgs a) 
   // positions of the rows' pairs, spread over the 16 lanes of a lane group: lane n takes the
   // slots n % 4, n % 4 + 4, .. of row n / 4
   constexpr int PPL = (KM + 3) / 4;  // pairs per lane
-  int seg_start[3];
+  int seg_start[3] = {0x7fffffff, 0x7fffffff, 0x7fffffff};
+  if constexpr (!DIRECT) {
 #pragma unroll
-  for (int i = 0; i < 3; ++i) seg_start[i] = (i + 1 < K) ? a.offsets[i + 1] : 0x7fffffff;
+    for (int i = 0; i < 3; ++i) seg_start[i] = (i + 1 < K) ? a.offsets[i + 1] : 0x7fffffff;
+  }
   int qv[PPL];
+  float wd[PPL];
   {
     const long long t = min(r0 + 4 * G + (n >> 2), N - 1);
 #pragma unroll
-    for (int m = 0; m < PPL; ++m) qv[m] = a.inv[t * k + min((n & 3) + 4 * m, k - 1)];
+    for (int m = 0; m < PPL; ++m) {
+      const long long p = t * k + min((n & 3) + 4 * m, k - 1);
+      if constexpr (DIRECT) {
+        qv[m] = a.fuse.idx[p];
+        wd[m] = a.fuse.w[p];
+      } else {
+        qv[m] = a.inv[p];
+      }
+    }
   }
   __builtin_amdgcn_sched_barrier(0);
   // 2. the slice of every adapter's A, straight into LDS
@@ -130,9 +169,17 @@ __global__ __launch_bounds__(kDThreads, 2) void shrink_dense(const DenseArgs a) 
   float wv[PPL];
 #pragma unroll
   for (int m = 0; m < PPL; ++m) {
-    const int q = ((n & 3) + 4 * m < k) ? qv[m] : -1;
-    ev[m] = q < 0 ? -1 : (q >= seg_start[0]) + (q >= seg_start[1]) + (q >= seg_start[2]);
-    wv[m] = a.perm_w[max(q, 0)];  // returns behind the x rows
+    const bool slot = (n & 3) + 4 * m < k;
+    if constexpr (DIRECT) {
+      // the pair's adapter as given (outside [0, K): unrouted) and its weight, the values the
+      // dispatch copies into perm_w
+      ev[m] = (slot && qv[m] >= 0 && qv[m] < K) ? qv[m] : -1;
+      wv[m] = wd[m];
+    } else {
+      const int q = slot ? qv[m] : -1;
+      ev[m] = q < 0 ? -1 : (q >= seg_start[0]) + (q >= seg_start[1]) + (q >= seg_start[2]);
+      wv[m] = a.perm_w[max(q, 0)];  // returns behind the x rows
+    }
   }
   __syncthreads();  // every wave's A pieces are in LDS
   // gate weight of each of the lane's rows on each adapter: the sum over the row's slots (the
@@ -327,9 +374,9 @@ __global__ __launch_bounds__(kDThreads, 2) void expand_dense(const DenseArgs a) 
   if (has1) epilogue_store<Y0F32, YF32>(o1, yc1, yrows, c0 + b1 * kColBlock, n, 0xFu);
 }
 
-template <int RB, bool IND, int KM>
+template <int RB, bool IND, int KM, bool DIRECT>
 hipError_t launch_shrink_dense_t(const DenseArgs& da, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((shrink_dense<RB, IND, KM>), dim3(grid), dim3(kDThreads), 0, s, da);
+  hipLaunchKernelGGL((shrink_dense<RB, IND, KM, DIRECT>), dim3(grid), dim3(kDThreads), 0, s, da);
   return hipGetLastError();
 }
 template <int RB, bool IND, bool Y0F, bool YF>
@@ -340,12 +387,19 @@ hipError_t launch_expand_dense_t(const DenseArgs& da, int grid, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_dense_block(const ApplyLaunch* as, int n, const size_t* ws_off, hipStream_t s, bool* taken) {
+hipError_t launch_dense_block(const ApplyLaunch* as, int n, const size_t* ws_off, hipStream_t s, bool* taken,
+                              const DenseFuse* fuse) {
   const ApplyLaunch& a0 = as[0];
   *taken = false;
   // k <= K <= 4 here (a token's slots: at most four)
   if (!dense_block_ok(a0.K, a0.tgt.r_pad) || a0.k > 4) return hipSuccess;
+  const long long P = (long long)a0.N * a0.k;
+  if (fuse != nullptr && P > kDenseFuseMaxPairs) return hipSuccess;  // K <= 4 here
   DenseArgs da{};
+  if (fuse != nullptr) {
+    da.fuse = *fuse;
+    da.disp_wgs = (int)(8 * ((P + 8 * kDThreads - 1) / (8 * kDThreads)));
+  }
   da.offsets = a0.offsets;
   da.perm_w = a0.perm_w;
   da.inv = a0.inv;
@@ -386,7 +440,7 @@ hipError_t launch_dense_block(const ApplyLaunch* as, int n, const size_t* ws_off
   for (int i = 0; i < it.n_s; ++i) da.item_s[i] = it.s[i];
   for (int i = 0; i < it.n_e; ++i) da.item_e[i] = it.e[i];
   const int groups = (da.npairs + 7) / 8;
-  const int grid_s = 8 * groups * da.items_s, grid_e = 8 * groups * 2 * da.items_e;
+  const int grid_s = da.disp_wgs + 8 * groups * da.items_s, grid_e = 8 * groups * 2 * da.items_e;
   const int RBv = a0.tgt.r_pad / 16;
   hipError_t err = hipSuccess;
 #define MOLORA_DENSE_RB(...)                                  \
@@ -399,10 +453,13 @@ hipError_t launch_dense_block(const ApplyLaunch* as, int n, const size_t* ws_off
   }
 #define MOLORA_DENSE_BOOL(V, NAME, ...) \
   if (V) { constexpr bool NAME = true; __VA_ARGS__; } else { constexpr bool NAME = false; __VA_ARGS__; }
+  const bool direct = fuse != nullptr;
   if (a0.k <= 2) {
-    MOLORA_DENSE_RB(MOLORA_DENSE_BOOL(a0.indirect, IND, err = (launch_shrink_dense_t<RB, IND, 2>(da, grid_s, s))))
+    MOLORA_DENSE_RB(MOLORA_DENSE_BOOL(a0.indirect, IND, MOLORA_DENSE_BOOL(direct, DIR,
+        err = (launch_shrink_dense_t<RB, IND, 2, DIR>(da, grid_s, s)))))
   } else {
-    MOLORA_DENSE_RB(MOLORA_DENSE_BOOL(a0.indirect, IND, err = (launch_shrink_dense_t<RB, IND, 4>(da, grid_s, s))))
+    MOLORA_DENSE_RB(MOLORA_DENSE_BOOL(a0.indirect, IND, MOLORA_DENSE_BOOL(direct, DIR,
+        err = (launch_shrink_dense_t<RB, IND, 4, DIR>(da, grid_s, s)))))
   }
   if (err != hipSuccess) return err;
   MOLORA_DENSE_RB(MOLORA_DENSE_BOOL(a0.indirect, IND, MOLORA_DENSE_BOOL(a0.y0_f32, Y0F,

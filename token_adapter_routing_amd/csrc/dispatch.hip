@@ -59,7 +59,7 @@ __global__ __launch_bounds__(kDispThreads) void dispatch_wide(const int32_t* __r
                                                               int32_t* __restrict__ perm, float* __restrict__ perm_w,
                                                               int32_t* __restrict__ inv) {
   __shared__ DispatchLds<kDispThreads> L;
-  dispatch_wide_part<kDispThreads>(L, ArraySource{idx, w}, P, K, counts, offsets, perm, perm_w, inv);
+  dispatch_wide_part<kDispThreads>(L, ArraySource{idx, w}, P, K, blockIdx.x, counts, offsets, perm, perm_w, inv);
 }
 
 hipError_t launch_dispatch(const int32_t* idx, const float* w, int P, int K, int32_t* counts, int32_t* offsets,

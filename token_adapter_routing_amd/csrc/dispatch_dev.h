@@ -261,58 +261,55 @@ __device__ void dispatch_scatter_part(DispatchLds<NT>& L, Src src, int P, int K,
   }
 }
 
-// One launch over several workgroups for few adapters (K <= kDispWideMaxK) and at most
-// kDispMaxE * NT pairs: workgroup b owns the pairs [b*NT, min(P, (b+1)*NT)).  Every workgroup
-// loads all P adapters once -- thread t holds pairs j*NT + t, so its own pair is the j = b one
-// -- and counts them per adapter with one ballot per adapter and wave load (no atomics), in
-// total (-> offsets) and before its own range (-> where its pairs of each adapter start), then
-// scatters its range stably.  Workgroup 0 writes counts and offsets.
+// One launch over several workgroups for few adapters (K <= kDispWideMaxK): workgroup b of the
+// dispatch owns the pairs [b*NT, min(P, (b+1)*NT)).  Every workgroup loads all P adapters --
+// thread t holds pairs s0 + j*NT + t, so its own pair is one of them -- and counts them per
+// adapter with one ballot per adapter and wave load (no atomics), in total (-> offsets) and
+// before its own range (-> where its pairs of each adapter start), then scatters its range
+// stably.  Workgroup 0 writes counts and offsets.  Each workgroup reads every pair, so this
+// suits up to a few thousand pairs.
 constexpr int kDispWideMaxK = 16;
-template <int NT, typename Src>
-__device__ void dispatch_wide_part(DispatchLds<NT>& L, Src src, int P, int K, int32_t* __restrict__ counts,
+template <int NT, typename Src, int MAXK = kDispWideMaxK>  // MAXK: a bound on K known at compile time
+__device__ void dispatch_wide_part(DispatchLds<NT>& L, Src src, int P, int K, int b, int32_t* __restrict__ counts,
                                    int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
                                    float* __restrict__ perm_w, int32_t* __restrict__ inv) {
   constexpr int NW = NT / kWave;
   static_assert(2 * NW * 64 <= kDispMaxE * NW * 64, "per-wave count table");
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int b = blockIdx.x, c0 = b * NT, c1 = min(P, c0 + NT);
-  int tot[kDispWideMaxK], pre[kDispWideMaxK];
+  const int c0 = b * NT, c1 = min(P, c0 + NT);
+  int tot[MAXK], pre[MAXK];
 #pragma unroll
-  for (int e = 0; e < kDispWideMaxK; ++e) tot[e] = pre[e] = 0;
-  int ev[kDispMaxE];
-  float wv[kDispMaxE];
-  {
-    float wo = 0.f;
+  for (int e = 0; e < MAXK; ++e) tot[e] = pre[e] = 0;
+  int eo = -1;  // this thread's own pair c0 + tid: adapter and gate weight
+  float wo = 0.f;
+  for (int s0 = 0; s0 < P; s0 += kDispMaxE * NT) {
+    int ev[kDispMaxE];
 #pragma unroll
     for (int j = 0; j < kDispMaxE; ++j) {
-      const int p = j * NT + tid;
-      float wd;
+      const int p = s0 + j * NT + tid;
+      float wd = 0.f;
       ev[j] = -1;
       if (p < P) src(p, ev[j], wd);
-      if (j == b && p < P) wo = wd;  // the gate weight of this thread's own pair
+      if (s0 + j * NT == c0) {  // uniform: the load that holds this workgroup's range
+        eo = ev[j];
+        wo = wd;
+      }
     }
-    // this workgroup's range: pair c0 + tid is the j = b load
-    int eo = -1;
-#pragma unroll
-    for (int j = 0; j < kDispMaxE; ++j)
-      if (j == b) eo = ev[j];
 #pragma unroll
     for (int j = 0; j < kDispMaxE; ++j) {
-      const uint64_t before = __ballot(j * NT + tid < c0);
+      const uint64_t before = __ballot(s0 + j * NT + tid < c0);
 #pragma unroll
-      for (int e = 0; e < kDispWideMaxK; ++e)
+      for (int e = 0; e < MAXK; ++e)
         if (e < K) {
           const uint64_t m = __ballot(ev[j] == e);
           tot[e] += __popcll(m);
           pre[e] += __popcll(m & before);
         }
     }
-    ev[0] = eo;
-    wv[0] = wo;
   }
   int mt = 0, mp = 0;
 #pragma unroll
-  for (int e = 0; e < kDispWideMaxK; ++e)
+  for (int e = 0; e < MAXK; ++e)
     if (lane == e) {
       mt = tot[e];
       mp = pre[e];
@@ -340,6 +337,10 @@ __device__ void dispatch_wide_part(DispatchLds<NT>& L, Src src, int P, int K, in
     }
   }
   __syncthreads();
+  int ev[kDispMaxE];
+  float wv[kDispMaxE];
+  ev[0] = eo;
+  wv[0] = wo;
   disp_scatter<NT>(L, ev, wv, c0, c1, 1, K, disp_nbits(K), perm, perm_w, inv);
 }
 

@@ -51,7 +51,20 @@ struct ApplyLaunch {
 // routing, target i's partials at (char*)as[0].ws + ws_off[i] (block_ws_bytes each).  Sets
 // *taken = false and enqueues nothing when the hot set or the targets' slices do not fit the
 // dense kernels.
-hipError_t launch_dense_block(const ApplyLaunch* as, int n, const size_t* ws_off, hipStream_t s, bool* taken);
+// fuse != NULL: the routing comes as (idx, w) [N*k] (inv, perm_w and offsets unused) and the
+// shrink launch also runs the dispatch of those pairs into the given outputs (up to
+// kDenseFuseMaxPairs pairs; above that *taken = false).
+struct DenseFuse {
+  const int32_t* idx;
+  const float* w;
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* perm;
+  float* perm_w;
+  int32_t* inv;
+};
+hipError_t launch_dense_block(const ApplyLaunch* as, int n, const size_t* ws_off, hipStream_t s, bool* taken,
+                              const DenseFuse* fuse = nullptr);
 
 // Per-pair shrink without gate weight or scale (64-row grouped tiles) into hout [P][r_pad] fp32.
 // hs_out != NULL: write bf16 hi / lo of perm_w * scale * h at [q][2][r_pad] instead of hout.

@@ -76,6 +76,7 @@ size_t block_ws_bytes(int N, int k, int K, int r_pad, int d_in);
 // shrink items grouped by the x they read (per slice, the group's targets in turn), expand
 // items per target in slice order.  An item is (target << 8) | slice.
 constexpr int kDenseMaxItems = 256;
+constexpr int kDenseFuseMaxPairs = 8192;  // pairs whose dispatch rides in the dense shrink launch
 MOLORA_HD inline bool dense_block_ok(int K, int r_pad) { return K >= 1 && K * r_pad <= 64; }
 struct DenseItems {
   bool ok;    // false: more items than the table holds, or a target with more than 255 slices
