@@ -229,9 +229,11 @@ int molora_dispatch(const int32_t *idx, const float *w, int N, int k, int K,
  *   y       device [N][d_out] out, dtype y_dtype
  *   offsets, perm, perm_w, inv: the outputs of molora_dispatch for this
  *           routing (all four required)
- *   path    MOLORA_PATH_AUTO (r <= 32: for k == 1 _TILE when N >= 1024 and
- *           K <= 4, else _GROUPED; for k > 1 _TILE when K <= 16 and N*k >= 192,
- *           else _GROUPED; r > 32: _GROUPED from 1024 pairs, else _SKINNY;
+ *   path    MOLORA_PATH_AUTO (small hot sets, K * r_pad <= 64: _BLOCK from
+ *           1024 tokens at k == 1 and from 192 pairs at k > 1, else _GROUPED;
+ *           otherwise r <= 32: for k == 1 _TILE when N >= 1024 and K <= 4, else
+ *           _GROUPED; for k > 1 _TILE when K <= 16 and N*k >= 192, else
+ *           _GROUPED; r > 32: _GROUPED from 1024 pairs, else _SKINNY;
  *           molora_apply_path reports the choice),
  *           _GROUPED (MFMA tiles of grouped rows of one adapter: 16 rows for
  *           k == 1 and r <= 32; otherwise up to 64 rows, the tile height chosen
@@ -280,11 +282,12 @@ int molora_apply(const molora_hotset *hs, int target, const void *x, const void 
  *           targets[i] (y[i] distinct; y0[i] may equal y[i]); one y0_dtype
  *           and one y_dtype for all
  *   N, k, offsets, perm, perm_w, inv, path: as in molora_apply (shared);
- *           AUTO as in molora_apply, except _BLOCK instead of _TILE when
- *           k > 1 and n > 1
+ *           AUTO as in molora_apply, except that for n > 1 small hot sets
+ *           (K * r_pad <= 64) take _BLOCK from 192 pairs and _BLOCK replaces
+ *           _TILE when k > 1
  *   ws      device workspace of at least molora_apply_multi_workspace()
  *           bytes, 256-byte aligned (no initial contents needed)
- * Results equal n molora_apply calls bit for bit.  Errors as molora_apply;
+ * Results equal n molora_apply calls on the resolved path bit for bit.  Errors as molora_apply;
  * MOLORA_ENOTSUP for n outside [1, 8].
  * ------------------------------------------------------------------------ */
 int molora_apply_multi_workspace(const molora_hotset *hs, int n, const int *targets, int N,

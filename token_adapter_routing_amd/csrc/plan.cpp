@@ -89,6 +89,14 @@ int apply_resolve_path(int N, int k, int path, int K, int r_pad) {
   // adapters.  For k > 1 the tile path applies a token's pairs in one workgroup, where the
   // grouped path would carry the sum through memory between rank passes.  Ranks above 32: the
   // 64-row grouped tiles from 1024 pairs on; below that the skinny path's split reductions.
+  // Small hot sets (every adapter's 512-wide slice in LDS at once, K * r_pad <= 64): the
+  // dense-slot 64-token blocks win from 1024 tokens at k = 1 and from 192 pairs at k > 1
+  // (measured at d = 2048..6144, 256..8192 tokens, K = 2..4, r = 16 and 32: 1.1-1.8x over the
+  // tile path, which reads every adapter a tile uses whole); below that the grouped tiles.
+  if (dense_block_ok(K, r_pad)) {
+    if (k > 1) return P >= 192 ? kPathBlock : kPathGrouped;
+    return P >= 1024 ? kPathBlock : kPathGrouped;
+  }
   if (r_pad <= 32) {
     if (k > 1) return (K <= kApplyTileMaxAdapters && P >= 192) ? kPathTile : kPathGrouped;
     return (P >= 1024 && K <= 4) ? kPathTile : kPathGrouped;
@@ -97,9 +105,12 @@ int apply_resolve_path(int N, int k, int path, int K, int r_pad) {
 }
 
 // AUTO for several targets: as for one, except that tile-local applies with k > 1 become the
-// 64-token blocks, whose two launches then cover every target.
+// 64-token blocks, whose two launches then cover every target, and that small hot sets take
+// the dense-slot blocks from 192 pairs at any k (one launch per phase for all targets: 2-3.4x
+// over the grouped tiles at 256..1024 tokens, measured).
 int apply_multi_resolve_path(int n, int N, int k, int path, int K, int r_pad) {
   const int p = apply_resolve_path(N, k, path, K, r_pad);
+  if (path == kPathAuto && n > 1 && dense_block_ok(K, r_pad) && (long long)N * k >= 192) return kPathBlock;
   return (path == kPathAuto && p == kPathTile && k > 1 && n > 1) ? kPathBlock : p;
 }
 
