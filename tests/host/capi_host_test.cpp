@@ -845,6 +845,24 @@ static void test_dense_items() {
   for (int sl = 0; sl < 4; ++sl)
     for (int j = 0; j < 5; ++j)
       CHECK(d.s[5 * sl + j] == ((first[j] << 8) | sl), "group order at %d: %04x", 5 * sl + j, d.s[5 * sl + j]);
+  // columns: one x group at one slice; the kernel's decode of a workgroup number covers every
+  // (pair block group, item) once for any number of pair block groups
+  for (int i = 0; i < d.n_s; ++i) {
+    const int c0 = d.col_start[i], len = d.col_len[i];
+    CHECK(c0 <= i && i < c0 + len && c0 + len <= d.n_s, "column of item %d", i);
+    for (int j = c0; j < c0 + len; ++j)
+      CHECK((d.s[j] & 255) == (d.s[i] & 255) && xg[d.s[j] >> 8] == xg[d.s[i] >> 8], "column mixes items %d, %d", i, j);
+  }
+  for (int npg : {1, 3, 4, 7}) {
+    std::vector<int> seen((size_t)npg * d.n_s, 0);
+    for (int q = 0; q < npg * d.n_s; ++q) {
+      const int i0 = q / npg, c0 = d.col_start[i0], len = d.col_len[i0], local = q - npg * c0;
+      const int pbg = local / len, item = c0 + local % len;
+      CHECK(pbg >= 0 && pbg < npg && item >= c0 && item < c0 + len, "decode q=%d npg=%d", q, npg);
+      if (pbg >= 0 && pbg < npg) ++seen[(size_t)pbg * d.n_s + item];
+    }
+    for (int v : seen) CHECK(v == 1, "decode coverage npg=%d", npg);
+  }
   // capacity: 8 targets of 33 slices overflow the shrink table
   int xg8[8], ks8[8], cs8[8];
   for (int i = 0; i < 8; ++i) {

@@ -280,7 +280,8 @@ def test_stress_full_size(k):
 def test_qwen_layer_multi_auto_all_targets():
     """The Qwen3-1.7B-shaped layer as the bench runs it: router MLP, top-2, dispatch, then one
     molora_apply_multi over all 7 targets on AUTO (which resolves to the 64-token block path for
-    several targets with k > 1), bf16 and fp32 y; every target against the oracle."""
+    several targets with k > 1), bf16 and fp32 y; every target against the oracle.  Then the
+    row's fused line (router with a workspace, molora_dispatch_apply_multi): the same bits."""
     m = need_gpu()
     c = synth.qwen_layer()
     r = c.router
@@ -296,10 +297,25 @@ def test_qwen_layer_multi_auto_all_targets():
         m.molora_apply_multi_workspace(hs, list(range(7)), c.N, c.k, m.PATH_BLOCK, torch.bfloat16)
     y16 = m.molora_apply_multi(hs, xs, y0s, offsets, perm, perm_w, inv, k=c.k, y_dtype=torch.bfloat16)
     y32 = m.molora_apply_multi(hs, xs, y0s, offsets, perm, perm_w, inv, k=c.k, y_dtype=torch.float32)
+    # the bench row's fastest line: the router with a workspace, then dispatch and the 7 applies
+    # in one call (the dispatch inside the block shrink's launch) -- the same routing bits, the
+    # same dispatch outputs and the same y bits
+    rws = torch.empty(m.molora_route_topk_workspace(c.N, c.targets[0].d_in), dtype=torch.uint8, device="cuda")
+    l2, i2, w2, f2 = m.molora_route_topk(
+        c.k, c.K, x=xs[0], W1=dev_bf16(np.ascontiguousarray(r["W1"].T)), b1=dev(r["b1"]),
+        W2=dev_bf16(np.ascontiguousarray(r["W2"].T)), b2=dev(r["b2"]), ws=rws)
+    for a, b in ((l2, logits), (i2, idx), (w2, w), (f2, flags)):
+        np.testing.assert_array_equal(host(a), host(b))
+    yf, meta = m.molora_dispatch_apply_multi(hs, xs, y0s, i2.reshape(-1), w2.reshape(-1), c.K, c.k,
+                                             y_dtype=torch.bfloat16)
+    n_routed = int(host(offsets)[-1])
+    for a, b, full in zip(meta, (counts, offsets, perm, perm_w, inv), (True, True, False, False, True)):
+        np.testing.assert_array_equal(host(a) if full else host(a)[:n_routed], host(b) if full else host(b)[:n_routed])
     for ti, t in enumerate(c.targets):
         ref = oracle_from_gpu_routing(t, c.scale, gi, gw, c.K, c.k)
         check_bf16_output(host(y16[ti]), ref)
         check_float_output(host(y32[ti]), ref, f64(t.y0))
+        np.testing.assert_array_equal(host(yf[ti]), host(y16[ti]))
 
 
 @pytest.mark.parametrize("path", [0, 4])

@@ -23,11 +23,11 @@
 // the two give the same bits.
 //
 // Several targets run in one launch of each kernel: workgroup b works on the (target, slice)
-// item of a table in the arguments, and targets that read the same x are interleaved per
-// slice, so the shrink workgroups of one x slice run close together on one XCD (workgroups are
-// dispatched round robin over the 8 XCDs) and the later ones find the rows in its L2.  Every
-// item of pair block pb runs on XCD pb mod 8 in both kernels, where the expand finds the
-// partials the shrink wrote.
+// item of a table in the arguments.  In the shrink, the targets that read the same x form a
+// column per slice; an XCD runs the columns in turn, each over its pair blocks with the
+// column's targets back to back, so the x rows of a block and the column's A slices stay in
+// its L2 (workgroups are dispatched round robin over the 8 XCDs).  Every item of pair block pb
+// runs on XCD pb mod 8 in both kernels, where the expand finds the partials the shrink wrote.
 #include "dispatch_dev.h"
 #include "molora_launch.h"
 #include "molora_mfma.h"
@@ -63,6 +63,8 @@ struct DenseArgs {
   int nblocks, npairs;  // 64-token blocks, 128-token pair blocks
   int items_s, items_e;
   uint16_t item_s[kDenseMaxItems];  // shrink items: (target << 8) | d_in slice
+  uint16_t col_start[kDenseMaxItems];  // the shrink column (x group, slice) of each item
+  uint8_t col_len[kDenseMaxItems];
   uint16_t item_e[kDenseMaxItems];  // expand items: (target << 8) | d_out slice
 };
 
@@ -107,9 +109,15 @@ __global__ __launch_bounds__(kDThreads, 2) void shrink_dense(const DenseArgs a) 
     bid -= a.disp_wgs;  // a multiple of 8: the XCD of every item is unchanged
   }
   const int xcd = bid & 7, qb = bid >> 3;
-  const int pb = (qb / a.items_s) * 8 + xcd;
+  // an XCD takes the columns (one x group at one slice) in turn, each over its pair blocks, and
+  // a column's targets back to back: the x rows and the column's A slices stay in its L2
+  const int npg = (a.npairs + 7) / 8;
+  const int i0 = qb / npg;  // an item of this workgroup's column
+  const int cs = a.col_start[i0], len = a.col_len[i0];
+  const int local = qb - npg * cs;
+  const int pb = (local / len) * 8 + xcd;
   if (pb >= a.npairs) return;
-  const int item = a.item_s[qb % a.items_s];
+  const int item = a.item_s[cs + local % len];
   const DenseTarget& T = a.t[item >> 8];
   const int sl = item & 255;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -437,7 +445,11 @@ hipError_t launch_dense_block(const ApplyLaunch* as, int n, const size_t* ws_off
   *taken = true;
   da.items_s = it.n_s;
   da.items_e = it.n_e;
-  for (int i = 0; i < it.n_s; ++i) da.item_s[i] = it.s[i];
+  for (int i = 0; i < it.n_s; ++i) {
+    da.item_s[i] = it.s[i];
+    da.col_start[i] = it.col_start[i];
+    da.col_len[i] = it.col_len[i];
+  }
   for (int i = 0; i < it.n_e; ++i) da.item_e[i] = it.e[i];
   const int groups = (da.npairs + 7) / 8;
   const int grid_s = da.disp_wgs + 8 * groups * da.items_s, grid_e = 8 * groups * 2 * da.items_e;

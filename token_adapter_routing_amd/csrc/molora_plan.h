@@ -82,6 +82,10 @@ struct DenseItems {
   bool ok;    // false: more items than the table holds, or a target with more than 255 slices
   int n_s, n_e;
   uint16_t s[kDenseMaxItems], e[kDenseMaxItems];
+  // shrink columns: the items of one x group at one slice, s[col_start[i] .. + col_len[i])
+  // for every item i of the column
+  uint16_t col_start[kDenseMaxItems];
+  uint8_t col_len[kDenseMaxItems];
 };
 // x_group[i]: index of the first target that reads the same x rows as target i.
 DenseItems dense_items(int n, const int* x_group, const int* kslices, const int* cslices);

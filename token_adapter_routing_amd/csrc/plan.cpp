@@ -45,7 +45,8 @@ DenseItems dense_items(int n, const int* x_group, const int* kslices, const int*
   if (!d.ok) return d;
   for (int g = 0; g < n; ++g) {
     if (x_group[g] != g) continue;  // not the first target of its group
-    for (int sl = 0; sl < kslices[g]; ++sl)
+    for (int sl = 0; sl < kslices[g]; ++sl) {
+      const int c0 = d.n_s;
       for (int i = g; i < n; ++i)
         if (x_group[i] == g && sl < kslices[i]) {
           if (d.n_s == kDenseMaxItems) {
@@ -54,6 +55,11 @@ DenseItems dense_items(int n, const int* x_group, const int* kslices, const int*
           }
           d.s[d.n_s++] = (uint16_t)((i << 8) | sl);
         }
+      for (int i = c0; i < d.n_s; ++i) {
+        d.col_start[i] = (uint16_t)c0;
+        d.col_len[i] = (uint8_t)(d.n_s - c0);
+      }
+    }
   }
   for (int i = 0; i < n; ++i)
     for (int cs = 0; cs < cslices[i]; ++cs) {
