@@ -10,12 +10,16 @@
 //                 waves takes one 16-token row block through every step of the slice and every
 //                 adapter, then scales each row's partial by that token's gate weight on the
 //                 adapter (the sum of its slots' weights there, 0 if it does not use it) and
-//                 stores the partials [block][adapter][slice][64][r_pad] fp32.
+//                 stores one partial plane per adapter, [block][plane][slice][64][r_pad] fp32 --
+//                 or, when a token has fewer slots than there are adapters (k < K), one plane
+//                 per slot holding its adapter's partial (a slot that repeats an earlier slot's
+//                 adapter holds 0).
 //                 The routing (grouped position -> adapter from the offsets, gate weight from
 //                 perm_w) returns while the x rows are in flight.
 //   expand_dense  workgroup = 64 tokens x one 512-wide d_out slice of one target.  The B^T
-//                 slices of all K adapters (straight into LDS), the partials and the y0 rows
-//                 are requested at once, in that order (loads return in issue order), so h
+//                 slices of all K adapters (straight into LDS), the slots' adapters (per-slot
+//                 planes), the partials and the y0 rows are requested at once, in that order
+//                 (loads return in issue order), so h
 //                 (alpha/r x the slice sum, split into bf16 hi / lo) and the MFMAs run while
 //                 the y0 rows are still arriving; y = y0 + sum_e h_e B_e.
 // With one slot per token of weight 1 (vocabulary routing) every rounding step is the split
@@ -58,6 +62,7 @@ struct DenseArgs {
   const int32_t* inv;
   DenseFuse fuse;  // routing as (idx, w) and, from disp_wgs leading workgroups, the dispatch
   int disp_wgs;
+  int per_slot;    // k < K: one partial plane per routed slot (else one per adapter)
   int N, K, k;
   float scale;
   int nblocks, npairs;  // 64-token blocks, 128-token pair blocks
@@ -239,6 +244,39 @@ __global__ __launch_bounds__(kDThreads, 2) void shrink_dense(const DenseArgs a) 
   if (tb >= a.nblocks) return;  // second half of an odd last pair: no such block (wave-uniform)
   const int rowb = r0 % kBTok;
   fold_weights();
+  if (a.per_slot) {
+    // one plane per routed slot s: the partial of the slot's adapter times the token's weight
+    // on it; a slot repeating an earlier slot's adapter stores 0 (the earlier one holds the sum)
+    static_assert(PPL == 1, "a row's slots sit in four lanes");
+    int es[4][4];  // [row i][slot s]: lane 4i + s of the group holds the pair
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) es[i][t] = __shfl(ev[0], 16 * G + 4 * i + t, kWave);
+#pragma unroll
+    for (int t = 0; t < KM; ++t) {
+      if (t < k) {
+        float* dst = T.part + block_part_index(tb, t, sl, K, T.kslices, r_pad) + (size_t)(rowb + 4 * G) * r_pad + n;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int e = es[i][t];
+          bool first = e >= 0;
+#pragma unroll
+          for (int t2 = 0; t2 < KM; ++t2)
+            if (t2 < t) first = first && es[i][t2] != e;
+#pragma unroll
+          for (int u = 0; u < RB; ++u) {
+            float v = 0.f;
+#pragma unroll
+            for (int ee = 0; ee < 4 / RB; ++ee)
+              if (first && ee == e) v = (acc[0][ee][u][i] + acc[1][ee][u][i]) * wt[ee][i];
+            dst[(size_t)i * r_pad + 16 * u] = v;
+          }
+        }
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int e = 0; e < 4 / RB; ++e) {
     if (e < K) {
@@ -281,13 +319,43 @@ __global__ __launch_bounds__(kDThreads, 2) void expand_dense(const DenseArgs a) 
   const int b0 = min(2 * ch, nb - 1), b1 = min(2 * ch + 1, nb - 1);
   const bool has0 = 2 * ch < nb, has1 = 2 * ch + 1 < nb;
 
+  const bool per_slot = a.per_slot != 0;
+  if (per_slot) {
+    // h rows of the adapters a token does not use stay 0
+    for (int i = threadIdx.x; i < (int)(sizeof(hb) / 16); i += kDThreads)
+      reinterpret_cast<u32x4_t*>(hb)[i] = u32x4_t{0u, 0u, 0u, 0u};
+    __syncthreads();
+  }
   // 1. every adapter's B^T rows of the slice, straight into LDS
   for (int e = 0; e < K; ++e)
     dense_lds_copy(Bs + e * kBSlice * RP, adapter_B<INDIRECT>(T.tgt, e) + (size_t)c0 * RP, (c1 - c0) * RP * 2, wave,
                    lane);
   __builtin_amdgcn_sched_barrier(0);
-  // 2. the partials: thread item v = (adapter, token, rank quad), its first KS slices
-  const int nq = K * kBTok * RQ;
+  // per-slot planes: the adapter of every slot of each item's token (grouped position -> adapter
+  // by the offsets, or the routing as given)
+  const int kk = a.k;
+  const int nplanes = per_slot ? kk : K;
+  int rq_[QPT][4];
+  int seg_start[3] = {0x7fffffff, 0x7fffffff, 0x7fffffff};
+  if (per_slot) {
+    if (a.fuse.idx == nullptr) {
+#pragma unroll
+      for (int i = 0; i < 3; ++i) seg_start[i] = (i + 1 < K) ? a.offsets[i + 1] : 0x7fffffff;
+    }
+#pragma unroll
+    for (int j = 0; j < QPT; ++j) {
+      const int v = min(j * kDThreads + (int)threadIdx.x, nplanes * kBTok * RQ - 1);
+      const long long t = min(t0 + (v / RQ) % kBTok, N - 1);
+#pragma unroll
+      for (int s2 = 0; s2 < 4; ++s2) {
+        const long long pp = t * kk + min(s2, kk - 1);
+        rq_[j][s2] = a.fuse.idx != nullptr ? a.fuse.idx[pp] : a.inv[pp];
+      }
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  // 2. the partials: thread item v = (plane, token, rank quad), its first KS slices
+  const int nq = nplanes * kBTok * RQ;
   const float* pbase = T.part + block_part_index(tb, 0, 0, K, T.kslices, RP);
   const size_t slice_f = (size_t)kBTok * RP, adapter_f = (size_t)T.kslices * slice_f;
   u32x4_t pv[QPT][KS];
@@ -320,14 +388,33 @@ __global__ __launch_bounds__(kDThreads, 2) void expand_dense(const DenseArgs a) 
   for (int j = 0; j < QPT; ++j) {
     const int v = j * kDThreads + (int)threadIdx.x;
     if (v < nq) {
-      const int e = v / (kBTok * RQ), tok = (v / RQ) % kBTok, rk = 4 * (v % RQ);
+      const int plane = v / (kBTok * RQ), tok = (v / RQ) % kBTok, rk = 4 * (v % RQ);
+      // the adapter whose h row this plane fills: the plane itself, or the slot's adapter
+      // (nothing for an unrouted slot or one that repeats an earlier slot's adapter)
+      int e = plane;
+      if (per_slot) {
+        int es[4];
+#pragma unroll
+        for (int s2 = 0; s2 < 4; ++s2) {
+          const int q = rq_[j][s2];
+          if (a.fuse.idx != nullptr) es[s2] = (s2 < kk && q >= 0 && q < K) ? q : -1;
+          else es[s2] = (s2 < kk && q >= 0) ? (q >= seg_start[0]) + (q >= seg_start[1]) + (q >= seg_start[2]) : -1;
+        }
+        e = -1;
+#pragma unroll
+        for (int s2 = 0; s2 < 4; ++s2)
+          if (s2 == plane) e = es[s2];
+#pragma unroll
+        for (int s2 = 0; s2 < 4; ++s2)
+          if (s2 < plane && es[s2] == e) e = -1;
+      }
       float sum[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < KS; ++s)
         if (s < T.kslices)
 #pragma unroll
           for (int c = 0; c < 4; ++c) sum[c] += __uint_as_float(pv[j][s][c]);
-      const float* src = pbase + (size_t)e * adapter_f + (size_t)4 * (v % (kBTok * RQ));
+      const float* src = pbase + (size_t)plane * adapter_f + (size_t)4 * (v % (kBTok * RQ));
       for (int s = KS; s < T.kslices; ++s) {
         const u32x4_t pw = ld16(src + (size_t)s * slice_f);
 #pragma unroll
@@ -341,10 +428,12 @@ __global__ __launch_bounds__(kDThreads, 2) void expand_dense(const DenseArgs a) 
         hi[c] = __builtin_bit_cast(uint16_t, h);
         lo[c] = __builtin_bit_cast(uint16_t, (__bf16)(hv - (float)h));
       }
-      uint16_t* hp = hb + ((size_t)(e * 2) * kBTok + tok) * RP + rk;
-      *reinterpret_cast<uint2*>(hp) = make_uint2(hi[0] | ((uint32_t)hi[1] << 16), hi[2] | ((uint32_t)hi[3] << 16));
-      *reinterpret_cast<uint2*>(hp + kBTok * RP) =
-          make_uint2(lo[0] | ((uint32_t)lo[1] << 16), lo[2] | ((uint32_t)lo[3] << 16));
+      if (e >= 0) {
+        uint16_t* hp = hb + ((size_t)(e * 2) * kBTok + tok) * RP + rk;
+        *reinterpret_cast<uint2*>(hp) = make_uint2(hi[0] | ((uint32_t)hi[1] << 16), hi[2] | ((uint32_t)hi[3] << 16));
+        *reinterpret_cast<uint2*>(hp + kBTok * RP) =
+            make_uint2(lo[0] | ((uint32_t)lo[1] << 16), lo[2] | ((uint32_t)lo[3] << 16));
+      }
     }
   }
   __syncthreads();  // h and every wave's B pieces are in LDS
@@ -416,6 +505,7 @@ hipError_t launch_dense_block(const ApplyLaunch* as, int n, const size_t* ws_off
   da.k = a0.k;
   da.scale = a0.scale;
   da.nblocks = (a0.N + kBTok - 1) / kBTok;
+  da.per_slot = a0.k < a0.K;
   da.npairs = (a0.N + kDTok - 1) / kDTok;
   int kslices[kApplyMaxMulti], cslices[kApplyMaxMulti];
   for (int i = 0; i < n; ++i) {
