@@ -203,9 +203,11 @@ int molora_route_topk(const void *x, int N, int d, const void *W1, const float *
  *           -1 for an unrouted pair
  *   ws      device workspace of at least molora_dispatch_workspace() bytes
  *           (may be NULL when that size is 0; no initial contents needed).
- *           Up to 8192 pairs one workgroup sorts them (size 0); above that
- *           the sort runs as two launches over up to 128 workgroups and the
- *           workspace holds their per-adapter counts (4*K bytes each).
+ *           Up to 8192 pairs one launch sorts them (size 0): one workgroup, or
+ *           above 4096 pairs with K <= 16 a workgroup per 1024 pairs, each
+ *           counting all pairs; above 8192 the sort runs as two launches over
+ *           up to 128 workgroups and the workspace holds their per-adapter
+ *           counts (4*K bytes each).
  *           Calls that share a workspace must not run concurrently.
  * Supported: 1 <= K <= 64, 1 <= k <= 8, N*k < 2^31.
  * ------------------------------------------------------------------------ */
@@ -230,7 +232,7 @@ int molora_dispatch(const int32_t *idx, const float *w, int N, int k, int K,
  *   offsets, perm, perm_w, inv: the outputs of molora_dispatch for this
  *           routing (all four required)
  *   path    MOLORA_PATH_AUTO (small hot sets, K * r_pad <= 64: _BLOCK from
- *           1024 tokens at k == 1 and from 192 pairs at k > 1, else _GROUPED;
+ *           192 pairs at k > 1, else _GROUPED; at k == 1 _BLOCK from 4096 tokens;
  *           otherwise r <= 32: for k == 1 _TILE when N >= 1024 and K <= 4, else
  *           _GROUPED; for k > 1 _TILE when K <= 16 and N*k >= 192, else
  *           _GROUPED; r > 32: _GROUPED from 1024 pairs, else _SKINNY;

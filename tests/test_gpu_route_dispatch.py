@@ -147,7 +147,7 @@ def _check_dispatch(idx_np, w_np, K, k, out):
                                    (333, 3, 7), (2048, 1, 64), (5000, 8, 64), (16384, 4, 16), (16384, 1, 16),
                                    (40000, 2, 2), (8192, 1, 3), (8193, 1, 3), (1048579, 1, 64),
                                    (2049, 1, 4), (1025, 2, 64), (3000, 2, 5), (1365, 6, 16), (1537, 1, 16),
-                                   (2730, 3, 11), (1024, 1, 4)])
+                                   (2730, 3, 11), (1024, 1, 4), (4097, 1, 16), (2731, 3, 9)])
 def test_dispatch_random(N, k, K):
     m = need_gpu()
     g = np.random.default_rng(N + k * 7 + K)

@@ -96,12 +96,13 @@ int apply_resolve_path(int N, int k, int path, int K, int r_pad) {
   // grouped path would carry the sum through memory between rank passes.  Ranks above 32: the
   // 64-row grouped tiles from 1024 pairs on; below that the skinny path's split reductions.
   // Small hot sets (every adapter's 512-wide slice in LDS at once, K * r_pad <= 64): the
-  // dense-slot 64-token blocks win from 1024 tokens at k = 1 and from 192 pairs at k > 1
-  // (measured at d = 2048..6144, 256..8192 tokens, K = 2..4, r = 16 and 32: 1.1-1.8x over the
-  // tile path, which reads every adapter a tile uses whole); below that the grouped tiles.
+  // dense-slot 64-token blocks from 192 pairs at k > 1 and from 4096 tokens at k = 1 (measured
+  // at d = 2048..6144, 256..8192 tokens, K = 2..4, r = 16 and 32: 1.1-1.5x over the tile path,
+  // which reads every adapter a tile uses whole).  Below 4096 tokens at k = 1 their shrink has
+  // fewer workgroups than the chip has CUs and loses to the tile path with cold inputs.
   if (dense_block_ok(K, r_pad)) {
     if (k > 1) return P >= 192 ? kPathBlock : kPathGrouped;
-    return P >= 1024 ? kPathBlock : kPathGrouped;
+    if (N >= 4096) return kPathBlock;
   }
   if (r_pad <= 32) {
     if (k > 1) return (K <= kApplyTileMaxAdapters && P >= 192) ? kPathTile : kPathGrouped;
