@@ -100,13 +100,25 @@ static void apply_writes(const ApplyLaunch& a) {
   }
   if (a.path == kPathTile || (a.path == kPathGrouped && a.k == 1)) return;  // no workspace
   if (gm_path(a.path, a.k, a.K, a.tgt.r_pad)) {
-    if (a.k == 1) return;  // one pass, no workspace
+    // a pass's slice partials (every tile of the bound, every 512-wide d_in slice) and h rows
+    auto gs_writes = [&](long long rows) {
+      const GSRegion g = gs_region(a.path, rows, a.K, a.tgt.r_pad, a.tgt.d_in);
+      CHECK(g.nwg == p.gs.nwg && g.total == p.gs.total, "split pass region");
+      const long long kslices = (a.tgt.d_in + kBSlice - 1) / kBSlice;
+      write_span<float>(ws + p.gs_off, 0, (size_t)g.nwg * kslices * 64 * a.tgt.r_pad, "gs partials");
+      write_span<uint16_t>(ws + p.gs_off + g.hb_off, 0, (size_t)g.nwg * 2 * 64 * a.tgt.r_pad, "gs h rows");
+    };
+    if (a.k == 1) {
+      gs_writes(P);
+      return;
+    }
     if (gm_tokblock(a.k)) {
       write_span<uint16_t>(ws + p.hpart_off, 0, (size_t)P * 2 * a.tgt.r_pad, "pair h");  // shrink-only tiles
       return;
     }
     rank_sort_writes(ws + p.sort_off, P, a.k, a.K);
     if (!a.y_f32) write_span<float>(ws + p.z_off, 0, (size_t)a.N * a.tgt.d_out, "z");
+    gs_writes(a.N);
     return;
   }
   const int ns = a.path == kPathSkinny ? skinny_splits(a.tgt.d_in) : 1;

@@ -17,7 +17,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmolora.so")
-SOURCES = ["capi.cpp", "plan.cpp", "route.hip", "dispatch.hip", "apply.hip", "dense.hip", "backward.hip", "xf.hip", "xfmr.cpp"]
+SOURCES = ["capi.cpp", "plan.cpp", "route.hip", "dispatch.hip", "apply.hip", "dense.hip", "gsplit.hip", "backward.hip", "xf.hip", "xfmr.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

@@ -17,11 +17,15 @@
 //                      [BLOCK] 64-token blocks in two launches (block_dev.h): partial shrinks
 //                      per 512-wide d_in slice into the workspace, then expands per 512-wide
 //                      column slice; step_shrink_block / step_expand_block route from the ids.
-//   apply_gm           [GROUPED, rank > 32 or k > 1] equal row ranges of the grouped order in
-//                      64-row sub-tiles (gm_dev.h); k > 1: slot_sort (or slot_hist +
-//                      slot_scatter) orders the pairs by (rank among the token's pairs,
-//                      adapter), one pass per rank carries the sum in fp32, finish_tokens
-//                      writes the tokens the last pass does not reach.
+//   gs_shrink, gs_finalize, gs_expand
+//                      [GROUPED, rank > 32 or k > 1] one pass over the 64-row tiles of the
+//                      grouped order (gm_dev.h tiling) in three launches split over 512-wide
+//                      slices (gsplit.hip); k = 2, 3: slot_sort (or slot_hist + slot_scatter)
+//                      orders the pairs by (rank among the token's pairs, adapter), one pass
+//                      per rank: within a pass every token has at most one row, so no two
+//                      workgroups write one row; the passes carry the sum in fp32 and
+//                      finish_tokens writes the tokens the last pass does not reach; k >= 4:
+//                      pair_shrink_gm + expand_tokblock below.
 //   apply_fused_k1     [GROUPED, k = 1, rank <= 32] 16 grouped rows of one adapter (gathered
 //                      through perm) and a slice of output columns; shrink and expand fused.
 //   shrink_grouped     [SKINNY, GROUPED k > 1 with k*K > 64] the grouped shrink into an fp32
@@ -782,16 +786,6 @@ __global__ __launch_bounds__(kSThreads) void split_expand(StepArgs a, SplitGeom 
   if (has1) epilogue_store<Y0F32, YF32>(o1, yc1, yrows, c0 + b1 * kColBlock, n, 0xFu);
 }
 
-// --------------------------------------------------------------------------------------
-// Grouped 64-row tiles (gm_dev.h).  k > 1 runs as k passes, one per slot, chained through y
-// (y = y0 + slot 0's deltas, then y += slot 1's, ...): within a pass every token has at most one
-// row, so no two workgroups write one row, and the sum order is fixed.  The per-slot grouped
-// orders come from one stable counting sort of the grouped positions by (slot, adapter).
-template <int RB, bool INDIRECT, bool Y0F32, bool YF32>
-__global__ __launch_bounds__(kGMThreads) void apply_gm(GMArgs a) {
-  __shared__ GMLds<RB> L;
-  gm_range<RB, INDIRECT, Y0F32, YF32>(a, L);
-}
 // --------------------------------------------------------------------------------------
 // k > 1 on the grouped order: the shrink-only 64-row tiles write w * alpha/r * h of every pair
 // as bf16 hi / lo rows (Hs, by grouped position); then a workgroup owns 64 consecutive tokens
@@ -1589,11 +1583,6 @@ static hipError_t launch_t8_t(const T8ApplyArgs& ta, int grid, hipStream_t s) {
   hipLaunchKernelGGL((apply_t8<RB, IND, Y0F, YF>), dim3(grid), dim3(kT8Threads), 0, s, ta);
   return hipGetLastError();
 }
-template <int RB, bool IND, bool Y0F, bool YF>
-static hipError_t launch_gm_t(const GMArgs& ga, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((apply_gm<RB, IND, Y0F, YF>), dim3(grid), dim3(kGMThreads), 0, s, ga);
-  return hipGetLastError();
-}
 template <bool Y0F, bool YF>
 static hipError_t launch_finish_t(const void* y0, const float* z, void* y, const int32_t* inv, int N, int k,
                                   int d_out, bool copy_y0, bool copy_z, hipStream_t s) {
@@ -1721,26 +1710,21 @@ hipError_t launch_apply(const ApplyLaunch& a, hipStream_t s) {
     const bool in_place = (a.y0 == a.y);
     GMArgs ga{};
     ga.tgt = a.tgt; ga.x = a.x; ga.N = a.N; ga.k = a.k; ga.scale = a.scale; ga.perm = a.perm; ga.nkeys = a.K;
-    // row tiles per segment (a multiple of 8 workgroups for the XCD mapping); column slices
-    // while there are fewer than 256 workgroups
+    // row tiles per segment, each run as one workgroup per 512-wide slice (the tiling of the
+    // plan's grouped-split region)
     const long long rows_max = a.k == 1 ? P : a.N;  // rows of one pass
-    const GMTiling tl = gm_tiling(a.path, rows_max, a.K);
-    const long long nwg = (tl.max_tiles + 7) / 8 * 8;
-    const int nblk = a.tgt.d_out / kColBlock;
-    int cg = 1;
-    while (nwg * cg < 256 && nblk % (2 * cg) == 0 && nblk / (2 * cg) >= 2) cg *= 2;
-    ga.col_groups = cg;
-    ga.nwg = (int)nwg;
+    const GMTiling tl = gm_tiling(a.path, rows_max, a.K, (a.tgt.d_in + kBSlice - 1) / kBSlice);
+    ga.col_groups = 1;
     ga.tile_rows = tl.rows;
     ga.fixed = tl.fixed;
-    const int grid = (int)nwg * cg;
+    // a pass = three launches over 512-wide slices of the tiles (gsplit.hip)
+    float* gs_part = reinterpret_cast<float*>(wsb + plan.gs_off);
+    uint16_t* gs_hb = reinterpret_cast<uint16_t*>(wsb + plan.gs_off + plan.gs.hb_off);
     auto pass = [&](const void* src, bool src_f32, void* dst, bool dst_f32) {
       ga.y0 = src;
       ga.y = dst;
-      hipError_t e = hipSuccess;
-      MOLORA_DISPATCH_RB(RBv, MOLORA_DISPATCH_BOOL(a.indirect, IND, MOLORA_DISPATCH_BOOL(src_f32, Y0F,
-          MOLORA_DISPATCH_BOOL(dst_f32, YF, e = (launch_gm_t<RB, IND, Y0F, YF>(ga, grid, s))))));
-      return e;
+      ga.nwg = plan.gs.nwg;
+      return launch_gs_pass(ga, gs_part, gs_hb, src_f32, dst_f32, a.indirect, s);
     };
     if (a.k == 1) {
       ga.key0 = 0; ga.offsets = a.offsets; ga.order = nullptr; ga.wts = a.perm_w;
@@ -2054,7 +2038,7 @@ hipError_t launch_pair_shrink_gm(const TargetDev& tgt, bool indirect, const uint
   GMArgs ga{};
   ga.tgt = tgt; ga.x = x; ga.k = k; ga.perm = perm; ga.offsets = offsets; ga.key0 = 0; ga.nkeys = K;
   ga.order = nullptr; ga.wts = perm_w; ga.scale = scale; ga.hout = hout; ga.hs_out = hs_out;
-  const GMTiling tl = gm_tiling(fixed_tiles ? kPathGroupedFixed : kPathGrouped, P, K);
+  const GMTiling tl = gm_tiling(fixed_tiles ? kPathGroupedFixed : kPathGrouped, P, K, 1);
   ga.tile_rows = tl.rows; ga.fixed = tl.fixed; ga.col_groups = 1;
   ga.nwg = (int)((tl.max_tiles + 7) / 8 * 8);
   const int RBv = tgt.r_pad / 16;

@@ -333,24 +333,20 @@ __device__ void gm_tile(const GMArgs& a, GMLds<RB>& L, int e, int row0, int nrow
 // cut into nt = ceil(c / tile_rows) tiles: balanced (tile i: rows c*i/nt .. c*(i+1)/nt) or,
 // fixed, tile_rows rows each but the last; the tiles are numbered segment by segment, so
 // consecutive tiles (which run on one XCD) mostly share their adapter in its L2.
-template <int RB, bool INDIRECT, bool Y0F32, bool YF32, bool SHRINK_ONLY = false>
-__device__ void gm_range(const GMArgs& a, GMLds<RB>& L) {
+// Tile w of the pass (every lane of the wave calls it): its adapter e and rows [r0, r1);
+// false past the pass's tiles (the same answer in every wave).
+__device__ __forceinline__ bool gm_locate(const GMArgs& a, int w, int& e, int& r0, int& r1) {
   const int lane = threadIdx.x & 63;
-  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-  const int per_xcd = a.nwg >> 3;
-  const int g = slot % a.col_groups;
-  const int w = xcd * per_xcd + slot / a.col_groups;
   const int M = a.tile_rows;
   const int s0l = lane < a.nkeys ? a.offsets[a.key0 + lane] : 0;
   const int cl = lane < a.nkeys ? a.offsets[a.key0 + lane + 1] - s0l : 0;
   const int ntl = (cl + M - 1) / M;
   const int incl = wave_incl_scan(ntl, lane);
   const uint64_t m = __ballot(lane < a.nkeys && w >= incl - ntl && w < incl);
-  if (m == 0) return;  // past the pass's tiles (the same answer in every wave)
-  const int e = __builtin_ctzll(m);
+  if (m == 0) return false;
+  e = __builtin_ctzll(m);
   const int s0 = __shfl(s0l, e, kWave), c = __shfl(cl, e, kWave), nt = __shfl(ntl, e, kWave);
   const int i = w - (__shfl(incl, e, kWave) - nt);
-  int r0, r1;
   if (a.fixed) {
     r0 = s0 + i * M;
     r1 = min(s0 + c, r0 + M);
@@ -358,6 +354,17 @@ __device__ void gm_range(const GMArgs& a, GMLds<RB>& L) {
     r0 = s0 + (int)((long long)c * i / nt);
     r1 = s0 + (int)((long long)c * (i + 1) / nt);
   }
+  return true;
+}
+
+template <int RB, bool INDIRECT, bool Y0F32, bool YF32, bool SHRINK_ONLY = false>
+__device__ void gm_range(const GMArgs& a, GMLds<RB>& L) {
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const int per_xcd = a.nwg >> 3;
+  const int g = slot % a.col_groups;
+  const int w = xcd * per_xcd + slot / a.col_groups;
+  int e, r0, r1;
+  if (!gm_locate(a, w, e, r0, r1)) return;
   const int cols = a.tgt.d_out / a.col_groups;
   gm_tile<RB, INDIRECT, Y0F32, YF32, SHRINK_ONLY>(a, L, e, r0, r1 - r0, g * cols, cols);
 }

@@ -1,0 +1,300 @@
+// Grouped tiles split over 512-wide slices (MoLoRA pages, thelatestinai.com: Figure 2 right,
+// tokens grouped by their selected adapter and one grouped GEMM per adapter; Table 10 shapes,
+// adapters up to rank 64).
+//
+// One pass over a grouped order (the tiles of gm_locate: each adapter segment cut into tiles of
+// at most 64 rows) in three launches, so that a workgroup's loads are one slice of the tile
+// instead of the whole of d_in and d_out:
+//   gs_shrink    (tile, d_in slice of 512): the tile's x rows over the slice against the
+//                adapter's A slice (straight into LDS); the two halves of the slice meet in
+//                LDS and the partial x A of the 64 rows goes to part[tile][slice] (fp32).
+//   gs_finalize  (tile): h = (sum of the slices in order) x gate weight x alpha/r per row, as
+//                bf16 hi / lo rows hb[tile] -- the expand's MFMA A operand.
+//   gs_expand    (tile, d_out slice of 512): the adapter's B^T slice (straight into LDS, in the
+//                XOR placement of the 64-row tiles, so the operand reads are conflict-free), the
+//                h rows and the tile's y0 rows are requested at once; y = y0 + h B for the rows
+//                of the tile (token rows; within a pass a token has at most one row).
+// Every launch numbers the tiles the same way: tile w runs on XCD w / (nwg / 8), with the
+// tiles of one adapter mostly on one XCD, whose L2 then holds the adapter's slices and the
+// tile's partials and h rows.
+#include "gm_dev.h"
+#include "molora_launch.h"
+
+namespace molora {
+
+namespace {
+
+constexpr int kGSThreads = 512;
+constexpr int kGSSteps = kBSlice / kStepK;  // 4
+
+struct GSArgs {
+  GMArgs g;        // the pass: tiles, rows, routing, adapters, x, y0 / y, scale
+  float* part;     // [nwg][kslices][64][r_pad] fp32
+  uint16_t* hb;    // [nwg][2][64][r_pad] bf16 hi / lo of the weighted h
+  int kslices, cslices;
+};
+
+constexpr int gs_vmcnt(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+// Tile and slice of workgroup b, for `slices` slices per tile (grid nwg * slices).
+__device__ __forceinline__ void gs_tile_slice(const GMArgs& g, int slices, int& w, int& sl) {
+  const int xcd = blockIdx.x & 7, q = blockIdx.x >> 3;
+  w = xcd * (g.nwg >> 3) + q / slices;
+  sl = q % slices;
+}
+
+// Token of row rl of tile rows [r0, r0 + nrows) (rows past the end repeat the first).
+__device__ __forceinline__ int gs_token(const GMArgs& g, int r0, int nrows, int rl) {
+  const int rr = r0 + (rl < nrows ? rl : 0);
+  const int q = g.order != nullptr ? g.order[rr] : rr;
+  return g.perm[q] / g.k;
+}
+
+template <int RB, bool INDIRECT>
+__global__ __launch_bounds__(kGSThreads, 2) void gs_shrink(const GSArgs a) {
+  __shared__ alignas(16) uint16_t As[kGSSteps * 4 * RB * 512];  // [step][chunk][u] pieces of 1 KB
+  int w, sl, e, r0, r1;
+  gs_tile_slice(a.g, a.kslices, w, sl);
+  if (!gm_locate(a.g, w, e, r0, r1)) return;
+  const int nrows = r1 - r0;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n = lane & 15, G = lane >> 4, rb = wave & 3, kh = wave >> 2;
+  const int d_in = a.g.tgt.d_in, r_pad = a.g.tgt.r_pad;
+  const int S = d_in / kStepK;
+  const int s0 = sl * kGSSteps, s1 = min(s0 + kGSSteps, S), ns = s1 - s0;
+  constexpr int piece = RB * 16 * kStepK;  // elements of one step's pieces
+  // the x row of the lane's MFMA row (16 rb + n): its token first (the HBM stream waits on it)
+  const int tok = gs_token(a.g, r0, nrows, 16 * rb + n);
+  const uint16_t* xp = a.g.x + (size_t)tok * d_in + 8 * G;
+  __builtin_amdgcn_sched_barrier(0);
+  // the adapter's A slice straight into LDS
+  {
+    const char* src = reinterpret_cast<const char*>(adapter_A<INDIRECT>(a.g.tgt, e) + (size_t)s0 * piece);
+    char* dst = reinterpret_cast<char*>(As);
+    for (int off = wave * 1024; off < ns * piece * 2; off += 8 * 1024)
+      __builtin_amdgcn_global_load_lds(src + off + 16 * lane, dst + off, 16, 0, 0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  // this wave's half of the slice (2 steps) of the x row
+  const int w0 = min(s0 + 2 * kh, s1), w1 = min(w0 + 2, s1);
+  u32x4_t xv[2][4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int st = max(min(w0 + i, w1 - 1), s0);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) xv[i][c] = ld16_nt(xp + (size_t)st * kStepK + 32 * c);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(gs_vmcnt(8));  // this wave's A pieces have landed (only x is younger)
+  __syncthreads();
+  f32x4_t acc[RB];
+#pragma unroll
+  for (int u = 0; u < RB; ++u) acc[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    if (w0 + i < w1) {
+      const uint16_t* ap = As + (size_t)(w0 + i - s0) * piece;
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int u = 0; u < RB; ++u) {
+          // lane (n, G) takes its 16 bytes at position 4n + G of the 1 KB piece (slab swizzle)
+          const u32x4_t av = *reinterpret_cast<const u32x4_t*>(ap + ((c * RB + u) * 64 + 4 * n + G) * 8);
+          acc[u] = mfma16x16x32(as_bf16x8(xv[i][c]), as_bf16x8(av), acc[u]);
+        }
+    }
+  }
+  // the halves meet in LDS (the A pieces' bytes); half 0 stores the sums
+  __syncthreads();
+  constexpr int kRS = RB * 16 + 4;
+  float* red = reinterpret_cast<float*>(As);
+  static_assert(sizeof(float) * 4 * 16 * kRS <= sizeof(As), "partial sums fit in the A pieces' LDS");
+  if (kh == 1) {
+#pragma unroll
+    for (int u = 0; u < RB; ++u)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) red[(rb * 16 + 4 * G + i) * kRS + u * 16 + n] = acc[u][i];
+  }
+  __syncthreads();
+  if (kh == 0) {
+    float* dst = a.part + (((size_t)w * a.kslices + sl) * kGMRows + 16 * rb) * r_pad;
+#pragma unroll
+    for (int u = 0; u < RB; ++u)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        dst[(size_t)(4 * G + i) * r_pad + u * 16 + n] = acc[u][i] + red[(rb * 16 + 4 * G + i) * kRS + u * 16 + n];
+  }
+}
+
+template <int RB>
+__global__ __launch_bounds__(kGSThreads) void gs_finalize(const GSArgs a) {
+  constexpr int RP = RB * 16, RQ = RP / 4;
+  constexpr int QPT = (kGMRows * RQ + kGSThreads - 1) / kGSThreads;  // 16-byte quads per thread
+  constexpr int KS = 8;                                               // slices requested together
+  int w, sl, e, r0, r1;
+  gs_tile_slice(a.g, 1, w, sl);
+  if (!gm_locate(a.g, w, e, r0, r1)) return;
+  const int nrows = r1 - r0;
+  const float* base = a.part + (size_t)w * a.kslices * kGMRows * RP;
+  uint16_t* hb = a.hb + (size_t)w * 2 * kGMRows * RP;
+#pragma unroll
+  for (int j = 0; j < QPT; ++j) {
+    const int v = j * kGSThreads + (int)threadIdx.x;
+    if (v >= kGMRows * RQ) break;
+    const int row = v / RQ, rk = 4 * (v % RQ);
+    const float wt = row < nrows ? a.g.wts[r0 + row] * a.g.scale : 0.f;
+    const float* src = base + (size_t)row * RP + rk;
+    float sum[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < a.kslices; s0 += KS) {
+      u32x4_t pv[KS];
+#pragma unroll
+      for (int s = 0; s < KS; ++s)
+        if (s0 + s < a.kslices) pv[s] = ld16(src + (size_t)(s0 + s) * kGMRows * RP);
+#pragma unroll
+      for (int s = 0; s < KS; ++s)
+        if (s0 + s < a.kslices)
+#pragma unroll
+          for (int c = 0; c < 4; ++c) sum[c] += __uint_as_float(pv[s][c]);
+    }
+    uint32_t hi2[2], lo2[2];
+#pragma unroll
+    for (int c = 0; c < 4; c += 2) {
+      float hv[2], lv[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        hv[t] = sum[c + t] * wt;
+        lv[t] = hv[t] - (float)(__bf16)hv[t];
+      }
+      hi2[c / 2] = pack_bf16x2(hv[0], hv[1]);
+      lo2[c / 2] = pack_bf16x2(lv[0], lv[1]);
+    }
+    *reinterpret_cast<uint2*>(hb + (size_t)row * RP + rk) = make_uint2(hi2[0], hi2[1]);
+    *reinterpret_cast<uint2*>(hb + (size_t)(kGMRows + row) * RP + rk) = make_uint2(lo2[0], lo2[1]);
+  }
+}
+
+template <int RB, bool INDIRECT, bool Y0F32, bool YF32>
+__global__ __launch_bounds__(kGSThreads, 2) void gs_expand(const GSArgs a) {
+  constexpr int RP = RB * 16, SPR = 2 * RB;  // 16-byte slots per B^T row
+  constexpr size_t y0b = Y0F32 ? 4 : 2, yb = YF32 ? 4 : 2;
+  constexpr int NY0 = Y0F32 ? 16 : 8;
+  __shared__ alignas(16) uint16_t Bs[kBSlice * RP];  // B^T rows of the slice, XOR-placed slots
+  int w, cs, e, r0, r1;
+  gs_tile_slice(a.g, a.cslices, w, cs);
+  if (!gm_locate(a.g, w, e, r0, r1)) return;
+  const int nrows = r1 - r0;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n = lane & 15, G = lane >> 4, rb = wave & 3, ch = wave >> 2;
+  const int d_out = a.g.tgt.d_out;
+  const int c0 = cs * kBSlice, c1 = min(c0 + kBSlice, d_out);
+  const int nb = (c1 - c0) / kColBlock;
+  const int b0 = min(2 * ch, nb - 1), b1 = min(2 * ch + 1, nb - 1);
+  const bool has0 = 2 * ch < nb, has1 = 2 * ch + 1 < nb;
+  // 0. the tokens of the lane's rows 4G + i of its row block (rows past the tile repeat its
+  //    first and are not stored): first, since the y0 stream waits on them
+  const int tokl = gs_token(a.g, r0, nrows, 16 * rb + n);
+  const char* y0rows[4];
+  char* yrows[4];
+  unsigned vmask = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int t = __shfl(tokl, 4 * G + i, kWave);
+    y0rows[i] = reinterpret_cast<const char*>(a.g.y0) + (size_t)t * d_out * y0b;
+    yrows[i] = reinterpret_cast<char*>(a.g.y) + (size_t)t * d_out * yb;
+    vmask |= (16 * rb + 4 * G + i < nrows ? 1u : 0u) << i;
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  // 1. the B^T slice: LDS slot P (row P / SPR, slot P % SPR) holds the row's slot P % SPR XOR
+  //    gm_b_swz(row), so lane l of a 1 KB piece fetches the source slot that belongs at l
+  {
+    const char* src = reinterpret_cast<const char*>(adapter_B<INDIRECT>(a.g.tgt, e) + (size_t)c0 * RP);
+    char* dst = reinterpret_cast<char*>(Bs);
+    const int npieces = (c1 - c0) * SPR / 64;
+    for (int p = wave; p < npieces; p += 8) {
+      const int P = 64 * p + lane, row = P / SPR, slot = (P % SPR) ^ gm_b_swz<RB>(row);
+      __builtin_amdgcn_global_load_lds(src + ((size_t)row * SPR + slot) * 16, dst + (size_t)p * 1024, 16, 0, 0);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  // 2. the A operand: h rows of the tile (groups 0, 1 hi of ranks 16u + 8(G & 1) .., 2, 3 lo)
+  u32x4_t hv[RB];
+  {
+    const uint16_t* hrow = a.hb + ((size_t)w * 2 * kGMRows + (size_t)(G >> 1) * kGMRows + 16 * rb + n) * RP;
+#pragma unroll
+    for (int u = 0; u < RB; ++u) hv[u] = ld16(hrow + u * 16 + 8 * (G & 1));
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  // 3. the y0 rows
+  RowChunk<Y0F32> yc0, yc1;
+  load_row_chunk<Y0F32>(yc0, y0rows, c0 + b0 * kColBlock, n);
+  load_row_chunk<Y0F32>(yc1, y0rows, c0 + b1 * kColBlock, n);
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(gs_vmcnt(NY0));  // B pieces and h rows have landed (y0 may not)
+  __syncthreads();
+  f32x4_t o0[8], o1[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    o0[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    o1[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+  // lane's B^T slots: row 16j + n of the block, slot 2u + (G & 1), XOR-placed
+  int b_sl[RB];
+#pragma unroll
+  for (int u = 0; u < RB; ++u) b_sl[u] = (2 * u + (G & 1)) ^ gm_b_swz<RB>(n);
+  const uint16_t* bl0 = Bs + (size_t)(b0 * kColBlock + n) * RP;
+  const uint16_t* bl1 = Bs + (size_t)(b1 * kColBlock + n) * RP;
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+#pragma unroll
+    for (int u = 0; u < RB; ++u) {
+      const u32x4_t v0 = *reinterpret_cast<const u32x4_t*>(bl0 + (size_t)16 * j * RP + 8 * b_sl[u]);
+      const u32x4_t v1 = *reinterpret_cast<const u32x4_t*>(bl1 + (size_t)16 * j * RP + 8 * b_sl[u]);
+      o0[j] = mfma16x16x32(as_bf16x8(hv[u]), as_bf16x8(v0), o0[j]);
+      o1[j] = mfma16x16x32(as_bf16x8(hv[u]), as_bf16x8(v1), o1[j]);
+    }
+  if (has0) epilogue_store<Y0F32, YF32>(o0, yc0, yrows, c0 + b0 * kColBlock, n, vmask);
+  if (has1) epilogue_store<Y0F32, YF32>(o1, yc1, yrows, c0 + b1 * kColBlock, n, vmask);
+}
+
+}  // namespace
+
+hipError_t launch_gs_pass(const GMArgs& g, float* part, uint16_t* hb, bool y0_f32, bool y_f32, bool indirect,
+                          hipStream_t s) {
+  GSArgs a{};
+  a.g = g;
+  a.part = part;
+  a.hb = hb;
+  a.kslices = (g.tgt.d_in + kBSlice - 1) / kBSlice;
+  a.cslices = (g.tgt.d_out + kBSlice - 1) / kBSlice;
+  const int RBv = g.tgt.r_pad / 16;
+  hipError_t err = hipSuccess;
+#define MOLORA_GS_RB(...)                                 \
+  switch (RBv) {                                          \
+    case 1: { constexpr int RB = 1; __VA_ARGS__; } break; \
+    case 2: { constexpr int RB = 2; __VA_ARGS__; } break; \
+    case 3: { constexpr int RB = 3; __VA_ARGS__; } break; \
+    case 4: { constexpr int RB = 4; __VA_ARGS__; } break; \
+    default: return hipErrorInvalidValue;                 \
+  }
+#define MOLORA_GS_BOOL(V, NAME, ...) \
+  if (V) { constexpr bool NAME = true; __VA_ARGS__; } else { constexpr bool NAME = false; __VA_ARGS__; }
+  MOLORA_GS_RB(MOLORA_GS_BOOL(indirect, IND, {
+    hipLaunchKernelGGL((gs_shrink<RB, IND>), dim3(g.nwg * a.kslices), dim3(kGSThreads), 0, s, a);
+    err = hipGetLastError();
+  }))
+  if (err != hipSuccess) return err;
+  MOLORA_GS_RB({
+    hipLaunchKernelGGL((gs_finalize<RB>), dim3(g.nwg), dim3(kGSThreads), 0, s, a);
+    err = hipGetLastError();
+  })
+  if (err != hipSuccess) return err;
+  MOLORA_GS_RB(MOLORA_GS_BOOL(indirect, IND, MOLORA_GS_BOOL(y0_f32, Y0F, MOLORA_GS_BOOL(y_f32, YF, {
+    hipLaunchKernelGGL((gs_expand<RB, IND, Y0F, YF>), dim3(g.nwg * a.cslices), dim3(kGSThreads), 0, s, a);
+    err = hipGetLastError();
+  }))))
+#undef MOLORA_GS_RB
+#undef MOLORA_GS_BOOL
+  return err;
+}
+
+}  // namespace molora

@@ -138,7 +138,8 @@ struct GMTiling {
   int fixed;     // 1: fixed 64-row tiles per segment
   long long max_tiles;  // upper bound on the tiles of a pass: ceil(rows_of_pass / rows) + keys
 };
-GMTiling gm_tiling(int path, long long rows_of_pass, int nkeys);
+// slices: workgroups per tile (the d_in slices of a split pass; 1 for one workgroup per tile).
+GMTiling gm_tiling(int path, long long rows_of_pass, int nkeys, int slices);
 
 // Rank sort of k > 1 (grouped and skinny paths): counts2 [k*K] and offsets2 [k*K+1] in a
 // 256-byte-aligned head, then perm2 [P] int32 and w2 [P] fp32, then the chip-wide sort's
@@ -150,6 +151,15 @@ RankSortPlan rank_sort_plan(long long P, int k, int K);
 
 // Workspace of one molora_apply on a resolved path: [skinny/grouped h partials][rank sort][z],
 // where z is the fp32 [N][d_out] carry of the k > 1 passes when y is bf16.
+// ---- grouped tiles split over 512-wide slices (a pass of the 64-row grouped tiles in three
+// launches): the pass's slice partials [nwg][kslices][64][r_pad] fp32, then its h rows
+// [nwg][2][64][r_pad] bf16; nwg = the pass's tile bound rounded up to whole XCD rounds.
+struct GSRegion {
+  int nwg;
+  size_t part_bytes, hb_off, total;
+};
+GSRegion gs_region(int path, long long rows_of_pass, int K, int r_pad, int d_in);
+
 struct ApplyPlan {
   int path;
   size_t hpart_off, hpart_bytes;  // shrink partials ([nsplit][P][r_pad] fp32): two-kernel paths,
@@ -158,6 +168,8 @@ struct ApplyPlan {
   size_t sort_off;                // rank sort region (k > 1 on the grouped / skinny passes)
   RankSortPlan sort;
   size_t z_off, z_bytes;          // fp32 carry
+  size_t gs_off;                  // 64-row grouped passes: the slice partials and h rows
+  GSRegion gs;
   size_t total;
 };
 ApplyPlan apply_plan(int N, int k, int K, int r_pad, int d_in, int d_out, bool y_f32, int path);

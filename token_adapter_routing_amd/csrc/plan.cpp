@@ -137,17 +137,18 @@ bool gm_path(int path, int k, int K, int r_pad) {
   return path == kPathGroupedFixed && (k == 1 || k * K <= 64);
 }
 
-// Adaptive: the tile height bound aims at 256 tiles over the pass (one round on the chip),
-// between 16 and 64 rows; every segment is then cut into ceil(count / rows) tiles of equal
-// height, so no tile spans two adapters and a small segment gets one short tile.  Fixed: 64-row
-// tiles per segment whatever its size (the fixed-tiling comparator).
-GMTiling gm_tiling(int path, long long rows_of_pass, int nkeys) {
+// Adaptive: the tile height bound aims at 256 workgroups over the pass (one round on the chip)
+// when each tile runs as `slices` workgroups, between 16 and 64 rows; every segment is then cut
+// into ceil(count / rows) tiles of equal height, so no tile spans two adapters and a small
+// segment gets one short tile.  Fixed: 64-row tiles per segment whatever its size (the
+// fixed-tiling comparator).
+GMTiling gm_tiling(int path, long long rows_of_pass, int nkeys, int slices) {
   GMTiling t{};
   t.fixed = path == kPathGroupedFixed ? 1 : 0;
   if (t.fixed) {
     t.rows = 64;
   } else {
-    const long long per = (rows_of_pass + 255) / 256;
+    const long long per = (rows_of_pass * std::max(1, slices) + 255) / 256;
     t.rows = (int)std::min<long long>(64, std::max<long long>(16, (per + 15) / 16 * 16));
   }
   t.max_tiles = (rows_of_pass + t.rows - 1) / t.rows + nkeys;
@@ -166,6 +167,17 @@ RankSortPlan rank_sort_plan(long long P, int k, int K) {
   return s;
 }
 
+GSRegion gs_region(int path, long long rows_of_pass, int K, int r_pad, int d_in) {
+  GSRegion g{};
+  const int kslices = (d_in + kBSlice - 1) / kBSlice;
+  const GMTiling tl = gm_tiling(path, rows_of_pass, K, kslices);
+  g.nwg = (int)((tl.max_tiles + 7) / 8 * 8);
+  g.part_bytes = (size_t)g.nwg * kslices * 64 * r_pad * sizeof(float);
+  g.hb_off = align256(g.part_bytes);
+  g.total = g.hb_off + (size_t)g.nwg * 2 * 64 * r_pad * sizeof(uint16_t);
+  return g;
+}
+
 ApplyPlan apply_plan(int N, int k, int K, int r_pad, int d_in, int d_out, bool y_f32, int path) {
   ApplyPlan a{};
   a.path = apply_resolve_path(N, k, path, K, r_pad);
@@ -177,7 +189,12 @@ ApplyPlan apply_plan(int N, int k, int K, int r_pad, int d_in, int d_out, bool y
     return a;
   }
   if (gm_path(a.path, k, K, r_pad)) {
-    if (k == 1) return a;
+    if (k == 1) {  // one pass over the grouped order
+      a.gs_off = 0;
+      a.gs = gs_region(a.path, P, K, r_pad, d_in);
+      a.total = a.gs.total;
+      return a;
+    }
     if (gm_tokblock(k)) {
       // w * scale * h of every pair as bf16 hi / lo [P][2][r_pad] for the token-block expand
       a.hpart_off = 0;
@@ -189,7 +206,9 @@ ApplyPlan apply_plan(int N, int k, int K, int r_pad, int d_in, int d_out, bool y
     a.sort = rank_sort_plan(P, k, K);
     a.z_off = a.sort.bytes;
     a.z_bytes = zb;
-    a.total = a.z_off + a.z_bytes;
+    a.gs_off = align256(a.z_off + a.z_bytes);  // one pass at a time: N rows each
+    a.gs = gs_region(a.path, N, K, r_pad, d_in);
+    a.total = a.gs_off + a.gs.total;
     return a;
   }
   if (a.path == kPathTile || (k == 1 && a.path == kPathGrouped)) return a;
