@@ -112,10 +112,6 @@ static void apply_writes(const ApplyLaunch& a) {
       gs_writes(P);
       return;
     }
-    if (gm_tokblock(a.k)) {
-      write_span<uint16_t>(ws + p.hpart_off, 0, (size_t)P * 2 * a.tgt.r_pad, "pair h");  // shrink-only tiles
-      return;
-    }
     rank_sort_writes(ws + p.sort_off, P, a.k, a.K);
     if (!a.y_f32) write_span<float>(ws + p.z_off, 0, (size_t)a.N * a.tgt.d_out, "z");
     gs_writes(a.N);

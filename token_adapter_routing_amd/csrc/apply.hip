@@ -24,8 +24,7 @@
 //                      orders the pairs by (rank among the token's pairs, adapter), one pass
 //                      per rank: within a pass every token has at most one row, so no two
 //                      workgroups write one row; the passes carry the sum in fp32 and
-//                      finish_tokens writes the tokens the last pass does not reach; k >= 4:
-//                      pair_shrink_gm + expand_tokblock below.
+//                      finish_tokens writes the tokens the last pass does not reach.
 //   apply_fused_k1     [GROUPED, k = 1, rank <= 32] 16 grouped rows of one adapter (gathered
 //                      through perm) and a slice of output columns; shrink and expand fused.
 //   shrink_grouped     [SKINNY, GROUPED k > 1 with k*K > 64] the grouped shrink into an fp32
@@ -786,256 +785,11 @@ __global__ __launch_bounds__(kSThreads) void split_expand(StepArgs a, SplitGeom 
   if (has1) epilogue_store<Y0F32, YF32>(o1, yc1, yrows, c0 + b1 * kColBlock, n, 0xFu);
 }
 
-// --------------------------------------------------------------------------------------
-// k > 1 on the grouped order: the shrink-only 64-row tiles write w * alpha/r * h of every pair
-// as bf16 hi / lo rows (Hs, by grouped position); then a workgroup owns 64 consecutive tokens
-// x 512 output columns (four 128-column groups).  It lists its tokens' routed pairs by key (LDS
-// counting sort) and cuts each key's pairs into 16-pair tiles; every wave walks the tiles on its
-// own, with the tile's rows of Hs as MFMA A operands (loaded two tiles ahead) and the key's B^T
-// rows for its 4 x 16 columns as B operands (the next key's requested one key ahead), and adds
-// the products into an fp32 accumulator [64][512] in LDS: in each group wave w owns output
-// columns 8n + w (the slab's column permutation), so no two waves touch one element, no tile
-// holds two pairs of one token, and every element takes its pairs in key order
-// (deterministic).  y0 is read once and y written once; a token without routed pairs gets y0.
-constexpr int kTBTok = 64;
-constexpr int kTBGroups = 4;                       // 128-column groups per workgroup
-constexpr int kTBCols = kTBGroups * kColBlock;     // 512
-constexpr int kTBThreads = 512;
-struct TokBlockArgs {
-  TargetDev tgt;
-  const uint16_t* Hs;  // [P][2][r_pad] bf16 hi / lo of w * scale * h, by grouped position
-  const int32_t* offsets;
-  const int32_t* perm;
-  const float* perm_w;
-  const int32_t* inv;
-  int N, k, K;
-  float scale;
-  const void* y0;
-  void* y;
-  int ncb;  // column blocks of 512 (the last may hold fewer groups)
-};
-
-// Sort keys: (occurrence of the adapter among the token's earlier slots) * K + adapter; a
-// token that lists one adapter twice has its pairs under different keys, so no 16-pair tile
-// holds two pairs of one token.
-constexpr int kTBKeys = 8 * 64;
-constexpr int kTBMaxTiles = kTBTok * 8 / 16 + kTBKeys;  // tiles of one block, at most
-template <int RB>
-struct TokBlockLds {
-  float acc[kTBTok][kTBCols];                   // 128 KB
-  int32_t plist[kTBTok * 8];                    // the block's grouped positions, key order
-  short ptok[kTBTok * 8];                       // token (within the block) of each plist entry
-  int cnt[kTBKeys + 1], cur[kTBKeys + 1];       // per key: pairs; fill cursor (ends at the key's end)
-  int offs[65];
-  int wtot[kTBThreads / kWave];                 // per-wave totals of the block scans
-  int tpos[kTBMaxTiles];                        // tile -> first plist entry
-  short tkey[kTBMaxTiles];                      // tile -> key
-  short tnext[kTBMaxTiles];                     // tile -> first tile of the next key
-  int ntiles;
-};
-
-// Exclusive scan of one int per thread over the workgroup (kTBThreads); *total gets the sum.
-__device__ __forceinline__ int tb_block_scan(int v, int* wtot, int* total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int inc = wave_incl_scan(v, lane);
-  if (lane == kWave - 1) wtot[wave] = inc;
-  __syncthreads();
-  int base = 0, all = 0;
-#pragma unroll
-  for (int w = 0; w < kTBThreads / kWave; ++w) {
-    base += w < wave ? wtot[w] : 0;
-    all += wtot[w];
-  }
-  *total = all;
-  __syncthreads();  // wtot is free again
-  return base + inc - v;
-}
-
-template <int RB, bool INDIRECT, bool Y0F32, bool YF32>
-__global__ __launch_bounds__(kTBThreads) void expand_tokblock(TokBlockArgs a) {
-  __shared__ TokBlockLds<RB> L;
-  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int n = lane & 15, G = lane >> 4;
-  const int cb = blockIdx.x % a.ncb, tb = blockIdx.x / a.ncb;  // cb % 8 = XCD when ncb % 8 == 0
-  const int t0 = tb * kTBTok;
-  const int ntok = min(kTBTok, a.N - t0);
-  const int d_out = a.tgt.d_out, r_pad = a.tgt.r_pad;
-  const int ngrp = min(kTBGroups, d_out / kColBlock - kTBGroups * cb);  // uniform
-  constexpr size_t y0b = Y0F32 ? 4 : 2, yb = YF32 ? 4 : 2;
-  for (int i = threadIdx.x; i < kTBTok * kTBCols; i += kTBThreads) (&L.acc[0][0])[i] = 0.f;
-  const int nkeys = a.k * a.K;
-  for (int i = threadIdx.x; i < nkeys; i += kTBThreads) L.cnt[i] = 0;
-  if (threadIdx.x <= a.K) L.offs[threadIdx.x] = a.offsets[threadIdx.x];
-  __syncthreads();
-  // the block's routed pairs (at most 8 per token, 512 per block): key of each, counted per key
-  const int npairs = ntok * a.k;
-  const long long p0 = (long long)t0 * a.k;
-  const int v = threadIdx.x;
-  int qv = -1, kv = -1;
-  if (v < npairs) {
-    const int q = a.inv[p0 + v];
-    if (q >= 0) {
-      const int e = segment_of(L.offs, a.K, q);
-      int dup = 0;
-      for (int s = v - v % a.k; s < v; ++s) {  // the token's earlier slots
-        const int qs = a.inv[p0 + s];
-        if (qs >= 0 && segment_of(L.offs, a.K, qs) == e) ++dup;
-      }
-      qv = q;
-      kv = dup * a.K + e;
-      atomicAdd(&L.cnt[kv], 1);
-    }
-  }
-  __syncthreads();
-  // key starts and the tile table (one thread per key; nkeys <= 512 = threads)
-  {
-    const int key = threadIdx.x;
-    const int c = key < nkeys ? L.cnt[key] : 0;
-    int tot = 0;
-    const int st = tb_block_scan(c, L.wtot, &tot);
-    const int nt = (c + 15) / 16;
-    int ntot = 0;
-    const int ts = tb_block_scan(nt, L.wtot, &ntot);
-    if (key < nkeys) {
-      L.cur[key] = st;
-      for (int b = 0; b < nt; ++b) {
-        L.tpos[ts + b] = st + 16 * b;
-        L.tkey[ts + b] = (short)key;
-        L.tnext[ts + b] = (short)(ts + nt);
-      }
-    }
-    if (threadIdx.x == 0) L.ntiles = ntot;
-  }
-  __syncthreads();
-  if (kv >= 0) {
-    const int pos = atomicAdd(&L.cur[kv], 1);
-    L.plist[pos] = qv;
-    L.ptok[pos] = (short)(v / a.k);
-  }
-  __syncthreads();
-  const int ntiles = L.ntiles;
-  auto rows_of = [&](int t) {
-    const int key = L.tkey[t];
-    return min(16, L.cur[key] - L.tpos[t]);  // cur ends at the key's end
-  };
-  // lane's slab rows (one per group) and output columns within the block
-  auto load_b = [&](u32x4_t (&bv)[kTBGroups][RB], int key) {
-    const uint16_t* Bt = adapter_B<INDIRECT>(a.tgt, key % a.K);
-#pragma unroll
-    for (int g = 0; g < kTBGroups; ++g) {
-      const int srow = (kTBGroups * cb + min(g, ngrp - 1)) * kColBlock + 16 * wave + n;
-#pragma unroll
-      for (int u = 0; u < RB; ++u) bv[g][u] = ld16(Bt + (size_t)srow * r_pad + (G & 1) * 8 + 16 * u);
-    }
-  };
-  // A operand of tile t for lane (pair row n, group G): groups 0, 1 hi of ranks
-  // 16u + 8(G & 1) .., groups 2, 3 lo of the same ranks
-  auto load_a = [&](u32x4_t (&av)[RB], int t) {
-    if (t < ntiles && n < rows_of(t)) {
-      const int q = L.plist[L.tpos[t] + n];
-      const uint16_t* row = a.Hs + (size_t)q * (2 * r_pad) + (G >> 1) * r_pad + 8 * (G & 1);
-#pragma unroll
-      for (int u = 0; u < RB; ++u) av[u] = ld16(row + 16 * u);
-    } else {
-#pragma unroll
-      for (int u = 0; u < RB; ++u) av[u] = u32x4_t{0u, 0u, 0u, 0u};
-    }
-  };
-  u32x4_t bv[kTBGroups][RB], bvn[kTBGroups][RB];
-  int bkey = -1;
-  auto apply_tile = [&](const u32x4_t (&av)[RB], int t) {
-    const int key = L.tkey[t];
-    if (key != bkey) {  // uniform: the next key's rows were requested one key ahead
-#pragma unroll
-      for (int g = 0; g < kTBGroups; ++g)
-#pragma unroll
-        for (int u = 0; u < RB; ++u) bv[g][u] = bvn[g][u];
-      bkey = key;
-      const int tn = L.tnext[t];
-      if (tn < ntiles) load_b(bvn, L.tkey[tn]);
-    }
-    const int rows = rows_of(t);
-    const int p0t = L.tpos[t];
-    int tk[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) tk[i] = 4 * G + i < rows ? L.ptok[p0t + 4 * G + i] : -1;
-    f32x4_t o[kTBGroups];
-#pragma unroll
-    for (int g = 0; g < kTBGroups; ++g) {
-      o[g] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int u = 0; u < RB; ++u) o[g] = mfma16x16x32(as_bf16x8(av[u]), as_bf16x8(bv[g][u]), o[g]);
-    }
-    // the tile's 4 x 4 accumulator elements of this lane are distinct (distinct tokens,
-    // distinct groups): all reads, then all writes, so the LDS round trips overlap
-    float cur[kTBGroups][4];
-#pragma unroll
-    for (int g = 0; g < kTBGroups; ++g)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        cur[g][i] = (g < ngrp && tk[i] >= 0) ? L.acc[tk[i] < 0 ? 0 : tk[i]][g * kColBlock + 8 * n + wave] : 0.f;
-#pragma unroll
-    for (int g = 0; g < kTBGroups; ++g)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (g < ngrp && tk[i] >= 0) L.acc[tk[i]][g * kColBlock + 8 * n + wave] = cur[g][i] + o[g][i];
-  };
-  if (ntiles > 0) load_b(bvn, L.tkey[0]);
-  u32x4_t aa[RB], ab[RB];
-  load_a(aa, 0);
-  load_a(ab, 1);
-  for (int t = 0; t < ntiles; t += 2) {
-    apply_tile(aa, t);
-    load_a(aa, t + 2);
-    if (t + 1 < ntiles) {
-      apply_tile(ab, t + 1);
-      load_a(ab, t + 3);
-    }
-  }
-  __syncthreads();  // the accumulator is complete
-  // y = y0 + acc, 8 columns per chunk: chunk c = threadIdx.x + 512 j is token c / 64,
-  // columns 8 (c % 64) ..
-  constexpr int kChunks = kTBTok * kTBCols / 8 / kTBThreads;  // 8
-  const int ncols = ngrp * kColBlock;
-#pragma unroll
-  for (int j = 0; j < kChunks; ++j) {
-    const int c = threadIdx.x + kTBThreads * j;
-    const int tl = c / (kTBCols / 8), c8 = c % (kTBCols / 8);
-    if (tl >= ntok || 8 * c8 >= ncols) continue;
-    const size_t off = (size_t)(t0 + tl) * d_out + (size_t)cb * kTBCols + 8 * c8;
-    const char* src = reinterpret_cast<const char*>(a.y0) + off * y0b;
-    float r[8];
-    if constexpr (Y0F32) {
-      const u32x4_t v0 = ld16_nt(src), v1 = ld16_nt(src + 16);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        r[i] = __uint_as_float(v0[i]);
-        r[4 + i] = __uint_as_float(v1[i]);
-      }
-    } else {
-      const u32x4_t v0 = ld16_nt(src);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) r[i] = bf16_to_f32((i & 1) ? (v0[i >> 1] >> 16) : (v0[i >> 1] & 0xffffu));
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) r[i] += L.acc[tl][8 * c8 + i];
-    char* dst = reinterpret_cast<char*>(a.y) + off * yb;
-    if constexpr (YF32) {
-      st16_nt(dst, u32x4_t{__float_as_uint(r[0]), __float_as_uint(r[1]), __float_as_uint(r[2]), __float_as_uint(r[3])});
-      st16_nt(dst + 16,
-              u32x4_t{__float_as_uint(r[4]), __float_as_uint(r[5]), __float_as_uint(r[6]), __float_as_uint(r[7])});
-    } else {
-      st16_nt(dst, u32x4_t{pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3]), pack_bf16x2(r[4], r[5]),
-                           pack_bf16x2(r[6], r[7])});
-    }
-  }
-}
-
 // Shrink only: unscaled h of every grouped pair (the backward's h and g).
 template <int RB, bool INDIRECT>
 __global__ __launch_bounds__(kGMThreads) void shrink_gm(GMArgs a) {
   __shared__ GMLds<RB> L;
-  gm_range<RB, INDIRECT, false, false, true>(a, L);
+  gm_shrink_tile<RB, INDIRECT>(a, L);
 }
 
 // Key of grouped position q: (rank of its pair among the token's routed pairs) * K + adapter;
@@ -1714,7 +1468,6 @@ hipError_t launch_apply(const ApplyLaunch& a, hipStream_t s) {
     // plan's grouped-split region)
     const long long rows_max = a.k == 1 ? P : a.N;  // rows of one pass
     const GMTiling tl = gm_tiling(a.path, rows_max, a.K, (a.tgt.d_in + kBSlice - 1) / kBSlice);
-    ga.col_groups = 1;
     ga.tile_rows = tl.rows;
     ga.fixed = tl.fixed;
     // a pass = three launches over 512-wide slices of the tiles (gsplit.hip)
@@ -1734,26 +1487,7 @@ hipError_t launch_apply(const ApplyLaunch& a, hipStream_t s) {
           err = (launch_finish_t<Y0F, YF>(a.y0, nullptr, a.y, a.inv, a.N, 1, a.tgt.d_out, true, false, s))));
       return err;
     }
-    if (gm_tokblock(a.k)) {
-      // k >= 4: h of every pair (shrink-only tiles over the whole grouped order), then one
-      // token-block expand that reads y0 once and writes y once
-      uint16_t* Hs = reinterpret_cast<uint16_t*>(wsb + plan.hpart_off);
-      err = launch_pair_shrink_gm(a.tgt, a.indirect, a.x, a.offsets, a.perm, a.K, a.k, P, nullptr, s,
-                                  a.path == kPathGroupedFixed, Hs, a.perm_w, a.scale);
-      if (err != hipSuccess) return err;
-      TokBlockArgs tb;
-      tb.tgt = a.tgt; tb.Hs = Hs; tb.offsets = a.offsets; tb.perm = a.perm; tb.perm_w = a.perm_w; tb.inv = a.inv;
-      tb.N = a.N; tb.k = a.k; tb.K = a.K; tb.scale = a.scale; tb.y0 = a.y0; tb.y = a.y;
-      tb.ncb = (a.tgt.d_out + kTBCols - 1) / kTBCols;
-      const int tgrid = ((a.N + kTBTok - 1) / kTBTok) * tb.ncb;
-      MOLORA_DISPATCH_RB(RBv, MOLORA_DISPATCH_BOOL(a.indirect, IND, MOLORA_DISPATCH_BOOL(a.y0_f32, Y0F,
-          MOLORA_DISPATCH_BOOL(a.y_f32, YF, {
-            hipLaunchKernelGGL((expand_tokblock<RB, IND, Y0F, YF>), dim3(tgrid), dim3(kTBThreads), 0, s, tb);
-            err = hipGetLastError();
-          }))));
-      return err;
-    }
-    // k = 2, 3: pass j applies the j-th routed pair of every token over the (rank, adapter)
+    // k > 1: pass j applies the j-th routed pair of every token over the (rank, adapter)
     // order of the slot sort; pass 0 reads y0, the last pass writes y and the passes in between
     // carry the sum in fp32 (in y itself when y is fp32, else in z), so a bf16 y is rounded once.
     RankSort rs;
@@ -2033,13 +1767,12 @@ hipError_t launch_step_vocab(const StepVocabLaunch& a, hipStream_t s) {
 // Per-pair shrink without gate weight or scale on the 64-row grouped tiles: hout[q] = x_t A_e
 // of grouped position q (the backward's h and g).
 hipError_t launch_pair_shrink_gm(const TargetDev& tgt, bool indirect, const uint16_t* x, const int32_t* offsets,
-                                 const int32_t* perm, int K, int k, long long P, float* hout, hipStream_t s,
-                                 bool fixed_tiles, uint16_t* hs_out, const float* perm_w, float scale) {
+                                 const int32_t* perm, int K, int k, long long P, float* hout, hipStream_t s) {
   GMArgs ga{};
   ga.tgt = tgt; ga.x = x; ga.k = k; ga.perm = perm; ga.offsets = offsets; ga.key0 = 0; ga.nkeys = K;
-  ga.order = nullptr; ga.wts = perm_w; ga.scale = scale; ga.hout = hout; ga.hs_out = hs_out;
-  const GMTiling tl = gm_tiling(fixed_tiles ? kPathGroupedFixed : kPathGrouped, P, K, 1);
-  ga.tile_rows = tl.rows; ga.fixed = tl.fixed; ga.col_groups = 1;
+  ga.order = nullptr; ga.hout = hout;
+  const GMTiling tl = gm_tiling(kPathGrouped, P, K, 1);
+  ga.tile_rows = tl.rows; ga.fixed = tl.fixed;
   ga.nwg = (int)((tl.max_tiles + 7) / 8 * 8);
   const int RBv = tgt.r_pad / 16;
   hipError_t err = hipSuccess;

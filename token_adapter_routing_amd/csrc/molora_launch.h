@@ -67,17 +67,15 @@ hipError_t launch_dense_block(const ApplyLaunch* as, int n, const size_t* ws_off
                               const DenseFuse* fuse = nullptr);
 
 struct GMArgs;  // gm_dev.h
-// One pass of the 64-row grouped tiles (g as for apply_gm; g.nwg from gs_region) in three
-// launches over 512-wide slices: partials into part, h rows into hb (gs_region's layout).
+// One pass of the 64-row grouped tiles (g: the pass's rows, routing and tiling; g.nwg from
+// gs_region) in three launches over 512-wide slices: partials into part, h rows into hb
+// (gs_region's layout).
 hipError_t launch_gs_pass(const GMArgs& g, float* part, uint16_t* hb, bool y0_f32, bool y_f32, bool indirect,
                           hipStream_t s);
 
 // Per-pair shrink without gate weight or scale (64-row grouped tiles) into hout [P][r_pad] fp32.
-// hs_out != NULL: write bf16 hi / lo of perm_w * scale * h at [q][2][r_pad] instead of hout.
 hipError_t launch_pair_shrink_gm(const TargetDev& tgt, bool indirect, const uint16_t* x, const int32_t* offsets,
-                                 const int32_t* perm, int K, int k, long long P, float* hout, hipStream_t s,
-                                 bool fixed_tiles = false, uint16_t* hs_out = nullptr,
-                                 const float* perm_w = nullptr, float scale = 1.f);
+                                 const int32_t* perm, int K, int k, long long P, float* hout, hipStream_t s);
 
 // Backward of the routed LoRA except dx: dA, dB, dw (any may be NULL) from x, gy and the
 // forward routing; ws holds bwd_plan() for these shapes.

@@ -125,12 +125,9 @@ int skinny_splits(int d_in);
 bool use_gm(int k, int K, int r_pad);
 // The resolved path runs the 64-row grouped kernel: the grouped path where use_gm holds, and
 // the fixed-tiling comparator wherever its rank passes apply (k == 1 or k*K <= 64).
+// k > 1 runs one split pass per pair rank with an fp32 carry (measured at K = 16, rank 64,
+// 16384 tokens, k = 4: 799 us, against 982 us for a token-block expand that read y0 once).
 bool gm_path(int path, int k, int K, int r_pad);
-// k > 1 on the 64-row grouped tiles: the token-block expand (y0 read once, y written once) from
-// k = 4 on; one pass per pair rank with an fp32 carry below (measured at K = 16, rank 64,
-// 16384 tokens: 534 / 852 us for the passes at k = 2 / 3 against 792 / 889 us; 983 against
-// 1147 us at k = 4).
-bool gm_tokblock(int k);
 // Row tiles of the 64-row grouped kernel: per segment (adapter) of a pass, ceil(count / rows)
 // tiles, balanced inside the segment (adaptive) or of exactly `rows` rows but the last (fixed).
 struct GMTiling {

@@ -130,8 +130,6 @@ int skinny_splits(int d_in) {
 
 bool use_gm(int k, int K, int r_pad) { return (k > 1 && k * K <= 64) || (k == 1 && r_pad > 32); }
 
-bool gm_tokblock(int k) { return k >= 4; }
-
 bool gm_path(int path, int k, int K, int r_pad) {
   if (path == kPathGrouped) return use_gm(k, K, r_pad);
   return path == kPathGroupedFixed && (k == 1 || k * K <= 64);
@@ -193,13 +191,6 @@ ApplyPlan apply_plan(int N, int k, int K, int r_pad, int d_in, int d_out, bool y
       a.gs_off = 0;
       a.gs = gs_region(a.path, P, K, r_pad, d_in);
       a.total = a.gs.total;
-      return a;
-    }
-    if (gm_tokblock(k)) {
-      // w * scale * h of every pair as bf16 hi / lo [P][2][r_pad] for the token-block expand
-      a.hpart_off = 0;
-      a.hpart_bytes = align256((size_t)P * 2 * r_pad * sizeof(uint16_t));
-      a.total = a.hpart_bytes;
       return a;
     }
     a.sort_off = 0;
