@@ -112,6 +112,31 @@ static void apply_writes(const ApplyLaunch& a) {
       gs_writes(P);
       return;
     }
+    if (gm_tuples(a.N, a.k, a.K)) {
+      // the pair shrink (partials of every pair's tiles), h by grouped position, the tuple
+      // sort (counts, offsets, at most N entries per pass) and the carry of k > 2
+      CHECK(p.tuples == 1, "pair passes planned");
+      const GSRegion g = gs_region(a.path, P, a.K, a.tgt.r_pad, a.tgt.d_in, false);
+      const long long kslices = (a.tgt.d_in + kBSlice - 1) / kBSlice;
+      write_span<float>(ws + p.gs_off, 0, (size_t)g.nwg * kslices * 64 * a.tgt.r_pad, "pair partials");
+      write_span<uint16_t>(ws + p.hq_off, 0, (size_t)P * 2 * a.tgt.r_pad, "pair h");
+      const int m2 = (a.k + 1) / 2, nkeys = m2 * a.K * (a.K + 1);
+      const int nb = (a.N + kTupleWGTokens - 1) / kTupleWGTokens;
+      const TupleSortPlan& t = p.tsort;
+      write_span<int32_t>(ws + p.tsort_off + t.bcnt_off, 0, (size_t)nb * nkeys, "tuple counts");
+      write_span<int32_t>(ws + p.tsort_off + t.toff_off, 0, (size_t)nkeys + 1, "tuple offsets");
+      // a pass's tiles: at most ceil(N / rows) + keys of the expand's tiling (rows >= 16)
+      const GMTiling te = gm_tiling(a.path, a.N, a.K * (a.K + 1), (a.tgt.d_out + 255) / 256);
+      CHECK(te.rows >= 16 && te.max_tiles <= t.tmax, "tile table bound");
+      write_span<int32_t>(ws + p.tsort_off + t.tiles_off, 0, (size_t)m2 * t.tmax * 4, "tuple tiles");
+      write_span<int32_t>(ws + p.tsort_off + t.ntile_off, 0, (size_t)m2, "tuple tile counts");
+      write_span<int32_t>(ws + p.tsort_off + t.etok_off, 0, (size_t)m2 * a.N, "tuple tokens");
+      write_span<int32_t>(ws + p.tsort_off + t.eqa_off, 0, (size_t)m2 * a.N, "tuple first pairs");
+      write_span<int32_t>(ws + p.tsort_off + t.eqb_off, 0, (size_t)m2 * a.N, "tuple second pairs");
+      if (!a.y_f32 && m2 > 1) write_span<float>(ws + p.z_off, 0, (size_t)a.N * a.tgt.d_out, "z");
+      return;
+    }
+    CHECK(p.tuples == 0, "rank passes planned");
     rank_sort_writes(ws + p.sort_off, P, a.k, a.K);
     if (!a.y_f32) write_span<float>(ws + p.z_off, 0, (size_t)a.N * a.tgt.d_out, "z");
     gs_writes(a.N);
@@ -906,6 +931,10 @@ int main() {
           for (int N : {0, 1, 100, 1024, 4097})
             for (int yd : {MOLORA_BF16, MOLORA_F32}) test_apply(K, r, 1024, 2048, N, k, path, yd);
   for (int N : {16384}) test_apply(16, 64, 4096, 4096, N, 4, MOLORA_PATH_AUTO, MOLORA_BF16);
+  for (int k : {2, 3, 4})  // pair passes at the stress shape
+    for (int yd : {MOLORA_BF16, MOLORA_F32}) test_apply(16, 64, 4096, 4096, 16384, k, MOLORA_PATH_GROUPED, yd);
+  for (int N : {2303, 2304, 65536})  // K (K + 1) = 72 keys per pass, four passes at k = 8
+    for (int k : {7, 8}) test_apply(8, 64, 512, 640, N, k, MOLORA_PATH_GROUPED, MOLORA_BF16);
   for (int path : {MOLORA_PATH_AUTO, MOLORA_PATH_SKINNY, MOLORA_PATH_BLOCK, MOLORA_PATH_GROUPED})
     for (int k : {1, 2})
       for (int N : {1, 256, 4096})

@@ -850,18 +850,18 @@ __global__ __launch_bounds__(1024) void slot_scatter(const int32_t* __restrict__
 }
 
 // After the passes: y = y0 for tokens with no routed pair (copy_y0, out-of-place calls) and
-// y = z (the fp32 pass buffer) for tokens whose last routed pair came before the last pass
-// (copy_z, when z is not y itself).  One wave per 64 tokens.
+// y = z (the fp32 pass buffer) for tokens whose routed pairs end before the last pass, i.e.
+// fewer than c_last of them (copy_z, when z is not y itself).  One wave per 64 tokens.
 template <bool Y0F32, bool YF32>
 __device__ __forceinline__ void finish_body(const void* y0, const float* z, void* y, const int32_t* __restrict__ inv,
-                                            int N, int k, int d_out, int copy_y0, int copy_z, int blk) {
+                                            int N, int k, int c_last, int d_out, int copy_y0, int copy_z, int blk) {
   const int lane = threadIdx.x & 63;
   const int base = (blk * 4 + (threadIdx.x >> 6)) * kWave;
   const int t = base + lane;
   int c = 0;
   if (t < N)
     for (int j = 0; j < k; ++j) c += inv[(long long)t * k + j] >= 0 ? 1 : 0;
-  uint64_t m = __ballot(t < N && ((copy_y0 && c == 0) || (copy_z && c > 0 && c < k)));
+  uint64_t m = __ballot(t < N && ((copy_y0 && c == 0) || (copy_z && c > 0 && c < c_last)));
   while (m) {
     const int l = __builtin_ctzll(m);
     m &= m - 1;
@@ -898,9 +898,9 @@ __device__ __forceinline__ void finish_body(const void* y0, const float* z, void
 }
 template <bool Y0F32, bool YF32>
 __global__ __launch_bounds__(256) void finish_tokens(const void* y0, const float* z, void* y,
-                                                     const int32_t* __restrict__ inv, int N, int k, int d_out,
-                                                     int copy_y0, int copy_z) {
-  finish_body<Y0F32, YF32>(y0, z, y, inv, N, k, d_out, copy_y0, copy_z, blockIdx.x);
+                                                     const int32_t* __restrict__ inv, int N, int k, int c_last,
+                                                     int d_out, int copy_y0, int copy_z) {
+  finish_body<Y0F32, YF32>(y0, z, y, inv, N, k, c_last, d_out, copy_y0, copy_z, blockIdx.x);
 }
 
 // --------------------------------------------------------------------------------------
@@ -1190,7 +1190,8 @@ __global__ __launch_bounds__(256) void expand_grouped_multi(ExpandMulti m) {
 template <bool Y0F32, bool YF32>
 __global__ __launch_bounds__(256) void finish_tokens_multi(FinishMulti m) {
   const int i = blockIdx.y;
-  finish_body<Y0F32, YF32>(m.y0[i], m.z[i], m.y[i], m.inv, m.N, m.k, m.d_out[i], m.copy_y0[i], m.copy_z[i], blockIdx.x);
+  finish_body<Y0F32, YF32>(m.y0[i], m.z[i], m.y[i], m.inv, m.N, m.k, m.k, m.d_out[i], m.copy_y0[i], m.copy_z[i],
+                           blockIdx.x);
 }
 
 // k > 1: grid = ceil(N/16) token tiles * col_groups.  KMAX bounds k (register arrays).
@@ -1339,9 +1340,9 @@ static hipError_t launch_t8_t(const T8ApplyArgs& ta, int grid, hipStream_t s) {
 }
 template <bool Y0F, bool YF>
 static hipError_t launch_finish_t(const void* y0, const float* z, void* y, const int32_t* inv, int N, int k,
-                                  int d_out, bool copy_y0, bool copy_z, hipStream_t s) {
-  hipLaunchKernelGGL((finish_tokens<Y0F, YF>), dim3((N + 255) / 256), dim3(256), 0, s, y0, z, y, inv, N, k, d_out,
-                     (int)copy_y0, (int)copy_z);
+                                  int d_out, bool copy_y0, bool copy_z, hipStream_t s, int c_last = 0) {
+  hipLaunchKernelGGL((finish_tokens<Y0F, YF>), dim3((N + 255) / 256), dim3(256), 0, s, y0, z, y, inv, N, k,
+                     c_last > 0 ? c_last : k, d_out, (int)copy_y0, (int)copy_z);
   return hipGetLastError();
 }
 template <int RB, bool IND, bool Y0F, bool YF>
@@ -1460,7 +1461,7 @@ hipError_t launch_apply(const ApplyLaunch& a, hipStream_t s) {
   }
 
   if (gm_path(a.path, a.k, a.K, a.tgt.r_pad)) {
-    // 64-row grouped tiles (k = 1: shrink and expand in one kernel; k > 1: below).
+    // 64-row grouped tiles split over 512-wide slices (k = 1: one pass; k > 1: below).
     const bool in_place = (a.y0 == a.y);
     GMArgs ga{};
     ga.tgt = a.tgt; ga.x = a.x; ga.N = a.N; ga.k = a.k; ga.scale = a.scale; ga.perm = a.perm; ga.nkeys = a.K;
@@ -1485,6 +1486,41 @@ hipError_t launch_apply(const ApplyLaunch& a, hipStream_t s) {
       if (err != hipSuccess || in_place) return err;
       MOLORA_DISPATCH_BOOL(a.y0_f32, Y0F, MOLORA_DISPATCH_BOOL(a.y_f32, YF,
           err = (launch_finish_t<Y0F, YF>(a.y0, nullptr, a.y, a.inv, a.N, 1, a.tgt.d_out, true, false, s))));
+      return err;
+    }
+    if (plan.tuples) {
+      // k > 1 in pair passes: h of every pair by grouped position (one split shrink over the
+      // dispatch's order), the tuple sort, then pass m applies each token's routed pairs of rank
+      // 2m and 2m + 1; pass 0 reads y0, the last writes y, the passes between carry the sum in
+      // fp32 (in y itself when y is fp32, else in z)
+      const int kslices = (a.tgt.d_in + kBSlice - 1) / kBSlice;
+      const GMTiling tp = gm_tiling(a.path, P, a.K, kslices);
+      uint16_t* hq = reinterpret_cast<uint16_t*>(wsb + plan.hq_off);
+      ga.key0 = 0; ga.offsets = a.offsets; ga.order = nullptr; ga.wts = a.perm_w;
+      ga.tile_rows = tp.rows; ga.fixed = tp.fixed; ga.nwg = plan.gs.nwg;
+      err = launch_gs_pair_shrink(ga, gs_part, hq, a.indirect, s);
+      if (err != hipSuccess) return err;
+      const TupleSortPlan& tsp = plan.tsort;
+      char* tsr = wsb + plan.tsort_off;
+      const GMTiling te = gm_tiling(a.path, a.N, tsp.kk, (a.tgt.d_out + 2 * kColBlock - 1) / (2 * kColBlock));
+      err = launch_tuple_sort(a.offsets, a.inv, a.N, a.k, a.K, tsr, tsp, te, s);
+      if (err != hipSuccess) return err;
+      GMArgs ge = ga;
+      ge.nwg = (int)((te.max_tiles + 7) / 8 * 8);
+      float* z = zbuf;
+      for (int m = 0; m < tsp.m2; ++m) {
+        const bool last = m == tsp.m2 - 1;
+        ge.y0 = m == 0 ? a.y0 : static_cast<const void*>(z);
+        ge.y = last ? a.y : static_cast<void*>(z);
+        err = launch_gs_expand_pairs(ge, tsr, tsp, m, hq, a.K, m == 0 ? (bool)a.y0_f32 : true,
+                                     last ? (bool)a.y_f32 : true, a.indirect, s);
+        if (err != hipSuccess) return err;
+      }
+      const bool copy_z = tsp.m2 > 1 && static_cast<void*>(z) != a.y;
+      if (in_place && !copy_z) return err;
+      MOLORA_DISPATCH_BOOL(a.y0_f32, Y0F, MOLORA_DISPATCH_BOOL(a.y_f32, YF,
+          err = (launch_finish_t<Y0F, YF>(a.y0, z, a.y, a.inv, a.N, a.k, a.tgt.d_out, !in_place, copy_z, s,
+                                          2 * tsp.m2 - 1))));
       return err;
     }
     // k > 1: pass j applies the j-th routed pair of every token over the (rank, adapter)

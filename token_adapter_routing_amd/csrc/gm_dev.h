@@ -202,23 +202,32 @@ __device__ void gm_shrink_rows(const GMArgs& a, GMLds<RB>& L, int e, int row0, i
 __device__ __forceinline__ bool gm_locate(const GMArgs& a, int w, int& e, int& r0, int& r1) {
   const int lane = threadIdx.x & 63;
   const int M = a.tile_rows;
-  const int s0l = lane < a.nkeys ? a.offsets[a.key0 + lane] : 0;
-  const int cl = lane < a.nkeys ? a.offsets[a.key0 + lane + 1] - s0l : 0;
-  const int ntl = (cl + M - 1) / M;
-  const int incl = wave_incl_scan(ntl, lane);
-  const uint64_t m = __ballot(lane < a.nkeys && w >= incl - ntl && w < incl);
-  if (m == 0) return false;
-  e = __builtin_ctzll(m);
-  const int s0 = __shfl(s0l, e, kWave), c = __shfl(cl, e, kWave), nt = __shfl(ntl, e, kWave);
-  const int i = w - (__shfl(incl, e, kWave) - nt);
-  if (a.fixed) {
-    r0 = s0 + i * M;
-    r1 = min(s0 + c, r0 + M);
-  } else {
-    r0 = s0 + (int)((long long)c * i / nt);
-    r1 = s0 + (int)((long long)c * (i + 1) / nt);
+  int before = 0;  // tiles of the keys of the earlier 64-key chunks
+  for (int kc = 0; kc < a.nkeys; kc += kWave) {
+    const int key = kc + lane;
+    const bool in = key < a.nkeys;
+    const int s0l = in ? a.offsets[a.key0 + key] : 0;
+    const int cl = in ? a.offsets[a.key0 + key + 1] - s0l : 0;
+    const int ntl = (cl + M - 1) / M;
+    const int incl = before + wave_incl_scan(ntl, lane);
+    const uint64_t m = __ballot(in && w >= incl - ntl && w < incl);
+    if (m != 0) {
+      const int l = __builtin_ctzll(m);
+      e = kc + l;
+      const int s0 = __shfl(s0l, l, kWave), c = __shfl(cl, l, kWave), nt = __shfl(ntl, l, kWave);
+      const int i = w - (__shfl(incl, l, kWave) - nt);
+      if (a.fixed) {
+        r0 = s0 + i * M;
+        r1 = min(s0 + c, r0 + M);
+      } else {
+        r0 = s0 + (int)((long long)c * i / nt);
+        r1 = s0 + (int)((long long)c * (i + 1) / nt);
+      }
+      return true;
+    }
+    before = __shfl(incl, kWave - 1, kWave);
   }
-  return true;
+  return false;
 }
 
 // Workgroup b takes tile (b % 8) * nwg / 8 + b / 8: consecutive tiles (mostly of one adapter)

@@ -17,7 +17,10 @@
 // Every launch numbers the tiles the same way: tile w runs on XCD w / (nwg / 8), with the
 // tiles of one adapter mostly on one XCD, whose L2 then holds the adapter's slices and the
 // tile's partials and h rows.
+#include <climits>
+
 #include "gm_dev.h"
+#include "molora.h"
 #include "molora_launch.h"
 
 namespace molora {
@@ -31,6 +34,7 @@ struct GSArgs {
   GMArgs g;        // the pass: tiles, rows, routing, adapters, x, y0 / y, scale
   float* part;     // [nwg][kslices][64][r_pad] fp32
   uint16_t* hb;    // [nwg][2][64][r_pad] bf16 hi / lo of the weighted h
+  uint16_t* hq;    // instead of hb (a pass over every pair, no order): [q][2][r_pad] by grouped position
   int kslices, cslices;
 };
 
@@ -136,7 +140,7 @@ __global__ __launch_bounds__(kGSThreads) void gs_finalize(const GSArgs a) {
   if (!gm_locate(a.g, w, e, r0, r1)) return;
   const int nrows = r1 - r0;
   const float* base = a.part + (size_t)w * a.kslices * kGMRows * RP;
-  uint16_t* hb = a.hb + (size_t)w * 2 * kGMRows * RP;
+  uint16_t* hb = a.hq == nullptr ? a.hb + (size_t)w * 2 * kGMRows * RP : nullptr;
 #pragma unroll
   for (int j = 0; j < QPT; ++j) {
     const int v = j * kGSThreads + (int)threadIdx.x;
@@ -168,8 +172,16 @@ __global__ __launch_bounds__(kGSThreads) void gs_finalize(const GSArgs a) {
       hi2[c / 2] = pack_bf16x2(hv[0], hv[1]);
       lo2[c / 2] = pack_bf16x2(lv[0], lv[1]);
     }
-    *reinterpret_cast<uint2*>(hb + (size_t)row * RP + rk) = make_uint2(hi2[0], hi2[1]);
-    *reinterpret_cast<uint2*>(hb + (size_t)(kGMRows + row) * RP + rk) = make_uint2(lo2[0], lo2[1]);
+    if (a.hq != nullptr) {
+      if (row < nrows) {
+        uint16_t* hq = a.hq + (size_t)(r0 + row) * 2 * RP + rk;
+        *reinterpret_cast<uint2*>(hq) = make_uint2(hi2[0], hi2[1]);
+        *reinterpret_cast<uint2*>(hq + RP) = make_uint2(lo2[0], lo2[1]);
+      }
+    } else {
+      *reinterpret_cast<uint2*>(hb + (size_t)row * RP + rk) = make_uint2(hi2[0], hi2[1]);
+      *reinterpret_cast<uint2*>(hb + (size_t)(kGMRows + row) * RP + rk) = make_uint2(lo2[0], lo2[1]);
+    }
   }
 }
 
@@ -256,20 +268,273 @@ __global__ __launch_bounds__(kGSThreads, 2) void gs_expand(const GSArgs a) {
   if (has1) epilogue_store<Y0F32, YF32>(o1, yc1, yrows, c0 + b1 * kColBlock, n, vmask);
 }
 
+// ---- pair passes (k > 1): pass m applies a token's routed pairs of rank 2m and 2m + 1 in one
+// tile row.  The shrink and finalize above run once over every pair in the dispatch's grouped
+// order and leave h by grouped position (hq); the tuple sort lists each pass's tokens by the
+// adapter pair (a, b) of those two pairs (b = K: the token has no pair of rank 2m + 1); the
+// pair expand cuts each key's rows into tiles like any other pass and applies
+// y = src + h_a B_a + h_b B_b (the two products summed in the MFMA accumulators, in that order).
+// A row's result does not depend on the other rows of its tile, so the order of a key's rows
+// (the sort is not stable) leaves every output bit unchanged.
+
+constexpr int kTSThreads = kTupleWGTokens;
+constexpr int kTCols = 2 * kColBlock;  // pair expand: output columns per workgroup
+
+struct TupleSortArgs {
+  const int32_t* offsets;  // the dispatch's offsets [K + 1]
+  const int32_t* inv;      // pair -> grouped position (-1: unrouted)
+  int N, k, K, nkeys;      // nkeys = passes x K (K + 1)
+  int m2, kk;              // passes, keys per pass
+  int tile_rows, fixed;    // the expand's tiling (GMTiling)
+  int tmax;                // tile entries per pass
+  int32_t* bcnt;           // [gridDim][nkeys]: the workgroup's counts, then its first positions
+  int32_t* toff;           // [nkeys + 1]
+  int4* tiles;             // [m2][tmax]: (key in the pass, first row, end row, 0)
+  int32_t* ntile;          // [m2]
+  int32_t* etok;
+  int32_t* eqa;
+  int32_t* eqb;
+};
+
+// f(key, q_a, q_b) for every pass of token t: its routed pairs ordered by adapter (equal
+// adapters by slot), taken two by two, so the keys of a pass concentrate on fewer adapter
+// pairs than in rank order.  Registers only: k <= MOLORA_MAX_TOPK, every loop unrolled.
+template <typename F>
+__device__ __forceinline__ void token_tuples(const TupleSortArgs& a, const int* offs, int t, F f) {
+  constexpr int KM = MOLORA_MAX_TOPK;
+  const int K1 = a.K + 1, KK = a.K * K1;
+  int ev[KM], qv[KM], pos[KM];
+  int c = 0;
+#pragma unroll
+  for (int j = 0; j < KM; ++j) {
+    const int q = j < a.k ? a.inv[(long long)t * a.k + j] : -1;
+    qv[j] = q;
+    ev[j] = q >= 0 ? segment_of(offs, a.K, q) : INT_MAX;  // unrouted pairs sort last
+    c += q >= 0 ? 1 : 0;
+  }
+#pragma unroll
+  for (int j = 0; j < KM; ++j) {
+    int p = 0;
+#pragma unroll
+    for (int i = 0; i < KM; ++i) p += (ev[i] < ev[j] || (ev[i] == ev[j] && i < j)) ? 1 : 0;
+    pos[j] = p;
+  }
+#pragma unroll
+  for (int m = 0; m < KM / 2; ++m) {
+    if (2 * m >= c) break;
+    int ea = 0, qa = -1, eb = a.K, qb = -1;
+#pragma unroll
+    for (int j = 0; j < KM; ++j) {
+      if (pos[j] == 2 * m) { ea = ev[j]; qa = qv[j]; }
+      if (pos[j] == 2 * m + 1 && 2 * m + 1 < c) { eb = ev[j]; qb = qv[j]; }
+    }
+    f(m * KK + ea * K1 + eb, qa, qb);
+  }
+}
+
+// LDS: offs [K + 1], then one counter per key
+__global__ __launch_bounds__(kTSThreads) void tuple_count(const TupleSortArgs a) {
+  extern __shared__ int ts_lds[];
+  int* offs = ts_lds;
+  int* cnt = ts_lds + a.K + 1;
+  for (int i = threadIdx.x; i <= a.K; i += kTSThreads) offs[i] = a.offsets[i];
+  for (int i = threadIdx.x; i < a.nkeys; i += kTSThreads) cnt[i] = 0;
+  __syncthreads();
+  const int t = blockIdx.x * kTSThreads + (int)threadIdx.x;
+  if (t < a.N) token_tuples(a, offs, t, [&](int key, int, int) { atomicAdd(&cnt[key], 1); });
+  __syncthreads();
+  for (int i = threadIdx.x; i < a.nkeys; i += kTSThreads) a.bcnt[(size_t)blockIdx.x * a.nkeys + i] = cnt[i];
+}
+
+// One workgroup: thread i owns a run of consecutive keys; toff = exclusive scan of the key
+// totals, and bcnt[b][key] becomes workgroup b's first position in the key.
+__global__ __launch_bounds__(kTSThreads) void tuple_scan(const TupleSortArgs a, int nb) {
+  __shared__ int wsum[kTSThreads / kWave];
+  const int per = (a.nkeys + kTSThreads - 1) / kTSThreads;
+  const int k0 = min((int)threadIdx.x * per, a.nkeys), k1 = min(k0 + per, a.nkeys);
+  int tot = 0;
+  for (int key = k0; key < k1; ++key)
+    for (int b = 0; b < nb; ++b) tot += a.bcnt[(size_t)b * a.nkeys + key];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int incl = wave_incl_scan(tot, lane);
+  if (lane == kWave - 1) wsum[wave] = incl;
+  __syncthreads();
+  int pos = incl - tot;
+  for (int w = 0; w < wave; ++w) pos += wsum[w];
+  for (int key = k0; key < k1; ++key) {
+    a.toff[key] = pos;
+    for (int b = 0; b < nb; ++b) {
+      const size_t i = (size_t)b * a.nkeys + key;
+      const int c = a.bcnt[i];
+      a.bcnt[i] = pos;
+      pos += c;
+    }
+  }
+  if (threadIdx.x == kTSThreads - 1) a.toff[a.nkeys] = pos;  // the last thread ends at the total
+  __syncthreads();
+  // each pass's tiles: key c rows -> nt = ceil(c / tile_rows) tiles, balanced (or fixed
+  // tile_rows rows), numbered key by key; thread i takes a run of consecutive keys of the pass
+  const int M = a.tile_rows;
+  const int per2 = (a.kk + kTSThreads - 1) / kTSThreads;
+  for (int m = 0; m < a.m2; ++m) {
+    const int q0 = min((int)threadIdx.x * per2, a.kk), q1 = min(q0 + per2, a.kk);
+    int nt = 0;
+    for (int q = q0; q < q1; ++q) {
+      const int c = a.toff[m * a.kk + q + 1] - a.toff[m * a.kk + q];
+      nt += (c + M - 1) / M;
+    }
+    const int tincl = wave_incl_scan(nt, lane);
+    __syncthreads();  // wsum's previous readers are done
+    if (lane == kWave - 1) wsum[wave] = tincl;
+    __syncthreads();
+    int w = tincl - nt;
+    for (int v = 0; v < wave; ++v) w += wsum[v];
+    for (int q = q0; q < q1; ++q) {
+      const int s0 = a.toff[m * a.kk + q], c = a.toff[m * a.kk + q + 1] - s0;
+      const int ntq = (c + M - 1) / M;
+      for (int i = 0; i < ntq; ++i, ++w) {
+        const int r0 = a.fixed ? s0 + i * M : s0 + (int)((long long)c * i / ntq);
+        const int r1 = a.fixed ? min(s0 + c, r0 + M) : s0 + (int)((long long)c * (i + 1) / ntq);
+        a.tiles[(size_t)m * a.tmax + w] = make_int4(q, r0, r1, 0);
+      }
+    }
+    if (threadIdx.x == kTSThreads - 1) a.ntile[m] = w;  // the last thread ends at the pass's count
+  }
+}
+
+__global__ __launch_bounds__(kTSThreads) void tuple_scatter(const TupleSortArgs a) {
+  extern __shared__ int ts_lds[];
+  int* offs = ts_lds;
+  int* cur = ts_lds + a.K + 1;
+  for (int i = threadIdx.x; i <= a.K; i += kTSThreads) offs[i] = a.offsets[i];
+  for (int i = threadIdx.x; i < a.nkeys; i += kTSThreads) cur[i] = a.bcnt[(size_t)blockIdx.x * a.nkeys + i];
+  __syncthreads();
+  const int t = blockIdx.x * kTSThreads + (int)threadIdx.x;
+  if (t < a.N)
+    token_tuples(a, offs, t, [&](int key, int qa, int qb) {
+      const int p = atomicAdd(&cur[key], 1);
+      a.etok[p] = t;
+      a.eqa[p] = qa;
+      a.eqb[p] = qb;
+    });
+}
+
+struct TupleArgs {
+  GMArgs g;  // the pass: target, y0 / y (g.nwg: the grid's tile slots, a multiple of 8)
+  const int4* tiles;     // the pass's tiles (key in the pass, first row, end row)
+  const int32_t* ntile;  // the pass's tile count
+  const int32_t* etok;
+  const int32_t* eqa;
+  const int32_t* eqb;
+  const uint16_t* hq;  // [P][2][r_pad] bf16 hi / lo of gate weight x alpha/r x h by grouped position
+  int K1;              // K + 1
+  int cslices;         // 256-wide column slices
+};
+
+// Workgroup = one tile x one 256-wide d_out slice; wave (rb, ch) takes row block rb and the
+// slice's 128-column block ch.  The tiles are spread over the XCDs in runs of ceil(count / 8)
+// consecutive tiles (mostly of one first adapter), so each XCD's L2 holds few B^T slices.  The
+// B^T slices of a (and b) go straight into LDS in the XOR placement, the rows' h operands and
+// y0 rows are requested behind them.
+template <int RB, bool INDIRECT, bool Y0F32, bool YF32>
+__global__ __launch_bounds__(kGSThreads, 2) void gs_expand_pairs(const TupleArgs a) {
+  constexpr int RP = RB * 16, SPR = 2 * RB;  // 16-byte slots per B^T row
+  constexpr size_t y0b = Y0F32 ? 4 : 2, yb = YF32 ? 4 : 2;
+  constexpr int NY0 = Y0F32 ? 8 : 4;
+  __shared__ alignas(16) uint16_t Bs[2][kTCols * RP];
+  const int nt = *a.ntile, per = (nt + 7) / 8;
+  const int q = blockIdx.x >> 3, wl = q / a.cslices, cs = q - wl * a.cslices;
+  const int w = (blockIdx.x & 7) * per + wl;
+  if (wl >= per || w >= nt) return;
+  const int4 tl = a.tiles[w];
+  const int e = tl.x, r0 = tl.y, r1 = tl.z;
+  const int ea = e / a.K1, eb = e - ea * a.K1;
+  const bool hasb = eb < a.K1 - 1;  // the same in every lane
+  const int nrows = r1 - r0;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n = lane & 15, G = lane >> 4, rb = wave & 3, ch = wave >> 2;
+  const int d_out = a.g.tgt.d_out;
+  const int c0 = cs * kTCols, c1 = min(c0 + kTCols, d_out);
+  const int nb = (c1 - c0) / kColBlock;
+  const int blk = min(ch, nb - 1);
+  const bool has = ch < nb;
+  // 0. the entry of the lane's MFMA row 16 rb + n (rows past the tile repeat its first and are
+  //    not stored): first, since the h and y0 streams wait on it
+  const int rl = 16 * rb + n, rr = r0 + (rl < nrows ? rl : 0);
+  const int tokl = a.etok[rr];
+  const int qal = a.eqa[rr];
+  const int qbl = hasb ? a.eqb[rr] : qal;
+  const char* y0rows[4];
+  char* yrows[4];
+  unsigned vmask = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int t = __shfl(tokl, 4 * G + i, kWave);
+    y0rows[i] = reinterpret_cast<const char*>(a.g.y0) + (size_t)t * d_out * y0b;
+    yrows[i] = reinterpret_cast<char*>(a.g.y) + (size_t)t * d_out * yb;
+    vmask |= (16 * rb + 4 * G + i < nrows ? 1u : 0u) << i;
+  }
+  // the lane's h rows: groups 0, 1 hi of ranks 16u + 8(G & 1) .., groups 2, 3 lo (addresses
+  // formed here, so the loads below wait on nothing)
+  const uint16_t* pa = a.hq + ((size_t)qal * 2 + (G >> 1)) * RP + 8 * (G & 1);
+  const uint16_t* pb = a.hq + ((size_t)qbl * 2 + (G >> 1)) * RP + 8 * (G & 1);
+  __builtin_amdgcn_sched_barrier(0);
+  // 1. the B^T slices: LDS slot P (row P / SPR) holds the row's slot P % SPR XOR gm_b_swz(row)
+  {
+    const int npieces = (c1 - c0) * SPR / 64;
+    for (int h = 0; h < (hasb ? 2 : 1); ++h) {
+      const char* src = reinterpret_cast<const char*>(adapter_B<INDIRECT>(a.g.tgt, h ? eb : ea) + (size_t)c0 * RP);
+      char* dst = reinterpret_cast<char*>(Bs[h]);
+      for (int p = wave; p < npieces; p += 8) {
+        const int P = 64 * p + lane, row = P / SPR, slot = (P % SPR) ^ gm_b_swz<RB>(row);
+        __builtin_amdgcn_global_load_lds(src + ((size_t)row * SPR + slot) * 16, dst + (size_t)p * 1024, 16, 0, 0);
+      }
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  // 2. the A operands
+  u32x4_t hva[RB], hvb[RB];
+#pragma unroll
+  for (int u = 0; u < RB; ++u) hva[u] = ld16(pa + u * 16);
+#pragma unroll
+  for (int u = 0; u < RB; ++u) hvb[u] = ld16(pb + u * 16);
+  __builtin_amdgcn_sched_barrier(0);
+  // 3. the y0 rows
+  RowChunk<Y0F32> yc;
+  load_row_chunk<Y0F32>(yc, y0rows, c0 + blk * kColBlock, n);
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(gs_vmcnt(NY0));  // B pieces and h rows have landed (y0 may not)
+  __syncthreads();
+  f32x4_t o[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) o[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  int b_sl[RB];
+#pragma unroll
+  for (int u = 0; u < RB; ++u) b_sl[u] = (2 * u + (G & 1)) ^ gm_b_swz<RB>(n);
+  const size_t roff = (size_t)(blk * kColBlock + n) * RP;
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+#pragma unroll
+    for (int u = 0; u < RB; ++u) {
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(Bs[0] + roff + (size_t)16 * j * RP + 8 * b_sl[u]);
+      o[j] = mfma16x16x32(as_bf16x8(hva[u]), as_bf16x8(v), o[j]);
+    }
+  if (hasb) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+      for (int u = 0; u < RB; ++u) {
+        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(Bs[1] + roff + (size_t)16 * j * RP + 8 * b_sl[u]);
+        o[j] = mfma16x16x32(as_bf16x8(hvb[u]), as_bf16x8(v), o[j]);
+      }
+  }
+  if (has) epilogue_store<Y0F32, YF32>(o, yc, yrows, c0 + blk * kColBlock, n, vmask);
+}
+
 }  // namespace
 
-hipError_t launch_gs_pass(const GMArgs& g, float* part, uint16_t* hb, bool y0_f32, bool y_f32, bool indirect,
-                          hipStream_t s) {
-  GSArgs a{};
-  a.g = g;
-  a.part = part;
-  a.hb = hb;
-  a.kslices = (g.tgt.d_in + kBSlice - 1) / kBSlice;
-  a.cslices = (g.tgt.d_out + kBSlice - 1) / kBSlice;
-  const int RBv = g.tgt.r_pad / 16;
-  hipError_t err = hipSuccess;
 #define MOLORA_GS_RB(...)                                 \
-  switch (RBv) {                                          \
+  switch (g.tgt.r_pad / 16) {                             \
     case 1: { constexpr int RB = 1; __VA_ARGS__; } break; \
     case 2: { constexpr int RB = 2; __VA_ARGS__; } break; \
     case 3: { constexpr int RB = 3; __VA_ARGS__; } break; \
@@ -278,6 +543,10 @@ hipError_t launch_gs_pass(const GMArgs& g, float* part, uint16_t* hb, bool y0_f3
   }
 #define MOLORA_GS_BOOL(V, NAME, ...) \
   if (V) { constexpr bool NAME = true; __VA_ARGS__; } else { constexpr bool NAME = false; __VA_ARGS__; }
+
+// gs_shrink over (tile, d_in slice), then gs_finalize per tile.
+static hipError_t gs_shrink_finalize(const GMArgs& g, const GSArgs& a, bool indirect, hipStream_t s) {
+  hipError_t err = hipSuccess;
   MOLORA_GS_RB(MOLORA_GS_BOOL(indirect, IND, {
     hipLaunchKernelGGL((gs_shrink<RB, IND>), dim3(g.nwg * a.kslices), dim3(kGSThreads), 0, s, a);
     err = hipGetLastError();
@@ -287,14 +556,85 @@ hipError_t launch_gs_pass(const GMArgs& g, float* part, uint16_t* hb, bool y0_f3
     hipLaunchKernelGGL((gs_finalize<RB>), dim3(g.nwg), dim3(kGSThreads), 0, s, a);
     err = hipGetLastError();
   })
+  return err;
+}
+
+hipError_t launch_gs_pass(const GMArgs& g, float* part, uint16_t* hb, bool y0_f32, bool y_f32, bool indirect,
+                          hipStream_t s) {
+  GSArgs a{};
+  a.g = g;
+  a.part = part;
+  a.hb = hb;
+  a.kslices = (g.tgt.d_in + kBSlice - 1) / kBSlice;
+  a.cslices = (g.tgt.d_out + kBSlice - 1) / kBSlice;
+  hipError_t err = gs_shrink_finalize(g, a, indirect, s);
   if (err != hipSuccess) return err;
   MOLORA_GS_RB(MOLORA_GS_BOOL(indirect, IND, MOLORA_GS_BOOL(y0_f32, Y0F, MOLORA_GS_BOOL(y_f32, YF, {
     hipLaunchKernelGGL((gs_expand<RB, IND, Y0F, YF>), dim3(g.nwg * a.cslices), dim3(kGSThreads), 0, s, a);
     err = hipGetLastError();
   }))))
-#undef MOLORA_GS_RB
-#undef MOLORA_GS_BOOL
   return err;
 }
+
+hipError_t launch_gs_pair_shrink(const GMArgs& g, float* part, uint16_t* hq, bool indirect, hipStream_t s) {
+  if (g.order != nullptr) return hipErrorInvalidValue;  // hq is indexed by the row's grouped position
+  GSArgs a{};
+  a.g = g;
+  a.part = part;
+  a.hq = hq;
+  a.kslices = (g.tgt.d_in + kBSlice - 1) / kBSlice;
+  a.cslices = 0;
+  return gs_shrink_finalize(g, a, indirect, s);
+}
+
+hipError_t launch_tuple_sort(const int32_t* offsets, const int32_t* inv, int N, int k, int K, char* region,
+                             const TupleSortPlan& tp, const GMTiling& tl, hipStream_t s) {
+  if (tl.rows < 16) return hipErrorInvalidValue;  // the tile table holds ceil(N / 16) + keys per pass
+  TupleSortArgs a{};
+  a.offsets = offsets;
+  a.inv = inv;
+  a.N = N; a.k = k; a.K = K; a.nkeys = tp.nkeys;
+  a.m2 = tp.m2; a.kk = tp.kk;
+  a.tile_rows = tl.rows; a.fixed = tl.fixed; a.tmax = tp.tmax;
+  a.tiles = reinterpret_cast<int4*>(region + tp.tiles_off);
+  a.ntile = reinterpret_cast<int32_t*>(region + tp.ntile_off);
+  a.bcnt = reinterpret_cast<int32_t*>(region + tp.bcnt_off);
+  a.toff = reinterpret_cast<int32_t*>(region + tp.toff_off);
+  a.etok = reinterpret_cast<int32_t*>(region + tp.etok_off);
+  a.eqa = reinterpret_cast<int32_t*>(region + tp.eqa_off);
+  a.eqb = reinterpret_cast<int32_t*>(region + tp.eqb_off);
+  const size_t lds = (size_t)(K + 1 + tp.nkeys) * sizeof(int);
+  hipLaunchKernelGGL(tuple_count, dim3(tp.nb), dim3(kTSThreads), lds, s, a);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(tuple_scan, dim3(1), dim3(kTSThreads), 0, s, a, tp.nb);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(tuple_scatter, dim3(tp.nb), dim3(kTSThreads), lds, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_gs_expand_pairs(const GMArgs& g, const char* region, const TupleSortPlan& tp, int m,
+                                  const uint16_t* hq, int K, bool y0_f32, bool y_f32, bool indirect, hipStream_t s) {
+  TupleArgs a{};
+  a.g = g;
+  a.tiles = reinterpret_cast<const int4*>(region + tp.tiles_off) + (size_t)m * tp.tmax;
+  a.ntile = reinterpret_cast<const int32_t*>(region + tp.ntile_off) + m;
+  a.etok = reinterpret_cast<const int32_t*>(region + tp.etok_off);
+  a.eqa = reinterpret_cast<const int32_t*>(region + tp.eqa_off);
+  a.eqb = reinterpret_cast<const int32_t*>(region + tp.eqb_off);
+  a.hq = hq;
+  a.K1 = K + 1;
+  a.cslices = (g.tgt.d_out + kTCols - 1) / kTCols;
+  hipError_t err = hipSuccess;
+  MOLORA_GS_RB(MOLORA_GS_BOOL(indirect, IND, MOLORA_GS_BOOL(y0_f32, Y0F, MOLORA_GS_BOOL(y_f32, YF, {
+    hipLaunchKernelGGL((gs_expand_pairs<RB, IND, Y0F, YF>), dim3(g.nwg * a.cslices), dim3(kGSThreads), 0, s, a);
+    err = hipGetLastError();
+  }))))
+  return err;
+}
+
+#undef MOLORA_GS_RB
+#undef MOLORA_GS_BOOL
 
 }  // namespace molora

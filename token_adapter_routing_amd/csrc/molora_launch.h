@@ -72,6 +72,16 @@ struct GMArgs;  // gm_dev.h
 // (gs_region's layout).
 hipError_t launch_gs_pass(const GMArgs& g, float* part, uint16_t* hb, bool y0_f32, bool y_f32, bool indirect,
                           hipStream_t s);
+// Pair passes (k > 1): the shrink and finalize of one pass over every pair of the dispatch's
+// grouped order (g.order null, g.nwg from gs_region over P rows), writing h by grouped position
+// into hq [P][2][r_pad]; the tuple sort into its region (tuple_sort_plan's layout), with each
+// pass's tiles of tiling tl (rows >= 16); the pair expand of pass m (g: target, y0 / y; g.nwg a
+// multiple of 8, at least the pass's tiles, over 256-wide column slices).
+hipError_t launch_gs_pair_shrink(const GMArgs& g, float* part, uint16_t* hq, bool indirect, hipStream_t s);
+hipError_t launch_tuple_sort(const int32_t* offsets, const int32_t* inv, int N, int k, int K, char* region,
+                             const TupleSortPlan& tp, const GMTiling& tl, hipStream_t s);
+hipError_t launch_gs_expand_pairs(const GMArgs& g, const char* region, const TupleSortPlan& tp, int m,
+                                  const uint16_t* hq, int K, bool y0_f32, bool y_f32, bool indirect, hipStream_t s);
 
 // Per-pair shrink without gate weight or scale (64-row grouped tiles) into hout [P][r_pad] fp32.
 hipError_t launch_pair_shrink_gm(const TargetDev& tgt, bool indirect, const uint16_t* x, const int32_t* offsets,

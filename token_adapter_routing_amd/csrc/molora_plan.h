@@ -155,7 +155,28 @@ struct GSRegion {
   int nwg;
   size_t part_bytes, hb_off, total;
 };
-GSRegion gs_region(int path, long long rows_of_pass, int K, int r_pad, int d_in);
+// with_hb = false: the partials only (a shrink whose finalize writes h by grouped position).
+GSRegion gs_region(int path, long long rows_of_pass, int K, int r_pad, int d_in, bool with_hb = true);
+
+// ---- k > 1 in passes over pairs of a token's routed pairs (the 64-row grouped tiles): pass m
+// applies the token's routed pairs of rank 2m and 2m + 1 together, so a k = 4 call reads and
+// writes the carry twice instead of four times.  A pass's keys are the adapter pairs (a, b),
+// b = K for "no second pair": K (K + 1) keys; the tuples are taken when the keys hold 32 rows
+// on average or more (N >= 32 K (K + 1)), below that the tiles would be mostly short.
+constexpr int kTupleWGTokens = 1024;  // tokens per workgroup of the tuple sort
+bool gm_tuples(int N, int k, int K);
+// The tuple sort's region: per-workgroup key counts bcnt [nb][nkeys] (then the workgroups'
+// first positions), the pass offsets toff [nkeys + 1], each pass's tiles [m2][tmax] (int4: key
+// in the pass, first row, end row) and tile count ntile [m2], and the entries (token, grouped
+// position of the first pair, of the second pair or -1) etok / eqa / eqb [m2 * N]; offsets
+// relative to the region's start.  tmax = ceil(N / 16) + K (K + 1) bounds a pass's tiles for
+// any tile height from 16 rows.
+struct TupleSortPlan {
+  int m2, kk, nkeys, nb;  // passes ceil(k / 2), keys per pass K (K + 1), all keys, workgroups
+  int tmax;
+  size_t bcnt_off, toff_off, tiles_off, ntile_off, etok_off, eqa_off, eqb_off, bytes;
+};
+TupleSortPlan tuple_sort_plan(int N, int k, int K);
 
 struct ApplyPlan {
   int path;
@@ -167,6 +188,10 @@ struct ApplyPlan {
   size_t z_off, z_bytes;          // fp32 carry
   size_t gs_off;                  // 64-row grouped passes: the slice partials and h rows
   GSRegion gs;
+  int tuples;                     // k > 1 in pair passes: the shrink of every pair, then
+  size_t hq_off, hq_bytes;        //   its h by grouped position [P][2][r_pad] bf16 hi / lo,
+  size_t tsort_off;               //   the tuple sort and the carry z
+  TupleSortPlan tsort;
   size_t total;
 };
 ApplyPlan apply_plan(int N, int k, int K, int r_pad, int d_in, int d_out, bool y_f32, int path);

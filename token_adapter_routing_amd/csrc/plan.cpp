@@ -165,15 +165,36 @@ RankSortPlan rank_sort_plan(long long P, int k, int K) {
   return s;
 }
 
-GSRegion gs_region(int path, long long rows_of_pass, int K, int r_pad, int d_in) {
+GSRegion gs_region(int path, long long rows_of_pass, int K, int r_pad, int d_in, bool with_hb) {
   GSRegion g{};
   const int kslices = (d_in + kBSlice - 1) / kBSlice;
   const GMTiling tl = gm_tiling(path, rows_of_pass, K, kslices);
   g.nwg = (int)((tl.max_tiles + 7) / 8 * 8);
   g.part_bytes = (size_t)g.nwg * kslices * 64 * r_pad * sizeof(float);
   g.hb_off = align256(g.part_bytes);
-  g.total = g.hb_off + (size_t)g.nwg * 2 * 64 * r_pad * sizeof(uint16_t);
+  g.total = with_hb ? g.hb_off + (size_t)g.nwg * 2 * 64 * r_pad * sizeof(uint16_t) : g.part_bytes;
   return g;
+}
+
+bool gm_tuples(int N, int k, int K) { return k > 1 && (long long)N >= 32LL * K * (K + 1); }
+
+TupleSortPlan tuple_sort_plan(int N, int k, int K) {
+  TupleSortPlan t{};
+  t.m2 = (k + 1) / 2;
+  t.kk = K * (K + 1);
+  t.nkeys = t.m2 * t.kk;
+  t.nb = std::max(1, (N + kTupleWGTokens - 1) / kTupleWGTokens);
+  const size_t ent = align256((size_t)t.m2 * N * sizeof(int32_t));
+  t.tmax = (N + 15) / 16 + t.kk;
+  t.bcnt_off = 0;
+  t.toff_off = align256((size_t)t.nb * t.nkeys * sizeof(int32_t));
+  t.tiles_off = t.toff_off + align256((size_t)(t.nkeys + 1) * sizeof(int32_t));
+  t.ntile_off = t.tiles_off + align256((size_t)t.m2 * t.tmax * 4 * sizeof(int32_t));
+  t.etok_off = t.ntile_off + align256((size_t)t.m2 * sizeof(int32_t));
+  t.eqa_off = t.etok_off + ent;
+  t.eqb_off = t.eqa_off + ent;
+  t.bytes = t.eqb_off + ent;
+  return t;
 }
 
 ApplyPlan apply_plan(int N, int k, int K, int r_pad, int d_in, int d_out, bool y_f32, int path) {
@@ -191,6 +212,19 @@ ApplyPlan apply_plan(int N, int k, int K, int r_pad, int d_in, int d_out, bool y
       a.gs_off = 0;
       a.gs = gs_region(a.path, P, K, r_pad, d_in);
       a.total = a.gs.total;
+      return a;
+    }
+    if (gm_tuples(N, k, K)) {
+      a.tuples = 1;
+      a.gs_off = 0;
+      a.gs = gs_region(a.path, P, K, r_pad, d_in, false);  // the shrink over every pair
+      a.hq_off = align256(a.gs.total);
+      a.hq_bytes = align256((size_t)P * 2 * r_pad * sizeof(uint16_t));
+      a.tsort_off = a.hq_off + a.hq_bytes;
+      a.tsort = tuple_sort_plan(N, k, K);
+      a.z_off = align256(a.tsort_off + a.tsort.bytes);
+      a.z_bytes = a.tsort.m2 > 1 ? zb : 0;
+      a.total = a.z_off + a.z_bytes;
       return a;
     }
     a.sort_off = 0;
