@@ -725,14 +725,15 @@ def row_stress(m, torch, dev, bf, f32, reps):
 def row_tiling(m, torch, dev, bf, f32, i32, reps):
     """Fixed against adaptive tiling of the 64-row grouped kernel (the pages' Table 9): adapter
     usage mixes 25% each, 80/10/5/5 and 95/2/2/1 (one adapter per token, 4 adapters of rank 64,
-    d=4096) at 2048 and 16384 tokens, and the stress workload's Zipf top-k (16 adapters of rank
-    64, 16384 tokens, k = 1..4).  Each entry: dispatch (and top-k) + apply as one graph."""
+    d=4096) at 512, 2048 and 16384 tokens (the adaptive bound is 16 rows at 512 tokens, 64 from
+    2048 on), and the stress workload's Zipf top-k (16 adapters of rank 64, 16384 tokens,
+    k = 1..4).  Each entry: dispatch (and top-k) + apply as one graph."""
     import synth
     out = {"workload": "grouped 64-row kernel, MOLORA_PATH_GROUPED (adaptive) vs MOLORA_PATH_GROUPED_FIXED",
            "mixes": {}, "zipf_stress": {}}
     mixes = {"uniform_25": (0.25, 0.25, 0.25, 0.25), "80_10_5_5": (0.8, 0.1, 0.05, 0.05),
              "95_2_2_1": (0.95, 0.02, 0.02, 0.01)}
-    for N in (2048, 16384):
+    for N in (512, 2048, 16384):
         for name, probs in mixes.items():
             c = synth.mixed_batch(N, probs, case_id=6, sub=N)
             t = c.targets[0]

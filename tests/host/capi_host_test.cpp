@@ -192,6 +192,14 @@ hipError_t launch_backward(const BackwardLaunch& a, hipStream_t) {
   g_last_backward_outputs = (a.dA != nullptr) + 2 * (a.dB != nullptr) + 4 * (a.dw != nullptr);
   const bool need_h = a.dB != nullptr || a.dw != nullptr, need_g = a.dA != nullptr || a.dw != nullptr;
   if (P > 0) {
+    // the split shrinks' partials: every tile of the bound, every 512-wide slice of d_in (h) or d_out (g)
+    for (int d : {need_h ? a.tgt.d_in : 0, need_g ? a.tgt.d_out : 0}) {
+      if (d == 0) continue;
+      const int kslices = (d + kBSlice - 1) / kBSlice;
+      const GMTiling tl = gm_tiling(kPathGrouped, P, a.K, kslices);
+      const long long nwg = (tl.max_tiles + 7) / 8 * 8;
+      write_span<float>(a.ws + p.gs_off, 0, (size_t)nwg * kslices * 64 * a.tgt.r_pad, "bwd shrink partials");
+    }
     if (need_h) write_span<float>(a.ws + p.h_off, 0, (size_t)p.nsh * P * a.tgt.r_pad, "bwd h");
     if (need_g) write_span<float>(a.ws + p.g_off, 0, (size_t)p.nsg * P * a.tgt.r_pad, "bwd g");
     const size_t planes = (size_t)p.nchunks * 2 * bwd_s_chunk_elems(a.tgt.r_pad, p.Qc);

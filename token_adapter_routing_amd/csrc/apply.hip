@@ -785,13 +785,6 @@ __global__ __launch_bounds__(kSThreads) void split_expand(StepArgs a, SplitGeom 
   if (has1) epilogue_store<Y0F32, YF32>(o1, yc1, yrows, c0 + b1 * kColBlock, n, 0xFu);
 }
 
-// Shrink only: unscaled h of every grouped pair (the backward's h and g).
-template <int RB, bool INDIRECT>
-__global__ __launch_bounds__(kGMThreads) void shrink_gm(GMArgs a) {
-  __shared__ GMLds<RB> L;
-  gm_shrink_tile<RB, INDIRECT>(a, L);
-}
-
 // Key of grouped position q: (rank of its pair among the token's routed pairs) * K + adapter;
 // weight: its gate weight.  Ranking the routed pairs (instead of using the slot index) makes
 // pass 0 hold every token's first routed pair, so only pass 0 reads y0.
@@ -1393,10 +1386,6 @@ static hipError_t launch_expand_tok_t(const ExpandArgs& ea, int grid, hipStream_
 #define MOLORA_DISPATCH_BOOL(V, NAME, ...) \
   if (V) { constexpr bool NAME = true; __VA_ARGS__; } else { constexpr bool NAME = false; __VA_ARGS__; }
 
-hipError_t launch_pair_shrink_gm(const TargetDev& tgt, bool indirect, const uint16_t* x, const int32_t* offsets,
-                                 const int32_t* perm, int K, int k, long long P, float* hout, hipStream_t s,
-                                 bool fixed_tiles, uint16_t* hs_out, const float* perm_w, float scale);
-
 // Rank sort of the grouped pairs for k > 1 passes, in the region of rank_sort_plan() at wsb
 // (counts2 and offsets2, perm2 and w2 = the order and weights, the chip-wide sort's counts).
 struct RankSort {
@@ -1798,27 +1787,6 @@ hipError_t launch_step_vocab(const StepVocabLaunch& a, hipStream_t s) {
       MOLORA_DISPATCH_BOOL(a.apply.y_f32, YF, err = (launch_step_t<RB, IND, Y0F, YF>(sa, grid, s))))));
   return err;
 }
-
-// --------------------------------------------------------------------------------------
-// Per-pair shrink without gate weight or scale on the 64-row grouped tiles: hout[q] = x_t A_e
-// of grouped position q (the backward's h and g).
-hipError_t launch_pair_shrink_gm(const TargetDev& tgt, bool indirect, const uint16_t* x, const int32_t* offsets,
-                                 const int32_t* perm, int K, int k, long long P, float* hout, hipStream_t s) {
-  GMArgs ga{};
-  ga.tgt = tgt; ga.x = x; ga.k = k; ga.perm = perm; ga.offsets = offsets; ga.key0 = 0; ga.nkeys = K;
-  ga.order = nullptr; ga.hout = hout;
-  const GMTiling tl = gm_tiling(kPathGrouped, P, K, 1);
-  ga.tile_rows = tl.rows; ga.fixed = tl.fixed;
-  ga.nwg = (int)((tl.max_tiles + 7) / 8 * 8);
-  const int RBv = tgt.r_pad / 16;
-  hipError_t err = hipSuccess;
-  MOLORA_DISPATCH_RB(RBv, MOLORA_DISPATCH_BOOL(indirect, IND, {
-    hipLaunchKernelGGL((shrink_gm<RB, IND>), dim3(ga.nwg), dim3(kGMThreads), 0, s, ga);
-    err = hipGetLastError();
-  }));
-  return err;
-}
-
 
 // --------------------------------------------------------------------------------------
 // Hot-set relayout of one adapter.

@@ -345,14 +345,15 @@ hipError_t launch_backward(const BackwardLaunch& a, hipStream_t s) {
   float* gp = need_g ? reinterpret_cast<float*>(a.ws + plan.g_off) : nullptr;
   uint16_t* sa = a.dA != nullptr ? reinterpret_cast<uint16_t*>(a.ws + plan.sa_off) : nullptr;
   uint16_t* sb = a.dB != nullptr ? reinterpret_cast<uint16_t*>(a.ws + plan.sb_off) : nullptr;
+  float* gsp = reinterpret_cast<float*>(a.ws + plan.gs_off);  // the shrinks' slice partials
   hipError_t err = hipSuccess;
   if (P > 0) {
     if (need_h) {
-      err = launch_pair_shrink_gm(a.tgt, a.indirect, a.x, a.offsets, a.perm, a.K, a.k, P, hp, s);
+      err = launch_pair_shrink_gm(a.tgt, a.indirect, a.x, a.offsets, a.perm, a.K, a.k, P, hp, gsp, s);
       if (err != hipSuccess) return err;
     }
     if (need_g) {
-      err = launch_pair_shrink_gm(a.tgt_t, a.indirect_t, a.gy, a.offsets, a.perm, a.K, a.k, P, gp, s);
+      err = launch_pair_shrink_gm(a.tgt_t, a.indirect_t, a.gy, a.offsets, a.perm, a.K, a.k, P, gp, gsp, s);
       if (err != hipSuccess) return err;
     }
     BwdPairArgs pa;

@@ -35,6 +35,7 @@ struct GSArgs {
   float* part;     // [nwg][kslices][64][r_pad] fp32
   uint16_t* hb;    // [nwg][2][64][r_pad] bf16 hi / lo of the weighted h
   uint16_t* hq;    // instead of hb (a pass over every pair, no order): [q][2][r_pad] by grouped position
+  float* hout;     // instead of hb: the unscaled h of grouped position q, [q][r_pad] fp32
   int kslices, cslices;
 };
 
@@ -140,13 +141,13 @@ __global__ __launch_bounds__(kGSThreads) void gs_finalize(const GSArgs a) {
   if (!gm_locate(a.g, w, e, r0, r1)) return;
   const int nrows = r1 - r0;
   const float* base = a.part + (size_t)w * a.kslices * kGMRows * RP;
-  uint16_t* hb = a.hq == nullptr ? a.hb + (size_t)w * 2 * kGMRows * RP : nullptr;
+  uint16_t* hb = a.hb != nullptr ? a.hb + (size_t)w * 2 * kGMRows * RP : nullptr;
 #pragma unroll
   for (int j = 0; j < QPT; ++j) {
     const int v = j * kGSThreads + (int)threadIdx.x;
     if (v >= kGMRows * RQ) break;
     const int row = v / RQ, rk = 4 * (v % RQ);
-    const float wt = row < nrows ? a.g.wts[r0 + row] * a.g.scale : 0.f;
+    const float wt = a.hout != nullptr ? 1.f : row < nrows ? a.g.wts[r0 + row] * a.g.scale : 0.f;
     const float* src = base + (size_t)row * RP + rk;
     float sum[4] = {0.f, 0.f, 0.f, 0.f};
     for (int s0 = 0; s0 < a.kslices; s0 += KS) {
@@ -159,6 +160,12 @@ __global__ __launch_bounds__(kGSThreads) void gs_finalize(const GSArgs a) {
         if (s0 + s < a.kslices)
 #pragma unroll
           for (int c = 0; c < 4; ++c) sum[c] += __uint_as_float(pv[s][c]);
+    }
+    if (a.hout != nullptr) {
+      if (row < nrows)
+        *reinterpret_cast<u32x4_t*>(a.hout + (size_t)(r0 + row) * RP + rk) =
+            u32x4_t{__float_as_uint(sum[0]), __float_as_uint(sum[1]), __float_as_uint(sum[2]), __float_as_uint(sum[3])};
+      continue;
     }
     uint32_t hi2[2], lo2[2];
 #pragma unroll
@@ -352,9 +359,16 @@ __global__ __launch_bounds__(kTSThreads) void tuple_scan(const TupleSortArgs a, 
   __shared__ int wsum[kTSThreads / kWave];
   const int per = (a.nkeys + kTSThreads - 1) / kTSThreads;
   const int k0 = min((int)threadIdx.x * per, a.nkeys), k1 = min(k0 + per, a.nkeys);
+  constexpr int CH = 16;  // counts requested together (their loads do not wait on each other)
   int tot = 0;
   for (int key = k0; key < k1; ++key)
-    for (int b = 0; b < nb; ++b) tot += a.bcnt[(size_t)b * a.nkeys + key];
+    for (int b0 = 0; b0 < nb; b0 += CH) {
+      int cv[CH];
+#pragma unroll
+      for (int j = 0; j < CH; ++j) cv[j] = b0 + j < nb ? a.bcnt[(size_t)(b0 + j) * a.nkeys + key] : 0;
+#pragma unroll
+      for (int j = 0; j < CH; ++j) tot += cv[j];
+    }
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int incl = wave_incl_scan(tot, lane);
   if (lane == kWave - 1) wsum[wave] = incl;
@@ -363,25 +377,33 @@ __global__ __launch_bounds__(kTSThreads) void tuple_scan(const TupleSortArgs a, 
   for (int w = 0; w < wave; ++w) pos += wsum[w];
   for (int key = k0; key < k1; ++key) {
     a.toff[key] = pos;
-    for (int b = 0; b < nb; ++b) {
-      const size_t i = (size_t)b * a.nkeys + key;
-      const int c = a.bcnt[i];
-      a.bcnt[i] = pos;
-      pos += c;
+    for (int b0 = 0; b0 < nb; b0 += CH) {
+      int cv[CH];
+#pragma unroll
+      for (int j = 0; j < CH; ++j) cv[j] = b0 + j < nb ? a.bcnt[(size_t)(b0 + j) * a.nkeys + key] : 0;
+#pragma unroll
+      for (int j = 0; j < CH; ++j) {
+        if (b0 + j < nb) a.bcnt[(size_t)(b0 + j) * a.nkeys + key] = pos;
+        pos += cv[j];
+      }
     }
   }
   if (threadIdx.x == kTSThreads - 1) a.toff[a.nkeys] = pos;  // the last thread ends at the total
   __syncthreads();
-  // each pass's tiles: key c rows -> nt = ceil(c / tile_rows) tiles, balanced (or fixed
-  // tile_rows rows), numbered key by key; thread i takes a run of consecutive keys of the pass
+  // each pass's tiles: key c rows -> nt = ceil(c / tile_rows) tiles, balanced (the first c % nt
+  // tiles one row taller) or fixed (tile_rows rows but the last), numbered key by key; thread i
+  // takes a run of consecutive keys of the pass
   const int M = a.tile_rows;
   const int per2 = (a.kk + kTSThreads - 1) / kTSThreads;
   for (int m = 0; m < a.m2; ++m) {
     const int q0 = min((int)threadIdx.x * per2, a.kk), q1 = min(q0 + per2, a.kk);
-    int nt = 0;
-    for (int q = q0; q < q1; ++q) {
-      const int c = a.toff[m * a.kk + q + 1] - a.toff[m * a.kk + q];
-      nt += (c + M - 1) / M;
+    int nt = 0, sq[2], cq[2];  // per2 <= 2: K (K + 1) <= 2 kTSThreads
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int q = q0 + j;
+      sq[j] = q < q1 ? a.toff[m * a.kk + q] : 0;
+      cq[j] = q < q1 ? a.toff[m * a.kk + q + 1] - sq[j] : 0;
+      nt += (cq[j] + M - 1) / M;
     }
     const int tincl = wave_incl_scan(nt, lane);
     __syncthreads();  // wsum's previous readers are done
@@ -389,13 +411,16 @@ __global__ __launch_bounds__(kTSThreads) void tuple_scan(const TupleSortArgs a, 
     __syncthreads();
     int w = tincl - nt;
     for (int v = 0; v < wave; ++v) w += wsum[v];
-    for (int q = q0; q < q1; ++q) {
-      const int s0 = a.toff[m * a.kk + q], c = a.toff[m * a.kk + q + 1] - s0;
-      const int ntq = (c + M - 1) / M;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int q = q0 + j, s0 = sq[j], c = cq[j];
+      const int ntq = (c + M - 1) / M;  // 0 past the run
+      const int h = a.fixed ? M : (ntq > 0 ? c / ntq : 0), rem = a.fixed ? 0 : c - h * max(ntq, 1);
+      int r0 = s0;
       for (int i = 0; i < ntq; ++i, ++w) {
-        const int r0 = a.fixed ? s0 + i * M : s0 + (int)((long long)c * i / ntq);
-        const int r1 = a.fixed ? min(s0 + c, r0 + M) : s0 + (int)((long long)c * (i + 1) / ntq);
+        const int r1 = min(s0 + c, r0 + h + (i < rem ? 1 : 0));
         a.tiles[(size_t)m * a.tmax + w] = make_int4(q, r0, r1, 0);
+        r0 = r1;
       }
     }
     if (threadIdx.x == kTSThreads - 1) a.ntile[m] = w;  // the last thread ends at the pass's count
@@ -587,9 +612,27 @@ hipError_t launch_gs_pair_shrink(const GMArgs& g, float* part, uint16_t* hq, boo
   return gs_shrink_finalize(g, a, indirect, s);
 }
 
+hipError_t launch_pair_shrink_gm(const TargetDev& tgt, bool indirect, const uint16_t* x, const int32_t* offsets,
+                                 const int32_t* perm, int K, int k, long long P, float* hout, float* part,
+                                 hipStream_t s) {
+  const int kslices = (tgt.d_in + kBSlice - 1) / kBSlice;
+  const GMTiling tl = gm_tiling(kPathGrouped, P, K, kslices);
+  GMArgs g{};
+  g.tgt = tgt; g.x = x; g.k = k; g.perm = perm; g.offsets = offsets; g.key0 = 0; g.nkeys = K; g.order = nullptr;
+  g.tile_rows = tl.rows; g.fixed = tl.fixed;
+  g.nwg = gs_region(kPathGrouped, P, K, tgt.r_pad, tgt.d_in, false).nwg;
+  GSArgs a{};
+  a.g = g;
+  a.part = part;
+  a.hout = hout;
+  a.kslices = kslices;
+  return gs_shrink_finalize(g, a, indirect, s);
+}
+
 hipError_t launch_tuple_sort(const int32_t* offsets, const int32_t* inv, int N, int k, int K, char* region,
                              const TupleSortPlan& tp, const GMTiling& tl, hipStream_t s) {
-  if (tl.rows < 16) return hipErrorInvalidValue;  // the tile table holds ceil(N / 16) + keys per pass
+  // the tile table holds ceil(N / 16) + keys per pass; the scan's threads take 2 keys of a pass at most
+  if (tl.rows < 16 || tp.kk > 2 * kTSThreads) return hipErrorInvalidValue;
   TupleSortArgs a{};
   a.offsets = offsets;
   a.inv = inv;

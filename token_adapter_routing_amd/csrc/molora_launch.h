@@ -83,9 +83,12 @@ hipError_t launch_tuple_sort(const int32_t* offsets, const int32_t* inv, int N, 
 hipError_t launch_gs_expand_pairs(const GMArgs& g, const char* region, const TupleSortPlan& tp, int m,
                                   const uint16_t* hq, int K, bool y0_f32, bool y_f32, bool indirect, hipStream_t s);
 
-// Per-pair shrink without gate weight or scale (64-row grouped tiles) into hout [P][r_pad] fp32.
+// Per-pair shrink without gate weight or scale into hout [P][r_pad] fp32 by grouped position:
+// the split shrink and finalize over the 64-row tiles of the dispatch's grouped order; part
+// holds the slice partials (gs_region(kPathGrouped, P, K, r_pad, d_in, false).part_bytes).
 hipError_t launch_pair_shrink_gm(const TargetDev& tgt, bool indirect, const uint16_t* x, const int32_t* offsets,
-                                 const int32_t* perm, int K, int k, long long P, float* hout, hipStream_t s);
+                                 const int32_t* perm, int K, int k, long long P, float* hout, float* part,
+                                 hipStream_t s);
 
 // Backward of the routed LoRA except dx: dA, dB, dw (any may be NULL) from x, gy and the
 // forward routing; ws holds bwd_plan() for these shapes.

@@ -225,6 +225,7 @@ struct BwdPlan {
   long long nchunks;       // upper bound on chunks: ceil(P / Qc) + K
   size_t h_off, h_bytes;   // h partials [nsh][P][r_pad] fp32
   size_t g_off, g_bytes;   // g partials [nsg][P][r_pad] fp32
+  size_t gs_off, gs_bytes; // the h and g shrinks' slice partials (one shrink at a time)
   size_t sa_off, sb_off, s_bytes;  // hi/lo chunks of scale*w*g (for dA) and scale*w*h (for dB)
   size_t part_off, part_bytes;     // weight-gradient partials, shared by dA then dB
   size_t apply_off, apply_bytes;   // dx: the apply on the transposed adapters

@@ -300,7 +300,7 @@ int wgrad_chunk(long long P, int D) {
 BwdPlan bwd_plan(int N, int k, int K, int r_pad, int d_in, int d_out, bool dx_f32, int dx_path) {
   BwdPlan b{};
   const long long P = (long long)N * k;
-  b.nsh = 1;  // the grouped shrink-only kernel reduces d whole per tile
+  b.nsh = 1;  // the split shrink's finalize sums the slices per row
   b.nsg = 1;
   b.Qc = wgrad_chunk(P, std::min(d_in, d_out));
   b.nchunks = (P + b.Qc - 1) / b.Qc + K;
@@ -311,6 +311,11 @@ BwdPlan bwd_plan(int N, int k, int K, int r_pad, int d_in, int d_out, bool dx_f3
   b.g_off = off;
   b.g_bytes = align256((size_t)b.nsg * P * r_pad * sizeof(float));
   off += b.g_bytes;
+  b.gs_off = off;
+  b.gs_bytes = P > 0 ? align256(std::max(gs_region(kPathGrouped, P, K, r_pad, d_in, false).part_bytes,
+                                         gs_region(kPathGrouped, P, K, r_pad, d_out, false).part_bytes))
+                     : 0;
+  off += b.gs_bytes;
   b.s_bytes = align256((size_t)b.nchunks * 2 * bwd_s_chunk_elems(r_pad, b.Qc) * sizeof(uint16_t));
   b.sa_off = off;
   off += b.s_bytes;
