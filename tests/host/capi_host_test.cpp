@@ -197,7 +197,8 @@ hipError_t launch_backward(const BackwardLaunch& a, hipStream_t) {
       if (d == 0) continue;
       const int kslices = (d + kBSlice - 1) / kBSlice;
       const GMTiling tl = gm_tiling(kPathGrouped, P, a.K, kslices);
-      const long long nwg = (tl.max_tiles + 7) / 8 * 8;
+      const long long nwg = (tl.max_tiles + 15) / 16 * 16;  // whole XCD rounds of tile pairs
+      CHECK(nwg == gs_region(kPathGrouped, P, a.K, a.tgt.r_pad, d, false).nwg, "bwd shrink tiles");
       write_span<float>(a.ws + p.gs_off, 0, (size_t)nwg * kslices * 64 * a.tgt.r_pad, "bwd shrink partials");
     }
     if (need_h) write_span<float>(a.ws + p.h_off, 0, (size_t)p.nsh * P * a.tgt.r_pad, "bwd h");

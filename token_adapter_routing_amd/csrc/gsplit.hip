@@ -55,22 +55,24 @@ __device__ __forceinline__ int gs_token(const GMArgs& g, int r0, int nrows, int 
   return g.perm[q] / g.k;
 }
 
-template <int RB, bool INDIRECT>
-__global__ __launch_bounds__(kGSThreads, 2) void gs_shrink(const GSArgs a) {
-  __shared__ alignas(16) uint16_t As[kGSSteps * 4 * RB * 512];  // [step][chunk][u] pieces of 1 KB
-  int w, sl, e, r0, r1;
-  gs_tile_slice(a.g, a.kslices, w, sl);
-  if (!gm_locate(a.g, w, e, r0, r1)) return;
-  const int nrows = r1 - r0;
+// One adapter's A slice against the x rows of one tile, or of two tiles of that adapter (TWO):
+// every A operand read from LDS then feeds both tiles' MFMAs, so a workgroup streams the slice
+// once for up to 128 rows.  The two halves of the slice's steps meet in LDS; half 0 stores the
+// partials of each tile at part[tile][slice].
+template <int RB, bool INDIRECT, bool TWO>
+__device__ __forceinline__ void gs_shrink_rows(const GSArgs& a, uint16_t* As, int e, int sl, const int (&wt)[2],
+                                               const int (&r0)[2], const int (&nrows)[2]) {
+  constexpr int T = TWO ? 2 : 1;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15, G = lane >> 4, rb = wave & 3, kh = wave >> 2;
   const int d_in = a.g.tgt.d_in, r_pad = a.g.tgt.r_pad;
   const int S = d_in / kStepK;
   const int s0 = sl * kGSSteps, s1 = min(s0 + kGSSteps, S), ns = s1 - s0;
   constexpr int piece = RB * 16 * kStepK;  // elements of one step's pieces
-  // the x row of the lane's MFMA row (16 rb + n): its token first (the HBM stream waits on it)
-  const int tok = gs_token(a.g, r0, nrows, 16 * rb + n);
-  const uint16_t* xp = a.g.x + (size_t)tok * d_in + 8 * G;
+  // the x rows of the lane's MFMA row (16 rb + n) in each tile: tokens first (the HBM stream waits on them)
+  const uint16_t* xp[T];
+#pragma unroll
+  for (int t = 0; t < T; ++t) xp[t] = a.g.x + (size_t)gs_token(a.g, r0[t], nrows[t], 16 * rb + n) * d_in + 8 * G;
   __builtin_amdgcn_sched_barrier(0);
   // the adapter's A slice straight into LDS
   {
@@ -80,21 +82,25 @@ __global__ __launch_bounds__(kGSThreads, 2) void gs_shrink(const GSArgs a) {
       __builtin_amdgcn_global_load_lds(src + off + 16 * lane, dst + off, 16, 0, 0);
   }
   __builtin_amdgcn_sched_barrier(0);
-  // this wave's half of the slice (2 steps) of the x row
+  // this wave's half of the slice (2 steps) of each x row
   const int w0 = min(s0 + 2 * kh, s1), w1 = min(w0 + 2, s1);
-  u32x4_t xv[2][4];
+  u32x4_t xv[T][2][4];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int st = max(min(w0 + i, w1 - 1), s0);
+  for (int t = 0; t < T; ++t)
 #pragma unroll
-    for (int c = 0; c < 4; ++c) xv[i][c] = ld16_nt(xp + (size_t)st * kStepK + 32 * c);
-  }
+    for (int i = 0; i < 2; ++i) {
+      const int st = max(min(w0 + i, w1 - 1), s0);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) xv[t][i][c] = ld16_nt(xp[t] + (size_t)st * kStepK + 32 * c);
+    }
   __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_waitcnt(gs_vmcnt(8));  // this wave's A pieces have landed (only x is younger)
+  __builtin_amdgcn_s_waitcnt(gs_vmcnt(8 * T));  // this wave's A pieces have landed (only x is younger)
   __syncthreads();
-  f32x4_t acc[RB];
+  f32x4_t acc[T][RB];
 #pragma unroll
-  for (int u = 0; u < RB; ++u) acc[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < T; ++t)
+#pragma unroll
+    for (int u = 0; u < RB; ++u) acc[t][u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     if (w0 + i < w1) {
@@ -105,7 +111,8 @@ __global__ __launch_bounds__(kGSThreads, 2) void gs_shrink(const GSArgs a) {
         for (int u = 0; u < RB; ++u) {
           // lane (n, G) takes its 16 bytes at position 4n + G of the 1 KB piece (slab swizzle)
           const u32x4_t av = *reinterpret_cast<const u32x4_t*>(ap + ((c * RB + u) * 64 + 4 * n + G) * 8);
-          acc[u] = mfma16x16x32(as_bf16x8(xv[i][c]), as_bf16x8(av), acc[u]);
+#pragma unroll
+          for (int t = 0; t < T; ++t) acc[t][u] = mfma16x16x32(as_bf16x8(xv[t][i][c]), as_bf16x8(av), acc[t][u]);
         }
     }
   }
@@ -113,21 +120,51 @@ __global__ __launch_bounds__(kGSThreads, 2) void gs_shrink(const GSArgs a) {
   __syncthreads();
   constexpr int kRS = RB * 16 + 4;
   float* red = reinterpret_cast<float*>(As);
-  static_assert(sizeof(float) * 4 * 16 * kRS <= sizeof(As), "partial sums fit in the A pieces' LDS");
+  static_assert(sizeof(float) * 2 * 4 * 16 * kRS <= sizeof(uint16_t) * kGSSteps * 4 * RB * 512,
+                "two tiles' partial sums fit in the A pieces' LDS");
   if (kh == 1) {
 #pragma unroll
-    for (int u = 0; u < RB; ++u)
+    for (int t = 0; t < T; ++t)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) red[(rb * 16 + 4 * G + i) * kRS + u * 16 + n] = acc[u][i];
+      for (int u = 0; u < RB; ++u)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) red[((t * 4 + rb) * 16 + 4 * G + i) * kRS + u * 16 + n] = acc[t][u][i];
   }
   __syncthreads();
   if (kh == 0) {
-    float* dst = a.part + (((size_t)w * a.kslices + sl) * kGMRows + 16 * rb) * r_pad;
 #pragma unroll
-    for (int u = 0; u < RB; ++u)
+    for (int t = 0; t < T; ++t) {
+      float* dst = a.part + (((size_t)wt[t] * a.kslices + sl) * kGMRows + 16 * rb) * r_pad;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        dst[(size_t)(4 * G + i) * r_pad + u * 16 + n] = acc[u][i] + red[(rb * 16 + 4 * G + i) * kRS + u * 16 + n];
+      for (int u = 0; u < RB; ++u)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          dst[(size_t)(4 * G + i) * r_pad + u * 16 + n] =
+              acc[t][u][i] + red[((t * 4 + rb) * 16 + 4 * G + i) * kRS + u * 16 + n];
+    }
+  }
+}
+
+// Workgroup = tiles (2j, 2j + 1) of its XCD's run x one 512-wide d_in slice (grid nwg / 2 x
+// kslices; nwg a multiple of 16).  Two tiles of one adapter share the A slice; a pair that
+// straddles two adapters runs one tile after the other.
+template <int RB, bool INDIRECT>
+__global__ __launch_bounds__(kGSThreads, 2) void gs_shrink(const GSArgs a) {
+  __shared__ alignas(16) uint16_t As[kGSSteps * 4 * RB * 512];  // [step][chunk][u] pieces of 1 KB
+  const int xcd = blockIdx.x & 7, q = blockIdx.x >> 3;
+  const int j = q / a.kslices, sl = q - j * a.kslices;
+  const int wa = xcd * (a.g.nwg >> 3) + 2 * j;
+  int ea, ra0, ra1, eb, rb0, rb1;
+  if (!gm_locate(a.g, wa, ea, ra0, ra1)) return;
+  const bool hasb = gm_locate(a.g, wa + 1, eb, rb0, rb1);
+  if (hasb && eb == ea) {
+    gs_shrink_rows<RB, INDIRECT, true>(a, As, ea, sl, {wa, wa + 1}, {ra0, rb0}, {ra1 - ra0, rb1 - rb0});
+    return;
+  }
+  gs_shrink_rows<RB, INDIRECT, false>(a, As, ea, sl, {wa, 0}, {ra0, 0}, {ra1 - ra0, 1});
+  if (hasb) {
+    __syncthreads();  // every wave has read its partial sums out of the A pieces' LDS
+    gs_shrink_rows<RB, INDIRECT, false>(a, As, eb, sl, {wa + 1, 0}, {rb0, 0}, {rb1 - rb0, 1});
   }
 }
 
@@ -571,9 +608,10 @@ __global__ __launch_bounds__(kGSThreads, 2) void gs_expand_pairs(const TupleArgs
 
 // gs_shrink over (tile, d_in slice), then gs_finalize per tile.
 static hipError_t gs_shrink_finalize(const GMArgs& g, const GSArgs& a, bool indirect, hipStream_t s) {
+  if (g.nwg % 16 != 0) return hipErrorInvalidValue;  // tile pairs within each XCD's run
   hipError_t err = hipSuccess;
   MOLORA_GS_RB(MOLORA_GS_BOOL(indirect, IND, {
-    hipLaunchKernelGGL((gs_shrink<RB, IND>), dim3(g.nwg * a.kslices), dim3(kGSThreads), 0, s, a);
+    hipLaunchKernelGGL((gs_shrink<RB, IND>), dim3(g.nwg / 2 * a.kslices), dim3(kGSThreads), 0, s, a);
     err = hipGetLastError();
   }))
   if (err != hipSuccess) return err;

@@ -150,7 +150,8 @@ RankSortPlan rank_sort_plan(long long P, int k, int K);
 // where z is the fp32 [N][d_out] carry of the k > 1 passes when y is bf16.
 // ---- grouped tiles split over 512-wide slices (a pass of the 64-row grouped tiles in three
 // launches): the pass's slice partials [nwg][kslices][64][r_pad] fp32, then its h rows
-// [nwg][2][64][r_pad] bf16; nwg = the pass's tile bound rounded up to whole XCD rounds.
+// [nwg][2][64][r_pad] bf16; nwg = the pass's tile bound rounded up to a multiple of 16 (whole
+// XCD rounds of tile pairs).
 struct GSRegion {
   int nwg;
   size_t part_bytes, hb_off, total;

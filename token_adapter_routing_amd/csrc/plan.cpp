@@ -169,7 +169,7 @@ GSRegion gs_region(int path, long long rows_of_pass, int K, int r_pad, int d_in,
   GSRegion g{};
   const int kslices = (d_in + kBSlice - 1) / kBSlice;
   const GMTiling tl = gm_tiling(path, rows_of_pass, K, kslices);
-  g.nwg = (int)((tl.max_tiles + 7) / 8 * 8);
+  g.nwg = (int)((tl.max_tiles + 15) / 16 * 16);  // tile pairs within each XCD's run
   g.part_bytes = (size_t)g.nwg * kslices * 64 * r_pad * sizeof(float);
   g.hb_off = align256(g.part_bytes);
   g.total = with_hb ? g.hb_off + (size_t)g.nwg * 2 * 64 * r_pad * sizeof(uint16_t) : g.part_bytes;
