@@ -287,29 +287,27 @@ __global__ __launch_bounds__(kGSThreads, 2) void gs_expand(const GSArgs a) {
   __builtin_amdgcn_sched_barrier(0);
   __builtin_amdgcn_s_waitcnt(gs_vmcnt(NY0));  // B pieces and h rows have landed (y0 may not)
   __syncthreads();
-  f32x4_t o0[8], o1[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    o0[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    o1[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  }
   // lane's B^T slots: row 16j + n of the block, slot 2u + (G & 1), XOR-placed
   int b_sl[RB];
 #pragma unroll
   for (int u = 0; u < RB; ++u) b_sl[u] = (2 * u + (G & 1)) ^ gm_b_swz<RB>(n);
-  const uint16_t* bl0 = Bs + (size_t)(b0 * kColBlock + n) * RP;
-  const uint16_t* bl1 = Bs + (size_t)(b1 * kColBlock + n) * RP;
+  // the two column blocks one after the other (one set of accumulators: two workgroups per CU)
+  auto block = [&](int b, const RowChunk<Y0F32>& yc, bool hs) {
+    const uint16_t* bl = Bs + (size_t)(b * kColBlock + n) * RP;
+    f32x4_t o[8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j)
+    for (int j = 0; j < 8; ++j) o[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int u = 0; u < RB; ++u) {
-      const u32x4_t v0 = *reinterpret_cast<const u32x4_t*>(bl0 + (size_t)16 * j * RP + 8 * b_sl[u]);
-      const u32x4_t v1 = *reinterpret_cast<const u32x4_t*>(bl1 + (size_t)16 * j * RP + 8 * b_sl[u]);
-      o0[j] = mfma16x16x32(as_bf16x8(hv[u]), as_bf16x8(v0), o0[j]);
-      o1[j] = mfma16x16x32(as_bf16x8(hv[u]), as_bf16x8(v1), o1[j]);
-    }
-  if (has0) epilogue_store<Y0F32, YF32>(o0, yc0, yrows, c0 + b0 * kColBlock, n, vmask);
-  if (has1) epilogue_store<Y0F32, YF32>(o1, yc1, yrows, c0 + b1 * kColBlock, n, vmask);
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+      for (int u = 0; u < RB; ++u) {
+        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(bl + (size_t)16 * j * RP + 8 * b_sl[u]);
+        o[j] = mfma16x16x32(as_bf16x8(hv[u]), as_bf16x8(v), o[j]);
+      }
+    if (hs) epilogue_store<Y0F32, YF32>(o, yc, yrows, c0 + b * kColBlock, n, vmask);
+  };
+  block(b0, yc0, has0);
+  block(b1, yc1, has1);
 }
 
 // ---- pair passes (k > 1): pass m applies a token's routed pairs of rank 2m and 2m + 1 in one
