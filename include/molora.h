@@ -238,13 +238,15 @@ int molora_dispatch(const int32_t *idx, const float *w, int N, int k, int K,
  *           _GROUPED; r > 32: _GROUPED from 1024 pairs, else _SKINNY;
  *           molora_apply_path reports the choice),
  *           _GROUPED (MFMA tiles of grouped rows of one adapter: 16 rows for
- *           k == 1 and r <= 32; otherwise up to 64 rows, the tile height chosen
- *           per adapter segment on the device from the offsets (each segment cut
- *           into equal tiles of at most a bound set by the pass's size, so no
- *           tile spans two adapters: thelatestinai.com, Table 9, adaptive
- *           tiling), and for k > 1 (k*K <= 64) one pass per routed pair of a
- *           token, the sum carried in fp32),
- *           _GROUPED_FIXED (the same 64-row kernel with fixed 64-row tiles per
+ *           k == 1 and r <= 32; otherwise passes over tiles of up to 64 rows,
+ *           each adapter segment cut on the device from the offsets into tiles
+ *           of balanced height so no tile spans two adapters (thelatestinai.com,
+ *           Table 9, adaptive tiling), every tile run as one workgroup per
+ *           512-wide slice of d_in (shrink) and of d_out (expand); for k > 1
+ *           (k*K <= 64) each pass applies two routed pairs of a token (keyed by
+ *           their adapter pair) once N >= 32 K (K + 1), else one routed pair of
+ *           every token, the sum carried in fp32 between passes),
+ *           _GROUPED_FIXED (the same passes with fixed 64-row tiles per
  *           segment, also for k == 1 and r <= 32: Table 9's fixed tiling, the
  *           comparator of the adaptive one),
  *           _SKINNY (the grouped shrink split over d_in, for small batches), or
