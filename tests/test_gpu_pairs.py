@@ -74,3 +74,39 @@ def test_pair_passes(N, K, r, k, di, do, layout, path):
         yin = y0.clone()
         m.molora_apply(hs, x, yin, offsets, perm, perm_w, inv, k=k, y=yin, path=path)
         np.testing.assert_array_equal(host(yin), outs[0])
+
+
+@pytest.mark.parametrize("mode", ["none_routed", "one_routed"])
+def test_pair_passes_sparse_routing(mode):
+    """Pair-pass sizes (N = 2304, K = 8, k = 4: two passes) where no token has a routed pair (y
+    = y0; every pass empty) or every token has exactly one (pass 0 holds only single pairs,
+    pass 1 nothing: the tokens' sums come from the carry), bf16 and fp32 y, in place."""
+    m = need_gpu()
+    N, K, r, k = 2304, 8, 64, 4
+    g = np.random.default_rng(11 if mode == "none_routed" else 12)
+    t, idx, w = _case(g, N, 512, 640, K, r, k)
+    idx = idx.reshape(N, k)
+    if mode == "none_routed":
+        idx[:] = -1
+    else:
+        keep = g.integers(0, k, N)
+        for j in range(k):
+            idx[keep != j, j] = -1
+        idx[np.arange(N), keep] = g.integers(0, K, N)
+    idx = idx.reshape(-1)
+    hs = m.molora_hotset_init([(dev_bf16(t.A), dev_bf16(t.B))], 1.0)
+    _, offsets, perm, perm_w, inv = m.molora_dispatch(dev(idx), dev(w), K, k)
+    x = dev_bf16(t.x)
+    ref = _oracle(t, 1.0, idx, w, K, k)
+    for y_dtype in (torch.bfloat16, torch.float32):
+        y0 = dev_bf16(t.y0).to(y_dtype)
+        y = host(m.molora_apply(hs, x, y0, offsets, perm, perm_w, inv, k=k, y_dtype=y_dtype, path=m.PATH_GROUPED))
+        if mode == "none_routed":
+            np.testing.assert_array_equal(y, host(y0))
+        elif y_dtype == torch.float32:
+            check_float_output(y, ref, f64(t.y0))
+        else:
+            check_bf16_output(y, ref)
+        yin = y0.clone()
+        m.molora_apply(hs, x, yin, offsets, perm, perm_w, inv, k=k, y=yin, path=m.PATH_GROUPED)
+        np.testing.assert_array_equal(host(yin), y)
