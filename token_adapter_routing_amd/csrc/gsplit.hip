@@ -5,11 +5,13 @@
 // One pass over a grouped order (the tiles of gm_locate: each adapter segment cut into tiles of
 // at most 64 rows) in three launches, so that a workgroup's loads are one slice of the tile
 // instead of the whole of d_in and d_out:
-//   gs_shrink    (tile, d_in slice of 512): the tile's x rows over the slice against the
-//                adapter's A slice (straight into LDS); the two halves of the slice meet in
-//                LDS and the partial x A of the 64 rows goes to part[tile][slice] (fp32).
+//   gs_shrink    (tile pair, d_in slice of 512): the x rows of two consecutive tiles over the
+//                slice against the adapter's A slice (straight into LDS, shared when both tiles
+//                belong to one adapter); the two halves of the slice meet in LDS and the
+//                partial x A of each tile's 64 rows goes to part[tile][slice] (fp32).
 //   gs_finalize  (tile): h = (sum of the slices in order) x gate weight x alpha/r per row, as
-//                bf16 hi / lo rows hb[tile] -- the expand's MFMA A operand.
+//                bf16 hi / lo rows hb[tile] -- the expand's MFMA A operand (or by grouped
+//                position: hq for the pair passes, unscaled fp32 hout for the backward).
 //   gs_expand    (tile, d_out slice of 512): the adapter's B^T slice (straight into LDS, in the
 //                XOR placement of the 64-row tiles, so the operand reads are conflict-free), the
 //                h rows and the tile's y0 rows are requested at once; y = y0 + h B for the rows
