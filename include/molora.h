@@ -206,8 +206,9 @@ int molora_route_topk(const void *x, int N, int d, const void *W1, const float *
  *           Up to 8192 pairs one launch sorts them (size 0): one workgroup, or
  *           above 4096 pairs with K <= 16 a workgroup per 1024 pairs, each
  *           counting all pairs; above 8192 the sort runs as two launches over
- *           up to 128 workgroups and the workspace holds their per-adapter
- *           counts (4*K bytes each).
+ *           workgroups of 1024 pairs each (of ceil(N*k / 128) rounded up to a
+ *           multiple of 1024 above 131072 pairs) and the workspace holds their
+ *           per-adapter counts (4*K bytes each).
  *           Calls that share a workspace must not run concurrently.
  * Supported: 1 <= K <= 64, 1 <= k <= 8, N*k < 2^31.
  * ------------------------------------------------------------------------ */

@@ -87,7 +87,10 @@ def test_host_validation_without_launch():
     assert L.molora_apply(nul, 0, nul, nul, 0, nul, 0, 4, 1, nul, nul, nul, nul, 0, nul, 0, nul) == 1
     sz = ctypes.c_size_t()
     assert L.molora_dispatch_workspace(2048, 4, 16, ctypes.byref(sz)) == 0 and sz.value == 0  # 8192 pairs: one workgroup
-    assert L.molora_dispatch_workspace(16384, 4, 16, ctypes.byref(sz)) == 0 and sz.value == 8 * 16 * 4
+    # 65536 pairs: 64 workgroups of 1024 pairs, 16 counts each
+    assert L.molora_dispatch_workspace(16384, 4, 16, ctypes.byref(sz)) == 0 and sz.value == 64 * 16 * 4
+    # 1M pairs: 128 workgroups of 8192 pairs
+    assert L.molora_dispatch_workspace(262144, 4, 16, ctypes.byref(sz)) == 0 and sz.value == 128 * 16 * 4
     assert L.molora_apply_workspace(nul, 0, 4, 1, 0, 0, ctypes.byref(sz)) == 1
     # multi-target apply: NULL hot set
     assert L.molora_apply_multi_workspace(nul, 2, nul, 4, 1, 0, 0, ctypes.byref(sz)) == 1

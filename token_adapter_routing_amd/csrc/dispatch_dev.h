@@ -207,11 +207,12 @@ __device__ void dispatch_hist_part(DispatchLds<NT>& L, Src src, int P, int K, in
   if (tid < 64) L.cnt[tid] = 0;
   __syncthreads();
   const int c0 = blockIdx.x * C, c1 = min(P, c0 + C);
+  const int E = min(kDispMaxE, (C + NT - 1) / NT);  // pairs per thread and pass (uniform)
   int ev[kDispMaxE];
   float wv[kDispMaxE];
-  for (int s0 = c0; s0 < c1; s0 += kDispMaxE * NT) {
-    disp_load<NT>(src, s0, c1, kDispMaxE, ev, wv);
-    disp_count<NT>(L, ev, kDispMaxE, K, nbits);
+  for (int s0 = c0; s0 < c1; s0 += E * NT) {
+    disp_load<NT>(src, s0, c1, E, ev, wv);
+    disp_count<NT>(L, ev, E, K, nbits);
   }
   __syncthreads();
   if (tid < K) bcnt[(size_t)blockIdx.x * K + tid] = L.cnt[tid];
@@ -228,15 +229,17 @@ __device__ void dispatch_scatter_part(DispatchLds<NT>& L, Src src, int P, int K,
   const int nbits = disp_nbits(K);
   const int b = blockIdx.x;
   if (tid < 64) {
-    int tot = 0, pre = 0;
-    if (tid < K)
-      for (int j = 0; j < nb; ++j) {
-        const int c = bcnt[(size_t)j * K + tid];
-        tot += c;
-        pre += j < b ? c : 0;
-      }
-    L.cnt[tid] = tot;
-    L.base[tid] = pre;
+    L.cnt[tid] = 0;
+    L.base[tid] = 0;
+  }
+  __syncthreads();
+  // totals and the part before this workgroup, per adapter: every count loaded by its own
+  // thread and added in LDS (integer sums: the order does not matter)
+  for (int i = tid; i < nb * K; i += NT) {
+    const int j = i / K, e = i - j * K;
+    const int c = bcnt[i];
+    atomicAdd(&L.cnt[e], c);
+    if (j < b) atomicAdd(&L.base[e], c);
   }
   __syncthreads();
   if (wave == 0) {
@@ -253,11 +256,12 @@ __device__ void dispatch_scatter_part(DispatchLds<NT>& L, Src src, int P, int K,
   }
   __syncthreads();
   const int c0 = b * C, c1 = min(P, c0 + C);
+  const int E = min(kDispMaxE, (C + NT - 1) / NT);
   int ev[kDispMaxE];
   float wv[kDispMaxE];
-  for (int s0 = c0; s0 < c1; s0 += kDispMaxE * NT) {
-    disp_load<NT>(src, s0, c1, kDispMaxE, ev, wv);
-    disp_scatter<NT>(L, ev, wv, s0, c1, kDispMaxE, K, nbits, perm, perm_w, inv);
+  for (int s0 = c0; s0 < c1; s0 += E * NT) {
+    disp_load<NT>(src, s0, c1, E, ev, wv);
+    disp_scatter<NT>(L, ev, wv, s0, c1, E, K, nbits, perm, perm_w, inv);
   }
 }
 

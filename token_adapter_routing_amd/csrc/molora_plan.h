@@ -28,6 +28,7 @@ constexpr int kSSlice = 512;     // split step: reduction or output columns per 
 constexpr int kStepMaxN = 4096;  // the vocabulary step's fused launches handle N <= this
 constexpr int kDispChunk = 8192; // pairs one 1024-thread dispatch workgroup sorts per pass
 constexpr int kDispMaxParts = 128;
+constexpr int kDispMinPart = 1024;  // pairs of one chip-wide dispatch workgroup, at least
 constexpr int kApplyTileMaxAdapters = 16;  // tile and block paths: distinct adapters (K <= 16)
 constexpr int kApplyMaxMulti = 8;          // targets of one molora_apply_multi call
 constexpr size_t kScratchBytes = size_t(8) << 20;  // device scratch of the allocation-free step

@@ -9,8 +9,9 @@ namespace molora {
 DispatchSplit dispatch_split(long long P) {
   DispatchSplit d{1, (int)P};
   if (P <= kDispChunk) return d;
-  long long C = (P + kDispMaxParts - 1) / kDispMaxParts;
-  C = (C + kDispChunk - 1) / kDispChunk * kDispChunk;
+  // parts of kDispMinPart pairs (one per thread) up to kDispMaxParts parts, then larger ones
+  long long C = std::max<long long>(kDispMinPart, (P + kDispMaxParts - 1) / kDispMaxParts);
+  C = (C + kDispMinPart - 1) / kDispMinPart * kDispMinPart;
   d.C = (int)C;
   d.nb = (int)((P + C - 1) / C);
   return d;
