@@ -4,7 +4,7 @@
 // weighted sum, here the softmax over the selected logits).
 //
 //   route_vocab_k   one thread per token: binary search of the id in the K+1 range bounds (LDS).
-//   route_topk_k    a workgroup owns 16 tokens.  Router mode: the first layer x W1^T (d -> 64)
+//   route_topk_k    router mode, a workgroup owns 16 tokens: the first layer x W1^T (d -> 64)
 //                   is an MFMA product with the same gather/shrink core as the LoRA shrink,
 //                   8 waves splitting d (every workgroup reads all of W1) and meeting in LDS;
 //                   bias and ReLU follow in LDS.  With a workspace the first layer runs as a
@@ -16,6 +16,8 @@
 //                   (wave max, ballot of lanes equal to it, lowest lane wins) pick the top-k
 //                   with ties to the lower adapter index; one more round gives the (k+1)-th
 //                   value for the near-tie flag, whose margin is taken in fp64.
+//   topk_logits_k   given logits: the same selection for 64 / SEG tokens per wave at once, one
+//                   per SEG-lane segment (SEG = 16, 32 or 64 >= K).
 #include <cmath>
 
 #include "molora_launch.h"
@@ -212,25 +214,20 @@ __device__ __forceinline__ void router_from_chunks(const float* __restrict__ par
   __syncthreads();
 }
 
-// Waves per workgroup: 8 with the router MLP (splitting d), 4 with given logits.
-template <bool ROUTER>
-struct TopkWaves {
-  static constexpr int NW = ROUTER ? 8 : 4;
-};
-
+// Router mode: 8 waves (splitting d in the first layer), 16 tokens per workgroup.
 // PART: the router's first layer comes from the chunk sums of router_l1_chunk_k.
-template <bool ROUTER, bool PART>
-__global__ __launch_bounds__(TopkWaves<ROUTER>::NW * 64) void route_topk_k(TopkArgs a) {
-  constexpr int NW = TopkWaves<ROUTER>::NW;
-  __shared__ float red[ROUTER && !PART ? RedLds<4, 8>::kFloats : 1];
-  __shared__ float hid[ROUTER ? 16 * 64 : 1];
+template <bool PART>
+__global__ __launch_bounds__(512) void route_topk_k(TopkArgs a) {
+  constexpr int NW = 8;
+  __shared__ float red[!PART ? RedLds<4, 8>::kFloats : 1];
+  __shared__ float hid[16 * 64];
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int t0 = blockIdx.x * 16;
   // lane e < K's row of W2 (64 bf16) and b2[e], requested before the first layer so that the
   // second layer does not wait on them
   u32x4_t w2r[8];
   float b2v = 0.f;
-  if constexpr (ROUTER) {
+  {
     const uint16_t* w2 = a.W2 + (size_t)min(lane, a.K - 1) * 64;
 #pragma unroll
     for (int q = 0; q < 8; ++q) w2r[q] = ld16(w2 + 8 * q);
@@ -244,24 +241,73 @@ __global__ __launch_bounds__(TopkWaves<ROUTER>::NW * 64) void route_topk_k(TopkA
     const int tok = t0 + row;
     if (tok >= a.N) break;  // uniform per wave
     float l = -INFINITY;
-    if constexpr (ROUTER) {
-      if (lane < a.K) {
-        float s = 0.f;
+    if (lane < a.K) {
+      float s = 0.f;
 #pragma unroll
-        for (int j = 0; j < 64; ++j) {
-          const uint32_t pair = w2r[j >> 3][(j >> 1) & 3];
-          s = fmaf(hid[row * 64 + j], bf16_to_f32((j & 1) ? (pair >> 16) : (pair & 0xffffu)), s);
-        }
-        if (a.b2 != nullptr) s += b2v;
-        l = s;
-        a.logits[(size_t)tok * a.K + lane] = l;
+      for (int j = 0; j < 64; ++j) {
+        const uint32_t pair = w2r[j >> 3][(j >> 1) & 3];
+        s = fmaf(hid[row * 64 + j], bf16_to_f32((j & 1) ? (pair >> 16) : (pair & 0xffffu)), s);
       }
-    } else {
-      if (lane < a.K) l = a.logits[(size_t)tok * a.K + lane];
+      if (a.b2 != nullptr) s += b2v;
+      l = s;
+      a.logits[(size_t)tok * a.K + lane] = l;
     }
     topk_one_token(l, a.K, a.k, lane, a.idx + (size_t)tok * a.k, a.w + (size_t)tok * a.k,
                    a.flags ? a.flags + tok : nullptr);
   }
+}
+
+// Given logits: a wave holds 64 / SEG tokens, one per SEG-lane segment (SEG >= K, lane e of a
+// segment = adapter e), and runs the selection of topk_one_token on all of them at once with
+// reductions over the segment (butterflies of SEG lanes).  For K <= SEG the lanes past K hold
+// -inf and 0, so every max and sum takes the same operands in the same order as the 64-lane
+// version: the same bits.
+template <int SEG>
+__global__ __launch_bounds__(256) void topk_logits_k(const float* __restrict__ logits, int N, int K, int k,
+                                                     int32_t* __restrict__ idx, float* __restrict__ w,
+                                                     uint8_t* __restrict__ flags) {
+  constexpr int TPW = kWave / SEG;  // tokens per wave
+  const int lane = threadIdx.x & 63, seg = lane / SEG, e = lane % SEG;
+  const int tok = (blockIdx.x * 4 + (int)(threadIdx.x >> 6)) * TPW + seg;
+  const bool mine = e < K && tok < N;
+  const float l = mine ? logits[(size_t)tok * K + e] : -INFINITY;
+  const uint64_t segbits = SEG == kWave ? ~0ull : (((1ull << SEG) - 1) << (seg * SEG));
+  auto seg_max = [&](float v) {
+#pragma unroll
+    for (int d = SEG / 2; d >= 1; d >>= 1) v = fmaxf(v, __shfl_xor(v, d, kWave));
+    return v;
+  };
+  auto seg_sum = [&](float v) {
+#pragma unroll
+    for (int d = SEG / 2; d >= 1; d >>= 1) v += __shfl_xor(v, d, kWave);
+    return v;
+  };
+  uint64_t taken = 0;  // this segment's selected lanes
+  float vmax = 0.f, kth = 0.f;
+  for (int s = 0; s < k; ++s) {
+    const bool avail = mine && !((taken >> lane) & 1ull);
+    const float m = seg_max(avail ? l : -INFINITY);
+    uint64_t bm = __ballot(avail && l == m) & segbits;
+    if (bm == 0) bm = __ballot(avail) & segbits;  // only reachable with non-finite logits
+    if (bm != 0) taken |= 1ull << __builtin_ctzll(bm);
+    if (s == 0) vmax = m;
+    kth = m;
+  }
+  bool near_tie = false;
+  if (k < K) {
+    const bool avail = mine && !((taken >> lane) & 1ull);
+    const float m2 = seg_max(avail ? l : -INFINITY);
+    near_tie = ((double)kth - (double)m2) < 1e-4;
+  }
+  const bool sel = (taken >> lane) & 1ull;
+  const float ex = sel ? expf(l - vmax) : 0.f;
+  const float sum = seg_sum(ex);
+  if (sel) {
+    const int slot = __popcll(taken & lanemask_lt(lane));  // ascending adapter order
+    idx[(size_t)tok * k + slot] = e;
+    w[(size_t)tok * k + slot] = ex / sum;
+  }
+  if (flags != nullptr && e == 0 && tok < N) flags[tok] = near_tie ? 1 : 0;
 }
 
 hipError_t launch_route_topk(const uint16_t* x, int N, int d, const uint16_t* W1, const float* b1,
@@ -276,11 +322,16 @@ hipError_t launch_route_topk(const uint16_t* x, int N, int d, const uint16_t* W1
                        d, W1, part);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((route_topk_k<true, true>), grid, dim3(TopkWaves<true>::NW * 64), 0, s, a);
+    hipLaunchKernelGGL((route_topk_k<true>), grid, dim3(512), 0, s, a);
   } else if (W1 != nullptr) {
-    hipLaunchKernelGGL((route_topk_k<true, false>), grid, dim3(TopkWaves<true>::NW * 64), 0, s, a);
+    hipLaunchKernelGGL((route_topk_k<false>), grid, dim3(512), 0, s, a);
   } else {
-    hipLaunchKernelGGL((route_topk_k<false, false>), grid, dim3(TopkWaves<false>::NW * 64), 0, s, a);
+    // given logits: 4 waves of 64 / SEG tokens per workgroup
+    const int seg = K <= 16 ? 16 : K <= 32 ? 32 : 64, per_wg = 4 * (kWave / seg);
+    const dim3 g2((N + per_wg - 1) / per_wg);
+    if (seg == 16) hipLaunchKernelGGL((topk_logits_k<16>), g2, dim3(256), 0, s, logits, N, K, k, idx, w, flags);
+    else if (seg == 32) hipLaunchKernelGGL((topk_logits_k<32>), g2, dim3(256), 0, s, logits, N, K, k, idx, w, flags);
+    else hipLaunchKernelGGL((topk_logits_k<64>), g2, dim3(256), 0, s, logits, N, K, k, idx, w, flags);
   }
   return hipGetLastError();
 }
