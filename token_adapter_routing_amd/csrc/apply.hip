@@ -1463,19 +1463,26 @@ hipError_t launch_apply(const ApplyLaunch& a, hipStream_t s) {
     // a pass = three launches over 512-wide slices of the tiles (gsplit.hip)
     float* gs_part = reinterpret_cast<float*>(wsb + plan.gs_off);
     uint16_t* gs_hb = reinterpret_cast<uint16_t*>(wsb + plan.gs_off + plan.gs.hb_off);
-    auto pass = [&](const void* src, bool src_f32, void* dst, bool dst_f32) {
+    auto pass = [&](const void* src, bool src_f32, void* dst, bool dst_f32, const FinishArgs* fin) {
       ga.y0 = src;
       ga.y = dst;
       ga.nwg = plan.gs.nwg;
-      return launch_gs_pass(ga, gs_part, gs_hb, src_f32, dst_f32, a.indirect, s);
+      return launch_gs_pass(ga, gs_part, gs_hb, src_f32, dst_f32, a.indirect, s, fin);
+    };
+    // the tokens the last pass does not reach, finished by extra workgroups of its expand:
+    // y0 for tokens without a routed pair (out of place), the fp32 carry z for tokens whose
+    // routed pairs end before the last pass (when z is not y itself)
+    auto finish = [&](const float* z, int c_last, bool copy_z) {
+      FinishArgs f{};
+      f.y0 = a.y0; f.z = z; f.y = a.y; f.inv = a.inv;
+      f.N = a.N; f.k = a.k; f.c_last = c_last; f.d_out = a.tgt.d_out;
+      f.y0_f32 = a.y0_f32; f.y_f32 = a.y_f32; f.copy_y0 = in_place ? 0 : 1; f.copy_z = copy_z ? 1 : 0;
+      return f;
     };
     if (a.k == 1) {
       ga.key0 = 0; ga.offsets = a.offsets; ga.order = nullptr; ga.wts = a.perm_w;
-      err = pass(a.y0, a.y0_f32, a.y, a.y_f32);
-      if (err != hipSuccess || in_place) return err;
-      MOLORA_DISPATCH_BOOL(a.y0_f32, Y0F, MOLORA_DISPATCH_BOOL(a.y_f32, YF,
-          err = (launch_finish_t<Y0F, YF>(a.y0, nullptr, a.y, a.inv, a.N, 1, a.tgt.d_out, true, false, s))));
-      return err;
+      const FinishArgs f = finish(nullptr, 1, false);
+      return pass(a.y0, a.y0_f32, a.y, a.y_f32, in_place ? nullptr : &f);
     }
     if (plan.tuples) {
       // k > 1 in pair passes: h of every pair by grouped position (one split shrink over the
@@ -1497,19 +1504,17 @@ hipError_t launch_apply(const ApplyLaunch& a, hipStream_t s) {
       GMArgs ge = ga;
       ge.nwg = (int)((te.max_tiles + 7) / 8 * 8);
       float* z = zbuf;
+      const bool copy_z = tsp.m2 > 1 && static_cast<void*>(z) != a.y;
+      const FinishArgs f = finish(z, 2 * tsp.m2 - 1, copy_z);
       for (int m = 0; m < tsp.m2; ++m) {
         const bool last = m == tsp.m2 - 1;
         ge.y0 = m == 0 ? a.y0 : static_cast<const void*>(z);
         ge.y = last ? a.y : static_cast<void*>(z);
         err = launch_gs_expand_pairs(ge, tsr, tsp, m, hq, a.K, m == 0 ? (bool)a.y0_f32 : true,
-                                     last ? (bool)a.y_f32 : true, a.indirect, s);
+                                     last ? (bool)a.y_f32 : true, a.indirect, s,
+                                     last && (!in_place || copy_z) ? &f : nullptr);
         if (err != hipSuccess) return err;
       }
-      const bool copy_z = tsp.m2 > 1 && static_cast<void*>(z) != a.y;
-      if (in_place && !copy_z) return err;
-      MOLORA_DISPATCH_BOOL(a.y0_f32, Y0F, MOLORA_DISPATCH_BOOL(a.y_f32, YF,
-          err = (launch_finish_t<Y0F, YF>(a.y0, z, a.y, a.inv, a.N, a.k, a.tgt.d_out, !in_place, copy_z, s,
-                                          2 * tsp.m2 - 1))));
       return err;
     }
     // k > 1: pass j applies the j-th routed pair of every token over the (rank, adapter)
@@ -1522,18 +1527,17 @@ hipError_t launch_apply(const ApplyLaunch& a, hipStream_t s) {
     int32_t* perm2 = rs.perm2;
     float* w2 = rs.w2;
     float* z = zbuf;
+    const bool copy_z = static_cast<void*>(z) != a.y;
+    const FinishArgs f = finish(z, a.k, copy_z);
     ga.offsets = offsets2; ga.order = perm2; ga.wts = w2;
     for (int j = 0; j < a.k; ++j) {
       ga.key0 = j * a.K;
       const bool last = j == a.k - 1;
       err = pass(j == 0 ? a.y0 : static_cast<const void*>(z), j == 0 ? (bool)a.y0_f32 : true,
-                 last ? a.y : static_cast<void*>(z), last ? (bool)a.y_f32 : true);
+                 last ? a.y : static_cast<void*>(z), last ? (bool)a.y_f32 : true,
+                 last && (!in_place || copy_z) ? &f : nullptr);
       if (err != hipSuccess) return err;
     }
-    const bool copy_z = static_cast<void*>(z) != a.y;
-    if (in_place && !copy_z) return err;
-    MOLORA_DISPATCH_BOOL(a.y0_f32, Y0F, MOLORA_DISPATCH_BOOL(a.y_f32, YF,
-        err = (launch_finish_t<Y0F, YF>(a.y0, z, a.y, a.inv, a.N, a.k, a.tgt.d_out, !in_place, copy_z, s))));
     return err;
   }
 

@@ -39,13 +39,55 @@ struct GSArgs {
   uint16_t* hq;    // instead of hb (a pass over every pair, no order): [q][2][r_pad] by grouped position
   float* hout;     // instead of hb: the unscaled h of grouped position q, [q][r_pad] fp32
   int kslices, cslices;
+  FinishArgs fin;  // the expand's first nfin8 workgroups finish the tokens the pass skips
+  int nfin8;       // a multiple of 8, so the other workgroups keep their XCDs
 };
 
 constexpr int gs_vmcnt(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
+// Finishing workgroup blk: tokens [blk * kFinishTok, + kFinishTok), a wave per 64; a token to
+// finish is copied by its whole wave (row dtypes chosen at run time: these rows are few).
+__device__ void finish_rows(const FinishArgs& f, int blk) {
+  const int lane = threadIdx.x & 63;
+  const int base = (blk * (kFinishTok / kWave) + (int)(threadIdx.x >> 6)) * kWave;
+  const int t = base + lane;
+  int c = 0;
+  if (t < f.N)
+    for (int j = 0; j < f.k; ++j) c += f.inv[(long long)t * f.k + j] >= 0 ? 1 : 0;
+  uint64_t m = __ballot(t < f.N && ((f.copy_y0 && c == 0) || (f.copy_z && c > 0 && c < f.c_last)));
+  while (m) {
+    const int l = __builtin_ctzll(m);
+    m &= m - 1;
+    const int tt = base + l;
+    const bool from_y0 = __shfl(c, l, kWave) == 0;
+    for (int col = lane * 4; col < f.d_out; col += kWave * 4) {
+      float v[4];
+      const size_t o = (size_t)tt * f.d_out + col;
+      if (!from_y0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = f.z[o + i];
+      } else if (f.y0_f32) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = reinterpret_cast<const float*>(f.y0)[o + i];
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = bf16_to_f32(reinterpret_cast<const uint16_t*>(f.y0)[o + i]);
+      }
+      if (f.y_f32) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) reinterpret_cast<float*>(f.y)[o + i] = v[i];
+      } else {
+        uint32_t* p = reinterpret_cast<uint32_t*>(reinterpret_cast<uint16_t*>(f.y) + o);
+        p[0] = pack_bf16x2(v[0], v[1]);
+        p[1] = pack_bf16x2(v[2], v[3]);
+      }
+    }
+  }
+}
+
 // Tile and slice of workgroup b, for `slices` slices per tile (grid nwg * slices).
-__device__ __forceinline__ void gs_tile_slice(const GMArgs& g, int slices, int& w, int& sl) {
-  const int xcd = blockIdx.x & 7, q = blockIdx.x >> 3;
+__device__ __forceinline__ void gs_tile_slice(const GMArgs& g, int slices, int& w, int& sl, int b = blockIdx.x) {
+  const int xcd = b & 7, q = b >> 3;
   w = xcd * (g.nwg >> 3) + q / slices;
   sl = q % slices;
 }
@@ -237,8 +279,12 @@ __global__ __launch_bounds__(kGSThreads, 2) void gs_expand(const GSArgs a) {
   constexpr size_t y0b = Y0F32 ? 4 : 2, yb = YF32 ? 4 : 2;
   constexpr int NY0 = Y0F32 ? 16 : 8;
   __shared__ alignas(16) uint16_t Bs[kBSlice * RP];  // B^T rows of the slice, XOR-placed slots
+  if ((int)blockIdx.x < a.nfin8) {
+    finish_rows(a.fin, blockIdx.x);
+    return;
+  }
   int w, cs, e, r0, r1;
-  gs_tile_slice(a.g, a.cslices, w, cs);
+  gs_tile_slice(a.g, a.cslices, w, cs, blockIdx.x - a.nfin8);
   if (!gm_locate(a.g, w, e, r0, r1)) return;
   const int nrows = r1 - r0;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -482,6 +528,8 @@ __global__ __launch_bounds__(kTSThreads) void tuple_scatter(const TupleSortArgs 
 }
 
 struct TupleArgs {
+  FinishArgs fin;  // the first nfin8 workgroups finish the tokens the pass skips
+  int nfin8;       // a multiple of 8, so the other workgroups keep their XCDs
   GMArgs g;  // the pass: target, y0 / y (g.nwg: the grid's tile slots, a multiple of 8)
   const int4* tiles;     // the pass's tiles (key in the pass, first row, end row)
   const int32_t* ntile;  // the pass's tile count
@@ -504,9 +552,14 @@ __global__ __launch_bounds__(kGSThreads, 2) void gs_expand_pairs(const TupleArgs
   constexpr size_t y0b = Y0F32 ? 4 : 2, yb = YF32 ? 4 : 2;
   constexpr int NY0 = Y0F32 ? 8 : 4;
   __shared__ alignas(16) uint16_t Bs[2][kTCols * RP];
+  if ((int)blockIdx.x < a.nfin8) {
+    finish_rows(a.fin, blockIdx.x);
+    return;
+  }
+  const int bid = blockIdx.x - a.nfin8;
   const int nt = *a.ntile, per = (nt + 7) / 8;
-  const int q = blockIdx.x >> 3, wl = q / a.cslices, cs = q - wl * a.cslices;
-  const int w = (blockIdx.x & 7) * per + wl;
+  const int q = bid >> 3, wl = q / a.cslices, cs = q - wl * a.cslices;
+  const int w = (bid & 7) * per + wl;
   if (wl >= per || w >= nt) return;
   const int4 tl = a.tiles[w];
   const int e = tl.x, r0 = tl.y, r1 = tl.z;
@@ -623,17 +676,21 @@ static hipError_t gs_shrink_finalize(const GMArgs& g, const GSArgs& a, bool indi
 }
 
 hipError_t launch_gs_pass(const GMArgs& g, float* part, uint16_t* hb, bool y0_f32, bool y_f32, bool indirect,
-                          hipStream_t s) {
+                          hipStream_t s, const FinishArgs* fin) {
   GSArgs a{};
   a.g = g;
   a.part = part;
   a.hb = hb;
   a.kslices = (g.tgt.d_in + kBSlice - 1) / kBSlice;
   a.cslices = (g.tgt.d_out + kBSlice - 1) / kBSlice;
+  if (fin != nullptr) {
+    a.fin = *fin;
+    a.nfin8 = ((fin->N + kFinishTok - 1) / kFinishTok + 7) / 8 * 8;
+  }
   hipError_t err = gs_shrink_finalize(g, a, indirect, s);
   if (err != hipSuccess) return err;
   MOLORA_GS_RB(MOLORA_GS_BOOL(indirect, IND, MOLORA_GS_BOOL(y0_f32, Y0F, MOLORA_GS_BOOL(y_f32, YF, {
-    hipLaunchKernelGGL((gs_expand<RB, IND, Y0F, YF>), dim3(g.nwg * a.cslices), dim3(kGSThreads), 0, s, a);
+    hipLaunchKernelGGL((gs_expand<RB, IND, Y0F, YF>), dim3(a.nfin8 + g.nwg * a.cslices), dim3(kGSThreads), 0, s, a);
     err = hipGetLastError();
   }))))
   return err;
@@ -696,9 +753,14 @@ hipError_t launch_tuple_sort(const int32_t* offsets, const int32_t* inv, int N, 
 }
 
 hipError_t launch_gs_expand_pairs(const GMArgs& g, const char* region, const TupleSortPlan& tp, int m,
-                                  const uint16_t* hq, int K, bool y0_f32, bool y_f32, bool indirect, hipStream_t s) {
+                                  const uint16_t* hq, int K, bool y0_f32, bool y_f32, bool indirect, hipStream_t s,
+                                  const FinishArgs* fin) {
   TupleArgs a{};
   a.g = g;
+  if (fin != nullptr) {
+    a.fin = *fin;
+    a.nfin8 = ((fin->N + kFinishTok - 1) / kFinishTok + 7) / 8 * 8;
+  }
   a.tiles = reinterpret_cast<const int4*>(region + tp.tiles_off) + (size_t)m * tp.tmax;
   a.ntile = reinterpret_cast<const int32_t*>(region + tp.ntile_off) + m;
   a.etok = reinterpret_cast<const int32_t*>(region + tp.etok_off);
@@ -709,7 +771,8 @@ hipError_t launch_gs_expand_pairs(const GMArgs& g, const char* region, const Tup
   a.cslices = (g.tgt.d_out + kTCols - 1) / kTCols;
   hipError_t err = hipSuccess;
   MOLORA_GS_RB(MOLORA_GS_BOOL(indirect, IND, MOLORA_GS_BOOL(y0_f32, Y0F, MOLORA_GS_BOOL(y_f32, YF, {
-    hipLaunchKernelGGL((gs_expand_pairs<RB, IND, Y0F, YF>), dim3(g.nwg * a.cslices), dim3(kGSThreads), 0, s, a);
+    hipLaunchKernelGGL((gs_expand_pairs<RB, IND, Y0F, YF>), dim3(a.nfin8 + g.nwg * a.cslices), dim3(kGSThreads), 0, s,
+                       a);
     err = hipGetLastError();
   }))))
   return err;

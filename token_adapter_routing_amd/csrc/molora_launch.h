@@ -66,12 +66,26 @@ struct DenseFuse {
 hipError_t launch_dense_block(const ApplyLaunch* as, int n, const size_t* ws_off, hipStream_t s, bool* taken,
                               const DenseFuse* fuse = nullptr);
 
+// The tokens a pass does not reach, finished by extra workgroups at the start of the pass's
+// last expand launch (rows disjoint from the pass's own): y = y0 for tokens without a routed pair
+// (copy_y0), y = z (the fp32 carry) for tokens with fewer than c_last routed pairs (copy_z).
+struct FinishArgs {
+  const void* y0;
+  const float* z;
+  void* y;
+  const int32_t* inv;
+  int N, k, c_last, d_out;
+  int y0_f32, y_f32, copy_y0, copy_z;
+};
+constexpr int kFinishTok = 512;  // tokens per finishing workgroup (8 waves of 64)
+
 struct GMArgs;  // gm_dev.h
 // One pass of the 64-row grouped tiles (g: the pass's rows, routing and tiling; g.nwg from
 // gs_region) in three launches over 512-wide slices: partials into part, h rows into hb
 // (gs_region's layout).
 hipError_t launch_gs_pass(const GMArgs& g, float* part, uint16_t* hb, bool y0_f32, bool y_f32, bool indirect,
-                          hipStream_t s);
+                          hipStream_t s, const FinishArgs* fin = nullptr);
+// fin (optional): extra workgroups of the expand launch finish the tokens the pass does not reach.
 // Pair passes (k > 1): the shrink and finalize of one pass over every pair of the dispatch's
 // grouped order (g.order null, g.nwg from gs_region over P rows), writing h by grouped position
 // into hq [P][2][r_pad]; the tuple sort into its region (tuple_sort_plan's layout), with each
@@ -81,7 +95,8 @@ hipError_t launch_gs_pair_shrink(const GMArgs& g, float* part, uint16_t* hq, boo
 hipError_t launch_tuple_sort(const int32_t* offsets, const int32_t* inv, int N, int k, int K, char* region,
                              const TupleSortPlan& tp, const GMTiling& tl, hipStream_t s);
 hipError_t launch_gs_expand_pairs(const GMArgs& g, const char* region, const TupleSortPlan& tp, int m,
-                                  const uint16_t* hq, int K, bool y0_f32, bool y_f32, bool indirect, hipStream_t s);
+                                  const uint16_t* hq, int K, bool y0_f32, bool y_f32, bool indirect, hipStream_t s,
+                                  const FinishArgs* fin = nullptr);
 
 // Per-pair shrink without gate weight or scale into hout [P][r_pad] fp32 by grouped position:
 // the split shrink and finalize over the 64-row tiles of the dispatch's grouped order; part
