@@ -1498,7 +1498,11 @@ hipError_t launch_apply(const ApplyLaunch& a, hipStream_t s) {
       if (err != hipSuccess) return err;
       const TupleSortPlan& tsp = plan.tsort;
       char* tsr = wsb + plan.tsort_off;
-      const GMTiling te = gm_tiling(a.path, a.N, tsp.kk, (a.tgt.d_out + 2 * kColBlock - 1) / (2 * kColBlock));
+      // pair-expand tiles: balanced heights up to kPairTileRows rows (fixed tiling: 64-row tiles)
+      GMTiling te{};
+      te.fixed = a.path == kPathGroupedFixed ? 1 : 0;
+      te.rows = te.fixed ? kGMRows : kPairTileRows;
+      te.max_tiles = (a.N + te.rows - 1) / te.rows + tsp.kk;
       err = launch_tuple_sort(a.offsets, a.inv, a.N, a.k, a.K, tsr, tsp, te, s);
       if (err != hipSuccess) return err;
       GMArgs ge = ga;

@@ -541,8 +541,8 @@ struct TupleArgs {
   int cslices;         // 256-wide column slices
 };
 
-// Workgroup = one tile x one 256-wide d_out slice; wave (rb, ch) takes row block rb and the
-// slice's 128-column block ch.  The tiles are spread over the XCDs in runs of ceil(count / 8)
+// Workgroup = one tile (up to kPairTileRows = 128 rows) x one 256-wide d_out slice; wave w takes
+// row block w and both 128-column blocks of the slice, one after the other.  The tiles are spread over the XCDs in runs of ceil(count / 8)
 // consecutive tiles (mostly of one first adapter), so each XCD's L2 holds few B^T slices.  The
 // B^T slices of a (and b) go straight into LDS in the XOR placement, the rows' h operands and
 // y0 rows are requested behind them.
@@ -567,12 +567,10 @@ __global__ __launch_bounds__(kGSThreads, 2) void gs_expand_pairs(const TupleArgs
   const bool hasb = eb < a.K1 - 1;  // the same in every lane
   const int nrows = r1 - r0;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int n = lane & 15, G = lane >> 4, rb = wave & 3, ch = wave >> 2;
+  const int n = lane & 15, G = lane >> 4, rb = wave;  // 8 row blocks of 16 rows
   const int d_out = a.g.tgt.d_out;
   const int c0 = cs * kTCols, c1 = min(c0 + kTCols, d_out);
-  const int nb = (c1 - c0) / kColBlock;
-  const int blk = min(ch, nb - 1);
-  const bool has = ch < nb;
+  const int nb = (c1 - c0) / kColBlock;  // 1 or 2 column blocks, both taken by every wave
   // 0. the entry of the lane's MFMA row 16 rb + n (rows past the tile repeat its first and are
   //    not stored): first, since the h and y0 streams wait on it
   const int rl = 16 * rb + n, rr = r0 + (rl < nrows ? rl : 0);
@@ -614,36 +612,42 @@ __global__ __launch_bounds__(kGSThreads, 2) void gs_expand_pairs(const TupleArgs
 #pragma unroll
   for (int u = 0; u < RB; ++u) hvb[u] = ld16(pb + u * 16);
   __builtin_amdgcn_sched_barrier(0);
-  // 3. the y0 rows
-  RowChunk<Y0F32> yc;
-  load_row_chunk<Y0F32>(yc, y0rows, c0 + blk * kColBlock, n);
+  // 3. the y0 rows of both column blocks
+  RowChunk<Y0F32> yc0, yc1;
+  load_row_chunk<Y0F32>(yc0, y0rows, c0, n);
+  load_row_chunk<Y0F32>(yc1, y0rows, c0 + min(1, nb - 1) * kColBlock, n);
   __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_waitcnt(gs_vmcnt(NY0));  // B pieces and h rows have landed (y0 may not)
+  __builtin_amdgcn_s_waitcnt(gs_vmcnt(2 * NY0));  // B pieces and h rows have landed (y0 may not)
   __syncthreads();
-  f32x4_t o[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) o[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   int b_sl[RB];
 #pragma unroll
   for (int u = 0; u < RB; ++u) b_sl[u] = (2 * u + (G & 1)) ^ gm_b_swz<RB>(n);
-  const size_t roff = (size_t)(blk * kColBlock + n) * RP;
+  // the two column blocks one after the other (one set of accumulators)
+  auto block = [&](int blk, const RowChunk<Y0F32>& yc) {
+    const size_t roff = (size_t)(blk * kColBlock + n) * RP;
+    f32x4_t o[8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j)
-#pragma unroll
-    for (int u = 0; u < RB; ++u) {
-      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(Bs[0] + roff + (size_t)16 * j * RP + 8 * b_sl[u]);
-      o[j] = mfma16x16x32(as_bf16x8(hva[u]), as_bf16x8(v), o[j]);
-    }
-  if (hasb) {
+    for (int j = 0; j < 8; ++j) o[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < 8; ++j)
 #pragma unroll
       for (int u = 0; u < RB; ++u) {
-        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(Bs[1] + roff + (size_t)16 * j * RP + 8 * b_sl[u]);
-        o[j] = mfma16x16x32(as_bf16x8(hvb[u]), as_bf16x8(v), o[j]);
+        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(Bs[0] + roff + (size_t)16 * j * RP + 8 * b_sl[u]);
+        o[j] = mfma16x16x32(as_bf16x8(hva[u]), as_bf16x8(v), o[j]);
       }
-  }
-  if (has) epilogue_store<Y0F32, YF32>(o, yc, yrows, c0 + blk * kColBlock, n, vmask);
+    if (hasb) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+#pragma unroll
+        for (int u = 0; u < RB; ++u) {
+          const u32x4_t v = *reinterpret_cast<const u32x4_t*>(Bs[1] + roff + (size_t)16 * j * RP + 8 * b_sl[u]);
+          o[j] = mfma16x16x32(as_bf16x8(hvb[u]), as_bf16x8(v), o[j]);
+        }
+    }
+    epilogue_store<Y0F32, YF32>(o, yc, yrows, c0 + blk * kColBlock, n, vmask);
+  };
+  block(0, yc0);
+  if (nb > 1) block(1, yc1);
 }
 
 }  // namespace

@@ -166,6 +166,7 @@ GSRegion gs_region(int path, long long rows_of_pass, int K, int r_pad, int d_in,
 // b = K for "no second pair": K (K + 1) keys; the tuples are taken when the keys hold 32 rows
 // on average or more (N >= 32 K (K + 1)), below that the tiles would be mostly short.
 constexpr int kTupleWGTokens = 1024;  // tokens per workgroup of the tuple sort
+constexpr int kPairTileRows = 128;    // pair-expand tile height bound (8 row blocks of 16)
 bool gm_tuples(int N, int k, int K);
 // The tuple sort's region: per-workgroup key counts bcnt [nb][nkeys] (then the workgroups'
 // first positions), the pass offsets toff [nkeys + 1], each pass's tiles [m2][tmax] (int4: key
