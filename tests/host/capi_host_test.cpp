@@ -144,7 +144,10 @@ static void apply_writes(const ApplyLaunch& a) {
   }
   const int ns = a.path == kPathSkinny ? skinny_splits(a.tgt.d_in) : 1;
   write_span<float>(ws + p.hpart_off, 0, (size_t)ns * P * a.tgt.r_pad, "hpart");
-  if (a.path == kPathSkinny && a.k > 1 && a.k * a.K <= 64) {
+  if (a.path == kPathSkinny && decode_expand_fits(a.N, a.k, a.K, a.tgt.r_pad)) {
+    // the decode expand: the summed h rows [P][2][r_pad] bf16 (no sort, no carry)
+    write_span<uint16_t>(ws + p.hq_off, 0, (size_t)P * 2 * a.tgt.r_pad, "decode h rows");
+  } else if (a.path == kPathSkinny && a.k > 1 && a.k * a.K <= 64) {
     rank_sort_writes(ws + p.sort_off, P, a.k, a.K);
     if (!a.y_f32) write_span<float>(ws + p.z_off, 0, (size_t)a.N * a.tgt.d_out, "z");
   }
@@ -307,10 +310,14 @@ hipError_t launch_apply_multi(const ApplyLaunch* as, int n, hipStream_t) {
     return hipSuccess;
   }
   const long long P = (long long)a0.N * a0.k;
-  if (a0.k > 1) rank_sort_writes(ws + mp.sort_off, P, a0.k, a0.K);
+  CHECK(mp.decode == (decode_expand_fits(a0.N, a0.k, a0.K, a0.tgt.r_pad) && a0.path == kPathSkinny), "decode plan");
+  if (a0.k > 1 && !mp.decode) rank_sort_writes(ws + mp.sort_off, P, a0.k, a0.K);
   for (int i = 0; i < n; ++i) {
     write_span<float>(ws + mp.hpart_off[i], 0, (size_t)skinny_splits(d_in[i]) * P * a0.tgt.r_pad, "hpart (multi)");
-    if (a0.k > 1 && !a0.y_f32) write_span<float>(ws + mp.z_off[i], 0, (size_t)a0.N * d_out[i], "z (multi)");
+    if (mp.decode)
+      write_span<uint16_t>(ws + mp.hq_off[i], 0, (size_t)P * 2 * a0.tgt.r_pad, "decode h rows (multi)");
+    else if (a0.k > 1 && !a0.y_f32)
+      write_span<float>(ws + mp.z_off[i], 0, (size_t)a0.N * d_out[i], "z (multi)");
   }
   return hipSuccess;
 }
@@ -948,6 +955,9 @@ int main() {
     for (int k : {1, 2})
       for (int N : {1, 256, 4096})
         for (int yd : {MOLORA_BF16, MOLORA_F32}) test_multi(4, 16, N, k, path, yd);
+  for (int k : {2, 3, 4})  // the decode expand (K * r_pad = 1024) and just past its token bound
+    for (int N : {1, 256, 1024, 1025})
+      for (int yd : {MOLORA_BF16, MOLORA_F32}) test_multi(16, 64, N, k, MOLORA_PATH_SKINNY, yd);
   test_multi(16, 16, 4096, 2, MOLORA_PATH_BLOCK, MOLORA_BF16);  // no dense kernels: dispatch, then apply
   test_multi(4, 16, 8192, 2, MOLORA_PATH_BLOCK, MOLORA_BF16);   // 16384 pairs: dispatch, then apply
   for (int layout : {MOLORA_LAYOUT_DIRECT, MOLORA_LAYOUT_INDIRECT})

@@ -1187,6 +1187,182 @@ __global__ __launch_bounds__(256) void finish_tokens_multi(FinishMulti m) {
                            blockIdx.x);
 }
 
+// ---- decode-sized expand (k = 2..4, at most kDXMaxTok tokens, K * r_pad <= kDXMaxKR): the
+// summed h rows of every pair first (hsum_multi), then one launch over (target, 32-column
+// slice).  A workgroup holds that slice of every adapter's B^T in LDS and covers every token:
+// each wave owns 16-token row blocks and adds, in registers, the token's routed pairs in
+// adapter order (a repeated adapter once per slot, in slot order), then writes y = y0 + sum.
+// Each adapter's B^T is read once per call, and no sum is carried between launches.
+struct HsumMulti {
+  const float* hpart[kApplyMaxMulti];
+  uint16_t* hq[kApplyMaxMulti];
+  int nsplit[kApplyMaxMulti];
+  long long P;
+};
+
+// hq[q] = bf16 hi and lo of the sum over the splits (in order) of the weighted partials of
+// grouped position q, as [P][2][r_pad]; a thread per 8 ranks of a row.
+template <int RB>
+__global__ __launch_bounds__(256) void hsum_multi(HsumMulti m) {
+  constexpr int RP = RB * 16, CH = RP / 8;
+  const int i = blockIdx.y;
+  const long long v = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (v >= m.P * CH) return;
+  const long long q = v / CH;
+  const int c = (int)(v - q * CH);
+  float sum[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) sum[j] = 0.f;
+  for (int sp = 0; sp < m.nsplit[i]; ++sp) {
+    const float* p = m.hpart[i] + ((long long)sp * m.P + q) * RP + 8 * c;
+    const u32x4_t x0 = ld16(p), x1 = ld16(p + 4);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      sum[j] += __uint_as_float(x0[j]);
+      sum[j + 4] += __uint_as_float(x1[j]);
+    }
+  }
+  uint16_t* dst = m.hq[i] + q * 2 * RP + 8 * c;
+  *reinterpret_cast<bf16x8_t*>(dst) = split_hilo(sum, false);
+  *reinterpret_cast<bf16x8_t*>(dst + RP) = split_hilo(sum, true);
+}
+
+struct DecodeMulti {
+  TargetDev tgt[kApplyMaxMulti];
+  const void* y0[kApplyMaxMulti];
+  void* y[kApplyMaxMulti];
+  const uint16_t* hq[kApplyMaxMulti];
+  const int32_t* offsets;
+  const int32_t* inv;
+  int N, k, K;
+};
+
+constexpr int kDXThreads = 512;
+
+// Workgroup (slice x, target y): columns [32 x, 32 x + 32) of target y.  LDS row L of adapter
+// e's 32-row region holds output column 2 (L & 15) + (L >> 4) of the slice (the slab row of
+// that column within its 128-column block, 16-byte slots XORed with gm_b_swz(L)), so MFMA c's
+// lane n produces column 2n + c and a lane's two columns are adjacent in y.
+template <int RB, int KMAX, bool INDIRECT, bool Y0F32, bool YF32>
+__global__ __launch_bounds__(kDXThreads, 2) void expand_decode_multi(const DecodeMulti m) {
+  constexpr int RP = RB * 16, SPR = 2 * RB, NPC = kDXCols * SPR / 64;  // 1 KB pieces per adapter
+  static_assert(kDXCols == 32, "two MFMA column blocks per slice");
+  __shared__ alignas(16) uint16_t Bs[kDXMaxKR * kDXCols];
+  __shared__ int offs[65];
+  const int i = blockIdx.y;
+  const TargetDev& tg = m.tgt[i];
+  const int d_out = tg.d_out;
+  const int c0 = blockIdx.x * kDXCols;
+  if (c0 >= d_out) return;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n = lane & 15, G = lane >> 4;
+  // 1. the slice of every adapter's B^T, straight into LDS
+  {
+    const int blk0 = c0 & ~(kColBlock - 1), cw = c0 & (kColBlock - 1);
+    for (int p = wave; p < m.K * NPC; p += kDXThreads / kWave) {
+      const int e = p / NPC, pp = p - e * NPC;
+      const int P = 64 * pp + lane, L = P / SPR, slot = (P % SPR) ^ gm_b_swz<RB>(L);
+      const int lc = cw + 2 * (L & 15) + (L >> 4);  // column within the 128-column block
+      const int w = 16 * (lc & 7) + (lc >> 3);      // its slab row (the inverse of b_perm_col)
+      const char* src = reinterpret_cast<const char*>(adapter_B<INDIRECT>(tg, e) + (size_t)(blk0 + w) * RP) + slot * 16;
+      __builtin_amdgcn_global_load_lds(src, reinterpret_cast<char*>(Bs) + (size_t)p * 1024, 16, 0, 0);
+    }
+  }
+  if ((int)threadIdx.x <= m.K) offs[threadIdx.x] = m.offsets[threadIdx.x];
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  constexpr size_t y0b = Y0F32 ? 4 : 2, yb = YF32 ? 4 : 2;
+  const uint16_t* hq = m.hq[i];
+  const int N = m.N, k = m.k;
+  int b_sl[RB];
+#pragma unroll
+  for (int u = 0; u < RB; ++u) b_sl[u] = (2 * u + (G & 1)) ^ gm_b_swz<RB>(n);
+  for (int rb = wave; rb * 16 < N; rb += kDXThreads / kWave) {
+    // the lane's A row: token 16 rb + n, its routed pairs' adapters and h operands
+    const int tn = 16 * rb + n;
+    int es[KMAX];
+    bf16x8_t hs[KMAX][RB];
+    uint64_t mine = 0;
+#pragma unroll
+    for (int s = 0; s < KMAX; ++s) {
+      const int q = (s < k && tn < N) ? m.inv[(long long)tn * k + s] : -1;
+      es[s] = q >= 0 ? segment_of(offs, m.K, q) : -1;
+      if (q >= 0) mine |= 1ull << es[s];
+      const uint16_t* hp = hq + ((size_t)(q >= 0 ? q : 0) * 2 + (G >> 1)) * RP + 8 * (G & 1);
+#pragma unroll
+      for (int u = 0; u < RB; ++u) hs[s][u] = q >= 0 ? as_bf16x8(ld16(hp + 16 * u)) : bf16x8_t{};
+    }
+    // the y0 values of the lane's outputs: rows 4G + j, columns c0 + 2n, + 1
+    const int tb = 16 * rb + 4 * G;
+    float yv[4][2];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const size_t o = (size_t)min(tb + j, N - 1) * d_out + c0 + 2 * n;
+      if constexpr (Y0F32) {
+        const float2 v = *reinterpret_cast<const float2*>(reinterpret_cast<const float*>(m.y0[i]) + o);
+        yv[j][0] = v.x;
+        yv[j][1] = v.y;
+      } else {
+        const uint32_t v = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint16_t*>(m.y0[i]) + o);
+        yv[j][0] = __uint_as_float(v << 16);
+        yv[j][1] = __uint_as_float(v & 0xffff0000u);
+      }
+    }
+    uint64_t used = mine;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+      const uint32_t lo = __shfl_xor((uint32_t)used, d, kWave);
+      const uint32_t hi = __shfl_xor((uint32_t)(used >> 32), d, kWave);
+      used |= ((uint64_t)hi << 32) | lo;
+    }
+    f32x4_t o[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+    while (used) {
+      const int e = __builtin_ctzll(used);
+      used &= used - 1;
+      const uint16_t* Be = Bs + (size_t)e * kDXCols * RP;
+      unsigned pend = 0;
+#pragma unroll
+      for (int s = 0; s < KMAX; ++s) pend |= (es[s] == e ? 1u : 0u) << s;
+      // one round per occurrence of e among a token's slots (normally one)
+      do {
+        const int s0 = pend != 0 ? __builtin_ctz(pend) : -1;
+        pend &= pend - 1;
+        bf16x8_t hb[RB];
+#pragma unroll
+        for (int u = 0; u < RB; ++u) hb[u] = bf16x8_t{};
+#pragma unroll
+        for (int s = 0; s < KMAX; ++s)
+          if (s == s0) {
+#pragma unroll
+            for (int u = 0; u < RB; ++u) hb[u] = hs[s][u];
+          }
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+          for (int u = 0; u < RB; ++u) {
+            const u32x4_t v = *reinterpret_cast<const u32x4_t*>(Be + (size_t)(16 * c + n) * RP + 8 * b_sl[u]);
+            o[c] = mfma16x16x32(hb[u], as_bf16x8(v), o[c]);
+          }
+      } while (__ballot(pend != 0) != 0);
+    }
+    // y = y0 + the sum; a token without routed pairs keeps its y0 value
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int t = tb + j;
+      const bool routed = __shfl(mine != 0 ? 1 : 0, 4 * G + j, kWave) != 0;
+      if (t >= N) continue;
+      const float v0 = routed ? yv[j][0] + o[0][j] : yv[j][0];
+      const float v1 = routed ? yv[j][1] + o[1][j] : yv[j][1];
+      const size_t off = (size_t)t * d_out + c0 + 2 * n;
+      if constexpr (YF32) {
+        *reinterpret_cast<float2*>(reinterpret_cast<float*>(m.y[i]) + off) = make_float2(v0, v1);
+      } else {
+        *reinterpret_cast<uint32_t*>(reinterpret_cast<uint16_t*>(m.y[i]) + off) = pack_bf16x2(v0, v1);
+      }
+    }
+  }
+}
+
 // k > 1: grid = ceil(N/16) token tiles * col_groups.  KMAX bounds k (register arrays).
 template <int RB, int KMAX, bool INDIRECT, bool Y0F32, bool YF32>
 __global__ __launch_bounds__(256) void expand_tokens(ExpandArgs a) {
@@ -1247,16 +1423,24 @@ __global__ __launch_bounds__(256) void expand_tokens(ExpandArgs a) {
     while (rem) {
       const int e = __builtin_ctzll(rem);
       rem &= rem - 1;
-      bf16x8_t hb[RB];
+      unsigned pend = 0;
 #pragma unroll
-      for (int u = 0; u < RB; ++u) hb[u] = bf16x8_t{};
+      for (int s = 0; s < KMAX; ++s) pend |= (es[s] == e ? 1u : 0u) << s;
+      // one round per occurrence of e among a token's slots (normally one)
+      do {
+        const int s0 = pend != 0 ? __builtin_ctz(pend) : -1;
+        pend &= pend - 1;
+        bf16x8_t hb[RB];
 #pragma unroll
-      for (int s = 0; s < KMAX; ++s)
-        if (es[s] == e) {
+        for (int u = 0; u < RB; ++u) hb[u] = bf16x8_t{};
 #pragma unroll
-          for (int u = 0; u < RB; ++u) hb[u] = hs[s][u];
-        }
-      expand_mfma<RB>(o, hb, adapter_B<INDIRECT>(a.tgt, e), a.tgt.r_pad, c0 + blk * kColBlock, lane);
+        for (int s = 0; s < KMAX; ++s)
+          if (s == s0) {
+#pragma unroll
+            for (int u = 0; u < RB; ++u) hb[u] = hs[s][u];
+          }
+        expand_mfma<RB>(o, hb, adapter_B<INDIRECT>(a.tgt, e), a.tgt.r_pad, c0 + blk * kColBlock, lane);
+      } while (__ballot(pend != 0) != 0);
     }
     epilogue_store<Y0F32, YF32>(o, cur, yrows, c0 + blk * kColBlock, n, vmask);
   }
@@ -1385,6 +1569,29 @@ static hipError_t launch_expand_tok_t(const ExpandArgs& ea, int grid, hipStream_
   }
 #define MOLORA_DISPATCH_BOOL(V, NAME, ...) \
   if (V) { constexpr bool NAME = true; __VA_ARGS__; } else { constexpr bool NAME = false; __VA_ARGS__; }
+
+// The decode expand of n targets (hsum_multi, then expand_decode_multi): hm and dm hold every
+// target's pointers; max_dout is the widest d_out.
+static hipError_t launch_decode_expand(const HsumMulti& hm, const DecodeMulti& dm, int n, int max_dout, int RBv,
+                                       bool indirect, bool y0_f32, bool y_f32, hipStream_t s) {
+  if (dm.k < 2 || dm.k > 4 || dm.N > kDXMaxTok || dm.K * RBv * 16 > kDXMaxKR || dm.K > 64 || dm.inv == nullptr)
+    return hipErrorInvalidValue;
+  if (hm.P == 0) return hipSuccess;
+  const long long hthreads = hm.P * 2 * RBv;
+  MOLORA_DISPATCH_RB(RBv, hipLaunchKernelGGL((hsum_multi<RB>), dim3((unsigned)((hthreads + 255) / 256), n), dim3(256),
+                                             0, s, hm));
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const dim3 grid(max_dout / kDXCols, n);
+#define MOLORA_DX(KM)                                                                                      \
+  MOLORA_DISPATCH_RB(RBv, MOLORA_DISPATCH_BOOL(indirect, IND, MOLORA_DISPATCH_BOOL(y0_f32, Y0F,             \
+      MOLORA_DISPATCH_BOOL(y_f32, YF,                                                                      \
+          hipLaunchKernelGGL((expand_decode_multi<RB, KM, IND, Y0F, YF>), grid, dim3(kDXThreads), 0, s, dm)))))
+  if (dm.k <= 2) { MOLORA_DX(2) }
+  else { MOLORA_DX(4) }
+#undef MOLORA_DX
+  return hipGetLastError();
+}
 
 // Rank sort of the grouped pairs for k > 1 passes, in the region of rank_sort_plan() at wsb
 // (counts2 and offsets2, perm2 and w2 = the order and weights, the chip-wide sort's counts).
@@ -1582,6 +1789,17 @@ hipError_t launch_apply(const ApplyLaunch& a, hipStream_t s) {
         MOLORA_DISPATCH_BOOL(a.y_f32, YF, err = (launch_expand_k1_t<RB, IND, Y0F, YF>(ea, grid, s))))));
     return err;
   }
+  if (a.path == 2 && decode_expand_fits(a.N, a.k, a.K, a.tgt.r_pad)) {
+    HsumMulti hm{};
+    DecodeMulti dm{};
+    hm.hpart[0] = sa.hpart;
+    hm.hq[0] = reinterpret_cast<uint16_t*>(wsb + plan.hq_off);
+    hm.nsplit[0] = nsplit;
+    hm.P = P;
+    dm.tgt[0] = a.tgt; dm.y0[0] = a.y0; dm.y[0] = a.y; dm.hq[0] = hm.hq[0];
+    dm.offsets = a.offsets; dm.inv = a.inv; dm.N = a.N; dm.k = a.k; dm.K = a.K;
+    return launch_decode_expand(hm, dm, 1, a.tgt.d_out, RBv, a.indirect, a.y0_f32, a.y_f32, s);
+  }
   if (a.path == 2 && a.k * a.K <= 64) {
     // one grouped expand pass per rank of the routed pairs (as on the 64-row tiles), over
     // (adapter, 16-row tile, column group) workgroups, the sum carried in fp32
@@ -1695,6 +1913,21 @@ hipError_t launch_apply_multi(const ApplyLaunch* as, int n, hipStream_t s) {
       hipLaunchKernelGGL((shrink_grouped_multi<RB, IND>), dim3((int)tiles, max_split, n), dim3(256), 0, s, sm)));
   err = hipGetLastError();
   if (err != hipSuccess) return err;
+  if (mp.decode) {
+    HsumMulti hm{};
+    DecodeMulti dm{};
+    int max_dout = 0;
+    for (int i = 0; i < n; ++i) {
+      hm.hpart[i] = sm.a[i].hpart;
+      hm.hq[i] = reinterpret_cast<uint16_t*>(wsb + mp.hq_off[i]);
+      hm.nsplit[i] = sm.a[i].nsplit;
+      dm.tgt[i] = as[i].tgt; dm.y0[i] = as[i].y0; dm.y[i] = as[i].y; dm.hq[i] = hm.hq[i];
+      max_dout = std::max(max_dout, as[i].tgt.d_out);
+    }
+    hm.P = P;
+    dm.offsets = a0.offsets; dm.inv = a0.inv; dm.N = a0.N; dm.k = a0.k; dm.K = a0.K;
+    return launch_decode_expand(hm, dm, n, max_dout, RBv, a0.indirect, a0.y0_f32, a0.y_f32, s);
+  }
 
   ExpandMulti em;
   auto expand_args = [&](int i, long long t) {

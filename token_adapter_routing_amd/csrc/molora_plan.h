@@ -122,6 +122,15 @@ StepPlan step_plan(int N, int K, int r_pad, int d_in);
 int apply_resolve_path(int N, int k, int path, int K, int r_pad);
 int apply_multi_resolve_path(int n, int N, int k, int path, int K, int r_pad);
 int skinny_splits(int d_in);
+
+// Decode-sized skinny apply with k > 1: one expand launch per call over (target, 32-column
+// slice) workgroups that hold the B^T slices of every adapter in LDS and sum each token's
+// routed pairs in registers (no rank passes, no fp32 carry).  Bounds: 2 <= k <= 4, N tokens
+// at most kDXMaxTok, K * r_pad at most kDXMaxKR (64 KB of B^T per workgroup).
+constexpr int kDXCols = 32;
+constexpr int kDXMaxTok = 1024;
+constexpr int kDXMaxKR = 1024;
+bool decode_expand_fits(int N, int k, int K, int r_pad);
 // 64-row grouped tiles (r > 32, or k > 1 with k*K <= 64)
 bool use_gm(int k, int K, int r_pad);
 // The resolved path runs the 64-row grouped kernel: the grouped path where use_gm holds, and
@@ -201,7 +210,8 @@ ApplyPlan apply_plan(int N, int k, int K, int r_pad, int d_in, int d_out, bool y
 size_t apply_ws_bytes(int N, int k, int K, int r_pad, int d_in, int d_out, bool y_f32, int path);
 
 // Workspace of molora_apply_multi (n targets sharing one routing): on the fused skinny path
-// [rank sort][per target: h partials, z]; otherwise one apply_plan region per target.
+// [rank sort][per target: h partials, z], or per target [h partials, h rows] when the decode
+// expand takes the call; otherwise one apply_plan region per target.
 struct MultiPlan {
   int path;
   bool fused;
@@ -210,6 +220,8 @@ struct MultiPlan {
   size_t tgt_off[kApplyMaxMulti];   // start of target i's region
   size_t hpart_off[kApplyMaxMulti]; // fused: its h partials
   size_t z_off[kApplyMaxMulti];     // fused: its fp32 carry (bf16 y, k > 1), else 0
+  bool decode;                      // fused, decode_expand_fits: h rows instead of sort and carry
+  size_t hq_off[kApplyMaxMulti];    // decode: its h by grouped position [P][2][r_pad] bf16 hi / lo
   size_t total;
 };
 MultiPlan apply_multi_plan(int n, const int* d_in, const int* d_out, int N, int k, int K, int r_pad, bool y_f32,

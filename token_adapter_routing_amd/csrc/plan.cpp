@@ -129,6 +129,10 @@ int skinny_splits(int d_in) {
   return ns;
 }
 
+bool decode_expand_fits(int N, int k, int K, int r_pad) {
+  return k >= 2 && k <= 4 && N <= kDXMaxTok && K * r_pad <= kDXMaxKR;
+}
+
 bool use_gm(int k, int K, int r_pad) { return (k > 1 && k * K <= 64) || (k == 1 && r_pad > 32); }
 
 bool gm_path(int path, int k, int K, int r_pad) {
@@ -244,7 +248,11 @@ ApplyPlan apply_plan(int N, int k, int K, int r_pad, int d_in, int d_out, bool y
   a.hpart_off = 0;
   a.hpart_bytes = align256((size_t)ns * (size_t)P * (size_t)r_pad * sizeof(float));
   a.total = a.hpart_bytes;
-  if (a.path == kPathSkinny && k > 1 && k * K <= 64) {  // one expand pass per rank of the pairs
+  if (a.path == kPathSkinny && decode_expand_fits(N, k, K, r_pad)) {  // h rows for the decode expand
+    a.hq_off = a.hpart_bytes;
+    a.hq_bytes = align256((size_t)P * 2 * r_pad * sizeof(uint16_t));
+    a.total = a.hq_off + a.hq_bytes;
+  } else if (a.path == kPathSkinny && k > 1 && k * K <= 64) {  // one expand pass per rank of the pairs
     a.sort_off = a.hpart_bytes;
     a.sort = rank_sort_plan(P, k, K);
     a.z_off = a.sort_off + a.sort.bytes;
@@ -262,7 +270,8 @@ MultiPlan apply_multi_plan(int n, const int* d_in, const int* d_out, int N, int 
                            int path) {
   MultiPlan m{};
   m.path = apply_multi_resolve_path(n, N, k, path, K, r_pad);
-  m.fused = m.path == kPathSkinny && (k == 1 || k * K <= 64);
+  m.decode = m.path == kPathSkinny && decode_expand_fits(N, k, K, r_pad);
+  m.fused = m.path == kPathSkinny && (k == 1 || k * K <= 64 || m.decode);
   size_t off = 0;
   if (!m.fused) {
     for (int i = 0; i < n; ++i) {
@@ -273,7 +282,7 @@ MultiPlan apply_multi_plan(int n, const int* d_in, const int* d_out, int N, int 
     return m;
   }
   const long long P = (long long)N * k;
-  if (k > 1) {
+  if (k > 1 && !m.decode) {
     m.sort_off = 0;
     m.sort = rank_sort_plan(P, k, K);
     off = align256(m.sort.bytes);
@@ -282,7 +291,10 @@ MultiPlan apply_multi_plan(int n, const int* d_in, const int* d_out, int N, int 
     m.tgt_off[i] = off;
     m.hpart_off[i] = off;
     off += align256((size_t)skinny_splits(d_in[i]) * (size_t)P * (size_t)r_pad * sizeof(float));
-    if (k > 1 && !y_f32) {
+    if (m.decode) {
+      m.hq_off[i] = off;
+      off += align256((size_t)P * 2 * r_pad * sizeof(uint16_t));
+    } else if (k > 1 && !y_f32) {
       m.z_off[i] = off;
       off += align256((size_t)N * d_out[i] * sizeof(float));
     }
