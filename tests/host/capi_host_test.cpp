@@ -145,8 +145,10 @@ static void apply_writes(const ApplyLaunch& a) {
   const int ns = a.path == kPathSkinny ? skinny_splits(a.tgt.d_in) : 1;
   write_span<float>(ws + p.hpart_off, 0, (size_t)ns * P * a.tgt.r_pad, "hpart");
   if (a.path == kPathSkinny && decode_expand_fits(a.N, a.k, a.K, a.tgt.r_pad)) {
-    // the decode expand: the summed h rows [P][2][r_pad] bf16 (no sort, no carry)
+    // the decode expand: the summed h rows [P][2][r_pad] bf16 and the pairs' adapters, by pair
+    // id (no sort, no carry)
     write_span<uint16_t>(ws + p.hq_off, 0, (size_t)P * 2 * a.tgt.r_pad, "decode h rows");
+    write_span<int32_t>(ws + p.hq_off + decode_eid_off(P, a.tgt.r_pad), 0, (size_t)P, "decode adapters");
   } else if (a.path == kPathSkinny && a.k > 1 && a.k * a.K <= 64) {
     rank_sort_writes(ws + p.sort_off, P, a.k, a.K);
     if (!a.y_f32) write_span<float>(ws + p.z_off, 0, (size_t)a.N * a.tgt.d_out, "z");
@@ -314,10 +316,12 @@ hipError_t launch_apply_multi(const ApplyLaunch* as, int n, hipStream_t) {
   if (a0.k > 1 && !mp.decode) rank_sort_writes(ws + mp.sort_off, P, a0.k, a0.K);
   for (int i = 0; i < n; ++i) {
     write_span<float>(ws + mp.hpart_off[i], 0, (size_t)skinny_splits(d_in[i]) * P * a0.tgt.r_pad, "hpart (multi)");
-    if (mp.decode)
+    if (mp.decode) {
       write_span<uint16_t>(ws + mp.hq_off[i], 0, (size_t)P * 2 * a0.tgt.r_pad, "decode h rows (multi)");
-    else if (a0.k > 1 && !a0.y_f32)
+      write_span<int32_t>(ws + mp.hq_off[i] + decode_eid_off(P, a0.tgt.r_pad), 0, (size_t)P, "decode adapters (multi)");
+    } else if (a0.k > 1 && !a0.y_f32) {
       write_span<float>(ws + mp.z_off[i], 0, (size_t)a0.N * d_out[i], "z (multi)");
+    }
   }
   return hipSuccess;
 }

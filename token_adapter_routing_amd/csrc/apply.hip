@@ -1188,26 +1188,34 @@ __global__ __launch_bounds__(256) void finish_tokens_multi(FinishMulti m) {
 }
 
 // ---- decode-sized expand (k = 2..4, at most kDXMaxTok tokens, K * r_pad <= kDXMaxKR): the
-// summed h rows of every pair first (hsum_multi), then one launch over (target, 32-column
-// slice).  A workgroup holds that slice of every adapter's B^T in LDS and covers every token:
+// summed h rows of every pair first, by pair id (hsum_multi), then one launch over (target,
+// 32-column slice).  A workgroup holds that slice of every adapter's B^T in LDS and covers every token:
 // each wave owns 16-token row blocks and adds, in registers, the token's routed pairs in
 // adapter order (a repeated adapter once per slot, in slot order), then writes y = y0 + sum.
 // Each adapter's B^T is read once per call, and no sum is carried between launches.
 struct HsumMulti {
   const float* hpart[kApplyMaxMulti];
-  uint16_t* hq[kApplyMaxMulti];
+  uint16_t* hq[kApplyMaxMulti];   // [P][2][r_pad] bf16 hi / lo by pair id
+  int32_t* eid[kApplyMaxMulti];   // [P] adapter of each routed pair
   int nsplit[kApplyMaxMulti];
+  const int32_t* offsets;
+  const int32_t* perm;
   long long P;
+  int K;
 };
 
-// hq[q] = bf16 hi and lo of the sum over the splits (in order) of the weighted partials of
-// grouped position q, as [P][2][r_pad]; a thread per 8 ranks of a row.
+// For grouped position q < offsets[K]: hq[perm[q]] = bf16 hi and lo of the sum over the splits
+// (in order) of the weighted partials of q, and eid[perm[q]] = its adapter; a thread per 8
+// ranks of a row.  The expand then finds a token's pairs at fixed addresses.
 template <int RB>
 __global__ __launch_bounds__(256) void hsum_multi(HsumMulti m) {
   constexpr int RP = RB * 16, CH = RP / 8;
+  __shared__ int offs[65];
+  if ((int)threadIdx.x <= m.K) offs[threadIdx.x] = m.offsets[threadIdx.x];
+  __syncthreads();
   const int i = blockIdx.y;
   const long long v = (long long)blockIdx.x * 256 + threadIdx.x;
-  if (v >= m.P * CH) return;
+  if (v >= (long long)offs[m.K] * CH) return;
   const long long q = v / CH;
   const int c = (int)(v - q * CH);
   float sum[8];
@@ -1222,17 +1230,19 @@ __global__ __launch_bounds__(256) void hsum_multi(HsumMulti m) {
       sum[j + 4] += __uint_as_float(x1[j]);
     }
   }
-  uint16_t* dst = m.hq[i] + q * 2 * RP + 8 * c;
+  const int pid = m.perm[q];
+  uint16_t* dst = m.hq[i] + (size_t)pid * 2 * RP + 8 * c;
   *reinterpret_cast<bf16x8_t*>(dst) = split_hilo(sum, false);
   *reinterpret_cast<bf16x8_t*>(dst + RP) = split_hilo(sum, true);
+  if (c == 0) m.eid[i][pid] = segment_of(offs, m.K, (int)q);
 }
 
 struct DecodeMulti {
   TargetDev tgt[kApplyMaxMulti];
   const void* y0[kApplyMaxMulti];
   void* y[kApplyMaxMulti];
-  const uint16_t* hq[kApplyMaxMulti];
-  const int32_t* offsets;
+  const uint16_t* hq[kApplyMaxMulti];   // by pair id (hsum_multi)
+  const int32_t* eid[kApplyMaxMulti];   // adapter by pair id
   const int32_t* inv;
   int N, k, K;
 };
@@ -1248,7 +1258,6 @@ __global__ __launch_bounds__(kDXThreads, 2) void expand_decode_multi(const Decod
   constexpr int RP = RB * 16, SPR = 2 * RB, NPC = kDXCols * SPR / 64;  // 1 KB pieces per adapter
   static_assert(kDXCols == 32, "two MFMA column blocks per slice");
   __shared__ alignas(16) uint16_t Bs[kDXMaxKR * kDXCols];
-  __shared__ int offs[65];
   const int i = blockIdx.y;
   const TargetDev& tg = m.tgt[i];
   const int d_out = tg.d_out;
@@ -1268,11 +1277,11 @@ __global__ __launch_bounds__(kDXThreads, 2) void expand_decode_multi(const Decod
       __builtin_amdgcn_global_load_lds(src, reinterpret_cast<char*>(Bs) + (size_t)p * 1024, 16, 0, 0);
     }
   }
-  if ((int)threadIdx.x <= m.K) offs[threadIdx.x] = m.offsets[threadIdx.x];
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   constexpr size_t y0b = Y0F32 ? 4 : 2, yb = YF32 ? 4 : 2;
   const uint16_t* hq = m.hq[i];
+  const int32_t* eid = m.eid[i];
   const int N = m.N, k = m.k;
   int b_sl[RB];
 #pragma unroll
@@ -1285,12 +1294,19 @@ __global__ __launch_bounds__(kDXThreads, 2) void expand_decode_multi(const Decod
     uint64_t mine = 0;
 #pragma unroll
     for (int s = 0; s < KMAX; ++s) {
-      const int q = (s < k && tn < N) ? m.inv[(long long)tn * k + s] : -1;
-      es[s] = q >= 0 ? segment_of(offs, m.K, q) : -1;
-      if (q >= 0) mine |= 1ull << es[s];
-      const uint16_t* hp = hq + ((size_t)(q >= 0 ? q : 0) * 2 + (G >> 1)) * RP + 8 * (G & 1);
+      // the pair's routing, adapter and h operands are requested together (fixed addresses)
+      const bool in = s < k && tn < N;
+      const long long pid = in ? (long long)tn * k + s : 0;
+      const int q = in ? m.inv[pid] : -1;
+      const int e = in ? eid[pid] : 0;
+      const uint16_t* hp = hq + ((size_t)pid * 2 + (G >> 1)) * RP + 8 * (G & 1);
+      u32x4_t hv[RB];
 #pragma unroll
-      for (int u = 0; u < RB; ++u) hs[s][u] = q >= 0 ? as_bf16x8(ld16(hp + 16 * u)) : bf16x8_t{};
+      for (int u = 0; u < RB; ++u) hv[u] = in ? ld16(hp + 16 * u) : u32x4_t{0u, 0u, 0u, 0u};
+      es[s] = q >= 0 ? e : -1;
+      if (q >= 0) mine |= 1ull << e;
+#pragma unroll
+      for (int u = 0; u < RB; ++u) hs[s][u] = q >= 0 ? as_bf16x8(hv[u]) : bf16x8_t{};
     }
     // the y0 values of the lane's outputs: rows 4G + j, columns c0 + 2n, + 1
     const int tb = 16 * rb + 4 * G;
@@ -1574,7 +1590,8 @@ static hipError_t launch_expand_tok_t(const ExpandArgs& ea, int grid, hipStream_
 // target's pointers; max_dout is the widest d_out.
 static hipError_t launch_decode_expand(const HsumMulti& hm, const DecodeMulti& dm, int n, int max_dout, int RBv,
                                        bool indirect, bool y0_f32, bool y_f32, hipStream_t s) {
-  if (dm.k < 2 || dm.k > 4 || dm.N > kDXMaxTok || dm.K * RBv * 16 > kDXMaxKR || dm.K > 64 || dm.inv == nullptr)
+  if (dm.k < 2 || dm.k > 4 || dm.N > kDXMaxTok || dm.K * RBv * 16 > kDXMaxKR || dm.K > 64 || dm.inv == nullptr ||
+      hm.K != dm.K)
     return hipErrorInvalidValue;
   if (hm.P == 0) return hipSuccess;
   const long long hthreads = hm.P * 2 * RBv;
@@ -1794,10 +1811,11 @@ hipError_t launch_apply(const ApplyLaunch& a, hipStream_t s) {
     DecodeMulti dm{};
     hm.hpart[0] = sa.hpart;
     hm.hq[0] = reinterpret_cast<uint16_t*>(wsb + plan.hq_off);
+    hm.eid[0] = reinterpret_cast<int32_t*>(wsb + plan.hq_off + decode_eid_off(P, a.tgt.r_pad));
     hm.nsplit[0] = nsplit;
-    hm.P = P;
-    dm.tgt[0] = a.tgt; dm.y0[0] = a.y0; dm.y[0] = a.y; dm.hq[0] = hm.hq[0];
-    dm.offsets = a.offsets; dm.inv = a.inv; dm.N = a.N; dm.k = a.k; dm.K = a.K;
+    hm.offsets = a.offsets; hm.perm = a.perm; hm.P = P; hm.K = a.K;
+    dm.tgt[0] = a.tgt; dm.y0[0] = a.y0; dm.y[0] = a.y; dm.hq[0] = hm.hq[0]; dm.eid[0] = hm.eid[0];
+    dm.inv = a.inv; dm.N = a.N; dm.k = a.k; dm.K = a.K;
     return launch_decode_expand(hm, dm, 1, a.tgt.d_out, RBv, a.indirect, a.y0_f32, a.y_f32, s);
   }
   if (a.path == 2 && a.k * a.K <= 64) {
@@ -1920,12 +1938,13 @@ hipError_t launch_apply_multi(const ApplyLaunch* as, int n, hipStream_t s) {
     for (int i = 0; i < n; ++i) {
       hm.hpart[i] = sm.a[i].hpart;
       hm.hq[i] = reinterpret_cast<uint16_t*>(wsb + mp.hq_off[i]);
+      hm.eid[i] = reinterpret_cast<int32_t*>(wsb + mp.hq_off[i] + decode_eid_off(P, a0.tgt.r_pad));
       hm.nsplit[i] = sm.a[i].nsplit;
-      dm.tgt[i] = as[i].tgt; dm.y0[i] = as[i].y0; dm.y[i] = as[i].y; dm.hq[i] = hm.hq[i];
+      dm.tgt[i] = as[i].tgt; dm.y0[i] = as[i].y0; dm.y[i] = as[i].y; dm.hq[i] = hm.hq[i]; dm.eid[i] = hm.eid[i];
       max_dout = std::max(max_dout, as[i].tgt.d_out);
     }
-    hm.P = P;
-    dm.offsets = a0.offsets; dm.inv = a0.inv; dm.N = a0.N; dm.k = a0.k; dm.K = a0.K;
+    hm.offsets = a0.offsets; hm.perm = a0.perm; hm.P = P; hm.K = a0.K;
+    dm.inv = a0.inv; dm.N = a0.N; dm.k = a0.k; dm.K = a0.K;
     return launch_decode_expand(hm, dm, n, max_dout, RBv, a0.indirect, a0.y0_f32, a0.y_f32, s);
   }
 

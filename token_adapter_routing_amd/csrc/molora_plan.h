@@ -131,6 +131,9 @@ constexpr int kDXCols = 32;
 constexpr int kDXMaxTok = 1024;
 constexpr int kDXMaxKR = 1024;
 bool decode_expand_fits(int N, int k, int K, int r_pad);
+// The decode region: h rows [P][2][r_pad] bf16 by pair id, then the pairs' adapters [P] int32.
+size_t decode_eid_off(long long P, int r_pad);
+size_t decode_hq_bytes(long long P, int r_pad);
 // 64-row grouped tiles (r > 32, or k > 1 with k*K <= 64)
 bool use_gm(int k, int K, int r_pad);
 // The resolved path runs the 64-row grouped kernel: the grouped path where use_gm holds, and
@@ -221,7 +224,7 @@ struct MultiPlan {
   size_t hpart_off[kApplyMaxMulti]; // fused: its h partials
   size_t z_off[kApplyMaxMulti];     // fused: its fp32 carry (bf16 y, k > 1), else 0
   bool decode;                      // fused, decode_expand_fits: h rows instead of sort and carry
-  size_t hq_off[kApplyMaxMulti];    // decode: its h by grouped position [P][2][r_pad] bf16 hi / lo
+  size_t hq_off[kApplyMaxMulti];    // decode: its h rows and pair adapters (decode_hq_bytes)
   size_t total;
 };
 MultiPlan apply_multi_plan(int n, const int* d_in, const int* d_out, int N, int k, int K, int r_pad, bool y_f32,

@@ -133,6 +133,11 @@ bool decode_expand_fits(int N, int k, int K, int r_pad) {
   return k >= 2 && k <= 4 && N <= kDXMaxTok && K * r_pad <= kDXMaxKR;
 }
 
+size_t decode_eid_off(long long P, int r_pad) { return align256((size_t)P * 2 * r_pad * sizeof(uint16_t)); }
+size_t decode_hq_bytes(long long P, int r_pad) {
+  return decode_eid_off(P, r_pad) + align256((size_t)P * sizeof(int32_t));
+}
+
 bool use_gm(int k, int K, int r_pad) { return (k > 1 && k * K <= 64) || (k == 1 && r_pad > 32); }
 
 bool gm_path(int path, int k, int K, int r_pad) {
@@ -250,7 +255,7 @@ ApplyPlan apply_plan(int N, int k, int K, int r_pad, int d_in, int d_out, bool y
   a.total = a.hpart_bytes;
   if (a.path == kPathSkinny && decode_expand_fits(N, k, K, r_pad)) {  // h rows for the decode expand
     a.hq_off = a.hpart_bytes;
-    a.hq_bytes = align256((size_t)P * 2 * r_pad * sizeof(uint16_t));
+    a.hq_bytes = decode_hq_bytes(P, r_pad);
     a.total = a.hq_off + a.hq_bytes;
   } else if (a.path == kPathSkinny && k > 1 && k * K <= 64) {  // one expand pass per rank of the pairs
     a.sort_off = a.hpart_bytes;
@@ -293,7 +298,7 @@ MultiPlan apply_multi_plan(int n, const int* d_in, const int* d_out, int N, int 
     off += align256((size_t)skinny_splits(d_in[i]) * (size_t)P * (size_t)r_pad * sizeof(float));
     if (m.decode) {
       m.hq_off[i] = off;
-      off += align256((size_t)P * 2 * r_pad * sizeof(uint16_t));
+      off += decode_hq_bytes(P, r_pad);
     } else if (k > 1 && !y_f32) {
       m.z_off[i] = off;
       off += align256((size_t)N * d_out[i] * sizeof(float));
