@@ -1047,7 +1047,9 @@ __device__ __forceinline__ void shrink_grouped_body(const ShrinkArgs& a, float* 
 template <int RB, bool INDIRECT>
 __global__ __launch_bounds__(256) void shrink_grouped(ShrinkArgs a) {
   __shared__ float red[RedLds<RB>::kFloats];
-  shrink_grouped_body<RB, INDIRECT>(a, red, blockIdx.x, blockIdx.y);
+  const int T = xcd_tile_slot(a.offsets, a.K, blockIdx.x, threadIdx.x & 63);
+  if (T < 0) return;
+  shrink_grouped_body<RB, INDIRECT>(a, red, T, blockIdx.y);
 }
 
 // Sum the nsplit partials of grouped row q for the lane's rank pieces and split hi/lo.
@@ -1172,7 +1174,9 @@ __global__ __launch_bounds__(256) void shrink_grouped_multi(ShrinkMulti m) {
   __shared__ float red[RedLds<RB>::kFloats];
   const ShrinkArgs& a = m.a[blockIdx.z];
   if ((int)blockIdx.y >= a.nsplit) return;
-  shrink_grouped_body<RB, INDIRECT>(a, red, blockIdx.x, blockIdx.y);
+  const int T = xcd_tile_slot(a.offsets, a.K, blockIdx.x, threadIdx.x & 63);
+  if (T < 0) return;
+  shrink_grouped_body<RB, INDIRECT>(a, red, T, blockIdx.y);
 }
 template <int RB, bool INDIRECT, bool Y0F32, bool YF32>
 __global__ __launch_bounds__(256) void expand_grouped_multi(ExpandMulti m) {
@@ -1518,7 +1522,7 @@ static hipError_t launch_fused_t(const FusedArgs& fa, int grid, hipStream_t s) {
 }
 template <int RB, bool IND>
 static hipError_t launch_shrink_t(const ShrinkArgs& sa, int tiles, hipStream_t s) {
-  hipLaunchKernelGGL((shrink_grouped<RB, IND>), dim3(tiles, sa.nsplit), dim3(256), 0, s, sa);
+  hipLaunchKernelGGL((shrink_grouped<RB, IND>), dim3((tiles + 7) / 8 * 8, sa.nsplit), dim3(256), 0, s, sa);
   return hipGetLastError();
 }
 template <int RB, bool IND, bool Y0F, bool YF>
@@ -1928,7 +1932,7 @@ hipError_t launch_apply_multi(const ApplyLaunch* as, int n, hipStream_t s) {
     max_split = std::max(max_split, sa.nsplit);
   }
   MOLORA_DISPATCH_RB(RBv, MOLORA_DISPATCH_BOOL(a0.indirect, IND,
-      hipLaunchKernelGGL((shrink_grouped_multi<RB, IND>), dim3((int)tiles, max_split, n), dim3(256), 0, s, sm)));
+      hipLaunchKernelGGL((shrink_grouped_multi<RB, IND>), dim3((int)(tiles + 7) / 8 * 8, max_split, n), dim3(256), 0, s, sm)));
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   if (mp.decode) {

@@ -105,6 +105,18 @@ __device__ __forceinline__ bool find_tile(const int* __restrict__ offsets, int K
   return true;
 }
 
+// Tile slot of workgroup x for the tiles of find_tile spread over the 8 XCDs in runs: XCD
+// x % 8 takes tiles [j per, (j + 1) per) with per = ceil(tiles / 8), so an adapter's tiles
+// share an XCD's L2.  The grid's x extent must be a multiple of 8 and at least 8 per; returns
+// -1 for workgroups past the tiles.  Every lane of the wave must call this.
+__device__ __forceinline__ int xcd_tile_slot(const int* __restrict__ offsets, int K, int x, int lane) {
+  int nt = 0;
+  if (lane < K) nt = (offsets[lane + 1] - offsets[lane] + kTileRows - 1) / kTileRows;
+  const int total = __shfl(wave_incl_scan(nt, lane), kWave - 1, kWave);
+  const int per = (total + 7) / 8, j = x >> 3;
+  return j < per ? (x & 7) * per + j : -1;
+}
+
 // Vocabulary range lookup (largest e with b[e] <= v, if b[0] <= v < b[K]; else -1), on bounds
 // held in LDS or registers.
 __device__ __forceinline__ int vocab_owner(int v, const int* b, int K) {
