@@ -250,7 +250,10 @@ int molora_dispatch(const int32_t *idx, const float *w, int N, int k, int K,
  *           _GROUPED_FIXED (the same passes with fixed 64-row tiles per
  *           segment, also for k == 1 and r <= 32: Table 9's fixed tiling, the
  *           comparator of the adaptive one),
- *           _SKINNY (the grouped shrink split over d_in, for small batches), or
+ *           _SKINNY (the grouped shrink split over d_in, for small batches;
+ *           with 2 <= k <= 4, N <= 1024 and K * r_pad <= 1024 one expand
+ *           launch over 32-column slices adds each token's routed pairs in
+ *           registers: no rank passes and no fp32 carry), or
  *           _TILE (8 consecutive tokens per workgroup, every adapter the tile
  *           uses applied in turn; needs K <= 16), or
  *           _BLOCK (64 consecutive tokens per block, two launches: the shrink
@@ -280,8 +283,9 @@ int molora_apply(const molora_hotset *hs, int target, const void *x, const void 
  * adapter targets of a layer, q/k/v/o/gate/up/down, all follow the token's
  * routing decision): the apply of molora_apply for n <= 8 distinct targets,
  * with one launch per phase for all of them on the skinny path (the rank
- * sort of k > 1 done once) and on the block path; the grouped and tile
- * paths apply the targets in turn.
+ * sort of k > 1 done once, or at decode sizes one expand launch for every
+ * target) and on the block path; the grouped and tile paths apply the
+ * targets in turn.
  *   targets host int [n]: hot-set target of each projection (distinct)
  *   x, y0, y host arrays [n] of device pointers, as in molora_apply for
  *           targets[i] (y[i] distinct; y0[i] may equal y[i]); one y0_dtype
