@@ -130,3 +130,41 @@ def test_decode_none_routed():
         y = m.molora_apply(hs, dev_bf16(tgs[0].x), y0, offsets, perm, perm_w, inv, k=k, y_dtype=y_dtype,
                            path=m.PATH_SKINNY)
         np.testing.assert_array_equal(host(y), host(y0))
+
+
+def test_decode_graph_replays():
+    """The decode path captured in a HIP graph (h rows, then the expand of 3 targets): every
+    replay, with eager calls and synchronisations between them, gives the eager bits."""
+    m = need_gpu()
+    N, K, r, k = 256, 16, 64, 3
+    g = np.random.default_rng(77)
+    tgs = _targets(g, N, K, r, DIMS)
+    idx, w = _routing(g, N, K, k)
+    hs = m.molora_hotset_init([(dev_bf16(t.A), dev_bf16(t.B)) for t in tgs], 2.0)
+    _, offsets, perm, perm_w, inv = m.molora_dispatch(dev(idx), dev(w), K, k)
+    xs = [dev_bf16(t.x) for t in tgs]
+    y0s = [dev_bf16(t.y0) for t in tgs]
+    tids = list(range(len(tgs)))
+    ws = torch.zeros(m.molora_apply_multi_workspace(hs, tids, N, k, m.PATH_SKINNY, torch.bfloat16),
+                     dtype=torch.uint8, device="cuda")
+    eager = [host(v) for v in m.molora_apply_multi(hs, xs, y0s, offsets, perm, perm_w, inv, k=k,
+                                                   path=m.PATH_SKINNY, ws=ws)]
+    outs = [torch.empty_like(v) for v in y0s]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        m.molora_apply_multi(hs, xs, y0s, offsets, perm, perm_w, inv, k=k, ys=outs, path=m.PATH_SKINNY, ws=ws)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=s):
+        m.molora_apply_multi(hs, xs, y0s, offsets, perm, perm_w, inv, k=k, ys=outs, path=m.PATH_SKINNY, ws=ws)
+    for rep in range(3):
+        for v in outs:
+            v.zero_()
+        m.molora_apply_multi(hs, xs, y0s, offsets, perm, perm_w, inv, k=k, path=m.PATH_SKINNY)  # eager work between
+        torch.cuda.synchronize()
+        with torch.cuda.stream(s):
+            graph.replay()
+        torch.cuda.synchronize()
+        for i in range(len(tgs)):
+            np.testing.assert_array_equal(host(outs[i]), eager[i])
