@@ -168,3 +168,22 @@ def test_decode_graph_replays():
         torch.cuda.synchronize()
         for i in range(len(tgs)):
             np.testing.assert_array_equal(host(outs[i]), eager[i])
+
+
+@pytest.mark.parametrize("N,K,r,k", [(1025, 16, 64, 2), (1025, 64, 16, 2), (256, 64, 32, 2), (256, 8, 64, 5)])
+def test_decode_bounds_fall_back(N, K, r, k):
+    """Just past the decode path's bounds (1025 tokens; K r_pad = 2048; k = 5) the skinny path
+    runs its rank passes or token expand: multi-target equals per-target calls and the oracle."""
+    m = need_gpu()
+    g = np.random.default_rng(N + K + r + k)
+    tgs = _targets(g, N, K, r, DIMS[:2])
+    idx, w = _routing(g, N, K, k)
+    hs = m.molora_hotset_init([(dev_bf16(t.A), dev_bf16(t.B)) for t in tgs], 2.0)
+    _, offsets, perm, perm_w, inv = m.molora_dispatch(dev(idx), dev(w), K, k)
+    xs = [dev_bf16(t.x) for t in tgs]
+    y0s = [dev_bf16(t.y0) for t in tgs]
+    ys = m.molora_apply_multi(hs, xs, y0s, offsets, perm, perm_w, inv, k=k, path=m.PATH_SKINNY)
+    for i, t in enumerate(tgs):
+        single = m.molora_apply(hs, xs[i], y0s[i], offsets, perm, perm_w, inv, k=k, target=i, path=m.PATH_SKINNY)
+        np.testing.assert_array_equal(host(ys[i]), host(single))
+        check_bf16_output(host(ys[i]), _oracle(t, 2.0, idx, w, K, k))
