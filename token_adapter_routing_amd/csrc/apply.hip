@@ -20,17 +20,22 @@
 //   gs_shrink, gs_finalize, gs_expand
 //                      [GROUPED, rank > 32 or k > 1] one pass over the 64-row tiles of the
 //                      grouped order (gm_dev.h tiling) in three launches split over 512-wide
-//                      slices (gsplit.hip); k = 2, 3: slot_sort (or slot_hist + slot_scatter)
+//                      slices (gsplit.hip); k > 1 from 32 K (K + 1) tokens: pair passes, each
+//                      applying two of a token's routed pairs (gs_expand_pairs over the tuple
+//                      sort's tiles); below that slot_sort (or slot_hist + slot_scatter)
 //                      orders the pairs by (rank among the token's pairs, adapter), one pass
-//                      per rank: within a pass every token has at most one row, so no two
-//                      workgroups write one row; the passes carry the sum in fp32 and
-//                      finish_tokens writes the tokens the last pass does not reach.
+//                      per rank.  Within a pass every token has at most one row, so no two
+//                      workgroups write one row; the passes carry the sum in fp32 and leading
+//                      workgroups of the last expand write the tokens it does not reach.
 //   apply_fused_k1     [GROUPED, k = 1, rank <= 32] 16 grouped rows of one adapter (gathered
 //                      through perm) and a slice of output columns; shrink and expand fused.
 //   shrink_grouped     [SKINNY, GROUPED k > 1 with k*K > 64] the grouped shrink into an fp32
 //                      workspace (weighted by gate and alpha/r), split over d_in, then
 //   expand_grouped_k1  one adapter per token, or one pass per rank (k*K <= 64), or
-//   expand_tokens      token-major over every adapter of a 16-token tile (k*K > 64).
+//   expand_tokens      token-major over every adapter of a 16-token tile (k*K > 64), or
+//   hsum_multi +       [SKINNY, k = 2..4, N <= 1024, K*r_pad <= 1024] the h rows by pair id,
+//   expand_decode_multi then one launch over 32-column slices, every adapter's B^T slice in
+//                      LDS and each token's routed pairs summed in registers.
 //   *_multi            the same phases for several targets sharing one routing, one launch
 //                      per phase (molora_apply_multi).
 //   relayout_A / _B, seqpass_meta: hot-set layout and the per-sequence comparator's metadata.
