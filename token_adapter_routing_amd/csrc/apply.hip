@@ -1026,7 +1026,9 @@ __device__ __forceinline__ void shrink_grouped_body(const ShrinkArgs& a, float* 
   f32x4_t acc[RB];
 #pragma unroll
   for (int u = 0; u < RB; ++u) acc[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  shrink_steps_batched<RB, true>(acc, a.x + (size_t)tok * d_in, At, d_in, sa + (len * wave) / 4,
+  // one step per batch: fewer registers, more waves per SIMD (the skinny workgroups are many
+  // and short; measured faster than two-step batches at rank 64)
+  shrink_steps_batched<RB, true, RB == 1 ? 4 : 1>(acc, a.x + (size_t)tok * d_in, At, d_in, sa + (len * wave) / 4,
                                  sa + (len * (wave + 1)) / 4, lane);
   shrink_to_lds<RB>(acc, red, wave, lane);
   __syncthreads();

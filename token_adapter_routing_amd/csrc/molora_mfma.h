@@ -42,11 +42,11 @@ struct ShrinkBatch {
   static constexpr int SB = RB == 1 ? 4 : 2;
 };
 
-template <int RB, bool SWZ>
+// SB: steps whose loads are issued together (more loads in flight, more registers).
+template <int RB, bool SWZ, int SB = ShrinkBatch<RB>::SB>
 __device__ __forceinline__ void shrink_steps_batched(f32x4_t (&acc)[RB], const uint16_t* __restrict__ xrow,
                                                      const uint16_t* __restrict__ A, int d_in, int s0,
                                                      int s1, int lane) {
-  constexpr int SB = ShrinkBatch<RB>::SB;
   const int n = lane & 15, G = lane >> 4;
   const uint16_t* xp = xrow + G * 8;
   for (int sb = s0; sb < s1; sb += SB) {
