@@ -547,7 +547,7 @@ struct TupleArgs {
 // B^T slices of a (and b) go straight into LDS in the XOR placement, the rows' h operands and
 // y0 rows are requested behind them.
 template <int RB, bool INDIRECT, bool Y0F32, bool YF32>
-__global__ __launch_bounds__(kGSThreads, 2) void gs_expand_pairs(const TupleArgs a) {
+__global__ __launch_bounds__(kGSThreads, 4) void gs_expand_pairs(const TupleArgs a) {
   constexpr int RP = RB * 16, SPR = 2 * RB;  // 16-byte slots per B^T row
   constexpr size_t y0b = Y0F32 ? 4 : 2, yb = YF32 ? 4 : 2;
   constexpr int NY0 = Y0F32 ? 8 : 4;
@@ -613,11 +613,13 @@ __global__ __launch_bounds__(kGSThreads, 2) void gs_expand_pairs(const TupleArgs
   for (int u = 0; u < RB; ++u) hvb[u] = ld16(pb + u * 16);
   __builtin_amdgcn_sched_barrier(0);
   // 3. the y0 rows of both column blocks
+  //    (fp32 rows: the second block's after the first block's MFMAs, which keeps the kernel at
+  //    128 VGPRs, two workgroups per CU)
   RowChunk<Y0F32> yc0, yc1;
   load_row_chunk<Y0F32>(yc0, y0rows, c0, n);
-  load_row_chunk<Y0F32>(yc1, y0rows, c0 + min(1, nb - 1) * kColBlock, n);
+  if constexpr (!Y0F32) load_row_chunk<Y0F32>(yc1, y0rows, c0 + min(1, nb - 1) * kColBlock, n);
   __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_waitcnt(gs_vmcnt(2 * NY0));  // B pieces and h rows have landed (y0 may not)
+  __builtin_amdgcn_s_waitcnt(gs_vmcnt(Y0F32 ? NY0 : 2 * NY0));  // B pieces and h rows have landed (y0 may not)
   __syncthreads();
   int b_sl[RB];
 #pragma unroll
@@ -647,7 +649,10 @@ __global__ __launch_bounds__(kGSThreads, 2) void gs_expand_pairs(const TupleArgs
     epilogue_store<Y0F32, YF32>(o, yc, yrows, c0 + blk * kColBlock, n, vmask);
   };
   block(0, yc0);
-  if (nb > 1) block(1, yc1);
+  if (nb > 1) {
+    if constexpr (Y0F32) load_row_chunk<Y0F32>(yc1, y0rows, c0 + kColBlock, n);
+    block(1, yc1);
+  }
 }
 
 }  // namespace
